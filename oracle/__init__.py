@@ -1,0 +1,179 @@
+"""CPU oracle of the routed-expert MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it and
+shares no code with it: the C source (``oracle.c``) restates the layer's
+definition from the pages in plain loops (fp32 router in a fixed order, exact
+top-k, fp64 FFN).  This wrapper only marshals numpy arrays.
+
+Parity pins (what ties this oracle to the pages and to mathematics rather
+than to itself) live in tests/test_oracle_pins.py; every function below has
+at least one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+IQ2, Q2K, Q8 = 1, 2, 3
+_BW = {IQ2: 256, Q2K: 256, Q8: 32}
+_BB = {IQ2: 66, Q2K: 84, Q8: 34}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (no fast-math; IEEE fmaf and additions)."""
+    tmp = _SO + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+                           "-Wall", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_SO)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.orc_half.argtypes, L.orc_half.restype = [ctypes.c_uint16], ctypes.c_double
+        L.orc_logit.argtypes, L.orc_logit.restype = [P, I, I64, P, I], ctypes.c_float
+        L.orc_router_logits.argtypes = [P, I, I, I, P, I, P]
+        L.orc_topk.argtypes = [P, I, I, I, P]
+        L.orc_route_weights.argtypes = [P, P, I, I, I, P]
+        L.orc_bucket.argtypes = [P, I, I, I, P, P, P, P]
+        L.orc_dequant.argtypes, L.orc_dequant.restype = [I, P, I64, P, P], I
+        L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I, P, P, P, P, I, I, P, I, P, P, P]
+        L.orc_ffn.restype = I
+        L.orc_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _x(x, x_dtype):
+    return _c(x, np.uint16 if x_dtype == BF16 else np.float32)
+
+
+def threads() -> int:
+    return lib().orc_threads()
+
+
+def half(bits: int) -> float:
+    return lib().orc_half(bits)
+
+
+def router_logits(x, x_dtype, W) -> np.ndarray:
+    """z [T, E] fp32 in the fixed summation order (see oracle.c)."""
+    x = _x(x, x_dtype)
+    W = _c(W, np.float32)
+    T, d = x.shape
+    E = W.shape[0]
+    z = np.empty((T, E), dtype=np.float32)
+    lib().orc_router_logits(_p(x), x_dtype, T, d, _p(W), E, _p(z))
+    return z
+
+
+def topk(z, k) -> np.ndarray:
+    z = _c(z, np.float32)
+    T, E = z.shape
+    idx = np.empty((T, k), dtype=np.int32)
+    lib().orc_topk(_p(z), T, E, k, _p(idx))
+    return idx
+
+
+def route_weights(z, idx) -> np.ndarray:
+    z = _c(z, np.float32)
+    idx = _c(idx, np.int32)
+    T, E = z.shape
+    k = idx.shape[1]
+    wt = np.empty((T, k), dtype=np.float32)
+    lib().orc_route_weights(_p(z), _p(idx), T, E, k, _p(wt))
+    return wt
+
+
+def route(x, x_dtype, W, k):
+    """(z, idx, wt) for every token of x."""
+    z = router_logits(x, x_dtype, W)
+    idx = topk(z, k)
+    return z, idx, route_weights(z, idx)
+
+
+def bucket(idx, E):
+    """(counts [E], offsets [E+1], perm [n], pos [n]) of the flat routes."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    n = T * k
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    perm = np.empty(n, np.int32)
+    pos = np.empty(n, np.int32)
+    lib().orc_bucket(_p(idx), T, k, E, _p(counts), _p(offsets), _p(perm), _p(pos))
+    return counts, offsets, perm, pos
+
+
+def dequant(fmt, blocks, grid=None) -> np.ndarray:
+    """Every weight of consecutive blocks, exactly, as float64."""
+    blocks = _c(blocks, np.uint8).reshape(-1)
+    nb = blocks.size // _BB[fmt]
+    assert nb * _BB[fmt] == blocks.size
+    out = np.empty(nb * _BW[fmt], dtype=np.float64)
+    g = None if grid is None else _c(grid, np.uint8)
+    if fmt == IQ2 and g is None:
+        raise ValueError("IQ2 needs a grid")
+    rc = lib().orc_dequant(fmt, _p(blocks), nb, _p(g), _p(out))
+    if rc != 0:
+        raise ValueError("bad format")
+    return out
+
+
+def ffn(layer, x, x_dtype, idx, wt, tokens=None) -> np.ndarray:
+    """Expert FFN + shared expert for the listed tokens (all if None).
+
+    layer: a synth.Layer (canonical bytes).  Returns y [len(tokens), d] fp32.
+    """
+    s = layer.spec
+    x = _x(x, x_dtype)
+    T = x.shape[0]
+    idx = _c(idx, np.int32)
+    wt = _c(wt, np.float32)
+    tok = None if tokens is None else _c(tokens, np.int32)
+    n_tok = T if tok is None else tok.size
+    y = np.empty((n_tok, s.d), dtype=np.float32)
+    sh = s.has_shared
+    k = idx.shape[1]  # routes per token as given (may differ from the layer's top_k)
+    rc = lib().orc_ffn(s.E, s.d, s.f, k, s.fmt_gate_up, s.fmt_down, _p(_c(layer.w_gate, np.uint8)),
+                       _p(_c(layer.w_up, np.uint8)), _p(_c(layer.w_down, np.uint8)), _p(_c(layer.grid, np.uint8)),
+                       int(sh), s.fmt_shared if sh else 0,
+                       _p(_c(layer.s_gate, np.uint8)) if sh else None,
+                       _p(_c(layer.s_up, np.uint8)) if sh else None,
+                       _p(_c(layer.s_down, np.uint8)) if sh else None,
+                       _p(x), x_dtype, T, _p(tok), n_tok, _p(idx), _p(wt), _p(y))
+    if rc != 0:
+        raise ValueError("oracle ffn: token or expert index out of range")
+    return y
+
+
+def layer_forward(layer, x, x_dtype, tokens=None):
+    """Routing + FFN for the listed tokens: returns (y, idx, wt) for them."""
+    x = _x(x, x_dtype)
+    xs = x if tokens is None else x[np.asarray(tokens)]
+    _, idx, wt = route(xs, x_dtype, layer.w_router, layer.spec.k)
+    return ffn(layer, xs, x_dtype, idx, wt), idx, wt

@@ -1,0 +1,365 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU oracle of the routed-expert
+ * MoE layer.  TEST INFRASTRUCTURE ONLY: the product path never loads it;
+ * only the tests, the smoke check and the CPU-baseline leg of the benchmark
+ * may call it.  It shares no code, header or table with the GPU library; it
+ * restates the definitions from the pages and from the byte layouts in its
+ * own words.
+ *
+ * What is computed, step by step:
+ *   router logits  fp32, in the fixed order given at orc_logit()
+ *   selection      exact top-k on the logits, ties to the lower index
+ *   mixing weights sigmoid of the chosen logits, normalised to sum one (fp64)
+ *   bucketing      stable counting sort of the flat routes by expert
+ *   dequantisation every weight exactly, in fp64
+ *   expert FFN     h = silu(G x) * (U x), ye = D h, all in fp64
+ *   combine        y = sum_j wt_j * ye_j + shared(x), fp64, rounded to fp32
+ *
+ * Sources: the layer's sum y = sum_k rw_k * ye_k + ysh with ye taken before
+ * the routing weight is the per-layer MoE sum on "YoungAi -- DeepSeek V4.1
+ * Flash on one DGX Spark", section 4.2 (sidecar gains set to one).  384
+ * experts with 6 chosen per token: same page, section 2.2.  The format mix
+ * (IQ2_XXS-like gate/up, Q2_K-like down, Q8 shared expert, unquantized
+ * router): "Running DeepSeek V4 Flash on an RTX 5080 with 16GB VRAM Under
+ * Linux/WSL2 via DS4", model section, and the txtmix teardown "ds4 拆解",
+ * section 3.  The pages name no score function, activation, summation order
+ * or byte layout; the readings used here are: sigmoid scores, selection on
+ * the raw logit, SwiGLU experts with silu(g) = g / (1 + exp(-g)), the fixed
+ * router order below, and the byte layouts restated at each decoder.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math:
+ * the router order relies on IEEE fmaf and plain additions).
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_IQ2 1
+#define ORC_Q2K 2
+#define ORC_Q8 3
+
+/* ---------------------------------------------------------------------- */
+/* scalar decoding of stored numbers                                      */
+/* ---------------------------------------------------------------------- */
+
+/* IEEE binary16 -> double, exactly (normal, subnormal, inf, nan). */
+double orc_half(uint16_t h) {
+  int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(m + 1024), e - 25);
+  return sign ? -v : v;
+}
+
+/* bf16 bits -> fp32, exactly (the bits are the upper half of an fp32). */
+static float bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+static uint32_t rd32(const uint8_t* p) {
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+static float x_at(const void* x, int x_dtype, int64_t i) {
+  if (x_dtype == ORC_BF16) return bf16_to_f32(((const uint16_t*)x)[i]);
+  return ((const float*)x)[i];
+}
+
+/* ---------------------------------------------------------------------- */
+/* router                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * One router logit in fp32.  The pages give no summation order; exact
+ * indices on both sides need one.  Order used: 64 partial sums start at
+ * +0; element i goes to partial (i / 4) mod 64, each partial consuming its
+ * elements in increasing i with one fused multiply-add each; the partials
+ * are then folded pairwise, halving the count each step: p[l] += p[l + s]
+ * for s = 32, 16, 8, 4, 2, 1; the logit is p[0].
+ */
+float orc_logit(const void* x, int x_dtype, int64_t x_off, const float* w, int d) {
+  float p[64];
+  for (int l = 0; l < 64; l++) p[l] = 0.0f;
+  for (int i = 0; i < d; i++) {
+    int l = (i / 4) % 64;
+    p[l] = fmaf(x_at(x, x_dtype, x_off + i), w[i], p[l]);
+  }
+  for (int s = 32; s >= 1; s /= 2)
+    for (int l = 0; l < s; l++) p[l] = p[l] + p[l + s];
+  return p[0];
+}
+
+/* z[t][e] for all tokens and experts; W is [E][d] fp32, expert-major. */
+void orc_router_logits(const void* x, int x_dtype, int T, int d, const float* W, int E, float* z) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; t++)
+    for (int e = 0; e < E; e++) z[(int64_t)t * E + e] = orc_logit(x, x_dtype, (int64_t)t * d, W + (int64_t)e * d, d);
+}
+
+/*
+ * Exact top-k: repeatedly take the best expert not taken yet.  "Best" is
+ * the larger logit; among equal logits (IEEE equality, so -0 equals +0)
+ * the lower index wins because the scan keeps the first maximum it meets.
+ * Selecting on the logit rather than on sigmoid(logit) gives the same
+ * order in exact arithmetic (sigmoid is strictly increasing).
+ */
+void orc_topk(const float* z, int T, int E, int k, int32_t* idx) {
+  for (int t = 0; t < T; t++) {
+    const float* zt = z + (int64_t)t * E;
+    char* taken = (char*)calloc((size_t)E, 1);
+    for (int r = 0; r < k; r++) {
+      int best = -1;
+      for (int e = 0; e < E; e++)
+        if (!taken[e] && (best < 0 || zt[e] > zt[best])) best = e;
+      taken[best] = 1;
+      idx[(int64_t)t * k + r] = best;
+    }
+    free(taken);
+  }
+}
+
+/*
+ * Mixing weights: s_j = 1 / (1 + exp(-z_j)) for the k selected experts, in
+ * double precision; w_j = s_j / (s_0 + ... + s_{k-1}) with the sum taken in
+ * rank order; stored as fp32.  No extra routed scaling factor.  Selection
+ * keys and mixing weights are separate quantities (YoungAi page, section
+ * 4.2: a selection bias leaves the mixing weights untouched); with no bias
+ * both come from the same logit.
+ */
+void orc_route_weights(const float* z, const int32_t* idx, int T, int E, int k, float* wt) {
+  for (int t = 0; t < T; t++) {
+    double s[64], sum = 0.0;
+    for (int j = 0; j < k; j++) {
+      double zj = (double)z[(int64_t)t * E + idx[(int64_t)t * k + j]];
+      s[j] = 1.0 / (1.0 + exp(-zj));
+    }
+    for (int j = 0; j < k; j++) sum += s[j];
+    for (int j = 0; j < k; j++) wt[(int64_t)t * k + j] = (float)(s[j] / sum);
+  }
+}
+
+/*
+ * Bucketing: a stable counting sort of the flat routes r = t*k + j by their
+ * expert idx[r].  counts, exclusive offsets (offsets[E] = n), perm = routes
+ * ordered by (expert, r), pos = inverse of perm.  Grouping a chunk's tokens
+ * by expert is what lets one pass over an expert's weights serve all of
+ * its rows (YoungAi page, section 4.4, the verify-batch expert kernel).
+ */
+void orc_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                int32_t* pos) {
+  int64_t n = (int64_t)T * k;
+  for (int e = 0; e < E; e++) counts[e] = 0;
+  for (int64_t r = 0; r < n; r++) counts[idx[r]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; e++) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+  for (int e = 0; e < E; e++) next[e] = offsets[e];
+  for (int64_t r = 0; r < n; r++) {
+    int32_t p = next[idx[r]]++;
+    perm[p] = (int32_t)r;
+    pos[r] = p;
+  }
+  free(next);
+}
+
+/* ---------------------------------------------------------------------- */
+/* dequantisation (every value exact in fp64)                              */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * IQ2XXS_L block, 256 weights in 66 bytes: fp16 d; then for sub-block
+ * j = 0..7 two little-endian words A_j, B_j.  A_j byte i is the grid row of
+ * 8-weight group 4j+i; B_j bits 7i..7i+6 are that group's 7 stored signs
+ * and bits 28..31 the sub-block scale s.  The 8th sign of a group is the
+ * parity of its 7 stored signs.  w = d * (2s+1) * grid[row][p] * sign.
+ */
+static void deq_iq2(const uint8_t* b, const uint8_t* grid, double* w) {
+  double d = orc_half(rd16(b));
+  for (int j = 0; j < 8; j++) {
+    uint32_t A = rd32(b + 2 + 8 * j), B = rd32(b + 6 + 8 * j);
+    int s = (int)(B >> 28);
+    for (int i = 0; i < 4; i++) {
+      int row = (int)((A >> (8 * i)) & 255u);
+      int sg = (int)((B >> (7 * i)) & 127u);
+      int parity = __builtin_popcount((unsigned)sg) & 1;
+      for (int p = 0; p < 8; p++) {
+        int neg = p < 7 ? (sg >> p) & 1 : parity;
+        double v = d * (double)(2 * s + 1) * (double)grid[row * 8 + p];
+        w[32 * j + 8 * i + p] = neg ? -v : v;
+      }
+    }
+  }
+}
+
+/*
+ * Q2K_L block, 256 weights in 84 bytes: fp16 d, fp16 dmin, 16 bytes of
+ * (scale low nibble, min high nibble) per 16-weight sub-block, 64 bytes of
+ * 2-bit quants (weight i in bits 2(i%4) of byte i/4).
+ * w_i = d * sc_j * q_i - dmin * m_j, j = i / 16.
+ */
+static void deq_q2k(const uint8_t* b, double* w) {
+  double d = orc_half(rd16(b)), dmin = orc_half(rd16(b + 2));
+  for (int i = 0; i < 256; i++) {
+    int j = i / 16;
+    int sc = b[4 + j] & 15, m = b[4 + j] >> 4;
+    int q = (b[20 + i / 4] >> (2 * (i % 4))) & 3;
+    w[i] = d * (double)sc * (double)q - dmin * (double)m;
+  }
+}
+
+/* Q8_0_L block, 32 weights in 34 bytes: fp16 d then int8 q[32]; w = d q. */
+static void deq_q8(const uint8_t* b, double* w) {
+  double d = orc_half(rd16(b));
+  for (int i = 0; i < 32; i++) w[i] = d * (double)(int8_t)b[2 + i];
+}
+
+static int block_weights(int fmt) { return fmt == ORC_Q8 ? 32 : 256; }
+static int block_bytes(int fmt) { return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : 34; }
+
+/* Decode n_blocks consecutive blocks of `fmt` into fp64. Returns 0 on success. */
+int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t* grid, double* out) {
+  if (fmt != ORC_IQ2 && fmt != ORC_Q2K && fmt != ORC_Q8) return -1;
+  int bw = block_weights(fmt), bb = block_bytes(fmt);
+  for (int64_t i = 0; i < n_blocks; i++) {
+    const uint8_t* b = blocks + i * bb;
+    double* w = out + i * bw;
+    if (fmt == ORC_IQ2)
+      deq_iq2(b, grid, w);
+    else if (fmt == ORC_Q2K)
+      deq_q2k(b, w);
+    else
+      deq_q8(b, w);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* expert FFN                                                              */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * out[n] = sum_i W[n][i] * v[i] over the `rows` rows of one matrix of
+ * `fmt` (row n of expert matrix starts at n * row_bytes), fp64 throughout,
+ * each dot product summed in increasing i.
+ */
+static void matvec(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid, const double* v,
+                   double* out) {
+  int64_t nbk = K / block_weights(fmt);
+  int64_t row_bytes = nbk * block_bytes(fmt);
+#pragma omp parallel
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(static)
+    for (int n = 0; n < rows; n++) {
+      orc_dequant(fmt, mat + (int64_t)n * row_bytes, nbk, grid, w);
+      double acc = 0.0;
+      for (int i = 0; i < K; i++) acc += w[i] * v[i];
+      out[n] = acc;
+    }
+    free(w);
+  }
+}
+
+/* silu(g) = g * sigmoid(g) = g / (1 + exp(-g)). */
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/*
+ * One SwiGLU expert on one token: out = D (silu(G x) * (U x)).
+ * G, U: [f][d]; D: [d][f].
+ */
+static void expert(int fmt_gu, const uint8_t* G, const uint8_t* U, int fmt_dn, const uint8_t* D, int d, int f,
+                   const uint8_t* grid, const double* x, double* out, double* g, double* u) {
+  matvec(fmt_gu, G, f, d, grid, x, g);
+  matvec(fmt_gu, U, f, d, grid, x, u);
+  for (int n = 0; n < f; n++) g[n] = silu(g[n]) * u[n];
+  matvec(fmt_dn, D, d, f, grid, g, out);
+}
+
+static int64_t mat_bytes(int fmt, int rows, int K) {
+  return (int64_t)rows * (K / block_weights(fmt)) * block_bytes(fmt);
+}
+
+/*
+ * Expert FFN of a layer for the tokens listed in `tokens` (n_tok of them;
+ * NULL means tokens 0..T-1) with caller-given routes idx/wt [T][k]:
+ *   acc = sum_j wt[t][j] * D_e(silu(G_e x_t) * (U_e x_t))  (j in rank order)
+ *       + D_s(silu(G_s x_t) * (U_s x_t))                    (if has_shared)
+ *   y[row] = fp32(acc)  (round to nearest even), row = position in `tokens`.
+ * The routing weight multiplies each expert's down-projection output, as in
+ * the per-layer sum of the YoungAi page, section 4.2.
+ */
+int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
+            const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+            const uint8_t* s_up, const uint8_t* s_down, const void* x, int x_dtype, int T, const int32_t* tokens,
+            int n_tok, const int32_t* idx, const float* wt, float* y) {
+  int64_t gu_bytes = mat_bytes(fmt_gu, f, d), dn_bytes = mat_bytes(fmt_dn, d, f);
+  double* xv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  double* ye = (double*)malloc(sizeof(double) * (size_t)d);
+  double* g = (double*)malloc(sizeof(double) * (size_t)f);
+  double* u = (double*)malloc(sizeof(double) * (size_t)f);
+  int count = tokens ? n_tok : T, status = 0;
+  for (int r = 0; r < count && status == 0; r++) {
+    int t = tokens ? tokens[r] : r;
+    if (t < 0 || t >= T) {
+      status = -1;
+      break;
+    }
+    for (int i = 0; i < d; i++) xv[i] = (double)x_at(x, x_dtype, (int64_t)t * d + i);
+    for (int i = 0; i < d; i++) acc[i] = 0.0;
+    for (int j = 0; j < k; j++) {
+      int e = idx[(int64_t)t * k + j];
+      if (e < 0 || e >= E) {
+        status = -1;
+        break;
+      }
+      expert(fmt_gu, w_gate + e * gu_bytes, w_up + e * gu_bytes, fmt_dn, w_down + e * dn_bytes, d, f, grid, xv, ye,
+             g, u);
+      double w = (double)wt[(int64_t)t * k + j];
+      for (int i = 0; i < d; i++) acc[i] += w * ye[i];
+    }
+    if (status != 0) break;
+    if (has_shared) {
+      expert(fmt_sh, s_gate, s_up, fmt_sh, s_down, d, f, grid, xv, ye, g, u);
+      for (int i = 0; i < d; i++) acc[i] += ye[i];
+    }
+    for (int i = 0; i < d; i++) y[(int64_t)r * d + i] = (float)acc[i];
+  }
+  free(xv);
+  free(acc);
+  free(ye);
+  free(g);
+  free(u);
+  return status;
+}
+
+/* Routing of the listed tokens: logits, exact top-k and mixing weights. */
+void orc_route(const void* x, int x_dtype, int T, int d, const float* W, int E, int k, float* z, int32_t* idx,
+               float* wt) {
+  orc_router_logits(x, x_dtype, T, d, W, E, z);
+  orc_topk(z, T, E, k, idx);
+  orc_route_weights(z, idx, T, E, k, wt);
+}
+
+/* Number of OpenMP threads a parallel region would use (reported by bench). */
+int orc_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}

@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties one oracle function to a closed form, a hand-worked value, a
+textbook/library routine it does not use, an invariant, or brute force, so
+that a plausible slip (a dropped term, a wrong sign or index, a transposed
+operand, a different summation order) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_moe_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "format_worked_values.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _bytes(h):
+    return np.frombuffer(bytes.fromhex(h.replace(" ", "")), dtype=np.uint8)
+
+
+# ---------------------------------------------------------------- fp16 ----
+def test_half_matches_numpy_float16_on_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half(int(b)) for b in bits])
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.array_equal(got[~both_nan], ref[~both_nan])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+# ------------------------------------------------------- formats: worked ----
+def _golden_grid(g):
+    grid = np.ones((256, 8), dtype=np.uint8)
+    for r, vals in g["iq2_grid_rows"].items():
+        grid[int(r)] = vals
+    return grid
+
+
+def test_iq2_worked_blocks():
+    g = _golden()
+    grid = _golden_grid(g)
+    base = {b["name"]: b for b in g["iq2_blocks"]}
+    for b in g["iq2_blocks"]:
+        groups = base[b.get("same_groups_as", b["name"])]["groups"]
+        want = np.array(groups, dtype=np.float64).reshape(-1) * b["scale"]
+        got = oracle.dequant(oracle.IQ2, _bytes(b["hex"]), grid)
+        assert np.array_equal(got, want), b["name"]
+
+
+def test_iq2_packer_reproduces_hand_bytes():
+    b = _golden()["iq2_blocks"][0]
+    f = b["fields"]
+    packed = synth.pack_iq2(np.array([1.0], np.float16), np.array([f["rows"]], np.uint8),
+                            np.array([f["signs7"]], np.uint8), np.array([f["scales"]], np.uint8))
+    assert np.array_equal(packed.reshape(-1), _bytes(b["hex"]))
+
+
+def test_q2k_worked_block_and_packer():
+    b = _golden()["q2k_blocks"][0]
+    want = np.array(b["subblocks"], dtype=np.float64).reshape(-1)
+    assert np.array_equal(oracle.dequant(oracle.Q2K, _bytes(b["hex"])), want)
+    f = b["fields"]
+    q = np.tile([0, 1, 2, 3], 64).reshape(16, 16).astype(np.uint8)
+    q[1] = 3
+    q[2] = 2
+    packed = synth.pack_q2k(np.array([0.5], np.float16), np.array([0.25], np.float16),
+                            np.array([f["sc"]], np.uint8), np.array([f["m"]], np.uint8), q.reshape(1, 256))
+    assert np.array_equal(packed.reshape(-1), _bytes(b["hex"]))
+
+
+def test_q8_worked_blocks():
+    g = _golden()["q8_blocks"]
+    a = np.array(g[0]["weights"], dtype=np.float64)
+    assert np.array_equal(oracle.dequant(oracle.Q8, _bytes(g[0]["hex"])), a)
+    assert np.array_equal(oracle.dequant(oracle.Q8, _bytes(g[1]["hex"])), a * g[1]["scale_vs_q8_a"])
+    q = np.array([-128, 127] + list(range(-14, 16)), dtype=np.int8)
+    assert np.array_equal(synth.pack_q8(np.array([0.5], np.float16), q[None]).reshape(-1), _bytes(g[0]["hex"]))
+
+
+# ---------------------------------------------------- formats: round trip ----
+def test_q2k_round_trip_exact_on_representable_blocks():
+    rng = np.random.default_rng(1)
+    nb = 64
+    d = (rng.uniform(0.5, 2.0, nb) * 1e-3).astype(np.float16)
+    dmin = (rng.uniform(0.5, 2.0, nb) * 1e-3).astype(np.float16)
+    sc = rng.integers(1, 16, (nb, 16)).astype(np.uint8)
+    m = rng.integers(0, 16, (nb, 16)).astype(np.uint8)
+    sc[:, 3] = 15  # makes max step / 15 equal d exactly
+    m[:, 5] = 15   # makes max offset / 15 equal dmin exactly
+    q = rng.integers(0, 4, (nb, 16, 16)).astype(np.uint8)
+    q[:, :, 0] = 0  # every sub-block spans its full range [-dmin m, 3 d sc - dmin m]
+    q[:, :, 1] = 3
+    w = oracle.dequant(oracle.Q2K, synth.pack_q2k(d, dmin, sc, m, q.reshape(nb, 256)))
+    assert np.array_equal(oracle.dequant(oracle.Q2K, synth.quantize_q2k(w)), w)
+
+
+def test_q2k_error_bound_on_gaussian_blocks():
+    # |w - dq(q(w))| <= step/2 inside the range, plus the scale-rounding slack:
+    # |err| <= 0.5 d sc_j + 1.6 d + 0.6 dmin  (derivation in quantize_q2k's notes)
+    rng = np.random.default_rng(2)
+    w = rng.normal(0, 0.02, (200, 256))
+    blocks = synth.quantize_q2k(w)
+    back = oracle.dequant(oracle.Q2K, blocks).reshape(200, 16, 16)
+    d = blocks[:, 0:2].copy().view("<f2").astype(np.float64)
+    dmin = blocks[:, 2:4].copy().view("<f2").astype(np.float64)
+    sc = (blocks[:, 4:20] & 15).astype(np.float64)
+    bound = 0.5 * d * sc + 1.6 * d + 0.6 * dmin
+    assert np.all(np.abs(back - w.reshape(200, 16, 16)) <= bound[:, :, None] + 1e-12)
+    # and it is a real quantizer, not a constant (which would give 1.0): four
+    # levels over a 16-sample Gaussian range leave an RMS error near 0.34 sigma
+    assert np.sqrt(np.mean((back.reshape(200, 256) - w) ** 2)) / 0.02 < 0.45
+
+
+def test_q8_round_trip_and_error_bound():
+    rng = np.random.default_rng(3)
+    nb = 64
+    d = (rng.uniform(0.5, 2.0, nb) * 1e-3).astype(np.float16)
+    q = rng.integers(-127, 128, (nb, 32)).astype(np.int8)
+    q[:, 7] = 127 * np.where(rng.integers(0, 2, nb) > 0, 1, -1)
+    w = oracle.dequant(oracle.Q8, synth.pack_q8(d, q))
+    assert np.array_equal(oracle.dequant(oracle.Q8, synth.quantize_q8(w)), w)
+    g = rng.normal(0, 0.02, (100, 32))
+    blk = synth.quantize_q8(g)
+    dd = blk[:, 0:2].copy().view("<f2").astype(np.float64)
+    back = oracle.dequant(oracle.Q8, blk).reshape(100, 32)
+    assert np.all(np.abs(back - g) <= 0.57 * dd + 1e-12)
+
+
+def test_iq2_round_trip_exact_on_representable_blocks():
+    grid = synth.make_grid(0)
+    rng = np.random.default_rng(4)
+    nb = 3
+    d = (rng.uniform(0.5, 2.0, nb) * 1e-4).astype(np.float16)
+    rows = rng.integers(0, 256, (nb, 32)).astype(np.uint8)
+    signs = rng.integers(0, 128, (nb, 32)).astype(np.uint8)
+    scales = rng.integers(0, 16, (nb, 8)).astype(np.uint8)
+    scales[:, 2] = 15
+    rows[:, 8] = int(np.nonzero(grid[:, 0] == 7)[0][0])  # one weight has |code| = 31 * 7
+    w = oracle.dequant(oracle.IQ2, synth.pack_iq2(d, rows, signs, scales), grid)
+    again = oracle.dequant(oracle.IQ2, synth.quantize_iq2(w, grid), grid)
+    assert np.array_equal(again, w)
+
+
+def test_iq2_parity_sign_makes_negatives_even():
+    grid = synth.make_grid(0)
+    blk = synth.random_iq2(np.random.default_rng(5), 50)
+    w = oracle.dequant(oracle.IQ2, blk, grid).reshape(-1, 8)
+    assert np.all((w < 0).sum(axis=1) % 2 == 0)
+    assert np.all(w != 0)
+
+
+def test_grid_rows_distinct_and_odd():
+    grid = synth.make_grid(0)
+    assert grid.shape == (256, 8)
+    assert set(np.unique(grid)) <= {1, 3, 5, 7}
+    assert np.unique(grid, axis=0).shape[0] == 256
+
+
+# ----------------------------------------------------------------- router ----
+def _logit(xv, wv):
+    x = np.asarray(xv, np.float32)[None]
+    W = np.asarray(wv, np.float32)[None]
+    return float(oracle.router_logits(x, oracle.F32, W)[0, 0])
+
+
+def test_router_fold_order_hand_computed():
+    # products 2^24 at i=0 (partial 0), 1 at i=4 (partial 1), -2^24 at i=128
+    # (partial 32).  Folding s=32 first cancels the big terms exactly, then
+    # the 1 survives: z = 1.  A left-to-right sum gives 2^24 + 1 -> 2^24 and
+    # then 0; folding adjacent pairs first also loses the 1.
+    d = 256
+    x = np.zeros(d)
+    w = np.ones(d)
+    x[0], x[4], x[128] = 2.0 ** 24, 1.0, -(2.0 ** 24)
+    assert _logit(x, w) == 1.0
+
+
+def test_router_partial_assignment_hand_computed():
+    # elements 0..3 belong to the same partial and are consumed in order:
+    # 2^24, +1 (rounds back to 2^24), +1 (again), -2^24 -> z = 0.  With a
+    # strided assignment (i mod 64) the same products would give z = 1.
+    d = 256
+    x = np.zeros(d)
+    w = np.ones(d)
+    x[0:4] = [2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)]
+    assert _logit(x, w) == 0.0
+
+
+def test_router_fma_single_rounding():
+    # partial 0 takes -1 * 1 first (p = -1), then a * a with a = 1 + 2^-12:
+    # a fused multiply-add keeps a^2 - 1 = 2^-11 + 2^-24 exactly, while a
+    # separate multiply would round a^2 to 1 + 2^-11 first and give 2^-11.
+    a = np.float32(1.0 + 2.0 ** -12)
+    x = np.zeros(256, np.float32)
+    w = np.zeros(256, np.float32)
+    x[0], w[0] = -1.0, 1.0
+    x[1], w[1] = a, a
+    assert _logit(x, w) == 2.0 ** -11 + 2.0 ** -24
+
+
+def test_router_basis_vectors_read_one_weight():
+    rng = np.random.default_rng(6)
+    W = rng.normal(0, 0.02, (8, 512)).astype(np.float32)
+    for i in [0, 3, 4, 255, 256, 511]:
+        x = np.zeros((1, 512), np.float32)
+        x[0, i] = 1.0
+        assert np.array_equal(oracle.router_logits(x, oracle.F32, W)[0], W[:, i])
+
+
+def test_router_error_bound_against_fp64():
+    rng = np.random.default_rng(7)
+    d, E = 4096, 64
+    x = rng.normal(0, 1, (4, d)).astype(np.float32)
+    W = rng.normal(0, 0.02, (E, d)).astype(np.float32)
+    z = oracle.router_logits(x, oracle.F32, W).astype(np.float64)
+    exact = x.astype(np.float64) @ W.astype(np.float64).T
+    mag = np.abs(x.astype(np.float64)) @ np.abs(W.astype(np.float64)).T
+    n = d // 64 + 6  # longest chain of roundings: one partial, then the folds
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    assert np.all(np.abs(z - exact) <= gamma * mag)
+
+
+def test_router_bf16_input_is_widened_exactly():
+    rng = np.random.default_rng(8)
+    xb = synth.f32_to_bf16_bits(rng.normal(0, 1, (3, 256)).astype(np.float32))
+    W = rng.normal(0, 0.02, (5, 256)).astype(np.float32)
+    zf = oracle.router_logits(synth.bf16_bits_to_f32(xb), oracle.F32, W)
+    zb = oracle.router_logits(xb, oracle.BF16, W)
+    assert np.array_equal(zf, zb)
+
+
+# ------------------------------------------------------------------ top-k ----
+def test_topk_matches_brute_force_with_ties():
+    rng = np.random.default_rng(9)
+    for E, k in [(8, 2), (384, 6), (37, 16), (5, 5)]:
+        z = rng.integers(-3, 4, (20, E)).astype(np.float32)  # many exact ties
+        idx = oracle.topk(z, k)
+        for t in range(20):
+            want = sorted(range(E), key=lambda e: (-z[t, e], e))[:k]
+            assert list(idx[t]) == want
+
+
+def test_topk_special_cases():
+    z = np.zeros((1, 10), np.float32)
+    assert list(oracle.topk(z, 4)[0]) == [0, 1, 2, 3]          # all equal -> lowest indices
+    z = np.array([[0.5, 0.0, 0.5, -0.0, 0.25]], np.float32)
+    assert list(oracle.topk(z, 4)[0]) == [0, 2, 4, 1]         # -0 == +0 -> lower index 1
+    z = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert list(oracle.topk(z, 3)[0]) == [0, 1, 2]
+    rng = np.random.default_rng(10)
+    z = rng.normal(size=(3, 12)).astype(np.float32)
+    for t in range(3):                                        # k = E: a full permutation
+        assert sorted(oracle.topk(z, 12)[t]) == list(range(12))
+    # duplicated router rows give equal logits: the lower expert wins
+    W = rng.normal(0, 0.02, (6, 256)).astype(np.float32)
+    W[4] = W[1]
+    x = rng.normal(0, 1, (5, 256)).astype(np.float32)
+    _, idx, _ = oracle.route(x, oracle.F32, W, 6)
+    for t in range(5):
+        assert list(idx[t]).index(1) == list(idx[t]).index(4) - 1
+
+
+# ---------------------------------------------------------------- weights ----
+def test_weights_closed_forms():
+    z = np.array([[0.0, math.log(3.0), -5.0]], np.float32)
+    wt = oracle.route_weights(z, np.array([[1, 0]], np.int32))
+    # sigmoid(log 3) = 3/4, sigmoid(0) = 1/2 -> 0.75/1.25, 0.5/1.25
+    assert abs(wt[0, 0] - 0.6) < 1e-7 and abs(wt[0, 1] - 0.4) < 1e-7
+    assert oracle.route_weights(z, np.array([[2]], np.int32))[0, 0] == 1.0
+    zz = np.full((1, 6), 0.3, np.float32)
+    assert np.allclose(oracle.route_weights(zz, np.arange(6, dtype=np.int32)[None]), 1 / 6, atol=1e-7)
+
+
+def test_weights_sum_to_one_and_positive():
+    rng = np.random.default_rng(11)
+    z = rng.normal(0, 3, (50, 384)).astype(np.float32)
+    idx = oracle.topk(z, 6)
+    wt = oracle.route_weights(z, idx)
+    assert np.all(wt > 0)
+    assert np.all(np.abs(wt.astype(np.float64).sum(axis=1) - 1) < 1e-6)
+    assert np.all(np.diff(wt, axis=1) <= 0)  # rank order -> non-increasing weights
+
+
+# ---------------------------------------------------------------- buckets ----
+def test_bucket_matches_stable_argsort():
+    rng = np.random.default_rng(12)
+    for T, k, E in [(1, 6, 384), (1024, 6, 384), (7, 2, 8), (0, 6, 384), (33, 16, 20)]:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+        counts, offsets, perm, pos = oracle.bucket(idx, E)
+        flat = idx.reshape(-1)
+        assert np.array_equal(counts, np.bincount(flat, minlength=E))
+        assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts) and offsets[-1] == T * k
+        assert np.array_equal(perm, np.argsort(flat, kind="stable"))
+        assert np.array_equal(pos[perm], np.arange(T * k))
+
+
+def test_bucket_mean_load_matches_closed_form():
+    # T*k/E routed rows per expert on average: 8,192 tokens x 6 / 384 = 128,
+    # the ~128 rows per expert the YoungAi page (section 4.2) quotes.
+    rng = np.random.default_rng(13)
+    idx = np.stack([rng.choice(384, 6, replace=False) for _ in range(8192)]).astype(np.int32)
+    counts, *_ = oracle.bucket(idx, 384)
+    assert counts.mean() == 128.0
+
+
+# -------------------------------------------------------------------- FFN ----
+def _q8_identity_layer(E, d, f, gate_col, up_col, has_shared):
+    """Q8 layer with d = 1: gate row n reads x[gate_col], up row n reads
+    x[up_col], down row r reads h[r] (r < f) -- so y has a closed form."""
+    def mat(rows, K, col_of_row):
+        q = np.zeros((rows, K), np.int8)
+        for r in range(rows):
+            c = col_of_row(r)
+            if c is not None:
+                q[r, c] = 1
+        return synth.pack_q8(np.ones(rows * K // 32, np.float16), q.reshape(-1, 32)).reshape(-1)
+
+    spec = synth.LayerSpec(E=E, k=1, d=d, f=f, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_Q8,
+                           has_shared=has_shared, fmt_shared=synth.FMT_Q8)
+    g = mat(f, d, lambda r: gate_col)
+    u = mat(f, d, lambda r: up_col)
+    dn = mat(d, f, lambda r: r if r < f else None)
+    L = synth.Layer(spec=spec, w_gate=np.tile(g, E), w_up=np.tile(u, E), w_down=np.tile(dn, E),
+                    grid=synth.make_grid(0), w_router=np.zeros((E, d), np.float32))
+    if has_shared:
+        L.s_gate, L.s_up, L.s_down = g, u, dn
+    return L
+
+
+def test_ffn_closed_form_swiglu():
+    d, f = 64, 32
+    L = _q8_identity_layer(E=2, d=d, f=f, gate_col=0, up_col=1, has_shared=True)
+    x = np.zeros((1, d), np.float32)
+    x[0, 0], x[0, 1] = 1.0, 2.0
+    # g = 1, u = 2 -> h = silu(1) * 2 = 2 / (1 + e^-1); y[r] = wt * h + h for r < f
+    h = 2.0 / (1.0 + math.exp(-1.0))
+    y = oracle.ffn(L, x, oracle.F32, np.array([[1]], np.int32), np.array([[0.25]], np.float32))
+    want = np.zeros(d)
+    want[:f] = 1.25 * h
+    assert np.allclose(y[0], want, rtol=1e-7, atol=0)
+    x[0, 0] = -3.0  # silu(-3) = -3 / (1 + e^3)
+    y = oracle.ffn(L, x, oracle.F32, np.array([[0]], np.int32), np.array([[1.0]], np.float32))
+    assert np.allclose(y[0, :f], 2 * (-3.0 / (1 + math.exp(3.0))) * 2.0, rtol=1e-7)
+
+
+def _dense(L, fmt, blob, e, rows, K):
+    per = blob.size // (L.spec.E if e is not None else 1)
+    b = blob if e is None else blob[e * per:(e + 1) * per]
+    return oracle.dequant(fmt, b, L.grid).reshape(rows, K)
+
+
+def _numpy_ffn(L, x, idx, wt):
+    s = L.spec
+    y = np.zeros((x.shape[0], s.d))
+    for t in range(x.shape[0]):
+        xv = x[t].astype(np.float64)
+        for j in range(s.k):
+            e = idx[t, j]
+            g = _dense(L, s.fmt_gate_up, L.w_gate, e, s.f, s.d) @ xv
+            u = _dense(L, s.fmt_gate_up, L.w_up, e, s.f, s.d) @ xv
+            h = g / (1 + np.exp(-g)) * u
+            y[t] += float(wt[t, j]) * (_dense(L, s.fmt_down, L.w_down, e, s.d, s.f) @ h)
+        if s.has_shared:
+            g = _dense(L, s.fmt_shared, L.s_gate, None, s.f, s.d) @ xv
+            u = _dense(L, s.fmt_shared, L.s_up, None, s.f, s.d) @ xv
+            y[t] += _dense(L, s.fmt_shared, L.s_down, None, s.d, s.f) @ (g / (1 + np.exp(-g)) * u)
+    return y
+
+
+@pytest.mark.parametrize("spec", [
+    synth.TINY_SPEC,
+    synth.scaled_spec(E=6, k=3, d=512, f=256),                       # IQ2 gate/up, Q2K down, Q8 shared
+    synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_IQ2,
+                      fmt_shared=synth.FMT_Q2K),
+])
+def test_ffn_matches_numpy_dense_matmul(spec):
+    L = synth.random_layer(spec, seed=3, workload="pin")
+    x = synth.activations(3, ("pin", "x"), 5, spec.d, synth.F32)
+    _, idx, wt = oracle.route(x, oracle.F32, L.w_router, spec.k)
+    y = oracle.ffn(L, x, oracle.F32, idx, wt)
+    ref = _numpy_ffn(L, x, idx, wt)
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+
+
+def test_ffn_invariants():
+    spec = synth.scaled_spec(E=6, k=3, d=256, f=256, has_shared=False)
+    L = synth.random_layer(spec, seed=4, workload="inv")
+    x = synth.activations(4, ("inv", "x"), 3, spec.d, synth.F32)
+    _, idx, wt = oracle.route(x, oracle.F32, L.w_router, spec.k)
+    y = oracle.ffn(L, x, oracle.F32, idx, wt)
+    # relabelling experts (weights and routes together) changes nothing
+    perm = np.array([3, 5, 0, 1, 4, 2])
+    inv = np.argsort(perm)
+
+    def relabel(blob):
+        per = blob.size // spec.E
+        return np.concatenate([blob[perm[e] * per:(perm[e] + 1) * per] for e in range(spec.E)])
+    L2 = synth.Layer(spec=spec, w_gate=relabel(L.w_gate), w_up=relabel(L.w_up), w_down=relabel(L.w_down),
+                     grid=L.grid, w_router=L.w_router[perm])
+    assert np.array_equal(oracle.ffn(L2, x, oracle.F32, inv[idx].astype(np.int32), wt), y)
+    # doubling every down-projection scale doubles the (routed-only) output exactly
+    dn = L.w_down.reshape(-1, 84).copy()
+    for off in (0, 2):
+        v = dn[:, off:off + 2].copy().view("<f2").astype(np.float32) * 2
+        dn[:, off:off + 2] = v.astype("<f2").view(np.uint8).reshape(-1, 2)
+    L3 = synth.Layer(spec=spec, w_gate=L.w_gate, w_up=L.w_up, w_down=dn.reshape(-1), grid=L.grid,
+                     w_router=L.w_router)
+    assert np.array_equal(oracle.ffn(L3, x, oracle.F32, idx, wt), 2 * y)
+    # one-hot routing weights pick one expert's output
+    one = np.zeros_like(wt)
+    one[:, 1] = 1.0
+    y1 = oracle.ffn(L, x, oracle.F32, idx, one)
+    for t in range(3):
+        solo = oracle.ffn(L, x[t:t + 1], oracle.F32, idx[t:t + 1, 1:2].copy(), np.ones((1, 1), np.float32))
+        assert np.array_equal(y1[t], solo[0])
+    # a token subset gives the same rows as the full call
+    assert np.array_equal(oracle.ffn(L, x, oracle.F32, idx, wt, tokens=[2, 0]), y[[2, 0]])
+
+
+def test_tiny_workload_layer_forward_against_dense():
+    L = synth.tiny_layer(0)
+    x = synth.activations(0, ("tiny", "x"), 4, 256, synth.F32)
+    y, idx, wt = oracle.layer_forward(L, x, oracle.F32)
+    ref = _numpy_ffn(L, x, idx, wt)
+    assert np.allclose(y, ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+    assert np.all(np.abs(wt.sum(axis=1) - 1) < 1e-6)
+
+
+def test_session_routes_distinct_expert_curve():
+    # the reuse generator follows the pages' distinct-expert curve over 1..5
+    # consecutive tokens: 6, 10.0, 13.3, 17.4, 21.7 (YoungAi page, section 2.2).
+    # The printed increments (4.0, 3.3, 4.1, 4.3) dip at the third token, which
+    # no memoryless reuse model reproduces; the model sits ~0.55 above 13.3 and
+    # within ~0.35 of the other points, hence the 0.7 band.
+    idx, wt = synth.session_routes(0, sessions=2000, steps=5, tag="curve")
+    per = idx.reshape(5, 2000, 6)
+    means = [np.mean([len(set(per[:n, s].reshape(-1))) for s in range(2000)]) for n in range(1, 6)]
+    for got, want in zip(means, [6, 10.0, 13.3, 17.4, 21.7]):
+        assert abs(got - want) < 0.7, means
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])  # distinct per token
+    assert np.all(np.abs(wt.sum(axis=1) - 1) < 1e-6)
+
+
+def test_zipf_routes_are_skewed_and_distinct():
+    idx, _ = synth.zipf_routes(0, 4096)
+    counts = np.bincount(idx.reshape(-1), minlength=384)
+    assert counts.sum() == 4096 * 6 and counts.max() > 20 * max(1, np.median(counts))
+    assert np.all(np.sort(idx, axis=1)[:, 1:] != np.sort(idx, axis=1)[:, :-1])
