@@ -1,0 +1,610 @@
+// C ABI of libqmoe (declarations and contracts: include/moe.h).
+//
+// Host side only: argument validation (before anything is enqueued),
+// workspace carving, path selection and launches.  The narrow C interface
+// that hides tensor internals from its callers follows the ds4 engine's
+// design of a small public header over a fixed in-engine layout ("ds4
+// timeline", files.btbytes.com: ds4.h as the narrow public API), and the
+// refusal of unknown formats and versions follows the fail-loudly format
+// whitelist on "YoungAi -- DeepSeek V4.1 Flash on one DGX Spark", section 4.1.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace qmoe;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_err;
+
+static int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+static int ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+static int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_CHECK(expr, what)                  \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// profiling (events on the launch stream; eager use only)
+// ---------------------------------------------------------------------------
+namespace qmoe {
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+static std::mutex g_prof_mu;
+static std::vector<ProfRec> g_prof;
+static bool g_prof_on = false;
+
+int prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof_on) return -1;
+  ProfRec r;
+  r.name = name;
+  if (hipEventCreate(&r.a) != hipSuccess) return -1;
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    return -1;
+  }
+  (void)hipEventRecord(r.a, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back(r);
+  return (int)g_prof.size() - 1;
+}
+
+void prof_end(int id, hipStream_t s) {
+  if (id < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (id < (int)g_prof.size()) (void)hipEventRecord(g_prof[id].b, s);
+}
+}  // namespace qmoe
+
+extern "C" int moe_profile_enable(int32_t on) {
+  g_prof_on = on != 0;
+  return ok();
+}
+
+extern "C" int moe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return ok();
+}
+
+extern "C" int moe_profile_collect(int32_t max_kernels, char* names, int64_t* launches, double* total_ms,
+                                   int32_t* n_kernels) {
+  if (!names || !launches || !total_ms || !n_kernels || max_kernels < 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_profile_collect: null output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<std::string> keys;
+  std::vector<double> ms;
+  std::vector<int64_t> cnt;
+  for (auto& r : g_prof) {
+    HIP_CHECK(hipEventSynchronize(r.b), "hipEventSynchronize");
+    float t = 0.f;
+    HIP_CHECK(hipEventElapsedTime(&t, r.a, r.b), "hipEventElapsedTime");
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != r.name) i++;
+    if (i == keys.size()) {
+      keys.push_back(r.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += t;
+    cnt[i] += 1;
+  }
+  const int n = (int)keys.size() < max_kernels ? (int)keys.size() : max_kernels;
+  for (int i = 0; i < n; i++) {
+    strncpy(names + 48 * i, keys[i].c_str(), 47);
+    names[48 * i + 47] = 0;
+    launches[i] = cnt[i];
+    total_ms[i] = ms[i];
+  }
+  *n_kernels = n;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+static bool fmt_known(int f) { return f == MOE_FMT_IQ2XXS_L || f == MOE_FMT_Q2K_L || f == MOE_FMT_Q8_0_L; }
+
+#define NEED_PTR(p, what)                                                                       \
+  do {                                                                                          \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is null", fn, what);                     \
+    if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, what); \
+  } while (0)
+
+static int check_dims(const char* fn, int E, int d, int k) {
+  if (E < 1 || E > MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d not in [1, %d]", fn, E, MAX_EXPERTS);
+  if (!pow2_in(d, 256, 8192)) return fail(MOE_ERR_INVALID_ARG, "%s: d_model %d is not a power of two in [256, 8192]", fn, d);
+  if (k < 1 || k > TOPK_MAX_K || k > E)
+    return fail(MOE_ERR_INVALID_ARG, "%s: top_k %d not in [1, min(n_experts, %d)]", fn, k, TOPK_MAX_K);
+  return MOE_OK;
+}
+
+static int check_T(const char* fn, int T) {
+  if (T < 0 || T > 65536) return fail(MOE_ERR_INVALID_ARG, "%s: T %d not in [0, 65536]", fn, T);
+  return MOE_OK;
+}
+
+static int check_dtype(const char* fn, int x_dtype) {
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown activation dtype %d", fn, x_dtype);
+  return MOE_OK;
+}
+
+// Checks every field of a layer that the compute paths read.
+static int check_layer(const char* fn, const moe_layer* L, bool need_router) {
+  if (!L) return fail(MOE_ERR_INVALID_ARG, "%s: layer is null", fn);
+  if (L->abi_version != MOE_ABI_VERSION)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: layer abi_version %u, library speaks %d", fn, L->abi_version, MOE_ABI_VERSION);
+  int rc = check_dims(fn, L->n_experts, L->d_model, L->top_k);
+  if (rc) return rc;
+  if (!pow2_in(L->d_ff, 256, 8192)) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff %d is not a power of two in [256, 8192]", fn, L->d_ff);
+  if (!fmt_known(L->fmt_gate_up)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown gate/up format %d", fn, L->fmt_gate_up);
+  if (!fmt_known(L->fmt_down)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown down format %d", fn, L->fmt_down);
+  if (L->layout != MOE_LAYOUT_DEVICE) {
+    if (L->layout == MOE_LAYOUT_CANONICAL)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: weights must be in MOE_LAYOUT_DEVICE (convert with moe_repack)", fn);
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown layout %d", fn, L->layout);
+  }
+  if (L->has_shared != 0 && L->has_shared != 1) return fail(MOE_ERR_INVALID_ARG, "%s: has_shared must be 0 or 1", fn);
+  NEED_PTR(L->w_gate, "w_gate");
+  NEED_PTR(L->w_up, "w_up");
+  NEED_PTR(L->w_down, "w_down");
+  bool iq2 = L->fmt_gate_up == MOE_FMT_IQ2XXS_L || L->fmt_down == MOE_FMT_IQ2XXS_L;
+  if (L->has_shared) {
+    if (!fmt_known(L->fmt_shared)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown shared format %d", fn, L->fmt_shared);
+    NEED_PTR(L->s_gate, "s_gate");
+    NEED_PTR(L->s_up, "s_up");
+    NEED_PTR(L->s_down, "s_down");
+    iq2 = iq2 || L->fmt_shared == MOE_FMT_IQ2XXS_L;
+  }
+  if (iq2) NEED_PTR(L->iq2_grid, "iq2_grid");
+  if (need_router) NEED_PTR(L->w_router, "w_router");
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------
+namespace {
+struct Carve {
+  size_t off = 0;
+  uint8_t* base = nullptr;
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+struct RouteWs {
+  float* z;
+};
+struct DecodeWs {
+  float* h;
+};
+struct PrefillWs {
+  int32_t *counts, *offsets, *tile_start, *perm, *pos;
+  void *H, *Hs;
+  float *Ye, *Ysh;
+};
+struct LayerWs {
+  float* z;
+  int32_t* idx;
+  float* wt;
+};
+
+void carve_route(Carve& c, RouteWs& w, int E, int T) { w.z = (float*)c.take((size_t)T * E * 4); }
+void carve_decode(Carve& c, DecodeWs& w, int T, int k, int f) { w.h = (float*)c.take((size_t)(T * k + T) * f * 4); }
+void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, int has_shared, bool bucket_out) {
+  const size_t n = (size_t)T * k;
+  if (!bucket_out) {
+    w.counts = (int32_t*)c.take((size_t)E * 4);
+    w.offsets = (int32_t*)c.take((size_t)(E + 1) * 4);
+    w.perm = (int32_t*)c.take(n * 4);
+  }
+  w.tile_start = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.pos = (int32_t*)c.take(n * 4);
+  w.H = c.take(n * f * 2);
+  w.Ye = (float*)c.take(n * d * 4);
+  if (has_shared) {
+    w.Hs = c.take((size_t)T * f * 2);
+    w.Ysh = (float*)c.take((size_t)T * d * 4);
+  } else {
+    w.Hs = nullptr;
+    w.Ysh = nullptr;
+  }
+}
+void carve_layer_routes(Carve& c, LayerWs& w, int E, int T, int k) {
+  w.z = (float*)c.take((size_t)T * E * 4);
+  w.idx = (int32_t*)c.take((size_t)T * k * 4);
+  w.wt = (float*)c.take((size_t)T * k * 4);
+}
+
+size_t ws_route(int E, int T) {
+  Carve c;
+  RouteWs w;
+  carve_route(c, w, E, T);
+  return c.off;
+}
+size_t ws_decode(int T, int k, int f) {
+  Carve c;
+  DecodeWs w;
+  carve_decode(c, w, T, k, f);
+  return c.off;
+}
+size_t ws_prefill(int E, int T, int k, int d, int f, int sh) {
+  Carve c;
+  PrefillWs w;
+  carve_prefill(c, w, E, T, k, d, f, sh, false);
+  return c.off;
+}
+size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
+  Carve c;
+  LayerWs lw;
+  carve_layer_routes(c, lw, E, T, k);
+  if (path == MOE_PATH_DECODE) {
+    DecodeWs w;
+    carve_decode(c, w, T, k, f);
+  } else {
+    PrefillWs w;
+    carve_prefill(c, w, E, T, k, d, f, sh, false);
+  }
+  return c.off;
+}
+}  // namespace
+
+static int resolve_path(int path, int T) {
+  if (path == MOE_PATH_AUTO) return T <= DECODE_MAX_T ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  return path;
+}
+
+// ---------------------------------------------------------------------------
+// exported entry points
+// ---------------------------------------------------------------------------
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+extern "C" const char* moe_last_error(void) { return g_err.c_str(); }
+
+extern "C" const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int moe_matrix_bytes(int32_t fmt, int32_t n_experts, int32_t rows, int32_t K, size_t* bytes) {
+  const char* fn = "moe_matrix_bytes";
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "%s: bytes is null", fn);
+  if (!fmt_known(fmt)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
+  if (n_experts < 1 || rows < 1 || K < 1 || K % block_weights(fmt) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad shape (%d experts, %d rows, K %d)", fn, n_experts, rows, K);
+  *bytes = (size_t)n_experts * rows * (K / block_weights(fmt)) * block_bytes(fmt);
+  return ok();
+}
+
+extern "C" int moe_workspace_bytes(const moe_layer* L, int32_t T, int32_t op, size_t* bytes) {
+  const char* fn = "moe_workspace_bytes";
+  if (!L || !bytes) return fail(MOE_ERR_INVALID_ARG, "%s: null argument", fn);
+  int rc = check_T(fn, T);
+  if (rc) return rc;
+  if (op == MOE_OP_ROUTE) {
+    if (L->n_experts < 1 || L->n_experts > MAX_EXPERTS)
+      return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d not in [1, %d]", fn, L->n_experts, MAX_EXPERTS);
+    *bytes = ws_route(L->n_experts, T);
+    return ok();
+  }
+  rc = check_dims(fn, L->n_experts, L->d_model, L->top_k);
+  if (rc) return rc;
+  if (!pow2_in(L->d_ff, 256, 8192)) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff %d is not a power of two in [256, 8192]", fn, L->d_ff);
+  const int E = L->n_experts, d = L->d_model, f = L->d_ff, k = L->top_k, sh = L->has_shared ? 1 : 0;
+  switch (op) {
+    case MOE_OP_DECODE: *bytes = ws_decode(T, k, f); break;
+    case MOE_OP_PREFILL: *bytes = ws_prefill(E, T, k, d, f, sh); break;
+    case MOE_OP_LAYER: {
+      size_t b = ws_layer(E, T, k, d, f, sh, MOE_PATH_PREFILL);
+      if (T <= DECODE_MAX_T) {
+        const size_t b2 = ws_layer(E, T, k, d, f, sh, MOE_PATH_DECODE);
+        if (b2 > b) b = b2;
+      }
+      *bytes = b;
+      break;
+    }
+    default: return fail(MOE_ERR_INVALID_ARG, "%s: unknown op %d", fn, op);
+  }
+  return ok();
+}
+
+extern "C" int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t K, const void* src, void* dst,
+                          int32_t direction, void* stream) {
+  const char* fn = "moe_repack";
+  if (!fmt_known(fmt)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
+  if (n_experts < 1 || rows < 1 || K < 1 || K % block_weights(fmt) != 0)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad shape (%d experts, %d rows, K %d)", fn, n_experts, rows, K);
+  if (direction != MOE_REPACK_TO_DEVICE && direction != MOE_REPACK_TO_CANONICAL)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown direction %d", fn, direction);
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "%s: null buffer", fn);
+  if (src == dst) return fail(MOE_ERR_INVALID_ARG, "%s: src and dst must be distinct buffers", fn);
+  const int64_t nb = (int64_t)n_experts * rows * (K / block_weights(fmt));
+  hipStream_t s = (hipStream_t)stream;
+  const int pid = prof_begin("repack", s);
+  hipError_t e = launch_repack(fmt, nb, src, dst, direction == MOE_REPACK_TO_DEVICE, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+extern "C" int moe_route_topk(const float* w_router, int32_t E, int32_t d, const void* x, int32_t x_dtype, int32_t T,
+                              int32_t k, int32_t* idx, float* wt, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_route_topk";
+  int rc = check_dims(fn, E, d, k);
+  if (rc) return rc;
+  if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
+  if (T == 0) return ok();
+  NEED_PTR(w_router, "w_router");
+  NEED_PTR(x, "x");
+  NEED_PTR(idx, "idx");
+  NEED_PTR(wt, "wt");
+  NEED_PTR(ws, "workspace");
+  const size_t need = ws_route(E, T);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  Carve c;
+  c.base = (uint8_t*)ws;
+  RouteWs w;
+  carve_route(c, w, E, T);
+  hipStream_t s = (hipStream_t)stream;
+  int pid = prof_begin(T <= ROUTER_ROWS_MAX_T ? "router_rows" : "router_tiled", s);
+  hipError_t e = launch_router(w_router, E, d, x, x_dtype, T, w.z, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  pid = prof_begin("topk", s);
+  e = launch_topk(w.z, T, E, k, idx, wt, nullptr, nullptr, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+extern "C" int moe_bucket(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* pos, void* stream) {
+  const char* fn = "moe_bucket";
+  if (E < 1 || E > MAX_EXPERTS) return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d not in [1, %d]", fn, E, MAX_EXPERTS);
+  if (k < 1 || k > TOPK_MAX_K || k > E) return fail(MOE_ERR_INVALID_ARG, "%s: top_k %d out of range", fn, k);
+  int rc = check_T(fn, T);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  NEED_PTR(idx, "idx");
+  NEED_PTR(counts, "counts");
+  NEED_PTR(offsets, "offsets");
+  NEED_PTR(perm, "perm");
+  NEED_PTR(pos, "pos");
+  hipStream_t s = (hipStream_t)stream;
+  const int pid = prof_begin("bucket", s);
+  hipError_t e = launch_bucket(idx, T, k, E, counts, offsets, perm, pos, nullptr, 1, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+static DecodeLaunch decode_launch(const moe_layer* L, const void* x, int x_dtype, int T) {
+  DecodeLaunch D{};
+  D.E = L->n_experts;
+  D.d = L->d_model;
+  D.f = L->d_ff;
+  D.k = L->top_k;
+  D.T = T;
+  D.fmt_gate_up = L->fmt_gate_up;
+  D.fmt_down = L->fmt_down;
+  D.fmt_shared = L->fmt_shared;
+  D.has_shared = L->has_shared;
+  D.w_gate = L->w_gate;
+  D.w_up = L->w_up;
+  D.w_down = L->w_down;
+  D.s_gate = L->s_gate;
+  D.s_up = L->s_up;
+  D.s_down = L->s_down;
+  D.grid = L->iq2_grid;
+  D.w_router = L->w_router;
+  D.x = x;
+  D.x_dtype = x_dtype;
+  return D;
+}
+
+static PrefillLaunch prefill_launch(const moe_layer* L, const void* x, int x_dtype, int T) {
+  PrefillLaunch P{};
+  P.E = L->n_experts;
+  P.d = L->d_model;
+  P.f = L->d_ff;
+  P.k = L->top_k;
+  P.T = T;
+  P.fmt_gate_up = L->fmt_gate_up;
+  P.fmt_down = L->fmt_down;
+  P.fmt_shared = L->fmt_shared;
+  P.has_shared = L->has_shared;
+  P.w_gate = L->w_gate;
+  P.w_up = L->w_up;
+  P.w_down = L->w_down;
+  P.s_gate = L->s_gate;
+  P.s_up = L->s_up;
+  P.s_down = L->s_down;
+  P.grid = L->iq2_grid;
+  P.x = x;
+  P.x_dtype = x_dtype;
+  return P;
+}
+
+// bucketing + grouped GEMMs + combine for routes already in device memory
+static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_dtype, int T, const int32_t* idx,
+                       const float* wt, float* y, int32_t* bucket_out, Carve& c, hipStream_t s) {
+  const int E = L->n_experts, k = L->top_k;
+  PrefillWs w;
+  carve_prefill(c, w, E, T, k, L->d_model, L->d_ff, L->has_shared, bucket_out != nullptr);
+  if (bucket_out) {
+    w.counts = bucket_out;
+    w.offsets = bucket_out + E;
+    w.perm = bucket_out + 2 * E + 1;
+  }
+  PrefillLaunch P = prefill_launch(L, x, x_dtype, T);
+  P.counts = w.counts;
+  P.offsets = w.offsets;
+  P.tile_start = w.tile_start;
+  P.perm = w.perm;
+  P.pos = w.pos;
+  P.wt = wt;
+  P.H = w.H;
+  P.Hs = w.Hs;
+  P.Ye = w.Ye;
+  P.Ysh = w.Ysh;
+  P.y = y;
+  const int tile_m = x_dtype == MOE_BF16 ? PREFILL_BM : PREFILL_BM_SPLIT;
+  int pid = prof_begin("bucket", s);
+  hipError_t e = launch_bucket(idx, T, k, E, w.counts, w.offsets, w.perm, w.pos, w.tile_start, tile_m, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  e = launch_prefill_gemms(P, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+extern "C" int moe_expert_ffn_decode(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, const int32_t* idx,
+                                     const float* wt, float* y, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_expert_ffn_decode";
+  int rc = check_layer(fn, L, false);
+  if (rc) return rc;
+  if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
+  if (T > DECODE_MAX_T) return fail(MOE_ERR_INVALID_ARG, "%s: T %d above the decode limit %d", fn, T, DECODE_MAX_T);
+  if (T == 0) return ok();
+  NEED_PTR(x, "x");
+  NEED_PTR(idx, "idx");
+  NEED_PTR(wt, "wt");
+  NEED_PTR(y, "y");
+  NEED_PTR(ws, "workspace");
+  const size_t need = ws_decode(T, L->top_k, L->d_ff);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  Carve c;
+  c.base = (uint8_t*)ws;
+  DecodeWs w;
+  carve_decode(c, w, T, L->top_k, L->d_ff);
+  DecodeLaunch D = decode_launch(L, x, x_dtype, T);
+  D.idx = const_cast<int32_t*>(idx);
+  D.wt = const_cast<float*>(wt);
+  D.h = w.h;
+  D.y = y;
+  D.fused_topk = 0;
+  hipError_t e = launch_decode(D, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+extern "C" int moe_expert_ffn_prefill(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T,
+                                      const int32_t* idx, const float* wt, float* y, int32_t* bucket_out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const char* fn = "moe_expert_ffn_prefill";
+  int rc = check_layer(fn, L, false);
+  if (rc) return rc;
+  if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
+  if (T == 0) return ok();
+  NEED_PTR(x, "x");
+  NEED_PTR(idx, "idx");
+  NEED_PTR(wt, "wt");
+  NEED_PTR(y, "y");
+  NEED_PTR(ws, "workspace");
+  if (bucket_out && ((uintptr_t)bucket_out & 3u)) return fail(MOE_ERR_INVALID_ARG, "%s: bucket_out misaligned", fn);
+  const size_t need = ws_prefill(L->n_experts, T, L->top_k, L->d_model, L->d_ff, L->has_shared);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  Carve c;
+  c.base = (uint8_t*)ws;
+  return run_prefill(fn, L, x, x_dtype, T, idx, wt, y, bucket_out, c, (hipStream_t)stream);
+}
+
+extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,
+                                 int32_t* idx_out, float* wt_out, int32_t path, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  const char* fn = "moe_layer_forward";
+  int rc = check_layer(fn, L, true);
+  if (rc) return rc;
+  if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
+  if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
+  const int p = resolve_path(path, T);
+  if (p == MOE_PATH_DECODE && T > DECODE_MAX_T)
+    return fail(MOE_ERR_INVALID_ARG, "%s: T %d above the decode limit %d", fn, T, DECODE_MAX_T);
+  if (T == 0) return ok();
+  NEED_PTR(x, "x");
+  NEED_PTR(y, "y");
+  NEED_PTR(ws, "workspace");
+  if (idx_out && !aligned16(idx_out)) return fail(MOE_ERR_INVALID_ARG, "%s: idx_out is not 16-byte aligned", fn);
+  if (wt_out && !aligned16(wt_out)) return fail(MOE_ERR_INVALID_ARG, "%s: wt_out is not 16-byte aligned", fn);
+  const int E = L->n_experts, k = L->top_k;
+  const size_t need = ws_layer(E, T, k, L->d_model, L->d_ff, L->has_shared, p);
+  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  Carve c;
+  c.base = (uint8_t*)ws;
+  LayerWs lw;
+  carve_layer_routes(c, lw, E, T, k);
+  hipStream_t s = (hipStream_t)stream;
+  if (p == MOE_PATH_DECODE) {
+    DecodeWs w;
+    carve_decode(c, w, T, k, L->d_ff);
+    DecodeLaunch D = decode_launch(L, x, x_dtype, T);
+    D.z = lw.z;
+    D.idx = lw.idx;
+    D.wt = lw.wt;
+    D.idx_out = idx_out;
+    D.wt_out = wt_out;
+    D.h = w.h;
+    D.y = y;
+    D.fused_topk = 1;
+    hipError_t e = launch_decode(D, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ok();
+  }
+  int pid = prof_begin(T <= ROUTER_ROWS_MAX_T ? "router_rows" : "router_tiled", s);
+  hipError_t e = launch_router(L->w_router, E, L->d_model, x, x_dtype, T, lw.z, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  pid = prof_begin("topk", s);
+  e = launch_topk(lw.z, T, E, k, lw.idx, lw.wt, idx_out, wt_out, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return run_prefill(fn, L, x, x_dtype, T, lw.idx, lw.wt, y, nullptr, c, s);
+}

@@ -1,0 +1,83 @@
+// Internal definitions shared by the HIP kernels and the host API of libqmoe.
+// (Not shared with the CPU oracle, which restates everything independently.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+enum : int { X_F32 = 0, X_BF16 = 1 };
+enum : int { FMT_IQ2 = 1, FMT_Q2K = 2, FMT_Q8 = 3 };
+
+// Weights per block and bytes per block of each format (canonical layout).
+__host__ __device__ constexpr int block_weights(int fmt) { return fmt == FMT_Q8 ? 32 : 256; }
+__host__ __device__ constexpr int block_bytes(int fmt) { return fmt == FMT_IQ2 ? 66 : fmt == FMT_Q2K ? 84 : 34; }
+
+// A weight tensor in the device layout: n_experts matrices of `rows` rows by
+// K inputs.  Planes (see include/moe.h):
+//   IQ2: p_scale = fp16 d[R][nb],            p_a = payload[R][nb][64]
+//   Q2K: p_scale = {fp16 d, dmin}[R][nb],    p_a = scale bytes[R][nb][16],
+//        p_b = quants[R][nb][64]
+//   Q8 : p_scale = fp16 d[R][nb],            p_a = int8 q[R][nb][32]
+struct QMat {
+  const uint8_t* p_scale;
+  const uint8_t* p_a;
+  const uint8_t* p_b;
+  int fmt;
+  int rows;  // rows per expert
+  int K;     // inputs per row
+  int nb;    // blocks per row
+};
+
+inline QMat make_qmat(const void* base, int fmt, int n_experts, int rows, int K) {
+  QMat m;
+  const uint8_t* b = static_cast<const uint8_t*>(base);
+  int64_t nb = K / block_weights(fmt);
+  int64_t R = (int64_t)n_experts * rows;
+  m.fmt = fmt;
+  m.rows = rows;
+  m.K = K;
+  m.nb = (int)nb;
+  m.p_scale = b;
+  if (fmt == FMT_IQ2) {
+    m.p_a = b + R * nb * 2;
+    m.p_b = nullptr;
+  } else if (fmt == FMT_Q2K) {
+    m.p_a = b + R * nb * 4;
+    m.p_b = b + R * nb * 20;
+  } else {
+    m.p_a = b + R * nb * 2;
+    m.p_b = nullptr;
+  }
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Load 16 bytes (as 4 dwords) with a plain vector load.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Non-temporal 16-byte load for weights that are streamed exactly once.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace qmoe

@@ -1,0 +1,76 @@
+// Launchers of the HIP kernels (host side), used by the C-ABI layer api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace qmoe {
+
+// Limits (mirrored by the validation in api.cpp and documented in moe.h).
+constexpr int MAX_EXPERTS = 1024;
+constexpr int TOPK_MAX_K = 16;
+constexpr int TOPK_MAX_PER_LANE = MAX_EXPERTS / 64;
+constexpr int ROUTER_ROWS_MAX_T = 16;  // above this the tiled router runs
+constexpr int DECODE_MAX_T = 8;
+
+// Per-kernel timing hooks (api.hip): HIP events recorded on the launch
+// stream around one launch when profiling is enabled; no-ops otherwise.
+int prof_begin(const char* name, hipStream_t s);
+void prof_end(int id, hipStream_t s);
+
+// route.hip
+hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtype, int T, float* z, hipStream_t s);
+hipError_t launch_topk(const float* z, int T, int E, int k, int32_t* idx, float* wt, int32_t* idx2, float* wt2,
+                       hipStream_t s);
+
+// bucket.hip.  tile_start (nullable): [E+1] exclusive prefix of
+// ceil(counts[e] / tile_m) -- the M-tile schedule of the grouped GEMMs.
+hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* pos, int32_t* tile_start, int tile_m, hipStream_t s);
+
+// decode.hip: the three decode launches of one layer (or of given routes).
+struct DecodeLaunch {
+  int E, d, f, k, T;
+  int fmt_gate_up, fmt_down, fmt_shared, has_shared;
+  const void *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down;
+  const uint8_t* grid;
+  const float* w_router;   // used when fused_topk
+  const void* x;
+  int x_dtype;
+  float* z;                // [T][E] workspace (fused_topk)
+  int32_t* idx;            // [T][k] routes: written (fused_topk) or read
+  float* wt;               // [T][k]
+  int32_t* idx_out;        // nullable copies for the caller (fused_topk)
+  float* wt_out;
+  float* h;                // [T*k + T][f] workspace
+  float* y;                // [T][d]
+  int fused_topk;          // 1: run the router in K1 and top-k in K2
+};
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
+
+// prefill.hip: grouped GEMMs + combine (bucketing already done).
+constexpr int PREFILL_BM = 64;        // M tile (bf16 activations)
+constexpr int PREFILL_BM_SPLIT = 32;  // M tile when fp32 activations are split in two
+struct PrefillLaunch {
+  int E, d, f, k, T;
+  int fmt_gate_up, fmt_down, fmt_shared, has_shared;
+  const void *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down;
+  const uint8_t* grid;
+  const void* x;
+  int x_dtype;
+  const int32_t *counts, *offsets, *tile_start, *perm, *pos;
+  const float* wt;
+  void* H;      // fp16 [T*k][f]
+  void* Hs;     // fp16 [T][f]
+  float* Ye;    // [T*k][d]
+  float* Ysh;   // [T][d]
+  float* y;     // [T][d]
+};
+hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s);
+
+// repack.hip
+hipError_t launch_repack(int fmt, int64_t n_blocks, const void* src, void* dst, int to_device, hipStream_t s);
+
+}  // namespace qmoe

@@ -1,0 +1,260 @@
+"""Thin Python binding of libqmoe (C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch tensors on the GPU; PyTorch supplies device memory and the
+current stream.  If the library is not built this module raises on load --
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+MOE_ABI_VERSION = 1
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_FMT_NONE, MOE_FMT_IQ2XXS_L, MOE_FMT_Q2K_L, MOE_FMT_Q8_0_L = 0, 1, 2, 3
+MOE_LAYOUT_CANONICAL, MOE_LAYOUT_DEVICE = 0, 1
+MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_LAYER = 0, 1, 2, 3
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_DECODE_MAX_T = 8
+MOE_REPACK_TO_DEVICE, MOE_REPACK_TO_CANONICAL = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_WORKSPACE",
+           -4: "MOE_ERR_HIP"}
+
+
+class MoeLayer(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32),
+        ("n_experts", ctypes.c_int32),
+        ("d_model", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("fmt_gate_up", ctypes.c_int32),
+        ("fmt_down", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("w_gate", ctypes.c_void_p),
+        ("w_up", ctypes.c_void_p),
+        ("w_down", ctypes.c_void_p),
+        ("iq2_grid", ctypes.c_void_p),
+        ("w_router", ctypes.c_void_p),
+        ("has_shared", ctypes.c_int32),
+        ("fmt_shared", ctypes.c_int32),
+        ("s_gate", ctypes.c_void_p),
+        ("s_up", ctypes.c_void_p),
+        ("s_down", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_P, _I32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_abi_version": ([], ctypes.c_int),
+            "moe_last_error": ([], ctypes.c_char_p),
+            "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "moe_matrix_bytes": ([_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+            "moe_workspace_bytes": ([ctypes.POINTER(MoeLayer), _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
+            "moe_repack": ([_I32, _I32, _I32, _I32, _P, _P, _I32, _P], ctypes.c_int),
+            "moe_route_topk": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "moe_bucket": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
+            "moe_expert_ffn_decode": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
+                                      ctypes.c_int),
+            "moe_expert_ffn_prefill": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P],
+                                       ctypes.c_int),
+            "moe_layer_forward": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _I32, _P, _SZ, _P],
+                                  ctypes.c_int),
+            "moe_profile_enable": ([_I32], ctypes.c_int),
+            "moe_profile_reset": ([], ctypes.c_int),
+            "moe_profile_collect": ([_I32, _P, _P, _P, _P], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def x_dtype_of(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, not {x.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI, minus the moe_ prefix)
+# ---------------------------------------------------------------------------
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def matrix_bytes(fmt: int, n_experts: int, rows: int, K: int) -> int:
+    out = _SZ()
+    _check(lib().moe_matrix_bytes(fmt, n_experts, rows, K, ctypes.byref(out)))
+    return out.value
+
+
+def workspace_bytes(layer: MoeLayer, T: int, op: int) -> int:
+    out = _SZ()
+    _check(lib().moe_workspace_bytes(ctypes.byref(layer), T, op, ctypes.byref(out)))
+    return out.value
+
+
+def repack(fmt, n_experts, rows, K, src: torch.Tensor, dst: torch.Tensor, direction=MOE_REPACK_TO_DEVICE,
+           stream=None) -> None:
+    _check(lib().moe_repack(fmt, n_experts, rows, K, _ptr(src), _ptr(dst), direction, _stream(stream)))
+
+
+def route_topk(w_router, x, k, idx, wt, ws, stream=None) -> None:
+    E, d = w_router.shape
+    _check(lib().moe_route_topk(_ptr(w_router), E, d, _ptr(x), x_dtype_of(x), x.shape[0], k, _ptr(idx), _ptr(wt),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bucket(idx, E, counts, offsets, perm, pos, stream=None) -> None:
+    T, k = idx.shape
+    _check(lib().moe_bucket(_ptr(idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(pos),
+                            _stream(stream)))
+
+
+def expert_ffn_decode(layer: MoeLayer, x, idx, wt, y, ws, stream=None) -> None:
+    _check(lib().moe_expert_ffn_decode(ctypes.byref(layer), _ptr(x), x_dtype_of(x), x.shape[0], _ptr(idx), _ptr(wt),
+                                       _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def expert_ffn_prefill(layer: MoeLayer, x, idx, wt, y, ws, bucket_out=None, stream=None) -> None:
+    _check(lib().moe_expert_ffn_prefill(ctypes.byref(layer), _ptr(x), x_dtype_of(x), x.shape[0], _ptr(idx),
+                                        _ptr(wt), _ptr(y), _ptr(bucket_out), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_forward(layer: MoeLayer, x, y, ws, idx_out=None, wt_out=None, path=MOE_PATH_AUTO, stream=None) -> None:
+    _check(lib().moe_layer_forward(ctypes.byref(layer), _ptr(x), x_dtype_of(x), x.shape[0], _ptr(y), _ptr(idx_out),
+                                   _ptr(wt_out), path, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def profile_enable(on: bool) -> None:
+    _check(lib().moe_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    _check(lib().moe_profile_reset())
+
+
+def profile_collect(max_kernels: int = 32) -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded so far."""
+    names = ctypes.create_string_buffer(48 * max_kernels)
+    launches = (ctypes.c_int64 * max_kernels)()
+    ms = (ctypes.c_double * max_kernels)()
+    n = ctypes.c_int32()
+    _check(lib().moe_profile_collect(max_kernels, ctypes.addressof(names), ctypes.addressof(launches),
+                                     ctypes.addressof(ms), ctypes.addressof(n)))
+    out = {}
+    for i in range(n.value):
+        name = names.raw[48 * i:48 * (i + 1)].split(b"\0", 1)[0].decode()
+        out[name] = (launches[i], ms[i])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# device-resident layer (memory management for callers and tests)
+# ---------------------------------------------------------------------------
+def _to_device_bytes(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1)).to(device)
+
+
+class DeviceLayer:
+    """A layer whose weights live on the GPU in the device layout.
+
+    Built from canonical bytes (host numpy arrays): each tensor is uploaded
+    and converted with moe_repack.  `.desc` is the moe_layer descriptor.
+    """
+
+    def __init__(self, E, d, f, k, fmt_gate_up, fmt_down, w_gate, w_up, w_down, grid, w_router,
+                 fmt_shared=MOE_FMT_NONE, s_gate=None, s_up=None, s_down=None, device="cuda"):
+        self.E, self.d, self.f, self.k = E, d, f, k
+        self.device = torch.device(device)
+        self.tensors = {}
+        self.tensors["w_gate"] = self._prep(fmt_gate_up, E, f, d, w_gate)
+        self.tensors["w_up"] = self._prep(fmt_gate_up, E, f, d, w_up)
+        self.tensors["w_down"] = self._prep(fmt_down, E, d, f, w_down)
+        self.tensors["grid"] = _to_device_bytes(np.asarray(grid, np.uint8), self.device)
+        self.tensors["w_router"] = torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.device)
+        has_shared = s_gate is not None
+        if has_shared:
+            self.tensors["s_gate"] = self._prep(fmt_shared, 1, f, d, s_gate)
+            self.tensors["s_up"] = self._prep(fmt_shared, 1, f, d, s_up)
+            self.tensors["s_down"] = self._prep(fmt_shared, 1, d, f, s_down)
+        t = self.tensors
+        self.desc = MoeLayer(
+            abi_version=MOE_ABI_VERSION, n_experts=E, d_model=d, d_ff=f, top_k=k, fmt_gate_up=fmt_gate_up,
+            fmt_down=fmt_down, layout=MOE_LAYOUT_DEVICE, w_gate=_ptr(t["w_gate"]), w_up=_ptr(t["w_up"]),
+            w_down=_ptr(t["w_down"]), iq2_grid=_ptr(t["grid"]), w_router=_ptr(t["w_router"]),
+            has_shared=1 if has_shared else 0, fmt_shared=fmt_shared if has_shared else 0,
+            s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")))
+        torch.cuda.synchronize(self.device)
+
+    def _prep(self, fmt, E, rows, K, canonical: np.ndarray) -> torch.Tensor:
+        n = matrix_bytes(fmt, E, rows, K)
+        if canonical.size != n:
+            raise ValueError(f"expected {n} bytes, got {canonical.size}")
+        src = _to_device_bytes(canonical, self.device)
+        dst = torch.empty(n, dtype=torch.uint8, device=self.device)
+        repack(fmt, E, rows, K, src, dst, MOE_REPACK_TO_DEVICE)
+        return dst
+
+    @classmethod
+    def from_synth(cls, L, device="cuda"):
+        """From a quantized_moe_amd.synth.Layer (canonical bytes)."""
+        s = L.spec
+        return cls(s.E, s.d, s.f, s.k, s.fmt_gate_up, s.fmt_down, L.w_gate, L.w_up, L.w_down, L.grid, L.w_router,
+                   fmt_shared=s.fmt_shared if s.has_shared else MOE_FMT_NONE, s_gate=L.s_gate, s_up=L.s_up,
+                   s_down=L.s_down, device=device)
+
+    def workspace(self, T: int, op: int = MOE_OP_LAYER) -> torch.Tensor:
+        n = workspace_bytes(self.desc, T, op)
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)

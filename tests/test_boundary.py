@@ -1,0 +1,160 @@
+"""The C-ABI boundary on the CPU: symbols, sizes and argument validation.
+
+Every call here is rejected by host-side validation (or is a T = 0 no-op)
+before any HIP call, so these run without a GPU.  The fake pointers are never
+dereferenced; no call in this file may pass validation with them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_amd import lib, synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = lib.lib()
+    names = _declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    for required in ["moe_route_topk", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward"]:
+        assert required in names
+
+
+def test_abi_and_status_strings():
+    assert lib.abi_version() == lib.MOE_ABI_VERSION
+    L = lib.lib()
+    for code, name in [(0, b"MOE_OK"), (-1, b"MOE_ERR_INVALID_ARG"), (-2, b"MOE_ERR_UNSUPPORTED"),
+                       (-3, b"MOE_ERR_WORKSPACE"), (-4, b"MOE_ERR_HIP")]:
+        assert L.moe_status_string(code) == name
+
+
+@pytest.mark.parametrize("fmt,E,rows,K", [(1, 384, 2048, 4096), (2, 384, 4096, 2048), (3, 1, 2048, 4096),
+                                          (2, 8, 512, 256)])
+def test_matrix_bytes_matches_format_sizes(fmt, E, rows, K):
+    assert lib.matrix_bytes(fmt, E, rows, K) == synth.matrix_bytes(fmt, E, rows, K)
+
+
+def test_matrix_bytes_of_the_decode_layer():
+    # 2,162,688 B per IQ2 matrix, 2,752,512 B per Q2K matrix, 8,912,896 per Q8 matrix
+    assert lib.matrix_bytes(1, 1, 2048, 4096) == 2162688
+    assert lib.matrix_bytes(2, 1, 4096, 2048) == 2752512
+    assert lib.matrix_bytes(3, 1, 2048, 4096) == 8912896
+
+
+def _layer(**over):
+    fields = dict(abi_version=lib.MOE_ABI_VERSION, n_experts=384, d_model=4096, d_ff=2048, top_k=6,
+                  fmt_gate_up=1, fmt_down=2, layout=lib.MOE_LAYOUT_DEVICE, w_gate=256, w_up=512, w_down=768,
+                  iq2_grid=1024, w_router=1280, has_shared=1, fmt_shared=3, s_gate=1536, s_up=1792, s_down=2048)
+    fields.update(over)
+    return lib.MoeLayer(**fields)
+
+
+def _ffn_decode(layer, T=1, x=4096, idx=4352, wt=4608, y=4864, ws=5120, ws_bytes=0):
+    L = lib.lib()
+    return L.moe_expert_ffn_decode(ctypes.byref(layer), x, lib.MOE_F32, T, idx, wt, y, ws, ws_bytes, None)
+
+
+def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
+    L = lib.lib()
+    return L.moe_layer_forward(ctypes.byref(layer), x, dtype, T, y, None, None, path, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(abi_version=2), lib.MOE_ERR_UNSUPPORTED),
+    (dict(layout=lib.MOE_LAYOUT_CANONICAL), lib.MOE_ERR_UNSUPPORTED),
+    (dict(layout=7), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_gate_up=9), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_down=0), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_shared=4), lib.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=0), lib.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=1025), lib.MOE_ERR_INVALID_ARG),
+    (dict(d_model=4000), lib.MOE_ERR_INVALID_ARG),
+    (dict(d_model=128), lib.MOE_ERR_INVALID_ARG),
+    (dict(d_ff=16384), lib.MOE_ERR_INVALID_ARG),
+    (dict(top_k=0), lib.MOE_ERR_INVALID_ARG),
+    (dict(top_k=17), lib.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=4, top_k=5), lib.MOE_ERR_INVALID_ARG),
+    (dict(w_gate=0), lib.MOE_ERR_INVALID_ARG),
+    (dict(w_down=0x1008), lib.MOE_ERR_INVALID_ARG),       # misaligned
+    (dict(iq2_grid=0), lib.MOE_ERR_INVALID_ARG),          # IQ2 in use needs the grid
+    (dict(s_up=0), lib.MOE_ERR_INVALID_ARG),
+    (dict(has_shared=2), lib.MOE_ERR_INVALID_ARG),
+])
+def test_layer_validation(over, code):
+    assert _ffn_decode(_layer(**over)) == code
+    assert lib.last_error() != ""
+
+
+def test_grid_not_needed_without_iq2_and_shared_optional():
+    layer = _layer(fmt_gate_up=2, iq2_grid=0, has_shared=0, s_gate=0, s_up=0, s_down=0)
+    # gets past layer validation; fails on the (deliberately) empty workspace
+    assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE
+
+
+def test_router_needed_only_by_the_whole_layer():
+    layer = _layer(w_router=0)
+    assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE
+    assert _forward(layer) == lib.MOE_ERR_INVALID_ARG
+
+
+def test_T_limits_and_noop():
+    layer = _layer()
+    assert _ffn_decode(layer, T=-1) == lib.MOE_ERR_INVALID_ARG
+    assert _ffn_decode(layer, T=9) == lib.MOE_ERR_INVALID_ARG            # decode path holds T <= 8
+    assert _forward(layer, T=9, path=lib.MOE_PATH_DECODE) == lib.MOE_ERR_INVALID_ARG
+    assert _forward(layer, T=65537) == lib.MOE_ERR_INVALID_ARG
+    assert _forward(layer, T=0, x=0, y=0, ws=0) == lib.MOE_OK            # T = 0: nothing to do
+    assert _forward(layer, path=5) == lib.MOE_ERR_INVALID_ARG
+    assert _forward(layer, dtype=2) == lib.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_too_small_is_rejected_before_launch():
+    layer = _layer()
+    assert _forward(layer, T=1, ws_bytes=16) == lib.MOE_ERR_WORKSPACE
+    assert _forward(layer, T=1024, ws_bytes=1 << 20) == lib.MOE_ERR_WORKSPACE
+    assert "need" in lib.last_error()
+
+
+def test_workspace_sizes_cover_their_buffers():
+    layer = _layer()
+    E, d, f, k = 384, 4096, 2048, 6
+    assert lib.workspace_bytes(layer, 1, lib.MOE_OP_ROUTE) >= E * 4
+    # decode: hidden activations of k routed + 1 shared expert per token
+    assert lib.workspace_bytes(layer, 8, lib.MOE_OP_DECODE) >= (8 * k + 8) * f * 4
+    # prefill: fp16 H [T*k][f] + fp32 Ye [T*k][d] + shared H/Y + routing buffers
+    T = 1024
+    need = T * k * f * 2 + T * k * d * 4 + T * f * 2 + T * d * 4 + (3 * E + 2 * T * k) * 4
+    assert lib.workspace_bytes(layer, T, lib.MOE_OP_PREFILL) >= need
+    assert lib.workspace_bytes(layer, T, lib.MOE_OP_LAYER) >= lib.workspace_bytes(layer, T, lib.MOE_OP_PREFILL)
+    assert lib.workspace_bytes(layer, 1, lib.MOE_OP_LAYER) >= lib.workspace_bytes(layer, 1, lib.MOE_OP_DECODE)
+
+
+def test_route_and_bucket_validation():
+    L = lib.lib()
+    assert L.moe_route_topk(256, 384, 4096, 512, 0, 1, 0, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(256, 2000, 4096, 512, 0, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(256, 384, 4096, 512, 0, 1, 6, 768, 1024, 1280, 0, None) == lib.MOE_ERR_WORKSPACE
+    assert L.moe_route_topk(256, 384, 4096, 512, 3, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_bucket(256, 4, 6, 384, 0, 512, 768, 1024, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bucket(256, 4, 0, 384, 256, 512, 768, 1024, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_bucket(0, 0, 6, 384, 0, 0, 0, 0, None) == lib.MOE_OK
+
+
+def test_repack_validation():
+    L = lib.lib()
+    assert L.moe_repack(5, 1, 16, 256, 256, 512, 0, None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_repack(1, 1, 16, 100, 256, 512, 0, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_repack(1, 1, 16, 256, 256, 256, 0, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_repack(1, 1, 16, 256, 256, 512, 3, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_repack(3, 1, 16, 32, 0, 512, 0, None) == lib.MOE_ERR_INVALID_ARG

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Bar: expert indices and buckets bit-exact; routing weights within 1e-6;
+layer outputs within 1e-3 relative L2 (fp32 accumulation; the oracle
+accumulates in fp64).  Full-size workloads are checked on sampled tokens the
+oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_amd import lib, synth
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+WT_TOL = 1e-6
+DEV = torch.device("cuda:0")
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def to_dev_x(x, dt):
+    if dt == synth.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+
+
+def run_layer(dl, x, dt, path):
+    T = x.shape[0]
+    xt = to_dev_x(x, dt)
+    y = torch.empty(T, dl.d, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, dl.k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T, dl.k, dtype=torch.float32, device=DEV)
+    lib.layer_forward(dl.desc, xt, y, dl.workspace(T), idx_out=idx, wt_out=wt, path=path)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), wt.cpu().numpy()
+
+
+def run_ffn(dl, x, dt, idx, wt, path, bucket=False):
+    T = x.shape[0]
+    xt = to_dev_x(x, dt)
+    it = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
+    wt_ = torch.from_numpy(np.ascontiguousarray(wt, np.float32)).to(DEV)
+    y = torch.empty(T, dl.d, dtype=torch.float32, device=DEV)
+    if path == lib.MOE_PATH_DECODE:
+        lib.expert_ffn_decode(dl.desc, xt, it, wt_, y, dl.workspace(T, lib.MOE_OP_DECODE))
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+    bo = torch.empty(2 * dl.E + 1 + T * dl.k, dtype=torch.int32, device=DEV) if bucket else None
+    lib.expert_ffn_prefill(dl.desc, xt, it, wt_, y, dl.workspace(T, lib.MOE_OP_PREFILL), bucket_out=bo)
+    torch.cuda.synchronize()
+    return (y.cpu().numpy(), bo.cpu().numpy()) if bucket else y.cpu().numpy()
+
+
+# --------------------------------------------------------------- tiny ----
+@pytest.mark.parametrize("path", [lib.MOE_PATH_DECODE, lib.MOE_PATH_PREFILL])
+def test_tiny_workload(path):
+    """E=8, k=2, d=256, f=512, T=4, fp32; Q2K weights quantized from N(0,0.02)."""
+    L = synth.tiny_layer(0)
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(0, ("tiny", "x"), 4, 256, synth.F32)
+    y, idx, wt = run_layer(dl, x, synth.F32, path)
+    y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+    assert np.array_equal(idx, idx_ref)
+    assert np.max(np.abs(wt - wt_ref)) <= WT_TOL
+    assert rel_l2(y, y_ref) <= REL_L2
+
+
+# ------------------------------------------------ format / shape matrix ----
+FORMAT_CASES = [
+    # (E, k, d, f, gate/up, down, shared fmt or None, T, dtype)
+    (16, 4, 256, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 3, synth.F32),
+    (16, 4, 256, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 37, synth.BF16),
+    (16, 4, 256, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 37, synth.F32),
+    (12, 3, 512, 256, synth.FMT_Q8, synth.FMT_IQ2, synth.FMT_Q2K, 5, synth.F32),
+    (12, 3, 512, 256, synth.FMT_Q8, synth.FMT_IQ2, synth.FMT_Q2K, 70, synth.BF16),
+    (10, 2, 1024, 256, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_IQ2, 8, synth.F32),
+    (10, 2, 1024, 256, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_IQ2, 65, synth.BF16),
+    (8, 1, 8192, 256, synth.FMT_IQ2, synth.FMT_Q2K, None, 2, synth.F32),      # two chunks per lane (d)
+    (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 2, synth.F32),  # two chunks per lane (f)
+    (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 20, synth.BF16),
+    (16, 16, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 4, synth.F32),  # k = E
+    (16, 16, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 33, synth.BF16),
+    (1000, 5, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 6, synth.F32),  # many experts
+    (1000, 5, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 90, synth.BF16),
+]
+
+
+@pytest.mark.parametrize("case", FORMAT_CASES, ids=lambda c: f"E{c[0]}k{c[1]}d{c[2]}f{c[3]}fmt{c[4]}{c[5]}"
+                         f"{c[6]}T{c[7]}{'bf16' if c[8] else 'f32'}")
+def test_layer_formats_and_shapes(case):
+    E, k, d, f, fgu, fdn, fsh, T, dt = case
+    spec = synth.scaled_spec(E=E, k=k, d=d, f=f, fmt_gate_up=fgu, fmt_down=fdn, has_shared=fsh is not None,
+                             fmt_shared=fsh or synth.FMT_Q8)
+    L = synth.random_layer(spec, seed=5, workload="shapes")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(5, ("shapes", "x", E, d, f, T), T, d, dt)
+    y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, dt)
+    paths = [lib.MOE_PATH_PREFILL] + ([lib.MOE_PATH_DECODE] if T <= lib.MOE_DECODE_MAX_T else [])
+    for path in paths:
+        y, idx, wt = run_layer(dl, x, dt, path)
+        assert np.array_equal(idx, idx_ref), path
+        assert np.max(np.abs(wt - wt_ref)) <= WT_TOL, path
+        assert rel_l2(y, y_ref) <= REL_L2, (path, rel_l2(y, y_ref))
+
+
+# ------------------------------------------------------------- routing ----
+def test_route_topk_ties_and_zero():
+    E, d, k = 64, 256, 6
+    rng = np.random.default_rng(3)
+    W = rng.normal(0, 0.02, (E, d)).astype(np.float32)
+    W[17] = W[5]          # duplicated rows: equal logits, lower index first
+    W[40] = W[5]
+    W[60] = 0.0           # z = +0 for every token
+    W[61] = -0.0 * W[61]  # z = +-0: ties with expert 60
+    x = rng.normal(0, 1, (9, d)).astype(np.float32)
+    x[3] = 0.0            # all logits equal (+0): experts 0..k-1
+    Wt = torch.from_numpy(W).to(DEV)
+    xt = torch.from_numpy(x).to(DEV)
+    idx = torch.empty(9, k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(9, k, dtype=torch.float32, device=DEV)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    lib.route_topk(Wt, xt, k, idx, wt, ws)
+    torch.cuda.synchronize()
+    _, idx_ref, wt_ref = oracle.route(x, oracle.F32, W, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert list(idx_ref[3]) == [0, 1, 2, 3, 4, 5]
+    assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
+
+
+@pytest.mark.parametrize("T,dt", [(1, synth.F32), (7, synth.BF16), (1024, synth.BF16), (300, synth.F32)])
+def test_route_topk_full_router(T, dt):
+    """384 experts x d=4096 router, both router kernels (T <= 16 and tiled)."""
+    W = synth.router_weights(0, ("decode", 0, "router"), 384, 4096)
+    x = synth.activations(0, ("route", T), T, 4096, dt)
+    idx = torch.empty(T, 6, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T, 6, dtype=torch.float32, device=DEV)
+    ws = torch.empty(T * 384 * 4 + 4096, dtype=torch.uint8, device=DEV)
+    lib.route_topk(torch.from_numpy(W).to(DEV), to_dev_x(x, dt), 6, idx, wt, ws)
+    torch.cuda.synchronize()
+    _, idx_ref, wt_ref = oracle.route(x, dt, W, 6)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 6, 384), (3, 2, 8), (1024, 6, 384), (4096, 6, 384), (50, 16, 17)])
+def test_bucket_bit_exact(T, k, E):
+    rng = np.random.default_rng(T + k + E)
+    if T == 4096:
+        idx, _ = synth.zipf_routes(0, T)
+    else:
+        idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    it = torch.from_numpy(idx).to(DEV)
+    outs = [torch.empty(n, dtype=torch.int32, device=DEV) for n in (E, E + 1, T * k, T * k)]
+    lib.bucket(it, E, *outs)
+    torch.cuda.synchronize()
+    for got, want in zip(outs, oracle.bucket(idx, E)):
+        assert np.array_equal(got.cpu().numpy(), want)
+
+
+# ------------------------------------------------------ full-size layers ----
+@pytest.fixture(scope="module")
+def decode_layer():
+    L = synth.random_layer(synth.DECODE_SPEC, seed=0, workload="decode")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    yield L, dl
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_decode_single_token_full_layer(decode_layer):
+    """384 experts, top-6, d=4096, f=2048, shared Q8 expert, T=1 fp32 (the decode workload)."""
+    L, dl = decode_layer
+    for i in range(3):
+        x = synth.activations(0, ("decode", "x", i), 1, 4096, synth.F32)
+        y, idx, wt = run_layer(dl, x, synth.F32, lib.MOE_PATH_AUTO)
+        y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+        assert np.array_equal(idx, idx_ref)
+        assert np.max(np.abs(wt - wt_ref)) <= WT_TOL
+        assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
+
+
+def test_prefill_chunk_full_layer(decode_layer):
+    """The decode layer with a 1024-token bf16 chunk (the prefill workload):
+    routes for all 1024 tokens bit-exact, outputs checked on sampled tokens."""
+    L, dl = decode_layer
+    T = 1024
+    x = synth.activations(0, ("prefill", "x"), T, 4096, synth.BF16)
+    y, idx, wt = run_layer(dl, x, synth.BF16, lib.MOE_PATH_AUTO)
+    _, idx_ref, wt_ref = oracle.route(x, oracle.BF16, L.w_router, 6)
+    assert np.array_equal(idx, idx_ref)
+    assert np.max(np.abs(wt - wt_ref)) <= WT_TOL
+    assert len(np.unique(idx)) > 370  # hash-like routing touches nearly every expert
+    tok = np.array([0, 1, 2, 511, 512, 1000, 1022, 1023] + list(range(100, 900, 50)))
+    y_ref = oracle.ffn(L, x, oracle.BF16, idx_ref, wt_ref, tokens=tok)
+    assert rel_l2(y[tok], y_ref) <= REL_L2, rel_l2(y[tok], y_ref)
+
+
+def test_small_batch_both_paths(decode_layer):
+    """16 tokens of 4 interleaved sessions with expert reuse, fp32, caller routes."""
+    L, dl = decode_layer
+    idx, wt = synth.session_routes(0)
+    x = synth.activations(0, ("small_batch", "x"), 16, 4096, synth.F32)
+    y_ref = oracle.ffn(L, x, oracle.F32, idx, wt)
+    y_pf = run_ffn(dl, x, synth.F32, idx, wt, lib.MOE_PATH_PREFILL)
+    assert rel_l2(y_pf, y_ref) <= REL_L2
+    y_dec = np.concatenate([run_ffn(dl, x[i:i + 8], synth.F32, idx[i:i + 8], wt[i:i + 8], lib.MOE_PATH_DECODE)
+                            for i in (0, 8)])
+    assert rel_l2(y_dec, y_ref) <= REL_L2
+
+
+def test_decode_batch_invariance(decode_layer):
+    """Decode rows of a batch equal separate single-row calls, bit for bit."""
+    L, dl = decode_layer
+    idx, wt = synth.session_routes(1, sessions=4, steps=1, tag="inv")
+    x = synth.activations(1, ("inv", "x"), 4, 4096, synth.F32)
+    y4 = run_ffn(dl, x, synth.F32, idx, wt, lib.MOE_PATH_DECODE)
+    for t in range(4):
+        y1 = run_ffn(dl, x[t:t + 1], synth.F32, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
+        assert np.array_equal(y1[0], y4[t])
+
+
+def test_determinism_and_graph_replay(decode_layer):
+    """Two eager runs are bitwise equal; a captured graph replays the same bits."""
+    L, dl = decode_layer
+    for T, dt in [(1, synth.F32), (256, synth.BF16)]:
+        x = to_dev_x(synth.activations(2, ("det", T), T, 4096, dt), dt)
+        ws = dl.workspace(T)
+        y = torch.empty(T, 4096, dtype=torch.float32, device=DEV)
+        lib.layer_forward(dl.desc, x, y, ws)
+        torch.cuda.synchronize()
+        y0 = y.clone()
+        y.zero_()
+        lib.layer_forward(dl.desc, x, y, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            lib.layer_forward(dl.desc, x, y, ws)
+        for _ in range(3):
+            y.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y0)
+
+
+def test_repack_round_trip(decode_layer):
+    L, dl = decode_layer
+    for name, fmt, E, rows, K, canon in [("w_gate", 1, 384, 2048, 4096, L.w_gate),
+                                         ("w_down", 2, 384, 4096, 2048, L.w_down),
+                                         ("s_up", 3, 1, 2048, 4096, L.s_up)]:
+        back = torch.empty_like(dl.tensors[name])
+        lib.repack(fmt, E, rows, K, dl.tensors[name], back, lib.MOE_REPACK_TO_CANONICAL)
+        torch.cuda.synchronize()
+        assert np.array_equal(back.cpu().numpy(), canon), name
+
+
+def test_long_prefill_eight_layers():
+    """8 layers of the decode shape, 4096 bf16 tokens, Zipf(1.1) routes (caller
+    supplied): buckets bit-exact, outputs on tokens of the lightest and the
+    heaviest experts and a spread of others.  One layer resident at a time."""
+    T = 4096
+    for layer in range(synth.LONG_PREFILL_LAYERS):
+        print(f"long_prefill layer {layer}", flush=True)
+        L = synth.random_layer(synth.DECODE_SPEC, seed=0, workload="long_prefill", layer=layer)
+        dl = lib.DeviceLayer.from_synth(L, DEV)
+        idx, wt = synth.zipf_routes(0, T, layer=layer)
+        x = synth.activations(0, ("long_prefill", "x", layer), T, 4096, synth.BF16)
+        y, bo = run_ffn(dl, x, synth.BF16, idx, wt, lib.MOE_PATH_PREFILL, bucket=True)
+        counts, offsets, perm, _ = oracle.bucket(idx, 384)
+        assert np.array_equal(bo[:384], counts)
+        assert np.array_equal(bo[384:769], offsets)
+        assert np.array_equal(bo[769:], perm)
+        light = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+        heavy = int(np.argmax(counts))
+        tl = np.nonzero((idx == light).any(axis=1))[0][:4]
+        th = np.nonzero((idx == heavy).any(axis=1))[0][[0, -1]]
+        tok = np.unique(np.concatenate([tl, th, np.arange(0, T, 1024), [T - 1]]))
+        y_ref = oracle.ffn(L, x, oracle.BF16, idx, wt, tokens=tok)
+        assert rel_l2(y[tok], y_ref) <= REL_L2, (layer, rel_l2(y[tok], y_ref))
+        del dl
+        torch.cuda.empty_cache()
