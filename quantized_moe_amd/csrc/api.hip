@@ -217,7 +217,7 @@ struct RouteWs {
   float* z;
 };
 struct DecodeWs {
-  float* h;
+  void* quant;
 };
 struct PrefillWs {
   int32_t *counts, *offsets, *tile_start, *perm, *pos;
@@ -231,7 +231,7 @@ struct LayerWs {
 };
 
 void carve_route(Carve& c, RouteWs& w, int E, int T) { w.z = (float*)c.take((size_t)T * E * 4); }
-void carve_decode(Carve& c, DecodeWs& w, int T, int k, int f) { w.h = (float*)c.take((size_t)(T * k + T) * f * 4); }
+void carve_decode(Carve& c, DecodeWs& w, int T, int k, int d, int f) { w.quant = c.take(decode_quant_bytes(T, k, d, f)); }
 void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, int has_shared, bool bucket_out) {
   const size_t n = (size_t)T * k;
   if (!bucket_out) {
@@ -263,10 +263,10 @@ size_t ws_route(int E, int T) {
   carve_route(c, w, E, T);
   return c.off;
 }
-size_t ws_decode(int T, int k, int f) {
+size_t ws_decode(int T, int k, int d, int f) {
   Carve c;
   DecodeWs w;
-  carve_decode(c, w, T, k, f);
+  carve_decode(c, w, T, k, d, f);
   return c.off;
 }
 size_t ws_prefill(int E, int T, int k, int d, int f, int sh) {
@@ -281,7 +281,7 @@ size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
   carve_layer_routes(c, lw, E, T, k);
   if (path == MOE_PATH_DECODE) {
     DecodeWs w;
-    carve_decode(c, w, T, k, f);
+    carve_decode(c, w, T, k, d, f);
   } else {
     PrefillWs w;
     carve_prefill(c, w, E, T, k, d, f, sh, false);
@@ -339,7 +339,7 @@ extern "C" int moe_workspace_bytes(const moe_layer* L, int32_t T, int32_t op, si
   if (!pow2_in(L->d_ff, 256, 8192)) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff %d is not a power of two in [256, 8192]", fn, L->d_ff);
   const int E = L->n_experts, d = L->d_model, f = L->d_ff, k = L->top_k, sh = L->has_shared ? 1 : 0;
   switch (op) {
-    case MOE_OP_DECODE: *bytes = ws_decode(T, k, f); break;
+    case MOE_OP_DECODE: *bytes = ws_decode(T, k, d, f); break;
     case MOE_OP_PREFILL: *bytes = ws_prefill(E, T, k, d, f, sh); break;
     case MOE_OP_LAYER: {
       size_t b = ws_layer(E, T, k, d, f, sh, MOE_PATH_PREFILL);
@@ -518,16 +518,16 @@ extern "C" int moe_expert_ffn_decode(const moe_layer* L, const void* x, int32_t 
   NEED_PTR(wt, "wt");
   NEED_PTR(y, "y");
   NEED_PTR(ws, "workspace");
-  const size_t need = ws_decode(T, L->top_k, L->d_ff);
+  const size_t need = ws_decode(T, L->top_k, L->d_model, L->d_ff);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   Carve c;
   c.base = (uint8_t*)ws;
   DecodeWs w;
-  carve_decode(c, w, T, L->top_k, L->d_ff);
+  carve_decode(c, w, T, L->top_k, L->d_model, L->d_ff);
   DecodeLaunch D = decode_launch(L, x, x_dtype, T);
   D.idx = const_cast<int32_t*>(idx);
   D.wt = const_cast<float*>(wt);
-  D.h = w.h;
+  D.quant = w.quant;
   D.y = y;
   D.fused_topk = 0;
   hipError_t e = launch_decode(D, (hipStream_t)stream);
@@ -584,14 +584,14 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
   hipStream_t s = (hipStream_t)stream;
   if (p == MOE_PATH_DECODE) {
     DecodeWs w;
-    carve_decode(c, w, T, k, L->d_ff);
+    carve_decode(c, w, T, k, L->d_model, L->d_ff);
     DecodeLaunch D = decode_launch(L, x, x_dtype, T);
     D.z = lw.z;
     D.idx = lw.idx;
     D.wt = lw.wt;
     D.idx_out = idx_out;
     D.wt_out = wt_out;
-    D.h = w.h;
+    D.quant = w.quant;
     D.y = y;
     D.fused_topk = 1;
     hipError_t e = launch_decode(D, s);

@@ -44,11 +44,12 @@ struct DecodeLaunch {
   float* wt;               // [T][k]
   int32_t* idx_out;        // nullable copies for the caller (fused_topk)
   float* wt_out;
-  float* h;                // [T*k + T][f] workspace
+  void* quant;             // decode_quant_bytes() of workspace: quantized x and h chunks
   float* y;                // [T][d]
   int fused_topk;          // 1: run the router in K1 and top-k in K2
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
+size_t decode_quant_bytes(int T, int k, int d, int f);
 
 // prefill.hip: grouped GEMMs + combine (bucketing already done).
 constexpr int PREFILL_BM = 64;        // M tile (bf16 activations)

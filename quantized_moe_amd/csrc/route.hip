@@ -144,21 +144,21 @@ hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtyp
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int T, int E, int k,
                                                    int32_t* __restrict__ idx, float* __restrict__ wt,
                                                    int32_t* __restrict__ idx2, float* __restrict__ wt2) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ int s_sel[4][TOPK_MAX_K];
+  __shared__ float s_z[4][TOPK_MAX_K];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  int sel[TOPK_MAX_K];
-  float zs[TOPK_MAX_K];
-  wave_topk(z + (int64_t)t * E, E, k, sel, zs);
-  if (lane == 0) {
+  wave_topk(z + (int64_t)t * E, E, k, s_sel[wave], s_z[wave]);
+  if (lane == 0) {  // lane 0 wrote the lists it reads back
     float w[TOPK_MAX_K];
-    topk_weights(zs, k, w);
+    topk_weights(s_z[wave], k, w);
 #pragma unroll
     for (int j = 0; j < TOPK_MAX_K; j++) {
       if (j >= k) continue;
-      idx[(int64_t)t * k + j] = sel[j];
+      idx[(int64_t)t * k + j] = s_sel[wave][j];
       wt[(int64_t)t * k + j] = w[j];
-      if (idx2) idx2[(int64_t)t * k + j] = sel[j];
+      if (idx2) idx2[(int64_t)t * k + j] = s_sel[wave][j];
       if (wt2) wt2[(int64_t)t * k + j] = w[j];
     }
   }

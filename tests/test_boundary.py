@@ -130,8 +130,9 @@ def test_workspace_sizes_cover_their_buffers():
     layer = _layer()
     E, d, f, k = 384, 4096, 2048, 6
     assert lib.workspace_bytes(layer, 1, lib.MOE_OP_ROUTE) >= E * 4
-    # decode: hidden activations of k routed + 1 shared expert per token
-    assert lib.workspace_bytes(layer, 8, lib.MOE_OP_DECODE) >= (8 * k + 8) * f * 4
+    # decode: quantized x chunks and quantized SwiGLU outputs of k routed + 1
+    # shared expert per token (128 bytes + one fp32 scale per 64 values)
+    assert lib.workspace_bytes(layer, 8, lib.MOE_OP_DECODE) >= 8 * (d // 64) * 132 + (8 * k + 8) * (f // 64) * 132
     # prefill: fp16 H [T*k][f] + fp32 Ye [T*k][d] + shared H/Y + routing buffers
     T = 1024
     need = T * k * f * 2 + T * k * d * 4 + T * f * 2 + T * d * 4 + (3 * E + 2 * T * k) * 4
