@@ -18,7 +18,8 @@ OUT = os.path.join(HERE, "libqmoe.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "route.hip", "bucket.hip", "repack.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "route.hip", "bucket.hip", "repack.hip", "decode.hip", "decode_k1.hip", "decode_k2.hip",
+           "decode_k3.hip", "prefill.hip"]
 # packed-fp32 VALU forms are disabled: only ordinary fp32 instructions
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
@@ -40,7 +41,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(9, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     cmd = ["hipcc", "-shared", "-o", tmp, f"--offload-arch={ARCH}"] + objs

@@ -586,7 +586,7 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
     DecodeWs w;
     carve_decode(c, w, T, k, L->d_model, L->d_ff);
     DecodeLaunch D = decode_launch(L, x, x_dtype, T);
-    D.z = lw.z;
+      D.z = lw.z;
     D.idx = lw.idx;
     D.wt = lw.wt;
     D.idx_out = idx_out;

@@ -30,7 +30,8 @@ hipError_t launch_topk(const float* z, int T, int E, int k, int32_t* idx, float*
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                          int32_t* pos, int32_t* tile_start, int tile_m, hipStream_t s);
 
-// decode.hip: the three decode launches of one layer (or of given routes).
+// decode.hip (+ decode_k1/k2/k3.hip): the three decode launches of one layer
+// (or of given routes).
 struct DecodeLaunch {
   int E, d, f, k, T;
   int fmt_gate_up, fmt_down, fmt_shared, has_shared;
@@ -44,9 +45,9 @@ struct DecodeLaunch {
   float* wt;               // [T][k]
   int32_t* idx_out;        // nullable copies for the caller (fused_topk)
   float* wt_out;
-  void* quant;             // decode_quant_bytes() of workspace: quantized x and h chunks
+  void* quant;             // decode_quant_bytes() of workspace: shared h, quantized h
   float* y;                // [T][d]
-  int fused_topk;          // 1: run the router in K1 and top-k in K2
+  int fused_topk;          // 1: router logits in the first launch, top-k in the second
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
 size_t decode_quant_bytes(int T, int k, int d, int f);

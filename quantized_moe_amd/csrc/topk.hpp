@@ -97,4 +97,16 @@ __device__ __forceinline__ void topk_weights(const float* zsel, int k, float* wt
     if (j < k) wt[j] = (float)(s[j] / sum);
 }
 
+// The same weights computed by a whole wave: lane j < k takes sigmoid(z_j)
+// in double precision, every lane sums s_0 .. s_{k-1} in rank order, and lane
+// j returns its w_j (lanes >= k return 0).  zsel is read by every lane.
+__device__ __forceinline__ float topk_weight_lane(const float* zsel, int k) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  if (lane < k) s = 1.0 / (1.0 + exp(-(double)zsel[lane]));
+  double sum = 0.0;
+  for (int j = 0; j < k; j++) sum += __shfl(s, j, 64);
+  return lane < k ? (float)(s / sum) : 0.0f;
+}
+
 }  // namespace qmoe
