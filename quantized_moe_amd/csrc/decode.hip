@@ -1,7 +1,7 @@
 // Decode path launcher: three launches per layer (or per set of given routes).
 //
-//   1. router logits (when routing is fused) and the shared expert's
-//      gate/up + SwiGLU;
+//   1. router logits (when routing is fused), x quantized for the routed
+//      gate/up, and the shared expert's gate/up + SwiGLU;
 //   2. exact top-k, routed gate/up + SwiGLU, routed and shared h quantized
 //      in groups of 16;
 //   3. routed and shared down projections and the fixed-order combine.
@@ -13,7 +13,7 @@
 
 namespace qmoe {
 namespace dec {
-hipError_t launch_k1(const DecodeArgs& a, const K1Plan& pl, int fmt_s, hipStream_t s);
+hipError_t launch_k1(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_layout, hipStream_t s);
 hipError_t launch_k2(const DecodeArgs& a, int fmt, int gcnt, int blocks, int down_layout, int shared_layout,
                      hipStream_t s);
 hipError_t launch_k3(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
@@ -26,13 +26,16 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecodeWsLayout {
-  size_t hsh, hq, hs, total;
+  size_t xq, xs, hsh, hq, hs, total;
 };
 
 DecodeWsLayout ws_layout(int T, int k, int d, int f) {
-  (void)d;
   DecodeWsLayout L;
   size_t off = 0;
+  L.xq = off;
+  off = align256(off + (size_t)T * (d / 64) * CHUNK_BYTES);
+  L.xs = off;
+  off = align256(off + (size_t)T * (d / 64) * 4);
   L.hsh = off;
   off = align256(off + (size_t)T * f * 4);
   L.hq = off;
@@ -92,6 +95,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.wt_out = L.wt_out;
   const DecodeWsLayout W = ws_layout(L.T, L.k, L.d, L.f);
   uint8_t* q = static_cast<uint8_t*>(L.quant);
+  a.xq = q + W.xq;
+  a.xs = reinterpret_cast<float*>(q + W.xs);
   a.hsh = reinterpret_cast<float*>(q + W.hsh);
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);
@@ -112,7 +117,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     nb = nb < 1 ? 1 : (nb > ncu ? ncu : nb);
     const double per_block = (double)total / (double)nb;
     pl.epb = (int)(per_block / (double)rb + 0.5);
-    pl.epb = pl.epb < 1 ? 1 : (pl.epb > WAVES ? WAVES : pl.epb);
+    pl.epb = pl.epb < 1 ? 1 : (pl.epb > WAVES - 1 ? WAVES - 1 : pl.epb);  // the last wave quantizes x
     pl.n_rb = (n_router + pl.epb - 1) / pl.epb;
     if (pl.n_steps > 0) {
       int64_t n_sb = nb - pl.n_rb;
@@ -123,10 +128,11 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
       pl.spb = 1;
       pl.n_sb = 0;
     }
+    pl.n_xb = pl.n_rb == 0 ? 1 : 0;  // x for the routed gate/up is quantized by a block of its own
   }
   {
     const int pid = prof_begin("decode_router_shared_gateup", s);
-    hipError_t e = launch_k1(a, pl, fs, s);
+    hipError_t e = launch_k1(a, pl, fs, nib_layout(L.fmt_gate_up), s);
     prof_end(pid, s);
     if (e != hipSuccess) return e;
   }

@@ -16,9 +16,9 @@
 //     Z = (X + 0x8888) ^ 0x8888, whose hex digits are the two's-complement
 //     nibbles of D_p.  The quantization error is at most s/2 = max|v|/61166
 //     per value: a relative error ~1e-5 on a dot product.
-//   * IQ2 weights come from one LDS table of 32768 dwords indexed by (grid
-//     row, 7 stored sign bits): the 8 signed magnitudes as nibbles, signs and
-//     parity already applied.  One ds_read_b32 per 8 weights.
+//   * IQ2 weights: the grid row's magnitudes and the stored signs come from
+//     two small LDS tables as nibbles u with w = 2u - 7, combined by one XOR
+//     (see Iq2Tab).
 //   * Q2K quants are already 2-bit integers: (W & 0x33333333) and
 //     ((W >> 2) & 0x33333333) are 8 nibble weights each.
 //   * Q8 weights use v_dot4 against the activation digit planes widened to
@@ -150,6 +150,130 @@ __device__ __forceinline__ void quant_wave(float v, int layout, uint8_t* __restr
   }
   if (lane < 32 && q < n_groups) reinterpret_cast<uint32_t*>(out)[lane] = word;
   if ((lane % GROUP) == 0 && lane / 16 < n_groups) scale_out[lane / GROUP] = m / (float)XMAX;
+}
+
+// Lane-parallel quantization: each lane turns 8 values (one half of a group
+// of 16, already in the nibble order of the layout) into its 4 plane words;
+// GL consecutive lanes share one scale (GL = 8: a chunk of 64, GL = 2: a
+// group of 16).  Returns the 4 words; *scale is the unit's scale.
+template <int GL>
+__device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
+  float m = 0.0f;
+#pragma unroll
+  for (int n = 0; n < 8; n++) m = fmaxf(m, fabsf(v[n]));
+  if constexpr (GL >= 2) m = fmaxf(m, dpp_f<0x111, 0xf>(m));
+  if constexpr (GL >= 4) m = fmaxf(m, dpp_f<0x112, 0xf>(m));
+  if constexpr (GL >= 8) m = fmaxf(m, dpp_f<0x114, 0xf>(m));
+  m = __shfl(m, (int)((threadIdx.x & 63) | (GL - 1)), 64);  // the unit's last lane holds its maximum
+  const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
+  scale = m / (float)XMAX;
+  uint32_t Z[8];
+#pragma unroll
+  for (int n = 0; n < 8; n++) Z[n] = to_digits(v[n], inv);
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; p++) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int n = 0; n < 8; n++) word |= ((Z[n] >> (4 * p)) & 15u) << (4 * n);
+    w[p] = word;
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The 8 values of half hh of the group of 16 starting at element e16 of an
+// fp32 vector, in the nibble order of `layout`.
+__device__ __forceinline__ void load_half_f32(const float* src, int64_t e16, int hh, int layout, float* v) {
+  if (layout == NIB_Q2K) {
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float4 f = *reinterpret_cast<const float4*>(src + e16 + 4 * i);
+      a[4 * i] = f.x;
+      a[4 * i + 1] = f.y;
+      a[4 * i + 2] = f.z;
+      a[4 * i + 3] = f.w;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; n++) v[n] = hh ? a[2 * n + 1] : a[2 * n];
+  } else {
+    const float4 f0 = *reinterpret_cast<const float4*>(src + e16 + 8 * hh);
+    const float4 f1 = *reinterpret_cast<const float4*>(src + e16 + 8 * hh + 4);
+    const float a[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+    for (int n = 0; n < 8; n++) v[n] = layout == NIB_Q8 ? a[(n & 1) ? 4 + (n >> 1) : (n >> 1)] : a[n];
+  }
+}
+
+__device__ __forceinline__ void load_half_bf16(const uint16_t* src, int64_t e16, int hh, int layout, float* v) {
+  const uint4 b0 = ld16(src + e16), b1 = ld16(src + e16 + 8);
+  const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  float a[16];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a[2 * i] = __uint_as_float(bw[i] << 16);
+    a[2 * i + 1] = __uint_as_float(bw[i] & 0xffff0000u);
+  }
+  // every index below is a compile-time constant (hh only selects), so a[]
+  // stays in registers
+#pragma unroll
+  for (int n = 0; n < 8; n++) {
+    const int q8 = (n & 1) ? 4 + (n >> 1) : (n >> 1);
+    const float q2k = hh ? a[2 * n + 1] : a[2 * n];
+    const float nq8 = hh ? a[8 + q8] : a[q8];
+    const float nat = hh ? a[8 + n] : a[n];
+    v[n] = layout == NIB_Q2K ? q2k : (layout == NIB_Q8 ? nq8 : nat);
+  }
+}
+
+// Quantize chunks [c0, c0 + 8) of 64 values of x (fp32 or bf16, nch chunks
+// in all, x taken as one flat vector) with one wave: lane L takes half L % 8
+// of chunk c0 + L / 8.  Chunk ch goes to q + 128 ch (groups of 32 bytes,
+// halves of 16), its scale to sc[ch].  load() only issues the loads.
+struct XOctet {
+  float v[8];
+  int ch, hg;
+  __device__ __forceinline__ void load(const void* x, int x_dtype, int nch, int c0, int layout) {
+    const int lane = threadIdx.x & 63;
+    ch = c0 + (lane >> 3);
+    hg = lane & 7;
+    const int chc = ch < nch ? ch : nch - 1;
+    if (x_dtype == X_BF16)
+      load_half_bf16(static_cast<const uint16_t*>(x), 64 * (int64_t)chc + 16 * (hg >> 1), hg & 1, layout, v);
+    else
+      load_half_f32(static_cast<const float*>(x), 64 * (int64_t)chc + 16 * (hg >> 1), hg & 1, layout, v);
+  }
+  __device__ __forceinline__ void store(int nch, uint8_t* q, float* sc) const {
+    float s;
+    const uint4 w = quant8<8>(v, s);
+    if (ch < nch) {
+      *reinterpret_cast<uint4*>(q + (int64_t)ch * CHUNK_BYTES + 16 * hg) = w;
+      if (hg == 0) sc[ch] = s;
+    }
+  }
+};
+
+__device__ __forceinline__ void quant_x8(const void* x, int x_dtype, int nch, int c0, int layout, uint8_t* q,
+                                         float* sc) {
+  XOctet o;
+  o.load(x, x_dtype, nch, c0, layout);
+  o.store(nch, q, sc);
+}
+
+// Quantize groups [g0, g0 + 32) of 16 fp32 values (ng groups in all) with one
+// wave: lane L takes half L % 2 of group g0 + L / 2.
+__device__ __forceinline__ void quant_g32(const float* h, int ng, int g0, int layout, uint8_t* q, float* sc) {
+  const int lane = threadIdx.x & 63;
+  const int g = g0 + (lane >> 1), hh = lane & 1;
+  const int gc = g < ng ? g : ng - 1;
+  float v[8];
+  load_half_f32(h, 16 * (int64_t)gc, hh, layout, v);
+  float s;
+  const uint4 w = quant8<2>(v, s);
+  if (g < ng) {
+    *reinterpret_cast<uint4*>(q + (int64_t)g * G16_BYTES + 16 * hh) = w;
+    if (hh == 0) sc[g] = s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -375,14 +499,26 @@ struct EPlanes {  // one expert's planes of a weight tensor in the device layout
   const uint8_t* b;
 };
 
+// A or B, chosen field by field (a select of values, never of addresses, so
+// that the planes stay in registers).
+__device__ __forceinline__ EPlanes pick_planes(bool second, const EPlanes& A, const EPlanes& B) {
+  EPlanes p;
+  p.scale = second ? B.scale : A.scale;
+  p.a = second ? B.a : A.a;
+  p.b = second ? B.b : A.b;
+  return p;
+}
+
+// Expert e's planes of a tensor whose format is a compile-time FMT.
+template <int FMT>
 __device__ __forceinline__ EPlanes expert_planes(const QMat& m, int e) {
   const int64_t r = (int64_t)e * m.rows * m.nb;  // blocks before this expert
   EPlanes p;
-  if (m.fmt == FMT_IQ2) {
+  if constexpr (FMT == FMT_IQ2) {
     p.scale = m.p_scale + r * 2;
     p.a = m.p_a + r * 64;
     p.b = nullptr;
-  } else if (m.fmt == FMT_Q2K) {
+  } else if constexpr (FMT == FMT_Q2K) {
     p.scale = m.p_scale + r * 4;
     p.a = m.p_a + r * 16;
     p.b = m.p_b + r * 64;
@@ -394,6 +530,10 @@ __device__ __forceinline__ EPlanes expert_planes(const QMat& m, int e) {
   return p;
 }
 
+// A piece: one lane's 16 bytes of codes of one row, plus the scales that
+// belong to them.  load() reads the codes; the scales come either straight
+// from their planes (scales_global) or from a copy of the rows' scale bytes
+// that the wave staged in LDS (scales_lds; see ScaleStage).
 template <int FMT>
 struct Piece;
 
@@ -404,7 +544,14 @@ struct Piece<FMT_IQ2> {  // words A0 B0 A1 B1 of sub-blocks 2 (pc % 4), +1 of su
   template <int NB>
   __device__ __forceinline__ void load(const EPlanes& p, uint32_t row, uint32_t pc) {
     v = ld16_stream(p.a + (row * NB * 64 + pc * 16));
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_global(const EPlanes& p, uint32_t row, uint32_t pc) {
     d = reinterpret_cast<const uint16_t*>(p.scale)[row * NB + pc / 4];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_lds(const uint8_t* rp, uint32_t pc) {
+    d = reinterpret_cast<const uint16_t*>(rp)[pc / 4];
   }
 };
 
@@ -415,8 +562,16 @@ struct Piece<FMT_Q2K> {  // quants of sub-blocks 4 (pc % 4) .. +3 of superblock 
   template <int NB>
   __device__ __forceinline__ void load(const EPlanes& p, uint32_t row, uint32_t pc) {
     q = ld16_stream(p.b + (row * NB * 64 + pc * 16));
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_global(const EPlanes& p, uint32_t row, uint32_t pc) {
     sc = *reinterpret_cast<const uint32_t*>(p.a + (row * NB * 16 + pc * 4));
     dm = reinterpret_cast<const uint32_t*>(p.scale)[row * NB + pc / 4];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_lds(const uint8_t* rp, uint32_t pc) {  // row: dm[NB] then sc[NB][16]
+    dm = reinterpret_cast<const uint32_t*>(rp)[pc / 4];
+    sc = reinterpret_cast<const uint32_t*>(rp + NB * 4)[pc];
   }
 };
 
@@ -427,97 +582,105 @@ struct Piece<FMT_Q8> {  // 16 int8 quants: half of block pc / 2
   template <int NB>
   __device__ __forceinline__ void load(const EPlanes& p, uint32_t row, uint32_t pc) {
     q = ld16_stream(p.a + (row * NB * 32 + pc * 16));
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_global(const EPlanes& p, uint32_t row, uint32_t pc) {
     d = reinterpret_cast<const uint16_t*>(p.scale)[row * NB + pc / 2];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_lds(const uint8_t* rp, uint32_t pc) {
+    d = reinterpret_cast<const uint16_t*>(rp)[pc / 2];
+  }
+};
+
+// Scale bytes of one row in format FMT with K inputs, as staged in LDS.
+template <int FMT, int K>
+struct RowScales {
+  static constexpr int NB = K / block_weights(FMT);
+  static constexpr int DM = FMT == FMT_Q2K ? NB * 4 : 0;                // Q2K (d, dmin) pairs
+  static constexpr int BYTES = FMT == FMT_Q2K ? NB * 20 : NB * 2;       // + Q2K sub-block scales
+  static constexpr bool STAGE = (BYTES % 16) == 0 && (DM % 16) == 0;    // whole 16-byte chunks
+};
+
+// The scale bytes of NM matrices x NR rows, copied by one wave into its LDS
+// area (row (m, j) at m * NR + j, RowScales::BYTES each) with one 16-byte
+// load per lane per 64 chunks.  issue() only loads (so these loads can be
+// put ahead of the code loads, which then return after them); store()
+// writes LDS.  Each lane maps its chunks to (row, plane) itself, so rows may
+// belong to different experts.
+template <int FMT, int K, int NM, int NR>
+struct ScaleStage {
+  using RS = RowScales<FMT, K>;
+  static constexpr int CPR = RS::BYTES / 16;  // chunks per row
+  static constexpr int CH = NM * NR * CPR;
+  static constexpr int NV = (CH + 63) / 64;
+  uint4 v[NV];
+  // rowsrc(m, j, planes, row) gives the expert planes and row index of (m, j)
+  template <class RowSrc>
+  __device__ __forceinline__ void issue(RowSrc rowsrc) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      int q = lane + 64 * i;
+      q = q < CH ? q : CH - 1;
+      const int r = q / CPR, cq = q % CPR;
+      const int m = r / NR, j = r % NR;
+      EPlanes P;
+      uint32_t row;
+      rowsrc(m, j, P, row);
+      const uint8_t* src;
+      if constexpr (FMT == FMT_Q2K) {
+        src = cq * 16 < RS::DM ? P.scale + row * RS::DM + cq * 16 : P.a + row * (RS::NB * 16) + (cq * 16 - RS::DM);
+      } else {
+        src = P.scale + row * RS::BYTES + cq * 16;
+      }
+      v[i] = ld16(src);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NV; i++)
+      if (lane + 64 * i < CH) *reinterpret_cast<uint4*>(lds + 16 * (lane + 64 * i)) = v[i];
+  }
+  static __device__ __forceinline__ const uint8_t* row(const uint8_t* lds, int m, int j) {
+    return lds + (m * NR + j) * RS::BYTES;
   }
 };
 
 // ---------------------------------------------------------------------------
-// IQ2 nibble table: entry (g, b) = the 8 weights of grid row g with stored
-// sign bits b (and the parity sign), as signed nibbles (element n in nibble
-// n).  128 KB of LDS, built per block.
+// IQ2 tables.  A grid magnitude m (odd, 1..7) becomes the nibble u = (m + 7)
+// / 2, so +m is u and -m is 7 - u = u ^ 7: pos[row] holds the 8 magnitudes
+// of a grid row as such nibbles (element n in nibble n), neg[b] holds 0x7 in
+// every nibble whose sign is negative for the 7 stored sign bits b (parity
+// sign included).  A group's weights are w_n = 2 u_n - 7 with
+// u = pos[row] ^ neg[b]: one XOR of two small-table words per 8 weights, and
+// sum w x = 2 sum u x - 7 sum x.  1.5 KB of LDS.
 // ---------------------------------------------------------------------------
-constexpr int IQ2_TAB_WORDS = 256 * 128;
-constexpr size_t IQ2_TAB_BYTES = (size_t)IQ2_TAB_WORDS * 4;
-
-struct Iq2Aux {
-  uint2 pm[256];       // per grid row: magnitudes as nibbles, and their negations
-  uint32_t mask[128];  // per stored sign pattern: 0xF in every negative nibble
+struct Iq2Tab {
+  uint32_t pos[256];
+  uint32_t neg[128];
 };
 
-// The table is built in two steps so that the global loads it needs (the
-// grid) can be in flight together with other loads: iq2_aux_prepare() for
-// items 0..383 (grid row i for i < 256, sign pattern i - 256 below 384), each
-// item by one thread with the grid row it loaded, then, after a barrier,
-// iq2_fill_table() by all 512 threads, then another barrier.
-__device__ __forceinline__ uint2 iq2_grid_row(const uint8_t* __restrict__ grid, int item) {
-  return (item >= 0 && item < 256) ? reinterpret_cast<const uint2*>(grid)[item] : make_uint2(0, 0);
-}
-
-__device__ __forceinline__ void iq2_aux_prepare(uint2 g, int item, Iq2Aux* aux) {
+// Items 0..383 (grid row i < 256, sign pattern i - 256), one per thread
+// `item`; the caller publishes the table with a barrier.
+__device__ __forceinline__ void iq2_build(const uint8_t* __restrict__ grid, int item, Iq2Tab* t) {
   if (item >= 0 && item < 256) {
-    uint32_t pos = 0, neg = 0;
+    const uint2 g = reinterpret_cast<const uint2*>(grid)[item];
+    uint32_t w = 0;
 #pragma unroll
     for (int n = 0; n < 8; n++) {
       const uint32_t m = ((n < 4 ? g.x : g.y) >> (8 * (n & 3))) & 255u;
-      pos |= (m & 15u) << (4 * n);
-      neg |= ((16u - m) & 15u) << (4 * n);
+      w |= (((m + 7u) >> 1) & 15u) << (4 * n);
     }
-    aux->pm[item] = make_uint2(pos, neg);
+    t->pos[item] = w;
   } else if (item >= 256 && item < 384) {
     const uint32_t b = item - 256;
     const uint32_t s8 = b | ((__popc(b) & 1u) << 7);
     uint32_t mk = 0;
 #pragma unroll
-    for (int n = 0; n < 8; n++) mk |= ((s8 >> n) & 1u) ? (0xfu << (4 * n)) : 0u;
-    aux->mask[b] = mk;
-  }
-}
-
-__device__ __forceinline__ void iq2_fill_table(uint32_t* tab, const Iq2Aux* aux) {
-  const int t = threadIdx.x;
-#pragma unroll 4
-  for (int it = 0; it < IQ2_TAB_WORDS / 4 / THREADS; it++) {
-    const int u = t + THREADS * it;  // entries 4u .. 4u + 3: grid row u / 32, sign patterns 4 (u % 32) + 0..3
-    const uint2 pm = aux->pm[u >> 5];
-    const uint4 mk = *reinterpret_cast<const uint4*>(&aux->mask[4 * (u & 31)]);
-    uint4 o;
-    o.x = (mk.x & pm.y) | (~mk.x & pm.x);
-    o.y = (mk.y & pm.y) | (~mk.y & pm.x);
-    o.z = (mk.z & pm.y) | (~mk.z & pm.x);
-    o.w = (mk.w & pm.y) | (~mk.w & pm.x);
-    reinterpret_cast<uint4*>(tab)[u] = o;
-  }
-}
-
-// Whole build by all 512 threads of the block, with its barriers.
-__device__ __forceinline__ void build_iq2_table(const uint8_t* __restrict__ grid, uint32_t* tab, Iq2Aux* aux) {
-  iq2_aux_prepare(iq2_grid_row(grid, threadIdx.x), threadIdx.x, aux);
-  __syncthreads();
-  iq2_fill_table(tab, aux);
-  __syncthreads();
-}
-
-// Quantize x_t (d values, fp32 or bf16) into chunks of 64 in `layout` at
-// q / sc (LDS or global), with the waves w0 .. WAVES-1 of the block: every
-// wave first issues the loads of all its chunks, then quantizes them.
-template <int MAXC>
-__device__ __forceinline__ void quant_x_chunks(const void* x, int x_dtype, int64_t off, int nch, int layout,
-                                               uint8_t* q, float* sc, int w0) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = WAVES - w0;
-  if (wave < w0) return;
-  float v[MAXC];
-#pragma unroll
-  for (int j = 0; j < MAXC; j++) {
-    const int ch = (wave - w0) + nw * j;
-    const int chc = ch < nch ? ch : nch - 1;
-    v[j] = x_dtype == X_BF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(x)[off + 64 * chc + lane])
-                             : static_cast<const float*>(x)[off + 64 * chc + lane];
-  }
-#pragma unroll
-  for (int j = 0; j < MAXC; j++) {
-    const int ch = (wave - w0) + nw * j;
-    if (ch < nch) quant_wave<64>(v[j], layout, q + (int64_t)ch * CHUNK_BYTES, sc + ch, 4);
+    for (int n = 0; n < 8; n++) mk |= ((s8 >> n) & 1u) ? (0x7u << (4 * n)) : 0u;
+    t->neg[b] = mk;
   }
 }
 
@@ -527,7 +690,7 @@ __device__ __forceinline__ void quant_x_chunks(const void* x, int x_dtype, int64
 // ---------------------------------------------------------------------------
 template <int CPL, bool PER16>
 __device__ __forceinline__ float piece_dot(const Piece<FMT_IQ2>& w, const ActNib<CPL, PER16>& a, int k,
-                                           const uint32_t* tab) {
+                                           const Iq2Tab* tab) {
   const uint32_t AB[4] = {w.v.x, w.v.y, w.v.z, w.v.w};
   int itot = 0;
   float ftot = 0.0f;
@@ -538,15 +701,17 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_IQ2>& w, const ActNib
     int acc[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint32_t e = tab[(((A >> (8 * i)) & 255u) << 7) | ((B >> (7 * i)) & 127u)];
+      const uint32_t u = tab->pos[(A >> (8 * i)) & 255u] ^ tab->neg[(B >> (7 * i)) & 127u];
       const int q = 2 * h + (i >> 1), hh = i & 1, slot = PER16 ? (i >> 1) : 0;
 #pragma unroll
-      for (int p = 0; p < 4; p++) acc[slot][p] = dot8(e, a.w[k][q][hh][p], acc[slot][p]);
+      for (int p = 0; p < 4; p++) acc[slot][p] = dot8(u, a.w[k][q][hh][p], acc[slot][p]);
     }
+    // sum w x = 2 sum u x - 7 sum x over each group of 16
     if constexpr (PER16) {
-      ftot += (float)(combine4(acc[0]) * mul) * a.s[k][2 * h] + (float)(combine4(acc[1]) * mul) * a.s[k][2 * h + 1];
+      ftot += (float)((2 * combine4(acc[0]) - 7 * a.Ai[k][2 * h]) * mul) * a.s[k][2 * h] +
+              (float)((2 * combine4(acc[1]) - 7 * a.Ai[k][2 * h + 1]) * mul) * a.s[k][2 * h + 1];
     } else {
-      itot += combine4(acc[0]) * mul;
+      itot += (2 * combine4(acc[0]) - 7 * (a.Ai[k][2 * h] + a.Ai[k][2 * h + 1])) * mul;
     }
   }
   const float d = half_bits_to_float(w.d);
@@ -558,7 +723,7 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_IQ2>& w, const ActNib
 
 template <int CPL, bool PER16>
 __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib<CPL, PER16>& a, int k,
-                                           const uint32_t*) {
+                                           const Iq2Tab*) {
   const uint32_t W[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
   int im = 0, in = 0;
   float fm = 0.0f, fn = 0.0f;
@@ -586,7 +751,7 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib
 }
 
 template <int CPL>
-__device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8N<CPL>& a, int k, const uint32_t*) {
+__device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8N<CPL>& a, int k, const Iq2Tab*) {
   int acc[4];
 #pragma unroll
   for (int p = 0; p < 4; p++)
@@ -596,7 +761,7 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8N<
 }
 
 template <int CPL>
-__device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8B<CPL>& a, int k, const uint32_t*) {
+__device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8B<CPL>& a, int k, const Iq2Tab*) {
   const int h = dot4(w.q.w, a.H[k][3], dot4(w.q.z, a.H[k][2], dot4(w.q.y, a.H[k][1], dot4(w.q.x, a.H[k][0], 0))));
   const int l = dot4(w.q.w, a.L[k][3], dot4(w.q.z, a.L[k][2], dot4(w.q.y, a.L[k][1], dot4(w.q.x, a.L[k][0], 0))));
   return (float)(h * 256 + l) * (a.s[k] * half_bits_to_float(w.d));
@@ -620,18 +785,22 @@ struct DecodeArgs {
   float* wt;         // [T][k]
   int32_t* idx_out;  // nullable caller copies
   float* wt_out;
+  uint8_t* xq;       // [T][d/64] x in chunks (layout of the routed gate/up format), from the first launch
+  float* xs;         // [T][d/64]
   float* hsh;        // [T][f] shared SwiGLU output, fp32
   uint8_t* hq;       // [T*k + T][f/16] quantized SwiGLU outputs (routed, then shared)
   float* hs;         // [T*k + T][f/16]
   float* y;          // [T][d]
 };
 
-// Work split of the first kernel: blocks [0, n_rb) hold epb router experts
-// each (one per wave), blocks [n_rb, n_rb + n_sb) hold spb consecutive
-// shared gate/up steps each; epb and spb are chosen so that every block
-// streams about the same number of bytes.
+// Work split of the first kernel: blocks [0, n_rb) hold epb (< 8) router
+// experts each (one per wave; the last wave quantizes x for the routed
+// gate/up), blocks [n_rb, n_rb + n_sb) hold spb consecutive shared gate/up
+// steps each; epb and spb are chosen so that every block streams about the
+// same number of bytes.
 struct K1Plan {
   int n_rb, epb, n_sb, spb, n_steps;
+  int n_xb;  // 1 when only a block quantizing x runs (no router, no shared expert)
 };
 
 }  // namespace dec

@@ -5,12 +5,13 @@
 // The routed h rows of all tokens (T * k * d_ff, route-major) are cut into
 // groups of 16, the unit of h's quantization scale; a block takes GCNT
 // consecutive groups of one token (8 waves, 2 GCNT rows each), so every block
-// streams the same bytes and finishes whole groups.  Block prologue, all in
+// streams the same bytes and finishes whole groups.  Block prologue, in
 // parallel: wave 0 selects the token's experts from the router logits (every
 // block of the token does the same exact top-k; the token's first block
-// publishes idx / wt); waves 1..7 quantize x_t into LDS, load the IQ2 grid
-// and (wave 7) quantize a share of the shared expert's h.  Then every wave
-// issues its weight loads and the IQ2 table is written while they fly.
+// publishes idx / wt); waves 1..7 build the IQ2 tables and (wave 7) quantize
+// a share of the shared expert's h.  Then every wave requests its rows' scale
+// bytes and first weights and the rows run software-pipelined (x comes
+// quantized from the first launch).
 #include "decode_common.hpp"
 #include "topk.hpp"
 
@@ -28,25 +29,23 @@ struct RoutedAct<FMT_Q8, D> {
 
 template <int FMT, int D, int GCNT>
 __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layout, int shared_layout) {
-  extern __shared__ uint32_t dyn_tab[];
-  __shared__ Iq2Aux aux;
-  __shared__ __attribute__((aligned(16))) uint8_t s_xq[(D / 64) * CHUNK_BYTES];
-  __shared__ float s_xs[D / 64];
-  __shared__ float hbuf[16 * GCNT];
+  __shared__ Iq2Tab itab;
+  __shared__ __attribute__((aligned(16))) float hbuf[16 * GCNT];
   __shared__ int s_sel[TOPK_MAX_K];
   __shared__ float s_zs[TOPK_MAX_K];
   using G = Geo<FMT, D>;
   constexpr int RPW = 2 * GCNT;  // h rows per wave
-  constexpr int STEPS = (RPW + G::RPS - 1) / G::RPS;
-  constexpr int BATCH_ = (FMT == FMT_Q8 ? 8 : 16) / (2 * G::CPL);
-  constexpr int BATCH = BATCH_ < 1 ? 1 : (BATCH_ < STEPS ? BATCH_ : STEPS);
+  constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
+  constexpr int PD = NS < 3 ? NS : 3;  // steps of loads kept in flight ahead of the compute
+  constexpr int SCL_BYTES = RowScales<FMT, D>::STAGE ? 2 * RPW * RowScales<FMT, D>::BYTES : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * SCL_BYTES];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane / G::LPR, c = lane % G::LPR;
   const int g0 = blockIdx.x * GCNT;  // first group of 16 rows
   const int R0 = 16 * g0;            // first routed h row (route-major over all tokens)
   const int t = R0 / (a.k * a.f);
 
-  // ---- prologue ----
+  // ---- prologue: only small loads, all issued before any weight load ----
   if (wave == 0) {
     if (a.fused_topk) {
       wave_topk(a.z + (int64_t)t * a.E, a.E, a.k, s_sel, s_zs);
@@ -63,95 +62,105 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
       s_sel[lane] = a.idx[(int64_t)t * a.k + lane];
     }
   } else {
-    const int aux_item = threadIdx.x - 64;  // waves 1..7 prepare the 384 table items
-    uint2 grow = make_uint2(0, 0);
-    if constexpr (FMT == FMT_IQ2) grow = iq2_grid_row(a.grid, aux_item);
-    float hv = 0.0f;
-    const int NQ = a.T * a.f / 64;  // quads of shared h groups, spread over the blocks
-    const bool do_sh = a.has_shared && wave == WAVES - 1 && (int)blockIdx.x < NQ;
-    if (do_sh) hv = a.hsh[(int64_t)blockIdx.x * 64 + lane];
-    quant_x_chunks<(D / 64 + WAVES - 2) / (WAVES - 1)>(a.x, a.x_dtype, (int64_t)t * D, D / 64, nib_layout(FMT), s_xq,
-                                                     s_xs, 1);
-    if constexpr (FMT == FMT_IQ2) iq2_aux_prepare(grow, aux_item, &aux);
-    if (do_sh) {
-      const int64_t base = (int64_t)a.T * a.k * (a.f / 16) + 4 * blockIdx.x;
-      quant_wave<16>(hv, shared_layout, a.hq + base * G16_BYTES, a.hs + base, 4);
-      for (int qd = blockIdx.x + gridDim.x; qd < NQ; qd += gridDim.x) {  // (only when blocks < quads)
-        const float v = a.hsh[(int64_t)qd * 64 + lane];
-        const int64_t b2 = (int64_t)a.T * a.k * (a.f / 16) + 4 * qd;
-        quant_wave<16>(v, shared_layout, a.hq + b2 * G16_BYTES, a.hs + b2, 4);
-      }
+    if constexpr (FMT == FMT_IQ2) iq2_build(a.grid, threadIdx.x - 64, &itab);  // waves 1..7: 384 items
+    if (a.has_shared && wave == WAVES - 1) {
+      // the shared expert's h (from the first launch): 32 groups per pass,
+      // the passes spread over the blocks
+      const int NG = a.T * a.f / 16;
+      const int64_t base = (int64_t)a.T * a.k * (a.f / 16);
+      for (int g0s = 32 * blockIdx.x; g0s < NG; g0s += 32 * gridDim.x)
+        quant_g32(a.hsh, NG, g0s, shared_layout, a.hq + base * G16_BYTES, a.hs + base);
     }
   }
   __syncthreads();
 
-  // ---- weights of this wave's rows ----
+  // ---- this wave's rows, software-pipelined ----
+  // The wave's RPW rows start at route r0 and cross at most one route
+  // boundary (at wave row jb), so two plane sets cover them.
+  using SS = ScaleStage<FMT, D, 2, RPW>;
+  constexpr bool STAGE = SS::RS::STAGE;
+  const int Rw = R0 + wave * RPW;   // first row of the wave
+  const int r0 = Rw / a.f;          // its route (global index)
+  const int n0 = Rw - r0 * a.f;     // its row inside the expert
+  const int jb = a.f - n0;          // rows j >= jb belong to route r0 + 1
+  const int r1 = min(r0 + 1, t * a.k + a.k - 1);  // (a block never leaves its token)
+  const int e0 = s_sel[r0 - t * a.k], e1 = s_sel[r1 - t * a.k];
+  const bool ok0 = (unsigned)e0 < (unsigned)a.E, ok1 = (unsigned)e1 < (unsigned)a.E;
+  const EPlanes G0 = expert_planes<FMT>(a.gate, ok0 ? e0 : 0), U0 = expert_planes<FMT>(a.up, ok0 ? e0 : 0);
+  const EPlanes G1 = expert_planes<FMT>(a.gate, ok1 ? e1 : 0), U1 = expert_planes<FMT>(a.up, ok1 ? e1 : 0);
+  auto rowsrc = [&](int m, int j, EPlanes& P, uint32_t& row) {
+    const bool second = j >= jb;
+    P = m == 0 ? pick_planes(second, G0, G1) : pick_planes(second, U0, U1);
+    row = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+  };
+  Piece<FMT> wg[NS][G::CPL], wu[NS][G::CPL];
+  int lr[NS];
+  bool ok[NS];
+  auto issue = [&](int s) {
+    const int jj = s * G::RPS + sub;  // row within the wave
+    const bool valid = jj < RPW;
+    const int j = valid ? jj : 0;
+    lr[s] = wave * RPW + j;
+    const bool second = j >= jb;
+    ok[s] = valid && (second ? ok1 : ok0);
+    const uint32_t n = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+    const EPlanes Gp = pick_planes(second, G0, G1);
+    const EPlanes Up = pick_planes(second, U0, U1);
 #pragma unroll
-  for (int s0 = 0; s0 < STEPS; s0 += BATCH) {
-    Piece<FMT> wg[BATCH][G::CPL], wu[BATCH][G::CPL];
-    int lr[BATCH];
-    bool ok[BATCH];
-#pragma unroll
-    for (int bb = 0; bb < BATCH; bb++) {
-      const int j = (s0 + bb) * G::RPS + sub;  // row within the wave
-      const bool valid = s0 + bb < STEPS && j < RPW;
-      lr[bb] = wave * RPW + (valid ? j : 0);
-      const int R = R0 + lr[bb];
-      const int e = s_sel[R / a.f - t * a.k];
-      const bool e_ok = (unsigned)e < (unsigned)a.E;
-      ok[bb] = valid && e_ok;
-      const uint32_t n = (uint32_t)(R % a.f);
-      const EPlanes Gp = expert_planes(a.gate, e_ok ? e : 0), Up = expert_planes(a.up, e_ok ? e : 0);
-#pragma unroll
-      for (int k = 0; k < G::CPL; k++) {
-        wg[bb][k].template load<G::NB>(Gp, n, c + G::LPR * k);
-        wu[bb][k].template load<G::NB>(Up, n, c + G::LPR * k);
+    for (int k = 0; k < G::CPL; k++) {
+      wg[s][k].template load<G::NB>(Gp, n, c + G::LPR * k);
+      wu[s][k].template load<G::NB>(Up, n, c + G::LPR * k);
+      if constexpr (!STAGE) {
+        wg[s][k].template scales_global<G::NB>(Gp, n, c + G::LPR * k);
+        wu[s][k].template scales_global<G::NB>(Up, n, c + G::LPR * k);
       }
     }
-    if constexpr (FMT == FMT_IQ2) {
-      if (s0 == 0) {  // the table is written while the first weights are in flight
-        iq2_fill_table(dyn_tab, &aux);
-        __syncthreads();
-      }
-    }
-    typename RoutedAct<FMT, D>::type act;
+  };
+  uint8_t* my_scales = s_scl + wave * SCL_BYTES;
+  SS ss;
+  if constexpr (STAGE) ss.issue(rowsrc);  // first: returns before the codes
+#pragma unroll
+  for (int s = 0; s < PD; s++) issue(s);
+  if constexpr (STAGE) ss.store(my_scales);
+  typename RoutedAct<FMT, D>::type act;
+  {
+    const uint8_t* xq = a.xq + (int64_t)t * (D / 64) * CHUNK_BYTES;
+    const float* xs = a.xs + (int64_t)t * (D / 64);
     if constexpr (FMT == FMT_Q8) {
-      act.template load<G::LPR, 64>(s_xq, s_xs, c);
+      act.template load<G::LPR, 64>(xq, xs, c);
     } else {
-      act.template load<G::LPR>(s_xq, s_xs, c);
-      if constexpr (FMT == FMT_Q2K) act.sums();
-    }
-#pragma unroll
-    for (int bb = 0; bb < BATCH; bb++) {
-      float g = 0.0f, u = 0.0f;
-#pragma unroll
-      for (int k = 0; k < G::CPL; k++) {
-        g += piece_dot(wg[bb][k], act, k, dyn_tab);
-        u += piece_dot(wu[bb][k], act, k, dyn_tab);
-      }
-      g = group_sum<G::LPR>(g);
-      u = group_sum<G::LPR>(u);
-      const int j = (s0 + bb) * G::RPS + sub;
-      if (c == G::LPR - 1 && s0 + bb < STEPS && j < RPW) hbuf[lr[bb]] = ok[bb] ? silu(g) * u : 0.0f;
+      act.template load<G::LPR>(xq, xs, c);
+      act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
     }
   }
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    if (s + PD < NS) issue(s + PD);
+    if constexpr (STAGE) {
+      const int j = min(s * G::RPS + sub, RPW - 1);
+#pragma unroll
+      for (int k = 0; k < G::CPL; k++) {
+        wg[s][k].template scales_lds<G::NB>(SS::row(my_scales, 0, j), c + G::LPR * k);
+        wu[s][k].template scales_lds<G::NB>(SS::row(my_scales, 1, j), c + G::LPR * k);
+      }
+    }
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) {
+      g += piece_dot(wg[s][k], act, k, &itab);
+      u += piece_dot(wu[s][k], act, k, &itab);
+    }
+    g = group_sum<G::LPR>(g);
+    u = group_sum<G::LPR>(u);
+    if (c == G::LPR - 1 && s * G::RPS + sub < RPW) hbuf[lr[s]] = ok[s] ? silu(g) * u : 0.0f;
+  }
   __syncthreads();
-  if (wave == 0)
-    quant_wave<16>(lane < 16 * GCNT ? hbuf[lane] : 0.0f, down_layout, a.hq + (int64_t)g0 * G16_BYTES, a.hs + g0,
-                   GCNT);
+  if (wave == 0) quant_g32(hbuf, GCNT, 0, down_layout, a.hq + (int64_t)g0 * G16_BYTES, a.hs + g0);
 }
 
 template <int FMT, int D, int GCNT>
 static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, int shared_layout, hipStream_t s) {
-  const size_t lds = FMT == FMT_IQ2 ? IQ2_TAB_BYTES : 0;
-  static bool attr = false;
-  if (!attr && lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)k2_kernel<FMT, D, GCNT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  k2_kernel<FMT, D, GCNT><<<dim3(blocks), THREADS, lds, s>>>(a, down_layout, shared_layout);
+  k2_kernel<FMT, D, GCNT><<<dim3(blocks), THREADS, 0, s>>>(a, down_layout, shared_layout);
   return hipGetLastError();
 }
 

@@ -27,8 +27,10 @@ struct DownAct<FMT_Q8, K> {
 // out-of-range expert id (a caller error) contributes zero.
 template <int FMT, int K, int ROWS>
 __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, const uint8_t* hq, const float* hs,
-                                          const uint32_t* tab, float* out) {
+                                          const Iq2Tab* tab, uint8_t* my_scales, float* out) {
   using G = Geo<FMT, K>;
+  using SS = ScaleStage<FMT, K, 1, ROWS>;
+  constexpr bool STAGE = SS::RS::STAGE;
   const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
   typename DownAct<FMT, K>::type act;
   if constexpr (FMT == FMT_Q8) {
@@ -40,62 +42,75 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
     if (lane < ROWS) out[lane] = 0.0f;
     return;
   }
-  const EPlanes Dp = expert_planes(m, e);
-  constexpr int STEPS = (ROWS + G::RPS - 1) / G::RPS;
-  constexpr int BATCH_ = (FMT == FMT_Q8 ? 4 : 8) / G::CPL;
-  constexpr int BATCH = BATCH_ < 1 ? 1 : (BATCH_ < STEPS ? BATCH_ : STEPS);
-  bool sums_done = false;
+  const EPlanes Dp = expert_planes<FMT>(m, e);
+  constexpr int NS = (ROWS + G::RPS - 1) / G::RPS;
+  constexpr int PD = NS < 3 ? NS : 3;  // steps of loads kept in flight ahead of the compute
+  Piece<FMT> w[NS][G::CPL];
+  auto issue = [&](int s) {
+    const int j = s * G::RPS + sub;
+    const uint32_t n = (uint32_t)(r0 + (j < ROWS ? j : 0));
 #pragma unroll
-  for (int s0 = 0; s0 < STEPS; s0 += BATCH) {
-    Piece<FMT> w[BATCH][G::CPL];
-#pragma unroll
-    for (int b = 0; b < BATCH; b++) {
-      const int j = (s0 + b) * G::RPS + sub;
-      const bool valid = s0 + b < STEPS && j < ROWS;
-      const uint32_t n = (uint32_t)(r0 + (valid ? j : 0));
-#pragma unroll
-      for (int k = 0; k < G::CPL; k++) w[b][k].template load<G::NB>(Dp, n, c + G::LPR * k);
+    for (int k = 0; k < G::CPL; k++) {
+      w[s][k].template load<G::NB>(Dp, n, c + G::LPR * k);
+      if constexpr (!STAGE) w[s][k].template scales_global<G::NB>(Dp, n, c + G::LPR * k);
     }
-    if constexpr (FMT == FMT_Q2K) {
-      if (!sums_done) {
-        act.sums();
-        sums_done = true;
-      }
-    }
+  };
+  SS ss;
+  if constexpr (STAGE)
+    ss.issue([&](int, int j, EPlanes& P, uint32_t& row) {
+      P = Dp;
+      row = (uint32_t)(r0 + j);
+    });
 #pragma unroll
-    for (int b = 0; b < BATCH; b++) {
-      float v = 0.0f;
+  for (int s = 0; s < PD; s++) issue(s);
+  if constexpr (STAGE) ss.store(my_scales);
+  if constexpr (FMT != FMT_Q8) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
 #pragma unroll
-      for (int k = 0; k < G::CPL; k++) v += piece_dot(w[b][k], act, k, tab);
-      v = group_sum<G::LPR>(v);
-      const int j = (s0 + b) * G::RPS + sub;
-      if (c == G::LPR - 1 && s0 + b < STEPS && j < ROWS) out[j] = v;
+  for (int s = 0; s < NS; s++) {
+    if (s + PD < NS) issue(s + PD);
+    const int j = s * G::RPS + sub;
+    if constexpr (STAGE) {
+#pragma unroll
+      for (int k = 0; k < G::CPL; k++)
+        w[s][k].template scales_lds<G::NB>(SS::row(my_scales, 0, j < ROWS ? j : 0), c + G::LPR * k);
     }
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) v += piece_dot(w[s][k], act, k, tab);
+    v = group_sum<G::LPR>(v);
+    if (c == G::LPR - 1 && j < ROWS) out[j] = v;
   }
 }
 
 template <int FR, int FS, int F>
 __global__ __launch_bounds__(THREADS) void k3_kernel(DecodeArgs a) {
-  extern __shared__ uint32_t dyn_tab[];
-  __shared__ Iq2Aux aux;
+  __shared__ Iq2Tab itab;
   __shared__ float ye[(TOPK_MAX_K + 1) * DN_ROWS];
+  constexpr int SCL_R = RowScales<FR, F>::STAGE ? DN_ROWS * RowScales<FR, F>::BYTES : 16;
+  constexpr int SCL_S = RowScales<FS, F>::STAGE ? (DN_ROWS / 2) * RowScales<FS, F>::BYTES : 16;
+  constexpr int SCL_BYTES = SCL_R > SCL_S ? SCL_R : SCL_S;
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * SCL_BYTES];
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.y;
   const int row0 = blockIdx.x * DN_ROWS;
-  if constexpr (FR == FMT_IQ2 || FS == FMT_IQ2) build_iq2_table(a.grid, dyn_tab, &aux);
+  if constexpr (FR == FMT_IQ2 || FS == FMT_IQ2) {
+    iq2_build(a.grid, threadIdx.x, &itab);
+    __syncthreads();
+  }
   constexpr int NG = F / 16;  // groups of 16 per h vector
   const int n_tasks = a.k + (a.has_shared ? 2 : 0);
   for (int task = wave; task < n_tasks; task += WAVES) {
     if (task < a.k) {
       const int64_t r = (int64_t)t * a.k + task;
       const int e = a.idx[r];
-      down_rows<FR, F, DN_ROWS>(a.down, e, a.E, row0, a.hq + r * NG * G16_BYTES, a.hs + r * NG, dyn_tab,
-                                ye + task * DN_ROWS);
+      down_rows<FR, F, DN_ROWS>(a.down, e, a.E, row0, a.hq + r * NG * G16_BYTES, a.hs + r * NG, &itab,
+                                s_scl + wave * SCL_BYTES, ye + task * DN_ROWS);
     } else {
       const int half = task - a.k;
       const int64_t src = (int64_t)a.T * a.k + t;
       down_rows<FS, F, DN_ROWS / 2>(a.s_down, 0, 1, row0 + half * (DN_ROWS / 2), a.hq + src * NG * G16_BYTES,
-                                    a.hs + src * NG, dyn_tab, ye + a.k * DN_ROWS + half * (DN_ROWS / 2));
+                                    a.hs + src * NG, &itab, s_scl + wave * SCL_BYTES,
+                                    ye + a.k * DN_ROWS + half * (DN_ROWS / 2));
     }
   }
   __syncthreads();
@@ -110,15 +125,7 @@ __global__ __launch_bounds__(THREADS) void k3_kernel(DecodeArgs a) {
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  const size_t lds = (FR == FMT_IQ2 || FS == FMT_IQ2) ? IQ2_TAB_BYTES : 0;
-  static bool attr = false;
-  if (!attr && lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)k3_kernel<FR, FS, F>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  k3_kernel<FR, FS, F><<<dim3(a.d / DN_ROWS, a.T), THREADS, lds, s>>>(a);
+  k3_kernel<FR, FS, F><<<dim3(a.d / DN_ROWS, a.T), THREADS, 0, s>>>(a);
   return hipGetLastError();
 }
 

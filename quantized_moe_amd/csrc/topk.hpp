@@ -53,32 +53,121 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Top-k of zt[0..E) by one full wave.  out_idx / out_z (k entries, rank
-// order) are written by lane 0 only; they are typically LDS arrays.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z) {
+// Top-k of zt[0..E) by one full wave, E <= 64 * SLOTS.  out_idx / out_z (k
+// entries, rank order) are written by lane 0 only; they are typically LDS
+// arrays.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[TOPK_MAX_PER_LANE];
-  float zv[TOPK_MAX_PER_LANE];
+  uint64_t key[SLOTS];
+  float zv[SLOTS];
 #pragma unroll
-  for (int i = 0; i < TOPK_MAX_PER_LANE; i++) zv[i] = zt[min(lane + 64 * i, E - 1)];  // unconditional: one wait
+  for (int i = 0; i < SLOTS; i++) zv[i] = zt[min(lane + 64 * i, E - 1)];  // unconditional: one wait
 #pragma unroll
-  for (int i = 0; i < TOPK_MAX_PER_LANE; i++) {
+  for (int i = 0; i < SLOTS; i++) {
     const int e = lane + 64 * i;
     key[i] = e < E ? (((uint64_t)logit_order_bits(zv[i]) << 32) | (uint32_t)~e) : 0ull;
   }
   for (int r = 0; r < k; r++) {
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < TOPK_MAX_PER_LANE; i++) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < SLOTS; i++) best = key[i] > best ? key[i] : best;
     best = wave_max_u64(best);
 #pragma unroll
-    for (int i = 0; i < TOPK_MAX_PER_LANE; i++)
+    for (int i = 0; i < SLOTS; i++)
       if (key[i] == best) key[i] = 0;
     if (lane == 0) {
       out_idx[r] = (int)~(uint32_t)best;
       out_z[r] = logit_from_order_bits((uint32_t)(best >> 32));
     }
   }
+}
+
+// Wave maximum / minimum of a 32-bit unsigned value, returned to every lane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
+  const int ident = MAX ? 0 : -1;
+#define QMOE_DPP_STEP(CTRL, RM)                                                              \
+  {                                                                                          \
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, CTRL, RM, 0xf, false); \
+    v = MAX ? (o > v ? o : v) : (o < v ? o : v);                                             \
+  }
+  QMOE_DPP_STEP(0x111, 0xf)
+  QMOE_DPP_STEP(0x112, 0xf)
+  QMOE_DPP_STEP(0x114, 0xf)
+  QMOE_DPP_STEP(0x118, 0xf)
+  QMOE_DPP_STEP(0x142, 0xa)
+  QMOE_DPP_STEP(0x143, 0xc)
+#undef QMOE_DPP_STEP
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k with each lane's keys sorted first (a sorting network on (logit key
+// descending, expert ascending)), so a round only compares list heads: the
+// wave maximum of the heads' logit keys, then the smallest expert among the
+// heads that reach it; the winner's lane pops its head.  Same result as
+// wave_topk_n: largest logit first, equal logits to the smaller index.
+template <int SLOTS>
+__device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, int E, int k, int* out_idx,
+                                                 float* out_z) {
+  static_assert(SLOTS == 4 || SLOTS == 8, "network for 4 or 8 keys");
+  const int lane = threadIdx.x & 63;
+  uint32_t key[SLOTS];
+  int ex[SLOTS];
+  float zv[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; i++) zv[i] = zt[min(lane + 64 * i, E - 1)];  // unconditional: one wait
+#pragma unroll
+  for (int i = 0; i < SLOTS; i++) {
+    ex[i] = lane + 64 * i;
+    key[i] = ex[i] < E ? logit_order_bits(zv[i]) : 0u;
+  }
+  auto cx = [&](int i, int j) {  // put the better of slots i < j first
+    const bool swap = key[j] > key[i] || (key[j] == key[i] && ex[j] < ex[i]);
+    const uint32_t ki = key[i], kj = key[j];
+    const int ei = ex[i], ej = ex[j];
+    key[i] = swap ? kj : ki;
+    key[j] = swap ? ki : kj;
+    ex[i] = swap ? ej : ei;
+    ex[j] = swap ? ei : ej;
+  };
+  if constexpr (SLOTS == 4) {
+    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+  } else {
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(1, 2); cx(5, 6);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+  }
+  for (int r = 0; r < k; r++) {
+    const uint32_t best = wave_ext_u32<true>(key[0]);
+    const uint32_t cand = key[0] == best ? (uint32_t)ex[0] : 0xffffffffu;
+    const uint32_t win = wave_ext_u32<false>(cand);
+    if (cand == win) {  // this lane's head is taken
+#pragma unroll
+      for (int i = 0; i < SLOTS - 1; i++) {
+        key[i] = key[i + 1];
+        ex[i] = ex[i + 1];
+      }
+      key[SLOTS - 1] = 0u;
+    }
+    if (lane == 0) {
+      out_idx[r] = (int)win;
+      out_z[r] = logit_from_order_bits(best);
+    }
+  }
+}
+
+// Any E <= MAX_EXPERTS.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z) {
+  if (E <= 256)
+    wave_topk_sorted<4>(zt, E, k, out_idx, out_z);
+  else if (E <= 512)
+    wave_topk_sorted<8>(zt, E, k, out_idx, out_z);
+  else
+    wave_topk_n<TOPK_MAX_PER_LANE>(zt, E, k, out_idx, out_z);
 }
 
 // Mixing weights from the selected logits: sigmoid in double precision,
