@@ -221,6 +221,8 @@ struct DecodeWs {
 };
 struct PrefillWs {
   int32_t *counts, *offsets, *tile_start, *perm, *pos;
+  uint16_t* x16;
+  float *xs, *route_xs;
   void *H, *Hs;
   float *Ye, *Ysh;
 };
@@ -241,6 +243,9 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   }
   w.tile_start = (int32_t*)c.take((size_t)(E + 1) * 4);
   w.pos = (int32_t*)c.take(n * 4);
+  w.x16 = (uint16_t*)c.take((size_t)T * d * 2);
+  w.xs = (float*)c.take((size_t)T * 4);
+  w.route_xs = (float*)c.take(n * 4);
   w.H = c.take(n * f * 2);
   w.Ye = (float*)c.take(n * d * 4);
   if (has_shared) {
@@ -490,12 +495,15 @@ static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_
   P.perm = w.perm;
   P.pos = w.pos;
   P.wt = wt;
+  P.x16 = w.x16;
+  P.xs = w.xs;
+  P.route_xs = w.route_xs;
   P.H = w.H;
   P.Hs = w.Hs;
   P.Ye = w.Ye;
   P.Ysh = w.Ysh;
   P.y = y;
-  const int tile_m = x_dtype == MOE_BF16 ? PREFILL_BM : PREFILL_BM_SPLIT;
+  const int tile_m = PREFILL_BM;
   int pid = prof_begin("bucket", s);
   hipError_t e = launch_bucket(idx, T, k, E, w.counts, w.offsets, w.perm, w.pos, w.tile_start, tile_m, s);
   prof_end(pid, s);

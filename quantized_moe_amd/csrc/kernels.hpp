@@ -53,8 +53,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
 size_t decode_quant_bytes(int T, int k, int d, int f);
 
 // prefill.hip: grouped GEMMs + combine (bucketing already done).
-constexpr int PREFILL_BM = 64;        // M tile (bf16 activations)
-constexpr int PREFILL_BM_SPLIT = 32;  // M tile when fp32 activations are split in two
+constexpr int PREFILL_BM = 32;  // M tile of the grouped GEMMs (rows of one expert's bucket)
 struct PrefillLaunch {
   int E, d, f, k, T;
   int fmt_gate_up, fmt_down, fmt_shared, has_shared;
@@ -64,6 +63,9 @@ struct PrefillLaunch {
   int x_dtype;
   const int32_t *counts, *offsets, *tile_start, *perm, *pos;
   const float* wt;
+  uint16_t* x16;  // fp16 [T][d]: x times a per-token power of two
+  float* xs;      // [T]: that power of two
+  float* route_xs;  // [T*k]: the same at each route, in bucket order
   void* H;      // fp16 [T*k][f]
   void* Hs;     // fp16 [T][f]
   float* Ye;    // [T*k][d]

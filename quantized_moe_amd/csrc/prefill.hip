@@ -1,74 +1,126 @@
-// Prefill path: grouped GEMMs over token buckets on bf16/fp16 MFMA.
+// Prefill path: grouped GEMMs over token buckets on fp16 MFMA.
 //
 // "YoungAi -- DeepSeek V4.1 Flash on one DGX Spark", section 4.4 runs prefill
 // experts on 16-bit matrix units and keeps every product exact by feeding
-// codewords that convert to bf16 without rounding.  The same idea on gfx950:
-// every B fragment handed to v_mfma is an exact small integer (IQ2: (2s+1) *
-// grid value <= 217; Q2K: sc * q <= 45), the fp16 superblock scales are applied
-// in an fp32 epilogue once per 256 inputs, and Q2K's min term is a second,
-// K=16 MFMA against per-sub-block sums of the A rows.  Q8 weights (the shared
-// expert) enter as an exact two-term split d*q = hi + lo.  A operands: bf16
-// activations as given; fp32 activations as bf16 hi + lo (two MFMAs); the
-// SwiGLU output h as fp16 (one rounding, relative 2^-11).
+// codewords that convert to 16-bit floats without rounding.  The same idea on
+// gfx950, with fp16 operands throughout:
+//   * every B fragment handed to v_mfma is an exact small integer (IQ2:
+//     (2s+1) * grid value <= 217; Q2K: sc * q <= 45), the fp16 superblock
+//     scales are applied in an fp32 epilogue once per 256 inputs, and Q2K's
+//     min term is a second, K=16 MFMA against per-sub-block sums of the A rows;
+//     Q8 weights (the shared expert) enter as an exact two-term split
+//     d*q = hi + lo;
+//   * the activations x are converted once to fp16 with a per-token power of
+//     two (exact) that puts max|x_t| in [2^13, 2^14), undone in the gate/up
+//     epilogue; the SwiGLU output h is stored as fp16 (one rounding, 2^-11).
 //
-// One persistent kernel serves all four GEMMs (routed gate/up, routed down,
-// shared gate/up, shared down).  A work item is (M tile of one expert's
-// bucket, N tile of 128 output rows); 8 waves own 16 output rows each and all
-// M sub-tiles, so each decoded B fragment feeds up to BM/16 MFMAs.  Tiles are
-// read from device memory (no host round trip).  Work items are mapped so
-// that all N tiles of an M tile run on one XCD and share its L2.
+// One persistent kernel per GEMM (routed gate/up, routed down, shared gate/up,
+// shared down).  A work item is (M tile of 32 rows of one expert's bucket, N
+// tile of 128 output rows): 8 waves own 16 output rows each and both 16-row
+// M sub-tiles, so each decoded B fragment feeds up to two MFMAs per matrix.
+// The K loop runs over 256-input superblocks and is software-pipelined across
+// work items: every wave keeps its weight loads PD superblocks ahead in
+// registers, the A rows of the next superblock are loaded while the current
+// one is computed and land in the other half of an LDS double buffer, and one
+// barrier per superblock separates the two.  Work items are mapped so that all
+// N tiles of an M tile run on one XCD and share its L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qmoe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum : int { AT_BF16 = 0, AT_F16 = 1 };
-
-constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_PAIRS = 8;              // wave pairs: 16 output rows each
+constexpr int GEMM_WAVES = 2 * GEMM_PAIRS;  // the two waves of a pair take the two halves of K
 constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-constexpr int GEMM_BN = 16 * GEMM_WAVES;  // output rows per work item
-constexpr int A_STRIDE = 256 + 8;         // LDS row stride of the A tile (elements)
+constexpr int GEMM_BN = 16 * GEMM_PAIRS;    // output rows per work item
+constexpr int BM = PREFILL_BM;            // M rows per work item
+constexpr int NSUB = BM / 16;             // 16-row MFMA sub-tiles
+constexpr int A_PIECES = BM * 32;         // 16-byte pieces of one A superblock chunk
+constexpr int A_ROW = 33 * 16;            // LDS bytes per A row (32 pieces + one of padding)
+constexpr int A_BUF = BM * A_ROW;         // LDS bytes per A buffer
+constexpr int TAB_COPIES = 16;            // LDS table copies (one per lane of a 16-lane row)
 
-template <int AT>
 __device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
-  if constexpr (AT == AT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
-                                                  0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
 }
-
-template <int AT>
 __device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
-  if constexpr (AT == AT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
-                                                     c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
-                                                 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                               0, 0);
 }
 
-// fp32 -> 16-bit value of the A/B type (round to nearest even).
-template <int AT>
-__device__ __forceinline__ uint32_t to16(float v) {
-  if constexpr (AT == AT_BF16)
-    return __builtin_bit_cast(uint16_t, (__bf16)v);
-  else
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
+// fp32 -> fp16 bits (round to nearest even) and back
+__device__ __forceinline__ uint32_t to_h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+__device__ __forceinline__ float from_h(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+
+// two fp16 lanes times two fp16 lanes
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
 }
-template <int AT>
-__device__ __forceinline__ float from16(uint32_t b) {
-  if constexpr (AT == AT_BF16)
-    return __uint_as_float(b << 16);
-  else
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+
+// ---------------------------------------------------------------------------
+// x -> fp16 with a per-token power-of-two scale
+// ---------------------------------------------------------------------------
+// x16[t][i] = fp16(x[t][i] * 2^-e_t), xs[t] = 2^e_t, with e_t such that
+// max_i |x[t][i]| * 2^-e_t lies in [2^13, 2^14) (e_t = 0 for a zero or
+// non-finite row), and route_xs[pos[t][j]] = 2^e_t for the token's k routes.
+// The scaling is exact; the fp16 rounding is the only error.
+__global__ __launch_bounds__(256) void x16_kernel(const void* __restrict__ x, int x_dtype, int d,
+                                                  uint16_t* __restrict__ x16, float* __restrict__ xs,
+                                                  const int32_t* __restrict__ pos, int k,
+                                                  float* __restrict__ route_xs) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  auto load4 = [&](int i, float* v) {
+    if (x_dtype == X_BF16) {
+      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + (int64_t)t * d + i);
+      v[0] = __uint_as_float(b.x << 16);
+      v[1] = __uint_as_float(b.x & 0xffff0000u);
+      v[2] = __uint_as_float(b.y << 16);
+      v[3] = __uint_as_float(b.y & 0xffff0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + (int64_t)t * d + i);
+      v[0] = f.x;
+      v[1] = f.y;
+      v[2] = f.z;
+      v[3] = f.w;
+    }
+  };
+  float m = 0.0f;
+  for (int i = 4 * tid; i < d; i += 1024) {
+    float v[4];
+    load4(i, v);
+#pragma unroll
+    for (int u = 0; u < 4; u++) m = fmaxf(m, fabsf(v[u]));
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int e = 0;
+  if (m > 0.0f && m <= 3.4e38f) {
+    int ex;
+    frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+    e = ex - 14;
+  }
+  const float sc = ldexpf(1.0f, -e);
+  for (int i = 4 * tid; i < d; i += 1024) {
+    float v[4];
+    load4(i, v);
+    const uint2 h = make_uint2(to_h(v[0] * sc) | (to_h(v[1] * sc) << 16), to_h(v[2] * sc) | (to_h(v[3] * sc) << 16));
+    *reinterpret_cast<uint2*>(x16 + (int64_t)t * d + i) = h;
+  }
+  if (tid == 0) xs[t] = ldexpf(1.0f, e);
+  // the same scale at each of the token's routes in bucket order
+  if (tid < k) route_xs[pos[(int64_t)t * k + tid]] = ldexpf(1.0f, e);
 }
 
 // ---------------------------------------------------------------------------
@@ -77,9 +129,9 @@ __device__ __forceinline__ float from16(uint32_t b) {
 struct GemmArgs {
   QMat B0, B1;                 // B0 = gate (or down), B1 = up (gate/up only)
   const uint8_t* grid;         // IQ2 grid [256][8]
-  // A operand source
-  const void* a_src;           // x (gate/up) or H (down)
-  int a_dtype;                 // X_BF16 / X_F32 for x; H is always fp16
+  const uint16_t* a16;         // fp16 A rows: x16 [T][K] (gate/up) or H [rows][K] (down)
+  int a16_bytes;               // size of a16 (below 2^31)
+  const float* rowxs;          // gate/up: scale of x16 for each row of the row space
   int K;                       // inputs (d for gate/up, f for down)
   int N;                       // output rows (f for gate/up, d for down)
   // grouping
@@ -97,93 +149,103 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // LDS tables (built once per persistent block)
 // ---------------------------------------------------------------------------
-// IQ2: t1[s][row] = 8 x 16-bit (2s+1)*grid[row][p]; sgn[b7] = XOR masks for
-// the 7 stored signs plus the parity sign.
-template <int AT>
-__device__ void build_iq2_tables(const uint8_t* grid, uint4* t1, uint4* sgn) {
-  for (int e = threadIdx.x; e < 16 * 256; e += blockDim.x) {
-    const int s = e >> 8, row = e & 255;
+// IQ2: tm[row][s] = the 8 grid magnitudes of row times (2s+1) as fp16 (exact
+// integers <= 217), 16 bytes, row stride 256 bytes: the byte address
+// row << 8 | s << 4 is one v_perm of the payload word and s << 4.
+// sgn[b7][c] = XOR masks of the 7 stored signs plus the parity sign, stored
+// TAB_COPIES times (copy c at bank quad c); lane l reads copy l % 16, so the
+// 16 lanes of a row never meet in a bank whatever patterns they look up.
+constexpr int IQ2_TM_BYTES = 256 * 16 * 16;
+constexpr int IQ2_SGN_BYTES = 128 * TAB_COPIES * 16;
+__device__ void build_iq2_tables(const uint8_t* grid, uint4* tm, uint4* sgn) {
+  for (int e = threadIdx.x; e < 256 * 16; e += blockDim.x) {
+    const int row = e >> 4, sc = 2 * (e & 15) + 1;
     const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * row);
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const uint32_t word = i < 2 ? g.x : g.y;
-      const float v0 = (float)((2 * s + 1) * ((word >> (16 * (i & 1))) & 255u));
-      const float v1 = (float)((2 * s + 1) * ((word >> (16 * (i & 1) + 8)) & 255u));
-      w[i] = to16<AT>(v0) | (to16<AT>(v1) << 16);
+      const uint32_t v0 = (word >> (16 * (i & 1))) & 255u, v1 = (word >> (16 * (i & 1) + 8)) & 255u;
+      w[i] = to_h((float)(sc * v0)) | (to_h((float)(sc * v1)) << 16);
     }
-    t1[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    tm[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  for (int b = threadIdx.x; b < 128; b += blockDim.x) {
+  for (int e = threadIdx.x; e < 128 * TAB_COPIES; e += blockDim.x) {
+    const uint32_t b = e / TAB_COPIES;
     const uint32_t s8 = b | ((__popc(b) & 1u) << 7);
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) w[i] = (((s8 >> (2 * i)) & 1u) << 15) | (((s8 >> (2 * i + 1)) & 1u) << 31);
-    sgn[b] = make_uint4(w[0], w[1], w[2], w[3]);
+    sgn[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
-// Q2K: tqs[sc][byte] = 4 x 16-bit sc * q_i for the four 2-bit quants of byte.
-template <int AT>
+// Q2K: tqs[sc][byte] = 4 x fp16 sc * q_i for the four 2-bit quants of byte.
 __device__ void build_q2k_table(uint2* tqs) {
   for (int e = threadIdx.x; e < 16 * 256; e += blockDim.x) {
     const int sc = e >> 8, b = e & 255;
     uint32_t v[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = to16<AT>((float)(sc * ((b >> (2 * i)) & 3)));
+    for (int i = 0; i < 4; i++) v[i] = to_h((float)(sc * ((b >> (2 * i)) & 3)));
     tqs[e] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
   }
 }
 
 // ---------------------------------------------------------------------------
-// B operand: one lane's weight row, one superblock (256 inputs) at a time.
+// B operand: one lane's weight row, half a superblock at a time.
 //
 // K order inside a superblock.  MFMA sums over K, so any permutation of the
 // 256 inputs applied to A and B alike gives the same product.  At k32 step q
 // lane group g4 = lane / 16 takes inputs 64*g4 + 8*q .. +7 (not the natural
-// 32*q + 8*g4): each lane then needs one contiguous slice of the block --
-// 16 bytes of IQ2 payload or Q2K quants, 64 bytes of Q8 quants -- and every
-// field index below is a compile-time constant.
+// 32*q + 8*g4): each lane then needs one contiguous slice of the block and
+// every field index below is a compile-time constant.  The two waves of a
+// pair split the steps: half h runs q = 4h .. 4h+3, i.e. inputs
+// 64*g4 + 32*h .. +31 -- one IQ2 or Q8 sub-block, two Q2K sub-blocks -- and
+// loads only that slice.  The A rows are laid out in LDS with the same
+// permutation (16-byte piece 8*g4 + q).
 // ---------------------------------------------------------------------------
 template <int FMT>
 struct BRegs;
 
+// load(m, row0, lrow, sb, g4, h): row0 is wave-uniform (the item's first
+// row), lrow the lane's row within it; the uniform part of every address is
+// formed apart so it stays in scalar registers.
 template <>
 struct BRegs<FMT_IQ2> {
-  uint4 p;  // (A, B) words of sub-blocks 2*g4 and 2*g4 + 1
-  float d;
-  __device__ __forceinline__ void load(const QMat& m, int64_t row, int sb, int g4) {
-    p = ld16_stream(m.p_a + (row * m.nb + sb) * 64 + 16 * g4);
-    d = half_bits_to_float(reinterpret_cast<const uint16_t*>(m.p_scale)[row * m.nb + sb]);
+  uint2 p;     // (A, B) words of sub-block 2*g4 + h
+  uint32_t d;  // fp16 bits of the superblock scale
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
+    const uint8_t* base = m.p_a + (row0 * m.nb + sb) * 64;
+    p = *reinterpret_cast<const uint2*>(base + (uint32_t)(lrow * m.nb * 64 + 16 * g4 + 8 * h));
+    const uint16_t* sbase = reinterpret_cast<const uint16_t*>(m.p_scale) + row0 * m.nb + sb;
+    d = sbase[(uint32_t)(lrow * m.nb)];
   }
 };
 
 template <>
 struct BRegs<FMT_Q2K> {
-  uint4 q;      // quant bytes 16*g4 .. +15 (inputs 64*g4 .. +63)
+  uint2 q;      // quant bytes 16*g4 + 8*h .. +7 (inputs 64*g4 + 32*h .. +31)
   uint32_t sc;  // scale/min bytes of sub-blocks 4*g4 .. +3
-  float d, dmin;
-  __device__ __forceinline__ void load(const QMat& m, int64_t row, int sb, int g4) {
-    const int64_t blk = row * m.nb + sb;
-    q = ld16_stream(m.p_b + blk * 64 + 16 * g4);
-    sc = *reinterpret_cast<const uint32_t*>(m.p_a + blk * 16 + 4 * g4);
-    const uint32_t dm = *reinterpret_cast<const uint32_t*>(m.p_scale + blk * 4);
-    d = half_bits_to_float(dm & 0xffffu);
-    dmin = half_bits_to_float(dm >> 16);
+  uint32_t dm;  // fp16 d | fp16 dmin << 16
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
+    const int64_t blk0 = row0 * m.nb + sb;
+    const uint32_t lb = (uint32_t)(lrow * m.nb);
+    q = *reinterpret_cast<const uint2*>(m.p_b + blk0 * 64 + (lb * 64 + 16 * g4 + 8 * h));
+    sc = *reinterpret_cast<const uint32_t*>(m.p_a + blk0 * 16 + (lb * 16 + 4 * g4));
+    dm = *reinterpret_cast<const uint32_t*>(m.p_scale + blk0 * 4 + lb * 4);
   }
 };
 
 template <>
 struct BRegs<FMT_Q8> {
-  uint4 q[4];  // quants of blocks 2*g4 and 2*g4 + 1 of the superblock (64 bytes)
-  float d[2];
-  __device__ __forceinline__ void load(const QMat& m, int64_t row, int sb, int g4) {
-    const int64_t blk = row * m.nb + sb * 8 + 2 * g4;
-#pragma unroll
-    for (int i = 0; i < 4; i++) q[i] = ld16_stream(m.p_a + blk * 32 + 16 * i);
-    const uint32_t dd = *reinterpret_cast<const uint32_t*>(m.p_scale + blk * 2);
-    d[0] = half_bits_to_float(dd & 0xffffu);
-    d[1] = half_bits_to_float(dd >> 16);
+  uint4 q[2];  // quants of block 2*g4 + h of the superblock (32 bytes)
+  uint32_t d;  // its fp16 scale
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
+    const int64_t blk0 = row0 * m.nb + sb * 8;
+    const uint32_t lb = (uint32_t)(lrow * m.nb + 2 * g4 + h);
+    q[0] = ld16_stream(m.p_a + blk0 * 32 + lb * 32);
+    q[1] = ld16_stream(m.p_a + blk0 * 32 + lb * 32 + 16);
+    d = reinterpret_cast<const uint16_t*>(m.p_scale)[blk0 + lb];
   }
 };
 
@@ -191,55 +253,60 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;  // i is a compile-time constant
 }
 
-// Fragment of k32 step q: 8 exact integers for inputs 64*g4 + 8q .. +7.
-template <int AT>
-__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2>& b, int q, const uint4* t1, const uint4* sgn) {
-  const uint32_t A = q < 4 ? b.p.x : b.p.z;
-  const uint32_t B = q < 4 ? b.p.y : b.p.w;
-  const int i = q & 3;  // group inside the sub-block
-  const uint32_t row = (A >> (8 * i)) & 255u;
-  const uint32_t sg = (B >> (7 * i)) & 127u;
-  const uint4 mag = t1[((B >> 28) << 8) | row];
-  const uint4 sm = sgn[sg];
-  return make_uint4(mag.x ^ sm.x, mag.y ^ sm.y, mag.z ^ sm.z, mag.w ^ sm.w);
+// IQ2 sub-block scale s (the top nibble of its B word) as s << 4
+__device__ __forceinline__ uint32_t iq2_scale16(uint32_t bword) { return (bword >> 24) & 0xf0u; }
+
+// Fragment of local step i (q = 4h + i): 8 exact integers, group i of the
+// lane's sub-block.  S16 = iq2_scale16 of the sub-block, CB = (lane % 16) << 4.
+__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2>& b, int i, uint32_t S16, uint32_t CB,
+                                          const uint8_t* tm, const uint8_t* sgn) {
+  const uint32_t A = b.p.x, B = b.p.y;
+  // row << 8 | s << 4: byte 0 from S16, byte 1 = byte i of A
+  const uint32_t maddr = __builtin_amdgcn_perm(A, S16, 0x0c0c0000u | ((4u + i) << 8));
+  // (7 sign bits) << 8 | copy << 4
+  const uint32_t sh = i == 0 ? (B << 8) : i == 1 ? (B << 1) : i == 2 ? (B >> 6) : (B >> 13);
+  const uint32_t saddr = (sh & 0x7f00u) | CB;
+  const uint4 m = *reinterpret_cast<const uint4*>(tm + maddr);
+  const uint4 s = *reinterpret_cast<const uint4*>(sgn + saddr);
+  return make_uint4(m.x ^ s.x, m.y ^ s.y, m.z ^ s.z, m.w ^ s.w);
 }
 
-template <int AT>
-__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K>& b, int q, const uint2* tqs) {
-  const uint32_t hw = (word_of(b.q, q >> 1) >> (16 * (q & 1))) & 0xffffu;  // quant bytes 2q, 2q+1
-  const uint32_t sc = (b.sc >> (8 * (q >> 1))) & 15u;                       // sub-block 4*g4 + q/2
-  const uint2 lo = tqs[(sc << 8) | (hw & 255u)];
-  const uint2 hi = tqs[(sc << 8) | (hw >> 8)];
+// Q2K fragment of local step i: quant bytes 2i, 2i+1 of the lane's 8, whose
+// sub-block scale is sc (SC = sc << 16); lookup byte address of quant byte x
+// is (sc << 8 | x) << 3 = perm(word, SC) >> 5 with x placed in byte 1.
+__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K>& b, int i, uint32_t SC, const uint8_t* tqs) {
+  const uint32_t w = (i >> 1) ? b.q.y : b.q.x;
+  const int x0 = 2 * (i & 1);  // quant bytes x0, x0 + 1 of word w
+  const uint32_t a0 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((4u + x0) << 8)) >> 5;
+  const uint32_t a1 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((5u + x0) << 8)) >> 5;
+  const uint2 lo = *reinterpret_cast<const uint2*>(tqs + a0);
+  const uint2 hi = *reinterpret_cast<const uint2*>(tqs + a1);
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // Q2K min-term B fragment (K = the 16 sub-blocks): m_j for j = 4*g4 .. +3,
 // which are exactly the high nibbles of this lane's scale word.
-template <int AT>
 __device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K>& b) {
   const uint32_t w = b.sc;
   const uint32_t m0 = (w >> 4) & 15u, m1 = (w >> 12) & 15u, m2 = (w >> 20) & 15u, m3 = (w >> 28) & 15u;
-  return make_uint2(to16<AT>((float)m0) | (to16<AT>((float)m1) << 16),
-                    to16<AT>((float)m2) | (to16<AT>((float)m3) << 16));
+  return make_uint2(to_h((float)m0) | (to_h((float)m1) << 16), to_h((float)m2) | (to_h((float)m3) << 16));
 }
 
-// Q8: d*q split into two 16-bit terms hi + lo (16 significant bits for bf16,
-// 22 for fp16; the exact product of an 8-bit quant and an 11-bit scale has 19).
-template <int AT>
-__device__ __forceinline__ void q8_frag(const BRegs<FMT_Q8>& b, int q, uint4& hi, uint4& lo) {
-  const int blk = q >> 2;            // block 2*g4 + blk
-  const int w0 = 2 * (q & 3);        // its dwords w0, w0 + 1
-  const uint32_t w2[2] = {word_of(b.q[2 * blk + (w0 >> 2)], w0 & 3), word_of(b.q[2 * blk + ((w0 + 1) >> 2)], (w0 + 1) & 3)};
-  const float d = b.d[blk];
+// Q8 fragment of local step i: d*q split into two fp16 terms hi + lo (22
+// significant bits; the exact product of an 8-bit quant and an 11-bit scale
+// has 19).
+__device__ __forceinline__ void q8_frag(const BRegs<FMT_Q8>& b, int i, uint4& hi, uint4& lo) {
+  const uint32_t w2[2] = {word_of(b.q[i >> 1], 2 * (i & 1)), word_of(b.q[i >> 1], 2 * (i & 1) + 1)};
+  const float d = from_h(b.d);
   uint32_t h[4], l[4];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint32_t word = w2[i >> 1];
-    const float v0 = d * (float)(int8_t)((word >> (16 * (i & 1))) & 255u);
-    const float v1 = d * (float)(int8_t)((word >> (16 * (i & 1) + 8)) & 255u);
-    const uint32_t h0 = to16<AT>(v0), h1 = to16<AT>(v1);
-    h[i] = h0 | (h1 << 16);
-    l[i] = to16<AT>(v0 - from16<AT>(h0)) | (to16<AT>(v1 - from16<AT>(h1)) << 16);
+  for (int j = 0; j < 4; j++) {
+    const uint32_t word = w2[j >> 1];
+    const float v0 = d * (float)(int8_t)((word >> (16 * (j & 1))) & 255u);
+    const float v1 = d * (float)(int8_t)((word >> (16 * (j & 1) + 8)) & 255u);
+    const uint32_t h0 = to_h(v0), h1 = to_h(v1);
+    h[j] = h0 | (h1 << 16);
+    l[j] = to_h(v0 - from_h(h0)) | (to_h(v1 - from_h(h1)) << 16);
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -248,243 +315,430 @@ __device__ __forceinline__ void q8_frag(const BRegs<FMT_Q8>& b, int q, uint4& hi
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int FMT, int AT, bool XSPLIT, bool GATEUP, int BM>
+template <int FMT, bool GATEUP>
 struct GemmLds {
-  static constexpr int kT1 = FMT == FMT_IQ2 ? 16 * 256 * 16 + 128 * 16 : 0;
-  static constexpr int kTQS = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
-  static constexpr int kA = BM * A_STRIDE * 2 * (XSPLIT ? 2 : 1);
-  static constexpr int kS = FMT == FMT_Q2K ? BM * 16 * 2 * 2 : 0;  // hi, lo
-  static constexpr int kTok = BM * 4;
-  static constexpr int kTiles = (MAX_EXPERTS + 1) * 4;
-  static constexpr int bytes = kT1 + kTQS + kA + kS + kTok + kTiles;
+  static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
+  static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
+  static constexpr int kTqs = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
+  static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
+  static constexpr int kS = FMT == FMT_Q2K ? 2 * 2 * BM * 16 * 2 : 0;  // Q2K sub-block sums: [buf][hi/lo][BM][16]
+  static constexpr int kTok = GATEUP ? 3 * BM * 8 : 0;                // token and scale of each row, 3 items
+  static constexpr int kRed = NSUB * 4 * GEMM_PAIRS * 64 * 4;          // one matrix's partial sums of the second halves
+  static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oA = oTqs + kTqs, oS = oA + kA, oTok = oS + kS,
+                       oRed = oTok + kTok, oTiles = oRed + kRed;
+  // then tile_start, counts, offsets of the routed experts: [3][E + 1]
+  static constexpr int bytes_for(int E) { return oTiles + 3 * (E + 1) * 4; }
 };
 
-template <int FMT, int AT, bool XSPLIT, bool GATEUP, int BM>
+// A work item's rows.
+struct Item {
+  int e;       // expert (0 for the shared expert)
+  int nt;      // N tile
+  int rows;    // valid rows (0: no item)
+  int p0;      // first row of the item in the bucket-ordered row space
+  int nm;      // active 16-row sub-tiles
+};
+
+template <int FMT, bool GATEUP, int PD>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
-  using L = GemmLds<FMT, AT, XSPLIT, GATEUP, BM>;
+  using L = GemmLds<FMT, GATEUP>;
   extern __shared__ __align__(16) uint8_t lds[];
-  uint4* t1 = reinterpret_cast<uint4*>(lds);
-  uint4* sgn = t1 + 16 * 256;
-  uint2* tqs = reinterpret_cast<uint2*>(lds + L::kT1);
-  uint16_t* sA = reinterpret_cast<uint16_t*>(lds + L::kT1 + L::kTQS);
-  uint16_t* sAlo = sA + BM * A_STRIDE;
-  uint16_t* sS = reinterpret_cast<uint16_t*>(lds + L::kT1 + L::kTQS + L::kA);  // [BM][16] hi, then lo
-  int* sTok = reinterpret_cast<int*>(lds + L::kT1 + L::kTQS + L::kA + L::kS);
-  int* sTiles = sTok + BM;
+  const uint8_t* tm = lds;
+  const uint8_t* sgn = lds + L::oSgn;
+  const uint8_t* tqs = lds + L::oTqs;
+  uint8_t* sA = lds + L::oA;
+  uint16_t* sS = reinterpret_cast<uint16_t*>(lds + L::oS);
+  int* sTok = reinterpret_cast<int*>(lds + L::oTok);              // [3][BM]
+  float* sXs = reinterpret_cast<float*>(lds + L::oTok) + 3 * BM;  // [3][BM]
+  float* sRed = reinterpret_cast<float*>(lds + L::oRed);
+  int* sTiles = reinterpret_cast<int*>(lds + L::oTiles);
+  int* sCounts = sTiles + (a.E + 1);
+  int* sOffsets = sCounts + (a.E + 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = wave % GEMM_PAIRS;  // output rows 16 wv .. of the N tile
+  const int h = wave / GEMM_PAIRS;   // K half: steps q = 4h .. 4h + 3 of every superblock
   const int g4 = lane >> 4, c16 = lane & 15;
 
-  if constexpr (FMT == FMT_IQ2) build_iq2_tables<AT>(a.grid, t1, sgn);
-  if constexpr (FMT == FMT_Q2K) build_q2k_table<AT>(tqs);
-  int total_tiles;
+  if constexpr (FMT == FMT_IQ2) build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn));
+  if constexpr (FMT == FMT_Q2K) build_q2k_table(reinterpret_cast<uint2*>(lds + L::oTqs));
   if (a.routed) {
-    for (int i = tid; i <= a.E; i += GEMM_THREADS) sTiles[i] = a.tile_start[i];
-    __syncthreads();
-    total_tiles = sTiles[a.E];
-  } else {
-    __syncthreads();
-    total_tiles = (a.n_rows + BM - 1) / BM;
+    for (int i = tid; i <= a.E; i += GEMM_THREADS) {
+      sTiles[i] = a.tile_start[i];
+      sOffsets[i] = a.offsets[i];
+      sCounts[i] = i < a.E ? a.counts[i] : 0;
+    }
   }
+  __syncthreads();
+  const int total_tiles = a.routed ? sTiles[a.E] : (a.n_rows + BM - 1) / BM;
   const int NT = a.N / GEMM_BN;
   const int nsb = a.K / 256;
 
   // work-item mapping: XCD-aware when there are enough M tiles
   const int nblk = gridDim.x;
   const bool xcd_map = total_tiles >= 16 && (nblk % 8) == 0;
-  const int xcd = blockIdx.x % 8, lb = blockIdx.x / 8, nbx = nblk / 8;
+  const int xcd = blockIdx.x % 8;
   const int n_items = xcd_map ? ((total_tiles - xcd + 7) / 8) * NT : total_tiles * NT;
-  const int first = xcd_map ? lb : blockIdx.x;
-  const int step = xcd_map ? nbx : nblk;
+  const int first = xcd_map ? blockIdx.x / 8 : blockIdx.x;
+  const int step = xcd_map ? nblk / 8 : nblk;
+  const int cnt = first < n_items ? (n_items - first + step - 1) / step : 0;
+  if (cnt == 0) return;  // uniform over the block
 
-  for (int it = first; it < n_items; it += step) {
-    const int mt = it / NT, nt = it % NT;
+  // item j of this block
+  auto item = [&](int j) {
+    Item it;
+    if (j >= cnt) {
+      it.e = it.nt = it.rows = it.p0 = it.nm = 0;
+      return it;
+    }
+    const int g = first + j * step;
+    const int mt = g / NT;
+    it.nt = g - mt * NT;
     const int tt = xcd_map ? xcd + 8 * mt : mt;
-    // which expert / rows
-    int e = 0, m0, rows, p0;
     if (a.routed) {
       int lo = 0, hi = a.E;  // largest e with tile_start[e] <= tt
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (sTiles[mid] <= tt) lo = mid; else hi = mid;
       }
-      // skip experts with zero tiles that share the same start
-      e = lo;
-      while (e + 1 < a.E && sTiles[e + 1] <= tt) e++;
-      m0 = (tt - sTiles[e]) * BM;
-      rows = min(BM, a.counts[e] - m0);
-      p0 = a.offsets[e] + m0;
+      int e = lo;
+      while (e + 1 < a.E && sTiles[e + 1] <= tt) e++;  // skip experts with no tiles
+      const int m0 = (tt - sTiles[e]) * BM;
+      it.e = e;
+      it.rows = min(BM, sCounts[e] - m0);
+      it.p0 = sOffsets[e] + m0;
     } else {
-      m0 = tt * BM;
-      rows = min(BM, a.n_rows - m0);
-      p0 = m0;
+      const int m0 = tt * BM;
+      it.e = 0;
+      it.rows = min(BM, a.n_rows - m0);
+      it.p0 = m0;
     }
-    const int nm = (rows + 15) >> 4;  // active 16-row sub-tiles
-    if (GATEUP) {
-      for (int i = tid; i < rows; i += GEMM_THREADS) sTok[i] = a.routed ? a.perm[p0 + i] / a.k : p0 + i;
+    it.nm = (it.rows + 15) >> 4;
+    // every lane computed the same item: say so, so it lives in SGPRs
+    it.e = __builtin_amdgcn_readfirstlane(it.e);
+    it.nt = __builtin_amdgcn_readfirstlane(it.nt);
+    it.rows = __builtin_amdgcn_readfirstlane(it.rows);
+    it.p0 = __builtin_amdgcn_readfirstlane(it.p0);
+    it.nm = __builtin_amdgcn_readfirstlane(it.nm);
+    return it;
+  };
+  // gate/up: token index and x scale of each row of item j, into slot j % 3.
+  // In the steady state the two loads are issued one item ahead (tok_issue)
+  // and written to LDS an item later (tok_commit), so no step waits for them.
+  int tok_r = 0;
+  float xs_r = 0.0f;
+  auto tok_issue = [&](const Item& it) {
+    if constexpr (GATEUP) {
+      const int i = tid % BM;  // every thread loads (uniform load count per step)
+      const int p = it.p0 + (i < it.rows ? i : 0);
+      tok_r = a.routed ? a.perm[p] : p;
+      xs_r = a.rowxs[p];
     }
-    __syncthreads();
+  };
+  auto tok_commit = [&](int j) {
+    if constexpr (GATEUP) {
+      if (tid < BM) {
+        sTok[(j % 3) * BM + tid] = a.routed ? tok_r / a.k : tok_r;
+        sXs[(j % 3) * BM + tid] = xs_r;
+      }
+    }
+  };
 
-    const int n = nt * GEMM_BN + wave * 16 + c16;  // this lane's output row (B column)
-    const int64_t brow = (int64_t)e * a.B0.rows + n;
+  // ---- A rows: issue (into registers) and store (into LDS) ----
+  // Thread tid holds piece tid: row tid / 32, piece tid % 32, stored at byte
+  // row * A_ROW + 16 * piece.  The row stride of 33 pieces puts the 16 rows an
+  // MFMA operand read touches in 16 different bank quads, and the piece of
+  // k32 step q is an immediate offset.  A loads are raw buffer loads: a piece
+  // outside the item's active rows is given an offset past the end of a16 and
+  // reads as zero, so every step issues the same loads.
+  static_assert(A_PIECES == GEMM_THREADS, "one A piece per thread");
+  // DA superblocks of A in flight in registers (set s % 2 holds superblock s)
+  constexpr int DA = PD % 2 == 0 ? 2 : 1;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.a16), (short)0, a.a16_bytes, 0x00020000);
+  const int a_row = tid >> 5, a_piece = tid & 31;
+  uint4 av0, av1;              // sets 0 and 1
+  int ap0 = -1, ap1 = -1;      // their LDS byte offset, -1 if inactive
+  auto issue_piece = [&](int j, const Item& it, int sb, uint4& v, int& pos) {
+    const bool active = a_row < 16 * it.nm;
+    int src;
+    if constexpr (GATEUP) {
+      src = sTok[(j % 3) * BM + a_row];
+    } else {
+      src = it.p0 + (a_row < it.rows ? a_row : 0);
+    }
+    const int off = active ? (src * a.K + sb * 256 + 8 * a_piece) * 2 : 0x7ffffff0;
+    const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0);
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+    pos = active ? a_row * A_ROW + 16 * a_piece : -1;
+  };
+  // (a branch on set, not a reference chosen by it: the sets stay in registers)
+  auto issueA = [&](int set, int j, const Item& it, int sb) {
+    if (set) issue_piece(j, it, sb, av1, ap1);
+    else issue_piece(j, it, sb, av0, ap0);
+  };
+  auto store_piece = [&](int buf, const uint4& v, int pos) {
+    uint8_t* dst = sA + buf * A_BUF;
+    if (pos >= 0) *reinterpret_cast<uint4*>(dst + pos) = v;
+    if constexpr (FMT == FMT_Q2K) {
+      // sub-block sums (16 inputs = pieces 2j, 2j+1, held by lanes t, t^1)
+      const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+      float sum = 0.0f;
+      sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v.x), one, sum, false);
+      sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v.y), one, sum, false);
+      sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v.z), one, sum, false);
+      sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v.w), one, sum, false);
+      if (pos < 0) sum = 0.0f;
+      const float o = __shfl_xor(sum, 1, 64);
+      if (pos >= 0 && (a_piece & 1) == 0) {
+        const float t = sum + o;
+        const uint32_t hs = to_h(t);
+        uint16_t* ss = sS + buf * (2 * BM * 16);
+        ss[a_row * 16 + (a_piece >> 1)] = (uint16_t)hs;
+        ss[BM * 16 + a_row * 16 + (a_piece >> 1)] = (uint16_t)to_h(t - from_h(hs));
+      }
+    }
+  };
+  auto storeA = [&](int set, int buf) {
+    if (set) store_piece(buf, av1, ap1);
+    else store_piece(buf, av0, ap0);
+  };
 
-    f32x4_t acc0[BM / 16], acc1[BM / 16], sb0[BM / 16], sb1[BM / 16];
+  // ---- B rows: PD superblocks in flight ----
+  BRegs<FMT> b0[PD], b1[PD];
+  // B row of this lane: (first row of the item's N tile, uniform) + lrow
+  const int lrow = wv * 16 + c16;
+  auto issueB = [&](int slot, const Item& it, int sb) {
 #pragma unroll
-    for (int m = 0; m < BM / 16; m++) acc0[m] = acc1[m] = sb0[m] = sb1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < PD; s++) {
+      if (s == slot) {  // (an item past the end has rows 0 and e = nt = 0: in bounds, unused)
+        const int64_t row0 = (int64_t)it.e * a.B0.rows + it.nt * GEMM_BN;
+        b0[s].load(a.B0, row0, lrow, sb, g4, h);
+        if constexpr (GATEUP) b1[s].load(a.B1, row0, lrow, sb, g4, h);
+      }
+    }
+  };
 
-    for (int sb = 0; sb < nsb; sb++) {
-      // ---- stage the A tile (rows x 256 inputs) into LDS ----
-      if constexpr (GATEUP) {
-        if constexpr (XSPLIT) {
-          const float* x = static_cast<const float*>(a.a_src);
-          for (int s = tid; s < rows * 64; s += GEMM_THREADS) {
-            const int i = s >> 6, c = s & 63;
-            const float4 v = *reinterpret_cast<const float4*>(x + (int64_t)sTok[i] * a.K + sb * 256 + 4 * c);
-            const float f[4] = {v.x, v.y, v.z, v.w};
-            uint32_t h[4], l[4];
+  f32x4_t acc0[NSUB], acc1[NSUB];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-              h[u] = to16<AT>(f[u]);
-              l[u] = to16<AT>(f[u] - from16<AT>(h[u]));
-            }
-            *reinterpret_cast<uint2*>(sA + i * A_STRIDE + 4 * c) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-            *reinterpret_cast<uint2*>(sAlo + i * A_STRIDE + 4 * c) =
-                make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+  for (int m = 0; m < NSUB; m++) acc0[m] = acc1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // One superblock half-step with NM (a compile-time 1 or 2) active
+  // sub-tiles: straight-line code, so the scheduler can overlap the table
+  // reads, the fragment arithmetic and the MFMAs of consecutive k32 steps.
+  auto compute = [&](auto nm_c, int slot, int buf) {
+    constexpr int NM = decltype(nm_c)::value;
+    const BRegs<FMT>& B0 = b0[slot];
+    const BRegs<FMT>& B1 = b1[slot];
+    const uint8_t* A = sA + buf * A_BUF + c16 * A_ROW + g4 * 128 + h * 64;
+    auto aread = [&](int m, int i) {
+      return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
+    };
+    if constexpr (FMT == FMT_Q8) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        uint4 f0, f0l, f1, f1l;
+        q8_frag(B0, i, f0, f0l);
+        if constexpr (GATEUP) q8_frag(B1, i, f1, f1l);
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          const uint4 av = aread(m, i);
+          acc0[m] = mfma32(av, f0, acc0[m]);
+          acc0[m] = mfma32(av, f0l, acc0[m]);
+          if constexpr (GATEUP) {
+            acc1[m] = mfma32(av, f1, acc1[m]);
+            acc1[m] = mfma32(av, f1l, acc1[m]);
           }
+        }
+      }
+    } else {
+      f32x4_t s0[NM], s1[NM];
+#pragma unroll
+      for (int m = 0; m < NM; m++) s0[m] = s1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint32_t CB = (uint32_t)c16 << 4;
+      uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
+      if constexpr (FMT == FMT_IQ2) {
+        S0 = iq2_scale16(B0.p.y);
+        if constexpr (GATEUP) S1 = iq2_scale16(B1.p.y);
+      } else {
+        sc0 = B0.sc >> (16 * h);  // scale bytes of sub-blocks 4*g4 + 2h, + 1
+        if constexpr (GATEUP) sc1 = B1.sc >> (16 * h);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        uint4 f0, f1;
+        if constexpr (FMT == FMT_IQ2) {
+          f0 = iq2_frag(B0, i, S0, CB, tm, sgn);
+          if constexpr (GATEUP) f1 = iq2_frag(B1, i, S1, CB, tm, sgn);
         } else {
-          const uint16_t* x = static_cast<const uint16_t*>(a.a_src);
-          for (int s = tid; s < rows * 32; s += GEMM_THREADS) {
-            const int i = s >> 5, c = s & 31;
-            *reinterpret_cast<uint4*>(sA + i * A_STRIDE + 8 * c) =
-                *reinterpret_cast<const uint4*>(x + (int64_t)sTok[i] * a.K + sb * 256 + 8 * c);
-          }
+          // low nibble of scale byte i/2, as sc << 16
+          const int sh = 16 - 8 * (i >> 1);
+          f0 = q2k_frag(B0, i, (sc0 << sh) & 0xf0000u, tqs);
+          if constexpr (GATEUP) f1 = q2k_frag(B1, i, (sc1 << sh) & 0xf0000u, tqs);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          const uint4 av = aread(m, i);
+          s0[m] = mfma32(av, f0, s0[m]);
+          if constexpr (GATEUP) s1[m] = mfma32(av, f1, s1[m]);
+        }
+        // keep the scheduler from hoisting every step's table reads (and
+        // their registers) to the top: at most two steps overlap
+        if (i == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      // superblock epilogue: fp32 scales (and, in the first half, Q2K's min term)
+      if constexpr (FMT == FMT_IQ2) {
+        const float d0 = from_h(B0.d), d1 = GATEUP ? from_h(B1.d) : 0.0f;
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          acc0[m] += d0 * s0[m];
+          if constexpr (GATEUP) acc1[m] += d1 * s1[m];
         }
       } else {
-        const uint16_t* h = static_cast<const uint16_t*>(a.a_src);
-        for (int s = tid; s < rows * 32; s += GEMM_THREADS) {
-          const int i = s >> 5, c = s & 31;
-          *reinterpret_cast<uint4*>(sA + i * A_STRIDE + 8 * c) =
-              *reinterpret_cast<const uint4*>(h + (int64_t)(p0 + i) * a.K + sb * 256 + 8 * c);
-        }
-      }
-      // ---- B registers of this superblock ----
-      BRegs<FMT> b0, b1;
-      b0.load(a.B0, brow, sb, g4);
-      if constexpr (GATEUP) b1.load(a.B1, brow, sb, g4);
-      __syncthreads();
-      // ---- Q2K min term: per-sub-block sums of the A rows (hi + lo) ----
-      if constexpr (FMT == FMT_Q2K) {
-        for (int s = tid; s < rows * 16; s += GEMM_THREADS) {
-          const int i = s >> 4, j = s & 15;
-          float sum = 0.0f;
-#pragma unroll
-          for (int u = 0; u < 16; u++) {
-            sum += from16<AT>(sA[i * A_STRIDE + 16 * j + u]);
-            if constexpr (XSPLIT) sum += from16<AT>(sAlo[i * A_STRIDE + 16 * j + u]);
-          }
-          const uint32_t sh = to16<AT>(sum);
-          sS[i * 16 + j] = (uint16_t)sh;
-          sS[BM * 16 + i * 16 + j] = (uint16_t)to16<AT>(sum - from16<AT>(sh));
-        }
-        __syncthreads();
-      }
-      // ---- 8 k32 steps ----
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        uint4 f0, f1, f0l, f1l;
-        if constexpr (FMT == FMT_IQ2) {
-          f0 = iq2_frag<AT>(b0, q, t1, sgn);
-          if constexpr (GATEUP) f1 = iq2_frag<AT>(b1, q, t1, sgn);
-        } else if constexpr (FMT == FMT_Q2K) {
-          f0 = q2k_frag<AT>(b0, q, tqs);
-          if constexpr (GATEUP) f1 = q2k_frag<AT>(b1, q, tqs);
-        } else {
-          q8_frag<AT>(b0, q, f0, f0l);
-          if constexpr (GATEUP) q8_frag<AT>(b1, q, f1, f1l);
+        const float dd0 = from_h(B0.dm & 0xffffu), dmin0 = from_h(B0.dm >> 16);
+        float dd1 = 0.0f, dmin1 = 0.0f;
+        if constexpr (GATEUP) {
+          dd1 = from_h(B1.dm & 0xffffu);
+          dmin1 = from_h(B1.dm >> 16);
         }
 #pragma unroll
-        for (int m = 0; m < BM / 16; m++) {
-          if (m < nm) {
-            // inputs 64*g4 + 8q .. +7 (the K order of the B fragments)
-            const uint4 av = *reinterpret_cast<const uint4*>(sA + (m * 16 + c16) * A_STRIDE + 64 * g4 + 8 * q);
-            uint4 avl;
-            if constexpr (XSPLIT) avl = *reinterpret_cast<const uint4*>(sAlo + (m * 16 + c16) * A_STRIDE + 64 * g4 + 8 * q);
-            if constexpr (FMT == FMT_Q8) {
-              acc0[m] = mfma32<AT>(av, f0, acc0[m]);
-              acc0[m] = mfma32<AT>(av, f0l, acc0[m]);
-              if constexpr (XSPLIT) acc0[m] = mfma32<AT>(avl, f0, acc0[m]);
-              if constexpr (GATEUP) {
-                acc1[m] = mfma32<AT>(av, f1, acc1[m]);
-                acc1[m] = mfma32<AT>(av, f1l, acc1[m]);
-                if constexpr (XSPLIT) acc1[m] = mfma32<AT>(avl, f1, acc1[m]);
-              }
-            } else {
-              sb0[m] = mfma32<AT>(av, f0, sb0[m]);
-              if constexpr (XSPLIT) sb0[m] = mfma32<AT>(avl, f0, sb0[m]);
-              if constexpr (GATEUP) {
-                sb1[m] = mfma32<AT>(av, f1, sb1[m]);
-                if constexpr (XSPLIT) sb1[m] = mfma32<AT>(avl, f1, sb1[m]);
-              }
-            }
-          }
+        for (int m = 0; m < NM; m++) {
+          acc0[m] += dd0 * s0[m];
+          if constexpr (GATEUP) acc1[m] += dd1 * s1[m];
         }
-      }
-      // ---- superblock epilogue: fp32 scales ----
-      if constexpr (FMT == FMT_IQ2) {
+        if (h == 0) {
+          const uint2 mf0 = q2k_min_frag(B0);
+          uint2 mf1;
+          if constexpr (GATEUP) mf1 = q2k_min_frag(B1);
+          const uint16_t* ss = sS + buf * (2 * BM * 16);
 #pragma unroll
-        for (int m = 0; m < BM / 16; m++) {
-          if (m < nm) {
-            acc0[m] += b0.d * sb0[m];
-            sb0[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int m = 0; m < NM; m++) {
+            const uint2 shi = *reinterpret_cast<const uint2*>(ss + (m * 16 + c16) * 16 + 4 * g4);
+            const uint2 slo = *reinterpret_cast<const uint2*>(ss + BM * 16 + (m * 16 + c16) * 16 + 4 * g4);
+            f32x4_t mm = mfma16(shi, mf0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            mm = mfma16(slo, mf0, mm);
+            acc0[m] -= dmin0 * mm;
             if constexpr (GATEUP) {
-              acc1[m] += b1.d * sb1[m];
-              sb1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-          }
-        }
-      } else if constexpr (FMT == FMT_Q2K) {
-        const uint2 mf0 = q2k_min_frag<AT>(b0);
-        uint2 mf1;
-        if constexpr (GATEUP) mf1 = q2k_min_frag<AT>(b1);
-#pragma unroll
-        for (int m = 0; m < BM / 16; m++) {
-          if (m < nm) {
-            const uint2 shi = *reinterpret_cast<const uint2*>(sS + (m * 16 + c16) * 16 + 4 * g4);
-            const uint2 slo = *reinterpret_cast<const uint2*>(sS + BM * 16 + (m * 16 + c16) * 16 + 4 * g4);
-            f32x4_t mm = mfma16<AT>(shi, mf0, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            mm = mfma16<AT>(slo, mf0, mm);
-            acc0[m] += b0.d * sb0[m] - b0.dmin * mm;
-            sb0[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (GATEUP) {
-              f32x4_t m1 = mfma16<AT>(shi, mf1, f32x4_t{0.f, 0.f, 0.f, 0.f});
-              m1 = mfma16<AT>(slo, mf1, m1);
-              acc1[m] += b1.d * sb1[m] - b1.dmin * m1;
-              sb1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+              f32x4_t m1 = mfma16(shi, mf1, f32x4_t{0.f, 0.f, 0.f, 0.f});
+              m1 = mfma16(slo, mf1, m1);
+              acc1[m] -= dmin1 * m1;
             }
           }
         }
       }
-      __syncthreads();  // A tile is overwritten by the next superblock
     }
+  };
 
-    // ---- output ----
+  // End of an item (after a barrier: every wave is past the item's last
+  // compute, so A buffer `freebuf` is free): the second-half waves hand their
+  // partial sums to the first-half waves, which write the outputs.
+  auto epilogue = [&](int j, const Item& it, int freebuf) {
+    // lane-derived values re-read through an opaque copy: nothing here is
+    // computed ahead of the loop and held (spilled) across it
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int wv = (int)(threadIdx.x >> 6) % GEMM_PAIRS, g4 = ln >> 4, c16 = ln & 15, lane = ln;
+    float* red1 = reinterpret_cast<float*>(sA + freebuf * A_BUF);  // second matrix (gate/up)
+    static_assert(NSUB * 4 * GEMM_PAIRS * 64 * 4 <= A_BUF, "partials fit an A buffer");
+    if (h == 1) {
 #pragma unroll
-    for (int m = 0; m < BM / 16; m++) {
-      if (m < nm) {
+      for (int m = 0; m < NSUB; m++) {
+        if (m < it.nm) {
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int i = m * 16 + 4 * g4 + r;
-          if (i < rows) {
-            if constexpr (GATEUP) {
-              const float h = silu(acc0[m][r]) * acc1[m][r];
-              static_cast<_Float16*>(a.out)[(int64_t)(p0 + i) * a.N + n] = (_Float16)h;
-            } else {
-              static_cast<float*>(a.out)[(int64_t)(p0 + i) * a.N + n] = acc0[m][r];
+          for (int r = 0; r < 4; r++) {
+            const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
+            sRed[o] = acc0[m][r];
+            if constexpr (GATEUP) red1[o] = acc1[m][r];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (h == 0) {
+      const int n = it.nt * GEMM_BN + wv * 16 + c16;  // this lane's output row (B column)
+#pragma unroll
+      for (int m = 0; m < NSUB; m++) {
+        if (m < it.nm) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
+            const int i = m * 16 + 4 * g4 + r;
+            const float v0 = acc0[m][r] + sRed[o];
+            if (i < it.rows) {
+              if constexpr (GATEUP) {
+                const float v1 = acc1[m][r] + red1[o];
+                const float xs = sXs[(j % 3) * BM + i];
+                const float hv = silu(v0 * xs) * (v1 * xs);
+                static_cast<_Float16*>(a.out)[(int64_t)(it.p0 + i) * a.N + n] = (_Float16)hv;
+              } else {
+                static_cast<float*>(a.out)[(int64_t)(it.p0 + i) * a.N + n] = v0;
+              }
             }
           }
         }
       }
     }
+#pragma unroll
+    for (int m = 0; m < NSUB; m++) acc0[m] = acc1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // ---- prologue ----
+  // Loads return in issue order, so A of superblock s + 1 is requested
+  // before the weight loads issued in the step before it is needed: waiting
+  // for it never waits for weights that are not yet due.
+  Item cur = item(0), nxt = item(1);
+  tok_issue(cur);
+  tok_commit(0);
+  tok_issue(nxt);
+  tok_commit(1);
+  tok_issue(item(2));
+  __syncthreads();
+  const int total = cnt * nsb;
+  issueA(0, 0, cur, 0);
+  if (DA == 2) {
+    if (nsb > 1) issueA(1, 0, cur, 1);
+    else issueA(1, 1, nxt, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < PD; s++) issueB(s, cur, s);  // PD divides nsb: all in item 0
+  storeA(0, 0);
+  __syncthreads();
+
+  // ---- steady state: step s = item j, superblock sb; items end only at the
+  // last step of a group of PD (PD divides nsb) ----
+  int j = 0, sbase = 0;
+  for (int s0 = 0; s0 < total; s0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; u++) {
+      const int s = s0 + u;
+      const int sb = sbase + u;
+      const bool last = u == PD - 1 && sbase + PD == nsb;
+      {  // A of step s + DA (item j or j + 1; past the end: no active rows)
+        const int sa = sb + DA;
+        if (sa >= nsb) issueA((u + DA) & 1, j + 1, nxt, sa - nsb);
+        else issueA((u + DA) & 1, j, cur, sa);
+      }
+      if (cur.nm == 2) compute(std::integral_constant<int, 2>{}, u, s & 1);
+      else compute(std::integral_constant<int, 1>{}, u, s & 1);
+      {  // weights of step s + PD (past the end: in bounds, unused)
+        const int sbB = sb + PD;
+        if (sbB >= nsb) issueB(u, nxt, sbB - nsb);
+        else issueB(u, cur, sbB);
+      }
+      if (last) {
+        __syncthreads();
+        epilogue(j, cur, s & 1);
+        cur = nxt;
+        nxt = item(j + 2);
+        tok_commit(j + 2);  // slot (j + 2) % 3 was last read for item j - 1
+        tok_issue(item(j + 3));
+        j++;
+      }
+      if (s + 1 < total) storeA((u + 1) & 1, (s + 1) & 1);
+      __syncthreads();
+    }
+    sbase += PD;
+    if (sbase == nsb) sbase = 0;
   }
 }
 
@@ -534,27 +788,50 @@ static int num_cus() {
   return g_num_cus;
 }
 
-template <int FMT, int AT, bool XSPLIT, bool GATEUP, int BM>
-static hipError_t run_gemm(const GemmArgs& a, int max_items, hipStream_t s) {
+template <int FMT, bool GATEUP, int PD>
+static hipError_t run_gemm_pd(const GemmArgs& a, int max_items, hipStream_t s) {
   const char* name = GATEUP ? (a.routed ? "prefill_gateup" : "prefill_shared_gateup")
                             : (a.routed ? "prefill_down" : "prefill_shared_down");
-  using L = GemmLds<FMT, AT, XSPLIT, GATEUP, BM>;
-  auto kern = gemm_kernel<FMT, AT, XSPLIT, GATEUP, BM>;
+  using L = GemmLds<FMT, GATEUP>;
+  auto kern = gemm_kernel<FMT, GATEUP, PD>;
+  const int bytes = L::bytes_for(a.routed ? a.E : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::bytes);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       L::bytes_for(MAX_EXPERTS));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  int grid = num_cus();
+  static int cached_bytes = -1, per_cu = 1;  // resident blocks per CU at that LDS size
+  if (bytes != cached_bytes) {
+    int nb = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, GEMM_THREADS, bytes);
+    if (e != hipSuccess) return e;
+    per_cu = nb > 0 ? nb : 1;
+    cached_bytes = bytes;
+  }
+  int grid = per_cu * num_cus();
   grid = (grid / 8) * 8;
-  if (grid < 8) grid = 8;
   if (max_items < grid) grid = ((max_items + 7) / 8) * 8;
   if (grid < 8) grid = 8;
   const int pid = prof_begin(name, s);
-  kern<<<dim3(grid), dim3(GEMM_THREADS), L::bytes, s>>>(a);
+  kern<<<dim3(grid), dim3(GEMM_THREADS), bytes, s>>>(a);
   prof_end(pid, s);
   return hipGetLastError();
+}
+
+template <int FMT, bool GATEUP>
+static hipError_t run_gemm(const GemmArgs& a, int max_items, hipStream_t s) {
+  const int nsb = a.K / 256;
+  // Superblocks of weights kept in flight per wave.  At 16 waves per CU a
+  // wave has 128 VGPRs: the two-matrix gate/up kernels hold two superblocks,
+  // the one-matrix down kernels four, and the Q8 kernels (4x the bytes per
+  // superblock and a heavier decode) one.
+  if constexpr (FMT != FMT_Q8) {
+    if (!GATEUP && nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4>(a, max_items, s);
+    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2>(a, max_items, s);
+  }
+  return run_gemm_pd<FMT, GATEUP, 1>(a, max_items, s);
 }
 
 #define PF_FMT_SWITCH(fmt, F, ...)                                     \
@@ -567,14 +844,24 @@ static hipError_t run_gemm(const GemmArgs& a, int max_items, hipStream_t s) {
 hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
   hipError_t err = hipSuccess;
   const int n = P.T * P.k;
+  // A operands are addressed with 32-bit buffer offsets
+  if ((int64_t)P.T * P.d * 2 >= (int64_t(1) << 31) || (int64_t)n * P.f * 2 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  {
+    const int pid = prof_begin("prefill_x16", s);
+    x16_kernel<<<dim3(P.T), 256, 0, s>>>(P.x, P.x_dtype, P.d, P.x16, P.xs, P.pos, P.k, P.route_xs);
+    prof_end(pid, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   // routed gate/up -> H (fp16, bucket order)
   {
     GemmArgs a{};
     a.B0 = make_qmat(P.w_gate, P.fmt_gate_up, P.E, P.f, P.d);
     a.B1 = make_qmat(P.w_up, P.fmt_gate_up, P.E, P.f, P.d);
     a.grid = P.grid;
-    a.a_src = P.x;
-    a.a_dtype = P.x_dtype;
+    a.a16 = P.x16;
+    a.a16_bytes = P.T * P.d * 2;
+    a.rowxs = P.route_xs;
     a.K = P.d;
     a.N = P.f;
     a.routed = 1;
@@ -585,22 +872,17 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.H;
-    if (P.x_dtype == X_BF16) {
-      const int max_items = (n / PREFILL_BM + P.E) * (P.f / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, AT_BF16, false, true, PREFILL_BM>(a, max_items, s)))
-    } else {
-      const int max_items = (n / PREFILL_BM_SPLIT + P.E) * (P.f / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, AT_BF16, true, true, PREFILL_BM_SPLIT>(a, max_items, s)))
-    }
+    const int max_items = (n / BM + P.E) * (P.f / GEMM_BN);
+    PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true>(a, max_items, s)))
     if (err != hipSuccess) return err;
   }
-  // routed down -> Ye (fp32, bucket order)
+  // routed down -> Ye (fp32, bucket order); same M tiles as the gate/up GEMM
   {
     GemmArgs a{};
     a.B0 = make_qmat(P.w_down, P.fmt_down, P.E, P.d, P.f);
     a.grid = P.grid;
-    a.a_src = P.H;
-    a.a_dtype = X_F32;
+    a.a16 = static_cast<const uint16_t*>(P.H);
+    a.a16_bytes = n * P.f * 2;
     a.K = P.f;
     a.N = P.d;
     a.routed = 1;
@@ -611,14 +893,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.Ye;
-    // same M tiles as the gate/up GEMM (the bucket tile schedule is shared)
-    if (P.x_dtype == X_BF16) {
-      const int max_items = (n / PREFILL_BM + P.E) * (P.d / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, AT_F16, false, false, PREFILL_BM>(a, max_items, s)))
-    } else {
-      const int max_items = (n / PREFILL_BM_SPLIT + P.E) * (P.d / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, AT_F16, false, false, PREFILL_BM_SPLIT>(a, max_items, s)))
-    }
+    const int max_items = (n / BM + P.E) * (P.d / GEMM_BN);
+    PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false>(a, max_items, s)))
     if (err != hipSuccess) return err;
   }
   if (P.has_shared) {
@@ -626,8 +902,9 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.B0 = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
     a.B1 = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
     a.grid = P.grid;
-    a.a_src = P.x;
-    a.a_dtype = P.x_dtype;
+    a.a16 = P.x16;
+    a.a16_bytes = P.T * P.d * 2;
+    a.rowxs = P.xs;
     a.K = P.d;
     a.N = P.f;
     a.routed = 0;
@@ -635,19 +912,14 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.E = 1;
     a.k = 1;
     a.out = P.Hs;
-    if (P.x_dtype == X_BF16) {
-      const int max_items = ((P.T + PREFILL_BM - 1) / PREFILL_BM) * (P.f / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, AT_BF16, false, true, PREFILL_BM>(a, max_items, s)))
-    } else {
-      const int max_items = ((P.T + PREFILL_BM_SPLIT - 1) / PREFILL_BM_SPLIT) * (P.f / GEMM_BN);
-      PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, AT_BF16, true, true, PREFILL_BM_SPLIT>(a, max_items, s)))
-    }
+    const int max_items = ((P.T + BM - 1) / BM) * (P.f / GEMM_BN);
+    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, max_items, s)))
     if (err != hipSuccess) return err;
     GemmArgs b{};
     b.B0 = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
     b.grid = P.grid;
-    b.a_src = P.Hs;
-    b.a_dtype = X_F32;
+    b.a16 = static_cast<const uint16_t*>(P.Hs);
+    b.a16_bytes = P.T * P.f * 2;
     b.K = P.f;
     b.N = P.d;
     b.routed = 0;
@@ -655,8 +927,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     b.E = 1;
     b.k = 1;
     b.out = P.Ysh;
-    const int max_items2 = ((P.T + PREFILL_BM - 1) / PREFILL_BM) * (P.d / GEMM_BN);
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, AT_F16, false, false, PREFILL_BM>(b, max_items2, s)))
+    const int max_items2 = ((P.T + BM - 1) / BM) * (P.d / GEMM_BN);
+    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false>(b, max_items2, s)))
     if (err != hipSuccess) return err;
   }
   const int pid = prof_begin("prefill_combine", s);
