@@ -68,6 +68,60 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 512 << 20  # calibration copy: reads and writes exactly this many bytes per dispatch
+
+# library kernel (as named by the per-launch timing hooks) -> substring of the
+# device kernel name in a rocprofv3 record
+KERNEL_SYMBOLS = {
+    "decode_router_shared_gateup": "k1_kernel",
+    "decode_gateup": "k2_kernel",
+    "decode_down_combine": "k3_kernel",
+    "prefill_gateup": "gemm_kernel<1, true",
+    "prefill_down": "gemm_kernel<2, false",
+}
+
+
+def pmc_summarize(fetch_dir: str, write_dir: str) -> int:
+    """HBM bytes per launch of each kernel from two rocprofv3 --pmc runs of
+    bench.py --pmc-mode (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = {}
+        for path in files:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES, "kernels": {}}
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        vals = per_kernel(d, counter)
+        copy = [v for name, vs in vals.items() if "copy" in name.lower() for v in vs]
+        if not copy:
+            raise SystemExit(f"no calibration copy kernel in the {counter} run")
+        cal = COPY_BYTES / (float(np.median(copy)) * 1024.0)  # bytes per counted byte
+        out[f"{key}_calibration"] = round(cal, 4)
+        for kname, sym in KERNEL_SYMBOLS.items():
+            vs = [v for name, vv in vals.items() if sym in name for v in vv]
+            if vs:
+                rec = out["kernels"].setdefault(kname, {"dispatches": len(vs)})
+                rec[f"{key}_bytes_per_launch"] = round(float(np.mean(vs)) * 1024.0 * cal)
+    for rec in out["kernels"].values():
+        if "fetch_bytes_per_launch" in rec and "write_bytes_per_launch" in rec:
+            rec["hbm_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -77,7 +131,15 @@ def main() -> int:
     ap.add_argument("--profile-steps", type=int, default=256, help="eager steps with per-kernel events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
+    ap.add_argument("--pmc-mode", action="store_true",
+                    help="no timing: a few decode and prefill steps and a plain copy of known size, for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two counter runs into profiles/traffic_counters.json (no GPU)")
     args = ap.parse_args()
+
+    if args.pmc_summarize:
+        return pmc_summarize(*args.pmc_summarize)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel sharding is "
@@ -119,6 +181,29 @@ def main() -> int:
     log(f"layers ready in {time.time() - t0:.1f}s (routed copies: 2 x {sum(t.numel() for t in second.values())/1e9:.2f} GB)")
 
     result = {}
+
+    if args.pmc_mode:
+        # decode steps, prefill steps, then the calibration copy (each kernel
+        # is one dispatch record in the counter runs)
+        xs = torch.from_numpy(synth.activations(0, ("bench", "decode-x"), N_DESC, d, synth.F32)).to(dev)
+        ys = torch.empty(N_DESC, d, dtype=torch.float32, device=dev)
+        ws = base.workspace(1)
+        for i in range(8):
+            lib.layer_forward(descs[i], xs[i:i + 1], ys[i:i + 1], ws)
+        T = 1024
+        xp = torch.from_numpy(synth.activations(0, ("bench", "prefill-x", 0), T, d, synth.BF16).view(np.int16)) \
+            .to(dev).view(torch.bfloat16)
+        yp = torch.empty(T, d, dtype=torch.float32, device=dev)
+        wsp = base.workspace(T)
+        for i in range(2):
+            lib.layer_forward(descs[i], xp, yp, wsp)
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"pmc mode done ({COPY_BYTES} B calibration copy x4)")
+        return 0
 
     # ------------------------------------------------------------ decode ----
     bytes_k1 = E * d * 4 + 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d) + d * 4
@@ -263,7 +348,7 @@ def main() -> int:
         import oracle
 
         threads = oracle.threads()
-        xs_h = synth.activations(0, ("bench", "cpu-x"), 64, d, synth.F32)
+        xs_h = synth.activations(0, ("bench", "cpu-x"), 1024, d, synth.F32)
         t0 = time.perf_counter()
         n = 0
         while n < xs_h.shape[0]:

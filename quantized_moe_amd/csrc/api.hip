@@ -63,7 +63,10 @@ static std::mutex g_prof_mu;
 static std::vector<ProfRec> g_prof;
 static bool g_prof_on = false;
 
+static thread_local hipEvent_t t_pend_a = nullptr, t_pend_b = nullptr;
+
 int prof_begin(const char* name, hipStream_t s) {
+  (void)s;
   if (!g_prof_on) return -1;
   ProfRec r;
   r.name = name;
@@ -72,16 +75,26 @@ int prof_begin(const char* name, hipStream_t s) {
     (void)hipEventDestroy(r.a);
     return -1;
   }
-  (void)hipEventRecord(r.a, s);
+  t_pend_a = r.a;
+  t_pend_b = r.b;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof.push_back(r);
   return (int)g_prof.size() - 1;
 }
 
+void prof_take_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = t_pend_a;
+  *stop = t_pend_b;
+  t_pend_a = t_pend_b = nullptr;
+}
+
 void prof_end(int id, hipStream_t s) {
   if (id < 0) return;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (id < (int)g_prof.size()) (void)hipEventRecord(g_prof[id].b, s);
+  if (t_pend_a != nullptr) {  // no launch consumed the pair: record it empty
+    (void)hipEventRecord(t_pend_a, s);
+    (void)hipEventRecord(t_pend_b, s);
+    t_pend_a = t_pend_b = nullptr;
+  }
 }
 }  // namespace qmoe
 

@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t* __restrict__
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                          int32_t* pos, int32_t* tile_start, int tile_m, hipStream_t s) {
   const int n = T * k;
-  bucket_kernel<<<dim3(E), 256, 0, s>>>(idx, n, E, counts, offsets, perm, pos, tile_start, tile_m > 0 ? tile_m : 1);
+  QMOE_LAUNCH(bucket_kernel, dim3(E), dim3(256), 0, s, idx, n, E, counts, offsets, perm, pos, tile_start,
+              tile_m > 0 ? tile_m : 1);
   return hipGetLastError();
 }
 

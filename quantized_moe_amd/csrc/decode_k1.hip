@@ -208,7 +208,7 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
 
 template <int FMT_S, int D>
 static hipError_t run_k1(const DecodeArgs& a, const K1Plan& pl, int gu_layout, hipStream_t s) {
-  k1_kernel<FMT_S, D><<<dim3(pl.n_rb + pl.n_sb + pl.n_xb), THREADS, 0, s>>>(a, pl, gu_layout);
+  QMOE_LAUNCH((k1_kernel<FMT_S, D>), dim3(pl.n_rb + pl.n_sb + pl.n_xb), dim3(THREADS), 0, s, a, pl, gu_layout);
   return hipGetLastError();
 }
 

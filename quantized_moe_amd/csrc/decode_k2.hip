@@ -160,7 +160,7 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
 
 template <int FMT, int D, int GCNT>
 static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, int shared_layout, hipStream_t s) {
-  k2_kernel<FMT, D, GCNT><<<dim3(blocks), THREADS, 0, s>>>(a, down_layout, shared_layout);
+  QMOE_LAUNCH((k2_kernel<FMT, D, GCNT>), dim3(blocks), dim3(THREADS), 0, s, a, down_layout, shared_layout);
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(THREADS) void k3_kernel(DecodeArgs a) {
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  k3_kernel<FR, FS, F><<<dim3(a.d / DN_ROWS, a.T), THREADS, 0, s>>>(a);
+  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 

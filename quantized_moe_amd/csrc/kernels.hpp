@@ -1,6 +1,7 @@
 // Launchers of the HIP kernels (host side), used by the C-ABI layer api.cpp.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,10 +16,21 @@ constexpr int TOPK_MAX_PER_LANE = MAX_EXPERTS / 64;
 constexpr int ROUTER_ROWS_MAX_T = 16;  // above this the tiled router runs
 constexpr int DECODE_MAX_T = 8;
 
-// Per-kernel timing hooks (api.hip): HIP events recorded on the launch
-// stream around one launch when profiling is enabled; no-ops otherwise.
+// Per-kernel timing hooks (api.hip).  When profiling is enabled, prof_begin
+// creates a start/stop event pair for the one launch that follows and hands it
+// to that launch through QMOE_LAUNCH, which gives them to
+// hipExtLaunchKernelGGL: the events are then stamped at the kernel's own
+// start and end (no dispatch gap).  No-ops otherwise.
 int prof_begin(const char* name, hipStream_t s);
 void prof_end(int id, hipStream_t s);
+void prof_take_events(hipEvent_t* start, hipEvent_t* stop);  // the pending pair, or nulls
+
+#define QMOE_LAUNCH(kern, grid, block, shmem, stream, ...)                                   \
+  do {                                                                                         \
+    hipEvent_t qmoe_ev_a_, qmoe_ev_b_;                                                          \
+    ::qmoe::prof_take_events(&qmoe_ev_a_, &qmoe_ev_b_);                                         \
+    hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, qmoe_ev_a_, qmoe_ev_b_, 0, __VA_ARGS__); \
+  } while (0)
 
 // route.hip
 hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtype, int T, float* z, hipStream_t s);

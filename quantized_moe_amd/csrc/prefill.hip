@@ -815,7 +815,7 @@ static hipError_t run_gemm_pd(const GemmArgs& a, int max_items, hipStream_t s) {
   if (max_items < grid) grid = ((max_items + 7) / 8) * 8;
   if (grid < 8) grid = 8;
   const int pid = prof_begin(name, s);
-  kern<<<dim3(grid), dim3(GEMM_THREADS), bytes, s>>>(a);
+  QMOE_LAUNCH(kern, dim3(grid), dim3(GEMM_THREADS), bytes, s, a);
   prof_end(pid, s);
   return hipGetLastError();
 }
@@ -849,7 +849,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     return hipErrorInvalidValue;
   {
     const int pid = prof_begin("prefill_x16", s);
-    x16_kernel<<<dim3(P.T), 256, 0, s>>>(P.x, P.x_dtype, P.d, P.x16, P.xs, P.pos, P.k, P.route_xs);
+    QMOE_LAUNCH(x16_kernel, dim3(P.T), dim3(256), 0, s, P.x, P.x_dtype, P.d, P.x16, P.xs, P.pos, P.k, P.route_xs);
     prof_end(pid, s);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -932,8 +932,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     if (err != hipSuccess) return err;
   }
   const int pid = prof_begin("prefill_combine", s);
-  combine_kernel<<<dim3(P.T), 256, 0, s>>>(P.Ye, P.has_shared ? P.Ysh : nullptr, P.pos, P.wt, P.k, P.d, P.T * P.k,
-                                           P.y);
+  QMOE_LAUNCH(combine_kernel, dim3(P.T), dim3(256), 0, s, (const float*)P.Ye, (const float*)(P.has_shared ? P.Ysh : nullptr),
+              (const int32_t*)P.pos, (const float*)P.wt, P.k, P.d, P.T * P.k, P.y);
   prof_end(pid, s);
   return hipGetLastError();
 }

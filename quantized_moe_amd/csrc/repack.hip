@@ -49,8 +49,8 @@ hipError_t launch_repack(int fmt, int64_t n_blocks, const void* src, void* dst, 
   if (n_blocks == 0) return hipSuccess;
   const int threads = 256;
   const int64_t grid = (n_blocks + threads - 1) / threads;
-  repack_kernel<<<dim3((unsigned)grid), dim3(threads), 0, s>>>(fmt, n_blocks, static_cast<const uint8_t*>(src),
-                                                                static_cast<uint8_t*>(dst), to_device);
+  QMOE_LAUNCH(repack_kernel, dim3((unsigned)grid), dim3(threads), 0, s, fmt, n_blocks, static_cast<const uint8_t*>(src),
+              static_cast<uint8_t*>(dst), to_device);
   return hipGetLastError();
 }
 

@@ -125,17 +125,17 @@ hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtyp
   if (T <= ROUTER_ROWS_MAX_T) {
     const dim3 grid((E + 3) / 4);
     switch (d / 256) {
-      case 1: router_rows_kernel<1><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
-      case 2: router_rows_kernel<2><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
-      case 4: router_rows_kernel<4><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
-      case 8: router_rows_kernel<8><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
-      case 16: router_rows_kernel<16><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
-      case 32: router_rows_kernel<32><<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z); break;
+      case 1: QMOE_LAUNCH(router_rows_kernel<1>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
+      case 2: QMOE_LAUNCH(router_rows_kernel<2>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
+      case 4: QMOE_LAUNCH(router_rows_kernel<4>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
+      case 8: QMOE_LAUNCH(router_rows_kernel<8>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
+      case 16: QMOE_LAUNCH(router_rows_kernel<16>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
+      case 32: QMOE_LAUNCH(router_rows_kernel<32>, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     const dim3 grid((E + RT_E - 1) / RT_E, (T + 4 * RT_T - 1) / (4 * RT_T));
-    router_tiled_kernel<<<grid, 256, 0, s>>>(W, E, d, x, x_dtype, T, z);
+    QMOE_LAUNCH(router_tiled_kernel, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z);
   }
   return hipGetLastError();
 }
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
 hipError_t launch_topk(const float* z, int T, int E, int k, int32_t* idx, float* wt, int32_t* idx2, float* wt2,
                        hipStream_t s) {
   if (T == 0) return hipSuccess;
-  topk_kernel<<<dim3((T + 3) / 4), 256, 0, s>>>(z, T, E, k, idx, wt, idx2, wt2);
+  QMOE_LAUNCH(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, T, E, k, idx, wt, idx2, wt2);
   return hipGetLastError();
 }
 
