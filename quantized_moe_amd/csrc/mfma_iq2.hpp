@@ -1,0 +1,91 @@
+// fp16 MFMA helpers and the IQ2 codebook tables shared by the prefill grouped
+// GEMMs and the decode gate/up GEMV.
+//
+// "YoungAi -- DeepSeek V4.1 Flash on one DGX Spark", section 4.4 feeds 16-bit
+// matrix units with codewords that convert without rounding.  Here every IQ2
+// B-operand value handed to v_mfma is the exact integer (2s+1) * g (s the
+// 4-bit sub-block scale, g in {1,3,5,7} the grid magnitude, so <= 217) with
+// its sign, in fp16; the fp16 superblock scale is applied to the fp32 result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int TAB_COPIES = 16;  // LDS table copies (one per lane of a 16-lane row)
+
+__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
+                                               0, 0);
+}
+
+// fp32 -> fp16 bits (round to nearest even) and back
+__device__ __forceinline__ uint32_t to_h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+__device__ __forceinline__ float from_h(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+
+// IQ2 tables in LDS.  tm[row][s] = the 8 grid magnitudes of row times (2s+1)
+// as fp16, 16 bytes, row stride 256 bytes: the byte address row << 8 | s << 4
+// is one v_perm of the payload word and s << 4.  sgn[b7][c] = XOR masks of the
+// 7 stored signs plus the parity sign, stored TAB_COPIES times (copy c at bank
+// quad c); lane l reads copy l % 16, so the 16 lanes of a row never meet in a
+// bank whatever patterns they look up.
+constexpr int IQ2_TM_BYTES = 256 * 16 * 16;
+constexpr int IQ2_SGN_BYTES = 128 * TAB_COPIES * 16;
+
+// Both tables, built by threads t0 .. t0 + nt - 1 of the block: a thread
+// that owns a grid row reads it once and writes its 16 scaled entries; the
+// sign table needs no loads and is spread over all of them.
+__device__ inline void build_iq2_tables(const uint8_t* grid, uint4* tm, uint4* sgn, int t0, int nt) {
+  for (int row = t0; row < 256; row += nt) {
+    const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * row);
+#pragma unroll 4
+    for (int sidx = 0; sidx < 16; sidx++) {
+      const int sc = 2 * sidx + 1;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint32_t word = i < 2 ? g.x : g.y;
+        const uint32_t v0 = (word >> (16 * (i & 1))) & 255u, v1 = (word >> (16 * (i & 1) + 8)) & 255u;
+        w[i] = to_h((float)(sc * v0)) | (to_h((float)(sc * v1)) << 16);
+      }
+      tm[row * 16 + sidx] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  for (int e = t0; e < 128 * TAB_COPIES; e += nt) {
+    const uint32_t b = e / TAB_COPIES;
+    const uint32_t s8 = b | ((__popc(b) & 1u) << 7);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) w[i] = (((s8 >> (2 * i)) & 1u) << 15) | (((s8 >> (2 * i + 1)) & 1u) << 31);
+    sgn[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// IQ2 sub-block scale s (the top nibble of its B word) as s << 4
+__device__ __forceinline__ uint32_t iq2_scale16(uint32_t bword) { return (bword >> 24) & 0xf0u; }
+
+// The 8 exact integers of group i (0..3) of a sub-block with payload words
+// (A, B): S16 = iq2_scale16(B), CB = (lane % 16) << 4.
+__device__ __forceinline__ uint4 iq2_frag_words(uint32_t A, uint32_t B, int i, uint32_t S16, uint32_t CB,
+                                                const uint8_t* tm, const uint8_t* sgn) {
+  // row << 8 | s << 4: byte 0 from S16, byte 1 = byte i of A
+  const uint32_t maddr = __builtin_amdgcn_perm(A, S16, 0x0c0c0000u | ((4u + i) << 8));
+  // (7 sign bits) << 8 | copy << 4
+  const uint32_t sh = i == 0 ? (B << 8) : i == 1 ? (B << 1) : i == 2 ? (B >> 6) : (B >> 13);
+  const uint32_t saddr = (sh & 0x7f00u) | CB;
+  const uint4 m = *reinterpret_cast<const uint4*>(tm + maddr);
+  const uint4 s = *reinterpret_cast<const uint4*>(sgn + saddr);
+  return make_uint4(m.x ^ s.x, m.y ^ s.y, m.z ^ s.z, m.w ^ s.w);
+}
+
+}  // namespace qmoe

@@ -8,8 +8,7 @@
 //     (2s+1) * grid value <= 217; Q2K: sc * q <= 45), the fp16 superblock
 //     scales are applied in an fp32 epilogue once per 256 inputs, and Q2K's
 //     min term is a second, K=16 MFMA against per-sub-block sums of the A rows;
-//     Q8 weights (the shared expert) enter as an exact two-term split
-//     d*q = hi + lo;
+//     Q8 weights (the shared expert) enter as fp16(d*q), rounded once;
 //   * the activations x are converted once to fp16 with a per-token power of
 //     two (exact) that puts max|x_t| in [2^13, 2^14), undone in the gate/up
 //     epilogue; the SwiGLU output h is stored as fp16 (one rounding, 2^-11).
@@ -28,13 +27,9 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_iq2.hpp"
 
 namespace qmoe {
-
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int GEMM_PAIRS = 8;              // wave pairs: 16 output rows each
 constexpr int GEMM_WAVES = 2 * GEMM_PAIRS;  // the two waves of a pair take the two halves of K
@@ -45,25 +40,6 @@ constexpr int NSUB = BM / 16;             // 16-row MFMA sub-tiles
 constexpr int A_PIECES = BM * 32;         // 16-byte pieces of one A superblock chunk
 constexpr int A_ROW = 33 * 16;            // LDS bytes per A row (32 pieces + one of padding)
 constexpr int A_BUF = BM * A_ROW;         // LDS bytes per A buffer
-constexpr int TAB_COPIES = 16;            // LDS table copies (one per lane of a 16-lane row)
-
-__device__ __forceinline__ f32x4_t mfma32(uint4 a, uint4 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
-                                                0, 0);
-}
-__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0,
-                                               0, 0);
-}
-
-// fp32 -> fp16 bits (round to nearest even) and back
-__device__ __forceinline__ uint32_t to_h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
-__device__ __forceinline__ float from_h(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
-
-// two fp16 lanes times two fp16 lanes
-__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) * __builtin_bit_cast(f16x2_t, b));
-}
 
 // ---------------------------------------------------------------------------
 // x -> fp16 with a per-token power-of-two scale
@@ -149,37 +125,6 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // LDS tables (built once per persistent block)
 // ---------------------------------------------------------------------------
-// IQ2: tm[row][s] = the 8 grid magnitudes of row times (2s+1) as fp16 (exact
-// integers <= 217), 16 bytes, row stride 256 bytes: the byte address
-// row << 8 | s << 4 is one v_perm of the payload word and s << 4.
-// sgn[b7][c] = XOR masks of the 7 stored signs plus the parity sign, stored
-// TAB_COPIES times (copy c at bank quad c); lane l reads copy l % 16, so the
-// 16 lanes of a row never meet in a bank whatever patterns they look up.
-constexpr int IQ2_TM_BYTES = 256 * 16 * 16;
-constexpr int IQ2_SGN_BYTES = 128 * TAB_COPIES * 16;
-__device__ void build_iq2_tables(const uint8_t* grid, uint4* tm, uint4* sgn) {
-  for (int e = threadIdx.x; e < 256 * 16; e += blockDim.x) {
-    const int row = e >> 4, sc = 2 * (e & 15) + 1;
-    const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * row);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint32_t word = i < 2 ? g.x : g.y;
-      const uint32_t v0 = (word >> (16 * (i & 1))) & 255u, v1 = (word >> (16 * (i & 1) + 8)) & 255u;
-      w[i] = to_h((float)(sc * v0)) | (to_h((float)(sc * v1)) << 16);
-    }
-    tm[e] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  for (int e = threadIdx.x; e < 128 * TAB_COPIES; e += blockDim.x) {
-    const uint32_t b = e / TAB_COPIES;
-    const uint32_t s8 = b | ((__popc(b) & 1u) << 7);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) w[i] = (((s8 >> (2 * i)) & 1u) << 15) | (((s8 >> (2 * i + 1)) & 1u) << 31);
-    sgn[e] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Q2K: tqs[sc][byte] = 4 x fp16 sc * q_i for the four 2-bit quants of byte.
 __device__ void build_q2k_table(uint2* tqs) {
   for (int e = threadIdx.x; e < 16 * 256; e += blockDim.x) {
@@ -253,22 +198,11 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;  // i is a compile-time constant
 }
 
-// IQ2 sub-block scale s (the top nibble of its B word) as s << 4
-__device__ __forceinline__ uint32_t iq2_scale16(uint32_t bword) { return (bword >> 24) & 0xf0u; }
-
 // Fragment of local step i (q = 4h + i): 8 exact integers, group i of the
 // lane's sub-block.  S16 = iq2_scale16 of the sub-block, CB = (lane % 16) << 4.
 __device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2>& b, int i, uint32_t S16, uint32_t CB,
                                           const uint8_t* tm, const uint8_t* sgn) {
-  const uint32_t A = b.p.x, B = b.p.y;
-  // row << 8 | s << 4: byte 0 from S16, byte 1 = byte i of A
-  const uint32_t maddr = __builtin_amdgcn_perm(A, S16, 0x0c0c0000u | ((4u + i) << 8));
-  // (7 sign bits) << 8 | copy << 4
-  const uint32_t sh = i == 0 ? (B << 8) : i == 1 ? (B << 1) : i == 2 ? (B >> 6) : (B >> 13);
-  const uint32_t saddr = (sh & 0x7f00u) | CB;
-  const uint4 m = *reinterpret_cast<const uint4*>(tm + maddr);
-  const uint4 s = *reinterpret_cast<const uint4*>(sgn + saddr);
-  return make_uint4(m.x ^ s.x, m.y ^ s.y, m.z ^ s.z, m.w ^ s.w);
+  return iq2_frag_words(b.p.x, b.p.y, i, S16, CB, tm, sgn);
 }
 
 // Q2K fragment of local step i: quant bytes 2i, 2i+1 of the lane's 8, whose
@@ -292,24 +226,20 @@ __device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K>& b) {
   return make_uint2(to_h((float)m0) | (to_h((float)m1) << 16), to_h((float)m2) | (to_h((float)m3) << 16));
 }
 
-// Q8 fragment of local step i: d*q split into two fp16 terms hi + lo (22
-// significant bits; the exact product of an 8-bit quant and an 11-bit scale
-// has 19).
-__device__ __forceinline__ void q8_frag(const BRegs<FMT_Q8>& b, int i, uint4& hi, uint4& lo) {
-  const uint32_t w2[2] = {word_of(b.q[i >> 1], 2 * (i & 1)), word_of(b.q[i >> 1], 2 * (i & 1) + 1)};
-  const float d = from_h(b.d);
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const uint32_t word = w2[j >> 1];
-    const float v0 = d * (float)(int8_t)((word >> (16 * (j & 1))) & 255u);
-    const float v1 = d * (float)(int8_t)((word >> (16 * (j & 1) + 8)) & 255u);
-    const uint32_t h0 = to_h(v0), h1 = to_h(v1);
-    h[j] = h0 | (h1 << 16);
-    l[j] = to_h(v0 - from_h(h0)) | (to_h(v1 - from_h(h1)) << 16);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
+// Q8 fragment of local step i: the 8 products d*q as fp16, each rounded once.
+// A quant byte b becomes the exact fp16 integer q: (b ^ 0x80) placed under an
+// fp16 exponent byte 0x64 reads 1024 + q + 128 (one v_perm per pair), minus
+// 1152 (one packed add); one packed multiply by (d, d) then rounds q*d.
+__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8>& b, int i) {
+  const uint32_t w0 = word_of(b.q[i >> 1], 2 * (i & 1)) ^ 0x80808080u;
+  const uint32_t w1 = word_of(b.q[i >> 1], 2 * (i & 1) + 1) ^ 0x80808080u;
+  const f16x2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2_t dd = {__builtin_bit_cast(_Float16, (uint16_t)b.d), __builtin_bit_cast(_Float16, (uint16_t)b.d)};
+  auto pair = [&](uint32_t w, uint32_t sel) {
+    const f16x2_t q = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(w, 0x64646464u, sel)) + bias;
+    return __builtin_bit_cast(uint32_t, q * dd);
+  };
+  return make_uint4(pair(w0, 0x00050004u), pair(w0, 0x00070006u), pair(w1, 0x00050004u), pair(w1, 0x00070006u));
 }
 
 // ---------------------------------------------------------------------------
@@ -360,7 +290,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   const int h = wave / GEMM_PAIRS;   // K half: steps q = 4h .. 4h + 3 of every superblock
   const int g4 = lane >> 4, c16 = lane & 15;
 
-  if constexpr (FMT == FMT_IQ2) build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn));
+  if constexpr (FMT == FMT_IQ2)
+    build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid, GEMM_THREADS);
   if constexpr (FMT == FMT_Q2K) build_q2k_table(reinterpret_cast<uint2*>(lds + L::oTqs));
   if (a.routed) {
     for (int i = tid; i <= a.E; i += GEMM_THREADS) {
@@ -374,11 +305,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   const int NT = a.N / GEMM_BN;
   const int nsb = a.K / 256;
 
-  // work-item mapping: XCD-aware when there are enough M tiles
+  // work-item mapping, XCD-aware (blocks are dealt to the 8 XCDs round-robin).
+  // Routed experts (few rows, many distinct weights): an XCD owns M tiles and
+  // runs all their N tiles, which share the M tile's A rows in its L2.  The
+  // shared expert (every row, one weight matrix): an XCD owns N tiles and its
+  // blocks sweep the M tiles across them, so each weight tile is read from
+  // HBM once and then served from that XCD's L2.
   const int nblk = gridDim.x;
-  const bool xcd_map = total_tiles >= 16 && (nblk % 8) == 0;
+  const bool n_major = !a.routed;
+  const bool xcd_map = (nblk % 8) == 0 && (n_major ? NT >= 8 : total_tiles >= 16);
   const int xcd = blockIdx.x % 8;
-  const int n_items = xcd_map ? ((total_tiles - xcd + 7) / 8) * NT : total_tiles * NT;
+  const int n_items = !xcd_map ? total_tiles * NT
+                      : n_major ? ((NT - xcd + 7) / 8) * total_tiles
+                                : ((total_tiles - xcd + 7) / 8) * NT;
   const int first = xcd_map ? blockIdx.x / 8 : blockIdx.x;
   const int step = xcd_map ? nblk / 8 : nblk;
   const int cnt = first < n_items ? (n_items - first + step - 1) / step : 0;
@@ -392,9 +331,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       return it;
     }
     const int g = first + j * step;
-    const int mt = g / NT;
-    it.nt = g - mt * NT;
-    const int tt = xcd_map ? xcd + 8 * mt : mt;
+    int tt;
+    if (n_major) {
+      const int nl = g / total_tiles;
+      tt = g - nl * total_tiles;
+      it.nt = xcd_map ? xcd + 8 * nl : nl;
+    } else {
+      const int mt = g / NT;
+      it.nt = g - mt * NT;
+      tt = xcd_map ? xcd + 8 * mt : mt;
+    }
     if (a.routed) {
       int lo = 0, hi = a.E;  // largest e with tile_start[e] <= tt
       while (hi - lo > 1) {
@@ -537,18 +483,14 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     if constexpr (FMT == FMT_Q8) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        uint4 f0, f0l, f1, f1l;
-        q8_frag(B0, i, f0, f0l);
-        if constexpr (GATEUP) q8_frag(B1, i, f1, f1l);
+        const uint4 f0 = q8_frag(B0, i);
+        uint4 f1;
+        if constexpr (GATEUP) f1 = q8_frag(B1, i);
 #pragma unroll
         for (int m = 0; m < NM; m++) {
           const uint4 av = aread(m, i);
           acc0[m] = mfma32(av, f0, acc0[m]);
-          acc0[m] = mfma32(av, f0l, acc0[m]);
-          if constexpr (GATEUP) {
-            acc1[m] = mfma32(av, f1, acc1[m]);
-            acc1[m] = mfma32(av, f1l, acc1[m]);
-          }
+          if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
         }
       }
     } else {
@@ -824,13 +766,12 @@ template <int FMT, bool GATEUP>
 static hipError_t run_gemm(const GemmArgs& a, int max_items, hipStream_t s) {
   const int nsb = a.K / 256;
   // Superblocks of weights kept in flight per wave.  At 16 waves per CU a
-  // wave has 128 VGPRs: the two-matrix gate/up kernels hold two superblocks,
-  // the one-matrix down kernels four, and the Q8 kernels (4x the bytes per
-  // superblock and a heavier decode) one.
+  // wave has 128 VGPRs: the two-matrix gate/up kernels and the Q8 kernels (4x
+  // the bytes per superblock) hold two superblocks, the 2-bit down kernels four.
   if constexpr (FMT != FMT_Q8) {
     if (!GATEUP && nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4>(a, max_items, s);
-    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2>(a, max_items, s);
   }
+  if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2>(a, max_items, s);
   return run_gemm_pd<FMT, GATEUP, 1>(a, max_items, s);
 }
 
