@@ -7,54 +7,10 @@
 // first, then quantize x into LDS together (once per token), then compute.
 // epb and spb are chosen by the host so that all blocks stream about the same
 // number of bytes.
-#include "decode_common.hpp"
+#include "decode_rows.hpp"
 
 namespace qmoe {
 namespace dec {
-
-// Router logits of expert e for every token, in the fixed fp32 order: lane l
-// owns partial l, i.e. elements 4 (l + 64 m) + 0..3 for m = 0, 1, ...; it
-// takes them in increasing order with one fmaf each; then the partials fold
-// as p[l] += p[l + s] for s = 32, 16, ..., 1.
-template <int D>
-__device__ __forceinline__ void router_item(const DecodeArgs& a, int e) {
-#pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63;
-  constexpr int CH = D / 256;
-  float4 w[CH];
-#pragma unroll
-  for (int m = 0; m < CH; m++) {
-    const uint4 v = ld16_stream(a.w_router + (int64_t)e * D + 4 * (lane + 64 * m));
-    w[m] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
-  }
-  for (int t = 0; t < a.T; t++) {
-    float4 xv[CH];
-    if (a.x_dtype == X_BF16) {
-      const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (int64_t)t * D;
-#pragma unroll
-      for (int m = 0; m < CH; m++) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(xb + 4 * (lane + 64 * m));
-        xv[m] = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
-                            __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
-      }
-    } else {
-      const float* xf = static_cast<const float*>(a.x) + (int64_t)t * D;
-#pragma unroll
-      for (int m = 0; m < CH; m++) xv[m] = *reinterpret_cast<const float4*>(xf + 4 * (lane + 64 * m));
-    }
-    float p = 0.0f;
-#pragma unroll
-    for (int m = 0; m < CH; m++) {
-      p = __builtin_fmaf(xv[m].x, w[m].x, p);
-      p = __builtin_fmaf(xv[m].y, w[m].y, p);
-      p = __builtin_fmaf(xv[m].z, w[m].z, p);
-      p = __builtin_fmaf(xv[m].w, w[m].w, p);
-    }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_down(p, s, 64);
-    if (lane == 0) a.z[(int64_t)t * a.E + e] = p;
-  }
-}
 
 template <int FMT, int D>
 struct XAct {

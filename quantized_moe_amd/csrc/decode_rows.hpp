@@ -1,0 +1,247 @@
+// Row loops of the decode kernels, shared by the three-launch decode
+// (decode_k1/k2/k3.hip) and the single-launch decode (decode_fused.hip):
+// router logits of one expert, a wave's run of routed gate/up rows, and a
+// wave's down-projection rows.
+#pragma once
+
+#include "decode_common.hpp"
+
+namespace qmoe {
+namespace dec {
+
+// Router logits of expert e for every token, in the fixed fp32 order: lane l
+// owns partial l, i.e. elements 4 (l + 64 m) + 0..3 for m = 0, 1, ...; it
+// takes them in increasing order with one fmaf each; then the partials fold
+// as p[l] += p[l + s] for s = 32, 16, ..., 1.
+template <int D>
+__device__ __forceinline__ void router_item(const DecodeArgs& a, int e) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  constexpr int CH = D / 256;
+  float4 w[CH];
+#pragma unroll
+  for (int m = 0; m < CH; m++) {
+    const uint4 v = ld16_stream(a.w_router + (int64_t)e * D + 4 * (lane + 64 * m));
+    w[m] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+  for (int t = 0; t < a.T; t++) {
+    float4 xv[CH];
+    if (a.x_dtype == X_BF16) {
+      const uint16_t* xb = static_cast<const uint16_t*>(a.x) + (int64_t)t * D;
+#pragma unroll
+      for (int m = 0; m < CH; m++) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(xb + 4 * (lane + 64 * m));
+        xv[m] = make_float4(__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                            __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u));
+      }
+    } else {
+      const float* xf = static_cast<const float*>(a.x) + (int64_t)t * D;
+#pragma unroll
+      for (int m = 0; m < CH; m++) xv[m] = *reinterpret_cast<const float4*>(xf + 4 * (lane + 64 * m));
+    }
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < CH; m++) {
+      p = __builtin_fmaf(xv[m].x, w[m].x, p);
+      p = __builtin_fmaf(xv[m].y, w[m].y, p);
+      p = __builtin_fmaf(xv[m].z, w[m].z, p);
+      p = __builtin_fmaf(xv[m].w, w[m].w, p);
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_down(p, s, 64);
+    if (lane == 0) a.z[(int64_t)t * a.E + e] = p;
+  }
+}
+
+template <int FMT, int D>
+struct RoutedAct {
+  using type = ActNib<Geo<FMT, D>::CPL, false>;
+};
+template <int D>
+struct RoutedAct<FMT_Q8, D> {
+  using type = ActQ8N<Geo<FMT_Q8, D>::CPL>;
+};
+
+// Bytes of LDS scale staging one wave needs for RPW gate/up rows.
+template <int FMT, int D, int RPW>
+constexpr int gateup_scale_bytes() {
+  return RowScales<FMT, D>::STAGE ? 2 * RPW * RowScales<FMT, D>::BYTES : 16;
+}
+
+// One wave's RPW consecutive routed h rows starting at global row Rw (rows
+// are route-major: route r = t k + j covers rows r f .. r f + f - 1) of token
+// t: gate and up rows of the route's expert against x (chunk-quantized at
+// xq / xs, global memory or LDS), SwiGLU, results to out[0 .. RPW) (0 for an
+// out-of-range expert id).  The rows cross at most one route boundary, so two
+// plane sets cover them.  Scale bytes are staged in my_scales, then PD steps
+// of weight loads are issued before x is read; the steps run
+// software-pipelined.
+template <int FMT, int D, int RPW, int PD>
+__device__ __forceinline__ void gateup_rows(const DecodeArgs& a, int Rw, int t, const int* s_sel, const uint8_t* xq,
+                                            const float* xs, const Iq2Tab* tab, uint8_t* my_scales, float* out) {
+  using G = Geo<FMT, D>;
+  constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
+  using SS = ScaleStage<FMT, D, 2, RPW>;
+  constexpr bool STAGE = SS::RS::STAGE;
+  const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
+  const int r0 = Rw / a.f;          // route of the first row (global index)
+  const int n0 = Rw - r0 * a.f;     // its row inside the expert
+  const int jb = a.f - n0;          // rows j >= jb belong to route r0 + 1
+  const int r1 = min(r0 + 1, t * a.k + a.k - 1);  // (a wave never leaves its token)
+  const int e0 = s_sel[r0 - t * a.k], e1 = s_sel[r1 - t * a.k];
+  const bool ok0 = (unsigned)e0 < (unsigned)a.E, ok1 = (unsigned)e1 < (unsigned)a.E;
+  const EPlanes G0 = expert_planes<FMT>(a.gate, ok0 ? e0 : 0), U0 = expert_planes<FMT>(a.up, ok0 ? e0 : 0);
+  const EPlanes G1 = expert_planes<FMT>(a.gate, ok1 ? e1 : 0), U1 = expert_planes<FMT>(a.up, ok1 ? e1 : 0);
+  Piece<FMT> wg[NS][G::CPL], wu[NS][G::CPL];
+  int lr[NS];
+  bool ok[NS];
+  auto issue = [&](int s) {
+    const int jj = s * G::RPS + sub;  // row within the run
+    const bool valid = jj < RPW;
+    const int j = valid ? jj : 0;
+    lr[s] = j;
+    const bool second = j >= jb;
+    ok[s] = valid && (second ? ok1 : ok0);
+    const uint32_t n = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+    const EPlanes Gp = pick_planes(second, G0, G1);
+    const EPlanes Up = pick_planes(second, U0, U1);
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) {
+      wg[s][k].template load<G::NB>(Gp, n, c + G::LPR * k);
+      wu[s][k].template load<G::NB>(Up, n, c + G::LPR * k);
+      if constexpr (!STAGE) {
+        wg[s][k].template scales_global<G::NB>(Gp, n, c + G::LPR * k);
+        wu[s][k].template scales_global<G::NB>(Up, n, c + G::LPR * k);
+      }
+    }
+  };
+  SS ss;
+  if constexpr (STAGE) {  // first: returns before the codes
+    ss.issue([&](int m, int j, EPlanes& P, uint32_t& row) {
+      const bool second = j >= jb;
+      P = m == 0 ? pick_planes(second, G0, G1) : pick_planes(second, U0, U1);
+      row = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+    });
+  }
+#pragma unroll
+  for (int s = 0; s < PD; s++) issue(s);
+  if constexpr (STAGE) ss.store(my_scales);
+  typename RoutedAct<FMT, D>::type act;
+  if constexpr (FMT == FMT_Q8) {
+    act.template load<G::LPR, 64>(xq, xs, c);
+  } else {
+    act.template load<G::LPR>(xq, xs, c);
+    act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
+  }
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    if (s + PD < NS) issue(s + PD);
+    if constexpr (STAGE) {
+      const int j = min(s * G::RPS + sub, RPW - 1);
+#pragma unroll
+      for (int k = 0; k < G::CPL; k++) {
+        wg[s][k].template scales_lds<G::NB>(SS::row(my_scales, 0, j), c + G::LPR * k);
+        wu[s][k].template scales_lds<G::NB>(SS::row(my_scales, 1, j), c + G::LPR * k);
+      }
+    }
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) {
+      g += piece_dot(wg[s][k], act, k, tab);
+      u += piece_dot(wu[s][k], act, k, tab);
+    }
+    g = group_sum<G::LPR>(g);
+    u = group_sum<G::LPR>(u);
+    if (c == G::LPR - 1 && s * G::RPS + sub < RPW) out[lr[s]] = ok[s] ? silu(g) * u : 0.0f;
+  }
+}
+
+template <int FMT, int K>
+struct DownAct {
+  using type = ActNib<Geo<FMT, K>::CPL, true>;
+};
+template <int K>
+struct DownAct<FMT_Q8, K> {
+  using type = ActQ8N<Geo<FMT_Q8, K>::CPL>;
+};
+
+// ROWS rows of one expert's down matrix against one h vector (quantized in
+// groups of 16), in three steps that the caller may order as it needs:
+// load_act() reads the h slice, issue() stages the rows' scale bytes and
+// requests the first PD steps of codes, run() computes (requesting the rest)
+// and writes the row results to out[0 .. ROWS).  An out-of-range expert id (a
+// caller error) contributes zero.
+template <int FMT, int K, int ROWS, int PD>
+struct DownRows {
+  using G = Geo<FMT, K>;
+  using SS = ScaleStage<FMT, K, 1, ROWS>;
+  static constexpr bool STAGE = SS::RS::STAGE;
+  static constexpr int NS = (ROWS + G::RPS - 1) / G::RPS;
+  static constexpr int SCALE_BYTES = STAGE ? ROWS * SS::RS::BYTES : 16;
+  static_assert(PD >= 1 && PD <= NS, "steps in flight");
+  typename DownAct<FMT, K>::type act;
+  Piece<FMT> w[NS][G::CPL];
+  EPlanes Dp;
+  int r0;
+  bool valid;
+
+  __device__ __forceinline__ void load_act(const uint8_t* hq, const float* hs) {
+    const int c = (threadIdx.x & 63) % G::LPR;
+    if constexpr (FMT == FMT_Q8) {
+      act.template load<G::LPR, 16>(hq, hs, c);
+    } else {
+      act.template load<G::LPR>(hq, hs, c);
+    }
+  }
+  __device__ __forceinline__ void issue_step(int s) {
+    const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
+    const int j = s * G::RPS + sub;
+    const uint32_t n = (uint32_t)(r0 + (j < ROWS ? j : 0));
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) {
+      w[s][k].template load<G::NB>(Dp, n, c + G::LPR * k);
+      if constexpr (!STAGE) w[s][k].template scales_global<G::NB>(Dp, n, c + G::LPR * k);
+    }
+  }
+  __device__ __forceinline__ void issue(const QMat& m, int e, int E, int row0, uint8_t* my_scales) {
+    valid = (unsigned)e < (unsigned)E;
+    if (!valid) return;
+    Dp = expert_planes<FMT>(m, e);
+    r0 = row0;
+    SS ss;
+    if constexpr (STAGE)
+      ss.issue([&](int, int j, EPlanes& P, uint32_t& row) {
+        P = Dp;
+        row = (uint32_t)(r0 + j);
+      });
+#pragma unroll
+    for (int s = 0; s < PD; s++) issue_step(s);
+    if constexpr (STAGE) ss.store(my_scales);
+  }
+  __device__ __forceinline__ void run(const Iq2Tab* tab, const uint8_t* my_scales, float* out) {
+    const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
+    if (!valid) {
+      if (lane < ROWS) out[lane] = 0.0f;
+      return;
+    }
+    if constexpr (FMT != FMT_Q8) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      if (s + PD < NS) issue_step(s + PD);
+      const int j = s * G::RPS + sub;
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int k = 0; k < G::CPL; k++)
+          w[s][k].template scales_lds<G::NB>(SS::row(my_scales, 0, j < ROWS ? j : 0), c + G::LPR * k);
+      }
+      float v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < G::CPL; k++) v += piece_dot(w[s][k], act, k, tab);
+      v = group_sum<G::LPR>(v);
+      if (c == G::LPR - 1 && j < ROWS) out[j] = v;
+    }
+  }
+};
+
+}  // namespace dec
+}  // namespace qmoe
