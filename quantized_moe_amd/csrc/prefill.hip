@@ -157,27 +157,22 @@ struct BRegs;
 // formed apart so it stays in scalar registers.
 template <>
 struct BRegs<FMT_IQ2> {
-  uint2 p;     // (A, B) words of sub-block 2*g4 + h
-  uint32_t d;  // fp16 bits of the superblock scale
+  uint2 p;  // (A, B) words of sub-block 2*g4 + h (the superblock scale comes in an SGroup)
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
     const uint8_t* base = m.p_a + (row0 * m.nb + sb) * 64;
     p = *reinterpret_cast<const uint2*>(base + (uint32_t)(lrow * m.nb * 64 + 16 * g4 + 8 * h));
-    const uint16_t* sbase = reinterpret_cast<const uint16_t*>(m.p_scale) + row0 * m.nb + sb;
-    d = sbase[(uint32_t)(lrow * m.nb)];
   }
 };
 
 template <>
 struct BRegs<FMT_Q2K> {
   uint2 q;      // quant bytes 16*g4 + 8*h .. +7 (inputs 64*g4 + 32*h .. +31)
-  uint32_t sc;  // scale/min bytes of sub-blocks 4*g4 .. +3
-  uint32_t dm;  // fp16 d | fp16 dmin << 16
+  uint32_t sc;  // scale/min bytes of sub-blocks 4*g4 .. +3 ((d, dmin) come in an SGroup)
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
     const int64_t blk0 = row0 * m.nb + sb;
     const uint32_t lb = (uint32_t)(lrow * m.nb);
     q = *reinterpret_cast<const uint2*>(m.p_b + blk0 * 64 + (lb * 64 + 16 * g4 + 8 * h));
     sc = *reinterpret_cast<const uint32_t*>(m.p_a + blk0 * 16 + (lb * 16 + 4 * g4));
-    dm = *reinterpret_cast<const uint32_t*>(m.p_scale + blk0 * 4 + lb * 4);
   }
 };
 
@@ -191,6 +186,51 @@ struct BRegs<FMT_Q8> {
     q[0] = ld16_stream(m.p_a + blk0 * 32 + lb * 32);
     q[1] = ld16_stream(m.p_a + blk0 * 32 + lb * 32 + 16);
     d = reinterpret_cast<const uint16_t*>(m.p_scale)[blk0 + lb];
+  }
+};
+
+// The superblock scales of PD consecutive superblocks sb0 .. sb0 + PD - 1 of
+// the lane's row, fetched with one load (they are contiguous in the scale
+// plane): IQ2 fp16 d, Q2K (fp16 d, fp16 dmin) pairs.  A vector-memory
+// instruction costs the address unit the same whatever its width, so one
+// load per PD superblocks instead of one per superblock.  (Q8 scales are per
+// 32-input block and stay with the codes.)
+template <int FMT, int PD>
+struct SGroup {
+  static constexpr int NW = FMT == FMT_IQ2 ? (PD + 1) / 2 : FMT == FMT_Q2K ? PD : 1;
+  uint32_t w[NW];
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb0) {
+    if constexpr (FMT == FMT_IQ2) {
+      const uint8_t* p = m.p_scale + ((row0 + lrow) * m.nb + sb0) * 2;
+      if constexpr (PD == 1) w[0] = *reinterpret_cast<const uint16_t*>(p);
+      if constexpr (PD == 2) w[0] = *reinterpret_cast<const uint32_t*>(p);
+      if constexpr (PD == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+      }
+    } else if constexpr (FMT == FMT_Q2K) {
+      const uint8_t* p = m.p_scale + ((row0 + lrow) * m.nb + sb0) * 4;
+      if constexpr (PD == 1) w[0] = *reinterpret_cast<const uint32_t*>(p);
+      if constexpr (PD == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+      }
+      if constexpr (PD == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+      }
+    }
+  }
+  // scale word of superblock sb0 + u (u a compile-time constant)
+  __device__ __forceinline__ uint32_t word(int u) const {
+    if constexpr (FMT == FMT_IQ2) return (w[u >> 1] >> (16 * (u & 1))) & 0xffffu;
+    if constexpr (FMT == FMT_Q2K) return w[u];
+    return 0u;
   }
 };
 
@@ -454,11 +494,18 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   BRegs<FMT> b0[PD], b1[PD];
   // B row of this lane: (first row of the item's N tile, uniform) + lrow
   const int lrow = wv * 16 + c16;
+  // scale groups: *n holds the group of the steps in flight, *c (copied from
+  // *n at the group's first step, after its compute) the current group's
+  SGroup<FMT, PD> g0n, g1n, g0c, g1c;
   auto issueB = [&](int slot, const Item& it, int sb) {
 #pragma unroll
     for (int s = 0; s < PD; s++) {
       if (s == slot) {  // (an item past the end has rows 0 and e = nt = 0: in bounds, unused)
         const int64_t row0 = (int64_t)it.e * a.B0.rows + it.nt * GEMM_BN;
+        if (s == 0) {  // the group's scales first: they return before its codes
+          g0n.load(a.B0, row0, lrow, sb);
+          if constexpr (GATEUP) g1n.load(a.B1, row0, lrow, sb);
+        }
         b0[s].load(a.B0, row0, lrow, sb, g4, h);
         if constexpr (GATEUP) b1[s].load(a.B1, row0, lrow, sb, g4, h);
       }
@@ -472,7 +519,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   // One superblock half-step with NM (a compile-time 1 or 2) active
   // sub-tiles: straight-line code, so the scheduler can overlap the table
   // reads, the fragment arithmetic and the MFMAs of consecutive k32 steps.
-  auto compute = [&](auto nm_c, int slot, int buf) {
+  auto compute = [&](auto nm_c, int slot, int buf, uint32_t sw0, uint32_t sw1) {
     constexpr int NM = decltype(nm_c)::value;
     const BRegs<FMT>& B0 = b0[slot];
     const BRegs<FMT>& B1 = b1[slot];
@@ -530,18 +577,18 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       }
       // superblock epilogue: fp32 scales (and, in the first half, Q2K's min term)
       if constexpr (FMT == FMT_IQ2) {
-        const float d0 = from_h(B0.d), d1 = GATEUP ? from_h(B1.d) : 0.0f;
+        const float d0 = from_h(sw0), d1 = GATEUP ? from_h(sw1) : 0.0f;
 #pragma unroll
         for (int m = 0; m < NM; m++) {
           acc0[m] += d0 * s0[m];
           if constexpr (GATEUP) acc1[m] += d1 * s1[m];
         }
       } else {
-        const float dd0 = from_h(B0.dm & 0xffffu), dmin0 = from_h(B0.dm >> 16);
+        const float dd0 = from_h(sw0 & 0xffffu), dmin0 = from_h(sw0 >> 16);
         float dd1 = 0.0f, dmin1 = 0.0f;
         if constexpr (GATEUP) {
-          dd1 = from_h(B1.dm & 0xffffu);
-          dmin1 = from_h(B1.dm >> 16);
+          dd1 = from_h(sw1 & 0xffffu);
+          dmin1 = from_h(sw1 >> 16);
         }
 #pragma unroll
         for (int m = 0; m < NM; m++) {
@@ -660,8 +707,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         if (sa >= nsb) issueA((u + DA) & 1, j + 1, nxt, sa - nsb);
         else issueA((u + DA) & 1, j, cur, sa);
       }
-      if (cur.nm == 2) compute(std::integral_constant<int, 2>{}, u, s & 1);
-      else compute(std::integral_constant<int, 1>{}, u, s & 1);
+      {
+        const uint32_t sw0 = u == 0 ? g0n.word(0) : g0c.word(u);
+        const uint32_t sw1 = u == 0 ? g1n.word(0) : g1c.word(u);
+        if (cur.nm == 2) compute(std::integral_constant<int, 2>{}, u, s & 1, sw0, sw1);
+        else compute(std::integral_constant<int, 1>{}, u, s & 1, sw0, sw1);
+        if (u == 0) {  // the group's scales are back (its first codes were waited for)
+          g0c = g0n;
+          g1c = g1n;
+        }
+      }
       {  // weights of step s + PD (past the end: in bounds, unused)
         const int sbB = sb + PD;
         if (sbB >= nsb) issueB(u, nxt, sbB - nsb);
