@@ -78,9 +78,31 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 constexpr int RT_E = 8, RT_T = 8;
 
+// x chunk of one lane as loaded (fp32: 4 floats, bf16: 4 values in 2 words),
+// widened to fp32 where it is used, so no load waits on a conversion.
+template <int XDT>
+struct XRaw {
+  uint4 v;
+  __device__ __forceinline__ void load(const void* x, int64_t row_off, int c) {
+    if constexpr (XDT == X_BF16) {
+      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + row_off + 4 * c);
+      v = make_uint4(b.x, b.y, 0u, 0u);
+    } else {
+      v = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + row_off + 4 * c);
+    }
+  }
+  __device__ __forceinline__ float4 f32() const {
+    if constexpr (XDT == X_BF16)
+      return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                         __uint_as_float(v.y & 0xffff0000u));
+    else
+      return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+  }
+};
+
+template <int XDT>
 __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restrict__ W, int E, int d,
-                                                           const void* __restrict__ x, int x_dtype, int T,
-                                                           float* __restrict__ z) {
+                                                           const void* __restrict__ x, int T, float* __restrict__ z) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int e0 = blockIdx.x * RT_E;
@@ -91,24 +113,46 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const float* __restri
   for (int i = 0; i < RT_T; i++)
 #pragma unroll
     for (int j = 0; j < RT_E; j++) acc[i][j] = 0.0f;
+  // Chunk m + 1's operands are requested before chunk m's arithmetic (two
+  // register sets), so the L2 latency overlaps the fused multiply-adds; the
+  // per-lane summation order is unchanged.
   const int chunks = d / 256;
-  for (int m = 0; m < chunks; m++) {
+  float4 wv[2][RT_E];
+  XRaw<XDT> xr[2][RT_T];
+  auto fetch = [&](int set, int m) {
     const int c = lane + 64 * m;
-    float4 wv[RT_E], xv[RT_T];
 #pragma unroll
     for (int j = 0; j < RT_E; j++) {
       const int e = min(e0 + j, E - 1);
-      wv[j] = *reinterpret_cast<const float4*>(W + (int64_t)e * d + 4 * c);
+      const float4 v = *reinterpret_cast<const float4*>(W + (int64_t)e * d + 4 * c);
+      if (set) wv[1][j] = v;
+      else wv[0][j] = v;
     }
 #pragma unroll
     for (int i = 0; i < RT_T; i++) {
       const int t = min(t0 + i, T - 1);
-      xv[i] = load_x4(x, x_dtype, (int64_t)t * d, c);
+      if (set) xr[1][i].load(x, (int64_t)t * d, c);
+      else xr[0][i].load(x, (int64_t)t * d, c);
     }
+  };
+  auto fmas = [&](int set) {
 #pragma unroll
-    for (int i = 0; i < RT_T; i++)
+    for (int i = 0; i < RT_T; i++) {
+      const float4 xv = set ? xr[1][i].f32() : xr[0][i].f32();
 #pragma unroll
-      for (int j = 0; j < RT_E; j++) acc[i][j] = fma4(xv[i], wv[j], acc[i][j]);
+      for (int j = 0; j < RT_E; j++) acc[i][j] = fma4(xv, set ? wv[1][j] : wv[0][j], acc[i][j]);
+    }
+  };
+  fetch(0, 0);
+  if (chunks == 1) {
+    fmas(0);
+  } else {  // d / 256 is a power of two: an even number of chunks
+    for (int m = 0; m < chunks; m += 2) {
+      fetch(1, m + 1);
+      fmas(0);
+      fetch(0, min(m + 2, chunks - 1));  // (after the last pair: a reload that is not used)
+      fmas(1);
+    }
   }
 #pragma unroll
   for (int i = 0; i < RT_T; i++)
@@ -135,7 +179,10 @@ hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtyp
     }
   } else {
     const dim3 grid((E + RT_E - 1) / RT_E, (T + 4 * RT_T - 1) / (4 * RT_T));
-    QMOE_LAUNCH(router_tiled_kernel, grid, dim3(256), 0, s, W, E, d, x, x_dtype, T, z);
+    if (x_dtype == X_BF16)
+      QMOE_LAUNCH(router_tiled_kernel<X_BF16>, grid, dim3(256), 0, s, W, E, d, x, T, z);
+    else
+      QMOE_LAUNCH(router_tiled_kernel<X_F32>, grid, dim3(256), 0, s, W, E, d, x, T, z);
   }
   return hipGetLastError();
 }
