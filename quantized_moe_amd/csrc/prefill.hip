@@ -14,15 +14,21 @@
 //     epilogue; the SwiGLU output h is stored as fp16 (one rounding, 2^-11).
 //
 // One persistent kernel per GEMM (routed gate/up, routed down, shared gate/up,
-// shared down).  A work item is (M tile of 32 rows of one expert's bucket, N
-// tile of 128 output rows): 8 waves own 16 output rows each and both 16-row
-// M sub-tiles, so each decoded B fragment feeds up to two MFMAs per matrix.
+// shared down), 16 waves per block.  A work item is (M tile of 32 rows of one
+// expert's bucket, N tile of output rows); every wave owns 16 output rows and
+// both 16-row M sub-tiles, so each decoded B fragment feeds up to two MFMAs
+// per matrix.  For the 2-bit formats each wave takes whole superblocks (KS =
+// 1, N tile 256): a lane's weights of a superblock are one 16-byte load.  For
+// Q8 (4x the bytes) the two waves of a pair split every superblock's inputs
+// (KS = 2, N tile 128) and their partial sums meet in LDS once per item.
 // The K loop runs over 256-input superblocks and is software-pipelined across
 // work items: every wave keeps its weight loads PD superblocks ahead in
 // registers, the A rows of the next superblock are loaded while the current
 // one is computed and land in the other half of an LDS double buffer, and one
-// barrier per superblock separates the two.  Work items are mapped so that all
-// N tiles of an M tile run on one XCD and share its L2.
+// barrier per superblock separates the two.  The address unit charges every
+// vector load the same, whatever its width, so the loads are as wide as the
+// layout allows.  Work items are mapped so that all N tiles of an M tile run
+// on one XCD and share its L2.
 #include <type_traits>
 
 #include "common.hpp"
@@ -31,10 +37,11 @@
 
 namespace qmoe {
 
-constexpr int GEMM_PAIRS = 8;              // wave pairs: 16 output rows each
-constexpr int GEMM_WAVES = 2 * GEMM_PAIRS;  // the two waves of a pair take the two halves of K
+constexpr int GEMM_PAIRS = 8;              // KS = 2: wave pairs, 16 output rows each
+constexpr int GEMM_WAVES = 2 * GEMM_PAIRS;  // (the two waves of a pair take the two halves of K)
 constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-constexpr int GEMM_BN = 16 * GEMM_PAIRS;    // output rows per work item
+// output rows per work item: 16 per wave, the waves of a pair sharing them (KS = 2) or not (KS = 1)
+__host__ __device__ constexpr int gemm_bn(int ks) { return 16 * GEMM_WAVES / ks; }
 constexpr int BM = PREFILL_BM;            // M rows per work item
 constexpr int NSUB = BM / 16;             // 16-row MFMA sub-tiles
 constexpr int A_PIECES = BM * 32;         // 16-byte pieces of one A superblock chunk
@@ -137,47 +144,73 @@ __device__ void build_q2k_table(uint2* tqs) {
 }
 
 // ---------------------------------------------------------------------------
-// B operand: one lane's weight row, half a superblock at a time.
+// B operand: one lane's weight row, a superblock (KS = 1) or half a
+// superblock (KS = 2) at a time.
 //
 // K order inside a superblock.  MFMA sums over K, so any permutation of the
 // 256 inputs applied to A and B alike gives the same product.  At k32 step q
 // lane group g4 = lane / 16 takes inputs 64*g4 + 8*q .. +7 (not the natural
 // 32*q + 8*g4): each lane then needs one contiguous slice of the block and
-// every field index below is a compile-time constant.  The two waves of a
-// pair split the steps: half h runs q = 4h .. 4h+3, i.e. inputs
-// 64*g4 + 32*h .. +31 -- one IQ2 or Q8 sub-block, two Q2K sub-blocks -- and
-// loads only that slice.  The A rows are laid out in LDS with the same
-// permutation (16-byte piece 8*g4 + q).
+// every field index below is a compile-time constant.  With KS = 1 a wave
+// runs all eight steps and a lane loads inputs 64*g4 .. +63 (two IQ2
+// sub-blocks, four Q2K ones).  With KS = 2 the two waves of a pair split the
+// steps: half h runs q = 4h .. 4h+3, i.e. inputs 64*g4 + 32*h .. +31.  The A
+// rows are laid out in LDS with the same permutation (16-byte piece 8*g4 + q).
 // ---------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int KS>
 struct BRegs;
 
 // load(m, row0, lrow, sb, g4, h): row0 is wave-uniform (the item's first
 // row), lrow the lane's row within it; the uniform part of every address is
 // formed apart so it stays in scalar registers.
-template <>
-struct BRegs<FMT_IQ2> {
-  uint2 p;  // (A, B) words of sub-block 2*g4 + h (the superblock scale comes in an SGroup)
+// KS = 2 (a wave takes half of each superblock's inputs): the lane's slice is
+// inputs 64*g4 + 32*h .. +31, one 8-byte load.  KS = 1 (a wave takes whole
+// superblocks): inputs 64*g4 .. +63, one 16-byte load -- half the load
+// instructions per weight.  Words 2*hh, 2*hh + 1 hold half hh of the slice.
+template <int KS>
+struct BRegs<FMT_IQ2, KS> {
+  uint32_t w[2 * (3 - KS)];  // (A, B) words of sub-block 2*g4 + h, or of 2*g4 and 2*g4 + 1
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
     const uint8_t* base = m.p_a + (row0 * m.nb + sb) * 64;
-    p = *reinterpret_cast<const uint2*>(base + (uint32_t)(lrow * m.nb * 64 + 16 * g4 + 8 * h));
+    if constexpr (KS == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(base + (uint32_t)(lrow * m.nb * 64 + 16 * g4 + 8 * h));
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(base + (uint32_t)(lrow * m.nb * 64 + 16 * g4));
+      w[0] = v.x;
+      w[1] = v.y;
+      w[2] = v.z;
+      w[3] = v.w;
+    }
   }
 };
 
-template <>
-struct BRegs<FMT_Q2K> {
-  uint2 q;      // quant bytes 16*g4 + 8*h .. +7 (inputs 64*g4 + 32*h .. +31)
-  uint32_t sc;  // scale/min bytes of sub-blocks 4*g4 .. +3 ((d, dmin) come in an SGroup)
+template <int KS>
+struct BRegs<FMT_Q2K, KS> {
+  uint32_t q[2 * (3 - KS)];  // quant bytes 16*g4 + 8*h .. +7, or 16*g4 .. +15
+  uint32_t sc;               // scale/min bytes of sub-blocks 4*g4 .. +3 ((d, dmin) come in an SGroup)
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
     const int64_t blk0 = row0 * m.nb + sb;
     const uint32_t lb = (uint32_t)(lrow * m.nb);
-    q = *reinterpret_cast<const uint2*>(m.p_b + blk0 * 64 + (lb * 64 + 16 * g4 + 8 * h));
+    if constexpr (KS == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(m.p_b + blk0 * 64 + (lb * 64 + 16 * g4 + 8 * h));
+      q[0] = v.x;
+      q[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(m.p_b + blk0 * 64 + (lb * 64 + 16 * g4));
+      q[0] = v.x;
+      q[1] = v.y;
+      q[2] = v.z;
+      q[3] = v.w;
+    }
     sc = *reinterpret_cast<const uint32_t*>(m.p_a + blk0 * 16 + (lb * 16 + 4 * g4));
   }
 };
 
-template <>
-struct BRegs<FMT_Q8> {
+template <int KS>
+struct BRegs<FMT_Q8, KS> {
+  static_assert(KS == 2, "Q8 weights use the half-superblock split");
   uint4 q[2];  // quants of block 2*g4 + h of the superblock (32 bytes)
   uint32_t d;  // its fp16 scale
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
@@ -240,16 +273,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 
 // Fragment of local step i (q = 4h + i): 8 exact integers, group i of the
 // lane's sub-block.  S16 = iq2_scale16 of the sub-block, CB = (lane % 16) << 4.
-__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2>& b, int i, uint32_t S16, uint32_t CB,
+template <int KS>
+__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2, KS>& b, int hh, int i, uint32_t S16, uint32_t CB,
                                           const uint8_t* tm, const uint8_t* sgn) {
-  return iq2_frag_words(b.p.x, b.p.y, i, S16, CB, tm, sgn);
+  return iq2_frag_words(b.w[2 * hh], b.w[2 * hh + 1], i, S16, CB, tm, sgn);
 }
 
 // Q2K fragment of local step i: quant bytes 2i, 2i+1 of the lane's 8, whose
 // sub-block scale is sc (SC = sc << 16); lookup byte address of quant byte x
 // is (sc << 8 | x) << 3 = perm(word, SC) >> 5 with x placed in byte 1.
-__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K>& b, int i, uint32_t SC, const uint8_t* tqs) {
-  const uint32_t w = (i >> 1) ? b.q.y : b.q.x;
+template <int KS>
+__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K, KS>& b, int hh, int i, uint32_t SC,
+                                          const uint8_t* tqs) {
+  const uint32_t w = (i >> 1) ? b.q[2 * hh + 1] : b.q[2 * hh];
   const int x0 = 2 * (i & 1);  // quant bytes x0, x0 + 1 of word w
   const uint32_t a0 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((4u + x0) << 8)) >> 5;
   const uint32_t a1 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((5u + x0) << 8)) >> 5;
@@ -260,7 +296,8 @@ __device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K>& b, int i, uint32
 
 // Q2K min-term B fragment (K = the 16 sub-blocks): m_j for j = 4*g4 .. +3,
 // which are exactly the high nibbles of this lane's scale word.
-__device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K>& b) {
+template <int KS>
+__device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K, KS>& b) {
   const uint32_t w = b.sc;
   const uint32_t m0 = (w >> 4) & 15u, m1 = (w >> 12) & 15u, m2 = (w >> 20) & 15u, m3 = (w >> 28) & 15u;
   return make_uint2(to_h((float)m0) | (to_h((float)m1) << 16), to_h((float)m2) | (to_h((float)m3) << 16));
@@ -270,7 +307,7 @@ __device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K>& b) {
 // A quant byte b becomes the exact fp16 integer q: (b ^ 0x80) placed under an
 // fp16 exponent byte 0x64 reads 1024 + q + 128 (one v_perm per pair), minus
 // 1152 (one packed add); one packed multiply by (d, d) then rounds q*d.
-__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8>& b, int i) {
+__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, 2>& b, int i) {
   const uint32_t w0 = word_of(b.q[i >> 1], 2 * (i & 1)) ^ 0x80808080u;
   const uint32_t w1 = word_of(b.q[i >> 1], 2 * (i & 1) + 1) ^ 0x80808080u;
   const f16x2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
@@ -285,7 +322,7 @@ __device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8>& b, int i) {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, int KS>
 struct GemmLds {
   static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
   static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
@@ -293,7 +330,7 @@ struct GemmLds {
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
   static constexpr int kS = FMT == FMT_Q2K ? 2 * 2 * BM * 16 * 2 : 0;  // Q2K sub-block sums: [buf][hi/lo][BM][16]
   static constexpr int kTok = GATEUP ? 3 * BM * 8 : 0;                // token and scale of each row, 3 items
-  static constexpr int kRed = NSUB * 4 * GEMM_PAIRS * 64 * 4;          // one matrix's partial sums of the second halves
+  static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
   static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oA = oTqs + kTqs, oS = oA + kA, oTok = oS + kS,
                        oRed = oTok + kTok, oTiles = oRed + kRed;
   // then tile_start, counts, offsets of the routed experts: [3][E + 1]
@@ -309,9 +346,10 @@ struct Item {
   int nm;      // active 16-row sub-tiles
 };
 
-template <int FMT, bool GATEUP, int PD>
+template <int FMT, bool GATEUP, int PD, int KS>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
-  using L = GemmLds<FMT, GATEUP>;
+  using L = GemmLds<FMT, GATEUP, KS>;
+  constexpr int BN = gemm_bn(KS);  // output rows per work item
   extern __shared__ __align__(16) uint8_t lds[];
   const uint8_t* tm = lds;
   const uint8_t* sgn = lds + L::oSgn;
@@ -326,8 +364,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   int* sOffsets = sCounts + (a.E + 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave % GEMM_PAIRS;  // output rows 16 wv .. of the N tile
-  const int h = wave / GEMM_PAIRS;   // K half: steps q = 4h .. 4h + 3 of every superblock
+  const int wv = KS == 2 ? wave % GEMM_PAIRS : wave;  // output rows 16 wv .. of the N tile
+  const int h = KS == 2 ? wave / GEMM_PAIRS : 0;      // K half: steps q = 4h .. 4h + 3 of every superblock
   const int g4 = lane >> 4, c16 = lane & 15;
 
   if constexpr (FMT == FMT_IQ2)
@@ -342,7 +380,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   }
   __syncthreads();
   const int total_tiles = a.routed ? sTiles[a.E] : (a.n_rows + BM - 1) / BM;
-  const int NT = a.N / GEMM_BN;
+  const int NT = a.N / BN;
   const int nsb = a.K / 256;
 
   // work-item mapping, XCD-aware (blocks are dealt to the 8 XCDs round-robin).
@@ -491,7 +529,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   };
 
   // ---- B rows: PD superblocks in flight ----
-  BRegs<FMT> b0[PD], b1[PD];
+  BRegs<FMT, KS> b0[PD], b1[PD];
   // B row of this lane: (first row of the item's N tile, uniform) + lrow
   const int lrow = wv * 16 + c16;
   // scale groups: *n holds the group of the steps in flight, *c (copied from
@@ -501,7 +539,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < PD; s++) {
       if (s == slot) {  // (an item past the end has rows 0 and e = nt = 0: in bounds, unused)
-        const int64_t row0 = (int64_t)it.e * a.B0.rows + it.nt * GEMM_BN;
+        const int64_t row0 = (int64_t)it.e * a.B0.rows + it.nt * BN;
         if (s == 0) {  // the group's scales first: they return before its codes
           g0n.load(a.B0, row0, lrow, sb);
           if constexpr (GATEUP) g1n.load(a.B1, row0, lrow, sb);
@@ -521,8 +559,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   // reads, the fragment arithmetic and the MFMAs of consecutive k32 steps.
   auto compute = [&](auto nm_c, int slot, int buf, uint32_t sw0, uint32_t sw1) {
     constexpr int NM = decltype(nm_c)::value;
-    const BRegs<FMT>& B0 = b0[slot];
-    const BRegs<FMT>& B1 = b1[slot];
+    const BRegs<FMT, KS>& B0 = b0[slot];
+    const BRegs<FMT, KS>& B1 = b1[slot];
     const uint8_t* A = sA + buf * A_BUF + c16 * A_ROW + g4 * 128 + h * 64;
     auto aread = [&](int m, int i) {
       return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
@@ -545,35 +583,39 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int m = 0; m < NM; m++) s0[m] = s1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t CB = (uint32_t)c16 << 4;
-      uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
-      if constexpr (FMT == FMT_IQ2) {
-        S0 = iq2_scale16(B0.p.y);
-        if constexpr (GATEUP) S1 = iq2_scale16(B1.p.y);
-      } else {
-        sc0 = B0.sc >> (16 * h);  // scale bytes of sub-blocks 4*g4 + 2h, + 1
-        if constexpr (GATEUP) sc1 = B1.sc >> (16 * h);
-      }
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        uint4 f0, f1;
+      for (int hh = 0; hh < 3 - KS; hh++) {  // halves of the lane's slice (one for KS = 2)
+        uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
         if constexpr (FMT == FMT_IQ2) {
-          f0 = iq2_frag(B0, i, S0, CB, tm, sgn);
-          if constexpr (GATEUP) f1 = iq2_frag(B1, i, S1, CB, tm, sgn);
+          S0 = iq2_scale16(B0.w[2 * hh + 1]);
+          if constexpr (GATEUP) S1 = iq2_scale16(B1.w[2 * hh + 1]);
         } else {
-          // low nibble of scale byte i/2, as sc << 16
-          const int sh = 16 - 8 * (i >> 1);
-          f0 = q2k_frag(B0, i, (sc0 << sh) & 0xf0000u, tqs);
-          if constexpr (GATEUP) f1 = q2k_frag(B1, i, (sc1 << sh) & 0xf0000u, tqs);
+          const int hs = KS == 2 ? h : hh;  // scale bytes of sub-blocks 4*g4 + 2hs, + 1
+          sc0 = B0.sc >> (16 * hs);
+          if constexpr (GATEUP) sc1 = B1.sc >> (16 * hs);
         }
 #pragma unroll
-        for (int m = 0; m < NM; m++) {
-          const uint4 av = aread(m, i);
-          s0[m] = mfma32(av, f0, s0[m]);
-          if constexpr (GATEUP) s1[m] = mfma32(av, f1, s1[m]);
+        for (int i = 0; i < 4; i++) {
+          uint4 f0, f1;
+          if constexpr (FMT == FMT_IQ2) {
+            f0 = iq2_frag(B0, hh, i, S0, CB, tm, sgn);
+            if constexpr (GATEUP) f1 = iq2_frag(B1, hh, i, S1, CB, tm, sgn);
+          } else {
+            // low nibble of scale byte i/2, as sc << 16
+            const int sh = 16 - 8 * (i >> 1);
+            f0 = q2k_frag(B0, hh, i, (sc0 << sh) & 0xf0000u, tqs);
+            if constexpr (GATEUP) f1 = q2k_frag(B1, hh, i, (sc1 << sh) & 0xf0000u, tqs);
+          }
+#pragma unroll
+          for (int m = 0; m < NM; m++) {
+            const uint4 av = aread(m, 4 * hh + i);
+            s0[m] = mfma32(av, f0, s0[m]);
+            if constexpr (GATEUP) s1[m] = mfma32(av, f1, s1[m]);
+          }
+          // keep the scheduler from hoisting every step's table reads (and
+          // their registers) to the top: at most two steps overlap
+          if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);
         }
-        // keep the scheduler from hoisting every step's table reads (and
-        // their registers) to the top: at most two steps overlap
-        if (i == 1) __builtin_amdgcn_sched_barrier(0);
       }
       // superblock epilogue: fp32 scales (and, in the first half, Q2K's min term)
       if constexpr (FMT == FMT_IQ2) {
@@ -626,10 +668,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     // computed ahead of the loop and held (spilled) across it
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int wv = (int)(threadIdx.x >> 6) % GEMM_PAIRS, g4 = ln >> 4, c16 = ln & 15, lane = ln;
+    const int wv = KS == 2 ? (int)(threadIdx.x >> 6) % GEMM_PAIRS : (int)(threadIdx.x >> 6);
+    const int g4 = ln >> 4, c16 = ln & 15, lane = ln;
     float* red1 = reinterpret_cast<float*>(sA + freebuf * A_BUF);  // second matrix (gate/up)
     static_assert(NSUB * 4 * GEMM_PAIRS * 64 * 4 <= A_BUF, "partials fit an A buffer");
-    if (h == 1) {
+    if (KS == 2 && h == 1) {
 #pragma unroll
       for (int m = 0; m < NSUB; m++) {
         if (m < it.nm) {
@@ -642,9 +685,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         }
       }
     }
-    __syncthreads();
+    if constexpr (KS == 2) __syncthreads();
     if (h == 0) {
-      const int n = it.nt * GEMM_BN + wv * 16 + c16;  // this lane's output row (B column)
+      const int n = it.nt * BN + wv * 16 + c16;  // this lane's output row (B column)
 #pragma unroll
       for (int m = 0; m < NSUB; m++) {
         if (m < it.nm) {
@@ -652,10 +695,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
           for (int r = 0; r < 4; r++) {
             const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
             const int i = m * 16 + 4 * g4 + r;
-            const float v0 = acc0[m][r] + sRed[o];
+            const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
             if (i < it.rows) {
               if constexpr (GATEUP) {
-                const float v1 = acc1[m][r] + red1[o];
+                const float v1 = KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r];
                 const float xs = sXs[(j % 3) * BM + i];
                 const float hv = silu(v0 * xs) * (v1 * xs);
                 static_cast<_Float16*>(a.out)[(int64_t)(it.p0 + i) * a.N + n] = (_Float16)hv;
@@ -785,12 +828,13 @@ static int num_cus() {
   return g_num_cus;
 }
 
-template <int FMT, bool GATEUP, int PD>
-static hipError_t run_gemm_pd(const GemmArgs& a, int max_items, hipStream_t s) {
+template <int FMT, bool GATEUP, int PD, int KS>
+static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
+  const int max_items = m_tiles * (a.N / gemm_bn(KS));
   const char* name = GATEUP ? (a.routed ? "prefill_gateup" : "prefill_shared_gateup")
                             : (a.routed ? "prefill_down" : "prefill_shared_down");
-  using L = GemmLds<FMT, GATEUP>;
-  auto kern = gemm_kernel<FMT, GATEUP, PD>;
+  using L = GemmLds<FMT, GATEUP, KS>;
+  auto kern = gemm_kernel<FMT, GATEUP, PD, KS>;
   const int bytes = L::bytes_for(a.routed ? a.E : 0);
   static bool attr_set = false;
   if (!attr_set) {
@@ -818,16 +862,25 @@ static hipError_t run_gemm_pd(const GemmArgs& a, int max_items, hipStream_t s) {
 }
 
 template <int FMT, bool GATEUP>
-static hipError_t run_gemm(const GemmArgs& a, int max_items, hipStream_t s) {
+static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int nsb = a.K / 256;
-  // Superblocks of weights kept in flight per wave.  At 16 waves per CU a
-  // wave has 128 VGPRs: the two-matrix gate/up kernels and the Q8 kernels (4x
-  // the bytes per superblock) hold two superblocks, the 2-bit down kernels four.
+  // 2-bit formats: a wave takes whole superblocks (KS = 1, 16-byte weight
+  // loads).  Q8 (4x the bytes per superblock): the two waves of a pair split
+  // each superblock (KS = 2).  Superblocks kept in flight (PD) per wave, at
+  // 128 VGPRs per wave (16 waves per CU).
   if constexpr (FMT != FMT_Q8) {
-    if (!GATEUP && nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4>(a, max_items, s);
+    if constexpr (!GATEUP) {
+      if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
+    }
+    // (two Q2K matrices hold more registers per superblock than two IQ2 ones)
+    if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
+      if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+    }
+    return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+  } else {
+    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 2>(a, m_tiles, s);
+    return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
   }
-  if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2>(a, max_items, s);
-  return run_gemm_pd<FMT, GATEUP, 1>(a, max_items, s);
 }
 
 #define PF_FMT_SWITCH(fmt, F, ...)                                     \
@@ -868,8 +921,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.H;
-    const int max_items = (n / BM + P.E) * (P.f / GEMM_BN);
-    PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true>(a, max_items, s)))
+    const int m_tiles = n / BM + P.E;
+    PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   // routed down -> Ye (fp32, bucket order); same M tiles as the gate/up GEMM
@@ -889,8 +942,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.Ye;
-    const int max_items = (n / BM + P.E) * (P.d / GEMM_BN);
-    PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false>(a, max_items, s)))
+    const int m_tiles = n / BM + P.E;
+    PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   if (P.has_shared) {
@@ -908,8 +961,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.E = 1;
     a.k = 1;
     a.out = P.Hs;
-    const int max_items = ((P.T + BM - 1) / BM) * (P.f / GEMM_BN);
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, max_items, s)))
+    const int m_tiles = (P.T + BM - 1) / BM;
+    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
     GemmArgs b{};
     b.B0 = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
@@ -923,8 +976,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     b.E = 1;
     b.k = 1;
     b.out = P.Ysh;
-    const int max_items2 = ((P.T + BM - 1) / BM) * (P.d / GEMM_BN);
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false>(b, max_items2, s)))
+    const int m_tiles2 = (P.T + BM - 1) / BM;
+    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false>(b, m_tiles2, s)))
     if (err != hipSuccess) return err;
   }
   const int pid = prof_begin("prefill_combine", s);
