@@ -17,10 +17,11 @@
 // shared down), 16 waves per block.  A work item is (M tile of 32 rows of one
 // expert's bucket, N tile of output rows); every wave owns 16 output rows and
 // both 16-row M sub-tiles, so each decoded B fragment feeds up to two MFMAs
-// per matrix.  For the 2-bit formats each wave takes whole superblocks (KS =
-// 1, N tile 256): a lane's weights of a superblock are one 16-byte load.  For
-// Q8 (4x the bytes) the two waves of a pair split every superblock's inputs
-// (KS = 2, N tile 128) and their partial sums meet in LDS once per item.
+// per matrix.  Each wave takes whole superblocks (KS = 1, N tile 256): a
+// lane's weights of a superblock are one 16-byte load for the 2-bit formats.
+// Only the Q8 gate/up (two matrices of 4x the bytes, which would spill) has
+// the two waves of a pair split every superblock's inputs (KS = 2, N tile
+// 128), their partial sums meeting in LDS once per item.
 // The K loop runs over 256-input superblocks and is software-pipelined across
 // work items: every wave keeps its weight loads PD superblocks ahead in
 // registers, the A rows of the next superblock are loaded while the current
@@ -210,15 +211,17 @@ struct BRegs<FMT_Q2K, KS> {
 
 template <int KS>
 struct BRegs<FMT_Q8, KS> {
-  static_assert(KS == 2, "Q8 weights use the half-superblock split");
-  uint4 q[2];  // quants of block 2*g4 + h of the superblock (32 bytes)
-  uint32_t d;  // its fp16 scale
+  uint4 q[2 * (3 - KS)];  // quants of block 2*g4 + h (32 bytes), or of blocks 2*g4, 2*g4 + 1 (64 bytes)
+  uint32_t d;             // fp16 scale of each block (KS = 1: both, one 4-byte load)
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
     const int64_t blk0 = row0 * m.nb + sb * 8;
-    const uint32_t lb = (uint32_t)(lrow * m.nb + 2 * g4 + h);
-    q[0] = ld16_stream(m.p_a + blk0 * 32 + lb * 32);
-    q[1] = ld16_stream(m.p_a + blk0 * 32 + lb * 32 + 16);
-    d = reinterpret_cast<const uint16_t*>(m.p_scale)[blk0 + lb];
+    const uint32_t lb = (uint32_t)(lrow * m.nb + 2 * g4 + (KS == 2 ? h : 0));
+#pragma unroll
+    for (int i = 0; i < 2 * (3 - KS); i++) q[i] = ld16_stream(m.p_a + blk0 * 32 + lb * 32 + 16 * i);
+    if constexpr (KS == 2)
+      d = reinterpret_cast<const uint16_t*>(m.p_scale)[blk0 + lb];
+    else
+      d = *reinterpret_cast<const uint32_t*>(m.p_scale + (blk0 + lb) * 2);
   }
 };
 
@@ -307,11 +310,13 @@ __device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K, KS>& b) {
 // A quant byte b becomes the exact fp16 integer q: (b ^ 0x80) placed under an
 // fp16 exponent byte 0x64 reads 1024 + q + 128 (one v_perm per pair), minus
 // 1152 (one packed add); one packed multiply by (d, d) then rounds q*d.
-__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, 2>& b, int i) {
-  const uint32_t w0 = word_of(b.q[i >> 1], 2 * (i & 1)) ^ 0x80808080u;
-  const uint32_t w1 = word_of(b.q[i >> 1], 2 * (i & 1) + 1) ^ 0x80808080u;
+template <int KS>
+__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, KS>& b, int hh, int i) {
+  const uint32_t w0 = word_of(b.q[2 * hh + (i >> 1)], 2 * (i & 1)) ^ 0x80808080u;
+  const uint32_t w1 = word_of(b.q[2 * hh + (i >> 1)], 2 * (i & 1) + 1) ^ 0x80808080u;
   const f16x2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const f16x2_t dd = {__builtin_bit_cast(_Float16, (uint16_t)b.d), __builtin_bit_cast(_Float16, (uint16_t)b.d)};
+  const uint16_t dh = (uint16_t)(b.d >> (16 * hh));
+  const f16x2_t dd = {__builtin_bit_cast(_Float16, dh), __builtin_bit_cast(_Float16, dh)};
   auto pair = [&](uint32_t w, uint32_t sel) {
     const f16x2_t q = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(w, 0x64646464u, sel)) + bias;
     return __builtin_bit_cast(uint32_t, q * dd);
@@ -567,15 +572,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     };
     if constexpr (FMT == FMT_Q8) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const uint4 f0 = q8_frag(B0, i);
-        uint4 f1;
-        if constexpr (GATEUP) f1 = q8_frag(B1, i);
+      for (int hh = 0; hh < 3 - KS; hh++) {
 #pragma unroll
-        for (int m = 0; m < NM; m++) {
-          const uint4 av = aread(m, i);
-          acc0[m] = mfma32(av, f0, acc0[m]);
-          if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
+        for (int i = 0; i < 4; i++) {
+          const uint4 f0 = q8_frag(B0, hh, i);
+          uint4 f1;
+          if constexpr (GATEUP) f1 = q8_frag(B1, hh, i);
+#pragma unroll
+          for (int m = 0; m < NM; m++) {
+            const uint4 av = aread(m, 4 * hh + i);
+            acc0[m] = mfma32(av, f0, acc0[m]);
+            if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
+          }
+          if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live fragments
         }
       }
     } else {
@@ -865,9 +874,8 @@ template <int FMT, bool GATEUP>
 static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int nsb = a.K / 256;
   // 2-bit formats: a wave takes whole superblocks (KS = 1, 16-byte weight
-  // loads).  Q8 (4x the bytes per superblock): the two waves of a pair split
-  // each superblock (KS = 2).  Superblocks kept in flight (PD) per wave, at
-  // 128 VGPRs per wave (16 waves per CU).
+  // loads).  Superblocks kept in flight (PD) per wave, at 128 VGPRs per wave
+  // (16 waves per CU).
   if constexpr (FMT != FMT_Q8) {
     if constexpr (!GATEUP) {
       if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
@@ -878,6 +886,12 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
     }
     return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
   } else {
+    // Q8: whole superblocks for the one-matrix down GEMM; the two-matrix
+    // gate/up keeps the pair split (whole superblocks of two matrices spill)
+    if constexpr (!GATEUP) {
+      if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+      return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+    }
     if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 2>(a, m_tiles, s);
     return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
   }
