@@ -265,6 +265,25 @@ def test_repack_round_trip(decode_layer):
         assert np.array_equal(back.cpu().numpy(), canon), name
 
 
+@pytest.mark.parametrize("fmt", [synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8])
+def test_repack_round_trip_all_widths(fmt):
+    """Canonical -> device -> canonical is the identity for every row width,
+    including the Q2K scale plane's partial superblock groups (1 or 2
+    superblocks per row)."""
+    rng = np.random.default_rng(fmt)
+    for K in (256, 512, 1024, 2048, 8192):
+        E, rows = 3, 5
+        n = E * rows * (K // (32 if fmt == synth.FMT_Q8 else 256)) * {1: 66, 2: 84, 3: 34}[fmt]
+        canon = rng.integers(0, 256, n, dtype=np.uint8)
+        src = torch.from_numpy(canon).to(DEV)
+        dev_buf = torch.empty_like(src)
+        back = torch.empty_like(src)
+        lib.repack(fmt, E, rows, K, src, dev_buf, lib.MOE_REPACK_TO_DEVICE)
+        lib.repack(fmt, E, rows, K, dev_buf, back, lib.MOE_REPACK_TO_CANONICAL)
+        torch.cuda.synchronize()
+        assert np.array_equal(back.cpu().numpy(), canon), (fmt, K)
+
+
 def test_long_prefill_eight_layers():
     """8 layers of the decode shape, 4096 bf16 tokens, Zipf(1.1) routes (caller
     supplied): buckets bit-exact, outputs on tokens of the lightest and the
