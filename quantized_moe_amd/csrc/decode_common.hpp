@@ -251,6 +251,34 @@ struct XOctet {
       if (hg == 0) sc[ch] = s;
     }
   }
+  // The same chunks as two signed byte planes (loaded with layout NIB_NAT):
+  // X = 256 H + L, |X| <= 32512, one scale per chunk; group u of a chunk is
+  // 32 bytes, H of its 16 values then L (see ActQ8B::load).
+  __device__ __forceinline__ void store_bytes(int nch, uint8_t* q, float* sc) const {
+    float m = 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; n++) m = fmaxf(m, fabsf(v[n]));
+    m = fmaxf(m, dpp_f<0x111, 0xf>(m));
+    m = fmaxf(m, dpp_f<0x112, 0xf>(m));
+    m = fmaxf(m, dpp_f<0x114, 0xf>(m));
+    m = __shfl(m, (int)((threadIdx.x & 63) | 7), 64);  // the chunk's last lane holds its maximum
+    const float inv = m > 0.0f ? 32512.0f / m : 0.0f;
+    uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+    for (int n = 0; n < 8; n++) {
+      const int X = (int)rintf(v[n] * inv);
+      const int Hh = (X + 128) >> 8;  // in [-127, 127]
+      const int Ll = X - (Hh << 8);   // in [-128, 127]
+      hw[n >> 2] |= ((uint32_t)Hh & 255u) << (8 * (n & 3));
+      lw[n >> 2] |= ((uint32_t)Ll & 255u) << (8 * (n & 3));
+    }
+    if (ch < nch) {
+      uint8_t* g = q + (int64_t)ch * CHUNK_BYTES + 32 * (hg >> 1) + 8 * (hg & 1);
+      *reinterpret_cast<uint2*>(g) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(g + 16) = make_uint2(lw[0], lw[1]);
+      if (hg == 0) sc[ch] = m / 32512.0f;
+    }
+  }
 };
 
 __device__ __forceinline__ void quant_x8(const void* x, int x_dtype, int nch, int c0, int layout, uint8_t* q,
@@ -431,6 +459,26 @@ template <int CPL>
 struct ActQ8B {
   uint32_t H[CPL][4], L[CPL][4];
   float s[CPL];
+  // pieces c + LPR k from chunks stored by XOctet::store_bytes (one scale
+  // per chunk of four pieces)
+  template <int LPR>
+  __device__ __forceinline__ void load(const uint8_t* q, const float* sc, int c) {
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
+      const int pc = c + LPR * k;
+      const uint4 hv = ld16(q + (int64_t)pc * G16_BYTES);
+      const uint4 lv = ld16(q + (int64_t)pc * G16_BYTES + 16);
+      H[k][0] = hv.x;
+      H[k][1] = hv.y;
+      H[k][2] = hv.z;
+      H[k][3] = hv.w;
+      L[k][0] = lv.x;
+      L[k][1] = lv.y;
+      L[k][2] = lv.z;
+      L[k][3] = lv.w;
+      s[k] = sc[pc / 4];
+    }
+  }
   __device__ __forceinline__ void quantize_piece(const float* x, int k) {
     float m = 0.0f;
 #pragma unroll
