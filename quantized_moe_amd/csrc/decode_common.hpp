@@ -42,27 +42,26 @@ namespace dec {
 constexpr int WAVES = 8;
 constexpr int THREADS = 64 * WAVES;
 constexpr int XMAX = 0x7777;      // |X| bound of the fixed-point activations
-constexpr int G16_BYTES = 32;     // one quantized group of 16 activations: 2 halves x 4 planes x 4 B
+constexpr int G16_BYTES = 32;     // one quantized group of 16 activations (nibble or byte planes)
 constexpr int CHUNK_BYTES = 128;  // 64 activations (four groups)
 constexpr int DN_ROWS = 16;       // down rows per block of the last kernel
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
-// Order of the 16 activations of a group inside its two halves x 8 nibbles,
-// chosen per consuming weight format so that weight words need no shuffling:
-//   NAT (IQ2): half hh holds elements 8 hh .. 8 hh + 7, nibble n = element n;
-//   Q2K      : half hh holds the elements of parity hh, nibble n = element 2n + hh
-//              (Q2K fields 0/2 and 1/3 of each quant byte);
-//   Q8       : half hh holds elements 8 hh + 0..7 with nibble 2i = element i and
-//              nibble 2i + 1 = element 4 + i (so the even and odd nibbles widen
-//              to the bytes of two consecutive int8 weight words).
-enum : int { NIB_NAT = 0, NIB_Q2K = 1, NIB_Q8 = 2 };
+// How the 16 activations of a group are stored (32 bytes), chosen per
+// consuming weight format so that weight words need no shuffling:
+//   NAT (IQ2): 4-bit digit planes, half hh holds elements 8 hh .. 8 hh + 7,
+//              nibble n = element n;
+//   Q2K      : 4-bit digit planes, half hh holds the elements of parity hh,
+//              nibble n = element 2n + hh (Q2K fields 0/2 and 1/3 of each
+//              quant byte);
+//   Q8       : two signed byte planes, X = 256 H + L with |X| <= 32512: bytes
+//              0..15 are H of elements 0..15, bytes 16..31 their L (each plane
+//              meets the int8 weight words directly, 8 dot4 per 16 weights).
+enum : int { NIB_NAT = 0, NIB_Q2K = 1, Q8_BYTES = 2 };
+constexpr int Q8_XMAX = 32512;  // |X| bound of the byte-plane activations
 
 __host__ __device__ constexpr int nib_layout(int fmt) {
-  return fmt == FMT_Q2K ? NIB_Q2K : (fmt == FMT_Q8 ? NIB_Q8 : NIB_NAT);
-}
-
-__host__ __device__ constexpr int nib_elem(int layout, int hh, int n) {
-  return layout == NIB_Q2K ? 2 * n + hh : (layout == NIB_Q8 ? 8 * hh + ((n & 1) ? 4 + (n >> 1) : (n >> 1)) : 8 * hh + n);
+  return fmt == FMT_Q2K ? NIB_Q2K : (fmt == FMT_Q8 ? Q8_BYTES : NIB_NAT);
 }
 
 // A row of K inputs in format FMT: 16-byte pieces, lanes per row, pieces per
@@ -108,63 +107,31 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Maximum of v >= 0 over each 16-lane row (GROUP = 16) or the wave (GROUP =
-// 64), returned to every lane of the row / wave.
-template <int GROUP>
-__device__ __forceinline__ float group_max_nonneg(float v) {
-  v = fmaxf(v, dpp_f<0x111, 0xf>(v));
-  v = fmaxf(v, dpp_f<0x112, 0xf>(v));
-  v = fmaxf(v, dpp_f<0x114, 0xf>(v));
-  v = fmaxf(v, dpp_f<0x118, 0xf>(v));  // lane 15 of each row holds the row maximum
-  if constexpr (GROUP == 16) {
-    return __shfl(v, (int)((threadIdx.x & 63) | 15), 64);
-  } else {
-    v = fmaxf(v, dpp_f<0x142, 0xa>(v));
-    v = fmaxf(v, dpp_f<0x143, 0xc>(v));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  }
-}
-
 __device__ __forceinline__ uint32_t to_digits(float v, float inv) {
   const int X = (int)rintf(v * inv);  // |X| <= XMAX
   return ((uint32_t)(X + 0x8888) ^ 0x8888u) & 0xffffu;
 }
 
-// Quantize 64 values (lane e holds element e of 4 consecutive groups of 16)
-// with one scale per GROUP lanes, and write the groups' nibble planes in
-// `layout`: 32 bytes per group at out, scales at scale_out[e / GROUP].  Only
-// the first n_groups groups are written.
-template <int GROUP>
-__device__ __forceinline__ void quant_wave(float v, int layout, uint8_t* __restrict__ out,
-                                           float* __restrict__ scale_out, int n_groups) {
-  const int lane = threadIdx.x & 63;
-  const float m = group_max_nonneg<GROUP>(fabsf(v));
-  const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
-  const uint32_t Z = to_digits(v, inv);
-  const int q = (lane >> 3) & 3, hh = (lane >> 2) & 1, p = lane & 3;  // word of lanes 0..31
-  uint32_t word = 0;
-#pragma unroll
-  for (int n = 0; n < 8; n++) {
-    const uint32_t z = (uint32_t)__shfl((int)Z, 16 * q + nib_elem(layout, hh, n), 64);
-    word |= ((z >> (4 * p)) & 15u) << (4 * n);
-  }
-  if (lane < 32 && q < n_groups) reinterpret_cast<uint32_t*>(out)[lane] = word;
-  if ((lane % GROUP) == 0 && lane / 16 < n_groups) scale_out[lane / GROUP] = m / (float)XMAX;
-}
-
-// Lane-parallel quantization: each lane turns 8 values (one half of a group
-// of 16, already in the nibble order of the layout) into its 4 plane words;
-// GL consecutive lanes share one scale (GL = 8: a chunk of 64, GL = 2: a
-// group of 16).  Returns the 4 words; *scale is the unit's scale.
+// Maximum of |v[0..7]| over each aligned unit of GL lanes (GL = 8: a chunk
+// of 64 values, GL = 2: a group of 16), returned to every lane of the unit.
 template <int GL>
-__device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
+__device__ __forceinline__ float unit_max8(const float* v) {
   float m = 0.0f;
 #pragma unroll
   for (int n = 0; n < 8; n++) m = fmaxf(m, fabsf(v[n]));
   if constexpr (GL >= 2) m = fmaxf(m, dpp_f<0x111, 0xf>(m));
   if constexpr (GL >= 4) m = fmaxf(m, dpp_f<0x112, 0xf>(m));
   if constexpr (GL >= 8) m = fmaxf(m, dpp_f<0x114, 0xf>(m));
-  m = __shfl(m, (int)((threadIdx.x & 63) | (GL - 1)), 64);  // the unit's last lane holds its maximum
+  return __shfl(m, (int)((threadIdx.x & 63) | (GL - 1)), 64);  // the unit's last lane holds its maximum
+}
+
+// Lane-parallel quantization to digit planes: each lane turns 8 values (one
+// half of a group of 16, already in the nibble order of the layout) into its
+// 4 plane words; GL consecutive lanes share one scale.  Returns the 4 words;
+// *scale is the unit's scale.
+template <int GL>
+__device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
+  const float m = unit_max8<GL>(v);
   const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
   scale = m / (float)XMAX;
   uint32_t Z[8];
@@ -179,6 +146,29 @@ __device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
     w[p] = word;
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The same to byte planes (Q8 consumers): 8 values in natural order become
+// 8 H bytes and 8 L bytes, X = 256 H + L = rint(v 32512 / m).  Writes H to
+// hq[0..8) and L to hq[16..24); *scale is the unit's scale.
+template <int GL>
+__device__ __forceinline__ void quant8_bytes(const float* v, uint8_t* hq, float& scale) {
+  const float m = unit_max8<GL>(v);
+  const float inv = m > 0.0f ? (float)Q8_XMAX / m : 0.0f;
+  scale = m / (float)Q8_XMAX;
+  uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+  for (int n = 0; n < 8; n++) {
+    const int X = (int)rintf(v[n] * inv);
+    const int Hh = (X + 128) >> 8;  // floor((X + 128) / 256), in [-127, 127]
+    const int Ll = X - (Hh << 8);   // in [-128, 127]
+    hw[n >> 2] |= ((uint32_t)Hh & 255u) << (8 * (n & 3));
+    lw[n >> 2] |= ((uint32_t)Ll & 255u) << (8 * (n & 3));
+  }
+  if (hq) {
+    *reinterpret_cast<uint2*>(hq) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2*>(hq + 16) = make_uint2(lw[0], lw[1]);
+  }
 }
 
 // The 8 values of half hh of the group of 16 starting at element e16 of an
@@ -201,7 +191,7 @@ __device__ __forceinline__ void load_half_f32(const float* src, int64_t e16, int
     const float4 f1 = *reinterpret_cast<const float4*>(src + e16 + 8 * hh + 4);
     const float a[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-    for (int n = 0; n < 8; n++) v[n] = layout == NIB_Q8 ? a[(n & 1) ? 4 + (n >> 1) : (n >> 1)] : a[n];
+    for (int n = 0; n < 8; n++) v[n] = a[n];
   }
 }
 
@@ -218,18 +208,16 @@ __device__ __forceinline__ void load_half_bf16(const uint16_t* src, int64_t e16,
   // stays in registers
 #pragma unroll
   for (int n = 0; n < 8; n++) {
-    const int q8 = (n & 1) ? 4 + (n >> 1) : (n >> 1);
     const float q2k = hh ? a[2 * n + 1] : a[2 * n];
-    const float nq8 = hh ? a[8 + q8] : a[q8];
     const float nat = hh ? a[8 + n] : a[n];
-    v[n] = layout == NIB_Q2K ? q2k : (layout == NIB_Q8 ? nq8 : nat);
+    v[n] = layout == NIB_Q2K ? q2k : nat;
   }
 }
 
 // Quantize chunks [c0, c0 + 8) of 64 values of x (fp32 or bf16, nch chunks
 // in all, x taken as one flat vector) with one wave: lane L takes half L % 8
-// of chunk c0 + L / 8.  Chunk ch goes to q + 128 ch (groups of 32 bytes,
-// halves of 16), its scale to sc[ch].  load() only issues the loads.
+// of chunk c0 + L / 8.  Chunk ch goes to q + 128 ch (groups of 32 bytes in
+// the layout's form), its scale to sc[ch].  load() only issues the loads.
 struct XOctet {
   float v[8];
   int ch, hg;
@@ -243,41 +231,18 @@ struct XOctet {
     else
       load_half_f32(static_cast<const float*>(x), 64 * (int64_t)chc + 16 * (hg >> 1), hg & 1, layout, v);
   }
-  __device__ __forceinline__ void store(int nch, uint8_t* q, float* sc) const {
+  // Digit planes (16 bytes per lane) or, for layout Q8_BYTES, byte planes
+  // (8 H bytes and 8 L bytes per lane); one scale per chunk.
+  __device__ __forceinline__ void store(int nch, uint8_t* q, float* sc, int layout) const {
     float s;
-    const uint4 w = quant8<8>(v, s);
-    if (ch < nch) {
-      *reinterpret_cast<uint4*>(q + (int64_t)ch * CHUNK_BYTES + 16 * hg) = w;
-      if (hg == 0) sc[ch] = s;
+    uint8_t* g = q + (int64_t)(ch < nch ? ch : 0) * CHUNK_BYTES;
+    if (layout == Q8_BYTES) {
+      quant8_bytes<8>(v, ch < nch ? g + 32 * (hg >> 1) + 8 * (hg & 1) : nullptr, s);
+    } else {
+      const uint4 w = quant8<8>(v, s);
+      if (ch < nch) *reinterpret_cast<uint4*>(g + 16 * hg) = w;
     }
-  }
-  // The same chunks as two signed byte planes (loaded with layout NIB_NAT):
-  // X = 256 H + L, |X| <= 32512, one scale per chunk; group u of a chunk is
-  // 32 bytes, H of its 16 values then L (see ActQ8B::load).
-  __device__ __forceinline__ void store_bytes(int nch, uint8_t* q, float* sc) const {
-    float m = 0.0f;
-#pragma unroll
-    for (int n = 0; n < 8; n++) m = fmaxf(m, fabsf(v[n]));
-    m = fmaxf(m, dpp_f<0x111, 0xf>(m));
-    m = fmaxf(m, dpp_f<0x112, 0xf>(m));
-    m = fmaxf(m, dpp_f<0x114, 0xf>(m));
-    m = __shfl(m, (int)((threadIdx.x & 63) | 7), 64);  // the chunk's last lane holds its maximum
-    const float inv = m > 0.0f ? 32512.0f / m : 0.0f;
-    uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
-#pragma unroll
-    for (int n = 0; n < 8; n++) {
-      const int X = (int)rintf(v[n] * inv);
-      const int Hh = (X + 128) >> 8;  // in [-127, 127]
-      const int Ll = X - (Hh << 8);   // in [-128, 127]
-      hw[n >> 2] |= ((uint32_t)Hh & 255u) << (8 * (n & 3));
-      lw[n >> 2] |= ((uint32_t)Ll & 255u) << (8 * (n & 3));
-    }
-    if (ch < nch) {
-      uint8_t* g = q + (int64_t)ch * CHUNK_BYTES + 32 * (hg >> 1) + 8 * (hg & 1);
-      *reinterpret_cast<uint2*>(g) = make_uint2(hw[0], hw[1]);
-      *reinterpret_cast<uint2*>(g + 16) = make_uint2(lw[0], lw[1]);
-      if (hg == 0) sc[ch] = m / 32512.0f;
-    }
+    if (ch < nch && hg == 0) sc[ch] = s;
   }
 };
 
@@ -285,7 +250,7 @@ __device__ __forceinline__ void quant_x8(const void* x, int x_dtype, int nch, in
                                          float* sc) {
   XOctet o;
   o.load(x, x_dtype, nch, c0, layout);
-  o.store(nch, q, sc);
+  o.store(nch, q, sc, layout);
 }
 
 // Quantize groups [g0, g0 + 32) of 16 fp32 values (ng groups in all) with one
@@ -297,11 +262,14 @@ __device__ __forceinline__ void quant_g32(const float* h, int ng, int g0, int la
   float v[8];
   load_half_f32(h, 16 * (int64_t)gc, hh, layout, v);
   float s;
-  const uint4 w = quant8<2>(v, s);
-  if (g < ng) {
-    *reinterpret_cast<uint4*>(q + (int64_t)g * G16_BYTES + 16 * hh) = w;
-    if (hh == 0) sc[g] = s;
+  uint8_t* p = q + (int64_t)(g < ng ? g : 0) * G16_BYTES;
+  if (layout == Q8_BYTES) {
+    quant8_bytes<2>(v, g < ng ? p + 8 * hh : nullptr, s);
+  } else {
+    const uint4 w = quant8<2>(v, s);
+    if (g < ng) *reinterpret_cast<uint4*>(p + 16 * hh) = w;
   }
+  if (g < ng && hh == 0) sc[g] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -358,110 +326,17 @@ struct ActNib {
         if constexpr (PER16) As[k][u] = s[k][u] * (float)Ai[k][u];
       }
   }
-  // lane-local quantization of 64 consecutive fp32 inputs per piece (chunk
-  // scaled): v points at input 0 of the row
-  template <int LPR>
-  __device__ __forceinline__ void from_f32(const float* v, int c, int layout) {
-    static_assert(!PER16, "lane-local quantization is chunk-scaled");
-#pragma unroll
-    for (int k = 0; k < CPL; k++) {
-      const int pc = c + LPR * k;
-      float x[64];
-#pragma unroll
-      for (int j = 0; j < 16; j++) {
-        const float4 f = *reinterpret_cast<const float4*>(v + 64 * pc + 4 * j);
-        x[4 * j] = f.x;
-        x[4 * j + 1] = f.y;
-        x[4 * j + 2] = f.z;
-        x[4 * j + 3] = f.w;
-      }
-      quantize_local(x, k, layout);
-    }
-  }
-  template <int LPR>
-  __device__ __forceinline__ void from_bf16(const uint16_t* v, int c, int layout) {
-    static_assert(!PER16, "lane-local quantization is chunk-scaled");
-#pragma unroll
-    for (int k = 0; k < CPL; k++) {
-      const int pc = c + LPR * k;
-      float x[64];
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const uint4 b = ld16(v + 64 * pc + 8 * j);
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          x[8 * j + 2 * i] = __uint_as_float(bw[i] << 16);
-          x[8 * j + 2 * i + 1] = __uint_as_float(bw[i] & 0xffff0000u);
-        }
-      }
-      quantize_local(x, k, layout);
-    }
-  }
-  __device__ __forceinline__ void quantize_local(const float* x, int k, int layout) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 64; i++) m = fmaxf(m, fabsf(x[i]));
-    const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
-    s[k][0] = m / (float)XMAX;
-    uint32_t Z[64];
-#pragma unroll
-    for (int i = 0; i < 64; i++) Z[i] = to_digits(x[i], inv);
-#pragma unroll
-    for (int u = 0; u < 4; u++)
-#pragma unroll
-      for (int hh = 0; hh < 2; hh++)
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int n = 0; n < 8; n++) {
-            const int e = 16 * u + (layout == NIB_Q2K ? 2 * n + hh : 8 * hh + n);
-            word |= ((Z[e] >> (4 * p)) & 15u) << (4 * n);
-          }
-          w[k][u][hh][p] = word;
-        }
-  }
 };
 
-// Q8 pieces (16 inputs = one group) from quantized groups: the digit planes
-// widened to bytes 16 D_p (even nibbles -> the first weight word of a half,
-// odd nibbles -> the second).  One scale per piece.
-template <int CPL>
-struct ActQ8N {
-  uint32_t e[CPL][2][4][2];
-  float s[CPL];
-  // GSCALE: 16 for group-quantized h (scale per piece), 64 for chunk-quantized x
-  template <int LPR, int GSCALE>
-  __device__ __forceinline__ void load(const uint8_t* q, const float* sc, int c) {
-#pragma unroll
-    for (int k = 0; k < CPL; k++) {
-      const int pc = c + LPR * k;
-      const uint8_t* p = q + (int64_t)pc * G16_BYTES;
-#pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        const uint4 v = ld16(p + 16 * hh);
-        const uint32_t N[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int pl = 0; pl < 4; pl++) {
-          e[k][hh][pl][0] = (N[pl] << 4) & 0xf0f0f0f0u;
-          e[k][hh][pl][1] = N[pl] & 0xf0f0f0f0u;
-        }
-      }
-      s[k] = sc[GSCALE == 16 ? pc : pc / 4] * 0.0625f;  // bytes carry 16 D_p
-    }
-  }
-};
-
-// Q8 pieces from lane-local 16-bit quantization of fp32 inputs: two byte
-// planes H, L with X = 256 H + L, |X| <= 32512, one scale per piece.
+// Q8 pieces (16 inputs = one group) as two signed byte planes H, L with
+// X = 256 H + L (layout Q8_BYTES), one scale per piece.
 template <int CPL>
 struct ActQ8B {
   uint32_t H[CPL][4], L[CPL][4];
   float s[CPL];
-  // pieces c + LPR k from chunks stored by XOctet::store_bytes (one scale
-  // per chunk of four pieces)
-  template <int LPR>
+  // pieces c + LPR k of groups at q; GSCALE: 16 for group-quantized h
+  // (scale per piece), 64 for chunk-quantized x (scale per four pieces)
+  template <int LPR, int GSCALE>
   __device__ __forceinline__ void load(const uint8_t* q, const float* sc, int c) {
 #pragma unroll
     for (int k = 0; k < CPL; k++) {
@@ -476,64 +351,7 @@ struct ActQ8B {
       L[k][1] = lv.y;
       L[k][2] = lv.z;
       L[k][3] = lv.w;
-      s[k] = sc[pc / 4];
-    }
-  }
-  __device__ __forceinline__ void quantize_piece(const float* x, int k) {
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) m = fmaxf(m, fabsf(x[i]));
-    const float inv = m > 0.0f ? 32512.0f / m : 0.0f;
-    s[k] = m / 32512.0f;
-#pragma unroll
-    for (int wd = 0; wd < 4; wd++) {
-      uint32_t hw = 0, lw = 0;
-#pragma unroll
-      for (int b = 0; b < 4; b++) {
-        const int X = (int)rintf(x[4 * wd + b] * inv);
-        const int Hh = (X + 128) >> 8;  // floor((X + 128) / 256), in [-127, 127]
-        const int Ll = X - (Hh << 8);   // in [-128, 127]
-        hw |= ((uint32_t)Hh & 255u) << (8 * b);
-        lw |= ((uint32_t)Ll & 255u) << (8 * b);
-      }
-      H[k][wd] = hw;
-      L[k][wd] = lw;
-    }
-  }
-  template <int LPR>
-  __device__ __forceinline__ void from_f32(const float* v, int c) {
-#pragma unroll
-    for (int k = 0; k < CPL; k++) {
-      const int pc = c + LPR * k;
-      float x[16];
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const float4 f = *reinterpret_cast<const float4*>(v + 16 * pc + 4 * j);
-        x[4 * j] = f.x;
-        x[4 * j + 1] = f.y;
-        x[4 * j + 2] = f.z;
-        x[4 * j + 3] = f.w;
-      }
-      quantize_piece(x, k);
-    }
-  }
-  template <int LPR>
-  __device__ __forceinline__ void from_bf16(const uint16_t* v, int c) {
-#pragma unroll
-    for (int k = 0; k < CPL; k++) {
-      const int pc = c + LPR * k;
-      float x[16];
-#pragma unroll
-      for (int j = 0; j < 2; j++) {
-        const uint4 b = ld16(v + 16 * pc + 8 * j);
-        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          x[8 * j + 2 * i] = __uint_as_float(bw[i] << 16);
-          x[8 * j + 2 * i + 1] = __uint_as_float(bw[i] & 0xffff0000u);
-        }
-      }
-      quantize_piece(x, k);
+      s[k] = sc[GSCALE == 16 ? pc : pc / 4];
     }
   }
 };
@@ -796,16 +614,6 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib
     return fm * d - fn * dmin;
   else
     return a.s[k][0] * ((float)im * d - (float)in * dmin);
-}
-
-template <int CPL>
-__device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8N<CPL>& a, int k, const Iq2Tab*) {
-  int acc[4];
-#pragma unroll
-  for (int p = 0; p < 4; p++)
-    acc[p] = dot4(w.q.w, a.e[k][1][p][1],
-                  dot4(w.q.z, a.e[k][1][p][0], dot4(w.q.y, a.e[k][0][p][1], dot4(w.q.x, a.e[k][0][p][0], 0))));
-  return (float)combine4(acc) * (a.s[k] * half_bits_to_float(w.d));
 }
 
 template <int CPL>

@@ -12,22 +12,13 @@
 namespace qmoe {
 namespace dec {
 
-template <int FMT, int D>
-struct XAct {
-  using type = ActNib<Geo<FMT, D>::CPL, false>;
-};
-template <int D>
-struct XAct<FMT_Q8, D> {
-  using type = ActQ8B<Geo<FMT_Q8, D>::CPL>;  // two byte planes: 8 dot4 per 16 weights
-};
-
 // A lane's activation slice from x chunks quantized in LDS.
 template <int FMT, int D>
-__device__ __forceinline__ void load_x_act(typename XAct<FMT, D>::type& act, const uint8_t* q, const float* sc) {
+__device__ __forceinline__ void load_x_act(typename RoutedAct<FMT, D>::type& act, const uint8_t* q, const float* sc) {
   using G = Geo<FMT, D>;
   const int c = (threadIdx.x & 63) % G::LPR;
   if constexpr (FMT == FMT_Q8) {
-    act.template load<G::LPR>(q, sc, c);
+    act.template load<G::LPR, 64>(q, sc, c);
   } else {
     act.template load<G::LPR>(q, sc, c);
     act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
@@ -72,16 +63,11 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
 #pragma unroll
     for (int i = 0; i < OPW; i++)
       xo[i].load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
-                 D / 64, 8 * (wave + WAVES * i), FMT_S == FMT_Q8 ? NIB_NAT : nib_layout(FMT_S));
+                 D / 64, 8 * (wave + WAVES * i), nib_layout(FMT_S));
   };
   auto x_store = [&]() {
 #pragma unroll
-    for (int i = 0; i < OPW; i++) {
-      if constexpr (FMT_S == FMT_Q8)
-        xo[i].store_bytes(D / 64, s_xq, s_xs);
-      else
-        xo[i].store(D / 64, s_xq, s_xs);
-    }
+    for (int i = 0; i < OPW; i++) xo[i].store(D / 64, s_xq, s_xs, nib_layout(FMT_S));
   };
   x_load(0);
   if constexpr (FMT_S == FMT_IQ2) iq2_build(a.grid, threadIdx.x, &itab);  // published by the barrier below
@@ -114,7 +100,7 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
     return ss;
   };
   auto compute = [&](int t) {
-    typename XAct<FMT_S, D>::type act;
+    typename RoutedAct<FMT_S, D>::type act;  // chunk-quantized x, as for the routed rows
     load_x_act<FMT_S, D>(act, s_xq, s_xs);
 #pragma unroll
     for (int i = 0; i < 2; i++) {

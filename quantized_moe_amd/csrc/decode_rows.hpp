@@ -59,7 +59,7 @@ struct RoutedAct {
 };
 template <int D>
 struct RoutedAct<FMT_Q8, D> {
-  using type = ActQ8N<Geo<FMT_Q8, D>::CPL>;
+  using type = ActQ8B<Geo<FMT_Q8, D>::CPL>;
 };
 
 // Bytes of LDS scale staging one wave needs for RPW gate/up rows.
@@ -162,7 +162,7 @@ struct DownAct {
 };
 template <int K>
 struct DownAct<FMT_Q8, K> {
-  using type = ActQ8N<Geo<FMT_Q8, K>::CPL>;
+  using type = ActQ8B<Geo<FMT_Q8, K>::CPL>;
 };
 
 // ROWS rows of one expert's down matrix against one h vector (quantized in
