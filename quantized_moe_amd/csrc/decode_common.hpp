@@ -83,6 +83,12 @@ __device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
   return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
+// First link of a chain (zero accumulator): the clamping three-operand form
+// takes the zero as an inline constant, where the two-operand form would need
+// a register copied from zero.  The clamp never acts: 8 products of 4-bit
+// values stay within +-512, 4 products of 8-bit values within +-65536.
+__device__ __forceinline__ int dot8_0(uint32_t a, uint32_t b) { return __builtin_amdgcn_sdot8((int)a, (int)b, 0, true); }
+__device__ __forceinline__ int dot4_0(uint32_t a, uint32_t b) { return __builtin_amdgcn_sdot4((int)a, (int)b, 0, true); }
 // sum_p 16^p acc[p]
 __device__ __forceinline__ int combine4(const int* acc) { return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0]; }
 
@@ -321,7 +327,7 @@ struct ActNib {
       for (int u = 0; u < 4; u++) {
         int acc[4];
 #pragma unroll
-        for (int p = 0; p < 4; p++) acc[p] = dot8(w[k][u][1][p], 0x11111111u, dot8(w[k][u][0][p], 0x11111111u, 0));
+        for (int p = 0; p < 4; p++) acc[p] = dot8(w[k][u][1][p], 0x11111111u, dot8_0(w[k][u][0][p], 0x11111111u));
         Ai[k][u] = combine4(acc);
         if constexpr (PER16) As[k][u] = s[k][u] * (float)Ai[k][u];
       }
@@ -570,14 +576,16 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_IQ2>& w, const ActNib
       const uint32_t u = tab->pos[(A >> (8 * i)) & 255u] ^ tab->neg[(B >> (7 * i)) & 127u];
       const int q = 2 * h + (i >> 1), hh = i & 1, slot = PER16 ? (i >> 1) : 0;
 #pragma unroll
-      for (int p = 0; p < 4; p++) acc[slot][p] = dot8(u, a.w[k][q][hh][p], acc[slot][p]);
+      for (int p = 0; p < 4; p++)
+        acc[slot][p] = (i == 0 || (PER16 && i == 2)) ? dot8_0(u, a.w[k][q][hh][p]) : dot8(u, a.w[k][q][hh][p], acc[slot][p]);
     }
-    // sum w x = 2 sum u x - 7 sum x over each group of 16
+    // sum w x = 2 sum u x - 7 sum x over each group of 16; |2 u - 7| <= 7
+    // and |X| <= 0x7777 keep a half's sum within 24 bits
     if constexpr (PER16) {
-      ftot += (float)((2 * combine4(acc[0]) - 7 * a.Ai[k][2 * h]) * mul) * a.s[k][2 * h] +
-              (float)((2 * combine4(acc[1]) - 7 * a.Ai[k][2 * h + 1]) * mul) * a.s[k][2 * h + 1];
+      ftot += (float)__mul24(2 * combine4(acc[0]) - 7 * a.Ai[k][2 * h], mul) * a.s[k][2 * h] +
+              (float)__mul24(2 * combine4(acc[1]) - 7 * a.Ai[k][2 * h + 1], mul) * a.s[k][2 * h + 1];
     } else {
-      itot += (2 * combine4(acc[0]) - 7 * (a.Ai[k][2 * h] + a.Ai[k][2 * h + 1])) * mul;
+      itot += __mul24(2 * combine4(acc[0]) - 7 * (a.Ai[k][2 * h] + a.Ai[k][2 * h + 1]), mul);
     }
   }
   const float d = half_bits_to_float(w.d);
@@ -598,7 +606,7 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib
     const uint32_t N0 = W[u] & 0x33333333u, N1 = (W[u] >> 2) & 0x33333333u;
     int acc[4];
 #pragma unroll
-    for (int p = 0; p < 4; p++) acc[p] = dot8(N1, a.w[k][u][1][p], dot8(N0, a.w[k][u][0][p], 0));
+    for (int p = 0; p < 4; p++) acc[p] = dot8(N1, a.w[k][u][1][p], dot8_0(N0, a.w[k][u][0][p]));
     const int D = combine4(acc);
     const int sc = (int)((w.sc >> (8 * u)) & 15u), m = (int)((w.sc >> (8 * u + 4)) & 15u);
     if constexpr (PER16) {
@@ -618,8 +626,8 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib
 
 template <int CPL>
 __device__ __forceinline__ float piece_dot(const Piece<FMT_Q8>& w, const ActQ8B<CPL>& a, int k, const Iq2Tab*) {
-  const int h = dot4(w.q.w, a.H[k][3], dot4(w.q.z, a.H[k][2], dot4(w.q.y, a.H[k][1], dot4(w.q.x, a.H[k][0], 0))));
-  const int l = dot4(w.q.w, a.L[k][3], dot4(w.q.z, a.L[k][2], dot4(w.q.y, a.L[k][1], dot4(w.q.x, a.L[k][0], 0))));
+  const int h = dot4(w.q.w, a.H[k][3], dot4(w.q.z, a.H[k][2], dot4(w.q.y, a.H[k][1], dot4_0(w.q.x, a.H[k][0]))));
+  const int l = dot4(w.q.w, a.L[k][3], dot4(w.q.z, a.L[k][2], dot4(w.q.y, a.L[k][1], dot4_0(w.q.x, a.L[k][0]))));
   return (float)(h * 256 + l) * (a.s[k] * half_bits_to_float(w.d));
 }
 
