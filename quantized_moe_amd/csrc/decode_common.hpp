@@ -89,8 +89,18 @@ __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
 // values stay within +-512, 4 products of 8-bit values within +-65536.
 __device__ __forceinline__ int dot8_0(uint32_t a, uint32_t b) { return __builtin_amdgcn_sdot8((int)a, (int)b, 0, true); }
 __device__ __forceinline__ int dot4_0(uint32_t a, uint32_t b) { return __builtin_amdgcn_sdot4((int)a, (int)b, 0, true); }
+// (a << S) + b in one instruction (the compiler splits it into a shift and
+// a three-input add)
+template <int S>
+__device__ __forceinline__ int lshl_add(int a, int b) {
+  int r;
+  asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(S), "v"(b));
+  return r;
+}
 // sum_p 16^p acc[p]
-__device__ __forceinline__ int combine4(const int* acc) { return ((acc[3] * 16 + acc[2]) * 16 + acc[1]) * 16 + acc[0]; }
+__device__ __forceinline__ int combine4(const int* acc) {
+  return lshl_add<4>(lshl_add<4>(lshl_add<4>(acc[3], acc[2]), acc[1]), acc[0]);
+}
 
 // ---------------------------------------------------------------------------
 // cross-lane sums and maxima with DPP (fixed order)
@@ -582,10 +592,10 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_IQ2>& w, const ActNib
     // sum w x = 2 sum u x - 7 sum x over each group of 16; |2 u - 7| <= 7
     // and |X| <= 0x7777 keep a half's sum within 24 bits
     if constexpr (PER16) {
-      ftot += (float)__mul24(2 * combine4(acc[0]) - 7 * a.Ai[k][2 * h], mul) * a.s[k][2 * h] +
-              (float)__mul24(2 * combine4(acc[1]) - 7 * a.Ai[k][2 * h + 1], mul) * a.s[k][2 * h + 1];
+      ftot += (float)__mul24(lshl_add<1>(combine4(acc[0]), -7 * a.Ai[k][2 * h]), mul) * a.s[k][2 * h] +
+              (float)__mul24(lshl_add<1>(combine4(acc[1]), -7 * a.Ai[k][2 * h + 1]), mul) * a.s[k][2 * h + 1];
     } else {
-      itot += __mul24(2 * combine4(acc[0]) - 7 * (a.Ai[k][2 * h] + a.Ai[k][2 * h + 1]), mul);
+      itot += __mul24(lshl_add<1>(combine4(acc[0]), -7 * (a.Ai[k][2 * h] + a.Ai[k][2 * h + 1])), mul);
     }
   }
   const float d = half_bits_to_float(w.d);
