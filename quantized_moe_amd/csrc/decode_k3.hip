@@ -5,8 +5,9 @@
 // weight).
 //
 // Block = 16 output rows of one token.  Tasks: the k routed experts (16 rows
-// each) and the shared expert in two halves of 8 rows; a wave runs one task
-// at a time with that task's h slice in registers.  Row results meet in LDS.
+// each, or two tasks of 8 rows) and the shared expert in two halves of 8
+// rows; a wave runs one task at a time with that task's h slice in
+// registers.  Row results meet in LDS.
 #include "decode_rows.hpp"
 
 namespace qmoe {
@@ -25,15 +26,20 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
   dr.run(tab, my_scales, out);
 }
 
-constexpr int K3_WAVES = WAVES;
+// Up to 2048 inputs per row: 16 waves, a routed expert's 16 rows as two
+// tasks of 8 (14 tasks for k = 6 spread over the four SIMDs); longer rows
+// need more registers per wave: 8 waves, one task per routed expert.
+constexpr int k3_waves(int F) { return F <= 2048 ? 16 : 8; }
 constexpr int SH_PARTS = 2;
 
 template <int FR, int FS, int F>
-__global__ __launch_bounds__(64 * K3_WAVES) void k3_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * k3_waves(F)) void k3_kernel(DecodeArgs a) {
+  constexpr int K3_WAVES = k3_waves(F);
+  constexpr int RT_PARTS = K3_WAVES / 8;
   __shared__ Iq2Tab itab;
   __shared__ float ye[(TOPK_MAX_K + 1) * DN_ROWS];
   constexpr int SH_ROWS = DN_ROWS / SH_PARTS;
-  constexpr int SCL_R = RowScales<FR, F>::STAGE ? DN_ROWS * RowScales<FR, F>::BYTES : 16;
+  constexpr int SCL_R = RowScales<FR, F>::STAGE ? (DN_ROWS / RT_PARTS) * RowScales<FR, F>::BYTES : 16;
   constexpr int SCL_S = RowScales<FS, F>::STAGE ? SH_ROWS * RowScales<FS, F>::BYTES : 16;
   constexpr int SCL_BYTES = SCL_R > SCL_S ? SCL_R : SCL_S;
   __shared__ __attribute__((aligned(16))) uint8_t s_scl[K3_WAVES * SCL_BYTES];
@@ -45,15 +51,18 @@ __global__ __launch_bounds__(64 * K3_WAVES) void k3_kernel(DecodeArgs a) {
     __syncthreads();
   }
   constexpr int NG = F / 16;  // groups of 16 per h vector
-  const int n_tasks = a.k + (a.has_shared ? SH_PARTS : 0);
+  constexpr int RT_ROWS = DN_ROWS / RT_PARTS;
+  const int n_rt = a.k * RT_PARTS;
+  const int n_tasks = n_rt + (a.has_shared ? SH_PARTS : 0);
   for (int task = wave; task < n_tasks; task += K3_WAVES) {
-    if (task < a.k) {
-      const int64_t r = (int64_t)t * a.k + task;
+    if (task < n_rt) {
+      const int q = task / RT_PARTS, part = task % RT_PARTS;
+      const int64_t r = (int64_t)t * a.k + q;
       const int e = a.idx[r];
-      down_rows<FR, F, DN_ROWS>(a.down, e, a.E, row0, a.hq + r * NG * G16_BYTES, a.hs + r * NG, &itab,
-                                s_scl + wave * SCL_BYTES, ye + task * DN_ROWS);
+      down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hq + r * NG * G16_BYTES, a.hs + r * NG,
+                                &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
     } else {
-      const int part = task - a.k;
+      const int part = task - n_rt;
       const int64_t src = (int64_t)a.T * a.k + t;
       down_rows<FS, F, SH_ROWS>(a.s_down, 0, 1, row0 + part * SH_ROWS, a.hq + src * NG * G16_BYTES,
                                 a.hs + src * NG, &itab, s_scl + wave * SCL_BYTES, ye + a.k * DN_ROWS + part * SH_ROWS);
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(64 * K3_WAVES) void k3_kernel(DecodeArgs a) {
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * K3_WAVES), 0, s, a);
+  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(F)), 0, s, a);
   return hipGetLastError();
 }
 
