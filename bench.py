@@ -73,7 +73,7 @@ COPY_BYTES = 512 << 20  # calibration copy: reads and writes exactly this many b
 # library kernel (as named by the per-launch timing hooks) -> substring of the
 # device kernel name in a rocprofv3 record
 KERNEL_SYMBOLS = {
-    "decode_router_shared_gateup": "k1_kernel",
+    "decode_router": "k1_kernel",
     "decode_gateup": "k2_kernel",
     "decode_down_combine": "k3_kernel",
     "prefill_gateup": "gemm_kernel<1, true",
@@ -206,12 +206,13 @@ def main() -> int:
         return 0
 
     # ------------------------------------------------------------ decode ----
-    bytes_k1 = E * d * 4 + 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d) + d * 4
-    bytes_k2 = k * 2 * lib.matrix_bytes(synth.FMT_IQ2, 1, f, d)
+    # one token: router + x in the first launch, the routed and the shared
+    # gate/up in the second, all down projections in the third
+    bytes_k1 = E * d * 4 + d * 4
+    bytes_k2 = k * 2 * lib.matrix_bytes(synth.FMT_IQ2, 1, f, d) + 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d)
     bytes_k3 = k * lib.matrix_bytes(synth.FMT_Q2K, 1, d, f) + lib.matrix_bytes(synth.FMT_Q8, 1, d, f) + d * 4
     decode_bytes = bytes_k1 + bytes_k2 + bytes_k3
-    decode_kernels = {"decode_router_shared_gateup": bytes_k1, "decode_gateup": bytes_k2,
-                      "decode_down_combine": bytes_k3}
+    decode_kernels = {"decode_router": bytes_k1, "decode_gateup": bytes_k2, "decode_down_combine": bytes_k3}
     if args.only in ("all", "decode"):
         xs = torch.from_numpy(synth.activations(0, ("bench", "decode-x"), N_DESC, d, synth.F32)).to(dev)
         ys = torch.empty(N_DESC, d, dtype=torch.float32, device=dev)

@@ -1,9 +1,10 @@
 // Decode path launcher: three launches per layer (or per set of given routes).
 //
-//   1. router logits (when routing is fused), x quantized for the routed
-//      gate/up, and the shared expert's gate/up + SwiGLU;
-//   2. exact top-k, routed gate/up + SwiGLU, routed and shared h quantized
-//      in groups of 16;
+//   1. router logits (when routing is fused), x quantized for the gate/up
+//      rows, and (more than one token) the shared expert's gate/up + SwiGLU;
+//   2. exact top-k, routed gate/up + SwiGLU, routed h quantized in groups of
+//      16, and (one token) the shared expert's gate/up + SwiGLU, which
+//      streams while the blocks wait for the router logits and the top-k;
 //   3. routed and shared down projections and the fixed-order combine.
 //
 // The kernels are in decode_k1/k2/k3.hip; their common pieces (activation
@@ -14,8 +15,7 @@
 namespace qmoe {
 namespace dec {
 hipError_t launch_k1(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_layout, hipStream_t s);
-hipError_t launch_k2(const DecodeArgs& a, int fmt, int gcnt, int blocks, int down_layout, int shared_layout,
-                     hipStream_t s);
+hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks, int down_layout, hipStream_t s);
 hipError_t launch_k3(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
 }  // namespace dec
 
@@ -26,7 +26,7 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecodeWsLayout {
-  size_t xq, xs, hsh, hq, hs, total;
+  size_t xq, xs, xq_s, xs_s, hsh, hq, hs, total;
 };
 
 DecodeWsLayout ws_layout(int T, int k, int d, int f) {
@@ -36,12 +36,16 @@ DecodeWsLayout ws_layout(int T, int k, int d, int f) {
   off = align256(off + (size_t)T * (d / 64) * CHUNK_BYTES);
   L.xs = off;
   off = align256(off + (size_t)T * (d / 64) * 4);
+  L.xq_s = off;
+  off = align256(off + (size_t)T * (d / 64) * CHUNK_BYTES);
+  L.xs_s = off;
+  off = align256(off + (size_t)T * (d / 64) * 4);
   L.hsh = off;
   off = align256(off + (size_t)T * f * 4);
   L.hq = off;
-  off = align256(off + (size_t)(T * k + T) * (f / 16) * G16_BYTES);
+  off = align256(off + (size_t)T * k * (f / 16) * G16_BYTES);
   L.hs = off;
-  off = align256(off + (size_t)(T * k + T) * (f / 16) * 4);
+  off = align256(off + (size_t)T * k * (f / 16) * 4);
   L.total = off;
   return L;
 }
@@ -97,6 +101,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   uint8_t* q = static_cast<uint8_t*>(L.quant);
   a.xq = q + W.xq;
   a.xs = reinterpret_cast<float*>(q + W.xs);
+  a.xq_s = q + W.xq_s;
+  a.xs_s = reinterpret_cast<float*>(q + W.xs_s);
+  a.shared_k2 = L.has_shared && L.T == 1;
   a.hsh = reinterpret_cast<float*>(q + W.hsh);
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);
@@ -110,7 +117,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     const int n_router = L.fused_topk ? L.E : 0;
     const int pw_s = fs == FMT_Q8 ? 16 : 64;
     const int rps_s = L.d / pw_s >= 64 ? 1 : 64 / (L.d / pw_s);
-    pl.n_steps = L.has_shared ? L.f / rps_s : 0;
+    pl.n_steps = L.has_shared && !a.shared_k2 ? L.f / rps_s : 0;
     const int64_t rb = (int64_t)L.d * 4, sb = 2 * rps_s * row_bytes(fs, L.d);
     const int64_t total = n_router * rb + (int64_t)pl.n_steps * sb;
     int64_t nb = total / (32 << 10);
@@ -131,7 +138,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     pl.n_xb = pl.n_rb == 0 ? 1 : 0;  // x for the routed gate/up is quantized by a block of its own
   }
   {
-    const int pid = prof_begin("decode_router_shared_gateup", s);
+    const int pid = prof_begin("decode_router", s);
     hipError_t e = launch_k1(a, pl, fs, nib_layout(L.fmt_gate_up), s);
     prof_end(pid, s);
     if (e != hipSuccess) return e;
@@ -154,7 +161,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
       }
     }
     const int pid = prof_begin("decode_gateup", s);
-    hipError_t e = launch_k2(a, L.fmt_gate_up, best, NG / best, nib_layout(L.fmt_down), nib_layout(fs), s);
+    hipError_t e = launch_k2(a, L.fmt_gate_up, fs, best, NG / best, nib_layout(L.fmt_down), s);
     prof_end(pid, s);
     if (e != hipSuccess) return e;
   }

@@ -164,6 +164,20 @@ __device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Byte planes of 4 values: X_n = rint(v_n inv) (|X| <= 32512) = 256 H + L
+// with H = floor((X + 128) / 256) and L in [-128, 127].  The fp32 sum
+// v inv + (1.5 2^23 + 128) is an integer in [2^23, 2^24), rounded as rint
+// rounds, whose bit pattern holds X + 128 in its low 16 bits: H is byte 1 of
+// it and L is byte 0 with the top bit flipped.  H bytes to hw, L bytes to lw.
+__device__ __forceinline__ void q8_planes4(const float* v, float inv, uint32_t& hw, uint32_t& lw) {
+#pragma clang fp contract(off)  // the product is rounded before the shift (rint of the fp32 product)
+  uint32_t y[4];
+#pragma unroll
+  for (int n = 0; n < 4; n++) y[n] = __float_as_uint(v[n] * inv + 12583040.0f);
+  hw = __builtin_amdgcn_perm(y[1], y[0], 0x0c0c0501u) | __builtin_amdgcn_perm(y[3], y[2], 0x05010c0cu);
+  lw = (__builtin_amdgcn_perm(y[1], y[0], 0x0c0c0400u) | __builtin_amdgcn_perm(y[3], y[2], 0x04000c0cu)) ^ 0x80808080u;
+}
+
 // The same to byte planes (Q8 consumers): 8 values in natural order become
 // 8 H bytes and 8 L bytes, X = 256 H + L = rint(v 32512 / m).  Writes H to
 // hq[0..8) and L to hq[16..24); *scale is the unit's scale.
@@ -172,15 +186,9 @@ __device__ __forceinline__ void quant8_bytes(const float* v, uint8_t* hq, float&
   const float m = unit_max8<GL>(v);
   const float inv = m > 0.0f ? (float)Q8_XMAX / m : 0.0f;
   scale = m / (float)Q8_XMAX;
-  uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
-#pragma unroll
-  for (int n = 0; n < 8; n++) {
-    const int X = (int)rintf(v[n] * inv);
-    const int Hh = (X + 128) >> 8;  // floor((X + 128) / 256), in [-127, 127]
-    const int Ll = X - (Hh << 8);   // in [-128, 127]
-    hw[n >> 2] |= ((uint32_t)Hh & 255u) << (8 * (n & 3));
-    lw[n >> 2] |= ((uint32_t)Ll & 255u) << (8 * (n & 3));
-  }
+  uint32_t hw[2], lw[2];
+  q8_planes4(v, inv, hw[0], lw[0]);
+  q8_planes4(v + 4, inv, hw[1], lw[1]);
   if (hq) {
     *reinterpret_cast<uint2*>(hq) = make_uint2(hw[0], hw[1]);
     *reinterpret_cast<uint2*>(hq + 16) = make_uint2(lw[0], lw[1]);
@@ -329,6 +337,48 @@ struct ActNib {
       }
     }
   }
+  // pieces c + LPR k quantized here from fp32 h (one scale per group of 16,
+  // the same digits and scales as quant_g32 gives), digits in `layout`
+  template <int LPR>
+  __device__ __forceinline__ void from_f32(const float* h, int c, int layout) {
+    static_assert(PER16, "lane-local quantization is group-scaled");
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
+      const int pc = c + LPR * k;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float4 f = *reinterpret_cast<const float4*>(h + 64 * pc + 16 * u + 4 * j);
+          v[4 * j] = f.x;
+          v[4 * j + 1] = f.y;
+          v[4 * j + 2] = f.z;
+          v[4 * j + 3] = f.w;
+        }
+        float m = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(v[n]));
+        const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
+        s[k][u] = m / (float)XMAX;
+        uint32_t Z[16];
+#pragma unroll
+        for (int n = 0; n < 16; n++) Z[n] = to_digits(v[n], inv);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+          for (int p = 0; p < 4; p++) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int n = 0; n < 8; n++) {
+              const uint32_t zq = layout == NIB_Q2K ? Z[2 * n + hh] : Z[8 * hh + n];
+              word |= ((zq >> (4 * p)) & 15u) << (4 * n);
+            }
+            w[k][u][hh][p] = word;
+          }
+      }
+    }
+  }
   // per-group sums of X (needed by Q2K's min term)
   __device__ __forceinline__ void sums() {
 #pragma unroll
@@ -368,6 +418,31 @@ struct ActQ8B {
       L[k][2] = lv.z;
       L[k][3] = lv.w;
       s[k] = sc[GSCALE == 16 ? pc : pc / 4];
+    }
+  }
+  // pieces c + LPR k quantized here from fp32 h (one scale per piece, the
+  // same bytes and scales as quant_g32 gives)
+  template <int LPR>
+  __device__ __forceinline__ void from_f32(const float* h, int c) {
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
+      const int pc = c + LPR * k;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float4 f = *reinterpret_cast<const float4*>(h + 16 * pc + 4 * j);
+        v[4 * j] = f.x;
+        v[4 * j + 1] = f.y;
+        v[4 * j + 2] = f.z;
+        v[4 * j + 3] = f.w;
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(v[n]));
+      const float inv = m > 0.0f ? (float)Q8_XMAX / m : 0.0f;
+      s[k] = m / (float)Q8_XMAX;
+#pragma unroll
+      for (int wd = 0; wd < 4; wd++) q8_planes4(v + 4 * wd, inv, H[k][wd], L[k][wd]);
     }
   }
 };
@@ -661,9 +736,12 @@ struct DecodeArgs {
   float* wt_out;
   uint8_t* xq;       // [T][d/64] x in chunks (layout of the routed gate/up format), from the first launch
   float* xs;         // [T][d/64]
+  uint8_t* xq_s;     // [T][d/64] x in the shared gate/up format's layout (when shared_k2)
+  float* xs_s;       // [T][d/64]
+  int shared_k2;     // the shared gate/up runs in the second launch (one token), not the first
   float* hsh;        // [T][f] shared SwiGLU output, fp32
-  uint8_t* hq;       // [T*k + T][f/16] quantized SwiGLU outputs (routed, then shared)
-  float* hs;         // [T*k + T][f/16]
+  uint8_t* hq;       // [T*k][f/16] quantized routed SwiGLU outputs
+  float* hs;         // [T*k][f/16]
   float* y;          // [T][d]
 };
 

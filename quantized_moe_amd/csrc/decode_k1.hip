@@ -1,5 +1,7 @@
-// First decode launch: router logits and the shared expert's gate/up +
-// SwiGLU (everything that depends on x alone).
+// First decode launch: router logits, x quantized for the gate/up rows, and
+// (for more than one token) the shared expert's gate/up + SwiGLU: everything
+// that depends on x alone.  A single token's shared gate/up runs in the
+// second launch instead, in the time its blocks wait for the routes.
 //
 // Blocks [0, n_rb) are router blocks: one expert per wave.  Blocks
 // [n_rb, n_rb + n_sb) are shared-expert blocks: each takes spb consecutive
@@ -43,7 +45,10 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
       if (e < a.E) router_item<D>(a, e);
     } else if (wave == WAVES - 1) {
       const int first = b < pl.n_rb ? b : 0, stride = pl.n_rb > 0 ? pl.n_rb : 1;
-      for (int o = first; o < n_oct; o += stride) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
+      for (int o = first; o < n_oct; o += stride) {
+        quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
+        if (a.shared_k2) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
+      }
     }
     return;
   }

@@ -1,6 +1,6 @@
-// Second decode launch: exact top-k, routed gate/up + SwiGLU, and the
-// quantization of the routed and shared SwiGLU outputs for the down
-// projections.
+// Second decode launch: exact top-k, routed gate/up + SwiGLU and the
+// quantization of the routed SwiGLU outputs for the down projections; for a
+// single token also the shared expert's gate/up + SwiGLU.
 //
 // The routed h rows of all tokens (T * k * d_ff, route-major) are cut into
 // groups of 16, the unit of h's quantization scale; a block takes GCNT
@@ -8,9 +8,10 @@
 // streams the same bytes and finishes whole groups.  Block prologue, in
 // parallel: wave 0 selects the token's experts from the router logits (every
 // block of the token does the same exact top-k; the token's first block
-// publishes idx / wt at its end); waves 1..7 build the IQ2 tables and (wave
-// 7) quantize a share of the shared expert's h.  Then every wave requests its rows' scale
-// bytes and first weights and the rows run software-pipelined (x comes
+// publishes idx / wt at its end); waves 1..7 build the IQ2 tables and run
+// the block's share of a single token's shared gate/up, whose weights stream
+// while the routes are not yet known.  Then every wave requests its rows'
+// scale bytes and first weights and the rows run software-pipelined (x comes
 // quantized from the first launch).
 #include "decode_rows.hpp"
 #include "topk.hpp"
@@ -18,8 +19,8 @@
 namespace qmoe {
 namespace dec {
 
-template <int FMT, int D, int GCNT>
-__global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layout, int shared_layout) {
+template <int FMT, int FS, int D, int GCNT>
+__global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layout) {
   __shared__ Iq2Tab itab;
   __shared__ __attribute__((aligned(16))) float hbuf[16 * GCNT];
   __shared__ int s_sel[TOPK_MAX_K];
@@ -28,14 +29,29 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   constexpr int RPW = 2 * GCNT;  // h rows per wave
   constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
   constexpr int PD = NS < 3 ? NS : 3;  // steps of loads kept in flight ahead of the compute
-  constexpr int SCL_BYTES = gateup_scale_bytes<FMT, D, RPW>();
+  constexpr int SH_RPW = 2;            // shared gate/up rows per wave call
+  constexpr int SH_NS = (SH_RPW + Geo<FS, D>::RPS - 1) / Geo<FS, D>::RPS;
+  constexpr int SCL_R = gateup_scale_bytes<FMT, D, RPW>(), SCL_S = gateup_scale_bytes<FS, D, SH_RPW>();
+  constexpr int SCL_BYTES = SCL_R > SCL_S ? SCL_R : SCL_S;
   __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * SCL_BYTES];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g0 = blockIdx.x * GCNT;  // first group of 16 rows
   const int R0 = 16 * g0;            // first routed h row (route-major over all tokens)
   const int t = R0 / (a.k * a.f);
 
-  // ---- prologue: only small loads, all issued before any weight load ----
+  // A single token's shared gate/up (shared_k2): pairs of rows spread over
+  // the blocks, taken by waves 1..7 of each block; h to hsh in fp32.
+  auto shared_rows = [&]() {
+    const int npair = a.f / SH_RPW;
+    const int ppb = (npair + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int p0 = (int)blockIdx.x * ppb, p1 = min(npair, p0 + ppb);
+    for (int pp = p0 + wave - 1; pp < p1; pp += WAVES - 1)
+      gateup_rows<FS, D, SH_RPW, SH_NS>(a.s_gate, a.s_up, 1, a.f, 1, SH_RPW * pp, 0, nullptr, 0, a.xq_s, a.xs_s,
+                                        &itab, s_scl + wave * SCL_BYTES, a.hsh + SH_RPW * pp);
+  };
+
+  // ---- prologue: wave 0 selects the routes while the others build the IQ2
+  // tables and run the shared gate/up (its weights do not depend on the routes)
   if (wave == 0) {
     if (a.fused_topk) {
       wave_topk(a.z + (int64_t)t * a.E, a.E, a.k, s_sel, s_zs);
@@ -43,21 +59,20 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
       s_sel[lane] = a.idx[(int64_t)t * a.k + lane];
     }
   } else {
-    if constexpr (FMT == FMT_IQ2) iq2_build(a.grid, threadIdx.x - 64, &itab);  // waves 1..7: 384 items
-    if (a.has_shared && wave == WAVES - 1) {
-      // the shared expert's h (from the first launch): 32 groups per pass,
-      // the passes spread over the blocks
-      const int NG = a.T * a.f / 16;
-      const int64_t base = (int64_t)a.T * a.k * (a.f / 16);
-      for (int g0s = 32 * blockIdx.x; g0s < NG; g0s += 32 * gridDim.x)
-        quant_g32(a.hsh, NG, g0s, shared_layout, a.hq + base * G16_BYTES, a.hs + base);
+    if constexpr (FMT == FMT_IQ2 || FS == FMT_IQ2) iq2_build(a.grid, threadIdx.x - 64, &itab);  // 384 items
+    if constexpr (FS != FMT_IQ2) {
+      if (a.shared_k2) shared_rows();
     }
   }
   __syncthreads();
+  if constexpr (FS == FMT_IQ2) {  // the tables are published only now
+    if (a.shared_k2 && wave > 0) shared_rows();
+  }
 
   // ---- this wave's rows, software-pipelined ----
-  gateup_rows<FMT, D, RPW, PD>(a, R0 + wave * RPW, t, s_sel, a.xq + (int64_t)t * (D / 64) * CHUNK_BYTES,
-                               a.xs + (int64_t)t * (D / 64), &itab, s_scl + wave * SCL_BYTES, hbuf + wave * RPW);
+  gateup_rows<FMT, D, RPW, PD>(a.gate, a.up, a.E, a.f, a.k, R0 + wave * RPW, t, s_sel, -1,
+                               a.xq + (int64_t)t * (D / 64) * CHUNK_BYTES, a.xs + (int64_t)t * (D / 64), &itab,
+                               s_scl + wave * SCL_BYTES, hbuf + wave * RPW);
   __syncthreads();
   if (wave == 0) quant_g32(hbuf, GCNT, 0, down_layout, a.hq + (int64_t)g0 * G16_BYTES, a.hs + g0);
   // The token's first block publishes its routes and mixing weights (needed
@@ -74,28 +89,36 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   }
 }
 
-template <int FMT, int D, int GCNT>
-static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, int shared_layout, hipStream_t s) {
-  QMOE_LAUNCH((k2_kernel<FMT, D, GCNT>), dim3(blocks), dim3(THREADS), 0, s, a, down_layout, shared_layout);
+template <int FMT, int FS, int D, int GCNT>
+static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, hipStream_t s) {
+  QMOE_LAUNCH((k2_kernel<FMT, FS, D, GCNT>), dim3(blocks), dim3(THREADS), 0, s, a, down_layout);
   return hipGetLastError();
 }
 
-template <int FMT, int D>
-static hipError_t run_k2_g(const DecodeArgs& a, int gcnt, int blocks, int dl, int sl, hipStream_t s) {
+template <int FMT, int FS, int D>
+static hipError_t run_k2_g(const DecodeArgs& a, int gcnt, int blocks, int dl, hipStream_t s) {
   switch (gcnt) {
-    case 3: return run_k2<FMT, D, 3>(a, blocks, dl, sl, s);
-    case 2: return run_k2<FMT, D, 2>(a, blocks, dl, sl, s);
-    default: return run_k2<FMT, D, 1>(a, blocks, dl, sl, s);
+    case 3: return run_k2<FMT, FS, D, 3>(a, blocks, dl, s);
+    case 2: return run_k2<FMT, FS, D, 2>(a, blocks, dl, s);
+    default: return run_k2<FMT, FS, D, 1>(a, blocks, dl, s);
   }
 }
 
-hipError_t launch_k2(const DecodeArgs& a, int fmt, int gcnt, int blocks, int down_layout, int shared_layout,
-                     hipStream_t s) {
-#define K2_FMT(D)                                                                              \
-  switch (fmt) {                                                                               \
-    case FMT_IQ2: return run_k2_g<FMT_IQ2, D>(a, gcnt, blocks, down_layout, shared_layout, s); \
-    case FMT_Q2K: return run_k2_g<FMT_Q2K, D>(a, gcnt, blocks, down_layout, shared_layout, s); \
-    default: return run_k2_g<FMT_Q8, D>(a, gcnt, blocks, down_layout, shared_layout, s);       \
+template <int FMT, int D>
+static hipError_t run_k2_s(const DecodeArgs& a, int fs, int gcnt, int blocks, int dl, hipStream_t s) {
+  switch (fs) {
+    case FMT_IQ2: return run_k2_g<FMT, FMT_IQ2, D>(a, gcnt, blocks, dl, s);
+    case FMT_Q2K: return run_k2_g<FMT, FMT_Q2K, D>(a, gcnt, blocks, dl, s);
+    default: return run_k2_g<FMT, FMT_Q8, D>(a, gcnt, blocks, dl, s);
+  }
+}
+
+hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks, int down_layout, hipStream_t s) {
+#define K2_FMT(D)                                                                  \
+  switch (fmt) {                                                                   \
+    case FMT_IQ2: return run_k2_s<FMT_IQ2, D>(a, fs, gcnt, blocks, down_layout, s); \
+    case FMT_Q2K: return run_k2_s<FMT_Q2K, D>(a, fs, gcnt, blocks, down_layout, s); \
+    default: return run_k2_s<FMT_Q8, D>(a, fs, gcnt, blocks, down_layout, s);       \
   }
   switch (a.d) {
     case 256: K2_FMT(256)

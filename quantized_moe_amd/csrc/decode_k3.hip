@@ -7,34 +7,41 @@
 // Block = 16 output rows of one token.  Tasks: the k routed experts (16 rows
 // each, or two tasks of 8 rows) and the shared expert in two halves of 8
 // rows; a wave runs one task at a time with that task's h slice in
-// registers.  Row results meet in LDS.
+// registers (the shared expert's fp32 h is quantized by the task itself).
+// Row results meet in LDS.
 #include "decode_rows.hpp"
 
 namespace qmoe {
 namespace dec {
 
 // ROWS rows of expert e's down matrix against one h vector (quantized in
-// groups of 16 at hq / hs); row results to out[0 .. ROWS).  The h slice is
-// requested before the codes, so both loads are in flight together.
+// groups of 16 at hq / hs, or fp32 at hf and quantized here when hq is
+// null); row results to out[0 .. ROWS).  The h slice is requested before the
+// codes, so both loads are in flight together.
 template <int FMT, int K, int ROWS>
 __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, const uint8_t* hq, const float* hs,
-                                          const Iq2Tab* tab, uint8_t* my_scales, float* out) {
+                                          const float* hf, const Iq2Tab* tab, uint8_t* my_scales, float* out) {
   constexpr int NS = DownRows<FMT, K, ROWS, 1>::NS;
   DownRows<FMT, K, ROWS, (NS < 3 ? NS : 3)> dr;  // three steps of loads kept in flight ahead of the compute
-  dr.load_act(hq, hs);
+  if (hq)
+    dr.load_act(hq, hs);
+  else
+    dr.load_act_f32(hf);
   dr.issue(m, e, E, r0, my_scales);
   dr.run(tab, my_scales, out);
 }
 
-// Up to 2048 inputs per row: 16 waves, a routed expert's 16 rows as two
-// tasks of 8 (14 tasks for k = 6 spread over the four SIMDs); longer rows
-// need more registers per wave: 8 waves, one task per routed expert.
-constexpr int k3_waves(int F) { return F <= 2048 ? 16 : 8; }
+// Up to 2048 inputs per row and a Q8 shared expert: 16 waves, a routed
+// expert's 16 rows as two tasks of 8 (14 tasks for k = 6 spread over the four
+// SIMDs); longer rows, or a 2-bit shared expert (whose h slice is quantized
+// from 64 fp32 values per piece), need more registers per wave: 8 waves, one
+// task per routed expert.
+constexpr int k3_waves(int FS, int F) { return F <= 2048 && FS == FMT_Q8 ? 16 : 8; }
 constexpr int SH_PARTS = 2;
 
 template <int FR, int FS, int F>
-__global__ __launch_bounds__(64 * k3_waves(F)) void k3_kernel(DecodeArgs a) {
-  constexpr int K3_WAVES = k3_waves(F);
+__global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) {
+  constexpr int K3_WAVES = k3_waves(FS, F);
   constexpr int RT_PARTS = K3_WAVES / 8;
   __shared__ Iq2Tab itab;
   __shared__ float ye[(TOPK_MAX_K + 1) * DN_ROWS];
@@ -60,12 +67,11 @@ __global__ __launch_bounds__(64 * k3_waves(F)) void k3_kernel(DecodeArgs a) {
       const int64_t r = (int64_t)t * a.k + q;
       const int e = a.idx[r];
       down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hq + r * NG * G16_BYTES, a.hs + r * NG,
-                                &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
+                                nullptr, &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
     } else {
       const int part = task - n_rt;
-      const int64_t src = (int64_t)a.T * a.k + t;
-      down_rows<FS, F, SH_ROWS>(a.s_down, 0, 1, row0 + part * SH_ROWS, a.hq + src * NG * G16_BYTES,
-                                a.hs + src * NG, &itab, s_scl + wave * SCL_BYTES, ye + a.k * DN_ROWS + part * SH_ROWS);
+      down_rows<FS, F, SH_ROWS>(a.s_down, 0, 1, row0 + part * SH_ROWS, nullptr, nullptr, a.hsh + (int64_t)t * F,
+                                &itab, s_scl + wave * SCL_BYTES, ye + a.k * DN_ROWS + part * SH_ROWS);
     }
   }
   __syncthreads();
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(64 * k3_waves(F)) void k3_kernel(DecodeArgs a) {
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(F)), 0, s, a);
+  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(FS, F)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -68,30 +68,32 @@ constexpr int gateup_scale_bytes() {
   return RowScales<FMT, D>::STAGE ? 2 * RPW * RowScales<FMT, D>::BYTES : 16;
 }
 
-// One wave's RPW consecutive routed h rows starting at global row Rw (rows
-// are route-major: route r = t k + j covers rows r f .. r f + f - 1) of token
-// t: gate and up rows of the route's expert against x (chunk-quantized at
-// xq / xs, global memory or LDS), SwiGLU, results to out[0 .. RPW) (0 for an
-// out-of-range expert id).  The rows cross at most one route boundary, so two
-// plane sets cover them.  Scale bytes are staged in my_scales, then PD steps
-// of weight loads are issued before x is read; the steps run
-// software-pipelined.
+// One wave's RPW consecutive h rows starting at global row Rw (rows are
+// route-major: route r = t k + j covers rows r f .. r f + f - 1) of token t:
+// gate and up rows (matrices gm, um of E experts with f rows each) of the
+// route's expert (s_sel[j], or fixed_e when fixed_e >= 0) against x
+// (chunk-quantized at xq / xs, global memory or LDS), SwiGLU, results to
+// out[0 .. RPW) (0 for an out-of-range expert id).  The rows cross at most
+// one route boundary, so two plane sets cover them.  Scale bytes are staged
+// in my_scales, then PD steps of weight loads are issued before x is read;
+// the steps run software-pipelined.
 template <int FMT, int D, int RPW, int PD>
-__device__ __forceinline__ void gateup_rows(const DecodeArgs& a, int Rw, int t, const int* s_sel, const uint8_t* xq,
-                                            const float* xs, const Iq2Tab* tab, uint8_t* my_scales, float* out) {
+__device__ __forceinline__ void gateup_rows(const QMat& gm, const QMat& um, int E, int f, int k, int Rw, int t,
+                                            const int* s_sel, int fixed_e, const uint8_t* xq, const float* xs,
+                                            const Iq2Tab* tab, uint8_t* my_scales, float* out) {
   using G = Geo<FMT, D>;
   constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
   using SS = ScaleStage<FMT, D, 2, RPW>;
   constexpr bool STAGE = SS::RS::STAGE;
   const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
-  const int r0 = Rw / a.f;          // route of the first row (global index)
-  const int n0 = Rw - r0 * a.f;     // its row inside the expert
-  const int jb = a.f - n0;          // rows j >= jb belong to route r0 + 1
-  const int r1 = min(r0 + 1, t * a.k + a.k - 1);  // (a wave never leaves its token)
-  const int e0 = s_sel[r0 - t * a.k], e1 = s_sel[r1 - t * a.k];
-  const bool ok0 = (unsigned)e0 < (unsigned)a.E, ok1 = (unsigned)e1 < (unsigned)a.E;
-  const EPlanes G0 = expert_planes<FMT>(a.gate, ok0 ? e0 : 0), U0 = expert_planes<FMT>(a.up, ok0 ? e0 : 0);
-  const EPlanes G1 = expert_planes<FMT>(a.gate, ok1 ? e1 : 0), U1 = expert_planes<FMT>(a.up, ok1 ? e1 : 0);
+  const int r0 = Rw / f;          // route of the first row (global index)
+  const int n0 = Rw - r0 * f;     // its row inside the expert
+  const int jb = f - n0;          // rows j >= jb belong to route r0 + 1
+  const int r1 = min(r0 + 1, t * k + k - 1);  // (a wave never leaves its token)
+  const int e0 = fixed_e >= 0 ? fixed_e : s_sel[r0 - t * k], e1 = fixed_e >= 0 ? fixed_e : s_sel[r1 - t * k];
+  const bool ok0 = (unsigned)e0 < (unsigned)E, ok1 = (unsigned)e1 < (unsigned)E;
+  const EPlanes G0 = expert_planes<FMT>(gm, ok0 ? e0 : 0), U0 = expert_planes<FMT>(um, ok0 ? e0 : 0);
+  const EPlanes G1 = expert_planes<FMT>(gm, ok1 ? e1 : 0), U1 = expert_planes<FMT>(um, ok1 ? e1 : 0);
   Piece<FMT> wg[NS][G::CPL], wu[NS][G::CPL];
   int lr[NS];
   bool ok[NS];
@@ -102,7 +104,7 @@ __device__ __forceinline__ void gateup_rows(const DecodeArgs& a, int Rw, int t, 
     lr[s] = j;
     const bool second = j >= jb;
     ok[s] = valid && (second ? ok1 : ok0);
-    const uint32_t n = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+    const uint32_t n = (uint32_t)(second ? n0 + j - f : n0 + j);
     const EPlanes Gp = pick_planes(second, G0, G1);
     const EPlanes Up = pick_planes(second, U0, U1);
 #pragma unroll
@@ -120,7 +122,7 @@ __device__ __forceinline__ void gateup_rows(const DecodeArgs& a, int Rw, int t, 
     ss.issue([&](int m, int j, EPlanes& P, uint32_t& row) {
       const bool second = j >= jb;
       P = m == 0 ? pick_planes(second, G0, G1) : pick_planes(second, U0, U1);
-      row = (uint32_t)(second ? n0 + j - a.f : n0 + j);
+      row = (uint32_t)(second ? n0 + j - f : n0 + j);
     });
   }
 #pragma unroll
@@ -191,6 +193,15 @@ struct DownRows {
       act.template load<G::LPR, 16>(hq, hs, c);
     } else {
       act.template load<G::LPR>(hq, hs, c);
+    }
+  }
+  // the same from the fp32 h vector, quantized here in groups of 16
+  __device__ __forceinline__ void load_act_f32(const float* h) {
+    const int c = (threadIdx.x & 63) % G::LPR;
+    if constexpr (FMT == FMT_Q8) {
+      act.template from_f32<G::LPR>(h, c);
+    } else {
+      act.template from_f32<G::LPR>(h, c, nib_layout(FMT));
     }
   }
   __device__ __forceinline__ void issue_step(int s) {
