@@ -123,9 +123,31 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t to_digits(float v, float inv) {
-  const int X = (int)rintf(v * inv);  // |X| <= XMAX
-  return ((uint32_t)(X + 0x8888) ^ 0x8888u) & 0xffffu;
+// Digit planes of 8 values: X_n = rint(v_n inv) (|X| <= XMAX) as four signed
+// hex digits, Z = ((X + 0x8888) ^ 0x8888) mod 2^16; returns plane p's word
+// (nibble n = digit p of Z_n) in component p.  The fp32 sum v inv + (1.5 2^23
+// + 0x8888) is an integer in [2^23, 2^24), rounded as rint rounds, whose bit
+// pattern holds X + 0x8888 in its low 16 bits; pairs of values share a word
+// and the 4 x 8 nibble transpose is done with masks, shifts and byte
+// permutes.
+__device__ __forceinline__ uint4 nib_planes8(const float* v, float inv) {
+#pragma clang fp contract(off)  // the product is rounded before the shift (rint of the fp32 product)
+  uint32_t y[8];
+#pragma unroll
+  for (int n = 0; n < 8; n++) y[n] = __float_as_uint(v[n] * inv + 12617864.0f);
+  uint32_t D[4], E[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const uint32_t A = __builtin_amdgcn_perm(y[2 * k + 1], y[2 * k], 0x05040100u) ^ 0x88888888u;  // Z_2k | Z_2k+1 << 16
+    const uint32_t B = A & 0x0f0f0f0fu, C = (A >> 4) & 0x0f0f0f0fu;  // digits 0, 2 / 1, 3 of both, one per byte
+    D[k] = B | (B >> 12);  // byte 0: digit 0 of Z_2k, Z_2k+1; byte 1: digit 2
+    E[k] = C | (C >> 12);  // byte 0: digit 1; byte 1: digit 3
+  }
+  auto gather = [](const uint32_t* W, uint32_t b) {  // byte b of W[0..3]
+    return __builtin_amdgcn_perm(W[1], W[0], 0x0c0c0400u + 0x0101u * b) |
+           __builtin_amdgcn_perm(W[3], W[2], 0x04000c0cu + 0x01010000u * b);
+  };
+  return make_uint4(gather(D, 0), gather(E, 0), gather(D, 1), gather(E, 1));
 }
 
 // Maximum of |v[0..7]| over each aligned unit of GL lanes (GL = 8: a chunk
@@ -150,18 +172,7 @@ __device__ __forceinline__ uint4 quant8(const float* v, float& scale) {
   const float m = unit_max8<GL>(v);
   const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
   scale = m / (float)XMAX;
-  uint32_t Z[8];
-#pragma unroll
-  for (int n = 0; n < 8; n++) Z[n] = to_digits(v[n], inv);
-  uint32_t w[4];
-#pragma unroll
-  for (int p = 0; p < 4; p++) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int n = 0; n < 8; n++) word |= ((Z[n] >> (4 * p)) & 15u) << (4 * n);
-    w[p] = word;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return nib_planes8(v, inv);
 }
 
 // Byte planes of 4 values: X_n = rint(v_n inv) (|X| <= 32512) = 256 H + L
@@ -361,21 +372,17 @@ struct ActNib {
         for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(v[n]));
         const float inv = m > 0.0f ? (float)XMAX / m : 0.0f;
         s[k][u] = m / (float)XMAX;
-        uint32_t Z[16];
 #pragma unroll
-        for (int n = 0; n < 16; n++) Z[n] = to_digits(v[n], inv);
+        for (int hh = 0; hh < 2; hh++) {
+          float vh[8];
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++)
-#pragma unroll
-          for (int p = 0; p < 4; p++) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int n = 0; n < 8; n++) {
-              const uint32_t zq = layout == NIB_Q2K ? Z[2 * n + hh] : Z[8 * hh + n];
-              word |= ((zq >> (4 * p)) & 15u) << (4 * n);
-            }
-            w[k][u][hh][p] = word;
-          }
+          for (int n = 0; n < 8; n++) vh[n] = layout == NIB_Q2K ? v[2 * n + hh] : v[8 * hh + n];
+          const uint4 pw = nib_planes8(vh, inv);
+          w[k][u][hh][0] = pw.x;
+          w[k][u][hh][1] = pw.y;
+          w[k][u][hh][2] = pw.z;
+          w[k][u][hh][3] = pw.w;
+        }
       }
     }
   }
