@@ -74,9 +74,9 @@ constexpr int gateup_scale_bytes() {
 // route's expert (s_sel[j], or fixed_e when fixed_e >= 0) against x
 // (chunk-quantized at xq / xs, global memory or LDS), SwiGLU, results to
 // out[0 .. RPW) (0 for an out-of-range expert id).  The rows cross at most
-// one route boundary, so two plane sets cover them.  Scale bytes are staged
-// in my_scales, then PD steps of weight loads are issued before x is read;
-// the steps run software-pipelined.
+// one route boundary, so two plane sets cover them.  The scale bytes (staged
+// in my_scales) and x are requested first, then PD steps of weight codes; the
+// steps run software-pipelined.
 template <int FMT, int D, int RPW, int PD>
 __device__ __forceinline__ void gateup_rows(const QMat& gm, const QMat& um, int E, int f, int k, int Rw, int t,
                                             const int* s_sel, int fixed_e, const uint8_t* xq, const float* xs,
@@ -125,16 +125,18 @@ __device__ __forceinline__ void gateup_rows(const QMat& gm, const QMat& um, int 
       row = (uint32_t)(second ? n0 + j - f : n0 + j);
     });
   }
-#pragma unroll
-  for (int s = 0; s < PD; s++) issue(s);
-  if constexpr (STAGE) ss.store(my_scales);
+  // x before the codes: loads complete in issue order, so the first step
+  // then waits only for its own codes
   typename RoutedAct<FMT, D>::type act;
   if constexpr (FMT == FMT_Q8) {
     act.template load<G::LPR, 64>(xq, xs, c);
   } else {
     act.template load<G::LPR>(xq, xs, c);
-    act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
   }
+#pragma unroll
+  for (int s = 0; s < PD; s++) issue(s);
+  if constexpr (STAGE) ss.store(my_scales);
+  if constexpr (FMT != FMT_Q8) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
 #pragma unroll
   for (int s = 0; s < NS; s++) {
     if (s + PD < NS) issue(s + PD);
