@@ -466,10 +466,14 @@ struct EPlanes {  // one expert's planes of a weight tensor in the device layout
 // A or B, chosen field by field (a select of values, never of addresses, so
 // that the planes stay in registers).
 __device__ __forceinline__ EPlanes pick_planes(bool second, const EPlanes& A, const EPlanes& B) {
+  // (the fields are read into values first: a conditional of two lvalues is
+  // itself an lvalue, i.e. a select of their addresses)
+  const uint8_t *as = A.scale, *aa = A.a, *ab = A.b;
+  const uint8_t *bs = B.scale, *ba = B.a, *bb = B.b;
   EPlanes p;
-  p.scale = second ? B.scale : A.scale;
-  p.a = second ? B.a : A.a;
-  p.b = second ? B.b : A.b;
+  p.scale = second ? bs : as;
+  p.a = second ? ba : aa;
+  p.b = second ? bb : ab;
   return p;
 }
 
