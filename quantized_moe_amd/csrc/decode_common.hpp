@@ -349,24 +349,31 @@ struct ActNib {
     }
   }
   // pieces c + LPR k quantized here from fp32 h (one scale per group of 16,
-  // the same digits and scales as quant_g32 gives), digits in `layout`
+  // the same digits and scales as quant_g32 gives), digits in `layout`:
+  // fetch_f32 only loads, so the caller can request other data before
+  // quant_f32 waits for it
   template <int LPR>
-  __device__ __forceinline__ void from_f32(const float* h, int c, int layout) {
-    static_assert(PER16, "lane-local quantization is group-scaled");
+  static __device__ __forceinline__ void fetch_f32(const float* h, int c, float (&raw)[CPL][64]) {
 #pragma unroll
     for (int k = 0; k < CPL; k++) {
       const int pc = c + LPR * k;
 #pragma unroll
-      for (int u = 0; u < 4; u++) {
-        float v[16];
+      for (int j = 0; j < 16; j++) {
+        const float4 f = *reinterpret_cast<const float4*>(h + 64 * pc + 4 * j);
+        raw[k][4 * j] = f.x;
+        raw[k][4 * j + 1] = f.y;
+        raw[k][4 * j + 2] = f.z;
+        raw[k][4 * j + 3] = f.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void quant_f32(const float (&raw)[CPL][64], int layout) {
+    static_assert(PER16, "lane-local quantization is group-scaled");
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float4 f = *reinterpret_cast<const float4*>(h + 64 * pc + 16 * u + 4 * j);
-          v[4 * j] = f.x;
-          v[4 * j + 1] = f.y;
-          v[4 * j + 2] = f.z;
-          v[4 * j + 3] = f.w;
-        }
+    for (int k = 0; k < CPL; k++)
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const float* v = raw[k] + 16 * u;
         float m = 0.0f;
 #pragma unroll
         for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(v[n]));
@@ -384,7 +391,6 @@ struct ActNib {
           w[k][u][hh][3] = pw.w;
         }
       }
-    }
   }
   // per-group sums of X (needed by Q2K's min term)
   __device__ __forceinline__ void sums() {
@@ -428,28 +434,33 @@ struct ActQ8B {
     }
   }
   // pieces c + LPR k quantized here from fp32 h (one scale per piece, the
-  // same bytes and scales as quant_g32 gives)
+  // same bytes and scales as quant_g32 gives): fetch_f32 only loads, so the
+  // caller can request other data before quant_f32 waits for it
   template <int LPR>
-  __device__ __forceinline__ void from_f32(const float* h, int c) {
+  static __device__ __forceinline__ void fetch_f32(const float* h, int c, float (&raw)[CPL][16]) {
 #pragma unroll
     for (int k = 0; k < CPL; k++) {
       const int pc = c + LPR * k;
-      float v[16];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const float4 f = *reinterpret_cast<const float4*>(h + 16 * pc + 4 * j);
-        v[4 * j] = f.x;
-        v[4 * j + 1] = f.y;
-        v[4 * j + 2] = f.z;
-        v[4 * j + 3] = f.w;
+        raw[k][4 * j] = f.x;
+        raw[k][4 * j + 1] = f.y;
+        raw[k][4 * j + 2] = f.z;
+        raw[k][4 * j + 3] = f.w;
       }
+    }
+  }
+  __device__ __forceinline__ void quant_f32(const float (&raw)[CPL][16]) {
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
       float m = 0.0f;
 #pragma unroll
-      for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(v[n]));
+      for (int n = 0; n < 16; n++) m = fmaxf(m, fabsf(raw[k][n]));
       const float inv = m > 0.0f ? (float)Q8_XMAX / m : 0.0f;
       s[k] = m / (float)Q8_XMAX;
 #pragma unroll
-      for (int wd = 0; wd < 4; wd++) q8_planes4(v + 4 * wd, inv, H[k][wd], L[k][wd]);
+      for (int wd = 0; wd < 4; wd++) q8_planes4(raw[k] + 4 * wd, inv, H[k][wd], L[k][wd]);
     }
   }
 };

@@ -5,8 +5,8 @@
 // weight).
 //
 // Block = 16 output rows of one token.  Tasks: the k routed experts (16 rows
-// each, or two tasks of 8 rows) and the shared expert in two halves of 8
-// rows; a wave runs one task at a time with that task's h slice in
+// each, or two tasks of 8 rows) and the shared expert (in two or four
+// tasks); a wave runs one task at a time with that task's h slice in
 // registers (the shared expert's fp32 h is quantized by the task itself).
 // Row results meet in LDS.
 #include "decode_rows.hpp"
@@ -23,26 +23,30 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
                                           const float* hf, const Iq2Tab* tab, uint8_t* my_scales, float* out) {
   constexpr int NS = DownRows<FMT, K, ROWS, 1>::NS;
   DownRows<FMT, K, ROWS, (NS < 3 ? NS : 3)> dr;  // three steps of loads kept in flight ahead of the compute
-  if (hq)
+  if (hq) {
     dr.load_act(hq, hs);
-  else
-    dr.load_act_f32(hf);
-  dr.issue(m, e, E, r0, my_scales);
+    dr.issue(m, e, E, r0, my_scales);
+  } else {
+    dr.fetch_act_f32(hf);
+    dr.issue(m, e, E, r0, my_scales);
+    dr.quant_act_f32();
+  }
   dr.run(tab, my_scales, out);
 }
 
 // Up to 2048 inputs per row and a Q8 shared expert: 16 waves, a routed
-// expert's 16 rows as two tasks of 8 (14 tasks for k = 6 spread over the four
-// SIMDs); longer rows, or a 2-bit shared expert (whose h slice is quantized
-// from 64 fp32 values per piece), need more registers per wave: 8 waves, one
-// task per routed expert.
+// expert's 16 rows as two tasks of 8 and the shared expert's as four tasks
+// of 4 (16 tasks for k = 6, four per SIMD); longer rows, or a 2-bit shared
+// expert (whose h slice is quantized from 64 fp32 values per piece), need
+// more registers per wave: 8 waves, one task per routed expert and two for
+// the shared expert.
 constexpr int k3_waves(int FS, int F) { return F <= 2048 && FS == FMT_Q8 ? 16 : 8; }
-constexpr int SH_PARTS = 2;
 
 template <int FR, int FS, int F>
 __global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) {
   constexpr int K3_WAVES = k3_waves(FS, F);
   constexpr int RT_PARTS = K3_WAVES / 8;
+  constexpr int SH_PARTS = K3_WAVES / 4;  // the shared expert's 16 rows as tasks of 4 (16 waves) or 8
   __shared__ Iq2Tab itab;
   __shared__ float ye[(TOPK_MAX_K + 1) * DN_ROWS];
   constexpr int SH_ROWS = DN_ROWS / SH_PARTS;

@@ -197,14 +197,19 @@ struct DownRows {
       act.template load<G::LPR>(hq, hs, c);
     }
   }
-  // the same from the fp32 h vector, quantized here in groups of 16
-  __device__ __forceinline__ void load_act_f32(const float* h) {
+  // the same from the fp32 h vector, quantized here in groups of 16: the
+  // values are requested first (fetch_act_f32, ahead of the codes) and
+  // quantized once they are back (quant_act_f32)
+  float hraw[G::CPL][FMT == FMT_Q8 ? 16 : 64];
+  __device__ __forceinline__ void fetch_act_f32(const float* h) {
     const int c = (threadIdx.x & 63) % G::LPR;
-    if constexpr (FMT == FMT_Q8) {
-      act.template from_f32<G::LPR>(h, c);
-    } else {
-      act.template from_f32<G::LPR>(h, c, nib_layout(FMT));
-    }
+    act.template fetch_f32<G::LPR>(h, c, hraw);
+  }
+  __device__ __forceinline__ void quant_act_f32() {
+    if constexpr (FMT == FMT_Q8)
+      act.quant_f32(hraw);
+    else
+      act.quant_f32(hraw, nib_layout(FMT));
   }
   __device__ __forceinline__ void issue_step(int s) {
     const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
