@@ -89,6 +89,12 @@ FORMAT_CASES = [
     (16, 16, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 33, synth.BF16),
     (1000, 5, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 6, synth.F32),  # many experts
     (1000, 5, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 90, synth.BF16),
+    # one token: the shared gate/up runs in the second decode launch, for every shared format
+    (12, 3, 512, 256, synth.FMT_Q8, synth.FMT_IQ2, synth.FMT_Q2K, 1, synth.F32),
+    (10, 2, 1024, 256, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_IQ2, 1, synth.BF16),
+    (16, 4, 256, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 1, synth.F32),
+    (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 1, synth.F32),  # several row pairs per wave
+    (8, 1, 8192, 256, synth.FMT_IQ2, synth.FMT_Q2K, None, 1, synth.F32),
 ]
 
 
