@@ -28,7 +28,11 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   using G = Geo<FMT, D>;
   constexpr int RPW = 2 * GCNT;  // h rows per wave
   constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
-  constexpr int PD = NS < 3 ? NS : 3;  // steps of loads kept in flight ahead of the compute
+  // One step of codes in flight ahead of the compute: the rows are bound by
+  // the decode arithmetic once streaming, and a deeper start (every wave of
+  // the GPU requesting several steps at the barrier) delays every wave's
+  // first step behind the whole flood (measured: depth 3 -> 1, -0.8 us).
+  constexpr int PD = 1;
   constexpr int SH_RPW = 2;            // shared gate/up rows per wave call
   constexpr int SH_NS = (SH_RPW + Geo<FS, D>::RPS - 1) / Geo<FS, D>::RPS;
   constexpr int SCL_R = gateup_scale_bytes<FMT, D, RPW>(), SCL_S = gateup_scale_bytes<FS, D, SH_RPW>();
