@@ -53,7 +53,9 @@ def lib():
         L.orc_route_weights.argtypes = [P, P, I, I, I, P]
         L.orc_bucket.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_dequant.argtypes, L.orc_dequant.restype = [I, P, I64, P, P], I
-        L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I, P, P, P, P, I, I, P, I, P, P, P]
+        L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I, P, P, P, P, P, I, I, P, I, P, P, P]
+        L.orc_sigmoid32.argtypes, L.orc_sigmoid32.restype = [ctypes.c_float], ctypes.c_float
+        L.orc_bias_keys.argtypes = [P, I, I, P, P]
         L.orc_ffn.restype = I
         L.orc_threads.restype = I
         _lib = L
@@ -109,10 +111,26 @@ def route_weights(z, idx) -> np.ndarray:
     return wt
 
 
-def route(x, x_dtype, W, k):
-    """(z, idx, wt) for every token of x."""
+def sigmoid32(z: float) -> float:
+    """The fixed fp32 sigmoid of the biased selection keys (see oracle.c)."""
+    return float(lib().orc_sigmoid32(float(z)))
+
+
+def bias_keys(z, b) -> np.ndarray:
+    """key[t, e] = sigmoid32(z[t, e]) + b[e] in fp32."""
+    z = _c(z, np.float32)
+    b = _c(b, np.float32)
+    T, E = z.shape
+    key = np.empty((T, E), dtype=np.float32)
+    lib().orc_bias_keys(_p(z), T, E, _p(b), _p(key))
+    return key
+
+
+def route(x, x_dtype, W, k, bias=None):
+    """(z, idx, wt) for every token of x; with a router bias the experts are
+    selected on sigmoid32(z) + bias, the weights still come from z."""
     z = router_logits(x, x_dtype, W)
-    idx = topk(z, k)
+    idx = topk(z if bias is None else bias_keys(z, bias), k)
     return z, idx, route_weights(z, idx)
 
 
@@ -159,13 +177,15 @@ def ffn(layer, x, x_dtype, idx, wt, tokens=None) -> np.ndarray:
     y = np.empty((n_tok, s.d), dtype=np.float32)
     sh = s.has_shared
     k = idx.shape[1]  # routes per token as given (may differ from the layer's top_k)
+    dg = getattr(layer, "down_gain", None)
+    gain = None if dg is None else _c(dg, np.float32)
     rc = lib().orc_ffn(s.E, s.d, s.f, k, s.fmt_gate_up, s.fmt_down, _p(_c(layer.w_gate, np.uint8)),
                        _p(_c(layer.w_up, np.uint8)), _p(_c(layer.w_down, np.uint8)), _p(_c(layer.grid, np.uint8)),
                        int(sh), s.fmt_shared if sh else 0,
                        _p(_c(layer.s_gate, np.uint8)) if sh else None,
                        _p(_c(layer.s_up, np.uint8)) if sh else None,
                        _p(_c(layer.s_down, np.uint8)) if sh else None,
-                       _p(x), x_dtype, T, _p(tok), n_tok, _p(idx), _p(wt), _p(y))
+                       _p(gain), _p(x), x_dtype, T, _p(tok), n_tok, _p(idx), _p(wt), _p(y))
     if rc != 0:
         raise ValueError("oracle ffn: token or expert index out of range")
     return y
@@ -175,5 +195,5 @@ def layer_forward(layer, x, x_dtype, tokens=None):
     """Routing + FFN for the listed tokens: returns (y, idx, wt) for them."""
     x = _x(x, x_dtype)
     xs = x if tokens is None else x[np.asarray(tokens)]
-    _, idx, wt = route(xs, x_dtype, layer.w_router, layer.spec.k)
+    _, idx, wt = route(xs, x_dtype, layer.w_router, layer.spec.k, getattr(layer, "router_bias", None))
     return ffn(layer, xs, x_dtype, idx, wt), idx, wt

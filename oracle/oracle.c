@@ -131,6 +131,53 @@ void orc_topk(const float* z, int T, int E, int k, int32_t* idx) {
 }
 
 /*
+ * Selection keys with a router bias (the sidecar's selection-only bias,
+ * YoungAi page, section 4.2: the bias moves which experts are chosen and
+ * leaves the mixing weights alone): key_e = sigmoid32(z_e) + b_e in fp32,
+ * then the same top-k as above on the keys.  sigmoid32 is a fixed sequence
+ * of IEEE fp32 operations (the pages give none; any implementation that
+ * performs exactly these operations reproduces every bit):
+ *   z clamped to [-80, 80]; t = -z
+ *   n = rint(t * log2(e)) by adding and subtracting 1.5 * 2^23
+ *   r = (t - n * ln2_hi) - n * ln2_lo        (ln2_hi has 16 significant bits,
+ *                                            so n * ln2_hi is exact)
+ *   p = ((((((r/720 + 1/120) r + 1/24) r + 1/6) r + 1/2) r + 1) r + 1)
+ *       (Taylor coefficients of e^r, Horner, each step a product then a sum)
+ *   e = p * 2^n                               (exact: 2^n built from bits)
+ *   sigmoid32 = 1 / (1 + e)                   (correctly rounded division)
+ * The constants are the fp32 values of the hex literals below.
+ */
+float orc_sigmoid32(float z) {
+  const float log2e = 0x1.715476p+0f, ln2_hi = 0x1.62e400p-1f, ln2_lo = 0x1.7f7d1cp-20f;
+  const float c720 = 0x1.6c16c2p-10f, c120 = 0x1.111112p-7f, c24 = 0x1.555556p-5f, c6 = 0x1.555556p-3f;
+  const float shifter = 0x1.8p+23f;
+  float zc = z < -80.0f ? -80.0f : (z > 80.0f ? 80.0f : z);
+  float t = -zc;
+  float kf = t * log2e;
+  float n = (kf + shifter) - shifter;
+  float r = (t - n * ln2_hi) - n * ln2_lo;
+  float p = c720;
+  p = p * r + c120;
+  p = p * r + c24;
+  p = p * r + c6;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  union {
+    uint32_t u;
+    float f;
+  } two_n;
+  two_n.u = (uint32_t)((int)n + 127) << 23;
+  float e = p * two_n.f;
+  return 1.0f / (1.0f + e);
+}
+
+void orc_bias_keys(const float* z, int T, int E, const float* b, float* key) {
+  for (int t = 0; t < T; t++)
+    for (int e = 0; e < E; e++) key[(int64_t)t * E + e] = orc_sigmoid32(z[(int64_t)t * E + e]) + b[e];
+}
+
+/*
  * Mixing weights: s_j = 1 / (1 + exp(-z_j)) for the k selected experts, in
  * double precision; w_j = s_j / (s_0 + ... + s_{k-1}) with the sum taken in
  * rank order; stored as fp32.  No extra routed scaling factor.  Selection
@@ -294,16 +341,19 @@ static int64_t mat_bytes(int fmt, int rows, int K) {
 /*
  * Expert FFN of a layer for the tokens listed in `tokens` (n_tok of them;
  * NULL means tokens 0..T-1) with caller-given routes idx/wt [T][k]:
- *   acc = sum_j wt[t][j] * D_e(silu(G_e x_t) * (U_e x_t))  (j in rank order)
- *       + D_s(silu(G_s x_t) * (U_s x_t))                    (if has_shared)
+ *   acc = sum_j wt[t][j] * (g_e * D_e(silu(G_e x_t) * (U_e x_t)))  (j in rank order)
+ *       + D_s(silu(G_s x_t) * (U_s x_t))                            (if has_shared)
+ * where g_e is expert e's per-output-channel down gain (down_gain [E][d],
+ * the sidecar's gains of the YoungAi page, section 4.2) or one when
+ * down_gain is NULL.
  *   y[row] = fp32(acc)  (round to nearest even), row = position in `tokens`.
  * The routing weight multiplies each expert's down-projection output, as in
  * the per-layer sum of the YoungAi page, section 4.2.
  */
 int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
             const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
-            const uint8_t* s_up, const uint8_t* s_down, const void* x, int x_dtype, int T, const int32_t* tokens,
-            int n_tok, const int32_t* idx, const float* wt, float* y) {
+            const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype, int T,
+            const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y) {
   int64_t gu_bytes = mat_bytes(fmt_gu, f, d), dn_bytes = mat_bytes(fmt_dn, d, f);
   double* xv = (double*)malloc(sizeof(double) * (size_t)d);
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
@@ -328,7 +378,10 @@ int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w
       expert(fmt_gu, w_gate + e * gu_bytes, w_up + e * gu_bytes, fmt_dn, w_down + e * dn_bytes, d, f, grid, xv, ye,
              g, u);
       double w = (double)wt[(int64_t)t * k + j];
-      for (int i = 0; i < d; i++) acc[i] += w * ye[i];
+      if (down_gain)
+        for (int i = 0; i < d; i++) acc[i] += w * ((double)down_gain[(int64_t)e * d + i] * ye[i]);
+      else
+        for (int i = 0; i < d; i++) acc[i] += w * ye[i];
     }
     if (status != 0) break;
     if (has_shared) {

@@ -303,6 +303,8 @@ class Layer:
     s_gate: np.ndarray | None = None
     s_up: np.ndarray | None = None
     s_down: np.ndarray | None = None
+    router_bias: np.ndarray | None = None  # float32 [E]: selection-only bias (None: select on the logits)
+    down_gain: np.ndarray | None = None    # float32 [E, d]: per-channel down gains (None: ones)
     meta: dict = field(default_factory=dict)
 
 

@@ -291,6 +291,83 @@ def test_weights_sum_to_one_and_positive():
     assert np.all(np.diff(wt, axis=1) <= 0)  # rank order -> non-increasing weights
 
 
+# ------------------------------------------------ selection bias, gains ----
+def test_sigmoid32_against_fp64_and_shape():
+    zs = np.concatenate([np.linspace(-90, 90, 20001), [0.0, 1e-30, -1e-30, 80.0, -80.0, 1e4, -1e4]]).astype(np.float32)
+    got = np.array([oracle.sigmoid32(float(z)) for z in zs], np.float64)
+    zc = np.clip(zs.astype(np.float64), -80, 80)
+    exact = 1.0 / (1.0 + np.exp(-zc))
+    assert np.all(np.abs(got - exact) <= 4e-7 * exact)            # a few fp32 ulp everywhere
+    assert oracle.sigmoid32(0.0) == 0.5                             # e = 1 exactly
+    order = np.argsort(zs, kind="stable")
+    assert np.all(np.diff(got[order]) >= 0)                         # non-decreasing
+    for z in [0.5, 3.0, 17.25, 60.0]:                               # sigma(z) + sigma(-z) = 1
+        assert abs(oracle.sigmoid32(z) + oracle.sigmoid32(-z) - 1.0) <= 2e-7
+    assert oracle.sigmoid32(100.0) == oracle.sigmoid32(80.0) == 1.0   # clamp
+    assert oracle.sigmoid32(-100.0) == oracle.sigmoid32(-80.0) > 0.0
+
+
+def test_bias_selection_against_brute_force_and_invariants():
+    rng = np.random.default_rng(21)
+    E, k, T = 40, 6, 25
+    z = rng.normal(0, 2, (T, E)).astype(np.float32)
+    b = rng.normal(0, 0.05, E).astype(np.float32)
+    key = oracle.bias_keys(z, b)
+    s32 = np.array([[oracle.sigmoid32(float(v)) for v in row] for row in z], np.float32)
+    assert np.array_equal(key, (s32 + b).astype(np.float32))        # one fp32 addition per key
+    # brute force on the keys, ties to the lower index
+    idx = oracle.topk(key, k)
+    for t in range(T):
+        assert list(idx[t]) == sorted(range(E), key=lambda e: (-key[t, e], e))[:k]
+    # zero bias selects as the logits do (sigmoid is increasing; distinct logits here)
+    assert np.array_equal(oracle.topk(oracle.bias_keys(z, np.zeros(E, np.float32)), k), oracle.topk(z, k))
+    # a large bias on a chosen set forces exactly that set, best logit first
+    forced = np.array([3, 11, 17, 22, 30, 39])
+    bb = np.zeros(E, np.float32)
+    bb[forced] = 4.0
+    sel = oracle.topk(oracle.bias_keys(z, bb), k)
+    for t in range(T):
+        assert sorted(sel[t]) == sorted(forced)
+        assert list(sel[t]) == sorted(forced, key=lambda e: (-z[t, e], e))
+    # equal keys: lower index first
+    zt = np.zeros((1, 8), np.float32)
+    assert list(oracle.topk(oracle.bias_keys(zt, np.full(8, 0.25, np.float32)), 3)[0]) == [0, 1, 2]
+    # the bias moves the selection, not the weights: weights = normalised sigmoid(z) of the chosen set
+    W = rng.normal(0, 0.02, (E, 256)).astype(np.float32)
+    xs = rng.normal(0, 1, (T, 256)).astype(np.float32)
+    zz, idx_b, wt_b = oracle.route(xs, oracle.F32, W, k, bias=bb)
+    for t in range(T):
+        s = 1.0 / (1.0 + np.exp(-zz[t, idx_b[t]].astype(np.float64)))
+        assert np.allclose(wt_b[t], s / s.sum(), rtol=0, atol=2e-7)
+        assert sorted(idx_b[t]) == sorted(forced)
+
+
+def test_down_gains_scale_each_expert_channel():
+    spec = synth.scaled_spec(E=6, k=3, d=256, f=256)
+    L = synth.random_layer(spec, seed=22, workload="gain")
+    x = synth.activations(22, ("gain", "x"), 4, spec.d, synth.F32)
+    _, idx, wt = oracle.route(x, oracle.F32, L.w_router, spec.k)
+    y0 = oracle.ffn(L, x, oracle.F32, idx, wt)
+    Lg = synth.Layer(**{**L.__dict__, "down_gain": np.ones((spec.E, spec.d), np.float32)})
+    assert np.array_equal(oracle.ffn(Lg, x, oracle.F32, idx, wt), y0)        # unit gains change nothing
+    # routed part alone (no shared expert): gains c_e scale expert e's contribution, per channel
+    spec_ns = synth.scaled_spec(E=6, k=3, d=256, f=256, has_shared=False)
+    Ln = synth.random_layer(spec_ns, seed=22, workload="gain")
+    ones = np.ones((1, 1), np.float32)
+    g = np.random.default_rng(23).uniform(0.5, 1.5, (6, 256)).astype(np.float32)
+    g[:, 7] = 0.0                                                           # a muted channel
+    Lng = synth.Layer(**{**Ln.__dict__, "down_gain": g})
+    for t in range(4):
+        e = int(idx[t, 0])
+        one = np.array([[e]], np.int32)
+        solo = oracle.ffn(Ln, x[t:t + 1], oracle.F32, one, ones)[0].astype(np.float64)
+        solo_g = oracle.ffn(Lng, x[t:t + 1], oracle.F32, one, ones)[0].astype(np.float64)
+        assert np.allclose(solo_g, g[e] * solo, rtol=1e-6, atol=1e-12)
+        assert solo_g[7] == 0.0
+    yng = oracle.ffn(Lng, x, oracle.F32, idx, wt)
+    assert np.all(yng[:, 7] == 0.0)
+
+
 # ---------------------------------------------------------------- buckets ----
 def test_bucket_matches_stable_argsort():
     rng = np.random.default_rng(12)
