@@ -18,10 +18,11 @@
  *   - Each expert is a SwiGLU FFN: h = silu(G x) * (U x), ye = D h.
  *   - The per-layer output is the weighted sum of the chosen experts' down
  *     projections plus the always-on shared expert:
- *         y_t = sum_j wt[t][j] * ye_{idx[t][j]}(x_t) + ysh(x_t)
- *     (YoungAi page, section 4.2, the engine's per-layer MoE sum, with the
- *     sidecar gains equal to one), where ye is taken before the routing
- *     weight is applied.
+ *         y_t = sum_j wt[t][j] * (g_e * ye_e(x_t)) + ysh(x_t),  e = idx[t][j]
+ *     (YoungAi page, section 4.2, the engine's per-layer MoE sum), where ye
+ *     is taken before the routing weight is applied and g_e is expert e's
+ *     optional per-output-channel down gain (the sidecar's gains; one when
+ *     moe_layer.down_gain is NULL), applied element-wise.
  *
  * Router definition used by every entry point (the pages name no score
  * function, summation order or tie rule; these are this library's readings):
@@ -40,6 +41,18 @@
  *   p[0].  bf16 activations are widened to fp32 exactly before use.
  *   Ranking on z rather than on sigmoid(z) gives the same order in exact
  *   arithmetic and keeps the selection independent of any exp routine.
+ *   With a router bias b (moe_layer.router_bias / the bias argument of
+ *   moe_route_topk, the sidecar's selection-only bias of the YoungAi page,
+ *   section 4.2) the selection ranks key[t][e] = sigmoid32(z[t][e]) + b[e]
+ *   (one fp32 addition) instead of z, with the same tie rule; the weights
+ *   are unchanged (still from z).  sigmoid32 is this fixed sequence of
+ *   IEEE fp32 operations, each rounded on its own:
+ *     zc = z clamped to [-80, 80]; t = -zc; kf = t * 0x1.715476p+0;
+ *     n = (kf + 0x1.8p+23) - 0x1.8p+23;
+ *     r = (t - n * 0x1.62e400p-1) - n * 0x1.7f7d1cp-20;
+ *     p = 0x1.6c16c2p-10; then p = p * r + c for c = 0x1.111112p-7,
+ *       0x1.555556p-5, 0x1.555556p-3, 0.5, 1, 1 in turn;
+ *     e = p * 2^n (2^n exact from its bits); sigmoid32 = 1 / (1 + e).
  *
  * -------------------------------------------------------------------------
  * Weight formats (canonical layout; all fields little-endian; the pages give
@@ -125,7 +138,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes. */
 #define MOE_OK 0
@@ -191,6 +204,8 @@ typedef struct moe_layer {
   const void* s_gate;         /* [f rows][d] */
   const void* s_up;           /* [f rows][d] */
   const void* s_down;         /* [d rows][f] */
+  const float* router_bias;   /* nullable fp32 [E]: selection-only router bias */
+  const float* down_gain;     /* nullable fp32 [E][d], 16-byte aligned: down gains */
 } moe_layer;
 
 /* ABI version compiled into the library (== MOE_ABI_VERSION of its header). */
@@ -233,13 +248,14 @@ int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t K,
 
 /*
  * Router and exact top-k (definition at the top of this header).
- *   w_router fp32 [E][d]; x [T][d] in x_dtype; idx int32 [T][k] (rank
- *   order); wt fp32 [T][k].  Workspace: moe_workspace_bytes(MOE_OP_ROUTE).
+ *   w_router fp32 [E][d]; bias nullable fp32 [E] (selection on the biased
+ *   keys when given); x [T][d] in x_dtype; idx int32 [T][k] (rank order);
+ *   wt fp32 [T][k].  Workspace: moe_workspace_bytes(MOE_OP_ROUTE).
  */
-int moe_route_topk(const float* w_router, int32_t E, int32_t d,
-                   const void* x, int32_t x_dtype, int32_t T, int32_t k,
-                   int32_t* idx, float* wt, void* ws, size_t ws_bytes,
-                   void* stream);
+int moe_route_topk(const float* w_router, const float* bias, int32_t E,
+                   int32_t d, const void* x, int32_t x_dtype, int32_t T,
+                   int32_t k, int32_t* idx, float* wt, void* ws,
+                   size_t ws_bytes, void* stream);
 
 /*
  * Token-to-expert bucketing of the T*k routes (flat route r = t*k + j with

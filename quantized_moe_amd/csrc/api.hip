@@ -208,6 +208,10 @@ static int check_layer(const char* fn, const moe_layer* L, bool need_router) {
   }
   if (iq2) NEED_PTR(L->iq2_grid, "iq2_grid");
   if (need_router) NEED_PTR(L->w_router, "w_router");
+  if (L->router_bias && ((uintptr_t)L->router_bias & 3u))
+    return fail(MOE_ERR_INVALID_ARG, "%s: router_bias is not 4-byte aligned", fn);
+  if (L->down_gain && !aligned16(L->down_gain))
+    return fail(MOE_ERR_INVALID_ARG, "%s: down_gain is not 16-byte aligned", fn);
   return MOE_OK;
 }
 
@@ -392,14 +396,16 @@ extern "C" int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t 
   return ok();
 }
 
-extern "C" int moe_route_topk(const float* w_router, int32_t E, int32_t d, const void* x, int32_t x_dtype, int32_t T,
-                              int32_t k, int32_t* idx, float* wt, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int moe_route_topk(const float* w_router, const float* bias, int32_t E, int32_t d, const void* x,
+                              int32_t x_dtype, int32_t T, int32_t k, int32_t* idx, float* wt, void* ws,
+                              size_t ws_bytes, void* stream) {
   const char* fn = "moe_route_topk";
   int rc = check_dims(fn, E, d, k);
   if (rc) return rc;
   if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
   if (T == 0) return ok();
   NEED_PTR(w_router, "w_router");
+  if (bias && ((uintptr_t)bias & 3u)) return fail(MOE_ERR_INVALID_ARG, "%s: bias is not 4-byte aligned", fn);
   NEED_PTR(x, "x");
   NEED_PTR(idx, "idx");
   NEED_PTR(wt, "wt");
@@ -416,7 +422,7 @@ extern "C" int moe_route_topk(const float* w_router, int32_t E, int32_t d, const
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   pid = prof_begin("topk", s);
-  e = launch_topk(w.z, T, E, k, idx, wt, nullptr, nullptr, s);
+  e = launch_topk(w.z, T, E, k, bias, idx, wt, nullptr, nullptr, s);
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -464,6 +470,8 @@ static DecodeLaunch decode_launch(const moe_layer* L, const void* x, int x_dtype
   D.w_router = L->w_router;
   D.x = x;
   D.x_dtype = x_dtype;
+  D.router_bias = L->router_bias;
+  D.down_gain = L->down_gain;
   return D;
 }
 
@@ -487,6 +495,7 @@ static PrefillLaunch prefill_launch(const moe_layer* L, const void* x, int x_dty
   P.grid = L->iq2_grid;
   P.x = x;
   P.x_dtype = x_dtype;
+  P.down_gain = L->down_gain;
   return P;
 }
 
@@ -507,6 +516,7 @@ static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_
   P.tile_start = w.tile_start;
   P.perm = w.perm;
   P.pos = w.pos;
+  P.idx = idx;
   P.wt = wt;
   P.x16 = w.x16;
   P.xs = w.xs;
@@ -624,7 +634,7 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   pid = prof_begin("topk", s);
-  e = launch_topk(lw.z, T, E, k, lw.idx, lw.wt, idx_out, wt_out, s);
+  e = launch_topk(lw.z, T, E, k, L->router_bias, lw.idx, lw.wt, idx_out, wt_out, s);
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return run_prefill(fn, L, x, x_dtype, T, lw.idx, lw.wt, y, nullptr, c, s);

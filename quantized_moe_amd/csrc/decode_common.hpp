@@ -761,6 +761,8 @@ struct DecodeArgs {
   uint8_t* xq_s;     // [T][d/64] x in the shared gate/up format's layout (when shared_k2)
   float* xs_s;       // [T][d/64]
   int shared_k2;     // the shared gate/up runs in the second launch (one token), not the first
+  const float* router_bias;  // nullable [E]: selection on sigmoid32(z) + bias
+  const float* down_gain;    // nullable [E][d]: per-channel gains of the routed outputs
   float* hsh;        // [T][f] shared SwiGLU output, fp32
   uint8_t* hq;       // [T*k][f/16] quantized routed SwiGLU outputs
   float* hs;         // [T*k][f/16]

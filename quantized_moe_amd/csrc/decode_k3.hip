@@ -1,8 +1,8 @@
 // Third decode launch: down projections of the routed experts and of the
-// shared expert, and the combine y = sum_j wt_j ye_j + ysh in that fixed
-// order (the per-layer MoE sum of "YoungAi -- DeepSeek V4.1 Flash on one DGX
-// Spark", section 4.2, with unit gains; ye is taken before the routing
-// weight).
+// shared expert, and the combine y = sum_j wt_j (g_j ye_j) + ysh in that
+// fixed order (the per-layer MoE sum of "YoungAi -- DeepSeek V4.1 Flash on
+// one DGX Spark", section 4.2; g_j the routed expert's per-channel down
+// gains, one when none are given; ye is taken before the routing weight).
 //
 // Block = 16 output rows of one token.  Tasks: the k routed experts (16 rows
 // each, or two tasks of 8 rows) and the shared expert (in two or four
@@ -82,7 +82,14 @@ __global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) 
   if ((int)threadIdx.x < DN_ROWS) {
     const int n = threadIdx.x;
     float acc = 0.0f;
-    for (int q = 0; q < a.k; q++) acc = __builtin_fmaf(a.wt[(int64_t)t * a.k + q], ye[q * DN_ROWS + n], acc);
+    for (int q = 0; q < a.k; q++) {
+      float v = ye[q * DN_ROWS + n];
+      if (a.down_gain) {  // (an out-of-range expert id contributed zero)
+        const int e = a.idx[(int64_t)t * a.k + q];
+        if ((unsigned)e < (unsigned)a.E) v *= a.down_gain[(int64_t)e * a.d + row0 + n];
+      }
+      acc = __builtin_fmaf(a.wt[(int64_t)t * a.k + q], v, acc);
+    }
     if (a.has_shared) acc += ye[a.k * DN_ROWS + n];
     a.y[(int64_t)t * a.d + row0 + n] = acc;
   }

@@ -34,8 +34,8 @@ void prof_take_events(hipEvent_t* start, hipEvent_t* stop);  // the pending pair
 
 // route.hip
 hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtype, int T, float* z, hipStream_t s);
-hipError_t launch_topk(const float* z, int T, int E, int k, int32_t* idx, float* wt, int32_t* idx2, float* wt2,
-                       hipStream_t s);
+hipError_t launch_topk(const float* z, int T, int E, int k, const float* bias, int32_t* idx, float* wt, int32_t* idx2,
+                       float* wt2, hipStream_t s);
 
 // bucket.hip.  tile_start (nullable): [E+1] exclusive prefix of
 // ceil(counts[e] / tile_m) -- the M-tile schedule of the grouped GEMMs.
@@ -60,6 +60,8 @@ struct DecodeLaunch {
   void* quant;             // decode_quant_bytes() of workspace: shared h, quantized h
   float* y;                // [T][d]
   int fused_topk;          // 1: router logits in the first launch, top-k in the second
+  const float* router_bias;  // nullable [E]: select on sigmoid32(z) + bias (fused_topk)
+  const float* down_gain;    // nullable [E][d]: per-channel gains of each routed expert's output
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
 size_t decode_quant_bytes(int T, int k, int d, int f);
@@ -74,7 +76,9 @@ struct PrefillLaunch {
   const void* x;
   int x_dtype;
   const int32_t *counts, *offsets, *tile_start, *perm, *pos;
+  const int32_t* idx;      // [T][k] routes (for the down gains)
   const float* wt;
+  const float* down_gain;  // nullable [E][d]
   uint16_t* x16;  // fp16 [T][d]: x times a per-token power of two
   float* xs;      // [T]: that power of two
   float* route_xs;  // [T*k]: the same at each route, in bucket order

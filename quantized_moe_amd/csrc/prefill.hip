@@ -792,11 +792,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: y[t] = sum_j wt[t][j] * Ye[pos[t*k+j]] + ysh[t]   (fixed j order)
+// combine: y[t] = sum_j wt[t][j] * (g_e * Ye[pos[t*k+j]]) + ysh[t]   (fixed j order; g_e the route's
+// per-channel down gains, one when none are given)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ye, const float* __restrict__ ysh,
                                                       const int32_t* __restrict__ pos, const float* __restrict__ wt,
-                                                      int k, int d, int n_routes, float* __restrict__ y) {
+                                                      const int32_t* __restrict__ idx, const float* __restrict__ gain,
+                                                      int E, int k, int d, int n_routes, float* __restrict__ y) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -804,7 +806,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int p = pos[(int64_t)t * k + j];
       if ((unsigned)p >= (unsigned)n_routes) continue;  // a route with an out-of-range expert id
       const float w = wt[(int64_t)t * k + j];
-      const float4 v = *reinterpret_cast<const float4*>(ye + (int64_t)p * d + 4 * c);
+      float4 v = *reinterpret_cast<const float4*>(ye + (int64_t)p * d + 4 * c);
+      if (gain) {  // per-channel down gains of the route's expert
+        const int e = idx[(int64_t)t * k + j];
+        if ((unsigned)e >= (unsigned)E) continue;
+        const float4 g = *reinterpret_cast<const float4*>(gain + (int64_t)e * d + 4 * c);
+        v = make_float4(g.x * v.x, g.y * v.y, g.z * v.z, g.w * v.w);
+      }
       acc.x = __builtin_fmaf(w, v.x, acc.x);
       acc.y = __builtin_fmaf(w, v.y, acc.y);
       acc.z = __builtin_fmaf(w, v.z, acc.z);
@@ -996,7 +1004,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
   }
   const int pid = prof_begin("prefill_combine", s);
   QMOE_LAUNCH(combine_kernel, dim3(P.T), dim3(256), 0, s, (const float*)P.Ye, (const float*)(P.has_shared ? P.Ysh : nullptr),
-              (const int32_t*)P.pos, (const float*)P.wt, P.k, P.d, P.T * P.k, P.y);
+              (const int32_t*)P.pos, (const float*)P.wt, P.idx, P.down_gain, P.E, P.k, P.d, P.T * P.k, P.y);
   prof_end(pid, s);
   return hipGetLastError();
 }

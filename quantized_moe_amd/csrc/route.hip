@@ -187,16 +187,18 @@ hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtyp
   return hipGetLastError();
 }
 
-// One wave per token.  idx2/wt2 are optional second copies (may be null).
+// One wave per token.  idx2/wt2 are optional second copies (may be null);
+// bias (nullable) selects on the biased sigmoid keys.
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int T, int E, int k,
-                                                   int32_t* __restrict__ idx, float* __restrict__ wt,
-                                                   int32_t* __restrict__ idx2, float* __restrict__ wt2) {
+                                                   const float* __restrict__ bias, int32_t* __restrict__ idx,
+                                                   float* __restrict__ wt, int32_t* __restrict__ idx2,
+                                                   float* __restrict__ wt2) {
   __shared__ int s_sel[4][TOPK_MAX_K];
   __shared__ float s_z[4][TOPK_MAX_K];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  wave_topk(z + (int64_t)t * E, E, k, s_sel[wave], s_z[wave]);
+  wave_topk(z + (int64_t)t * E, E, k, s_sel[wave], s_z[wave], bias);
   if (lane == 0) {  // lane 0 wrote the lists it reads back
     float w[TOPK_MAX_K];
     topk_weights(s_z[wave], k, w);
@@ -211,10 +213,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, 
   }
 }
 
-hipError_t launch_topk(const float* z, int T, int E, int k, int32_t* idx, float* wt, int32_t* idx2, float* wt2,
-                       hipStream_t s) {
+hipError_t launch_topk(const float* z, int T, int E, int k, const float* bias, int32_t* idx, float* wt, int32_t* idx2,
+                       float* wt2, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  QMOE_LAUNCH(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, T, E, k, idx, wt, idx2, wt2);
+  QMOE_LAUNCH(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, z, T, E, k, bias, idx, wt, idx2, wt2);
   return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Exact top-k of one token's router logits by one wave, and the mixing
-// weights of the selected experts.  Shared by the top-k kernel and the decode
+// Exact top-k of one token's router logits (or of its biased selection keys)
+// by one wave, and the mixing weights of the selected experts.  Shared by the top-k kernel and the decode
 // kernels that fuse top-k into their prologue.
 //
 // Every (logit, expert) pair becomes one 64-bit key: the logit's bits mapped
@@ -27,6 +27,37 @@ __device__ __forceinline__ uint32_t logit_order_bits(float z) {
 
 __device__ __forceinline__ float logit_from_order_bits(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The selection key of an expert under a router bias b: sigmoid32(z) + b in
+// fp32, where sigmoid32 is the fixed sequence of IEEE fp32 operations that
+// the interface defines (clamp z to [-80, 80]; t = -z; n = rint(t log2 e)
+// by adding and subtracting 1.5 2^23; r = (t - n ln2_hi) - n ln2_lo; the
+// degree-6 Taylor polynomial of e^r in Horner form, each step a product and
+// then a sum; e = p 2^n with 2^n built from its bits; 1 / (1 + e)), so that
+// every implementation performing these operations gets the same bits.
+__device__ __forceinline__ float sigmoid32(float z) {
+#pragma clang fp contract(off)  // every product and sum rounded on its own
+  const float zc = fminf(fmaxf(z, -80.0f), 80.0f);
+  const float t = -zc;
+  const float kf = t * 0x1.715476p+0f;
+  const float n = (kf + 0x1.8p+23f) - 0x1.8p+23f;
+  const float r = (t - n * 0x1.62e400p-1f) - n * 0x1.7f7d1cp-20f;
+  float p = 0x1.6c16c2p-10f;
+  p = p * r + 0x1.111112p-7f;
+  p = p * r + 0x1.555556p-5f;
+  p = p * r + 0x1.555556p-3f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  const float e = p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+  return 1.0f / (1.0f + e);
+}
+
+// The value a top-k ranks expert e on: its logit, or with a router bias its
+// biased sigmoid key.
+__device__ __forceinline__ float topk_rank_value(float z, const float* bias, int e) {
+  return bias ? sigmoid32(z) + bias[e] : z;
 }
 
 template <int CTRL, int ROW_MASK>
@@ -57,7 +88,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // entries, rank order) are written by lane 0 only; they are typically LDS
 // arrays.
 template <int SLOTS>
-__device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z) {
+__device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z,
+                                            const float* bias) {
   const int lane = threadIdx.x & 63;
   uint64_t key[SLOTS];
   float zv[SLOTS];
@@ -66,7 +98,8 @@ __device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E,
 #pragma unroll
   for (int i = 0; i < SLOTS; i++) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? (((uint64_t)logit_order_bits(zv[i]) << 32) | (uint32_t)~e) : 0ull;
+    const float v = topk_rank_value(zv[i], bias, min(e, E - 1));
+    key[i] = e < E ? (((uint64_t)logit_order_bits(v) << 32) | (uint32_t)~e) : 0ull;
   }
   for (int r = 0; r < k; r++) {
     uint64_t best = 0;
@@ -77,8 +110,9 @@ __device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E,
     for (int i = 0; i < SLOTS; i++)
       if (key[i] == best) key[i] = 0;
     if (lane == 0) {
-      out_idx[r] = (int)~(uint32_t)best;
-      out_z[r] = logit_from_order_bits((uint32_t)(best >> 32));
+      const int e = (int)~(uint32_t)best;
+      out_idx[r] = e;
+      out_z[r] = bias ? zt[e] : logit_from_order_bits((uint32_t)(best >> 32));
     }
   }
 }
@@ -109,7 +143,7 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
 // wave_topk_n: largest logit first, equal logits to the smaller index.
 template <int SLOTS>
 __device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, int E, int k, int* out_idx,
-                                                 float* out_z) {
+                                                 float* out_z, const float* bias) {
   static_assert(SLOTS == 4 || SLOTS == 8, "network for 4 or 8 keys");
   const int lane = threadIdx.x & 63;
   uint32_t key[SLOTS];
@@ -120,7 +154,7 @@ __device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, i
 #pragma unroll
   for (int i = 0; i < SLOTS; i++) {
     ex[i] = lane + 64 * i;
-    key[i] = ex[i] < E ? logit_order_bits(zv[i]) : 0u;
+    key[i] = ex[i] < E ? logit_order_bits(topk_rank_value(zv[i], bias, min(ex[i], E - 1))) : 0u;
   }
   auto cx = [&](int i, int j) {  // put the better of slots i < j first
     const bool swap = key[j] > key[i] || (key[j] == key[i] && ex[j] < ex[i]);
@@ -155,19 +189,21 @@ __device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, i
     }
     if (lane == 0) {
       out_idx[r] = (int)win;
-      out_z[r] = logit_from_order_bits(best);
+      out_z[r] = bias ? zt[win] : logit_from_order_bits(best);
     }
   }
 }
 
-// Any E <= MAX_EXPERTS.
-__device__ __forceinline__ void wave_topk(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z) {
+// Any E <= MAX_EXPERTS.  bias (nullable, [E]): rank on the biased sigmoid
+// keys instead of the logits; out_z always receives the selected logits.
+__device__ __forceinline__ void wave_topk(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z,
+                                          const float* bias) {
   if (E <= 256)
-    wave_topk_sorted<4>(zt, E, k, out_idx, out_z);
+    wave_topk_sorted<4>(zt, E, k, out_idx, out_z, bias);
   else if (E <= 512)
-    wave_topk_sorted<8>(zt, E, k, out_idx, out_z);
+    wave_topk_sorted<8>(zt, E, k, out_idx, out_z, bias);
   else
-    wave_topk_n<TOPK_MAX_PER_LANE>(zt, E, k, out_idx, out_z);
+    wave_topk_n<TOPK_MAX_PER_LANE>(zt, E, k, out_idx, out_z, bias);
 }
 
 // Mixing weights from the selected logits: sigmoid in double precision,

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
-MOE_ABI_VERSION = 1
+MOE_ABI_VERSION = 2
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FMT_NONE, MOE_FMT_IQ2XXS_L, MOE_FMT_Q2K_L, MOE_FMT_Q8_0_L = 0, 1, 2, 3
@@ -57,6 +57,8 @@ class MoeLayer(ctypes.Structure):
         ("s_gate", ctypes.c_void_p),
         ("s_up", ctypes.c_void_p),
         ("s_down", ctypes.c_void_p),
+        ("router_bias", ctypes.c_void_p),
+        ("down_gain", ctypes.c_void_p),
     ]
 
 
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_matrix_bytes": ([_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
             "moe_workspace_bytes": ([ctypes.POINTER(MoeLayer), _I32, _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
             "moe_repack": ([_I32, _I32, _I32, _I32, _P, _P, _I32, _P], ctypes.c_int),
-            "moe_route_topk": ([_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
+            "moe_route_topk": ([_P, _P, _I32, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _SZ, _P], ctypes.c_int),
             "moe_bucket": ([_P, _I32, _I32, _I32, _P, _P, _P, _P, _P], ctypes.c_int),
             "moe_expert_ffn_decode": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
                                       ctypes.c_int),
@@ -149,10 +151,10 @@ def repack(fmt, n_experts, rows, K, src: torch.Tensor, dst: torch.Tensor, direct
     _check(lib().moe_repack(fmt, n_experts, rows, K, _ptr(src), _ptr(dst), direction, _stream(stream)))
 
 
-def route_topk(w_router, x, k, idx, wt, ws, stream=None) -> None:
+def route_topk(w_router, x, k, idx, wt, ws, stream=None, bias=None) -> None:
     E, d = w_router.shape
-    _check(lib().moe_route_topk(_ptr(w_router), E, d, _ptr(x), x_dtype_of(x), x.shape[0], k, _ptr(idx), _ptr(wt),
-                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    _check(lib().moe_route_topk(_ptr(w_router), _ptr(bias), E, d, _ptr(x), x_dtype_of(x), x.shape[0], k, _ptr(idx),
+                                _ptr(wt), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bucket(idx, E, counts, offsets, perm, pos, stream=None) -> None:
@@ -215,7 +217,8 @@ class DeviceLayer:
     """
 
     def __init__(self, E, d, f, k, fmt_gate_up, fmt_down, w_gate, w_up, w_down, grid, w_router,
-                 fmt_shared=MOE_FMT_NONE, s_gate=None, s_up=None, s_down=None, device="cuda"):
+                 fmt_shared=MOE_FMT_NONE, s_gate=None, s_up=None, s_down=None, device="cuda",
+                 router_bias=None, down_gain=None):
         self.E, self.d, self.f, self.k = E, d, f, k
         self.device = torch.device(device)
         self.tensors = {}
@@ -229,13 +232,18 @@ class DeviceLayer:
             self.tensors["s_gate"] = self._prep(fmt_shared, 1, f, d, s_gate)
             self.tensors["s_up"] = self._prep(fmt_shared, 1, f, d, s_up)
             self.tensors["s_down"] = self._prep(fmt_shared, 1, d, f, s_down)
+        if router_bias is not None:
+            self.tensors["router_bias"] = torch.from_numpy(np.ascontiguousarray(router_bias, np.float32)).to(self.device)
+        if down_gain is not None:
+            self.tensors["down_gain"] = torch.from_numpy(np.ascontiguousarray(down_gain, np.float32)).to(self.device)
         t = self.tensors
         self.desc = MoeLayer(
             abi_version=MOE_ABI_VERSION, n_experts=E, d_model=d, d_ff=f, top_k=k, fmt_gate_up=fmt_gate_up,
             fmt_down=fmt_down, layout=MOE_LAYOUT_DEVICE, w_gate=_ptr(t["w_gate"]), w_up=_ptr(t["w_up"]),
             w_down=_ptr(t["w_down"]), iq2_grid=_ptr(t["grid"]), w_router=_ptr(t["w_router"]),
             has_shared=1 if has_shared else 0, fmt_shared=fmt_shared if has_shared else 0,
-            s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")))
+            s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")),
+            router_bias=_ptr(t.get("router_bias")), down_gain=_ptr(t.get("down_gain")))
         torch.cuda.synchronize(self.device)
 
     def _prep(self, fmt, E, rows, K, canonical: np.ndarray) -> torch.Tensor:
@@ -253,7 +261,8 @@ class DeviceLayer:
         s = L.spec
         return cls(s.E, s.d, s.f, s.k, s.fmt_gate_up, s.fmt_down, L.w_gate, L.w_up, L.w_down, L.grid, L.w_router,
                    fmt_shared=s.fmt_shared if s.has_shared else MOE_FMT_NONE, s_gate=L.s_gate, s_up=L.s_up,
-                   s_down=L.s_down, device=device)
+                   s_down=L.s_down, device=device, router_bias=getattr(L, "router_bias", None),
+                   down_gain=getattr(L, "down_gain", None))
 
     def workspace(self, T: int, op: int = MOE_OP_LAYER) -> torch.Tensor:
         n = workspace_bytes(self.desc, T, op)

@@ -71,7 +71,8 @@ def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(abi_version=2), lib.MOE_ERR_UNSUPPORTED),
+    (dict(abi_version=1), lib.MOE_ERR_UNSUPPORTED),      # the layout before router_bias / down_gain
+    (dict(abi_version=99), lib.MOE_ERR_UNSUPPORTED),
     (dict(layout=lib.MOE_LAYOUT_CANONICAL), lib.MOE_ERR_UNSUPPORTED),
     (dict(layout=7), lib.MOE_ERR_UNSUPPORTED),
     (dict(fmt_gate_up=9), lib.MOE_ERR_UNSUPPORTED),
@@ -90,6 +91,8 @@ def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
     (dict(iq2_grid=0), lib.MOE_ERR_INVALID_ARG),          # IQ2 in use needs the grid
     (dict(s_up=0), lib.MOE_ERR_INVALID_ARG),
     (dict(has_shared=2), lib.MOE_ERR_INVALID_ARG),
+    (dict(router_bias=0x1002), lib.MOE_ERR_INVALID_ARG),  # misaligned
+    (dict(down_gain=0x1008), lib.MOE_ERR_INVALID_ARG),    # not 16-byte aligned
 ])
 def test_layer_validation(over, code):
     assert _ffn_decode(_layer(**over)) == code
@@ -100,6 +103,16 @@ def test_grid_not_needed_without_iq2_and_shared_optional():
     layer = _layer(fmt_gate_up=2, iq2_grid=0, has_shared=0, s_gate=0, s_up=0, s_down=0)
     # gets past layer validation; fails on the (deliberately) empty workspace
     assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE
+
+
+def test_bias_and_gains_are_optional():
+    layer = _layer(router_bias=0x3000, down_gain=0x4000)
+    assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE                  # past validation
+    assert _route_bias_misaligned() == lib.MOE_ERR_INVALID_ARG
+
+
+def _route_bias_misaligned():
+    return lib.lib().moe_route_topk(256, 0x1002, 384, 4096, 512, 0, 1, 6, 768, 1024, 1280, 1 << 20, None)
 
 
 def test_router_needed_only_by_the_whole_layer():
@@ -143,10 +156,10 @@ def test_workspace_sizes_cover_their_buffers():
 
 def test_route_and_bucket_validation():
     L = lib.lib()
-    assert L.moe_route_topk(256, 384, 4096, 512, 0, 1, 0, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
-    assert L.moe_route_topk(256, 2000, 4096, 512, 0, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
-    assert L.moe_route_topk(256, 384, 4096, 512, 0, 1, 6, 768, 1024, 1280, 0, None) == lib.MOE_ERR_WORKSPACE
-    assert L.moe_route_topk(256, 384, 4096, 512, 3, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(256, None, 384, 4096, 512, 0, 1, 0, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(256, None, 2000, 4096, 512, 0, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(256, None, 384, 4096, 512, 0, 1, 6, 768, 1024, 1280, 0, None) == lib.MOE_ERR_WORKSPACE
+    assert L.moe_route_topk(256, None, 384, 4096, 512, 3, 1, 6, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_UNSUPPORTED
     assert L.moe_bucket(256, 4, 6, 384, 0, 512, 768, 1024, None) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_bucket(256, 4, 0, 384, 256, 512, 768, 1024, None) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_bucket(0, 0, 6, 384, 0, 0, 0, 0, None) == lib.MOE_OK

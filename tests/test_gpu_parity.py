@@ -116,6 +116,61 @@ def test_layer_formats_and_shapes(case):
         assert rel_l2(y, y_ref) <= REL_L2, (path, rel_l2(y, y_ref))
 
 
+# ------------------------------------------ selection bias, down gains ----
+def _bias_gain_layer(spec, seed, gains=True):
+    L = synth.random_layer(spec, seed=seed, workload="bias")
+    rng = np.random.default_rng(seed + 100)
+    bias = rng.normal(0, 0.05, spec.E).astype(np.float32)
+    bias[1] = bias[0]                      # with equal router rows: equal keys, the lower index first
+    L.w_router[1] = L.w_router[0]
+    gain = rng.uniform(0.5, 1.5, (spec.E, spec.d)).astype(np.float32) if gains else None
+    return synth.Layer(**{**L.__dict__, "router_bias": bias, "down_gain": gain})
+
+
+def test_route_topk_with_bias():
+    spec = synth.DECODE_SPEC
+    L = _bias_gain_layer(spec, 31, gains=False)
+    for T, dt in [(1, synth.F32), (13, synth.F32), (300, synth.BF16)]:
+        x = synth.activations(31, ("bias", "route", T), T, spec.d, dt)
+        idx = torch.empty(T, spec.k, dtype=torch.int32, device=DEV)
+        wt = torch.empty(T, spec.k, dtype=torch.float32, device=DEV)
+        ws = torch.empty(4 << 20, dtype=torch.uint8, device=DEV)
+        lib.route_topk(torch.from_numpy(L.w_router).to(DEV), to_dev_x(x, dt), spec.k, idx, wt, ws,
+                       bias=torch.from_numpy(L.router_bias).to(DEV))
+        torch.cuda.synchronize()
+        _, idx_ref, wt_ref = oracle.route(x, dt, L.w_router, spec.k, bias=L.router_bias)
+        assert np.array_equal(idx.cpu().numpy(), idx_ref), T
+        assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
+        if T == 300:  # the bias does move selections
+            assert not np.array_equal(oracle.route(x, dt, L.w_router, spec.k)[1], idx_ref)
+
+
+@pytest.mark.parametrize("T,dt", [(1, synth.F32), (3, synth.F32), (37, synth.BF16)])
+def test_layer_with_bias_and_gains(T, dt):
+    spec = synth.scaled_spec(E=24, k=4, d=512, f=512)
+    L = _bias_gain_layer(spec, 32)
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(32, ("bias", "layer", T), T, spec.d, dt)
+    y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, dt)
+    paths = [lib.MOE_PATH_PREFILL] + ([lib.MOE_PATH_DECODE] if T <= lib.MOE_DECODE_MAX_T else [])
+    for path in paths:
+        y, idx, wt = run_layer(dl, x, dt, path)
+        assert np.array_equal(idx, idx_ref), path
+        assert np.max(np.abs(wt - wt_ref)) <= WT_TOL, path
+        assert rel_l2(y, y_ref) <= REL_L2, (path, rel_l2(y, y_ref))
+
+
+def test_decode_layer_with_bias_and_gains_full_size():
+    L = _bias_gain_layer(synth.DECODE_SPEC, 33)
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(33, ("bias", "full"), 2, 4096, synth.F32)
+    y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+    for t in range(2):
+        y, idx, wt = run_layer(dl, x[t:t + 1], synth.F32, lib.MOE_PATH_AUTO)
+        assert np.array_equal(idx[0], idx_ref[t])
+        assert rel_l2(y[0], y_ref[t]) <= REL_L2
+
+
 # ------------------------------------------------------------- routing ----
 def test_route_topk_ties_and_zero():
     E, d, k = 64, 256, 6
