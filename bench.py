@@ -130,6 +130,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=40)
     ap.add_argument("--profile-steps", type=int, default=256, help="eager steps with per-kernel events")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias-gain", action="store_true",
+                    help="give every layer a router selection bias and per-channel down gains (not the headline)")
     ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
     ap.add_argument("--pmc-mode", action="store_true",
                     help="no timing: a few decode and prefill steps and a plain copy of known size, for "
@@ -175,8 +177,15 @@ def main() -> int:
         desc.w_gate, desc.w_up, desc.w_down = rc["w_gate"].data_ptr(), rc["w_up"].data_ptr(), rc["w_down"].data_ptr()
         desc.w_router = wr.data_ptr()
         desc.s_gate, desc.s_up, desc.s_down = (sh[n].data_ptr() for n in ("s_gate", "s_up", "s_down"))
+        extra = ()
+        if args.bias_gain:
+            rng = np.random.default_rng(1000 + i)
+            bias = torch.from_numpy(rng.normal(0, 0.05, E).astype(np.float32)).to(dev)
+            gain = torch.from_numpy(rng.uniform(0.5, 1.5, (E, d)).astype(np.float32)).to(dev)
+            desc.router_bias, desc.down_gain = bias.data_ptr(), gain.data_ptr()
+            extra = (bias, gain)
         descs.append(desc)
-        keep.append((wr, sh))
+        keep.append((wr, sh) + extra)
     torch.cuda.synchronize()
     log(f"layers ready in {time.time() - t0:.1f}s (routed copies: 2 x {sum(t.numel() for t in second.values())/1e9:.2f} GB)")
 
@@ -381,7 +390,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "decode: one MoE layer, 384 experts, top-6, d=4096, f=2048, shared Q8_0-like "
                                "expert, IQ2_XXS-like gate/up, Q2_K-like down, T=1 fp32 token",
-                   "layer_descriptors": N_DESC, "routed_copies": 2, "graph_steps": N_DESC},
+                   "layer_descriptors": N_DESC, "routed_copies": 2, "graph_steps": N_DESC,
+                   "router_bias_and_down_gains": bool(args.bias_gain)},
         "roofline": dec["roofline"] if dec else None,
         "cpu_baseline": cpu,
         "decode": dec,

@@ -245,6 +245,7 @@ struct PrefillWs {
 };
 struct LayerWs {
   float* z;
+  float* zkey;  // selection keys under a router bias
   int32_t* idx;
   float* wt;
 };
@@ -275,6 +276,7 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
 }
 void carve_layer_routes(Carve& c, LayerWs& w, int E, int T, int k) {
   w.z = (float*)c.take((size_t)T * E * 4);
+  w.zkey = (float*)c.take((size_t)T * E * 4);
   w.idx = (int32_t*)c.take((size_t)T * k * 4);
   w.wt = (float*)c.take((size_t)T * k * 4);
 }
@@ -618,6 +620,7 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
     carve_decode(c, w, T, k, L->d_model, L->d_ff);
     DecodeLaunch D = decode_launch(L, x, x_dtype, T);
       D.z = lw.z;
+    D.zkey = lw.zkey;
     D.idx = lw.idx;
     D.wt = lw.wt;
     D.idx_out = idx_out;

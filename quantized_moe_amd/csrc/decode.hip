@@ -98,6 +98,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.idx_out = L.idx_out;
   a.wt_out = L.wt_out;
   a.router_bias = L.router_bias;
+  a.zkey = L.zkey;
   a.down_gain = L.down_gain;
   const DecodeWsLayout W = ws_layout(L.T, L.k, L.d, L.f);
   uint8_t* q = static_cast<uint8_t*>(L.quant);

@@ -762,6 +762,7 @@ struct DecodeArgs {
   float* xs_s;       // [T][d/64]
   int shared_k2;     // the shared gate/up runs in the second launch (one token), not the first
   const float* router_bias;  // nullable [E]: selection on sigmoid32(z) + bias
+  float* zkey;               // [T][E] the selection keys (fused routing with a bias), from the first launch
   const float* down_gain;    // nullable [E][d]: per-channel gains of the routed outputs
   float* hsh;        // [T][f] shared SwiGLU output, fp32
   uint8_t* hq;       // [T*k][f/16] quantized routed SwiGLU outputs

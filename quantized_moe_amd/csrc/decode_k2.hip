@@ -58,7 +58,10 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   // tables and run the shared gate/up (its weights do not depend on the routes)
   if (wave == 0) {
     if (a.fused_topk) {
-      wave_topk(a.z + (int64_t)t * a.E, a.E, a.k, s_sel, s_zs, a.router_bias);
+      if (a.router_bias)  // keys computed with the logits in the first launch
+        wave_topk(a.zkey + (int64_t)t * a.E, a.E, a.k, s_sel, s_zs, nullptr, a.z + (int64_t)t * a.E);
+      else
+        wave_topk(a.z + (int64_t)t * a.E, a.E, a.k, s_sel, s_zs, nullptr);
     } else if (lane < a.k) {
       s_sel[lane] = a.idx[(int64_t)t * a.k + lane];
     }

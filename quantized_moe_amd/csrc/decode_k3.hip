@@ -20,15 +20,16 @@ namespace dec {
 // codes, so both loads are in flight together.
 template <int FMT, int K, int ROWS>
 __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, const uint8_t* hq, const float* hs,
-                                          const float* hf, const Iq2Tab* tab, uint8_t* my_scales, float* out) {
+                                          const float* hf, const float* gain, const Iq2Tab* tab, uint8_t* my_scales,
+                                          float* out) {
   constexpr int NS = DownRows<FMT, K, ROWS, 1>::NS;
   DownRows<FMT, K, ROWS, (NS < 3 ? NS : 3)> dr;  // three steps of loads kept in flight ahead of the compute
   if (hq) {
     dr.load_act(hq, hs);
-    dr.issue(m, e, E, r0, my_scales);
+    dr.issue(m, e, E, r0, my_scales, gain);
   } else {
     dr.fetch_act_f32(hf);
-    dr.issue(m, e, E, r0, my_scales);
+    dr.issue(m, e, E, r0, my_scales, gain);
     dr.quant_act_f32();
   }
   dr.run(tab, my_scales, out);
@@ -70,26 +71,21 @@ __global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) 
       const int q = task / RT_PARTS, part = task % RT_PARTS;
       const int64_t r = (int64_t)t * a.k + q;
       const int e = a.idx[r];
+      // the expert's output gains scale its row results (ye holds g * y_e)
+      const float* gain = a.down_gain && (unsigned)e < (unsigned)a.E ? a.down_gain + (int64_t)e * a.d : nullptr;
       down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hq + r * NG * G16_BYTES, a.hs + r * NG,
-                                nullptr, &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
+                                nullptr, gain, &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
     } else {
       const int part = task - n_rt;
       down_rows<FS, F, SH_ROWS>(a.s_down, 0, 1, row0 + part * SH_ROWS, nullptr, nullptr, a.hsh + (int64_t)t * F,
-                                &itab, s_scl + wave * SCL_BYTES, ye + a.k * DN_ROWS + part * SH_ROWS);
+                                nullptr, &itab, s_scl + wave * SCL_BYTES, ye + a.k * DN_ROWS + part * SH_ROWS);
     }
   }
   __syncthreads();
   if ((int)threadIdx.x < DN_ROWS) {
     const int n = threadIdx.x;
     float acc = 0.0f;
-    for (int q = 0; q < a.k; q++) {
-      float v = ye[q * DN_ROWS + n];
-      if (a.down_gain) {  // (an out-of-range expert id contributed zero)
-        const int e = a.idx[(int64_t)t * a.k + q];
-        if ((unsigned)e < (unsigned)a.E) v *= a.down_gain[(int64_t)e * a.d + row0 + n];
-      }
-      acc = __builtin_fmaf(a.wt[(int64_t)t * a.k + q], v, acc);
-    }
+    for (int q = 0; q < a.k; q++) acc = __builtin_fmaf(a.wt[(int64_t)t * a.k + q], ye[q * DN_ROWS + n], acc);
     if (a.has_shared) acc += ye[a.k * DN_ROWS + n];
     a.y[(int64_t)t * a.d + row0 + n] = acc;
   }

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "decode_common.hpp"
+#include "topk.hpp"
 
 namespace qmoe {
 namespace dec {
@@ -49,7 +50,10 @@ __device__ __forceinline__ void router_item(const DecodeArgs& a, int e) {
     }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_down(p, s, 64);
-    if (lane == 0) a.z[(int64_t)t * a.E + e] = p;
+    if (lane == 0) {
+      a.z[(int64_t)t * a.E + e] = p;
+      if (a.router_bias) a.zkey[(int64_t)t * a.E + e] = sigmoid32(p) + a.router_bias[e];
+    }
   }
 }
 
@@ -188,6 +192,8 @@ struct DownRows {
   EPlanes Dp;
   int r0;
   bool valid;
+  const float* grow;  // nullable: this expert's per-channel output gains, [d]
+  float gv[NS];       // the gains of the rows this lane writes
 
   __device__ __forceinline__ void load_act(const uint8_t* hq, const float* hs) {
     const int c = (threadIdx.x & 63) % G::LPR;
@@ -221,11 +227,21 @@ struct DownRows {
       if constexpr (!STAGE) w[s][k].template scales_global<G::NB>(Dp, n, c + G::LPR * k);
     }
   }
-  __device__ __forceinline__ void issue(const QMat& m, int e, int E, int row0, uint8_t* my_scales) {
+  __device__ __forceinline__ void issue(const QMat& m, int e, int E, int row0, uint8_t* my_scales,
+                                        const float* gain = nullptr) {
     valid = (unsigned)e < (unsigned)E;
     if (!valid) return;
     Dp = expert_planes<FMT>(m, e);
     r0 = row0;
+    grow = gain;
+    if (gain) {  // requested first: the oldest loads are back first
+      const int lane = threadIdx.x & 63, sub = lane / G::LPR;
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+        const int j = s * G::RPS + sub;
+        gv[s] = gain[r0 + (j < ROWS ? j : 0)];
+      }
+    }
     SS ss;
     if constexpr (STAGE)
       ss.issue([&](int, int j, EPlanes& P, uint32_t& row) {
@@ -256,6 +272,7 @@ struct DownRows {
 #pragma unroll
       for (int k = 0; k < G::CPL; k++) v += piece_dot(w[s][k], act, k, tab);
       v = group_sum<G::LPR>(v);
+      if (grow) v *= gv[s];
       if (c == G::LPR - 1 && j < ROWS) out[j] = v;
     }
   }

@@ -61,6 +61,7 @@ struct DecodeLaunch {
   float* y;                // [T][d]
   int fused_topk;          // 1: router logits in the first launch, top-k in the second
   const float* router_bias;  // nullable [E]: select on sigmoid32(z) + bias (fused_topk)
+  float* zkey;               // [T][E] workspace for the keys (fused_topk with a bias)
   const float* down_gain;    // nullable [E][d]: per-channel gains of each routed expert's output
 };
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);

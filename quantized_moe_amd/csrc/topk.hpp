@@ -89,7 +89,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // arrays.
 template <int SLOTS>
 __device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z,
-                                            const float* bias) {
+                                            const float* bias, const float* zsrc) {
   const int lane = threadIdx.x & 63;
   uint64_t key[SLOTS];
   float zv[SLOTS];
@@ -112,7 +112,7 @@ __device__ __forceinline__ void wave_topk_n(const float* __restrict__ zt, int E,
     if (lane == 0) {
       const int e = (int)~(uint32_t)best;
       out_idx[r] = e;
-      out_z[r] = bias ? zt[e] : logit_from_order_bits((uint32_t)(best >> 32));
+      out_z[r] = zsrc ? zsrc[e] : (bias ? zt[e] : logit_from_order_bits((uint32_t)(best >> 32)));
     }
   }
 }
@@ -143,7 +143,7 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
 // wave_topk_n: largest logit first, equal logits to the smaller index.
 template <int SLOTS>
 __device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, int E, int k, int* out_idx,
-                                                 float* out_z, const float* bias) {
+                                                 float* out_z, const float* bias, const float* zsrc) {
   static_assert(SLOTS == 4 || SLOTS == 8, "network for 4 or 8 keys");
   const int lane = threadIdx.x & 63;
   uint32_t key[SLOTS];
@@ -189,21 +189,23 @@ __device__ __forceinline__ void wave_topk_sorted(const float* __restrict__ zt, i
     }
     if (lane == 0) {
       out_idx[r] = (int)win;
-      out_z[r] = bias ? zt[win] : logit_from_order_bits(best);
+      out_z[r] = zsrc ? zsrc[win] : (bias ? zt[win] : logit_from_order_bits(best));
     }
   }
 }
 
 // Any E <= MAX_EXPERTS.  bias (nullable, [E]): rank on the biased sigmoid
-// keys instead of the logits; out_z always receives the selected logits.
+// keys of the logits zt instead of the logits.  zsrc (nullable): zt already
+// holds the selection keys and zsrc the logits.  out_z always receives the
+// selected logits.
 __device__ __forceinline__ void wave_topk(const float* __restrict__ zt, int E, int k, int* out_idx, float* out_z,
-                                          const float* bias) {
+                                          const float* bias, const float* zsrc = nullptr) {
   if (E <= 256)
-    wave_topk_sorted<4>(zt, E, k, out_idx, out_z, bias);
+    wave_topk_sorted<4>(zt, E, k, out_idx, out_z, bias, zsrc);
   else if (E <= 512)
-    wave_topk_sorted<8>(zt, E, k, out_idx, out_z, bias);
+    wave_topk_sorted<8>(zt, E, k, out_idx, out_z, bias, zsrc);
   else
-    wave_topk_n<TOPK_MAX_PER_LANE>(zt, E, k, out_idx, out_z, bias);
+    wave_topk_n<TOPK_MAX_PER_LANE>(zt, E, k, out_idx, out_z, bias, zsrc);
 }
 
 // Mixing weights from the selected logits: sigmoid in double precision,
