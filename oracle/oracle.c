@@ -41,6 +41,7 @@
 #define ORC_IQ2 1
 #define ORC_Q2K 2
 #define ORC_Q8 3
+#define ORC_Q4K 4
 
 /* ---------------------------------------------------------------------- */
 /* scalar decoding of stored numbers                                      */
@@ -266,6 +267,31 @@ static void deq_q2k(const uint8_t* b, double* w) {
   }
 }
 
+/*
+ * Q4K_L block (the 4-bit routed variant: the "ds4f-q4" models of "Running
+ * DeepSeek V4 Flash on an RTX 5080 ...", model section, whose routed Q4_K
+ * layout has the grouped kernels named in its CUDA section), 256 weights in
+ * 144 bytes: fp16 d, fp16 dmin; 8 bytes, one per 32-weight sub-block j,
+ * holding the low 4 bits of the 6-bit scale sc_j (low nibble) and of the
+ * 6-bit min m_j (high nibble); 4 bytes, byte p holding the top two bits of
+ * sc_2p, m_2p, sc_2p+1, m_2p+1 (bit pairs 0-1, 2-3, 4-5, 6-7); 128 bytes of
+ * 4-bit quants (weight i in bits 4(i%2) of byte i/2).
+ * w_i = d * sc_j * q_i - dmin * m_j, j = i / 32.
+ */
+static void deq_q4k(const uint8_t* b, double* w) {
+  double d = orc_half(rd16(b)), dmin = orc_half(rd16(b + 2));
+  for (int j = 0; j < 8; j++) {
+    int top = b[12 + j / 2] >> (4 * (j % 2));
+    int sc = (b[4 + j] & 15) | ((top & 3) << 4);
+    int m = (b[4 + j] >> 4) | (((top >> 2) & 3) << 4);
+    for (int t = 0; t < 32; t++) {
+      int i = 32 * j + t;
+      int q = (b[16 + i / 2] >> (4 * (i % 2))) & 15;
+      w[i] = d * (double)sc * (double)q - dmin * (double)m;
+    }
+  }
+}
+
 /* Q8_0_L block, 32 weights in 34 bytes: fp16 d then int8 q[32]; w = d q. */
 static void deq_q8(const uint8_t* b, double* w) {
   double d = orc_half(rd16(b));
@@ -273,11 +299,13 @@ static void deq_q8(const uint8_t* b, double* w) {
 }
 
 static int block_weights(int fmt) { return fmt == ORC_Q8 ? 32 : 256; }
-static int block_bytes(int fmt) { return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : 34; }
+static int block_bytes(int fmt) {
+  return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : fmt == ORC_Q4K ? 144 : 34;
+}
 
 /* Decode n_blocks consecutive blocks of `fmt` into fp64. Returns 0 on success. */
 int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t* grid, double* out) {
-  if (fmt != ORC_IQ2 && fmt != ORC_Q2K && fmt != ORC_Q8) return -1;
+  if (fmt != ORC_IQ2 && fmt != ORC_Q2K && fmt != ORC_Q8 && fmt != ORC_Q4K) return -1;
   int bw = block_weights(fmt), bb = block_bytes(fmt);
   for (int64_t i = 0; i < n_blocks; i++) {
     const uint8_t* b = blocks + i * bb;
@@ -286,6 +314,8 @@ int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t*
       deq_iq2(b, grid, w);
     else if (fmt == ORC_Q2K)
       deq_q2k(b, w);
+    else if (fmt == ORC_Q4K)
+      deq_q4k(b, w);
     else
       deq_q8(b, w);
   }

@@ -35,9 +35,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8 = 0, 1, 2, 3
-BLOCK_WEIGHTS = {FMT_IQ2: 256, FMT_Q2K: 256, FMT_Q8: 32}
-BLOCK_BYTES = {FMT_IQ2: 66, FMT_Q2K: 84, FMT_Q8: 34}
+FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8, FMT_Q4K = 0, 1, 2, 3, 4
+BLOCK_WEIGHTS = {FMT_IQ2: 256, FMT_Q2K: 256, FMT_Q8: 32, FMT_Q4K: 256}
+BLOCK_BYTES = {FMT_IQ2: 66, FMT_Q2K: 84, FMT_Q8: 34, FMT_Q4K: 144}
 
 F32, BF16 = 0, 1
 
@@ -118,6 +118,26 @@ def pack_q2k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, m: np.ndarray, q: 
     return out
 
 
+def pack_q4k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, m: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Q4K_L blocks.
+
+    d, dmin float16 [nb]; sc, m uint8 [nb, 8] (0..63); q uint8 [nb, 256] (0..15)
+    returns uint8 [nb, 144]
+    """
+    nb = d.shape[0]
+    sc = sc.astype(np.uint8) & 63
+    m = m.astype(np.uint8) & 63
+    out = np.empty((nb, 144), dtype=np.uint8)
+    out[:, 0:2] = np.ascontiguousarray(d.astype("<f2")).view(np.uint8).reshape(nb, 2)
+    out[:, 2:4] = np.ascontiguousarray(dmin.astype("<f2")).view(np.uint8).reshape(nb, 2)
+    out[:, 4:12] = (sc & 15) | ((m & 15) << 4)
+    top = (sc >> 4) | ((m >> 4) << 2)  # 4 bits per sub-block
+    out[:, 12:16] = top[:, 0::2] | (top[:, 1::2] << 4)
+    qq = q.reshape(nb, 128, 2).astype(np.uint8) & 15
+    out[:, 16:144] = qq[:, :, 0] | (qq[:, :, 1] << 4)
+    return out
+
+
 def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
     """Q8_0_L blocks.  d float16 [nb]; q int8 [nb, 32]; returns uint8 [nb, 34]."""
     nb = d.shape[0]
@@ -137,7 +157,9 @@ def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
 #   Q2K: sc, m ~ U{0..15}, q ~ U{0..3}; dmin = 1.5 d centres the weights;
 #        std ~ 14.9 d  ->  d ~ 1.35e-3
 #   Q8 : q ~ U{-128..127}, std ~ 73.9  ->  d ~ 2.7e-4
-IQ2_D, Q2K_D, Q8_D = 2.36e-4, 1.35e-3, 2.7e-4
+#   Q4K: sc, m ~ U{0..63}, q ~ U{0..15}; dmin = 7.5 d centres the weights;
+#        var = var(sc q) + 7.5^2 var(m) = 47532 + 19195 -> std 258 d -> d ~ 7.74e-5
+IQ2_D, Q2K_D, Q8_D, Q4K_D = 2.36e-4, 1.35e-3, 2.7e-4, 7.74e-5
 
 
 def _rand_scale(rng, nb, base):
@@ -174,6 +196,16 @@ def random_q2k(rng: np.random.Generator, nb: int) -> np.ndarray:
     return out
 
 
+def random_q4k(rng: np.random.Generator, nb: int) -> np.ndarray:
+    """Random Q4K_L blocks: uniform 6-bit sub-block scales and mins, 4-bit
+    quants; dmin = 7.5 d centres the weights on zero."""
+    out = _random_blocks(rng, nb, 144)
+    d = _rand_scale(rng, nb, Q4K_D)
+    _put_f16(out, 0, d)
+    _put_f16(out, 2, (d.astype(np.float32) * 7.5).astype(np.float16))
+    return out
+
+
 def random_q8(rng: np.random.Generator, nb: int) -> np.ndarray:
     """Random Q8_0_L blocks: uniform int8 quants in -128..127."""
     out = _random_blocks(rng, nb, 34)
@@ -181,7 +213,7 @@ def random_q8(rng: np.random.Generator, nb: int) -> np.ndarray:
     return out
 
 
-RANDOM_CODES = {FMT_IQ2: random_iq2, FMT_Q2K: random_q2k, FMT_Q8: random_q8}
+RANDOM_CODES = {FMT_IQ2: random_iq2, FMT_Q2K: random_q2k, FMT_Q8: random_q8, FMT_Q4K: random_q4k}
 
 
 def matrix_bytes(fmt: int, n_experts: int, rows: int, K: int) -> int:

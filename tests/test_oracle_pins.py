@@ -77,6 +77,56 @@ def test_q2k_worked_block_and_packer():
     assert np.array_equal(packed.reshape(-1), _bytes(b["hex"]))
 
 
+def test_q4k_worked_block_and_packer():
+    b = _golden()["q4k_blocks"][0]
+    want = np.array(b["subblocks"], dtype=np.float64).reshape(-1)
+    assert np.array_equal(oracle.dequant(oracle.Q4K, _bytes(b["hex"])), want)
+    f = b["fields"]
+    q = np.tile(np.arange(16), 16).reshape(8, 32).astype(np.uint8)
+    q[1], q[2], q[3] = 15, 7, 1
+    packed = synth.pack_q4k(np.array([0.5], np.float16), np.array([0.25], np.float16),
+                            np.array([f["sc"]], np.uint8), np.array([f["m"]], np.uint8), q.reshape(1, 256))
+    assert np.array_equal(packed.reshape(-1), _bytes(b["hex"]))
+
+
+def test_q4k_agrees_with_q2k_where_both_can_hold_the_block():
+    # A Q4K block whose 6-bit scales and mins fit 4 bits and whose quants fit
+    # 2 bits holds the same weights as the Q2K block with those fields (each
+    # 32-weight sub-block as two 16-weight ones): two decoders of different
+    # byte layouts must agree exactly.
+    rng = np.random.default_rng(5)
+    nb = 32
+    d = (rng.uniform(0.5, 2.0, nb) * 1e-3).astype(np.float16)
+    dmin = (rng.uniform(0.5, 2.0, nb) * 1e-3).astype(np.float16)
+    sc = rng.integers(0, 16, (nb, 8)).astype(np.uint8)
+    m = rng.integers(0, 16, (nb, 8)).astype(np.uint8)
+    q = rng.integers(0, 4, (nb, 256)).astype(np.uint8)
+    w4 = oracle.dequant(oracle.Q4K, synth.pack_q4k(d, dmin, sc, m, q))
+    w2 = oracle.dequant(oracle.Q2K, synth.pack_q2k(d, dmin, np.repeat(sc, 2, axis=1), np.repeat(m, 2, axis=1), q))
+    assert np.array_equal(w4, w2)
+    # the top bits: sc + 16 t adds 16 t d q to every weight of the sub-block,
+    # m + 16 t subtracts 16 t dmin
+    for j in range(8):
+        for field in ("sc", "m"):
+            sc2, m2 = sc.copy(), m.copy()
+            (sc2 if field == "sc" else m2)[:, j] += 48
+            w = oracle.dequant(oracle.Q4K, synth.pack_q4k(d, dmin, sc2, m2, q)).reshape(nb, 8, 32)
+            delta = w - w4.reshape(nb, 8, 32)
+            others = [i for i in range(8) if i != j]
+            assert np.all(delta[:, others] == 0)
+            if field == "sc":
+                expect = 48 * d.astype(np.float64)[:, None] * q.reshape(nb, 8, 32)[:, j]
+            else:
+                expect = -48 * np.broadcast_to(dmin.astype(np.float64)[:, None], (nb, 32))
+            assert np.allclose(delta[:, j], expect, rtol=1e-12, atol=0)
+
+
+def test_q4k_random_codes_are_centred_with_the_stated_spread():
+    blocks = synth.random_q4k(np.random.default_rng(6), 4096)
+    w = oracle.dequant(oracle.Q4K, blocks)
+    assert abs(w.mean()) < 2e-4 and 0.017 < w.std() < 0.023
+
+
 def test_q8_worked_blocks():
     g = _golden()["q8_blocks"]
     a = np.array(g[0]["weights"], dtype=np.float64)
