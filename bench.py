@@ -132,6 +132,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bias-gain", action="store_true",
                     help="give every layer a router selection bias and per-channel down gains (not the headline)")
+    ap.add_argument("--routed-fmt", choices=["iq2-q2k", "q4k"], default="iq2-q2k",
+                    help="routed experts: IQ2_XXS-like gate/up + Q2_K-like down (the headline), or Q4_K-like "
+                         "gate/up/down (the 4-bit variant; not the headline)")
     ap.add_argument("--only", choices=["all", "decode", "prefill"], default="all")
     ap.add_argument("--pmc-mode", action="store_true",
                     help="no timing: a few decode and prefill steps and a plain copy of known size, for "
@@ -155,7 +158,15 @@ def main() -> int:
     lib.lib()  # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     spec = synth.DECODE_SPEC
+    if args.routed_fmt == "q4k":
+        spec = synth.scaled_spec(E=spec.E, k=spec.k, d=spec.d, f=spec.f, fmt_gate_up=synth.FMT_Q4K,
+                                 fmt_down=synth.FMT_Q4K)
     E, k, d, f = spec.E, spec.k, spec.d, spec.f
+    FGU, FDN = spec.fmt_gate_up, spec.fmt_down
+    headline = args.routed_fmt == "iq2-q2k" and not args.bias_gain
+
+    def traffic(kernel):  # counters were taken on the headline configuration
+        return measured_traffic(kernel) if headline else None
 
     # ------------------------------------------------------------ layers ----
     t0 = time.time()
@@ -218,8 +229,8 @@ def main() -> int:
     # one token: router + x in the first launch, the routed and the shared
     # gate/up in the second, all down projections in the third
     bytes_k1 = E * d * 4 + d * 4
-    bytes_k2 = k * 2 * lib.matrix_bytes(synth.FMT_IQ2, 1, f, d) + 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d)
-    bytes_k3 = k * lib.matrix_bytes(synth.FMT_Q2K, 1, d, f) + lib.matrix_bytes(synth.FMT_Q8, 1, d, f) + d * 4
+    bytes_k2 = k * 2 * lib.matrix_bytes(FGU, 1, f, d) + 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d)
+    bytes_k3 = k * lib.matrix_bytes(FDN, 1, d, f) + lib.matrix_bytes(synth.FMT_Q8, 1, d, f) + d * 4
     decode_bytes = bytes_k1 + bytes_k2 + bytes_k3
     decode_kernels = {"decode_router": bytes_k1, "decode_gateup": bytes_k2, "decode_down_combine": bytes_k3}
     if args.only in ("all", "decode"):
@@ -274,7 +285,7 @@ def main() -> int:
                           "achieved_GBs": round(nbytes / (avg_us * 1e-6) / 1e9, 1)}
         dominant = max(kern, key=lambda n: kern[n]["avg_us"])
         dk = kern[dominant]
-        traffic = measured_traffic(dominant)
+        dom_traffic = traffic(dominant)
         result["decode"] = {
             "ms_per_step": ms_step,
             "tokens_per_s": 1000.0 / ms_step,
@@ -283,7 +294,7 @@ def main() -> int:
             "kernels": kern,
             "roofline": {"kernel": dominant, "bound": "hbm", "achieved": dk["achieved_GBs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(dk["achieved_GBs"] / HBM_PEAK_GBS, 4),
-                         "traffic": traffic},
+                         "traffic": dom_traffic},
         }
         # cross-check that the graph-replayed steps compute the eager result
         del g
@@ -312,7 +323,7 @@ def main() -> int:
         torch.cuda.synchronize()
         ms_p = ev0.elapsed_time(ev1) / P
         uniq = int(torch.unique(idx).numel())
-        routed_b = uniq * (2 * lib.matrix_bytes(synth.FMT_IQ2, 1, f, d) + lib.matrix_bytes(synth.FMT_Q2K, 1, d, f))
+        routed_b = uniq * (2 * lib.matrix_bytes(FGU, 1, f, d) + lib.matrix_bytes(FDN, 1, d, f))
         shared_b = 2 * lib.matrix_bytes(synth.FMT_Q8, 1, f, d) + lib.matrix_bytes(synth.FMT_Q8, 1, d, f)
         p_bytes = routed_b + shared_b + E * d * 4 + T * d * 2 + T * d * 4
         flops_routed = 2.0 * T * k * 3 * f * d
@@ -326,8 +337,8 @@ def main() -> int:
         prof = lib.profile_collect()
         lib.profile_enable(False)
         lib.profile_reset()
-        gu_b = uniq * 2 * lib.matrix_bytes(synth.FMT_IQ2, 1, f, d) + T * d * 2
-        dn_b = uniq * lib.matrix_bytes(synth.FMT_Q2K, 1, d, f)
+        gu_b = uniq * 2 * lib.matrix_bytes(FGU, 1, f, d) + T * d * 2
+        dn_b = uniq * lib.matrix_bytes(FDN, 1, d, f)
         pk = {}
         for name, (n, ms) in prof.items():
             pk[name] = {"avg_us": round(ms / n * 1000, 2), "launches": n}
@@ -349,7 +360,7 @@ def main() -> int:
             "kernels": pk,
             "roofline": {"kernel": pdom, "bound": "hbm", "achieved": pk[pdom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(pk[pdom]["achieved_GBs"] / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(pdom)},
+                         "traffic": traffic(pdom)},
         }
 
     # ------------------------------------------------------ CPU baseline ----
@@ -389,7 +400,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "decode: one MoE layer, 384 experts, top-6, d=4096, f=2048, shared Q8_0-like "
-                               "expert, IQ2_XXS-like gate/up, Q2_K-like down, T=1 fp32 token",
+                               "expert, " + ("IQ2_XXS-like gate/up, Q2_K-like down" if args.routed_fmt == "iq2-q2k"
+                                             else "Q4_K-like gate/up and down") + ", T=1 fp32 token",
+                   "routed_formats": args.routed_fmt,
                    "layer_descriptors": N_DESC, "routed_copies": 2, "graph_steps": N_DESC,
                    "router_bias_and_down_gains": bool(args.bias_gain)},
         "roofline": dec["roofline"] if dec else None,

@@ -84,6 +84,20 @@
  *   bytes 20..83 2-bit quants: q_i = (byte[20 + i/4] >> (2 (i % 4))) & 3,
  *   w_i = d * sc_j * q_i - dmin * m_j  with j = i / 16.
  *
+ * MOE_FMT_Q4K_L -- 256 weights in 144 bytes (4.5 bits per weight), the
+ *   4-bit routed-expert variant (the "ds4f-q4" models of "Running DeepSeek
+ *   V4 Flash on an RTX 5080 ...", model section, whose routed Q4_K layout
+ *   has the grouped kernels of that page's CUDA section); routed gate/up and
+ *   down only, not the shared expert:
+ *   bytes 0-1 d (fp16), bytes 2-3 dmin (fp16),
+ *   bytes 4..11  one byte per 32-weight sub-block j: low nibble = the low 4
+ *                bits of the 6-bit scale sc_j, high nibble = the low 4 bits
+ *                of the 6-bit min m_j,
+ *   bytes 12..15 byte p (p = 0..3) holds the top two bits of sc_2p (bits
+ *                0-1), m_2p (2-3), sc_2p+1 (4-5) and m_2p+1 (6-7),
+ *   bytes 16..143 4-bit quants: q_i = (byte[16 + i/2] >> (4 (i % 2))) & 15,
+ *   w_i = d * sc_j * q_i - dmin * m_j  with j = i / 32.
+ *
  * MOE_FMT_Q8_0_L -- 32 weights in 34 bytes (8.5 bits per weight):
  *   bytes 0-1 d (fp16), bytes 2..33 int8 q[32];  w_i = d * q_i.
  *
@@ -98,9 +112,12 @@
  *   Q2K_L    : plane DM {fp16 d, fp16 dmin}[R][nb]    (4 R nb bytes), then
  *              plane S  scale bytes[R][nb][16], then
  *              plane Q  quant bytes[R][nb][64]
+ *   Q4K_L    : plane DM {fp16 d, fp16 dmin}[R][nb]    (4 R nb bytes), then
+ *              plane S  scale bytes[R][nb][12], then
+ *              plane Q  quant bytes[R][nb][128]
  *   Q8_0_L   : plane D  fp16 d[R][nb]                 (2 R nb bytes), then
  *              plane Q  int8 q[R][nb][32]
- *   (nb counts 256-weight superblocks for IQ2XXS_L/Q2K_L and 32-weight
+ *   (nb counts 256-weight superblocks for IQ2XXS_L/Q2K_L/Q4K_L and 32-weight
  *   blocks for Q8_0_L.)  Plane offsets follow from R and nb alone.
  * -------------------------------------------------------------------------
  *
@@ -156,6 +173,7 @@ extern "C" {
 #define MOE_FMT_IQ2XXS_L 1
 #define MOE_FMT_Q2K_L 2
 #define MOE_FMT_Q8_0_L 3
+#define MOE_FMT_Q4K_L 4  /* routed experts only */
 
 /* Weight layouts. */
 #define MOE_LAYOUT_CANONICAL 0

@@ -9,17 +9,25 @@
 namespace qmoe {
 
 enum : int { X_F32 = 0, X_BF16 = 1 };
-enum : int { FMT_IQ2 = 1, FMT_Q2K = 2, FMT_Q8 = 3 };
+enum : int { FMT_IQ2 = 1, FMT_Q2K = 2, FMT_Q8 = 3, FMT_Q4K = 4 };
 
 // Weights per block and bytes per block of each format (canonical layout).
 __host__ __device__ constexpr int block_weights(int fmt) { return fmt == FMT_Q8 ? 32 : 256; }
-__host__ __device__ constexpr int block_bytes(int fmt) { return fmt == FMT_IQ2 ? 66 : fmt == FMT_Q2K ? 84 : 34; }
+__host__ __device__ constexpr int block_bytes(int fmt) {
+  return fmt == FMT_IQ2 ? 66 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : 34;
+}
+// Scale bytes per superblock of the two K-quant formats (sub-block scales and mins).
+__host__ __device__ constexpr int kq_scale_bytes(int fmt) { return fmt == FMT_Q4K ? 12 : 16; }
+// Quant bytes per superblock of the two K-quant formats.
+__host__ __device__ constexpr int kq_quant_bytes(int fmt) { return fmt == FMT_Q4K ? 128 : 64; }
 
 // A weight tensor in the device layout: n_experts matrices of `rows` rows by
 // K inputs.  Planes (see include/moe.h):
 //   IQ2: p_scale = fp16 d[R][nb],            p_a = payload[R][nb][64]
 //   Q2K: p_scale = {fp16 d, dmin}[R][nb],    p_a = scale bytes[R][nb][16],
 //        p_b = quants[R][nb][64]
+//   Q4K: p_scale = {fp16 d, dmin}[R][nb],    p_a = scale bytes[R][nb][12],
+//        p_b = quants[R][nb][128]
 //   Q8 : p_scale = fp16 d[R][nb],            p_a = int8 q[R][nb][32]
 struct QMat {
   const uint8_t* p_scale;
@@ -47,6 +55,9 @@ inline QMat make_qmat(const void* base, int fmt, int n_experts, int rows, int K)
   } else if (fmt == FMT_Q2K) {
     m.p_a = b + R * nb * 4;
     m.p_b = b + R * nb * 20;
+  } else if (fmt == FMT_Q4K) {
+    m.p_a = b + R * nb * 4;
+    m.p_b = b + R * nb * 16;
   } else {
     m.p_a = b + R * nb * 2;
     m.p_b = nullptr;

@@ -501,6 +501,10 @@ __device__ __forceinline__ EPlanes expert_planes(const QMat& m, int e) {
     p.scale = m.p_scale + r * 4;
     p.a = m.p_a + r * 16;
     p.b = m.p_b + r * 64;
+  } else if constexpr (FMT == FMT_Q4K) {
+    p.scale = m.p_scale + r * 4;
+    p.a = m.p_a + r * 12;
+    p.b = m.p_b + r * 128;
   } else {
     p.scale = m.p_scale + r * 2;
     p.a = m.p_a + r * 32;
@@ -554,6 +558,35 @@ struct Piece<FMT_Q2K> {  // quants of sub-blocks 4 (pc % 4) .. +3 of superblock 
   }
 };
 
+// Q4K: a piece is 64 inputs, the quants of sub-blocks 2 (pc % 4) and
+// 2 (pc % 4) + 1 of superblock pc / 4 (32 bytes, two 16-byte loads);
+// lo holds their two low-bit scale bytes, hi their top-bit byte.
+template <>
+struct Piece<FMT_Q4K> {
+  uint4 q0, q1;
+  uint32_t lo, hi, dm;
+  template <int NB>
+  __device__ __forceinline__ void load(const EPlanes& p, uint32_t row, uint32_t pc) {
+    const uint8_t* b = p.b + (row * NB * 128 + pc * 32);
+    q0 = ld16_stream(b);
+    q1 = ld16_stream(b + 16);
+  }
+  __device__ __forceinline__ void scale_bytes(const uint8_t* sb, uint32_t pc) {  // sb: the superblock's 12 bytes
+    lo = *reinterpret_cast<const uint16_t*>(sb + 2 * (pc % 4));
+    hi = sb[8 + pc % 4];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_global(const EPlanes& p, uint32_t row, uint32_t pc) {
+    scale_bytes(p.a + (row * NB + pc / 4) * 12, pc);
+    dm = reinterpret_cast<const uint32_t*>(p.scale)[row * NB + pc / 4];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_lds(const uint8_t* rp, uint32_t pc) {  // row: dm[NB] then sc[NB][12]
+    dm = reinterpret_cast<const uint32_t*>(rp)[pc / 4];
+    scale_bytes(rp + NB * 4 + (pc / 4) * 12, pc);
+  }
+};
+
 template <>
 struct Piece<FMT_Q8> {  // 16 int8 quants: half of block pc / 2
   uint4 q;
@@ -576,8 +609,9 @@ struct Piece<FMT_Q8> {  // 16 int8 quants: half of block pc / 2
 template <int FMT, int K>
 struct RowScales {
   static constexpr int NB = K / block_weights(FMT);
-  static constexpr int DM = FMT == FMT_Q2K ? NB * 4 : 0;                // Q2K (d, dmin) pairs
-  static constexpr int BYTES = FMT == FMT_Q2K ? NB * 20 : NB * 2;       // + Q2K sub-block scales
+  static constexpr bool KQ = FMT == FMT_Q2K || FMT == FMT_Q4K;
+  static constexpr int DM = KQ ? NB * 4 : 0;                                  // K-quant (d, dmin) pairs
+  static constexpr int BYTES = KQ ? NB * (4 + kq_scale_bytes(FMT)) : NB * 2;  // + sub-block scales
   static constexpr bool STAGE = (BYTES % 16) == 0 && (DM % 16) == 0;    // whole 16-byte chunks
 };
 
@@ -608,8 +642,9 @@ struct ScaleStage {
       uint32_t row;
       rowsrc(m, j, P, row);
       const uint8_t* src;
-      if constexpr (FMT == FMT_Q2K) {
-        src = cq * 16 < RS::DM ? P.scale + row * RS::DM + cq * 16 : P.a + row * (RS::NB * 16) + (cq * 16 - RS::DM);
+      if constexpr (RS::KQ) {
+        src = cq * 16 < RS::DM ? P.scale + row * RS::DM + cq * 16
+                               : P.a + row * (RS::NB * kq_scale_bytes(FMT)) + (cq * 16 - RS::DM);
       } else {
         src = P.scale + row * RS::BYTES + cq * 16;
       }
@@ -722,6 +757,44 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q2K>& w, const ActNib
     } else {
       im += sc * D;
       in += m * a.Ai[k][u];
+    }
+  }
+  const float d = half_bits_to_float(w.dm & 0xffffu), dmin = half_bits_to_float(w.dm >> 16);
+  if constexpr (PER16)
+    return fm * d - fn * dmin;
+  else
+    return a.s[k][0] * ((float)im * d - (float)in * dmin);
+}
+
+// Q4K: the 4-bit quants q meet the signed digit planes as q - 8 (q ^ 8 read
+// as a signed nibble); sum q x = sum (q - 8) x + 8 sum x.  A group's sum
+// stays within 15 * 0x7777 * 16 < 2^23, so the 6-bit scale multiplies with
+// a 24-bit integer multiply.
+template <int CPL, bool PER16>
+__device__ __forceinline__ float piece_dot(const Piece<FMT_Q4K>& w, const ActNib<CPL, PER16>& a, int k,
+                                           const Iq2Tab*) {
+  const uint32_t W[8] = {w.q0.x, w.q0.y, w.q0.z, w.q0.w, w.q1.x, w.q1.y, w.q1.z, w.q1.w};
+  int im = 0, in = 0;
+  float fm = 0.0f, fn = 0.0f;
+#pragma unroll
+  for (int sb = 0; sb < 2; sb++) {
+    const int sc = (int)(((w.lo >> (8 * sb)) & 15u) | (((w.hi >> (4 * sb)) & 3u) << 4));
+    const int m = (int)(((w.lo >> (8 * sb + 4)) & 15u) | (((w.hi >> (4 * sb + 2)) & 3u) << 4));
+#pragma unroll
+    for (int g = 0; g < 2; g++) {
+      const int u = 2 * sb + g;
+      const uint32_t N0 = W[2 * u] ^ 0x88888888u, N1 = W[2 * u + 1] ^ 0x88888888u;
+      int acc[4];
+#pragma unroll
+      for (int p = 0; p < 4; p++) acc[p] = dot8(N1, a.w[k][u][1][p], dot8_0(N0, a.w[k][u][0][p]));
+      const int D = lshl_add<3>(a.Ai[k][u], combine4(acc));
+      if constexpr (PER16) {
+        fm += (float)__mul24(sc, D) * a.s[k][u];
+        fn += (float)m * a.As[k][u];
+      } else {
+        im += __mul24(sc, D);
+        in += m * a.Ai[k][u];
+      }
     }
   }
   const float d = half_bits_to_float(w.dm & 0xffffu), dmin = half_bits_to_float(w.dm >> 16);

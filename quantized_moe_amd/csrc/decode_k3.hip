@@ -23,7 +23,11 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
                                           const float* hf, const float* gain, const Iq2Tab* tab, uint8_t* my_scales,
                                           float* out) {
   constexpr int NS = DownRows<FMT, K, ROWS, 1>::NS;
-  DownRows<FMT, K, ROWS, (NS < 3 ? NS : 3)> dr;  // three steps of loads kept in flight ahead of the compute
+  // three steps of loads kept in flight ahead of the compute; Q4K's pieces
+  // are twice as large (two steps, one for rows of more than 64 pieces)
+  constexpr int CPL = Geo<FMT, K>::CPL;
+  constexpr int PDMAX = FMT == FMT_Q4K ? (CPL > 1 ? 1 : 2) : 3;
+  DownRows<FMT, K, ROWS, (NS < PDMAX ? NS : PDMAX)> dr;
   if (hq) {
     dr.load_act(hq, hs);
     dr.issue(m, e, E, r0, my_scales, gain);
@@ -41,11 +45,12 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
 // expert (whose h slice is quantized from 64 fp32 values per piece), need
 // more registers per wave: 8 waves, one task per routed expert and two for
 // the shared expert.
-constexpr int k3_waves(int FS, int F) { return F <= 2048 && FS == FMT_Q8 ? 16 : 8; }
+// (Q4K routed rows, with twice the code registers per piece, take 8 waves.)
+constexpr int k3_waves(int FR, int FS, int F) { return F <= 2048 && FS == FMT_Q8 && FR != FMT_Q4K ? 16 : 8; }
 
 template <int FR, int FS, int F>
-__global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) {
-  constexpr int K3_WAVES = k3_waves(FS, F);
+__global__ __launch_bounds__(64 * k3_waves(FR, FS, F)) void k3_kernel(DecodeArgs a) {
+  constexpr int K3_WAVES = k3_waves(FR, FS, F);
   constexpr int RT_PARTS = K3_WAVES / 8;
   constexpr int SH_PARTS = K3_WAVES / 4;  // the shared expert's 16 rows as tasks of 4 (16 waves) or 8
   __shared__ Iq2Tab itab;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(64 * k3_waves(FS, F)) void k3_kernel(DecodeArgs a) 
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(FS, F)), 0, s, a);
+  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(FR, FS, F)), 0, s, a);
   return hipGetLastError();
 }
 
@@ -108,6 +113,7 @@ static hipError_t run_k3_f(const DecodeArgs& a, int fr, int fs, hipStream_t s) {
   switch (fr) {
     case FMT_IQ2: K3_FS(FMT_IQ2)
     case FMT_Q2K: K3_FS(FMT_Q2K)
+    case FMT_Q4K: K3_FS(FMT_Q4K)
     default: K3_FS(FMT_Q8)
   }
 #undef K3_FS

@@ -209,6 +209,27 @@ struct BRegs<FMT_Q2K, KS> {
   }
 };
 
+// Q4K: quants of sub-block 2*g4 + h (16 bytes, KS = 2) or of sub-blocks
+// 2*g4, 2*g4 + 1 (32 bytes); the superblock's 12 scale bytes come with one
+// 12-byte load, of which the lane keeps its two low-bit bytes and its
+// top-bit byte.
+template <int KS>
+struct BRegs<FMT_Q4K, KS> {
+  uint4 q[3 - KS];
+  uint32_t lo, hi;
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
+    const int64_t blk0 = row0 * m.nb + sb;
+    const uint32_t lb = (uint32_t)(lrow * m.nb);
+    const uint8_t* qp = m.p_b + blk0 * 128 + (lb * 128 + 32 * g4 + (KS == 2 ? 16 * h : 0));
+#pragma unroll
+    for (int i = 0; i < 3 - KS; i++) q[i] = *reinterpret_cast<const uint4*>(qp + 16 * i);
+    const uint3 v = *reinterpret_cast<const uint3*>(m.p_a + blk0 * 12 + lb * 12);
+    const uint32_t wlo = (g4 >> 1) ? v.y : v.x;
+    lo = (g4 & 1) ? wlo >> 16 : wlo & 0xffffu;
+    hi = (v.z >> (8 * g4)) & 255u;
+  }
+};
+
 template <int KS>
 struct BRegs<FMT_Q8, KS> {
   uint4 q[2 * (3 - KS)];  // quants of block 2*g4 + h (32 bytes), or of blocks 2*g4, 2*g4 + 1 (64 bytes)
@@ -233,7 +254,8 @@ struct BRegs<FMT_Q8, KS> {
 // 32-input block and stay with the codes.)
 template <int FMT, int PD>
 struct SGroup {
-  static constexpr int NW = FMT == FMT_IQ2 ? (PD + 1) / 2 : FMT == FMT_Q2K ? PD : 1;
+  static constexpr bool KQ = FMT == FMT_Q2K || FMT == FMT_Q4K;  // (d, dmin) pairs
+  static constexpr int NW = FMT == FMT_IQ2 ? (PD + 1) / 2 : KQ ? PD : 1;
   uint32_t w[NW];
   __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb0) {
     if constexpr (FMT == FMT_IQ2) {
@@ -245,7 +267,7 @@ struct SGroup {
         w[0] = v.x;
         w[1] = v.y;
       }
-    } else if constexpr (FMT == FMT_Q2K) {
+    } else if constexpr (KQ) {
       const uint8_t* p = m.p_scale + ((row0 + lrow) * m.nb + sb0) * 4;
       if constexpr (PD == 1) w[0] = *reinterpret_cast<const uint32_t*>(p);
       if constexpr (PD == 2) {
@@ -265,7 +287,7 @@ struct SGroup {
   // scale word of superblock sb0 + u (u a compile-time constant)
   __device__ __forceinline__ uint32_t word(int u) const {
     if constexpr (FMT == FMT_IQ2) return (w[u >> 1] >> (16 * (u & 1))) & 0xffffu;
-    if constexpr (FMT == FMT_Q2K) return w[u];
+    if constexpr (KQ) return w[u];
     return 0u;
   }
 };
@@ -297,13 +319,48 @@ __device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K, KS>& b, int hh, i
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// Q2K min-term B fragment (K = the 16 sub-blocks): m_j for j = 4*g4 .. +3,
-// which are exactly the high nibbles of this lane's scale word.
+// Q2K min-term B fragment (K = the 16 sub-blocks): 16 m_j for j = 4*g4 .. +3,
+// m_j being the high nibbles of this lane's scale word.
 template <int KS>
 __device__ __forceinline__ uint2 q2k_min_frag(const BRegs<FMT_Q2K, KS>& b) {
   const uint32_t w = b.sc;
   const uint32_t m0 = (w >> 4) & 15u, m1 = (w >> 12) & 15u, m2 = (w >> 20) & 15u, m3 = (w >> 28) & 15u;
-  return make_uint2(to_h((float)m0) | (to_h((float)m1) << 16), to_h((float)m2) | (to_h((float)m3) << 16));
+  // 16 m: the sums of A are stored divided by 16
+  return make_uint2(to_h((float)(16u * m0)) | (to_h((float)(16u * m1)) << 16),
+                    to_h((float)(16u * m2)) | (to_h((float)(16u * m3)) << 16));
+}
+
+// Q4K: 6-bit scale and min of the lane's sub-block sbl (0 or 1 of its pair).
+template <int KS>
+__device__ __forceinline__ uint32_t q4k_sc(const BRegs<FMT_Q4K, KS>& b, int sbl) {
+  return ((b.lo >> (8 * sbl)) & 15u) | (((b.hi >> (4 * sbl)) & 3u) << 4);
+}
+template <int KS>
+__device__ __forceinline__ uint32_t q4k_min(const BRegs<FMT_Q4K, KS>& b, int sbl) {
+  return ((b.lo >> (8 * sbl + 4)) & 15u) | (((b.hi >> (4 * sbl + 2)) & 3u) << 4);
+}
+
+// Q4K fragment of local step i: the 8 exact integers sc * q of quant word w
+// (elements 2j, 2j+1 in the low and high nibble of byte j).  Byte j goes to
+// bytes 0 and 2 under fp16 exponent bytes 0x64 (one v_perm); masking keeps
+// the low nibble in the first half (1024 + q) and the high nibble, four bits
+// up, in the second (1024 + 16 q); one packed fused multiply-add with
+// (sc, sc / 16) and (-1024 sc, -64 sc) leaves sc * q <= 945, exact in fp16.
+__device__ __forceinline__ uint4 q4k_frag(uint32_t w, f16x2_t mul, f16x2_t add) {
+  auto pair = [&](uint32_t sel) {
+    const uint32_t t = __builtin_amdgcn_perm(w, 0x64646464u, sel) & 0xfff0ff0fu;
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t), mul, add));
+  };
+  return make_uint4(pair(0x00040004u), pair(0x00050005u), pair(0x00060006u), pair(0x00070007u));
+}
+
+// Q4K min-term B fragment (K = the 16 groups of 16 inputs): group j belongs
+// to sub-block j / 2, so lane group g4 gives 16 m of sub-blocks 2*g4, 2*g4,
+// 2*g4 + 1, 2*g4 + 1.
+template <int KS>
+__device__ __forceinline__ uint2 q4k_min_frag(const BRegs<FMT_Q4K, KS>& b) {
+  const uint32_t m0 = to_h((float)(16u * q4k_min(b, 0))), m1 = to_h((float)(16u * q4k_min(b, 1)));  // (sums / 16)
+  return make_uint2(m0 | (m0 << 16), m1 | (m1 << 16));
 }
 
 // Q8 fragment of local step i: the 8 products d*q as fp16, each rounded once.
@@ -333,7 +390,7 @@ struct GemmLds {
   static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
   static constexpr int kTqs = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
-  static constexpr int kS = FMT == FMT_Q2K ? 2 * 2 * BM * 16 * 2 : 0;  // Q2K sub-block sums: [buf][hi/lo][BM][16]
+  static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
   static constexpr int kTok = GATEUP ? 3 * BM * 8 : 0;                // token and scale of each row, 3 items
   static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
   static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oA = oTqs + kTqs, oS = oA + kA, oTok = oS + kS,
@@ -509,8 +566,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   auto store_piece = [&](int buf, const uint4& v, int pos) {
     uint8_t* dst = sA + buf * A_BUF;
     if (pos >= 0) *reinterpret_cast<uint4*>(dst + pos) = v;
-    if constexpr (FMT == FMT_Q2K) {
-      // sub-block sums (16 inputs = pieces 2j, 2j+1, held by lanes t, t^1)
+    if constexpr (FMT == FMT_Q2K || FMT == FMT_Q4K) {
+      // sums of 16 inputs (pieces 2j, 2j+1, held by lanes t, t^1): Q2K's
+      // sub-blocks, halves of Q4K's
       const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
       float sum = 0.0f;
       sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, v.x), one, sum, false);
@@ -520,7 +578,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       if (pos < 0) sum = 0.0f;
       const float o = __shfl_xor(sum, 1, 64);
       if (pos >= 0 && (a_piece & 1) == 0) {
-        const float t = sum + o;
+        // stored / 16 (exact): scaled gate/up rows reach |a| < 2^14, and a
+        // sum of 16 of them would pass the fp16 range; the min fragments
+        // carry the factor 16 back (16 m <= 1008, exact)
+        const float t = (sum + o) * 0.0625f;
         const uint32_t hs = to_h(t);
         uint16_t* ss = sS + buf * (2 * BM * 16);
         ss[a_row * 16 + (a_piece >> 1)] = (uint16_t)hs;
@@ -595,9 +656,19 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 3 - KS; hh++) {  // halves of the lane's slice (one for KS = 2)
         uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
+        f16x2_t mul0 = {}, add0 = {}, mul1 = {}, add1 = {};
         if constexpr (FMT == FMT_IQ2) {
           S0 = iq2_scale16(B0.w[2 * hh + 1]);
           if constexpr (GATEUP) S1 = iq2_scale16(B1.w[2 * hh + 1]);
+        } else if constexpr (FMT == FMT_Q4K) {
+          const int sbl = KS == 2 ? h : hh;  // the lane's sub-block 2*g4 + sbl
+          auto consts = [&](uint32_t sc, f16x2_t& mul, f16x2_t& add) {
+            const float f = (float)sc;
+            mul = f16x2_t{(_Float16)f, (_Float16)(f * 0.0625f)};
+            add = f16x2_t{(_Float16)(-1024.0f * f), (_Float16)(-64.0f * f)};
+          };
+          consts(q4k_sc(B0, sbl), mul0, add0);
+          if constexpr (GATEUP) consts(q4k_sc(B1, sbl), mul1, add1);
         } else {
           const int hs = KS == 2 ? h : hh;  // scale bytes of sub-blocks 4*g4 + 2hs, + 1
           sc0 = B0.sc >> (16 * hs);
@@ -609,6 +680,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
           if constexpr (FMT == FMT_IQ2) {
             f0 = iq2_frag(B0, hh, i, S0, CB, tm, sgn);
             if constexpr (GATEUP) f1 = iq2_frag(B1, hh, i, S1, CB, tm, sgn);
+          } else if constexpr (FMT == FMT_Q4K) {
+            f0 = q4k_frag(word_of(B0.q[KS == 2 ? 0 : hh], i), mul0, add0);
+            if constexpr (GATEUP) f1 = q4k_frag(word_of(B1.q[KS == 2 ? 0 : hh], i), mul1, add1);
           } else {
             // low nibble of scale byte i/2, as sc << 16
             const int sh = 16 - 8 * (i >> 1);
@@ -647,9 +721,14 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
           if constexpr (GATEUP) acc1[m] += dd1 * s1[m];
         }
         if (h == 0) {
-          const uint2 mf0 = q2k_min_frag(B0);
-          uint2 mf1;
-          if constexpr (GATEUP) mf1 = q2k_min_frag(B1);
+          uint2 mf0, mf1;
+          if constexpr (FMT == FMT_Q4K) {
+            mf0 = q4k_min_frag(B0);
+            if constexpr (GATEUP) mf1 = q4k_min_frag(B1);
+          } else {
+            mf0 = q2k_min_frag(B0);
+            if constexpr (GATEUP) mf1 = q2k_min_frag(B1);
+          }
           const uint16_t* ss = sS + buf * (2 * BM * 16);
 #pragma unroll
           for (int m = 0; m < NM; m++) {
@@ -885,14 +964,24 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   // loads).  Superblocks kept in flight (PD) per wave, at 128 VGPRs per wave
   // (16 waves per CU).
   if constexpr (FMT != FMT_Q8) {
-    if constexpr (!GATEUP) {
+    if constexpr (!GATEUP && FMT != FMT_Q4K) {
       if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
     }
-    // (two Q2K matrices hold more registers per superblock than two IQ2 ones)
-    if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
-      if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+    // (two Q2K or Q4K matrices hold more registers per superblock than two
+    // IQ2 ones; one Q4K superblock holds twice the quant registers)
+    if constexpr (FMT == FMT_Q4K) {
+      if constexpr (GATEUP) {  // the two waves of a pair split each superblock (as Q8 gate/up; deeper spills)
+        return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+      } else {
+        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+      }
+    } else {
+      if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
+        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+      }
+      return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
     }
-    return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
   } else {
     // Q8: whole superblocks for the one-matrix down GEMM; the two-matrix
     // gate/up keeps the pair split (whole superblocks of two matrices spill)
@@ -909,6 +998,7 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   switch (fmt) {                                                       \
     case FMT_IQ2: { constexpr int F = FMT_IQ2; __VA_ARGS__; } break;   \
     case FMT_Q2K: { constexpr int F = FMT_Q2K; __VA_ARGS__; } break;   \
+    case FMT_Q4K: { constexpr int F = FMT_Q4K; __VA_ARGS__; } break;   \
     default: { constexpr int F = FMT_Q8; __VA_ARGS__; } break;         \
   }
 

@@ -27,6 +27,11 @@ __global__ void repack_kernel(int fmt, int64_t n_blocks, const uint8_t* __restri
     seg_off[0] = 0; seg_len[0] = 4;
     seg_off[1] = 4; seg_len[1] = 16;
     seg_off[2] = 20; seg_len[2] = 64;
+  } else if (fmt == FMT_Q4K) {
+    nseg = 3;
+    seg_off[0] = 0; seg_len[0] = 4;
+    seg_off[1] = 4; seg_len[1] = 12;
+    seg_off[2] = 16; seg_len[2] = 128;
   } else {
     nseg = 2;
     seg_off[0] = 0; seg_len[0] = 2;

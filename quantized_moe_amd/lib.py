@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 MOE_ABI_VERSION = 2
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_FMT_NONE, MOE_FMT_IQ2XXS_L, MOE_FMT_Q2K_L, MOE_FMT_Q8_0_L = 0, 1, 2, 3
+MOE_FMT_NONE, MOE_FMT_IQ2XXS_L, MOE_FMT_Q2K_L, MOE_FMT_Q8_0_L, MOE_FMT_Q4K_L = 0, 1, 2, 3, 4
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_DEVICE = 0, 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_LAYER = 0, 1, 2, 3
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2

@@ -95,6 +95,15 @@ FORMAT_CASES = [
     (16, 4, 256, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 1, synth.F32),
     (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 1, synth.F32),  # several row pairs per wave
     (8, 1, 8192, 256, synth.FMT_IQ2, synth.FMT_Q2K, None, 1, synth.F32),
+    # Q4K routed experts (the 4-bit variant), decode and prefill
+    (16, 4, 256, 512, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 1, synth.F32),
+    (16, 4, 256, 512, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 3, synth.F32),
+    (16, 4, 256, 512, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 37, synth.BF16),
+    (12, 3, 512, 1024, synth.FMT_IQ2, synth.FMT_Q4K, synth.FMT_Q2K, 1, synth.F32),
+    (12, 3, 1024, 512, synth.FMT_Q4K, synth.FMT_Q2K, synth.FMT_IQ2, 6, synth.BF16),
+    (10, 3, 2048, 1024, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 70, synth.BF16),
+    (8, 2, 256, 8192, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 2, synth.F32),   # two pieces per lane (f)
+    (8, 1, 8192, 256, synth.FMT_Q4K, synth.FMT_Q4K, None, 2, synth.F32),           # two pieces per lane (d)
 ]
 
 
@@ -114,6 +123,23 @@ def test_layer_formats_and_shapes(case):
         assert np.array_equal(idx, idx_ref), path
         assert np.max(np.abs(wt - wt_ref)) <= WT_TOL, path
         assert rel_l2(y, y_ref) <= REL_L2, (path, rel_l2(y, y_ref))
+
+
+@pytest.mark.parametrize("fgu", [synth.FMT_Q2K, synth.FMT_Q4K])
+def test_prefill_min_term_with_same_sign_rows(fgu):
+    """K-quant gate/up in prefill on rows of one sign and similar magnitude:
+    the per-16-input sums of the scaled rows (|a| < 2^14) exceed the fp16
+    range unless stored scaled (regression: NaN outputs)."""
+    spec = synth.scaled_spec(E=8, k=2, d=1024, f=512, fmt_gate_up=fgu, fmt_down=synth.FMT_Q2K)
+    L = synth.random_layer(spec, seed=9, workload="minterm")
+    T = 24
+    x = (1.0 + 0.1 * np.abs(synth.activations(9, ("minterm", "x"), T, 1024, synth.F32))).astype(np.float32)
+    x[1::2] *= -1.0
+    y, idx, wt = run_layer(lib.DeviceLayer.from_synth(L, DEV), x, synth.F32, lib.MOE_PATH_PREFILL)
+    y_ref, idx_ref, _ = oracle.layer_forward(L, x, synth.F32)
+    assert np.array_equal(idx, idx_ref)
+    assert np.all(np.isfinite(y))
+    assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
 
 
 # ------------------------------------------ selection bias, down gains ----
@@ -263,6 +289,33 @@ def test_prefill_chunk_full_layer(decode_layer):
     assert rel_l2(y[tok], y_ref) <= REL_L2, rel_l2(y[tok], y_ref)
 
 
+def test_q4k_layer_full_size_decode_and_prefill():
+    """The decode workload's shape with Q4K routed gate/up/down (the 4-bit
+    variant): one-token decode on three tokens, and a 1024-token bf16 chunk
+    with routes bit-exact and outputs on sampled tokens."""
+    spec = synth.scaled_spec(E=384, k=6, d=4096, f=2048, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q4K)
+    L = synth.random_layer(spec, seed=3, workload="q4k")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    try:
+        for i in range(3):
+            x = synth.activations(3, ("q4k", "x", i), 1, 4096, synth.F32)
+            y, idx, wt = run_layer(dl, x, synth.F32, lib.MOE_PATH_AUTO)
+            y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+            assert np.array_equal(idx, idx_ref)
+            assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
+        T = 1024
+        x = synth.activations(3, ("q4k", "prefill"), T, 4096, synth.BF16)
+        y, idx, wt = run_layer(dl, x, synth.BF16, lib.MOE_PATH_AUTO)
+        _, idx_ref, wt_ref = oracle.route(x, oracle.BF16, L.w_router, 6)
+        assert np.array_equal(idx, idx_ref)
+        tok = np.array([0, 1, 511, 512, 1022, 1023] + list(range(100, 900, 100)))
+        y_ref = oracle.ffn(L, x, oracle.BF16, idx_ref, wt_ref, tokens=tok)
+        assert rel_l2(y[tok], y_ref) <= REL_L2, rel_l2(y[tok], y_ref)
+    finally:
+        del dl
+        torch.cuda.empty_cache()
+
+
 def test_small_batch_both_paths(decode_layer):
     """16 tokens of 4 interleaved sessions with expert reuse, fp32, caller routes."""
     L, dl = decode_layer
@@ -326,7 +379,7 @@ def test_repack_round_trip(decode_layer):
         assert np.array_equal(back.cpu().numpy(), canon), name
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8])
+@pytest.mark.parametrize("fmt", [synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_Q4K])
 def test_repack_round_trip_all_widths(fmt):
     """Canonical -> device -> canonical is the identity for every row width,
     including the Q2K scale plane's partial superblock groups (1 or 2
@@ -334,7 +387,7 @@ def test_repack_round_trip_all_widths(fmt):
     rng = np.random.default_rng(fmt)
     for K in (256, 512, 1024, 2048, 8192):
         E, rows = 3, 5
-        n = E * rows * (K // (32 if fmt == synth.FMT_Q8 else 256)) * {1: 66, 2: 84, 3: 34}[fmt]
+        n = E * rows * (K // (32 if fmt == synth.FMT_Q8 else 256)) * {1: 66, 2: 84, 3: 34, 4: 144}[fmt]
         canon = rng.integers(0, 256, n, dtype=np.uint8)
         src = torch.from_numpy(canon).to(DEV)
         dev_buf = torch.empty_like(src)
