@@ -27,7 +27,6 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   __shared__ float s_zs[TOPK_MAX_K];
   using G = Geo<FMT, D>;
   constexpr int RPW = 2 * GCNT;  // h rows per wave
-  constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
   // One step of codes in flight ahead of the compute: the rows are bound by
   // the decode arithmetic once streaming, and a deeper start (every wave of
   // the GPU requesting several steps at the barrier) delays every wave's

@@ -171,9 +171,12 @@ def test_route_topk_with_bias():
             assert not np.array_equal(oracle.route(x, dt, L.w_router, spec.k)[1], idx_ref)
 
 
-@pytest.mark.parametrize("T,dt", [(1, synth.F32), (3, synth.F32), (37, synth.BF16)])
-def test_layer_with_bias_and_gains(T, dt):
-    spec = synth.scaled_spec(E=24, k=4, d=512, f=512)
+@pytest.mark.parametrize("T,dt,fmt", [(1, synth.F32, synth.FMT_IQ2), (3, synth.F32, synth.FMT_IQ2),
+                                      (37, synth.BF16, synth.FMT_IQ2), (1, synth.F32, synth.FMT_Q4K),
+                                      (8, synth.F32, synth.FMT_Q4K), (45, synth.BF16, synth.FMT_Q4K)])
+def test_layer_with_bias_and_gains(T, dt, fmt):
+    fdn = synth.FMT_Q2K if fmt == synth.FMT_IQ2 else synth.FMT_Q4K
+    spec = synth.scaled_spec(E=24, k=4, d=512, f=512, fmt_gate_up=fmt, fmt_down=fdn)
     L = _bias_gain_layer(spec, 32)
     dl = lib.DeviceLayer.from_synth(L, DEV)
     x = synth.activations(32, ("bias", "layer", T), T, spec.d, dt)
