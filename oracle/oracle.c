@@ -8,16 +8,19 @@
  *
  * What is computed, step by step:
  *   router logits  fp32, in the fixed order given at orc_logit()
- *   selection      exact top-k on the logits, ties to the lower index
+ *   selection      exact top-k on the logits, ties to the lower index (with
+ *                  a router bias: on the keys sigmoid32(z) + b, orc_bias_keys)
  *   mixing weights sigmoid of the chosen logits, normalised to sum one (fp64)
  *   bucketing      stable counting sort of the flat routes by expert
  *   dequantisation every weight exactly, in fp64
  *   expert FFN     h = silu(G x) * (U x), ye = D h, all in fp64
- *   combine        y = sum_j wt_j * ye_j + shared(x), fp64, rounded to fp32
+ *   combine        y = sum_j wt_j * (g_e * ye_j) + shared(x), fp64, rounded
+ *                  to fp32 (g_e the optional per-channel down gains, else 1)
  *
  * Sources: the layer's sum y = sum_k rw_k * ye_k + ysh with ye taken before
  * the routing weight is the per-layer MoE sum on "YoungAi -- DeepSeek V4.1
- * Flash on one DGX Spark", section 4.2 (sidecar gains set to one).  384
+ * Flash on one DGX Spark", section 4.2, with the sidecar's per-channel down
+ * gains and selection-only router bias optional (same section).  384
  * experts with 6 chosen per token: same page, section 2.2.  The format mix
  * (IQ2_XXS-like gate/up, Q2_K-like down, Q8 shared expert, unquantized
  * router): "Running DeepSeek V4 Flash on an RTX 5080 with 16GB VRAM Under
