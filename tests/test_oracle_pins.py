@@ -510,6 +510,7 @@ def _numpy_ffn(L, x, idx, wt):
     synth.scaled_spec(E=6, k=3, d=512, f=256),                       # IQ2 gate/up, Q2K down, Q8 shared
     synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_IQ2,
                       fmt_shared=synth.FMT_Q2K),
+    synth.scaled_spec(E=5, k=2, d=512, f=256, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q4K),
 ])
 def test_ffn_matches_numpy_dense_matmul(spec):
     L = synth.random_layer(spec, seed=3, workload="pin")
