@@ -54,6 +54,8 @@ def lib():
         L.orc_bucket.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_dequant.argtypes, L.orc_dequant.restype = [I, P, I64, P, P], I
         L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I, P, P, P, P, P, I, I, P, I, P, P, P]
+        L.orc_ffn_grouped.argtypes = L.orc_ffn.argtypes
+        L.orc_ffn_grouped.restype = I
         L.orc_sigmoid32.argtypes, L.orc_sigmoid32.restype = [ctypes.c_float], ctypes.c_float
         L.orc_bias_keys.argtypes = [P, I, I, P, P]
         L.orc_ffn.restype = I
@@ -162,10 +164,12 @@ def dequant(fmt, blocks, grid=None) -> np.ndarray:
     return out
 
 
-def ffn(layer, x, x_dtype, idx, wt, tokens=None) -> np.ndarray:
+def ffn(layer, x, x_dtype, idx, wt, tokens=None, grouped=False) -> np.ndarray:
     """Expert FFN + shared expert for the listed tokens (all if None).
 
     layer: a synth.Layer (canonical bytes).  Returns y [len(tokens), d] fp32.
+    grouped: evaluate expert by expert (orc_ffn_grouped: each expert
+    dequantised once, results bitwise those of the token-by-token loop).
     """
     s = layer.spec
     x = _x(x, x_dtype)
@@ -179,13 +183,16 @@ def ffn(layer, x, x_dtype, idx, wt, tokens=None) -> np.ndarray:
     k = idx.shape[1]  # routes per token as given (may differ from the layer's top_k)
     dg = getattr(layer, "down_gain", None)
     gain = None if dg is None else _c(dg, np.float32)
-    rc = lib().orc_ffn(s.E, s.d, s.f, k, s.fmt_gate_up, s.fmt_down, _p(_c(layer.w_gate, np.uint8)),
+    fn = lib().orc_ffn_grouped if grouped else lib().orc_ffn
+    rc = fn(s.E, s.d, s.f, k, s.fmt_gate_up, s.fmt_down, _p(_c(layer.w_gate, np.uint8)),
                        _p(_c(layer.w_up, np.uint8)), _p(_c(layer.w_down, np.uint8)), _p(_c(layer.grid, np.uint8)),
                        int(sh), s.fmt_shared if sh else 0,
                        _p(_c(layer.s_gate, np.uint8)) if sh else None,
                        _p(_c(layer.s_up, np.uint8)) if sh else None,
                        _p(_c(layer.s_down, np.uint8)) if sh else None,
                        _p(gain), _p(x), x_dtype, T, _p(tok), n_tok, _p(idx), _p(wt), _p(y))
+    if rc == -2:
+        raise MemoryError("oracle ffn: out of host memory")
     if rc != 0:
         raise ValueError("oracle ffn: token or expert index out of range")
     return y

@@ -431,6 +431,124 @@ int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w
   return status;
 }
 
+/*
+ * The same function as orc_ffn, with the loops over tokens and experts
+ * interchanged: every expert that a listed token routes to is dequantised
+ * once, then each of its (token, rank) pairs is evaluated with exactly the
+ * operations orc_ffn performs for it (fp64 dot products in increasing input
+ * order, the SwiGLU, the down projection), and the results are combined per
+ * token in rank order, then the shared expert, as orc_ffn does.  Every output
+ * is therefore bitwise the same as orc_ffn's; only the number of
+ * dequantisations changes (once per expert instead of once per token and
+ * route), which makes hundreds of tokens of a full-size layer affordable.
+ */
+static void matvec_deq(const double* W, int rows, int K, const double* v, double* out) {
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < rows; n++) {
+    const double* w = W + (int64_t)n * K;
+    double acc = 0.0;
+    for (int i = 0; i < K; i++) acc += w[i] * v[i];
+    out[n] = acc;
+  }
+}
+
+static double* deq_matrix(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid) {
+  int64_t nbk = K / block_weights(fmt), row_bytes = nbk * block_bytes(fmt);
+  double* W = (double*)malloc(sizeof(double) * (size_t)rows * (size_t)K);
+  if (!W) return NULL;
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < rows; n++) orc_dequant(fmt, mat + (int64_t)n * row_bytes, nbk, grid, W + (int64_t)n * K);
+  return W;
+}
+
+/* out = D (silu(G x) * (U x)) with dequantised G, U [f][d] and D [d][f]. */
+static void expert_deq(const double* G, const double* U, const double* D, int d, int f, const double* x,
+                       double* out, double* g, double* u) {
+  matvec_deq(G, f, d, x, g);
+  matvec_deq(U, f, d, x, u);
+  for (int n = 0; n < f; n++) g[n] = silu(g[n]) * u[n];
+  matvec_deq(D, d, f, g, out);
+}
+
+int orc_ffn_grouped(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
+                    const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+                    const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype,
+                    int T, const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y) {
+  int64_t gu_bytes = mat_bytes(fmt_gu, f, d), dn_bytes = mat_bytes(fmt_dn, d, f);
+  int count = tokens ? n_tok : T;
+  for (int r = 0; r < count; r++) {
+    int t = tokens ? tokens[r] : r;
+    if (t < 0 || t >= T) return -1;
+    for (int j = 0; j < k; j++) {
+      int e = idx[(int64_t)t * k + j];
+      if (e < 0 || e >= E) return -1;
+    }
+  }
+  double* ye = (double*)calloc((size_t)count * k * d, sizeof(double));    /* [r][j][d] */
+  double* ysh = (double*)calloc((size_t)count * d, sizeof(double));       /* [r][d] */
+  double* xv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* g = (double*)malloc(sizeof(double) * (size_t)f);
+  double* u = (double*)malloc(sizeof(double) * (size_t)f);
+  if (!ye || !ysh || !xv || !g || !u) {
+    free(ye); free(ysh); free(xv); free(g); free(u);
+    return -2;
+  }
+  int status = 0;
+  for (int e = 0; e < E && status == 0; e++) {
+    int used = 0;
+    for (int r = 0; r < count && !used; r++) {
+      int t = tokens ? tokens[r] : r;
+      for (int j = 0; j < k; j++) used |= idx[(int64_t)t * k + j] == e;
+    }
+    if (!used) continue;
+    double* G = deq_matrix(fmt_gu, w_gate + e * gu_bytes, f, d, grid);
+    double* U = deq_matrix(fmt_gu, w_up + e * gu_bytes, f, d, grid);
+    double* D = deq_matrix(fmt_dn, w_down + e * dn_bytes, d, f, grid);
+    if (!G || !U || !D) status = -2;
+    for (int r = 0; r < count && status == 0; r++) {
+      int t = tokens ? tokens[r] : r;
+      for (int j = 0; j < k; j++) {
+        if (idx[(int64_t)t * k + j] != e) continue;
+        for (int i = 0; i < d; i++) xv[i] = (double)x_at(x, x_dtype, (int64_t)t * d + i);
+        expert_deq(G, U, D, d, f, xv, ye + ((int64_t)r * k + j) * d, g, u);
+      }
+    }
+    free(G); free(U); free(D);
+  }
+  if (status == 0 && has_shared) {
+    double* G = deq_matrix(fmt_sh, s_gate, f, d, grid);
+    double* U = deq_matrix(fmt_sh, s_up, f, d, grid);
+    double* D = deq_matrix(fmt_sh, s_down, d, f, grid);
+    if (!G || !U || !D) status = -2;
+    for (int r = 0; r < count && status == 0; r++) {
+      int t = tokens ? tokens[r] : r;
+      for (int i = 0; i < d; i++) xv[i] = (double)x_at(x, x_dtype, (int64_t)t * d + i);
+      expert_deq(G, U, D, d, f, xv, ysh + (int64_t)r * d, g, u);
+    }
+    free(G); free(U); free(D);
+  }
+  if (status == 0) {
+    for (int r = 0; r < count; r++) {
+      int t = tokens ? tokens[r] : r;
+      for (int i = 0; i < d; i++) {
+        double acc = 0.0;
+        for (int j = 0; j < k; j++) {
+          int e = idx[(int64_t)t * k + j];
+          double w = (double)wt[(int64_t)t * k + j], v = ye[((int64_t)r * k + j) * d + i];
+          if (down_gain)
+            acc += w * ((double)down_gain[(int64_t)e * d + i] * v);
+          else
+            acc += w * v;
+        }
+        if (has_shared) acc += ysh[(int64_t)r * d + i];
+        y[(int64_t)r * d + i] = (float)acc;
+      }
+    }
+  }
+  free(ye); free(ysh); free(xv); free(g); free(u);
+  return status;
+}
+
 /* Routing of the listed tokens: logits, exact top-k and mixing weights. */
 void orc_route(const void* x, int x_dtype, int T, int d, const float* W, int E, int k, float* z, int32_t* idx,
                float* wt) {

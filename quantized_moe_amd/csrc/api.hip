@@ -98,6 +98,56 @@ void prof_end(int id, hipStream_t s) {
 }
 }  // namespace qmoe
 
+// ---------------------------------------------------------------------------
+// launch shapes (occupancy and CU count), cached per device and kernel
+// ---------------------------------------------------------------------------
+namespace qmoe {
+namespace {
+struct ShapeEntry {
+  int dev;
+  const void* kernel;
+  int lds_bytes;  // -1: the entry only records that the LDS limit was raised
+  int blocks_per_cu, n_cus;
+};
+std::mutex g_shape_mu;
+std::vector<ShapeEntry> g_shapes;
+}  // namespace
+
+hipError_t launch_shape(const void* kernel, int threads, int lds_bytes, int lds_max, int* blocks_per_cu,
+                        int* n_cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_shape_mu);
+  bool raised = false;
+  for (const ShapeEntry& x : g_shapes) {
+    if (x.dev != dev || x.kernel != kernel) continue;
+    if (x.lds_bytes == lds_bytes) {
+      *blocks_per_cu = x.blocks_per_cu;
+      *n_cus = x.n_cus;
+      return hipSuccess;
+    }
+    raised = true;
+  }
+  if (!raised && kernel != nullptr && lds_max > 0) {
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_max);
+    if (e != hipSuccess) return e;
+  }
+  int nb = 0, cus = 0;
+  if (kernel != nullptr) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, lds_bytes);
+    if (e != hipSuccess) return e;
+  }
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  ShapeEntry x{dev, kernel, lds_bytes, nb > 0 ? nb : 1, cus > 0 ? cus : 1};
+  g_shapes.push_back(x);
+  *blocks_per_cu = x.blocks_per_cu;
+  *n_cus = x.n_cus;
+  return hipSuccess;
+}
+}  // namespace qmoe
+
 extern "C" int moe_profile_enable(int32_t on) {
   g_prof_on = on != 0;
   return ok();
@@ -175,6 +225,16 @@ static int check_T(const char* fn, int T) {
   return MOE_OK;
 }
 
+// The prefill GEMMs address x16 [T][d] and H [T*k][f] (fp16) with 32-bit
+// byte offsets; checked before anything is enqueued.
+static int check_prefill_size(const char* fn, int T, int k, int d, int f) {
+  if (!prefill_fits(T, k, d, f))
+    return fail(MOE_ERR_INVALID_ARG,
+                "%s: T %d with top_k %d, d_model %d, d_ff %d exceeds the prefill path's 2^31-byte activation "
+                "buffers (T*d*2 and T*top_k*d_ff*2 must stay below 2^31)", fn, T, k, d, f);
+  return MOE_OK;
+}
+
 static int check_dtype(const char* fn, int x_dtype) {
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown activation dtype %d", fn, x_dtype);
@@ -245,6 +305,8 @@ struct PrefillWs {
   uint16_t* x16;
   float *xs, *route_xs;
   void *H, *Hs;
+  int8_t *Hexp, *Hsexp;
+  float *Hsc, *Hssc;
   float *Ye, *Ysh;
 };
 struct LayerWs {
@@ -269,12 +331,18 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   w.xs = (float*)c.take((size_t)T * 4);
   w.route_xs = (float*)c.take(n * 4);
   w.H = c.take(n * f * 2);
+  w.Hexp = (int8_t*)c.take(n * (f / 128));
+  w.Hsc = (float*)c.take(n * 4);
   w.Ye = (float*)c.take(n * d * 4);
   if (has_shared) {
     w.Hs = c.take((size_t)T * f * 2);
+    w.Hsexp = (int8_t*)c.take((size_t)T * (f / 128));
+    w.Hssc = (float*)c.take((size_t)T * 4);
     w.Ysh = (float*)c.take((size_t)T * d * 4);
   } else {
     w.Hs = nullptr;
+    w.Hsexp = nullptr;
+    w.Hssc = nullptr;
     w.Ysh = nullptr;
   }
 }
@@ -529,6 +597,10 @@ static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_
   P.route_xs = w.route_xs;
   P.H = w.H;
   P.Hs = w.Hs;
+  P.Hexp = w.Hexp;
+  P.Hsexp = w.Hsexp;
+  P.Hsc = w.Hsc;
+  P.Hssc = w.Hssc;
   P.Ye = w.Ye;
   P.Ysh = w.Ysh;
   P.y = y;
@@ -579,6 +651,7 @@ extern "C" int moe_expert_ffn_prefill(const moe_layer* L, const void* x, int32_t
   int rc = check_layer(fn, L, false);
   if (rc) return rc;
   if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
+  if ((rc = check_prefill_size(fn, T, L->top_k, L->d_model, L->d_ff))) return rc;
   if (T == 0) return ok();
   NEED_PTR(x, "x");
   NEED_PTR(idx, "idx");
@@ -605,6 +678,7 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
   const int p = resolve_path(path, T);
   if (p == MOE_PATH_DECODE && T > DECODE_MAX_T)
     return fail(MOE_ERR_INVALID_ARG, "%s: T %d above the decode limit %d", fn, T, DECODE_MAX_T);
+  if (p == MOE_PATH_PREFILL && (rc = check_prefill_size(fn, T, L->top_k, L->d_model, L->d_ff))) return rc;
   if (T == 0) return ok();
   NEED_PTR(x, "x");
   NEED_PTR(y, "y");

@@ -39,7 +39,10 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t* __restrict__
   __syncthreads();
   for (int r = tid; r < n; r += 256) {
     const int key = idx[r];
-    if ((unsigned)key < (unsigned)E) atomicAdd(&hist[key], 1);  // out-of-range routes are dropped
+    if ((unsigned)key < (unsigned)E)
+      atomicAdd(&hist[key], 1);
+    else if (e == 0)
+      pos[r] = n;  // an out-of-range route is dropped: no place in perm (pos = n marks it)
   }
   __syncthreads();
   int part_off = 0, part_tiles = 0;

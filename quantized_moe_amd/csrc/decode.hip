@@ -50,15 +50,10 @@ DecodeWsLayout ws_layout(int T, int k, int d, int f) {
   return L;
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
+// CUs of the current device (cached per device by launch_shape)
+hipError_t cu_count(int* n) {
+  int per_cu = 0;
+  return launch_shape(nullptr, 0, 0, 0, &per_cu, n);
 }
 
 int64_t row_bytes(int fmt, int K) { return (int64_t)(K / block_weights(fmt)) * block_bytes(fmt); }
@@ -111,7 +106,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);
   a.y = L.y;
-  const int ncu = cu_count();
+  int ncu = 256;
+  if (hipError_t e = cu_count(&ncu); e != hipSuccess) return e;
 
   // launch 1: router blocks of epb experts, shared blocks of spb steps, all
   // streaming about the same bytes

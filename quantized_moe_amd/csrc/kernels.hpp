@@ -32,6 +32,15 @@ void prof_take_events(hipEvent_t* start, hipEvent_t* stop);  // the pending pair
     hipExtLaunchKernelGGL(kern, grid, block, shmem, stream, qmoe_ev_a_, qmoe_ev_b_, 0, __VA_ARGS__); \
   } while (0)
 
+// Launch shape of a kernel on the current device (api.hip): the number of its
+// blocks of `threads` threads and `lds_bytes` of dynamic LDS that fit one CU
+// at once, and the device's CU count.  The first query for a kernel on a
+// device raises its dynamic-LDS limit to lds_max.  Results are cached per
+// (device, kernel, lds_bytes) under a lock, so concurrent host threads and
+// several devices are safe.  kernel = nullptr queries only the CU count.
+hipError_t launch_shape(const void* kernel, int threads, int lds_bytes, int lds_max, int* blocks_per_cu,
+                        int* n_cus);
+
 // route.hip
 hipError_t launch_router(const float* W, int E, int d, const void* x, int x_dtype, int T, float* z, hipStream_t s);
 hipError_t launch_topk(const float* z, int T, int E, int k, const float* bias, int32_t* idx, float* wt, int32_t* idx2,
@@ -83,13 +92,22 @@ struct PrefillLaunch {
   uint16_t* x16;  // fp16 [T][d]: x times a per-token power of two
   float* xs;      // [T]: that power of two
   float* route_xs;  // [T*k]: the same at each route, in bucket order
-  void* H;      // fp16 [T*k][f]
+  void* H;      // fp16 [T*k][f]: h * 2^-Hexp of its 128-column chunk
   void* Hs;     // fp16 [T][f]
+  int8_t* Hexp;   // [T*k][f/128]
+  int8_t* Hsexp;  // [T][f/128]
+  float* Hsc;     // [T*k]: 2^e of each H row once its chunks share one exponent
+  float* Hssc;    // [T]
   float* Ye;    // [T*k][d]
   float* Ysh;   // [T][d]
   float* y;     // [T][d]
 };
 hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s);
+// The grouped GEMMs address their A operands (x16, H, Hs) with 32-bit byte
+// offsets: false when T, k, d, f would pass 2^31.
+inline bool prefill_fits(int T, int k, int d, int f) {
+  return (int64_t)T * d * 2 < (int64_t(1) << 31) && (int64_t)T * k * f * 2 < (int64_t(1) << 31);
+}
 
 // repack.hip
 hipError_t launch_repack(int fmt, int64_t n_blocks, const void* src, void* dst, int to_device, hipStream_t s);

@@ -8,10 +8,18 @@
 //     (2s+1) * grid value <= 217; Q2K: sc * q <= 45), the fp16 superblock
 //     scales are applied in an fp32 epilogue once per 256 inputs, and Q2K's
 //     min term is a second, K=16 MFMA against per-sub-block sums of the A rows;
-//     Q8 weights (the shared expert) enter as fp16(d*q), rounded once;
+//     Q8 weights (the shared expert) enter as fp16(d*q*2^k), rounded once,
+//     with 2^k a power of two per output row and superblock that keeps every
+//     product a normal fp16 (undone in the fp32 epilogue);
 //   * the activations x are converted once to fp16 with a per-token power of
 //     two (exact) that puts max|x_t| in [2^13, 2^14), undone in the gate/up
-//     epilogue; the SwiGLU output h is stored as fp16 (one rounding, 2^-11).
+//     epilogue; the SwiGLU output h is stored as fp16 times a power of two
+//     per (row, 128 outputs) that puts max|h| over the work item's N tile
+//     (256 or 128 outputs) in [2^14, 2^15) (one rounding, 2^-11 relative,
+//     whatever the scale of x and of the weights); a short pass then brings
+//     every row to its largest exponent (exact but for fp16 subnormals,
+//     below 2^-24 of the row's maximum), and the down GEMM applies the row's
+//     power of two to its fp32 outputs.
 //
 // One persistent kernel per GEMM (routed gate/up, routed down, shared gate/up,
 // shared down), 16 waves per block.  A work item is (M tile of 32 rows of one
@@ -60,6 +68,7 @@ __global__ __launch_bounds__(256) void x16_kernel(const void* __restrict__ x, in
                                                   uint16_t* __restrict__ x16, float* __restrict__ xs,
                                                   const int32_t* __restrict__ pos, int k,
                                                   float* __restrict__ route_xs) {
+  const int n_routes = (int)gridDim.x * k;
   __shared__ float red[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   auto load4 = [&](int i, float* v) {
@@ -103,8 +112,12 @@ __global__ __launch_bounds__(256) void x16_kernel(const void* __restrict__ x, in
     *reinterpret_cast<uint2*>(x16 + (int64_t)t * d + i) = h;
   }
   if (tid == 0) xs[t] = ldexpf(1.0f, e);
-  // the same scale at each of the token's routes in bucket order
-  if (tid < k) route_xs[pos[(int64_t)t * k + tid]] = ldexpf(1.0f, e);
+  // the same scale at each of the token's routes in bucket order (a route
+  // whose expert id is out of range has no place: pos holds n_routes)
+  if (tid < k) {
+    const int p = pos[(int64_t)t * k + tid];
+    if ((unsigned)p < (unsigned)n_routes) route_xs[p] = ldexpf(1.0f, e);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -128,6 +141,9 @@ struct GemmArgs {
   const int32_t* perm;         // routed: [T*k]
   // output
   void* out;                   // gate/up: fp16 H [rows][N]; down: fp32 [rows][N]
+  // power-of-two exponents of H: H[row][c] = fp16(h * 2^-hexp[row][c / 128])
+  int8_t* hexp_out;            // gate/up: written, [rows][N / 128]
+  const float* row_scale;      // down: 2^e of each A row (H row = fp16(h 2^-e)), [rows]
 };
 
 // ---------------------------------------------------------------------------
@@ -363,22 +379,57 @@ __device__ __forceinline__ uint2 q4k_min_frag(const BRegs<FMT_Q4K, KS>& b) {
   return make_uint2(m0 | (m0 << 16), m1 | (m1 << 16));
 }
 
-// Q8 fragment of local step i: the 8 products d*q as fp16, each rounded once.
-// A quant byte b becomes the exact fp16 integer q: (b ^ 0x80) placed under an
-// fp16 exponent byte 0x64 reads 1024 + q + 128 (one v_perm per pair), minus
-// 1152 (one packed add); one packed multiply by (d, d) then rounds q*d.
+// Q8 block scales pre-multiplied by a power of two 2^k shared by the wave's
+// four lane groups, i.e. by one output row's superblock (KS = 1: the lane's
+// blocks 2*g4, 2*g4 + 1) or by the wave's half of it (KS = 2: block
+// 2*g4 + h).  k puts the largest |d| among them in [2^7, 2^8), so every
+// product d*q*2^k with 1 <= |q| <= 128 of that block is a normal fp16 below
+// 2^15 whatever the magnitude of d; a block with a much smaller d loses
+// only digits that are small against the largest block.  dw gets the scaled
+// fp16 words (fp32 product, one rounding); returns 2^-k for the epilogue.
 template <int KS>
-__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, KS>& b, int hh, int i) {
+__device__ __forceinline__ float q8_prescale(uint32_t d, uint32_t& dw) {
+  uint32_t e = (d >> 10) & 31u;  // biased fp16 exponent of each |d|
+  if constexpr (KS == 1) e = max(e, (d >> 26) & 31u);
+  e = max(e, (uint32_t)__shfl_xor((int)e, 16, 64));
+  e = max(e, (uint32_t)__shfl_xor((int)e, 32, 64));
+  const int k = 22 - (int)max(e, 1u);  // |d| < 2^(e - 14)  ->  |d| 2^k < 2^8
+  const float s = __builtin_amdgcn_ldexpf(1.0f, k);
+  dw = to_h(from_h(d & 0xffffu) * s);
+  if constexpr (KS == 1) dw |= to_h(from_h(d >> 16) * s) << 16;
+  return __builtin_amdgcn_ldexpf(1.0f, -k);
+}
+
+// Q8 fragment of local step i: the 8 products d*q (d the prescaled scale of
+// the block, from dw) as fp16, each rounded once.  A quant byte b becomes
+// the exact fp16 integer q: (b ^ 0x80) placed under an fp16 exponent byte
+// 0x64 reads 1024 + q + 128 (one v_perm per pair), minus 1152 (one packed
+// add); one packed multiply by (d, d) then rounds q*d.
+template <int KS>
+__device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, KS>& b, int hh, int i, uint32_t dw) {
   const uint32_t w0 = word_of(b.q[2 * hh + (i >> 1)], 2 * (i & 1)) ^ 0x80808080u;
   const uint32_t w1 = word_of(b.q[2 * hh + (i >> 1)], 2 * (i & 1) + 1) ^ 0x80808080u;
   const f16x2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const uint16_t dh = (uint16_t)(b.d >> (16 * hh));
+  const uint16_t dh = (uint16_t)(dw >> (16 * hh));
   const f16x2_t dd = {__builtin_bit_cast(_Float16, dh), __builtin_bit_cast(_Float16, dh)};
   auto pair = [&](uint32_t w, uint32_t sel) {
     const f16x2_t q = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(w, 0x64646464u, sel)) + bias;
     return __builtin_bit_cast(uint32_t, q * dd);
   };
   return make_uint4(pair(w0, 0x00050004u), pair(w0, 0x00070006u), pair(w1, 0x00050004u), pair(w1, 0x00070006u));
+}
+
+// Maximum of v over each 16-lane row of the wave (the 16 output columns an
+// MFMA result row spreads over), returned to every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xb1>{}));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4e>{}));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));  // row_mirror
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -391,10 +442,11 @@ struct GemmLds {
   static constexpr int kTqs = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
   static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
-  static constexpr int kTok = GATEUP ? 3 * BM * 8 : 0;                // token and scale of each row, 3 items
+  static constexpr int kTok = 3 * BM * 8;                             // token (gate/up) and scale of each row, 3 items
   static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
+  static constexpr int kMax = GATEUP ? 2 * BM * 4 : 0;                // gate/up: [item parity][BM] row maxima of |h|
   static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oA = oTqs + kTqs, oS = oA + kA, oTok = oS + kS,
-                       oRed = oTok + kTok, oTiles = oRed + kRed;
+                       oRed = oTok + kTok, oMax = oRed + kRed, oTiles = oMax + kMax;
   // then tile_start, counts, offsets of the routed experts: [3][E + 1]
   static constexpr int bytes_for(int E) { return oTiles + 3 * (E + 1) * 4; }
 };
@@ -421,6 +473,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   int* sTok = reinterpret_cast<int*>(lds + L::oTok);              // [3][BM]
   float* sXs = reinterpret_cast<float*>(lds + L::oTok) + 3 * BM;  // [3][BM]
   float* sRed = reinterpret_cast<float*>(lds + L::oRed);
+  uint32_t* sMax = reinterpret_cast<uint32_t*>(lds + L::oMax);  // gate/up: [j % 2][BM], fp32 bits of max|h|
   int* sTiles = reinterpret_cast<int*>(lds + L::oTiles);
   int* sCounts = sTiles + (a.E + 1);
   int* sOffsets = sCounts + (a.E + 1);
@@ -433,6 +486,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   if constexpr (FMT == FMT_IQ2)
     build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid, GEMM_THREADS);
   if constexpr (FMT == FMT_Q2K) build_q2k_table(reinterpret_cast<uint2*>(lds + L::oTqs));
+  if constexpr (GATEUP) {
+    if (tid < 2 * BM) sMax[tid] = 0u;
+  }
   if (a.routed) {
     for (int i = tid; i <= a.E; i += GEMM_THREADS) {
       sTiles[i] = a.tile_start[i];
@@ -508,25 +564,26 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     it.nm = __builtin_amdgcn_readfirstlane(it.nm);
     return it;
   };
-  // gate/up: token index and x scale of each row of item j, into slot j % 3.
-  // In the steady state the two loads are issued one item ahead (tok_issue)
-  // and written to LDS an item later (tok_commit), so no step waits for them.
+  // Per row of item j, into slot j % 3: gate/up, the token index and the x
+  // scale; down, the A row's scale (its output factor).  In the steady state
+  // the loads are issued one item ahead (tok_issue) and written to LDS an
+  // item later (tok_commit), so no step waits for them.
   int tok_r = 0;
   float xs_r = 0.0f;
   auto tok_issue = [&](const Item& it) {
+    const int i = tid % BM;  // every thread loads (uniform load count per step)
+    const int p = it.p0 + (i < it.rows ? i : 0);
     if constexpr (GATEUP) {
-      const int i = tid % BM;  // every thread loads (uniform load count per step)
-      const int p = it.p0 + (i < it.rows ? i : 0);
       tok_r = a.routed ? a.perm[p] : p;
       xs_r = a.rowxs[p];
+    } else {
+      xs_r = a.row_scale[p];
     }
   };
   auto tok_commit = [&](int j) {
-    if constexpr (GATEUP) {
-      if (tid < BM) {
-        sTok[(j % 3) * BM + tid] = a.routed ? tok_r / a.k : tok_r;
-        sXs[(j % 3) * BM + tid] = xs_r;
-      }
+    if (tid < BM) {
+      if constexpr (GATEUP) sTok[(j % 3) * BM + tid] = a.routed ? tok_r / a.k : tok_r;
+      sXs[(j % 3) * BM + tid] = xs_r;
     }
   };
 
@@ -632,21 +689,33 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
     };
     if constexpr (FMT == FMT_Q8) {
+      uint32_t dw0 = 0, dw1 = 0;
+      const float ps0 = q8_prescale<KS>(B0.d, dw0);
+      float ps1 = 0.0f;
+      if constexpr (GATEUP) ps1 = q8_prescale<KS>(B1.d, dw1);
+      f32x4_t s0[NM], s1[NM];
+#pragma unroll
+      for (int m = 0; m < NM; m++) s0[m] = s1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hh = 0; hh < 3 - KS; hh++) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint4 f0 = q8_frag(B0, hh, i);
+          const uint4 f0 = q8_frag(B0, hh, i, dw0);
           uint4 f1;
-          if constexpr (GATEUP) f1 = q8_frag(B1, hh, i);
+          if constexpr (GATEUP) f1 = q8_frag(B1, hh, i, dw1);
 #pragma unroll
           for (int m = 0; m < NM; m++) {
             const uint4 av = aread(m, 4 * hh + i);
-            acc0[m] = mfma32(av, f0, acc0[m]);
-            if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
+            s0[m] = mfma32(av, f0, s0[m]);
+            if constexpr (GATEUP) s1[m] = mfma32(av, f1, s1[m]);
           }
           if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live fragments
         }
+      }
+#pragma unroll
+      for (int m = 0; m < NM; m++) {
+        acc0[m] += ps0 * s0[m];
+        if constexpr (GATEUP) acc1[m] += ps1 * s1[m];
       }
     } else {
       f32x4_t s0[NM], s1[NM];
@@ -774,8 +843,73 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       }
     }
     if constexpr (KS == 2) __syncthreads();
-    if (h == 0) {
-      const int n = it.nt * BN + wv * 16 + c16;  // this lane's output row (B column)
+    const int n = it.nt * BN + wv * 16 + c16;  // this lane's output row (B column)
+    const int cl = wv * 16 + c16;              // ... inside the N tile
+    if constexpr (GATEUP) {
+      // Two phases around a barrier.  First h goes to LDS (both A buffers
+      // are free: the next superblock's A is stored after the epilogue) and
+      // each row's max|h| over the wave's 16 columns (DPP) into the row's
+      // maximum for the item (an LDS atomic maximum on the fp32 bits, which
+      // order like unsigned integers for non-negative values; buffer j % 2,
+      // cleared during item j - 1).  Then e follows from the row maximum and
+      // h is stored as fp16(h 2^-e).  (h goes through LDS rather than
+      // registers so that nothing is held across the barrier.)
+      constexpr int HROW = BN + 4;  // floats per row of the h tile (padded: the 4 row groups meet other banks)
+      static_assert(BM * HROW * 4 <= (KS == 1 ? 2 : 1) * A_BUF, "the h tile fits the free A buffers");
+      float* hbuf = reinterpret_cast<float*>(sA + (KS == 1 ? 0 : (freebuf ^ 1) * A_BUF));
+      uint32_t* rmax = sMax + (j & 1) * BM;
+      if (h == 0) {
+#pragma unroll
+        for (int m = 0; m < NSUB; m++) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
+            const int i = m * 16 + 4 * g4 + r;
+            float hv = 0.0f;
+            if (m < it.nm && i < it.rows) {
+              const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
+              const float v1 = KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r];
+              const float xs = sXs[(j % 3) * BM + i];
+              hv = silu(v0 * xs) * (v1 * xs);
+            }
+            hbuf[i * HROW + cl] = hv;
+            const float mx = row16_max(fabsf(hv));
+            if (c16 == 0) atomicMax(rmax + i, __float_as_uint(mx));
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < BM) sMax[((j + 1) & 1) * BM + tid] = 0u;  // the next item's maxima (last read by item j - 1)
+      if (h == 0) {
+        // wave-uniform bases (scalar registers), 32-bit lane offsets
+        _Float16* hout = static_cast<_Float16*>(a.out) + (int64_t)it.p0 * a.N + it.nt * BN;
+        int8_t* eout = a.hexp_out + (int64_t)it.p0 * (a.N / 128) + it.nt * (BN / 128) + wv;
+#pragma unroll
+        for (int m = 0; m < NSUB; m++) {
+          if (m < it.nm) {
+            const uint4 rm = *reinterpret_cast<const uint4*>(rmax + m * 16 + 4 * g4);
+            const uint32_t rmw[4] = {rm.x, rm.y, rm.z, rm.w};
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const int i = m * 16 + 4 * g4 + r;
+              if (i < it.rows) {
+                const float mx = __uint_as_float(rmw[r]);
+                int e = 0;
+                if (mx > 0.0f && mx <= 3.4e38f) {
+                  int ex;
+                  frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+                  e = min(max(ex - 15, -100), 100);
+                }
+                const float hv = hbuf[i * HROW + cl];
+                hout[i * a.N + cl] = (_Float16)(hv * __builtin_amdgcn_ldexpf(1.0f, -e));
+                if (wv < BN / 128 && c16 == 0) eout[i * (a.N / 128)] = (int8_t)e;  // one lane per row and chunk
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();  // the h tile is read before the next A store overwrites it
+    } else if (h == 0) {
 #pragma unroll
       for (int m = 0; m < NSUB; m++) {
         if (m < it.nm) {
@@ -784,16 +918,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
             const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
             const int i = m * 16 + 4 * g4 + r;
             const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
-            if (i < it.rows) {
-              if constexpr (GATEUP) {
-                const float v1 = KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r];
-                const float xs = sXs[(j % 3) * BM + i];
-                const float hv = silu(v0 * xs) * (v1 * xs);
-                static_cast<_Float16*>(a.out)[(int64_t)(it.p0 + i) * a.N + n] = (_Float16)hv;
-              } else {
-                static_cast<float*>(a.out)[(int64_t)(it.p0 + i) * a.N + n] = v0;
-              }
-            }
+            if (i < it.rows) static_cast<float*>(a.out)[(int64_t)it.p0 * a.N + (i * a.N + n)] = v0 * sXs[(j % 3) * BM + i];
           }
         }
       }
@@ -871,6 +996,48 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// row normalisation of H between the two GEMMs
+// ---------------------------------------------------------------------------
+// The gate/up epilogue stores each 128-output chunk c of a row as
+// fp16(h 2^-e_c).  One wave per row: e = max_c e_c; every chunk with e_c < e
+// is multiplied by 2^(e_c - e) in place (exact but for fp16 subnormals,
+// which lie below 2^-24 of the row's largest |h|), so the row is fp16(h 2^-e)
+// throughout and the down GEMM can scale its fp32 outputs by 2^e.  Rows
+// [0, n0) are H0's (routed, exponents e0), [n0, n0 + n1) H1's (shared).
+__global__ __launch_bounds__(256) void hnorm_kernel(uint16_t* __restrict__ H0, const int8_t* __restrict__ e0,
+                                                    float* __restrict__ sc0, int n0, uint16_t* __restrict__ H1,
+                                                    const int8_t* __restrict__ e1, float* __restrict__ sc1, int n1,
+                                                    int f) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n0 + n1) return;  // uniform per wave
+  const bool first = row < n0;
+  const int r = first ? row : row - n0;
+  uint16_t* h = (first ? H0 : H1) + (int64_t)r * f;
+  const int nch = f / 128;  // chunks per row (<= 64)
+  const int8_t* er = (first ? e0 : e1) + (int64_t)r * nch;
+  const int ec = lane < nch ? er[lane] : -128;
+  int e = ec;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) e = max(e, __shfl_xor(e, o, 64));
+  // 16-byte pieces: piece q of the row covers values 8q .. 8q + 7 (chunk q / 16)
+  for (int q = lane; q < f / 8; q += 64) {
+    const int d = __shfl(ec, q / 16, 64) - e;
+    if (d != 0) {
+      const _Float16 fac = (_Float16)__builtin_amdgcn_ldexpf(1.0f, d);
+      const f16x2_t ff = {fac, fac};
+      uint4 v = *reinterpret_cast<const uint4*>(h + 8 * q);
+      v.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.x) * ff);
+      v.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.y) * ff);
+      v.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.z) * ff);
+      v.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, v.w) * ff);
+      *reinterpret_cast<uint4*>(h + 8 * q) = v;
+    }
+  }
+  if (lane == 0) (first ? sc0 : sc1)[r] = __builtin_amdgcn_ldexpf(1.0f, e);
+}
+
+// ---------------------------------------------------------------------------
 // combine: y[t] = sum_j wt[t][j] * (g_e * Ye[pos[t*k+j]]) + ysh[t]   (fixed j order; g_e the route's
 // per-channel down gains, one when none are given)
 // ---------------------------------------------------------------------------
@@ -911,19 +1078,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-static int g_num_cus = 0;
-
-static int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
-}
-
 template <int FMT, bool GATEUP, int PD, int KS>
 static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int max_items = m_tiles * (a.N / gemm_bn(KS));
@@ -932,22 +1086,10 @@ static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
   using L = GemmLds<FMT, GATEUP, KS>;
   auto kern = gemm_kernel<FMT, GATEUP, PD, KS>;
   const int bytes = L::bytes_for(a.routed ? a.E : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       L::bytes_for(MAX_EXPERTS));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  static int cached_bytes = -1, per_cu = 1;  // resident blocks per CU at that LDS size
-  if (bytes != cached_bytes) {
-    int nb = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, GEMM_THREADS, bytes);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-    cached_bytes = bytes;
-  }
-  int grid = per_cu * num_cus();
+  int per_cu = 1, n_cus = 256;  // resident blocks per CU at that LDS size, CUs of the device
+  hipError_t e = launch_shape((const void*)kern, GEMM_THREADS, bytes, L::bytes_for(MAX_EXPERTS), &per_cu, &n_cus);
+  if (e != hipSuccess) return e;
+  int grid = per_cu * n_cus;
   grid = (grid / 8) * 8;
   if (max_items < grid) grid = ((max_items + 7) / 8) * 8;
   if (grid < 8) grid = 8;
@@ -989,7 +1131,7 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
       if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
       return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
     }
-    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 2>(a, m_tiles, s);
+    // (two superblocks in flight spill: measured 220 us against 152 us with one)
     return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
   }
 }
@@ -1004,10 +1146,7 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
 
 hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
   hipError_t err = hipSuccess;
-  const int n = P.T * P.k;
-  // A operands are addressed with 32-bit buffer offsets
-  if ((int64_t)P.T * P.d * 2 >= (int64_t(1) << 31) || (int64_t)n * P.f * 2 >= (int64_t(1) << 31))
-    return hipErrorInvalidValue;
+  const int n = P.T * P.k;  // (the host checked prefill_fits: A offsets stay below 2^31)
   {
     const int pid = prof_begin("prefill_x16", s);
     QMOE_LAUNCH(x16_kernel, dim3(P.T), dim3(256), 0, s, P.x, P.x_dtype, P.d, P.x16, P.xs, P.pos, P.k, P.route_xs);
@@ -1033,9 +1172,39 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.H;
+    a.hexp_out = P.Hexp;
     const int m_tiles = n / BM + P.E;
     PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
+  }
+  if (P.has_shared) {
+    GemmArgs a{};
+    a.B0 = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
+    a.B1 = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
+    a.grid = P.grid;
+    a.a16 = P.x16;
+    a.a16_bytes = P.T * P.d * 2;
+    a.rowxs = P.xs;
+    a.K = P.d;
+    a.N = P.f;
+    a.routed = 0;
+    a.n_rows = P.T;
+    a.E = 1;
+    a.k = 1;
+    a.out = P.Hs;
+    a.hexp_out = P.Hsexp;
+    const int m_tiles = (P.T + BM - 1) / BM;
+    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, m_tiles, s)))
+    if (err != hipSuccess) return err;
+  }
+  // every row of H and Hs to one exponent (the down GEMMs scale their outputs by it)
+  {
+    const int rows = n + (P.has_shared ? P.T : 0);
+    const int pid = prof_begin("prefill_hnorm", s);
+    QMOE_LAUNCH(hnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, static_cast<uint16_t*>(P.H), (const int8_t*)P.Hexp,
+                P.Hsc, n, static_cast<uint16_t*>(P.Hs), (const int8_t*)P.Hsexp, P.Hssc, P.has_shared ? P.T : 0, P.f);
+    prof_end(pid, s);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // routed down -> Ye (fp32, bucket order); same M tiles as the gate/up GEMM
   {
@@ -1054,28 +1223,12 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.Ye;
+    a.row_scale = P.Hsc;
     const int m_tiles = n / BM + P.E;
     PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   if (P.has_shared) {
-    GemmArgs a{};
-    a.B0 = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
-    a.B1 = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
-    a.grid = P.grid;
-    a.a16 = P.x16;
-    a.a16_bytes = P.T * P.d * 2;
-    a.rowxs = P.xs;
-    a.K = P.d;
-    a.N = P.f;
-    a.routed = 0;
-    a.n_rows = P.T;
-    a.E = 1;
-    a.k = 1;
-    a.out = P.Hs;
-    const int m_tiles = (P.T + BM - 1) / BM;
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, m_tiles, s)))
-    if (err != hipSuccess) return err;
     GemmArgs b{};
     b.B0 = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
     b.grid = P.grid;
@@ -1088,6 +1241,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     b.E = 1;
     b.k = 1;
     b.out = P.Ysh;
+    b.row_scale = P.Hssc;
     const int m_tiles2 = (P.T + BM - 1) / BM;
     PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false>(b, m_tiles2, s)))
     if (err != hipSuccess) return err;

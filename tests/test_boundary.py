@@ -141,6 +141,24 @@ def test_workspace_too_small_is_rejected_before_launch():
     assert "need" in lib.last_error()
 
 
+def test_prefill_offset_limit_is_checked_before_any_launch():
+    """The prefill path addresses H [T*k][f] fp16 with 32-bit offsets: T =
+    65536, k = 6, f = 4096 is inside the documented size limits but its H
+    needs 3 GiB.  The call must fail on the host, as an invalid argument,
+    before the router, top-k or bucketing kernels are enqueued (the fake
+    pointers would fault if anything were)."""
+    layer = _layer(d_ff=4096)
+    ws = 1 << 62  # a workspace "large enough": the size check must come first
+    assert _forward(layer, T=65536, ws_bytes=ws) == lib.MOE_ERR_INVALID_ARG
+    assert "2^31" in lib.last_error()
+    L = lib.lib()
+    rc = L.moe_expert_ffn_prefill(ctypes.byref(layer), 4096, lib.MOE_BF16, 65536, 4352, 4608, 4864, None, 5120,
+                                  ws, None)
+    assert rc == lib.MOE_ERR_INVALID_ARG
+    # x16 [T][d] alone: T = 65536, d = 8192 is 1 GiB (fits); with k = 16, f = 2048 H is 4 GiB
+    assert _forward(_layer(d_model=8192, top_k=16, d_ff=2048), T=65536, ws_bytes=ws) == lib.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_sizes_cover_their_buffers():
     layer = _layer()
     E, d, f, k = 384, 4096, 2048, 6
