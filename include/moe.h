@@ -325,6 +325,27 @@ int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype,
                       int32_t path, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same computation with the
+ * same kernels as moe_layer_forward (bitwise the same outputs); the
+ * workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds in each device's memory from its load until the process ends.
+ * Nothing is allocated by the call (the first call on a device looks up
+ * that device's array).  That covers every decode call (T <= 8 at any
+ * supported shape) and short prefill chunks; a call that would need more
+ * (moe_workspace_bytes(L, T, MOE_OP_LAYER) on its path) returns
+ * MOE_ERR_WORKSPACE and enqueues nothing.  Every call on one device shares
+ * that device's array, and the array keeps the last call's contents (no
+ * call needs it cleared): calls that overlap in time on one device (several
+ * streams or host threads) race, and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_layer_forward_noalloc(const moe_layer* L, const void* x, int32_t x_dtype,
+                              int32_t T, float* y, int32_t* idx_out,
+                              float* wt_out, int32_t path, void* stream);
+
+/*
  * Per-kernel timing with HIP events recorded on the stream each kernel is
  * launched on.  Eager use only: do not enable it while a stream is being
  * captured into a graph.  moe_profile_collect synchronises the recorded

@@ -666,10 +666,37 @@ extern "C" int moe_expert_ffn_prefill(const moe_layer* L, const void* x, int32_t
   return run_prefill(fn, L, x, x_dtype, T, idx, wt, y, bucket_out, c, (hipStream_t)stream);
 }
 
-extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,
-                                 int32_t* idx_out, float* wt_out, int32_t path, void* ws, size_t ws_bytes,
-                                 void* stream) {
-  const char* fn = "moe_layer_forward";
+// The device array behind moe_layer_forward_noalloc: a fixed workspace in
+// every device's memory, held until the process ends.  Its host-side name
+// is only a stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+// The address of the current device's `scratch`, looked up once per device
+// (under a lock) and kept.
+static int scratch_address(const char* fn, void** out) {
+  static std::mutex mu;
+  static std::vector<std::pair<int, void*>> addrs;
+  int dev = 0;
+  HIP_CHECK(hipGetDevice(&dev), fn);
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& a : addrs)
+    if (a.first == dev) {
+      *out = a.second;
+      return MOE_OK;
+    }
+  void* ptr = nullptr;
+  HIP_CHECK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), fn);
+  addrs.emplace_back(dev, ptr);
+  *out = ptr;
+  return MOE_OK;
+}
+
+// moe_layer_forward and moe_layer_forward_noalloc: validation, then the
+// launches on the caller's workspace or (noalloc) on `scratch`.
+static int layer_forward(const char* fn, const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,
+                         int32_t* idx_out, float* wt_out, int32_t path, void* ws, size_t ws_bytes, bool noalloc,
+                         void* stream) {
   int rc = check_layer(fn, L, true);
   if (rc) return rc;
   if ((rc = check_T(fn, T)) || (rc = check_dtype(fn, x_dtype))) return rc;
@@ -682,12 +709,20 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
   if (T == 0) return ok();
   NEED_PTR(x, "x");
   NEED_PTR(y, "y");
-  NEED_PTR(ws, "workspace");
+  if (!noalloc) NEED_PTR(ws, "workspace");
   if (idx_out && !aligned16(idx_out)) return fail(MOE_ERR_INVALID_ARG, "%s: idx_out is not 16-byte aligned", fn);
   if (wt_out && !aligned16(wt_out)) return fail(MOE_ERR_INVALID_ARG, "%s: wt_out is not 16-byte aligned", fn);
   const int E = L->n_experts, k = L->top_k;
   const size_t need = ws_layer(E, T, k, L->d_model, L->d_ff, L->has_shared, p);
-  if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  if (noalloc) {
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_WORKSPACE,
+                  "%s: this call needs %zu bytes of workspace, above the library's fixed %u-byte scratch array "
+                  "(fewer tokens, or moe_layer_forward with a workspace)", fn, need, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+    if ((rc = scratch_address(fn, &ws))) return rc;
+  } else if (ws_bytes < need) {
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  }
   Carve c;
   c.base = (uint8_t*)ws;
   LayerWs lw;
@@ -697,7 +732,7 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
     DecodeWs w;
     carve_decode(c, w, T, k, L->d_model, L->d_ff);
     DecodeLaunch D = decode_launch(L, x, x_dtype, T);
-      D.z = lw.z;
+    D.z = lw.z;
     D.zkey = lw.zkey;
     D.idx = lw.idx;
     D.wt = lw.wt;
@@ -719,4 +754,16 @@ extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dt
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return run_prefill(fn, L, x, x_dtype, T, lw.idx, lw.wt, y, nullptr, c, s);
+}
+
+extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,
+                                 int32_t* idx_out, float* wt_out, int32_t path, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return layer_forward("moe_layer_forward", L, x, x_dtype, T, y, idx_out, wt_out, path, ws, ws_bytes, false, stream);
+}
+
+extern "C" int moe_layer_forward_noalloc(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,
+                                         int32_t* idx_out, float* wt_out, int32_t path, void* stream) {
+  return layer_forward("moe_layer_forward_noalloc", L, x, x_dtype, T, y, idx_out, wt_out, path, nullptr, 0, true,
+                       stream);
 }

@@ -25,6 +25,7 @@ MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_LAYER = 0, 1, 2, 3
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_DECODE_MAX_T = 8
 MOE_REPACK_TO_DEVICE, MOE_REPACK_TO_CANONICAL = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int),
             "moe_layer_forward": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _I32, _P, _SZ, _P],
                                   ctypes.c_int),
+            "moe_layer_forward_noalloc": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _I32, _P],
+                                          ctypes.c_int),
             "moe_profile_enable": ([_I32], ctypes.c_int),
             "moe_profile_reset": ([], ctypes.c_int),
             "moe_profile_collect": ([_I32, _P, _P, _P, _P], ctypes.c_int),
@@ -177,6 +180,14 @@ def expert_ffn_prefill(layer: MoeLayer, x, idx, wt, y, ws, bucket_out=None, stre
 def layer_forward(layer: MoeLayer, x, y, ws, idx_out=None, wt_out=None, path=MOE_PATH_AUTO, stream=None) -> None:
     _check(lib().moe_layer_forward(ctypes.byref(layer), _ptr(x), x_dtype_of(x), x.shape[0], _ptr(y), _ptr(idx_out),
                                    _ptr(wt_out), path, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_forward_noalloc(layer: MoeLayer, x, y, idx_out=None, wt_out=None, path=MOE_PATH_AUTO,
+                          stream=None) -> None:
+    """moe_layer_forward on the library's fixed per-device scratch array
+    (MOE_NOALLOC_SCRATCH_BYTES; no workspace argument, nothing allocated)."""
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(layer), _ptr(x), x_dtype_of(x), x.shape[0], _ptr(y),
+                                           _ptr(idx_out), _ptr(wt_out), path, _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:
