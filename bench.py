@@ -397,7 +397,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i16-fixed-point x i2/i8 integer dot products, fp32 scales",
         "data": "synthetic",
         "config": {"workload": "decode: one MoE layer, 384 experts, top-6, d=4096, f=2048, shared Q8_0-like "
                                "expert, " + ("IQ2_XXS-like gate/up, Q2_K-like down" if args.routed_fmt == "iq2-q2k"

@@ -265,6 +265,25 @@ int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t K,
                const void* src, void* dst, int32_t direction, void* stream);
 
 /*
+ * Prepare a whole layer for the compute entry points: every weight tensor of
+ * `canonical` (layout MOE_LAYOUT_CANONICAL, all other fields as for the
+ * compute calls) is converted to the device layout, as moe_repack does, into
+ * the buffers the caller put in device_out->w_gate, w_up, w_down (and
+ * s_gate, s_up, s_down if the layer has a shared expert), each
+ * moe_matrix_bytes() of its tensor, 16-byte aligned, overlapping no source
+ * and no other destination.  Then *device_out [host] becomes *canonical with
+ * those six pointers and layout = MOE_LAYOUT_DEVICE: the grid, router, bias
+ * and gain arrays have a single layout and are shared, not copied.
+ * Everything is validated before the first launch; on an error *device_out
+ * is left unchanged.  Device copies with aligned quant streams follow the
+ * load-time payload re-alignment of the YoungAi page, section 4.4 (decode,
+ * VQ expert kernel); one call per layer keeps the layout internals behind
+ * the narrow interface of the ds4 timeline's public header.
+ */
+int moe_prepare_weights(const moe_layer* canonical, moe_layer* device_out,
+                        void* stream);
+
+/*
  * Router and exact top-k (definition at the top of this header).
  *   w_router fp32 [E][d]; bias nullable fp32 [E] (selection on the biased
  *   keys when given); x [T][d] in x_dtype; idx int32 [T][k] (rank order);

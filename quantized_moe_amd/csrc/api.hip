@@ -241,8 +241,9 @@ static int check_dtype(const char* fn, int x_dtype) {
   return MOE_OK;
 }
 
-// Checks every field of a layer that the compute paths read.
-static int check_layer(const char* fn, const moe_layer* L, bool need_router) {
+// Checks every field of a layer that the compute paths read (the weights in
+// `want_layout`: the compute entry points read only the device layout).
+static int check_layer(const char* fn, const moe_layer* L, bool need_router, int want_layout = MOE_LAYOUT_DEVICE) {
   if (!L) return fail(MOE_ERR_INVALID_ARG, "%s: layer is null", fn);
   if (L->abi_version != MOE_ABI_VERSION)
     return fail(MOE_ERR_UNSUPPORTED, "%s: layer abi_version %u, library speaks %d", fn, L->abi_version, MOE_ABI_VERSION);
@@ -251,9 +252,12 @@ static int check_layer(const char* fn, const moe_layer* L, bool need_router) {
   if (!pow2_in(L->d_ff, 256, 8192)) return fail(MOE_ERR_INVALID_ARG, "%s: d_ff %d is not a power of two in [256, 8192]", fn, L->d_ff);
   if (!fmt_known(L->fmt_gate_up)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown gate/up format %d", fn, L->fmt_gate_up);
   if (!fmt_known(L->fmt_down)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown down format %d", fn, L->fmt_down);
-  if (L->layout != MOE_LAYOUT_DEVICE) {
+  if (L->layout != want_layout) {
     if (L->layout == MOE_LAYOUT_CANONICAL)
-      return fail(MOE_ERR_UNSUPPORTED, "%s: weights must be in MOE_LAYOUT_DEVICE (convert with moe_repack)", fn);
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: weights must be in MOE_LAYOUT_DEVICE (convert with moe_prepare_weights or moe_repack)", fn);
+    if (L->layout == MOE_LAYOUT_DEVICE)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: the layer's weights are already in MOE_LAYOUT_DEVICE", fn);
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown layout %d", fn, L->layout);
   }
   if (L->has_shared != 0 && L->has_shared != 1) return fail(MOE_ERR_INVALID_ARG, "%s: has_shared must be 0 or 1", fn);
@@ -467,6 +471,67 @@ extern "C" int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t 
   hipError_t e = launch_repack(fmt, nb, src, dst, direction == MOE_REPACK_TO_DEVICE, s);
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+extern "C" int moe_prepare_weights(const moe_layer* canonical, moe_layer* device_out, void* stream) {
+  const char* fn = "moe_prepare_weights";
+  int rc = check_layer(fn, canonical, false, MOE_LAYOUT_CANONICAL);
+  if (rc) return rc;
+  if (!device_out) return fail(MOE_ERR_INVALID_ARG, "%s: device_out is null", fn);
+  const moe_layer& C = *canonical;
+  struct Job {
+    const char* name;
+    const void* src;
+    const void* dst;
+    int fmt, E, rows, K;
+  };
+  Job jobs[6] = {
+      {"w_gate", C.w_gate, device_out->w_gate, C.fmt_gate_up, C.n_experts, C.d_ff, C.d_model},
+      {"w_up", C.w_up, device_out->w_up, C.fmt_gate_up, C.n_experts, C.d_ff, C.d_model},
+      {"w_down", C.w_down, device_out->w_down, C.fmt_down, C.n_experts, C.d_model, C.d_ff},
+      {"s_gate", C.s_gate, device_out->s_gate, C.fmt_shared, 1, C.d_ff, C.d_model},
+      {"s_up", C.s_up, device_out->s_up, C.fmt_shared, 1, C.d_ff, C.d_model},
+      {"s_down", C.s_down, device_out->s_down, C.fmt_shared, 1, C.d_model, C.d_ff},
+  };
+  const int n_jobs = C.has_shared ? 6 : 3;
+  for (int i = 0; i < n_jobs; i++) {  // every destination, before anything is enqueued
+    const Job& j = jobs[i];
+    if (!j.dst) return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s is null", fn, j.name);
+    if (!aligned16(j.dst)) return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s is not 16-byte aligned", fn, j.name);
+    const size_t bytes = (size_t)j.E * j.rows * (j.K / block_weights(j.fmt)) * block_bytes(j.fmt);
+    const uintptr_t d0 = (uintptr_t)j.dst, d1 = d0 + bytes;
+    for (int k = 0; k < n_jobs; k++) {  // no destination may overlap a source or another destination
+      const Job& o = jobs[k];
+      const size_t ob = (size_t)o.E * o.rows * (o.K / block_weights(o.fmt)) * block_bytes(o.fmt);
+      const uintptr_t s0 = (uintptr_t)o.src, s1 = s0 + ob;
+      if (d0 < s1 && s0 < d1)
+        return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s overlaps the canonical %s", fn, j.name, o.name);
+      if (k != i) {
+        const uintptr_t t0 = (uintptr_t)o.dst, t1 = t0 + ob;
+        if (o.dst && d0 < t1 && t0 < d1)
+          return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s overlaps device_out->%s", fn, j.name, o.name);
+      }
+    }
+  }
+  hipStream_t s = (hipStream_t)stream;
+  for (int i = 0; i < n_jobs; i++) {
+    const Job& j = jobs[i];
+    const int64_t nb = (int64_t)j.E * j.rows * (j.K / block_weights(j.fmt));
+    const int pid = prof_begin("repack", s);
+    hipError_t e = launch_repack(j.fmt, nb, j.src, const_cast<void*>(j.dst), 1, s);
+    prof_end(pid, s);
+    if (e != hipSuccess) return hip_fail(e, fn);
+  }
+  moe_layer out = C;
+  out.layout = MOE_LAYOUT_DEVICE;
+  out.w_gate = jobs[0].dst;
+  out.w_up = jobs[1].dst;
+  out.w_down = jobs[2].dst;
+  out.s_gate = C.has_shared ? jobs[3].dst : nullptr;
+  out.s_up = C.has_shared ? jobs[4].dst : nullptr;
+  out.s_down = C.has_shared ? jobs[5].dst : nullptr;
+  *device_out = out;
   return ok();
 }
 

@@ -45,7 +45,6 @@ constexpr int XMAX = 0x7777;      // |X| bound of the fixed-point activations
 constexpr int G16_BYTES = 32;     // one quantized group of 16 activations (nibble or byte planes)
 constexpr int CHUNK_BYTES = 128;  // 64 activations (four groups)
 constexpr int DN_ROWS = 16;       // down rows per block of the last kernel
-constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
 // How the 16 activations of a group are stored (32 bytes), chosen per
 // consuming weight format so that weight words need no shuffling:

@@ -1,7 +1,6 @@
-// Row loops of the decode kernels, shared by the three-launch decode
-// (decode_k1/k2/k3.hip) and the single-launch decode (decode_fused.hip):
-// router logits of one expert, a wave's run of routed gate/up rows, and a
-// wave's down-projection rows.
+// Row loops of the three decode kernels (decode_k1/k2/k3.hip): router
+// logits of one expert, a wave's run of routed gate/up rows, and a wave's
+// down-projection rows.
 #pragma once
 
 #include "decode_common.hpp"

@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int),
             "moe_layer_forward_noalloc": ([ctypes.POINTER(MoeLayer), _P, _I32, _I32, _P, _P, _P, _I32, _P],
                                           ctypes.c_int),
+            "moe_prepare_weights": ([ctypes.POINTER(MoeLayer), ctypes.POINTER(MoeLayer), _P], ctypes.c_int),
             "moe_profile_enable": ([_I32], ctypes.c_int),
             "moe_profile_reset": ([], ctypes.c_int),
             "moe_profile_collect": ([_I32, _P, _P, _P, _P], ctypes.c_int),
@@ -152,6 +153,12 @@ def workspace_bytes(layer: MoeLayer, T: int, op: int) -> int:
 def repack(fmt, n_experts, rows, K, src: torch.Tensor, dst: torch.Tensor, direction=MOE_REPACK_TO_DEVICE,
            stream=None) -> None:
     _check(lib().moe_repack(fmt, n_experts, rows, K, _ptr(src), _ptr(dst), direction, _stream(stream)))
+
+
+def prepare_weights(canonical: MoeLayer, device_out: MoeLayer, stream=None) -> None:
+    """Whole-layer canonical -> device conversion into device_out's weight
+    buffers; device_out then describes the prepared layer."""
+    _check(lib().moe_prepare_weights(ctypes.byref(canonical), ctypes.byref(device_out), _stream(stream)))
 
 
 def route_topk(w_router, x, k, idx, wt, ws, stream=None, bias=None) -> None:
@@ -223,8 +230,9 @@ def _to_device_bytes(a: np.ndarray, device) -> torch.Tensor:
 class DeviceLayer:
     """A layer whose weights live on the GPU in the device layout.
 
-    Built from canonical bytes (host numpy arrays): each tensor is uploaded
-    and converted with moe_repack.  `.desc` is the moe_layer descriptor.
+    Built from canonical bytes (host numpy arrays): the tensors are uploaded
+    and the whole layer is converted with one moe_prepare_weights call.
+    `.desc` is the moe_layer descriptor of the prepared layer.
     """
 
     def __init__(self, E, d, f, k, fmt_gate_up, fmt_down, w_gate, w_up, w_down, grid, w_router,
@@ -232,39 +240,38 @@ class DeviceLayer:
                  router_bias=None, down_gain=None):
         self.E, self.d, self.f, self.k = E, d, f, k
         self.device = torch.device(device)
-        self.tensors = {}
-        self.tensors["w_gate"] = self._prep(fmt_gate_up, E, f, d, w_gate)
-        self.tensors["w_up"] = self._prep(fmt_gate_up, E, f, d, w_up)
-        self.tensors["w_down"] = self._prep(fmt_down, E, d, f, w_down)
+        has_shared = s_gate is not None
+        shapes = {"w_gate": (fmt_gate_up, E, f, d, w_gate), "w_up": (fmt_gate_up, E, f, d, w_up),
+                  "w_down": (fmt_down, E, d, f, w_down)}
+        if has_shared:
+            shapes.update({"s_gate": (fmt_shared, 1, f, d, s_gate), "s_up": (fmt_shared, 1, f, d, s_up),
+                           "s_down": (fmt_shared, 1, d, f, s_down)})
+        canon, self.tensors = {}, {}
+        for name, (fmt, n_e, rows, K, blob) in shapes.items():
+            n = matrix_bytes(fmt, n_e, rows, K)
+            if blob.size != n:
+                raise ValueError(f"{name}: expected {n} bytes, got {blob.size}")
+            canon[name] = _to_device_bytes(blob, self.device)
+            self.tensors[name] = torch.empty(n, dtype=torch.uint8, device=self.device)
         self.tensors["grid"] = _to_device_bytes(np.asarray(grid, np.uint8), self.device)
         self.tensors["w_router"] = torch.from_numpy(np.ascontiguousarray(w_router, np.float32)).to(self.device)
-        has_shared = s_gate is not None
-        if has_shared:
-            self.tensors["s_gate"] = self._prep(fmt_shared, 1, f, d, s_gate)
-            self.tensors["s_up"] = self._prep(fmt_shared, 1, f, d, s_up)
-            self.tensors["s_down"] = self._prep(fmt_shared, 1, d, f, s_down)
         if router_bias is not None:
             self.tensors["router_bias"] = torch.from_numpy(np.ascontiguousarray(router_bias, np.float32)).to(self.device)
         if down_gain is not None:
             self.tensors["down_gain"] = torch.from_numpy(np.ascontiguousarray(down_gain, np.float32)).to(self.device)
         t = self.tensors
-        self.desc = MoeLayer(
+        src = MoeLayer(
             abi_version=MOE_ABI_VERSION, n_experts=E, d_model=d, d_ff=f, top_k=k, fmt_gate_up=fmt_gate_up,
-            fmt_down=fmt_down, layout=MOE_LAYOUT_DEVICE, w_gate=_ptr(t["w_gate"]), w_up=_ptr(t["w_up"]),
-            w_down=_ptr(t["w_down"]), iq2_grid=_ptr(t["grid"]), w_router=_ptr(t["w_router"]),
-            has_shared=1 if has_shared else 0, fmt_shared=fmt_shared if has_shared else 0,
-            s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")),
+            fmt_down=fmt_down, layout=MOE_LAYOUT_CANONICAL, w_gate=_ptr(canon["w_gate"]),
+            w_up=_ptr(canon["w_up"]), w_down=_ptr(canon["w_down"]), iq2_grid=_ptr(t["grid"]),
+            w_router=_ptr(t["w_router"]), has_shared=1 if has_shared else 0,
+            fmt_shared=fmt_shared if has_shared else 0, s_gate=_ptr(canon.get("s_gate")),
+            s_up=_ptr(canon.get("s_up")), s_down=_ptr(canon.get("s_down")),
             router_bias=_ptr(t.get("router_bias")), down_gain=_ptr(t.get("down_gain")))
-        torch.cuda.synchronize(self.device)
-
-    def _prep(self, fmt, E, rows, K, canonical: np.ndarray) -> torch.Tensor:
-        n = matrix_bytes(fmt, E, rows, K)
-        if canonical.size != n:
-            raise ValueError(f"expected {n} bytes, got {canonical.size}")
-        src = _to_device_bytes(canonical, self.device)
-        dst = torch.empty(n, dtype=torch.uint8, device=self.device)
-        repack(fmt, E, rows, K, src, dst, MOE_REPACK_TO_DEVICE)
-        return dst
+        self.desc = MoeLayer(w_gate=_ptr(t["w_gate"]), w_up=_ptr(t["w_up"]), w_down=_ptr(t["w_down"]),
+                             s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")))
+        prepare_weights(src, self.desc)
+        torch.cuda.synchronize(self.device)  # the canonical copies are freed on return
 
     @classmethod
     def from_synth(cls, L, device="cuda"):

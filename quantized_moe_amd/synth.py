@@ -8,8 +8,9 @@ the method itself would draw do not exist here (the layer is deterministic).
 Workloads (the pages print no test vectors; every workload is synthetic):
 
 * ``tiny``      E=8, k=2, d=256, f=512, T=4, fp32 x.  Its weights are
-                N(0, 0.02) floats that the test oracle's quantizer encodes;
-                this module supplies only those floats (``gaussian``).
+                N(0, 0.02) floats (``gaussian``) encoded by the data-generation
+                quantizers at the end of this module (``quantize_q2k`` and
+                friends: offline encoders the layer never runs).
 * ``decode``    E=384, k=6, d=4096, f=2048, T=1, fp32 x; gate/up IQ2XXS_L,
                 down Q2K_L, shared expert Q8_0_L, all random valid codes.
                 DeepSeek V4.1 Flash has 384 experts per layer and routes 6

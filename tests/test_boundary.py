@@ -159,6 +159,30 @@ def test_prefill_offset_limit_is_checked_before_any_launch():
     assert _forward(_layer(d_model=8192, top_k=16, d_ff=2048), T=65536, ws_bytes=ws) == lib.MOE_ERR_INVALID_ARG
 
 
+def test_prepare_weights_validation():
+    """moe_prepare_weights validates the canonical layer and every
+    destination before its first launch; the fake pointers are never used."""
+    L = lib.lib()
+    canon = _layer(layout=lib.MOE_LAYOUT_CANONICAL, w_gate=1 << 40, w_up=2 << 40, w_down=3 << 40,
+                   s_gate=4 << 40, s_up=5 << 40, s_down=6 << 40)
+    dst = lib.MoeLayer(w_gate=7 << 40, w_up=8 << 40, w_down=9 << 40, s_gate=10 << 40, s_up=11 << 40, s_down=0)
+    assert L.moe_prepare_weights(ctypes.byref(canon), ctypes.byref(dst), None) == lib.MOE_ERR_INVALID_ARG
+    assert "s_down" in lib.last_error()
+    assert dst.layout == 0 and dst.n_experts == 0  # left unchanged
+    dst.s_down = (12 << 40) + 8  # misaligned
+    assert L.moe_prepare_weights(ctypes.byref(canon), ctypes.byref(dst), None) == lib.MOE_ERR_INVALID_ARG
+    dst.s_down = (1 << 40) + 4096  # inside the canonical w_gate
+    assert L.moe_prepare_weights(ctypes.byref(canon), ctypes.byref(dst), None) == lib.MOE_ERR_INVALID_ARG
+    assert "overlaps" in lib.last_error()
+    dst.s_down = (9 << 40) + 256  # inside another destination
+    assert L.moe_prepare_weights(ctypes.byref(canon), ctypes.byref(dst), None) == lib.MOE_ERR_INVALID_ARG
+    dev = _layer()  # already in the device layout
+    assert L.moe_prepare_weights(ctypes.byref(dev), ctypes.byref(dst), None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_prepare_weights(ctypes.byref(_layer(layout=lib.MOE_LAYOUT_CANONICAL, fmt_down=9)),
+                                 ctypes.byref(dst), None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_prepare_weights(ctypes.byref(canon), None, None) == lib.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_sizes_cover_their_buffers():
     layer = _layer()
     E, d, f, k = 384, 4096, 2048, 6
