@@ -186,10 +186,14 @@ extern "C" {
 #define MOE_OP_LAYER 3   /* moe_layer_forward, either path */
 
 /* Path choice for moe_layer_forward. */
-#define MOE_PATH_AUTO 0    /* decode path for T <= MOE_DECODE_MAX_T, else prefill */
+#define MOE_PATH_AUTO 0    /* decode path for T <= MOE_AUTO_DECODE_MAX_T, else prefill */
 #define MOE_PATH_DECODE 1  /* streaming GEMV path (T <= MOE_DECODE_MAX_T only) */
 #define MOE_PATH_PREFILL 2 /* bucketing + grouped MFMA GEMM path */
 #define MOE_DECODE_MAX_T 8
+/* Where MOE_PATH_AUTO switches to prefill: the largest T at which the decode
+ * path measured faster than the prefill path on the 384-expert, top-6,
+ * d=4096, f=2048 layer (bench.py, crossover). */
+#define MOE_AUTO_DECODE_MAX_T 8
 
 /* moe_repack directions. */
 #define MOE_REPACK_TO_DEVICE 0

@@ -60,6 +60,7 @@ def lib():
         L.orc_bias_keys.argtypes = [P, I, I, P, P]
         L.orc_ffn.restype = I
         L.orc_threads.restype = I
+        L.orc_set_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -78,6 +79,10 @@ def _x(x, x_dtype):
 
 def threads() -> int:
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
 
 
 def half(bits: int) -> float:

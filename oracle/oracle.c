@@ -557,6 +557,10 @@ void orc_route(const void* x, int x_dtype, int T, int d, const float* W, int E, 
   orc_route_weights(z, idx, T, E, k, wt);
 }
 
+/* Threads for the parallel regions that follow (n >= 1); bench uses it for
+ * a single-thread rate beside the all-cores one. */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* Number of OpenMP threads a parallel region would use (reported by bench). */
 int orc_threads(void) {
   int n = 1;

@@ -15,11 +15,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libqmoe.so")
+PROBE_OUT = os.path.join(HERE, "libqmoe_probe.so")  # measurement probes (not the layer's ABI)
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "bucket.hip", "repack.hip", "decode.hip", "decode_k1.hip", "decode_k2.hip",
            "decode_k3.hip", "prefill.hip"]
+PROBE_SOURCES = ["probe.hip"]
 # packed-fp32 VALU forms are disabled: only ordinary fp32 instructions
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
@@ -39,18 +41,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(9, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = ["hipcc", "-shared", "-o", tmp, f"--offload-arch={ARCH}"] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(10, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PROBE_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

@@ -391,7 +391,7 @@ size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
 }  // namespace
 
 static int resolve_path(int path, int T) {
-  if (path == MOE_PATH_AUTO) return T <= DECODE_MAX_T ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  if (path == MOE_PATH_AUTO) return T <= AUTO_DECODE_MAX_T ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   return path;
 }
 
@@ -443,7 +443,7 @@ extern "C" int moe_workspace_bytes(const moe_layer* L, int32_t T, int32_t op, si
     case MOE_OP_PREFILL: *bytes = ws_prefill(E, T, k, d, f, sh); break;
     case MOE_OP_LAYER: {
       size_t b = ws_layer(E, T, k, d, f, sh, MOE_PATH_PREFILL);
-      if (T <= DECODE_MAX_T) {
+      if (T <= AUTO_DECODE_MAX_T) {
         const size_t b2 = ws_layer(E, T, k, d, f, sh, MOE_PATH_DECODE);
         if (b2 > b) b = b2;
       }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "moe.h"
 
 namespace qmoe {
 
@@ -14,7 +15,8 @@ constexpr int MAX_EXPERTS = 1024;
 constexpr int TOPK_MAX_K = 16;
 constexpr int TOPK_MAX_PER_LANE = MAX_EXPERTS / 64;
 constexpr int ROUTER_ROWS_MAX_T = 16;  // above this the tiled router runs
-constexpr int DECODE_MAX_T = 8;
+constexpr int DECODE_MAX_T = MOE_DECODE_MAX_T;            // the decode path's limit
+constexpr int AUTO_DECODE_MAX_T = MOE_AUTO_DECODE_MAX_T;  // MOE_PATH_AUTO's switch to prefill
 
 // Per-kernel timing hooks (api.hip).  When profiling is enabled, prof_begin
 // creates a start/stop event pair for the one launch that follows and hands it
