@@ -23,9 +23,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-IQ2, Q2K, Q8, Q4K = 1, 2, 3, 4
-_BW = {IQ2: 256, Q2K: 256, Q8: 32, Q4K: 256}
-_BB = {IQ2: 66, Q2K: 84, Q8: 34, Q4K: 144}
+IQ2, Q2K, Q8, Q4K, MX4 = 1, 2, 3, 4, 5
+_BW = {IQ2: 256, Q2K: 256, Q8: 32, Q4K: 256, MX4: 32}
+_BB = {IQ2: 66, Q2K: 84, Q8: 34, Q4K: 144, MX4: 17}
 
 _lib = None
 

@@ -45,6 +45,7 @@
 #define ORC_Q2K 2
 #define ORC_Q8 3
 #define ORC_Q4K 4
+#define ORC_MX4 5
 
 /* ---------------------------------------------------------------------- */
 /* scalar decoding of stored numbers                                      */
@@ -295,20 +296,46 @@ static void deq_q4k(const uint8_t* b, double* w) {
   }
 }
 
+/*
+ * MXFP4_L block (the native MXFP4 routed experts of "Running DeepSeek V4
+ * Flash on an RTX 5080 ...", model section: FP4 values with one shared
+ * scale per 32 weights, 4.25 bits per weight as the YoungAi page, section
+ * 4.1, counts them), 32 weights in 17 bytes: byte 0 is an E8M0 scale, the
+ * power of two 2^(s - 127); bytes 1..16 hold E2M1 codes, weight 2i in the
+ * low nibble of byte 1 + i and weight 2i + 1 in the high nibble.
+ * An E2M1 code has a sign bit (bit 3), a 2-bit exponent E (bits 2..1) and a
+ * 1-bit mantissa M (bit 0): |value| = M / 2 when E = 0 (subnormal), else
+ * (1 + M / 2) * 2^(E - 1).  w = 2^(s - 127) * value.  (s = 255, the E8M0
+ * not-a-number, is not a valid block.)
+ */
+static double e2m1(int c) {
+  int E = (c >> 1) & 3, M = c & 1;
+  double mag = E == 0 ? 0.5 * M : (1.0 + 0.5 * M) * ldexp(1.0, E - 1);
+  return (c & 8) ? -mag : mag;
+}
+
+static void deq_mx4(const uint8_t* b, double* w) {
+  double scale = ldexp(1.0, (int)b[0] - 127);
+  for (int i = 0; i < 32; i++) {
+    int c = (b[1 + i / 2] >> (4 * (i % 2))) & 15;
+    w[i] = scale * e2m1(c);
+  }
+}
+
 /* Q8_0_L block, 32 weights in 34 bytes: fp16 d then int8 q[32]; w = d q. */
 static void deq_q8(const uint8_t* b, double* w) {
   double d = orc_half(rd16(b));
   for (int i = 0; i < 32; i++) w[i] = d * (double)(int8_t)b[2 + i];
 }
 
-static int block_weights(int fmt) { return fmt == ORC_Q8 ? 32 : 256; }
+static int block_weights(int fmt) { return fmt == ORC_Q8 || fmt == ORC_MX4 ? 32 : 256; }
 static int block_bytes(int fmt) {
-  return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : fmt == ORC_Q4K ? 144 : 34;
+  return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : fmt == ORC_Q4K ? 144 : fmt == ORC_MX4 ? 17 : 34;
 }
 
 /* Decode n_blocks consecutive blocks of `fmt` into fp64. Returns 0 on success. */
 int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t* grid, double* out) {
-  if (fmt != ORC_IQ2 && fmt != ORC_Q2K && fmt != ORC_Q8 && fmt != ORC_Q4K) return -1;
+  if (fmt != ORC_IQ2 && fmt != ORC_Q2K && fmt != ORC_Q8 && fmt != ORC_Q4K && fmt != ORC_MX4) return -1;
   int bw = block_weights(fmt), bb = block_bytes(fmt);
   for (int64_t i = 0; i < n_blocks; i++) {
     const uint8_t* b = blocks + i * bb;
@@ -319,6 +346,8 @@ int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t*
       deq_q2k(b, w);
     else if (fmt == ORC_Q4K)
       deq_q4k(b, w);
+    else if (fmt == ORC_MX4)
+      deq_mx4(b, w);
     else
       deq_q8(b, w);
   }

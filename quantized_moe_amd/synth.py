@@ -36,9 +36,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8, FMT_Q4K = 0, 1, 2, 3, 4
-BLOCK_WEIGHTS = {FMT_IQ2: 256, FMT_Q2K: 256, FMT_Q8: 32, FMT_Q4K: 256}
-BLOCK_BYTES = {FMT_IQ2: 66, FMT_Q2K: 84, FMT_Q8: 34, FMT_Q4K: 144}
+FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8, FMT_Q4K, FMT_MX4 = 0, 1, 2, 3, 4, 5
+BLOCK_WEIGHTS = {FMT_IQ2: 256, FMT_Q2K: 256, FMT_Q8: 32, FMT_Q4K: 256, FMT_MX4: 32}
+BLOCK_BYTES = {FMT_IQ2: 66, FMT_Q2K: 84, FMT_Q8: 34, FMT_Q4K: 144, FMT_MX4: 17}
 
 F32, BF16 = 0, 1
 
@@ -139,6 +139,17 @@ def pack_q4k(d: np.ndarray, dmin: np.ndarray, sc: np.ndarray, m: np.ndarray, q: 
     return out
 
 
+def pack_mx4(e: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """MXFP4_L blocks.  e uint8 [nb] (E8M0 scale exponents, 0..254); codes
+    uint8 [nb, 32] (E2M1 codes 0..15); returns uint8 [nb, 17]."""
+    nb = e.shape[0]
+    out = np.empty((nb, 17), dtype=np.uint8)
+    out[:, 0] = e.astype(np.uint8)
+    c = codes.reshape(nb, 16, 2).astype(np.uint8) & 15
+    out[:, 1:17] = c[:, :, 0] | (c[:, :, 1] << 4)
+    return out
+
+
 def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
     """Q8_0_L blocks.  d float16 [nb]; q int8 [nb, 32]; returns uint8 [nb, 34]."""
     nb = d.shape[0]
@@ -160,7 +171,10 @@ def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
 #   Q8 : q ~ U{-128..127}, std ~ 73.9  ->  d ~ 2.7e-4
 #   Q4K: sc, m ~ U{0..63}, q ~ U{0..15}; dmin = 7.5 d centres the weights;
 #        var = var(sc q) + 7.5^2 var(m) = 47532 + 19195 -> std 258 d -> d ~ 7.74e-5
+#   MX4: E2M1 codes ~ U{0..15}: E[v^2] = 8.5625 -> std 2.93; the E8M0
+#        exponent drawn from {119, 120} (scale 2^-8 or 2^-7): std ~ 0.018
 IQ2_D, Q2K_D, Q8_D, Q4K_D = 2.36e-4, 1.35e-3, 2.7e-4, 7.74e-5
+MX4_E = 120
 
 
 def _rand_scale(rng, nb, base):
@@ -214,7 +228,16 @@ def random_q8(rng: np.random.Generator, nb: int) -> np.ndarray:
     return out
 
 
-RANDOM_CODES = {FMT_IQ2: random_iq2, FMT_Q2K: random_q2k, FMT_Q8: random_q8, FMT_Q4K: random_q4k}
+def random_mx4(rng: np.random.Generator, nb: int) -> np.ndarray:
+    """Random MXFP4_L blocks: uniform E2M1 codes, scale exponent MX4_E - 1
+    or MX4_E."""
+    out = _random_blocks(rng, nb, 17)
+    out[:, 0] = (MX4_E + rng.integers(-1, 1, size=nb)).astype(np.uint8)
+    return out
+
+
+RANDOM_CODES = {FMT_IQ2: random_iq2, FMT_Q2K: random_q2k, FMT_Q8: random_q8, FMT_Q4K: random_q4k,
+                FMT_MX4: random_mx4}
 
 
 def matrix_bytes(fmt: int, n_experts: int, rows: int, K: int) -> int:
@@ -436,6 +459,26 @@ def quantize_q8(w: np.ndarray) -> np.ndarray:
     d = (np.abs(w).max(axis=1) / 127.0).astype(np.float16)
     q = np.clip(np.rint(_safe_div(w, d.astype(np.float64)[:, None])), -127, 127).astype(np.int8)
     return pack_q8(d, q)
+
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # magnitudes of codes 0..7 (OCP MX)
+
+
+def quantize_mx4(w: np.ndarray) -> np.ndarray:
+    """Float weights [nb * 32] -> MXFP4_L blocks [nb, 17]: the scale is the
+    smallest power of two 2^k with max|w| / 2^k <= 6 (k clamped to the E8M0
+    range), each weight takes the nearest E2M1 magnitude of |w| / 2^k (ties
+    to the even code) and the sign of w (zero keeps code 0)."""
+    w = np.asarray(w, dtype=np.float64).reshape(-1, 32)
+    nb = w.shape[0]
+    amax = np.abs(w).max(axis=1)
+    k = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 6.0)), 0).astype(np.int64)
+    k = np.clip(k, -127, 127)
+    v = np.abs(w) / np.exp2(k)[:, None]
+    dist = np.abs(v[:, :, None] - E2M1_GRID[None, None, :])
+    best = np.argmin(dist + 1e-12 * (np.arange(8) % 2)[None, None, :], axis=2)  # ties: even code
+    codes = best.astype(np.uint8) | np.where((w < 0) & (best > 0), 8, 0).astype(np.uint8)
+    return pack_mx4((k + 127).astype(np.uint8), codes)
 
 
 def quantize_iq2(w: np.ndarray, grid: np.ndarray) -> np.ndarray:

@@ -136,6 +136,49 @@ def test_q8_worked_blocks():
     assert np.array_equal(synth.pack_q8(np.array([0.5], np.float16), q[None]).reshape(-1), _bytes(g[0]["hex"]))
 
 
+def test_mx4_worked_blocks_and_packer():
+    """MXFP4 blocks worked by hand from the OCP MX definition of E2M1 (the
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) and E8M0 (2^(s - 127)), including
+    both ends of the scale range."""
+    g = {b["name"]: b for b in _golden()["mx4_blocks"]}
+    for name in ("mx4_a", "mx4_b"):
+        w = oracle.dequant(oracle.MX4, _bytes(g[name]["hex"]))
+        assert np.array_equal(w, np.array(g[name]["weights"]))
+    a = oracle.dequant(oracle.MX4, _bytes(g["mx4_a"]["hex"]))
+    assert np.array_equal(np.signbit(a[:16]), np.arange(16) >= 8)  # code 8 is -0
+    assert np.all(oracle.dequant(oracle.MX4, _bytes(g["mx4_c"]["hex"])) == 2.0 ** g["mx4_c"]["weights_log2"])
+    assert np.all(oracle.dequant(oracle.MX4, _bytes(g["mx4_d"]["hex"])) == g["mx4_d"]["weights_times_2_pow_minus_127"] * 2.0 ** 127)
+    codes = np.tile(np.arange(16, dtype=np.uint8), 2)[None]
+    assert np.array_equal(synth.pack_mx4(np.array([127], np.uint8), codes).reshape(-1), _bytes(g["mx4_a"]["hex"]))
+
+
+def test_mx4_round_trip_and_error_bound():
+    """Blocks whose weights lie on the E2M1 grid times a power of two survive
+    quantize -> dequantize exactly; Gaussian blocks round to the nearest grid
+    point: error at most half the grid gap around the value (0.25, 0.5 or 1
+    times the block scale)."""
+    rng = np.random.default_rng(11)
+    nb = 64
+    k = rng.integers(-20, 5, nb)
+    codes = rng.integers(0, 16, (nb, 32))
+    vals = synth.E2M1_GRID[codes & 7] * np.where(codes >= 8, -1.0, 1.0)
+    w = (vals * np.exp2(k)[:, None]).reshape(-1)
+    assert np.array_equal(oracle.dequant(oracle.MX4, synth.quantize_mx4(w)), w)
+    g = rng.normal(0, 0.02, 32 * 256)
+    blocks = synth.quantize_mx4(g)
+    back = oracle.dequant(oracle.MX4, blocks).reshape(-1, 32)
+    scale = np.exp2(blocks[:, 0].astype(np.float64) - 127)[:, None]
+    v = np.abs(g.reshape(-1, 32)) / scale
+    assert np.all(v <= 6.0 + 1e-12)
+    gap = np.where(v < 2, 0.25, np.where(v < 4, 0.5, 1.0))
+    assert np.all(np.abs(back - g.reshape(-1, 32)) <= gap * scale * (1 + 1e-12))
+
+
+def test_mx4_random_codes_spread():
+    w = oracle.dequant(oracle.MX4, synth.random_mx4(np.random.default_rng(12), 8192))
+    assert abs(w.mean()) < 3e-4 and 0.015 < w.std() < 0.022
+
+
 # ---------------------------------------------------- formats: round trip ----
 def test_q2k_round_trip_exact_on_representable_blocks():
     rng = np.random.default_rng(1)
@@ -511,6 +554,7 @@ def _numpy_ffn(L, x, idx, wt):
     synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_IQ2,
                       fmt_shared=synth.FMT_Q2K),
     synth.scaled_spec(E=5, k=2, d=512, f=256, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q4K),
+    synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4),
 ])
 def test_ffn_matches_numpy_dense_matmul(spec):
     L = synth.random_layer(spec, seed=3, workload="pin")
@@ -527,6 +571,7 @@ def test_ffn_matches_numpy_dense_matmul(spec):
                        fmt_shared=synth.FMT_Q2K), True),
     (synth.scaled_spec(E=7, k=4, d=256, f=256, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q2K,
                        has_shared=False), True),
+    (synth.scaled_spec(E=6, k=3, d=512, f=256, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4), False),
 ])
 def test_grouped_ffn_is_bitwise_the_token_loop(spec, gains):
     """The expert-grouped evaluation (each expert dequantised once) performs
