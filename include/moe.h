@@ -101,6 +101,17 @@
  * MOE_FMT_Q8_0_L -- 32 weights in 34 bytes (8.5 bits per weight):
  *   bytes 0-1 d (fp16), bytes 2..33 int8 q[32];  w_i = d * q_i.
  *
+ * MOE_FMT_MXFP4_L -- 32 weights in 17 bytes (4.25 bits per weight), the
+ *   native MXFP4 routed experts ("Running DeepSeek V4 Flash on an RTX 5080
+ *   ...", model section: FP4 values with one shared scale per 32 weights);
+ *   routed gate/up and down only, not the shared expert:
+ *   byte 0       E8M0 scale exponent s (0..254): scale = 2^(s - 127),
+ *   bytes 1..16  E2M1 codes: code_i = (byte[1 + i/2] >> (4 (i % 2))) & 15;
+ *                bit 3 is the sign, bits 2..1 the exponent E, bit 0 the
+ *                mantissa M: |value| = M/2 for E = 0, else (1 + M/2) 2^(E-1)
+ *                (0, 0.5, 1, 1.5, 2, 3, 4, 6),
+ *   w_i = 2^(s - 127) * value(code_i).
+ *
  * Device layout (MOE_LAYOUT_DEVICE).  The compute entry points read weights
  * only in this layout, produced from the canonical one by moe_repack (the
  * map is a bijection on bytes and the total size is unchanged).  Every
@@ -117,8 +128,10 @@
  *              plane Q  quant bytes[R][nb][128]
  *   Q8_0_L   : plane D  fp16 d[R][nb]                 (2 R nb bytes), then
  *              plane Q  int8 q[R][nb][32]
+ *   MXFP4_L  : plane S  E8M0 s[R][nb]                 (R nb bytes), then
+ *              plane Q  codes[R][nb][16]
  *   (nb counts 256-weight superblocks for IQ2XXS_L/Q2K_L/Q4K_L and 32-weight
- *   blocks for Q8_0_L.)  Plane offsets follow from R and nb alone.
+ *   blocks for Q8_0_L and MXFP4_L.)  Plane offsets follow from R and nb alone.
  * -------------------------------------------------------------------------
  *
  * Conventions for every entry point:
@@ -173,7 +186,8 @@ extern "C" {
 #define MOE_FMT_IQ2XXS_L 1
 #define MOE_FMT_Q2K_L 2
 #define MOE_FMT_Q8_0_L 3
-#define MOE_FMT_Q4K_L 4  /* routed experts only */
+#define MOE_FMT_Q4K_L 4    /* routed experts only */
+#define MOE_FMT_MXFP4_L 5  /* routed experts only */
 
 /* Weight layouts. */
 #define MOE_LAYOUT_CANONICAL 0
@@ -202,8 +216,8 @@ extern "C" {
 /*
  * One MoE layer.  [host] struct; the weight pointers are device pointers to
  * tensors in `layout`.  Compute entry points require MOE_LAYOUT_DEVICE.
- * Routed gate/up may be IQ2XXS_L, Q2K_L or Q8_0_L; down may be Q2K_L,
- * IQ2XXS_L or Q8_0_L; the shared expert (if present) uses fmt_shared for its
+ * Routed gate/up and down may each be any of the formats above; the shared
+ * expert (if present) uses fmt_shared (IQ2XXS_L, Q2K_L or Q8_0_L) for its
  * three matrices and has d_ff rows in gate/up like the routed experts.
  * iq2_grid is required whenever any matrix is IQ2XXS_L.
  */

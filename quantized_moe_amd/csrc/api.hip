@@ -203,7 +203,8 @@ extern "C" int moe_profile_collect(int32_t max_kernels, char* names, int64_t* la
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 static bool fmt_known(int f) {
-  return f == MOE_FMT_IQ2XXS_L || f == MOE_FMT_Q2K_L || f == MOE_FMT_Q8_0_L || f == MOE_FMT_Q4K_L;
+  return f == MOE_FMT_IQ2XXS_L || f == MOE_FMT_Q2K_L || f == MOE_FMT_Q8_0_L || f == MOE_FMT_Q4K_L ||
+         f == MOE_FMT_MXFP4_L;
 }
 
 #define NEED_PTR(p, what)                                                                       \
@@ -267,8 +268,9 @@ static int check_layer(const char* fn, const moe_layer* L, bool need_router, int
   bool iq2 = L->fmt_gate_up == MOE_FMT_IQ2XXS_L || L->fmt_down == MOE_FMT_IQ2XXS_L;
   if (L->has_shared) {
     if (!fmt_known(L->fmt_shared)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown shared format %d", fn, L->fmt_shared);
-    if (L->fmt_shared == MOE_FMT_Q4K_L)
-      return fail(MOE_ERR_UNSUPPORTED, "%s: Q4K_L is a routed-expert format (shared expert: IQ2XXS_L, Q2K_L or Q8_0_L)", fn);
+    if (L->fmt_shared == MOE_FMT_Q4K_L || L->fmt_shared == MOE_FMT_MXFP4_L)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: Q4K_L and MXFP4_L are routed-expert formats (shared expert: IQ2XXS_L, Q2K_L or Q8_0_L)", fn);
     NEED_PTR(L->s_gate, "s_gate");
     NEED_PTR(L->s_up, "s_up");
     NEED_PTR(L->s_down, "s_down");

@@ -9,12 +9,12 @@
 namespace qmoe {
 
 enum : int { X_F32 = 0, X_BF16 = 1 };
-enum : int { FMT_IQ2 = 1, FMT_Q2K = 2, FMT_Q8 = 3, FMT_Q4K = 4 };
+enum : int { FMT_IQ2 = 1, FMT_Q2K = 2, FMT_Q8 = 3, FMT_Q4K = 4, FMT_MX4 = 5 };
 
 // Weights per block and bytes per block of each format (canonical layout).
-__host__ __device__ constexpr int block_weights(int fmt) { return fmt == FMT_Q8 ? 32 : 256; }
+__host__ __device__ constexpr int block_weights(int fmt) { return fmt == FMT_Q8 || fmt == FMT_MX4 ? 32 : 256; }
 __host__ __device__ constexpr int block_bytes(int fmt) {
-  return fmt == FMT_IQ2 ? 66 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : 34;
+  return fmt == FMT_IQ2 ? 66 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : fmt == FMT_MX4 ? 17 : 34;
 }
 // Scale bytes per superblock of the two K-quant formats (sub-block scales and mins).
 __host__ __device__ constexpr int kq_scale_bytes(int fmt) { return fmt == FMT_Q4K ? 12 : 16; }
@@ -29,6 +29,7 @@ __host__ __device__ constexpr int kq_quant_bytes(int fmt) { return fmt == FMT_Q4
 //   Q4K: p_scale = {fp16 d, dmin}[R][nb],    p_a = scale bytes[R][nb][12],
 //        p_b = quants[R][nb][128]
 //   Q8 : p_scale = fp16 d[R][nb],            p_a = int8 q[R][nb][32]
+//   MX4: p_scale = E8M0 e[R][nb],            p_a = E2M1 codes[R][nb][16]
 struct QMat {
   const uint8_t* p_scale;
   const uint8_t* p_a;
@@ -58,6 +59,9 @@ inline QMat make_qmat(const void* base, int fmt, int n_experts, int rows, int K)
   } else if (fmt == FMT_Q4K) {
     m.p_a = b + R * nb * 4;
     m.p_b = b + R * nb * 16;
+  } else if (fmt == FMT_MX4) {
+    m.p_a = b + R * nb;
+    m.p_b = nullptr;
   } else {
     m.p_a = b + R * nb * 2;
     m.p_b = nullptr;

@@ -60,7 +60,7 @@ enum : int { NIB_NAT = 0, NIB_Q2K = 1, Q8_BYTES = 2 };
 constexpr int Q8_XMAX = 32512;  // |X| bound of the byte-plane activations
 
 __host__ __device__ constexpr int nib_layout(int fmt) {
-  return fmt == FMT_Q2K ? NIB_Q2K : (fmt == FMT_Q8 ? Q8_BYTES : NIB_NAT);
+  return fmt == FMT_Q2K ? NIB_Q2K : (fmt == FMT_Q8 || fmt == FMT_MX4 ? Q8_BYTES : NIB_NAT);
 }
 
 // A row of K inputs in format FMT: 16-byte pieces, lanes per row, pieces per
@@ -68,7 +68,7 @@ __host__ __device__ constexpr int nib_layout(int fmt) {
 // LPR reads pieces c + LPR * k (k < CPL) of row sub of the step.
 template <int FMT, int K>
 struct Geo {
-  static constexpr int PW = FMT == FMT_Q8 ? 16 : 64;  // inputs per piece
+  static constexpr int PW = FMT == FMT_Q8 ? 16 : FMT == FMT_MX4 ? 32 : 64;  // inputs per piece
   static constexpr int PR = K / PW;                   // pieces per row
   static constexpr int LPR = PR < 64 ? PR : 64;
   static constexpr int CPL = PR / LPR;
@@ -464,6 +464,38 @@ struct ActQ8B {
   }
 };
 
+// MXFP4 pieces (32 inputs = two groups of 16) as the two signed byte planes
+// H, L of each group (layout Q8_BYTES, natural order), one scale per group
+// (group-quantized h) or per 64-input chunk (x).
+template <int CPL>
+struct ActMx4 {
+  uint32_t H[CPL][8], L[CPL][8];
+  float s[CPL][2];
+  // pieces c + LPR k of groups at q; GSCALE: 16 for group-quantized h, 64
+  // for chunk-quantized x
+  template <int LPR, int GSCALE>
+  __device__ __forceinline__ void load(const uint8_t* q, const float* sc, int c) {
+#pragma unroll
+    for (int k = 0; k < CPL; k++) {
+      const int g0 = 2 * (c + LPR * k);
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const uint4 hv = ld16(q + (int64_t)(g0 + j) * G16_BYTES);
+        const uint4 lv = ld16(q + (int64_t)(g0 + j) * G16_BYTES + 16);
+        H[k][4 * j] = hv.x;
+        H[k][4 * j + 1] = hv.y;
+        H[k][4 * j + 2] = hv.z;
+        H[k][4 * j + 3] = hv.w;
+        L[k][4 * j] = lv.x;
+        L[k][4 * j + 1] = lv.y;
+        L[k][4 * j + 2] = lv.z;
+        L[k][4 * j + 3] = lv.w;
+        s[k][j] = sc[GSCALE == 16 ? g0 + j : (g0 + j) / 4];
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // weight pieces: one lane's 16 bytes of codes of one row plus its scales
 // ---------------------------------------------------------------------------
@@ -504,6 +536,10 @@ __device__ __forceinline__ EPlanes expert_planes(const QMat& m, int e) {
     p.scale = m.p_scale + r * 4;
     p.a = m.p_a + r * 12;
     p.b = m.p_b + r * 128;
+  } else if constexpr (FMT == FMT_MX4) {
+    p.scale = m.p_scale + r;
+    p.a = m.p_a + r * 16;
+    p.b = nullptr;
   } else {
     p.scale = m.p_scale + r * 2;
     p.a = m.p_a + r * 32;
@@ -604,13 +640,33 @@ struct Piece<FMT_Q8> {  // 16 int8 quants: half of block pc / 2
   }
 };
 
+// MXFP4: a piece is one block, 32 E2M1 codes (two per byte, the even weight
+// in the low nibble), with its E8M0 scale byte.
+template <>
+struct Piece<FMT_MX4> {
+  uint4 q;
+  uint32_t e;
+  template <int NB>
+  __device__ __forceinline__ void load(const EPlanes& p, uint32_t row, uint32_t pc) {
+    q = ld16_stream(p.a + (row * NB + pc) * 16);
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_global(const EPlanes& p, uint32_t row, uint32_t pc) {
+    e = p.scale[row * NB + pc];
+  }
+  template <int NB>
+  __device__ __forceinline__ void scales_lds(const uint8_t* rp, uint32_t pc) {
+    e = rp[pc];
+  }
+};
+
 // Scale bytes of one row in format FMT with K inputs, as staged in LDS.
 template <int FMT, int K>
 struct RowScales {
   static constexpr int NB = K / block_weights(FMT);
   static constexpr bool KQ = FMT == FMT_Q2K || FMT == FMT_Q4K;
   static constexpr int DM = KQ ? NB * 4 : 0;                                  // K-quant (d, dmin) pairs
-  static constexpr int BYTES = KQ ? NB * (4 + kq_scale_bytes(FMT)) : NB * 2;  // + sub-block scales
+  static constexpr int BYTES = KQ ? NB * (4 + kq_scale_bytes(FMT)) : NB * (FMT == FMT_MX4 ? 1 : 2);  // + sub-block scales
   static constexpr bool STAGE = (BYTES % 16) == 0 && (DM % 16) == 0;    // whole 16-byte chunks
 };
 
@@ -801,6 +857,44 @@ __device__ __forceinline__ float piece_dot(const Piece<FMT_Q4K>& w, const ActNib
     return fm * d - fn * dmin;
   else
     return a.s[k][0] * ((float)im * d - (float)in * dmin);
+}
+
+// Four E2M1 codes (one per byte, 0..15) -> four int8 values 2 w (exact
+// integers: 0, 1, 2, 3, 4, 6, 8, 12 with the sign of bit 3).  Two byte
+// permutes look the magnitude up in the positive and in the negative table
+// (bytes 0..3 of the second operand, 4..7 of the first); a bitfield select
+// keeps the negative entry where bit 3 is set.
+__device__ __forceinline__ uint32_t mx4_bytes(uint32_t n) {
+  const uint32_t m = n & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0c080604u, 0x03020100u, m);
+  const uint32_t neg = __builtin_amdgcn_perm(0xf4f8fafcu, 0xfdfeff00u, m);
+  const uint32_t sgn = ((n >> 3) & 0x01010101u) * 0xffu;
+  return (neg & sgn) | (pos & ~sgn);
+}
+
+// MXFP4 piece: sum 2w H and 2w L over each group of 16 (exact integers:
+// |2w| <= 12, |H| <= 127, |L| <= 128), X = 256 H + L, times the group's
+// scale and 2^(e - 128) (the block scale 2^(e - 127) over the factor 2).
+template <int CPL>
+__device__ __forceinline__ float piece_dot(const Piece<FMT_MX4>& w, const ActMx4<CPL>& a, int k, const Iq2Tab*) {
+  const uint32_t W[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+  int hs[2], ls[2];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {  // word i: weights 8i .. 8i + 7 (group i / 2)
+    const uint32_t lo = W[i] & 0x0f0f0f0fu, hi = (W[i] >> 4) & 0x0f0f0f0fu;
+    const uint32_t b0 = mx4_bytes(__builtin_amdgcn_perm(hi, lo, 0x05010400u));  // weights 8i .. 8i + 3
+    const uint32_t b1 = mx4_bytes(__builtin_amdgcn_perm(hi, lo, 0x07030602u));  // 8i + 4 .. 8i + 7
+    const int g = i >> 1, j = 4 * g + 2 * (i & 1);
+    if ((i & 1) == 0) {
+      hs[g] = dot4(b1, a.H[k][j + 1], dot4_0(b0, a.H[k][j]));
+      ls[g] = dot4(b1, a.L[k][j + 1], dot4_0(b0, a.L[k][j]));
+    } else {
+      hs[g] = dot4(b1, a.H[k][j + 1], dot4(b0, a.H[k][j], hs[g]));
+      ls[g] = dot4(b1, a.L[k][j + 1], dot4(b0, a.L[k][j], ls[g]));
+    }
+  }
+  const float v = (float)(hs[0] * 256 + ls[0]) * a.s[k][0] + (float)(hs[1] * 256 + ls[1]) * a.s[k][1];
+  return __builtin_amdgcn_ldexpf(v, (int)w.e - 128);
 }
 
 template <int CPL>

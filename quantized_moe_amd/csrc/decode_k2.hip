@@ -125,6 +125,7 @@ hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks,
     case FMT_IQ2: return run_k2_s<FMT_IQ2, D>(a, fs, gcnt, blocks, down_layout, s); \
     case FMT_Q2K: return run_k2_s<FMT_Q2K, D>(a, fs, gcnt, blocks, down_layout, s); \
     case FMT_Q4K: return run_k2_s<FMT_Q4K, D>(a, fs, gcnt, blocks, down_layout, s); \
+    case FMT_MX4: return run_k2_s<FMT_MX4, D>(a, fs, gcnt, blocks, down_layout, s); \
     default: return run_k2_s<FMT_Q8, D>(a, fs, gcnt, blocks, down_layout, s);       \
   }
   switch (a.d) {

@@ -24,11 +24,15 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
                                           float* out) {
   constexpr int NS = DownRows<FMT, K, ROWS, 1>::NS;
   // three steps of loads kept in flight ahead of the compute; Q4K's pieces
-  // are twice as large (two steps, one for rows of more than 64 pieces)
+  // are twice as large and MXFP4's carry twice the activation registers
+  // (two steps, one for rows of more than 64 pieces)
   constexpr int CPL = Geo<FMT, K>::CPL;
-  constexpr int PDMAX = FMT == FMT_Q4K ? (CPL > 1 ? 1 : 2) : 3;
+  constexpr int PDMAX = FMT == FMT_Q4K || FMT == FMT_MX4 ? (CPL > 1 ? 1 : 2) : 3;
   DownRows<FMT, K, ROWS, (NS < PDMAX ? NS : PDMAX)> dr;
-  if (hq) {
+  if constexpr (FMT == FMT_MX4) {  // routed experts only: h always comes quantized
+    dr.load_act(hq, hs);
+    dr.issue(m, e, E, r0, my_scales, gain);
+  } else if (hq) {
     dr.load_act(hq, hs);
     dr.issue(m, e, E, r0, my_scales, gain);
   } else {
@@ -114,6 +118,7 @@ static hipError_t run_k3_f(const DecodeArgs& a, int fr, int fs, hipStream_t s) {
     case FMT_IQ2: K3_FS(FMT_IQ2)
     case FMT_Q2K: K3_FS(FMT_Q2K)
     case FMT_Q4K: K3_FS(FMT_Q4K)
+    case FMT_MX4: K3_FS(FMT_MX4)
     default: K3_FS(FMT_Q8)
   }
 #undef K3_FS

@@ -64,6 +64,10 @@ template <int D>
 struct RoutedAct<FMT_Q8, D> {
   using type = ActQ8B<Geo<FMT_Q8, D>::CPL>;
 };
+template <int D>
+struct RoutedAct<FMT_MX4, D> {
+  using type = ActMx4<Geo<FMT_MX4, D>::CPL>;
+};
 
 // Bytes of LDS scale staging one wave needs for RPW gate/up rows.
 template <int FMT, int D, int RPW>
@@ -131,7 +135,7 @@ __device__ __forceinline__ void gateup_rows(const QMat& gm, const QMat& um, int 
   // x before the codes: loads complete in issue order, so the first step
   // then waits only for its own codes
   typename RoutedAct<FMT, D>::type act;
-  if constexpr (FMT == FMT_Q8) {
+  if constexpr (FMT == FMT_Q8 || FMT == FMT_MX4) {
     act.template load<G::LPR, 64>(xq, xs, c);
   } else {
     act.template load<G::LPR>(xq, xs, c);
@@ -139,7 +143,7 @@ __device__ __forceinline__ void gateup_rows(const QMat& gm, const QMat& um, int 
 #pragma unroll
   for (int s = 0; s < PD; s++) issue(s);
   if constexpr (STAGE) ss.store(my_scales);
-  if constexpr (FMT != FMT_Q8) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
+  if constexpr (FMT != FMT_Q8 && FMT != FMT_MX4) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
 #pragma unroll
   for (int s = 0; s < NS; s++) {
     if (s + PD < NS) issue(s + PD);
@@ -171,6 +175,10 @@ template <int K>
 struct DownAct<FMT_Q8, K> {
   using type = ActQ8B<Geo<FMT_Q8, K>::CPL>;
 };
+template <int K>
+struct DownAct<FMT_MX4, K> {
+  using type = ActMx4<Geo<FMT_MX4, K>::CPL>;
+};
 
 // ROWS rows of one expert's down matrix against one h vector (quantized in
 // groups of 16), in three steps that the caller may order as it needs:
@@ -196,7 +204,7 @@ struct DownRows {
 
   __device__ __forceinline__ void load_act(const uint8_t* hq, const float* hs) {
     const int c = (threadIdx.x & 63) % G::LPR;
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (FMT == FMT_Q8 || FMT == FMT_MX4) {
       act.template load<G::LPR, 16>(hq, hs, c);
     } else {
       act.template load<G::LPR>(hq, hs, c);
@@ -257,7 +265,7 @@ struct DownRows {
       if (lane < ROWS) out[lane] = 0.0f;
       return;
     }
-    if constexpr (FMT != FMT_Q8) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
+    if constexpr (FMT != FMT_Q8 && FMT != FMT_MX4) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       if (s + PD < NS) issue_step(s + PD);

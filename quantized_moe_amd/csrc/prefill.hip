@@ -262,6 +262,24 @@ struct BRegs<FMT_Q8, KS> {
   }
 };
 
+// MXFP4: the codes of block 2*g4 + h (16 bytes, KS = 2) or of blocks 2*g4,
+// 2*g4 + 1 (32 bytes), and their E8M0 scale bytes.
+template <int KS>
+struct BRegs<FMT_MX4, KS> {
+  uint4 q[3 - KS];
+  uint32_t e;
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int h) {
+    const int64_t blk0 = row0 * m.nb + sb * 8;
+    const uint32_t lb = (uint32_t)(lrow * m.nb + 2 * g4 + (KS == 2 ? h : 0));
+#pragma unroll
+    for (int i = 0; i < 3 - KS; i++) q[i] = *reinterpret_cast<const uint4*>(m.p_a + (blk0 + lb) * 16 + 16 * i);
+    if constexpr (KS == 2)
+      e = m.p_scale[blk0 + lb];
+    else
+      e = *reinterpret_cast<const uint16_t*>(m.p_scale + blk0 + lb);
+  }
+};
+
 // The superblock scales of PD consecutive superblocks sb0 .. sb0 + PD - 1 of
 // the lane's row, fetched with one load (they are contiguous in the scale
 // plane): IQ2 fp16 d, Q2K (fp16 d, fp16 dmin) pairs.  A vector-memory
@@ -417,6 +435,34 @@ __device__ __forceinline__ uint4 q8_frag(const BRegs<FMT_Q8, KS>& b, int hh, int
     return __builtin_bit_cast(uint32_t, q * dd);
   };
   return make_uint4(pair(w0, 0x00050004u), pair(w0, 0x00070006u), pair(w1, 0x00050004u), pair(w1, 0x00070006u));
+}
+
+// MXFP4 block scales brought to the wave's superblock (KS = 1: the lane's
+// blocks 2*g4, 2*g4 + 1; KS = 2: block 2*g4 + h; the four lane groups
+// together hold the output row's 8 blocks, or their half): em = the largest
+// E8M0 exponent among them; f0, f1 = 2^(e_b - em) for the lane's blocks, the
+// factors the conversion applies (exact: an E2M1 value times a power of two
+// <= 1 is an fp16, or below 2^-24 of the superblock's largest weights);
+// returns 2^(em - 127), applied to the superblock's fp32 partial sums.
+template <int KS>
+__device__ __forceinline__ float mx4_prescale(uint32_t e, float& f0, float& f1) {
+  const int e0 = (int)(e & 255u), e1 = KS == 1 ? (int)((e >> 8) & 255u) : e0;
+  int em = max(e0, e1);
+  em = max(em, __shfl_xor(em, 16, 64));
+  em = max(em, __shfl_xor(em, 32, 64));
+  f0 = __builtin_amdgcn_ldexpf(1.0f, e0 - em);
+  f1 = __builtin_amdgcn_ldexpf(1.0f, e1 - em);
+  return __builtin_amdgcn_ldexpf(1.0f, em - 127);
+}
+
+// MXFP4 fragment: the 8 codes of quant word w (element 2j, 2j + 1 in the low
+// and high nibble of byte j) as fp16 values times f, by the hardware
+// conversion (exact for a power-of-two f).
+__device__ __forceinline__ uint4 mx4_frag(uint32_t w, float f) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, f, 3)));
 }
 
 // Maximum of v over each 16-lane row of the wave (the 16 output columns an
@@ -688,7 +734,36 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     auto aread = [&](int m, int i) {
       return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
     };
-    if constexpr (FMT == FMT_Q8) {
+    if constexpr (FMT == FMT_MX4) {
+      float f00, f01, f10 = 0.f, f11 = 0.f;
+      const float ps0 = mx4_prescale<KS>(B0.e, f00, f01);
+      float ps1 = 0.0f;
+      if constexpr (GATEUP) ps1 = mx4_prescale<KS>(B1.e, f10, f11);
+      f32x4_t s0[NM], s1[NM];
+#pragma unroll
+      for (int m = 0; m < NM; m++) s0[m] = s1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < 3 - KS; hh++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const uint4 f0 = mx4_frag(word_of(B0.q[hh], i), hh ? f01 : f00);
+          uint4 f1;
+          if constexpr (GATEUP) f1 = mx4_frag(word_of(B1.q[hh], i), hh ? f11 : f10);
+#pragma unroll
+          for (int m = 0; m < NM; m++) {
+            const uint4 av = aread(m, 4 * hh + i);
+            s0[m] = mfma32(av, f0, s0[m]);
+            if constexpr (GATEUP) s1[m] = mfma32(av, f1, s1[m]);
+          }
+          if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);  // bound the live fragments
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NM; m++) {
+        acc0[m] += ps0 * s0[m];
+        if constexpr (GATEUP) acc1[m] += ps1 * s1[m];
+      }
+    } else if constexpr (FMT == FMT_Q8) {
       uint32_t dw0 = 0, dw1 = 0;
       const float ps0 = q8_prescale<KS>(B0.d, dw0);
       float ps1 = 0.0f;
@@ -1102,37 +1177,46 @@ static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
 template <int FMT, bool GATEUP>
 static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int nsb = a.K / 256;
-  // 2-bit formats: a wave takes whole superblocks (KS = 1, 16-byte weight
-  // loads).  Superblocks kept in flight (PD) per wave, at 128 VGPRs per wave
-  // (16 waves per CU).
-  if constexpr (FMT != FMT_Q8) {
-    if constexpr (!GATEUP && FMT != FMT_Q4K) {
-      if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
-    }
-    // (two Q2K or Q4K matrices hold more registers per superblock than two
-    // IQ2 ones; one Q4K superblock holds twice the quant registers)
-    if constexpr (FMT == FMT_Q4K) {
-      if constexpr (GATEUP) {  // the two waves of a pair split each superblock (as Q8 gate/up; deeper spills)
-        return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
-      } else {
-        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
-      }
-    } else {
-      if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
-        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-      }
+  if constexpr (FMT == FMT_MX4) {  // whole superblocks per wave: 32 bytes of codes per lane and matrix
+    if constexpr (GATEUP) {
       return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
-    }
-  } else {
-    // Q8: whole superblocks for the one-matrix down GEMM; the two-matrix
-    // gate/up keeps the pair split (whole superblocks of two matrices spill)
-    if constexpr (!GATEUP) {
+    } else {
       if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
       return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
     }
-    // (two superblocks in flight spill: measured 220 us against 152 us with one)
-    return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+  } else {
+    // 2-bit formats: a wave takes whole superblocks (KS = 1, 16-byte weight
+    // loads).  Superblocks kept in flight (PD) per wave, at 128 VGPRs per wave
+    // (16 waves per CU).
+    if constexpr (FMT != FMT_Q8) {
+      if constexpr (!GATEUP && FMT != FMT_Q4K) {
+        if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
+      }
+      // (two Q2K or Q4K matrices hold more registers per superblock than two
+      // IQ2 ones; one Q4K superblock holds twice the quant registers)
+      if constexpr (FMT == FMT_Q4K) {
+        if constexpr (GATEUP) {  // the two waves of a pair split each superblock (as Q8 gate/up; deeper spills)
+          return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+        } else {
+          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+          return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+        }
+      } else {
+        if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
+          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+        }
+        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+      }
+    } else {
+      // Q8: whole superblocks for the one-matrix down GEMM; the two-matrix
+      // gate/up keeps the pair split (whole superblocks of two matrices spill)
+      if constexpr (!GATEUP) {
+        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+      }
+      // (two superblocks in flight spill: measured 220 us against 152 us with one)
+      return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+    }
   }
 }
 
@@ -1141,6 +1225,7 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
     case FMT_IQ2: { constexpr int F = FMT_IQ2; __VA_ARGS__; } break;   \
     case FMT_Q2K: { constexpr int F = FMT_Q2K; __VA_ARGS__; } break;   \
     case FMT_Q4K: { constexpr int F = FMT_Q4K; __VA_ARGS__; } break;   \
+    case FMT_MX4: { constexpr int F = FMT_MX4; __VA_ARGS__; } break;   \
     default: { constexpr int F = FMT_Q8; __VA_ARGS__; } break;         \
   }
 

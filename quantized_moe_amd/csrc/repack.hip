@@ -32,6 +32,10 @@ __global__ void repack_kernel(int fmt, int64_t n_blocks, const uint8_t* __restri
     seg_off[0] = 0; seg_len[0] = 4;
     seg_off[1] = 4; seg_len[1] = 12;
     seg_off[2] = 16; seg_len[2] = 128;
+  } else if (fmt == FMT_MX4) {
+    nseg = 2;
+    seg_off[0] = 0; seg_len[0] = 1;
+    seg_off[1] = 1; seg_len[1] = 16;
   } else {
     nseg = 2;
     seg_off[0] = 0; seg_len[0] = 2;

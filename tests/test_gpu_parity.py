@@ -111,6 +111,16 @@ FORMAT_CASES = [
     (10, 3, 2048, 1024, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 70, synth.BF16),
     (8, 2, 256, 8192, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q8, 2, synth.F32),   # two pieces per lane (f)
     (8, 1, 8192, 256, synth.FMT_Q4K, synth.FMT_Q4K, None, 2, synth.F32),           # two pieces per lane (d)
+    # MXFP4 routed experts (E8M0 scale per 32 E2M1 weights), decode and prefill
+    (16, 4, 256, 512, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 1, synth.F32),
+    (16, 4, 256, 512, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 3, synth.F32),
+    (16, 4, 256, 512, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 37, synth.BF16),
+    (12, 3, 512, 1024, synth.FMT_IQ2, synth.FMT_MX4, synth.FMT_Q2K, 1, synth.F32),
+    (12, 3, 1024, 512, synth.FMT_MX4, synth.FMT_Q2K, synth.FMT_IQ2, 6, synth.BF16),
+    (10, 3, 2048, 1024, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 70, synth.BF16),
+    (8, 2, 256, 8192, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 2, synth.F32),   # four pieces per lane (f)
+    (8, 1, 8192, 256, synth.FMT_MX4, synth.FMT_MX4, None, 2, synth.F32),           # four pieces per lane (d)
+    (9, 2, 256, 256, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 40, synth.F32),   # rows of 8 pieces: 8 rows per wave step
 ]
 
 
@@ -180,9 +190,10 @@ def test_route_topk_with_bias():
 
 @pytest.mark.parametrize("T,dt,fmt", [(1, synth.F32, synth.FMT_IQ2), (3, synth.F32, synth.FMT_IQ2),
                                       (37, synth.BF16, synth.FMT_IQ2), (1, synth.F32, synth.FMT_Q4K),
-                                      (8, synth.F32, synth.FMT_Q4K), (45, synth.BF16, synth.FMT_Q4K)])
+                                      (8, synth.F32, synth.FMT_Q4K), (45, synth.BF16, synth.FMT_Q4K),
+                                      (2, synth.F32, synth.FMT_MX4), (45, synth.BF16, synth.FMT_MX4)])
 def test_layer_with_bias_and_gains(T, dt, fmt):
-    fdn = synth.FMT_Q2K if fmt == synth.FMT_IQ2 else synth.FMT_Q4K
+    fdn = {synth.FMT_IQ2: synth.FMT_Q2K, synth.FMT_Q4K: synth.FMT_Q4K, synth.FMT_MX4: synth.FMT_MX4}[fmt]
     spec = synth.scaled_spec(E=24, k=4, d=512, f=512, fmt_gate_up=fmt, fmt_down=fdn)
     L = _bias_gain_layer(spec, 32)
     dl = lib.DeviceLayer.from_synth(L, DEV)
@@ -328,6 +339,59 @@ def test_q4k_layer_full_size_decode_and_prefill():
         torch.cuda.empty_cache()
 
 
+def test_mxfp4_layer_full_size_decode_and_prefill():
+    """The decode workload's shape with MXFP4 routed gate/up/down (the
+    native-FP4 experts): one-token decode on three tokens, and a 1024-token
+    bf16 chunk with routes bit-exact and 64 tokens compared one by one."""
+    spec = synth.scaled_spec(E=384, k=6, d=4096, f=2048, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4)
+    L = synth.random_layer(spec, seed=4, workload="mx4")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    try:
+        for i in range(3):
+            x = synth.activations(4, ("mx4", "x", i), 1, 4096, synth.F32)
+            y, idx, wt = run_layer(dl, x, synth.F32, lib.MOE_PATH_AUTO)
+            y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+            assert np.array_equal(idx, idx_ref)
+            assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
+        T = 1024
+        x = synth.activations(4, ("mx4", "prefill"), T, 4096, synth.BF16)
+        y, idx, wt = run_layer(dl, x, synth.BF16, lib.MOE_PATH_AUTO)
+        _, idx_ref, wt_ref = oracle.route(x, oracle.BF16, L.w_router, 6)
+        assert np.array_equal(idx, idx_ref)
+        tok = np.unique(np.concatenate([np.arange(0, T, 16), [1, T - 1]]))
+        y_ref = oracle.ffn(L, x, oracle.BF16, idx_ref, wt_ref, tokens=tok, grouped=True)
+        err = per_token_rel_l2(y[tok], y_ref)
+        assert err.max() <= REL_L2, err.max()
+    finally:
+        del dl
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shift", [-20, 20])
+def test_mxfp4_block_scales_far_from_unit(shift):
+    """MXFP4 experts whose E8M0 exponents sit 20 binades below or above the
+    usual, with a spread of 12 binades inside each row: every token within
+    the bar on both paths."""
+    spec = synth.scaled_spec(E=12, k=3, d=1024, f=512, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4)
+    L = synth.random_layer(spec, seed=45, workload="mx4scale")
+    rng = np.random.default_rng(45 + shift)
+
+    def shifted(blob):
+        b = blob.reshape(-1, 17).copy()
+        b[:, 0] = np.clip(b[:, 0].astype(np.int64) + shift + rng.integers(-6, 7, b.shape[0]), 1, 254).astype(np.uint8)
+        return b.reshape(-1)
+    L = synth.Layer(**{**L.__dict__, "w_gate": shifted(L.w_gate), "w_up": shifted(L.w_up),
+                       "w_down": shifted(L.w_down)})
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    for T, dt, path in ((40, synth.BF16, lib.MOE_PATH_PREFILL), (3, synth.F32, lib.MOE_PATH_DECODE)):
+        x = synth.activations(45, ("mx4scale", T), T, spec.d, dt)
+        y, idx, wt = run_layer(dl, x, dt, path)
+        y_ref, idx_ref, _ = oracle.layer_forward(L, x, dt)
+        assert np.array_equal(idx, idx_ref)
+        err = per_token_rel_l2(y, y_ref)
+        assert err.max() <= REL_L2, (shift, path, err.max())
+
+
 def test_small_batch_both_paths(decode_layer):
     """16 tokens of 4 interleaved sessions with expert reuse, fp32, caller routes."""
     L, dl = decode_layer
@@ -466,6 +530,7 @@ SCALE_SPECS = [
     synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q4K),
     synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_IQ2,
                       fmt_shared=synth.FMT_Q2K),
+    synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4),
 ]
 
 
