@@ -40,7 +40,7 @@ def test_abi_and_status_strings():
 
 
 @pytest.mark.parametrize("fmt,E,rows,K", [(1, 384, 2048, 4096), (2, 384, 4096, 2048), (3, 1, 2048, 4096),
-                                          (2, 8, 512, 256), (4, 384, 2048, 4096)])
+                                          (2, 8, 512, 256), (4, 384, 2048, 4096), (5, 384, 4096, 2048)])
 def test_matrix_bytes_matches_format_sizes(fmt, E, rows, K):
     assert lib.matrix_bytes(fmt, E, rows, K) == synth.matrix_bytes(fmt, E, rows, K)
 
@@ -51,6 +51,7 @@ def test_matrix_bytes_of_the_decode_layer():
     assert lib.matrix_bytes(2, 1, 4096, 2048) == 2752512
     assert lib.matrix_bytes(3, 1, 2048, 4096) == 8912896
     assert lib.matrix_bytes(4, 1, 2048, 4096) == 4718592   # Q4K: 144 B per 256 weights
+    assert lib.matrix_bytes(5, 1, 2048, 4096) == 4456448   # MXFP4: 17 B per 32 weights
 
 
 def _layer(**over):
@@ -79,7 +80,8 @@ def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
     (dict(fmt_gate_up=9), lib.MOE_ERR_UNSUPPORTED),
     (dict(fmt_down=0), lib.MOE_ERR_UNSUPPORTED),
     (dict(fmt_shared=4), lib.MOE_ERR_UNSUPPORTED),        # Q4K_L: routed experts only
-    (dict(fmt_shared=5), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_shared=5), lib.MOE_ERR_UNSUPPORTED),        # MXFP4_L: routed experts only
+    (dict(fmt_shared=6), lib.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=0), lib.MOE_ERR_INVALID_ARG),
     (dict(n_experts=1025), lib.MOE_ERR_INVALID_ARG),
     (dict(d_model=4000), lib.MOE_ERR_INVALID_ARG),
@@ -211,7 +213,8 @@ def test_route_and_bucket_validation():
 
 def test_repack_validation():
     L = lib.lib()
-    assert L.moe_repack(5, 1, 16, 256, 256, 512, 0, None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_repack(9, 1, 16, 256, 256, 512, 0, None) == lib.MOE_ERR_UNSUPPORTED
+    assert L.moe_repack(5, 1, 16, 48, 256, 512, 0, None) == lib.MOE_ERR_INVALID_ARG  # MXFP4: K % 32
     assert L.moe_repack(4, 1, 16, 100, 256, 512, 0, None) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_repack(1, 1, 16, 100, 256, 512, 0, None) == lib.MOE_ERR_INVALID_ARG
     assert L.moe_repack(1, 1, 16, 256, 256, 256, 0, None) == lib.MOE_ERR_INVALID_ARG
