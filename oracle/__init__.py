@@ -23,7 +23,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
-IQ2, Q2K, Q8, Q4K, MX4 = 1, 2, 3, 4, 5
+IQ2, Q2K, Q8, Q4K, MX4, VQ12, VQ13 = 1, 2, 3, 4, 5, 6, 7
 _BW = {IQ2: 256, Q2K: 256, Q8: 32, Q4K: 256, MX4: 32}
 _BB = {IQ2: 66, Q2K: 84, Q8: 34, Q4K: 144, MX4: 17}
 
@@ -32,7 +32,7 @@ _lib = None
 
 def build() -> str:
     """Compile liboracle.so with gcc (no fast-math; IEEE fmaf and additions)."""
-    tmp = _SO + ".tmp"
+    tmp = "%s.%d.tmp" % (_SO, os.getpid())
     subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
                            "-Wall", "-o", tmp, _SRC, "-lm"])
     os.replace(tmp, _SO)
@@ -53,7 +53,9 @@ def lib():
         L.orc_route_weights.argtypes = [P, P, I, I, I, P]
         L.orc_bucket.argtypes = [P, I, I, I, P, P, P, P]
         L.orc_dequant.argtypes, L.orc_dequant.restype = [I, P, I64, P, P], I
-        L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, I, I, P, P, P, P, P, I, I, P, I, P, P, P]
+        L.orc_dequant_rows.argtypes, L.orc_dequant_rows.restype = [I, P, I64, I, P, P, P], I
+        L.orc_e4m3.argtypes, L.orc_e4m3.restype = [I], ctypes.c_double
+        L.orc_ffn.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, I, P, P, P, P, P, I, I, P, I, P, P, P]
         L.orc_ffn_grouped.argtypes = L.orc_ffn.argtypes
         L.orc_ffn_grouped.restype = I
         L.orc_sigmoid32.argtypes, L.orc_sigmoid32.restype = [ctypes.c_float], ctypes.c_float
@@ -169,6 +171,31 @@ def dequant(fmt, blocks, grid=None) -> np.ndarray:
     return out
 
 
+def vq_row_bytes(fmt, K) -> int:
+    """Bytes of one VQ row of K weights: fp16 gain, 12-bit stream, bit plane."""
+    return 2 + 3 * K // 16 + (K // 64 if fmt == VQ13 else 0)
+
+
+def e4m3(code: int) -> float:
+    """The value of one E4M3 byte (nan for the two not-a-number codes)."""
+    return lib().orc_e4m3(int(code))
+
+
+def dequant_rows(fmt, rows, K, grid=None, codebook=None) -> np.ndarray:
+    """Every weight of consecutive rows of K weights, exactly, as float64
+    [n_rows, K] (block formats row by row; VQ rows with the codebook)."""
+    rows = _c(rows, np.uint8).reshape(-1)
+    rb = vq_row_bytes(fmt, K) if fmt in (VQ12, VQ13) else K // _BW[fmt] * _BB[fmt]
+    n = rows.size // rb
+    assert n * rb == rows.size
+    out = np.empty((n, K), dtype=np.float64)
+    g = None if grid is None else _c(grid, np.uint8)
+    cb = None if codebook is None else _c(codebook, np.uint8)
+    if lib().orc_dequant_rows(fmt, _p(rows), n, K, _p(g), _p(cb), _p(out)) != 0:
+        raise ValueError("bad format or missing codebook")
+    return out
+
+
 def ffn(layer, x, x_dtype, idx, wt, tokens=None, grouped=False) -> np.ndarray:
     """Expert FFN + shared expert for the listed tokens (all if None).
 
@@ -188,10 +215,11 @@ def ffn(layer, x, x_dtype, idx, wt, tokens=None, grouped=False) -> np.ndarray:
     k = idx.shape[1]  # routes per token as given (may differ from the layer's top_k)
     dg = getattr(layer, "down_gain", None)
     gain = None if dg is None else _c(dg, np.float32)
+    cb = getattr(layer, "vq_codebook", None)
     fn = lib().orc_ffn_grouped if grouped else lib().orc_ffn
     rc = fn(s.E, s.d, s.f, k, s.fmt_gate_up, s.fmt_down, _p(_c(layer.w_gate, np.uint8)),
                        _p(_c(layer.w_up, np.uint8)), _p(_c(layer.w_down, np.uint8)), _p(_c(layer.grid, np.uint8)),
-                       int(sh), s.fmt_shared if sh else 0,
+                       _p(None if cb is None else _c(cb, np.uint8)), int(sh), s.fmt_shared if sh else 0,
                        _p(_c(layer.s_gate, np.uint8)) if sh else None,
                        _p(_c(layer.s_up, np.uint8)) if sh else None,
                        _p(_c(layer.s_down, np.uint8)) if sh else None,
@@ -199,7 +227,7 @@ def ffn(layer, x, x_dtype, idx, wt, tokens=None, grouped=False) -> np.ndarray:
     if rc == -2:
         raise MemoryError("oracle ffn: out of host memory")
     if rc != 0:
-        raise ValueError("oracle ffn: token or expert index out of range")
+        raise ValueError("oracle ffn: token or expert index out of range, or unusable format")
     return y
 
 

@@ -12,7 +12,8 @@
  *                  a router bias: on the keys sigmoid32(z) + b, orc_bias_keys)
  *   mixing weights sigmoid of the chosen logits, normalised to sum one (fp64)
  *   bucketing      stable counting sort of the flat routes by expert
- *   dequantisation every weight exactly, in fp64
+ *   dequantisation every weight exactly, in fp64 (block formats; VQ rows
+ *                  with a per-layer E4M3 codebook)
  *   expert FFN     h = silu(G x) * (U x), ye = D h, all in fp64
  *   combine        y = sum_j wt_j * (g_e * ye_j) + shared(x), fp64, rounded
  *                  to fp32 (g_e the optional per-channel down gains, else 1)
@@ -25,7 +26,9 @@
  * (IQ2_XXS-like gate/up, Q2_K-like down, Q8 shared expert, unquantized
  * router): "Running DeepSeek V4 Flash on an RTX 5080 with 16GB VRAM Under
  * Linux/WSL2 via DS4", model section, and the txtmix teardown "ds4 拆解",
- * section 3.  The pages name no score function, activation, summation order
+ * section 3.  The 8-dimensional VQ routed format (one 12- or 13-bit index
+ * per 8 weights, one fp16 gain per row, E4M3 codewords shared by a layer):
+ * YoungAi page, section 4.1.  The pages name no score function, activation, summation order
  * or byte layout; the readings used here are: sigmoid scores, selection on
  * the raw logit, SwiGLU experts with silu(g) = g / (1 + exp(-g)), the fixed
  * router order below, and the byte layouts restated at each decoder.
@@ -46,6 +49,8 @@
 #define ORC_Q8 3
 #define ORC_Q4K 4
 #define ORC_MX4 5
+#define ORC_VQ12 6
+#define ORC_VQ13 7
 
 /* ---------------------------------------------------------------------- */
 /* scalar decoding of stored numbers                                      */
@@ -322,6 +327,50 @@ static void deq_mx4(const uint8_t* b, double* w) {
   }
 }
 
+/*
+ * E4M3 byte (the FP8 codewords of the YoungAi page, section 4.1): sign bit
+ * 7, 4-bit exponent E (bits 6..3, bias 7), 3-bit mantissa M; |value| =
+ * M / 8 * 2^-6 for E = 0, else (1 + M / 8) * 2^(E - 7); E = 15 with M = 7 is
+ * not a number (not a valid codeword); there are no infinities.
+ */
+double orc_e4m3(int b) {
+  int E = (b >> 3) & 15, M = b & 7;
+  if (E == 15 && M == 7) return NAN;
+  double mag = E == 0 ? ldexp((double)M, -9) : ldexp((double)(8 + M), E - 10);
+  return (b & 128) ? -mag : mag;
+}
+
+/*
+ * VQ rows (the 8-dimensional vector quantization of the YoungAi page,
+ * section 4.1: every 8 consecutive weights of a routed-expert row are one
+ * 12-bit or 13-bit index into a per-layer codebook, times one fp16 gain per
+ * row).  A row of K weights is:
+ *   bytes 0-1                fp16 gain g,
+ *   next 3K/16 bytes         the 12-bit index stream: index j occupies bits
+ *                            12j .. 12j + 11 of the stream, least
+ *                            significant bit first (bit b of the stream is
+ *                            bit b % 8 of byte b / 8),
+ *   next K/64 bytes (VQ13)   the bit plane: bit j (bit j % 8 of byte j / 8)
+ *                            is bit 12 of index j (the "12 + 1" layout).
+ *   w[8j + i] = g * codebook[index_j][i], codewords as E4M3 bytes [n][8].
+ */
+static int64_t vq_row_bytes(int fmt, int K) { return 2 + 3 * (int64_t)K / 16 + (fmt == ORC_VQ13 ? K / 64 : 0); }
+
+static void deq_vq_row(int fmt, const uint8_t* row, int K, const uint8_t* cb, double* w) {
+  double g = orc_half(rd16(row));
+  const uint8_t* stream = row + 2;
+  const uint8_t* plane = stream + 3 * K / 16;
+  for (int j = 0; j < K / 8; j++) {
+    int idx = 0;
+    for (int b = 0; b < 12; b++) {
+      int64_t bit = 12 * (int64_t)j + b;
+      idx |= ((stream[bit / 8] >> (bit % 8)) & 1) << b;
+    }
+    if (fmt == ORC_VQ13) idx |= ((plane[j / 8] >> (j % 8)) & 1) << 12;
+    for (int i = 0; i < 8; i++) w[8 * j + i] = g * orc_e4m3(cb[8 * idx + i]);
+  }
+}
+
 /* Q8_0_L block, 32 weights in 34 bytes: fp16 d then int8 q[32]; w = d q. */
 static void deq_q8(const uint8_t* b, double* w) {
   double d = orc_half(rd16(b));
@@ -331,6 +380,12 @@ static void deq_q8(const uint8_t* b, double* w) {
 static int block_weights(int fmt) { return fmt == ORC_Q8 || fmt == ORC_MX4 ? 32 : 256; }
 static int block_bytes(int fmt) {
   return fmt == ORC_IQ2 ? 66 : fmt == ORC_Q2K ? 84 : fmt == ORC_Q4K ? 144 : fmt == ORC_MX4 ? 17 : 34;
+}
+
+/* Bytes of one row of K weights in `fmt`. */
+static int64_t row_bytes_of(int fmt, int K) {
+  if (fmt == ORC_VQ12 || fmt == ORC_VQ13) return vq_row_bytes(fmt, K);
+  return (int64_t)(K / block_weights(fmt)) * block_bytes(fmt);
 }
 
 /* Decode n_blocks consecutive blocks of `fmt` into fp64. Returns 0 on success. */
@@ -354,6 +409,24 @@ int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t*
   return 0;
 }
 
+/*
+ * Decode n_rows consecutive rows of K weights of any format (the block
+ * formats row by row, VQ rows with the codebook cb).  Returns 0 on success.
+ */
+int orc_dequant_rows(int fmt, const uint8_t* rows, int64_t n_rows, int K, const uint8_t* grid, const uint8_t* cb,
+                     double* out) {
+  int64_t rb = row_bytes_of(fmt, K);
+  for (int64_t r = 0; r < n_rows; r++) {
+    if (fmt == ORC_VQ12 || fmt == ORC_VQ13) {
+      if (!cb) return -1;
+      deq_vq_row(fmt, rows + r * rb, K, cb, out + r * K);
+    } else if (orc_dequant(fmt, rows + r * rb, K / block_weights(fmt), grid, out + r * K) != 0) {
+      return -1;
+    }
+  }
+  return 0;
+}
+
 /* ---------------------------------------------------------------------- */
 /* expert FFN                                                              */
 /* ---------------------------------------------------------------------- */
@@ -363,16 +436,15 @@ int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t*
  * `fmt` (row n of expert matrix starts at n * row_bytes), fp64 throughout,
  * each dot product summed in increasing i.
  */
-static void matvec(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid, const double* v,
-                   double* out) {
-  int64_t nbk = K / block_weights(fmt);
-  int64_t row_bytes = nbk * block_bytes(fmt);
+static void matvec(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid, const uint8_t* cb,
+                   const double* v, double* out) {
+  int64_t row_bytes = row_bytes_of(fmt, K);
 #pragma omp parallel
   {
     double* w = (double*)malloc(sizeof(double) * (size_t)K);
 #pragma omp for schedule(static)
     for (int n = 0; n < rows; n++) {
-      orc_dequant(fmt, mat + (int64_t)n * row_bytes, nbk, grid, w);
+      orc_dequant_rows(fmt, mat + (int64_t)n * row_bytes, 1, K, grid, cb, w);
       double acc = 0.0;
       for (int i = 0; i < K; i++) acc += w[i] * v[i];
       out[n] = acc;
@@ -388,17 +460,21 @@ static double silu(double g) { return g / (1.0 + exp(-g)); }
  * One SwiGLU expert on one token: out = D (silu(G x) * (U x)).
  * G, U: [f][d]; D: [d][f].
  */
-static void expert(int fmt_gu, const uint8_t* G, const uint8_t* U, int fmt_dn, const uint8_t* D, int d, int f,
-                   const uint8_t* grid, const double* x, double* out, double* g, double* u) {
-  matvec(fmt_gu, G, f, d, grid, x, g);
-  matvec(fmt_gu, U, f, d, grid, x, u);
-  for (int n = 0; n < f; n++) g[n] = silu(g[n]) * u[n];
-  matvec(fmt_dn, D, d, f, grid, g, out);
+/* Whether fmt names a format this file decodes (VQ rows need a codebook). */
+static int fmt_usable(int fmt, const uint8_t* cb) {
+  if (fmt == ORC_VQ12 || fmt == ORC_VQ13) return cb != NULL;
+  return fmt == ORC_IQ2 || fmt == ORC_Q2K || fmt == ORC_Q8 || fmt == ORC_Q4K || fmt == ORC_MX4;
 }
 
-static int64_t mat_bytes(int fmt, int rows, int K) {
-  return (int64_t)rows * (K / block_weights(fmt)) * block_bytes(fmt);
+static void expert(int fmt_gu, const uint8_t* G, const uint8_t* U, int fmt_dn, const uint8_t* D, int d, int f,
+                   const uint8_t* grid, const uint8_t* cb, const double* x, double* out, double* g, double* u) {
+  matvec(fmt_gu, G, f, d, grid, cb, x, g);
+  matvec(fmt_gu, U, f, d, grid, cb, x, u);
+  for (int n = 0; n < f; n++) g[n] = silu(g[n]) * u[n];
+  matvec(fmt_dn, D, d, f, grid, cb, g, out);
 }
+
+static int64_t mat_bytes(int fmt, int rows, int K) { return (int64_t)rows * row_bytes_of(fmt, K); }
 
 /*
  * Expert FFN of a layer for the tokens listed in `tokens` (n_tok of them;
@@ -413,9 +489,11 @@ static int64_t mat_bytes(int fmt, int rows, int K) {
  * the per-layer sum of the YoungAi page, section 4.2.
  */
 int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
-            const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+            const uint8_t* w_down, const uint8_t* grid, const uint8_t* cb, int has_shared, int fmt_sh,
+            const uint8_t* s_gate,
             const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype, int T,
             const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y) {
+  if (!fmt_usable(fmt_gu, cb) || !fmt_usable(fmt_dn, cb) || (has_shared && !fmt_usable(fmt_sh, cb))) return -1;
   int64_t gu_bytes = mat_bytes(fmt_gu, f, d), dn_bytes = mat_bytes(fmt_dn, d, f);
   double* xv = (double*)malloc(sizeof(double) * (size_t)d);
   double* acc = (double*)malloc(sizeof(double) * (size_t)d);
@@ -437,8 +515,8 @@ int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w
         status = -1;
         break;
       }
-      expert(fmt_gu, w_gate + e * gu_bytes, w_up + e * gu_bytes, fmt_dn, w_down + e * dn_bytes, d, f, grid, xv, ye,
-             g, u);
+      expert(fmt_gu, w_gate + e * gu_bytes, w_up + e * gu_bytes, fmt_dn, w_down + e * dn_bytes, d, f, grid, cb, xv,
+             ye, g, u);
       double w = (double)wt[(int64_t)t * k + j];
       if (down_gain)
         for (int i = 0; i < d; i++) acc[i] += w * ((double)down_gain[(int64_t)e * d + i] * ye[i]);
@@ -447,7 +525,7 @@ int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w
     }
     if (status != 0) break;
     if (has_shared) {
-      expert(fmt_sh, s_gate, s_up, fmt_sh, s_down, d, f, grid, xv, ye, g, u);
+      expert(fmt_sh, s_gate, s_up, fmt_sh, s_down, d, f, grid, cb, xv, ye, g, u);
       for (int i = 0; i < d; i++) acc[i] += ye[i];
     }
     for (int i = 0; i < d; i++) y[(int64_t)r * d + i] = (float)acc[i];
@@ -481,12 +559,12 @@ static void matvec_deq(const double* W, int rows, int K, const double* v, double
   }
 }
 
-static double* deq_matrix(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid) {
-  int64_t nbk = K / block_weights(fmt), row_bytes = nbk * block_bytes(fmt);
+static double* deq_matrix(int fmt, const uint8_t* mat, int rows, int K, const uint8_t* grid, const uint8_t* cb) {
+  int64_t row_bytes = row_bytes_of(fmt, K);
   double* W = (double*)malloc(sizeof(double) * (size_t)rows * (size_t)K);
   if (!W) return NULL;
 #pragma omp parallel for schedule(static)
-  for (int n = 0; n < rows; n++) orc_dequant(fmt, mat + (int64_t)n * row_bytes, nbk, grid, W + (int64_t)n * K);
+  for (int n = 0; n < rows; n++) orc_dequant_rows(fmt, mat + (int64_t)n * row_bytes, 1, K, grid, cb, W + (int64_t)n * K);
   return W;
 }
 
@@ -500,9 +578,11 @@ static void expert_deq(const double* G, const double* U, const double* D, int d,
 }
 
 int orc_ffn_grouped(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
-                    const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+                    const uint8_t* w_down, const uint8_t* grid, const uint8_t* cb, int has_shared, int fmt_sh,
+                    const uint8_t* s_gate,
                     const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype,
                     int T, const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y) {
+  if (!fmt_usable(fmt_gu, cb) || !fmt_usable(fmt_dn, cb) || (has_shared && !fmt_usable(fmt_sh, cb))) return -1;
   int64_t gu_bytes = mat_bytes(fmt_gu, f, d), dn_bytes = mat_bytes(fmt_dn, d, f);
   int count = tokens ? n_tok : T;
   for (int r = 0; r < count; r++) {
@@ -530,9 +610,9 @@ int orc_ffn_grouped(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const ui
       for (int j = 0; j < k; j++) used |= idx[(int64_t)t * k + j] == e;
     }
     if (!used) continue;
-    double* G = deq_matrix(fmt_gu, w_gate + e * gu_bytes, f, d, grid);
-    double* U = deq_matrix(fmt_gu, w_up + e * gu_bytes, f, d, grid);
-    double* D = deq_matrix(fmt_dn, w_down + e * dn_bytes, d, f, grid);
+    double* G = deq_matrix(fmt_gu, w_gate + e * gu_bytes, f, d, grid, cb);
+    double* U = deq_matrix(fmt_gu, w_up + e * gu_bytes, f, d, grid, cb);
+    double* D = deq_matrix(fmt_dn, w_down + e * dn_bytes, d, f, grid, cb);
     if (!G || !U || !D) status = -2;
     for (int r = 0; r < count && status == 0; r++) {
       int t = tokens ? tokens[r] : r;
@@ -545,9 +625,9 @@ int orc_ffn_grouped(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const ui
     free(G); free(U); free(D);
   }
   if (status == 0 && has_shared) {
-    double* G = deq_matrix(fmt_sh, s_gate, f, d, grid);
-    double* U = deq_matrix(fmt_sh, s_up, f, d, grid);
-    double* D = deq_matrix(fmt_sh, s_down, d, f, grid);
+    double* G = deq_matrix(fmt_sh, s_gate, f, d, grid, cb);
+    double* U = deq_matrix(fmt_sh, s_up, f, d, grid, cb);
+    double* D = deq_matrix(fmt_sh, s_down, d, f, grid, cb);
     if (!G || !U || !D) status = -2;
     for (int r = 0; r < count && status == 0; r++) {
       int t = tokens ? tokens[r] : r;

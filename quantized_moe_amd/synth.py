@@ -36,9 +36,11 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8, FMT_Q4K, FMT_MX4 = 0, 1, 2, 3, 4, 5
+FMT_NONE, FMT_IQ2, FMT_Q2K, FMT_Q8, FMT_Q4K, FMT_MX4, FMT_VQ12, FMT_VQ13 = 0, 1, 2, 3, 4, 5, 6, 7
 BLOCK_WEIGHTS = {FMT_IQ2: 256, FMT_Q2K: 256, FMT_Q8: 32, FMT_Q4K: 256, FMT_MX4: 32}
 BLOCK_BYTES = {FMT_IQ2: 66, FMT_Q2K: 84, FMT_Q8: 34, FMT_Q4K: 144, FMT_MX4: 17}
+VQ_FORMATS = (FMT_VQ12, FMT_VQ13)
+VQ_CODES = {FMT_VQ12: 4096, FMT_VQ13: 8192}
 
 F32, BF16 = 0, 1
 
@@ -150,6 +152,26 @@ def pack_mx4(e: np.ndarray, codes: np.ndarray) -> np.ndarray:
     return out
 
 
+def pack_vq(gain: np.ndarray, idx: np.ndarray, bits: int) -> np.ndarray:
+    """VQ12_L / VQ13_L rows.  gain float16 [R]; idx integers [R, K/8] below
+    2^bits (bits 12 or 13); returns uint8 [R, 2 + 3K/16 (+ K/64 for 13)]:
+    the fp16 gain, the low 12 bits of every index as one little-endian bit
+    stream (index j at stream bits 12j..12j+11), then for 13 bits a plane
+    holding bit 12 of index j at bit j."""
+    idx = np.asarray(idx, dtype=np.int64)
+    R, n = idx.shape
+    assert n % (8 if bits == 13 else 2) == 0 and bits in (12, 13) and idx.min(initial=0) >= 0 and idx.max(initial=0) < (1 << bits)
+    lo = idx & 0xFFF
+    pairs = lo.reshape(R, n // 2, 2)  # two 12-bit indices = three bytes
+    v = pairs[:, :, 0] | (pairs[:, :, 1] << 12)
+    stream = np.stack([v & 255, (v >> 8) & 255, (v >> 16) & 255], axis=2).reshape(R, 3 * n // 2)
+    parts = [np.ascontiguousarray(gain.astype("<f2")).view(np.uint8).reshape(R, 2), stream.astype(np.uint8)]
+    if bits == 13:
+        hi = ((idx >> 12) & 1).reshape(R, n // 8, 8)
+        parts.append((hi << np.arange(8)).sum(axis=2).astype(np.uint8))
+    return np.concatenate(parts, axis=1)
+
+
 def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
     """Q8_0_L blocks.  d float16 [nb]; q int8 [nb, 32]; returns uint8 [nb, 34]."""
     nb = d.shape[0]
@@ -173,8 +195,11 @@ def pack_q8(d: np.ndarray, q: np.ndarray) -> np.ndarray:
 #        var = var(sc q) + 7.5^2 var(m) = 47532 + 19195 -> std 258 d -> d ~ 7.74e-5
 #   MX4: E2M1 codes ~ U{0..15}: E[v^2] = 8.5625 -> std 2.93; the E8M0
 #        exponent drawn from {119, 120} (scale 2^-8 or 2^-7): std ~ 0.018
+#   VQ : codewords from make_codebook have an RMS near 1.5, so a row gain
+#        near 0.0137 gives std ~ 0.02
 IQ2_D, Q2K_D, Q8_D, Q4K_D = 2.36e-4, 1.35e-3, 2.7e-4, 7.74e-5
 MX4_E = 120
+VQ_G = 0.0137
 
 
 def _rand_scale(rng, nb, base):
@@ -236,19 +261,66 @@ def random_mx4(rng: np.random.Generator, nb: int) -> np.ndarray:
     return out
 
 
+def random_vq(rng: np.random.Generator, rows: int, K: int, bits: int) -> np.ndarray:
+    """Random VQ rows: uniform indices below 2^bits, gains near VQ_G."""
+    gain = _rand_scale(rng, rows, VQ_G)
+    idx = rng.integers(0, 1 << bits, size=(rows, K // 8))
+    return pack_vq(gain, idx, bits)
+
+
 RANDOM_CODES = {FMT_IQ2: random_iq2, FMT_Q2K: random_q2k, FMT_Q8: random_q8, FMT_Q4K: random_q4k,
                 FMT_MX4: random_mx4}
 
 
+def row_bytes(fmt: int, K: int) -> int:
+    """Bytes of one canonical row of K weights."""
+    if fmt in VQ_FORMATS:
+        return 2 + 3 * K // 16 + (K // 64 if fmt == FMT_VQ13 else 0)
+    return (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
+
+
 def matrix_bytes(fmt: int, n_experts: int, rows: int, K: int) -> int:
-    return n_experts * rows * (K // BLOCK_WEIGHTS[fmt]) * BLOCK_BYTES[fmt]
+    return n_experts * rows * row_bytes(fmt, K)
 
 
 def random_matrix(seed, tag, fmt: int, rows: int, K: int) -> np.ndarray:
-    """One expert's matrix of random valid codes: uint8 [rows * K/bw * bb]."""
+    """One expert's matrix of random valid codes: uint8 [rows * row_bytes]."""
     rng = rng_for(seed, *tag)
+    if fmt in VQ_FORMATS:
+        return random_vq(rng, rows, K, 12 if fmt == FMT_VQ12 else 13).reshape(-1)
     nb = rows * (K // BLOCK_WEIGHTS[fmt])
     return RANDOM_CODES[fmt](rng, nb).reshape(-1)
+
+
+E4M3_NAN = (0x7F, 0xFF)
+
+
+def make_codebook(seed: int, n: int, tag=(), every_code: bool = False) -> np.ndarray:
+    """A per-layer codebook of n codewords of 8 E4M3 bytes: uint8 [n, 8].
+
+    The first codewords hold, in increasing byte order, every code whose
+    exponent field is at most 9 (magnitudes up to 7.5: both zeros, every
+    subnormal, the small normals; 160 codes = 20 codewords), or with
+    every_code all 256 byte values (32 codewords, the two not-a-number codes
+    replaced by +0 and -0, so up to the largest magnitude 448).  The others
+    take a random sign, a random 3-bit mantissa and an exponent field in
+    4..8 (magnitudes 0.125 .. 3.75, RMS near 1.5, like codewords trained on
+    rows normalised to unit RMS)."""
+    rng = rng_for(seed, "vq-codebook", n, *tag)
+    codes = np.arange(256, dtype=np.int64)
+    if every_code:
+        codes[0x7F], codes[0xFF] = 0x00, 0x80
+    else:
+        codes = codes[((codes >> 3) & 15) <= 9]
+    first = codes.reshape(-1, 8)
+    cb = np.empty((n, 8), dtype=np.uint8)
+    cb[:len(first)] = first
+    m = n - len(first)
+    sign = rng.integers(0, 2, size=(m, 8)) << 7
+    expo = rng.integers(4, 9, size=(m, 8)) << 3
+    mant = rng.integers(0, 8, size=(m, 8))
+    cb[len(first):] = (sign | expo | mant).astype(np.uint8)
+    return cb
 
 
 def make_grid(seed: int) -> np.ndarray:
@@ -361,6 +433,7 @@ class Layer:
     s_down: np.ndarray | None = None
     router_bias: np.ndarray | None = None  # float32 [E]: selection-only bias (None: select on the logits)
     down_gain: np.ndarray | None = None    # float32 [E, d]: per-channel down gains (None: ones)
+    vq_codebook: np.ndarray | None = None  # uint8 [4096 or 8192, 8] E4M3 codewords (VQ routed formats)
     meta: dict = field(default_factory=dict)
 
 
@@ -389,11 +462,19 @@ def random_layer(spec: LayerSpec, seed: int = 0, workload: str = "decode", layer
         w_down[e * dn:(e + 1) * dn] = random_matrix(seed, (workload, layer, e, "down"), spec.fmt_down, d, f)
     L = Layer(spec=spec, w_gate=w_gate, w_up=w_up, w_down=w_down, grid=make_grid(seed),
               w_router=router_weights(seed, (workload, layer, "router"), E, d))
+    n_codes = codebook_size(spec)
+    if n_codes:
+        L.vq_codebook = make_codebook(seed, n_codes, (workload, layer))
     if spec.has_shared:
         L.s_gate = random_matrix(seed, (workload, layer, "shared", "gate"), spec.fmt_shared, f, d)
         L.s_up = random_matrix(seed, (workload, layer, "shared", "up"), spec.fmt_shared, f, d)
         L.s_down = random_matrix(seed, (workload, layer, "shared", "down"), spec.fmt_shared, d, f)
     return L
+
+
+def codebook_size(spec: LayerSpec) -> int:
+    """Codewords a layer's codebook needs (0: no VQ routed format)."""
+    return max([VQ_CODES.get(spec.fmt_gate_up, 0), VQ_CODES.get(spec.fmt_down, 0)])
 
 
 def scaled_spec(E, k, d, f, fmt_gate_up=FMT_IQ2, fmt_down=FMT_Q2K, has_shared=True, fmt_shared=FMT_Q8):

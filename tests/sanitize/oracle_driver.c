@@ -19,12 +19,16 @@ void orc_route_weights(const float* z, const int32_t* idx, int T, int E, int k, 
 void orc_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                 int32_t* pos);
 int orc_dequant(int fmt, const uint8_t* blocks, int64_t n_blocks, const uint8_t* grid, double* out);
+int orc_dequant_rows(int fmt, const uint8_t* rows, int64_t n_rows, int K, const uint8_t* grid, const uint8_t* cb,
+                     double* out);
+double orc_e4m3(int b);
 int orc_ffn(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
-            const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+            const uint8_t* w_down, const uint8_t* grid, const uint8_t* cb, int has_shared, int fmt_sh, const uint8_t* s_gate,
             const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype, int T,
             const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y);
 int orc_ffn_grouped(int E, int d, int f, int k, int fmt_gu, int fmt_dn, const uint8_t* w_gate, const uint8_t* w_up,
-                    const uint8_t* w_down, const uint8_t* grid, int has_shared, int fmt_sh, const uint8_t* s_gate,
+                    const uint8_t* w_down, const uint8_t* grid, const uint8_t* cb, int has_shared, int fmt_sh,
+                    const uint8_t* s_gate,
                     const uint8_t* s_up, const uint8_t* s_down, const float* down_gain, const void* x, int x_dtype,
                     int T, const int32_t* tokens, int n_tok, const int32_t* idx, const float* wt, float* y);
 
@@ -32,18 +36,35 @@ static uint32_t lcg = 12345u;
 static uint32_t next(void) { return lcg = lcg * 1664525u + 1013904223u; }
 static float unif(void) { return (float)(next() >> 8) / 16777216.0f - 0.5f; }
 
-static int bw(int fmt) { return fmt == 3 ? 32 : 256; }
-static int bb(int fmt) { return fmt == 1 ? 66 : fmt == 2 ? 84 : fmt == 4 ? 144 : 34; }
+static int bw(int fmt) { return fmt == 3 || fmt == 5 ? 32 : 256; }
+static int bb(int fmt) { return fmt == 1 ? 66 : fmt == 2 ? 84 : fmt == 4 ? 144 : fmt == 5 ? 17 : 34; }
 
-/* random blocks with scale fields set to 2^-10 (fp16 0x1400) */
+/* random blocks with scale fields set to 2^-10 (fp16 0x1400; E8M0 0x75) */
 static uint8_t* blocks(int fmt, int n) {
   uint8_t* b = (uint8_t*)malloc((size_t)n * bb(fmt));
   for (int i = 0; i < n * bb(fmt); i++) b[i] = (uint8_t)(next() >> 24);
   for (int i = 0; i < n; i++) {
     uint8_t* p = b + (size_t)i * bb(fmt);
+    if (fmt == 5) { p[0] = 0x75; continue; }
     p[0] = 0x00; p[1] = 0x14;
     if (fmt == 2 || fmt == 4) { p[2] = 0x00; p[3] = 0x14; }
   }
+  return b;
+}
+
+/* bytes of one row of K weights (VQ rows: gain, 12-bit stream, 13-bit plane) */
+static int row_bytes(int fmt, int K) {
+  if (fmt == 6 || fmt == 7) return 2 + 3 * K / 16 + (fmt == 7 ? K / 64 : 0);
+  return K / bw(fmt) * bb(fmt);
+}
+
+/* a random matrix of `rows` rows of K weights */
+static uint8_t* matrix(int fmt, int rows, int K) {
+  if (fmt != 6 && fmt != 7) return blocks(fmt, rows * K / bw(fmt));
+  int rb = row_bytes(fmt, K);
+  uint8_t* b = (uint8_t*)malloc((size_t)rows * rb);
+  for (int i = 0; i < rows * rb; i++) b[i] = (uint8_t)(next() >> 24);
+  for (int r = 0; r < rows; r++) { b[(size_t)r * rb] = 0x00; b[(size_t)r * rb + 1] = 0x14; }
   return b;
 }
 
@@ -71,36 +92,48 @@ int main(void) {
   for (int i = -100; i <= 100; i++) acc += orc_sigmoid32((float)i);
   int32_t counts[E], offsets[E + 1], perm[T * k], pos[T * k];
   orc_bucket(idx, T, k, E, counts, offsets, perm, pos);
-  for (int fmt = 1; fmt <= 4; fmt++) {
+  /* codebook of 8192 E4M3 codewords, bit 3 cleared: even exponent fields, never 15, all finite */
+  static uint8_t cb[8192 * 8];
+  for (int i = 0; i < 8192 * 8; i++) cb[i] = (uint8_t)(next() >> 24) & 0xf7;
+  for (int c = 0; c < 256; c++) acc += isnan(orc_e4m3(c)) ? 0.0 : orc_e4m3(c) * 1e-9;
+  for (int fmt = 1; fmt <= 5; fmt++) {
     uint8_t* b = blocks(fmt, 3);
     double w[3 * 256];
     if (orc_dequant(fmt, b, 3, grid, w) != 0) return 2;
     for (int i = 0; i < 3 * bw(fmt); i++) acc += w[i];
     free(b);
   }
-  const int fmts[3][3] = {{1, 2, 3}, {4, 4, 3}, {3, 1, 2}};
-  for (int c = 0; c < 3; c++) {
+  for (int fmt = 6; fmt <= 7; fmt++) {
+    uint8_t* b = matrix(fmt, 3, 256);
+    double w[3 * 256];
+    if (orc_dequant_rows(fmt, b, 3, 256, NULL, cb, w) != 0) return 9;
+    if (orc_dequant_rows(fmt, b, 3, 256, NULL, NULL, w) != -1) return 10;
+    for (int i = 0; i < 3 * 256; i++) acc += w[i];
+    free(b);
+  }
+  const int fmts[5][3] = {{1, 2, 3}, {4, 4, 3}, {3, 1, 2}, {5, 5, 3}, {7, 6, 3}};
+  for (int c = 0; c < 5; c++) {
     const int fgu = fmts[c][0], fdn = fmts[c][1], fsh = fmts[c][2];
-    uint8_t* g = blocks(fgu, E * f * d / bw(fgu));
-    uint8_t* u = blocks(fgu, E * f * d / bw(fgu));
-    uint8_t* dn = blocks(fdn, E * d * f / bw(fdn));
-    uint8_t* sg = blocks(fsh, f * d / bw(fsh));
-    uint8_t* su = blocks(fsh, f * d / bw(fsh));
-    uint8_t* sd = blocks(fsh, d * f / bw(fsh));
+    uint8_t* g = matrix(fgu, E * f, d);
+    uint8_t* u = matrix(fgu, E * f, d);
+    uint8_t* dn = matrix(fdn, E * d, f);
+    uint8_t* sg = matrix(fsh, f, d);
+    uint8_t* su = matrix(fsh, f, d);
+    uint8_t* sd = matrix(fsh, d, f);
     int32_t tok[3] = {4, 0, 4};
-    if (orc_ffn(E, d, f, k, fgu, fdn, g, u, dn, grid, 1, fsh, sg, su, sd, c ? gain : NULL, x, 0, T, NULL, 0, idx,
+    if (orc_ffn(E, d, f, k, fgu, fdn, g, u, dn, grid, cb, 1, fsh, sg, su, sd, c ? gain : NULL, x, 0, T, NULL, 0, idx,
                 wt, y) != 0) return 3;
-    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, 1, fsh, sg, su, sd, c ? gain : NULL, x, 0, T, NULL, 0,
+    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, cb, 1, fsh, sg, su, sd, c ? gain : NULL, x, 0, T, NULL, 0,
                         idx, wt, y2) != 0) return 4;
     if (memcmp(y, y2, sizeof y) != 0) return 5;
-    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, 0, 0, NULL, NULL, NULL, NULL, xb, 1, T, tok, 3, idx,
+    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, cb, 0, 0, NULL, NULL, NULL, NULL, xb, 1, T, tok, 3, idx,
                         wt, y2) != 0) return 6;
     int32_t bad[T * k];
     memcpy(bad, idx, sizeof bad);
     bad[3] = E;
-    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, 0, 0, NULL, NULL, NULL, NULL, x, 0, T, NULL, 0, bad,
+    if (orc_ffn_grouped(E, d, f, k, fgu, fdn, g, u, dn, grid, cb, 0, 0, NULL, NULL, NULL, NULL, x, 0, T, NULL, 0, bad,
                         wt, y2) != -1) return 7;
-    if (orc_ffn(E, d, f, k, fgu, fdn, g, u, dn, grid, 0, 0, NULL, NULL, NULL, NULL, x, 0, T, NULL, 0, bad, wt,
+    if (orc_ffn(E, d, f, k, fgu, fdn, g, u, dn, grid, cb, 0, 0, NULL, NULL, NULL, NULL, x, 0, T, NULL, 0, bad, wt,
                 y2) != -1) return 8;
     for (int i = 0; i < T * d; i++) acc += y[i];
     free(g); free(u); free(dn); free(sg); free(su); free(sd);

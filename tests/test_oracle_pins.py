@@ -152,6 +152,103 @@ def test_mx4_worked_blocks_and_packer():
     assert np.array_equal(synth.pack_mx4(np.array([127], np.uint8), codes).reshape(-1), _bytes(g["mx4_a"]["hex"]))
 
 
+def _torch_e4m3(codes):
+    """E4M3 bytes decoded by torch's float8_e4m3fn (a library routine the
+    oracle does not use), as float64."""
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_every_code_matches_torch_float8():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _torch_e4m3(codes)
+    got = np.array([oracle.e4m3(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_hand_values():
+    for c in _golden()["e4m3_values"]:
+        v = oracle.e4m3(int(c["code"], 16))
+        if c["value"] is None:
+            assert math.isnan(v), c
+        else:
+            assert v == c["value"] and math.copysign(1, v) == math.copysign(1, c["value"]), c
+
+
+def _vq_codebook(entry):
+    cb = np.zeros((entry["n_codes"], 8), np.uint8)
+    for i, h in entry["codewords"].items():
+        cb[int(i)] = _bytes(h)
+    return cb
+
+
+def test_vq_worked_rows_and_packer():
+    g = {r["name"]: r for r in _golden()["vq_rows"]}
+    a, b = g["vq12_a"], g["vq13_b"]
+    w = oracle.dequant_rows(oracle.VQ12, _bytes(a["hex"]), a["K"], codebook=_vq_codebook(a))
+    assert np.array_equal(w.reshape(-1), a["weights"])
+    assert np.array_equal(np.signbit(w.reshape(-1)), np.signbit(a["weights"]))
+    w = oracle.dequant_rows(oracle.VQ13, _bytes(b["hex"]), b["K"], codebook=_vq_codebook(b))
+    assert np.array_equal(w.reshape(-1), np.repeat(b["weights_per_group"], 8))
+    # the packer reproduces the hand bytes
+    assert np.array_equal(synth.pack_vq(np.array([1.0], np.float16), np.array([a["indices"]]), 12).reshape(-1),
+                          _bytes(a["hex"]))
+    assert np.array_equal(synth.pack_vq(np.array([-0.5], np.float16), np.array([b["indices"]]), 13).reshape(-1),
+                          _bytes(b["hex"]))
+    # a VQ row needs its codebook
+    with pytest.raises(ValueError):
+        oracle.dequant_rows(oracle.VQ12, _bytes(a["hex"]), a["K"])
+
+
+def _vq_dense_by_bits(rows, K, fmt, codebook):
+    """VQ rows decoded a second way: indices read with numpy's unpackbits
+    (little bit order) from the documented layout, codewords through torch's
+    float8_e4m3fn.  Returns float64 [R, K]."""
+    n = K // 8
+    rb = 2 + 3 * K // 16 + (K // 64 if fmt == synth.FMT_VQ13 else 0)
+    rows = np.asarray(rows, np.uint8).reshape(-1, rb)
+    gain = rows[:, 0:2].copy().view("<f2").astype(np.float64).reshape(-1)
+    bits = np.unpackbits(rows[:, 2:2 + 3 * K // 16], axis=1, bitorder="little").reshape(-1, n, 12)
+    idx = (bits.astype(np.int64) << np.arange(12)).sum(axis=2)
+    if fmt == synth.FMT_VQ13:
+        plane = np.unpackbits(rows[:, 2 + 3 * K // 16:], axis=1, bitorder="little")[:, :n]
+        idx += plane.astype(np.int64) << 12
+    cw = _torch_e4m3(codebook)
+    return gain[:, None] * cw[idx].reshape(-1, K)
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_VQ12, synth.FMT_VQ13])
+def test_vq_random_rows_against_bit_unpacking(fmt):
+    """Many rows of random indices (so every index bit and every row's own
+    plane matters), several row lengths, against the second decoder."""
+    bits = 12 if fmt == synth.FMT_VQ12 else 13
+    cb = synth.make_codebook(5, synth.VQ_CODES[fmt])
+    for K in (64, 256, 2048):
+        rows = synth.random_vq(np.random.default_rng(K + bits), 17, K, bits)
+        got = oracle.dequant_rows(fmt, rows, K, codebook=cb)
+        ref = _vq_dense_by_bits(rows, K, fmt, cb)
+        assert np.array_equal(got, ref)
+        assert np.all(np.isfinite(got))
+
+
+def test_vq_codebook_spread_and_special_codes():
+    cb = synth.make_codebook(0, 4096)
+    v = _torch_e4m3(cb)
+    assert np.all(np.isfinite(v)) and np.abs(v).max() == 7.5
+    assert set(np.unique(cb[:20])) == {c for c in range(256) if (c >> 3) & 15 <= 9}
+    rms = np.sqrt(np.mean(v[20:] ** 2))
+    assert 1.3 < rms < 1.7
+    every = synth.make_codebook(0, 4096, every_code=True)
+    assert set(np.unique(every[:32])) == set(range(256)) - {0x7F, 0xFF}
+    assert np.all(np.isfinite(_torch_e4m3(every))) and np.abs(_torch_e4m3(every)).max() == 448
+    rows = synth.random_vq(np.random.default_rng(3), 512, 256, 12)
+    w = oracle.dequant_rows(oracle.VQ12, rows, 256, codebook=cb)
+    assert 0.015 < w.std() < 0.03
+
+
 def test_mx4_round_trip_and_error_bound():
     """Blocks whose weights lie on the E2M1 grid times a power of two survive
     quantize -> dequantize exactly; Gaussian blocks round to the nearest grid
@@ -527,6 +624,8 @@ def test_ffn_closed_form_swiglu():
 def _dense(L, fmt, blob, e, rows, K):
     per = blob.size // (L.spec.E if e is not None else 1)
     b = blob if e is None else blob[e * per:(e + 1) * per]
+    if fmt in synth.VQ_FORMATS:
+        return _vq_dense_by_bits(b, K, fmt, L.vq_codebook)
     return oracle.dequant(fmt, b, L.grid).reshape(rows, K)
 
 
@@ -555,6 +654,8 @@ def _numpy_ffn(L, x, idx, wt):
                       fmt_shared=synth.FMT_Q2K),
     synth.scaled_spec(E=5, k=2, d=512, f=256, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q4K),
     synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4),
+    synth.scaled_spec(E=5, k=2, d=256, f=512, fmt_gate_up=synth.FMT_VQ12, fmt_down=synth.FMT_VQ12),
+    synth.scaled_spec(E=5, k=3, d=512, f=256, fmt_gate_up=synth.FMT_VQ13, fmt_down=synth.FMT_VQ13),
 ])
 def test_ffn_matches_numpy_dense_matmul(spec):
     L = synth.random_layer(spec, seed=3, workload="pin")
@@ -572,6 +673,7 @@ def test_ffn_matches_numpy_dense_matmul(spec):
     (synth.scaled_spec(E=7, k=4, d=256, f=256, fmt_gate_up=synth.FMT_Q4K, fmt_down=synth.FMT_Q2K,
                        has_shared=False), True),
     (synth.scaled_spec(E=6, k=3, d=512, f=256, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4), False),
+    (synth.scaled_spec(E=6, k=3, d=256, f=512, fmt_gate_up=synth.FMT_VQ13, fmt_down=synth.FMT_VQ12), True),
 ])
 def test_grouped_ffn_is_bitwise_the_token_loop(spec, gains):
     """The expert-grouped evaluation (each expert dequantised once) performs
