@@ -233,9 +233,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--bias-gain", action="store_true",
                     help="give every layer a router selection bias and per-channel down gains (not the headline)")
-    ap.add_argument("--routed-fmt", choices=["iq2-q2k", "q4k", "mxfp4"], default="iq2-q2k",
-                    help="routed experts: IQ2_XXS-like gate/up + Q2_K-like down (the headline), Q4_K-like "
-                         "or MXFP4 gate/up/down (variants; not the headline)")
+    ap.add_argument("--routed-fmt", choices=["iq2-q2k", "q4k", "mxfp4", "vq12", "vq13"], default="iq2-q2k",
+                    help="routed experts: IQ2_XXS-like gate/up + Q2_K-like down (the headline), Q4_K-like, "
+                         "MXFP4 or 12/13-bit VQ gate/up/down (variants; not the headline)")
     ap.add_argument("--only", default="all",
                     help="comma list of: decode, prefill, small-batch, crossover, long-prefill, probes (default all)")
     ap.add_argument("--pmc-mode", action="store_true",
@@ -267,7 +267,8 @@ def main() -> int:
     timer = Timer(torch)
     spec = synth.DECODE_SPEC
     if args.routed_fmt != "iq2-q2k":
-        fr = synth.FMT_Q4K if args.routed_fmt == "q4k" else synth.FMT_MX4
+        fr = {"q4k": synth.FMT_Q4K, "mxfp4": synth.FMT_MX4, "vq12": synth.FMT_VQ12,
+              "vq13": synth.FMT_VQ13}[args.routed_fmt]
         spec = synth.scaled_spec(E=spec.E, k=spec.k, d=spec.d, f=spec.f, fmt_gate_up=fr, fmt_down=fr)
     E, k, d, f = spec.E, spec.k, spec.d, spec.f
     FGU, FDN = spec.fmt_gate_up, spec.fmt_down
@@ -638,12 +639,17 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i16-fixed-point x i2/i8 integer dot products, fp32 scales",
+        "dtype": ("fp32 activations x E4M3 codewords (routed), i16-fixed-point x i8 (shared)"
+                  if args.routed_fmt in ("vq12", "vq13")
+                  else "i16-fixed-point x i2/i8 integer dot products, fp32 scales"),
         "data": "synthetic",
         "config": {"workload": "decode: one MoE layer, 384 experts, top-6, d=4096, f=2048, shared Q8_0-like "
                                "expert, " + {"iq2-q2k": "IQ2_XXS-like gate/up, Q2_K-like down",
                                              "q4k": "Q4_K-like gate/up and down",
-                                             "mxfp4": "MXFP4 gate/up and down"}[args.routed_fmt] + ", T=1 fp32 token",
+                                             "mxfp4": "MXFP4 gate/up and down",
+                                             "vq12": "VQ 12-bit codeword indices gate/up and down",
+                                             "vq13": "VQ 13-bit codeword indices gate/up and down"}[args.routed_fmt]
+                               + ", T=1 fp32 token",
                    "routed_formats": args.routed_fmt,
                    "layer_descriptors": N_DESC, "routed_copies": 2, "graph_steps": N_DESC,
                    "router_bias_and_down_gains": bool(args.bias_gain)},

@@ -112,6 +112,31 @@
  *                (0, 0.5, 1, 1.5, 2, 3, 4, 6),
  *   w_i = 2^(s - 127) * value(code_i).
  *
+ * MOE_FMT_VQ12_L / MOE_FMT_VQ13_L -- rows of 8-dimensional vector-quantized
+ *   weights, the routed-expert base format of "YoungAi -- DeepSeek V4.1 Flash
+ *   on one DGX Spark", section 4.1: every 8 consecutive weights of a row are
+ *   one 12-bit (1.5 bits per weight) or 13-bit (1.625) index into the
+ *   layer's codebook, times one fp16 gain per row; routed gate/up and down
+ *   only.  There are no blocks: a tensor is [expert][row] rows of
+ *   2 + 3K/16 (+ K/64 for 13 bits) bytes, K a multiple of 64:
+ *   bytes 0-1          gain g (fp16),
+ *   next 3K/16 bytes   the low 12 bits of every index as one little-endian
+ *                      bit stream: index j occupies stream bits 12j ..
+ *                      12j + 11, bit b of the stream being bit b % 8 of
+ *                      stream byte b / 8,
+ *   next K/64 bytes    (13 bits only) the bit plane: bit j % 8 of plane byte
+ *                      j / 8 is bit 12 of index j (the page's "12 + 1"
+ *                      layout, which keeps the 12-bit stream's geometry);
+ *   w[8j + i] = g * C[idx_j][i]  (i = 0..7).
+ *   The codebook C (moe_layer.vq_codebook) is uint8 [n][8]: codeword c is 8
+ *   E4M3 bytes (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits
+ *   2..0; exponent 0 is subnormal, M/8 * 2^-6; the largest finite value is
+ *   448; 0x7f and 0xff are not numbers and must not occur), n = 4096 or 8192
+ *   (moe_layer.vq_codes), at least 2^bits for every VQ matrix of the layer.
+ *   One codebook serves all experts and the three matrices of a layer (same
+ *   page and section), so a layer's routed gate/up and down are either both
+ *   VQ formats (of either width) or neither.
+ *
  * Device layout (MOE_LAYOUT_DEVICE).  The compute entry points read weights
  * only in this layout, produced from the canonical one by moe_repack (the
  * map is a bijection on bytes and the total size is unchanged).  Every
@@ -130,6 +155,10 @@
  *              plane Q  int8 q[R][nb][32]
  *   MXFP4_L  : plane S  E8M0 s[R][nb]                 (R nb bytes), then
  *              plane Q  codes[R][nb][16]
+ *   VQ12_L   : plane G  fp16 gain[R]                   (2 R bytes), then
+ *              plane I  index stream[R][3K/16]
+ *   VQ13_L   : planes G and I as for VQ12_L, then
+ *              plane B  bit plane[R][K/64]
  *   (nb counts 256-weight superblocks for IQ2XXS_L/Q2K_L/Q4K_L and 32-weight
  *   blocks for Q8_0_L and MXFP4_L.)  Plane offsets follow from R and nb alone.
  * -------------------------------------------------------------------------
@@ -168,7 +197,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes. */
 #define MOE_OK 0
@@ -188,6 +217,8 @@ extern "C" {
 #define MOE_FMT_Q8_0_L 3
 #define MOE_FMT_Q4K_L 4    /* routed experts only */
 #define MOE_FMT_MXFP4_L 5  /* routed experts only */
+#define MOE_FMT_VQ12_L 6   /* routed experts only; needs moe_layer.vq_codebook */
+#define MOE_FMT_VQ13_L 7   /* routed experts only; needs a codebook of 8192 codewords */
 
 /* Weight layouts. */
 #define MOE_LAYOUT_CANONICAL 0
@@ -219,7 +250,9 @@ extern "C" {
  * Routed gate/up and down may each be any of the formats above; the shared
  * expert (if present) uses fmt_shared (IQ2XXS_L, Q2K_L or Q8_0_L) for its
  * three matrices and has d_ff rows in gate/up like the routed experts.
- * iq2_grid is required whenever any matrix is IQ2XXS_L.
+ * iq2_grid is required whenever any matrix is IQ2XXS_L; vq_codebook and
+ * vq_codes whenever a routed matrix is VQ12_L or VQ13_L (otherwise they are
+ * not read).
  */
 typedef struct moe_layer {
   uint32_t abi_version;       /* must equal MOE_ABI_VERSION */
@@ -242,6 +275,8 @@ typedef struct moe_layer {
   const void* s_down;         /* [d rows][f] */
   const float* router_bias;   /* nullable fp32 [E]: selection-only router bias */
   const float* down_gain;     /* nullable fp32 [E][d], 16-byte aligned: down gains */
+  const uint8_t* vq_codebook; /* E4M3 codewords [vq_codes][8], 16-byte aligned (VQ formats) */
+  int32_t vq_codes;           /* 4096 or 8192 (VQ formats) */
 } moe_layer;
 
 /* ABI version compiled into the library (== MOE_ABI_VERSION of its header). */
@@ -290,8 +325,8 @@ int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t K,
  * s_gate, s_up, s_down if the layer has a shared expert), each
  * moe_matrix_bytes() of its tensor, 16-byte aligned, overlapping no source
  * and no other destination.  Then *device_out [host] becomes *canonical with
- * those six pointers and layout = MOE_LAYOUT_DEVICE: the grid, router, bias
- * and gain arrays have a single layout and are shared, not copied.
+ * those six pointers and layout = MOE_LAYOUT_DEVICE: the grid, router, bias,
+ * gain and codebook arrays have a single layout and are shared, not copied.
  * Everything is validated before the first launch; on an error *device_out
  * is left unchanged.  Device copies with aligned quant streams follow the
  * load-time payload re-alignment of the YoungAi page, section 4.4 (decode,

@@ -204,8 +204,10 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 static bool fmt_known(int f) {
   return f == MOE_FMT_IQ2XXS_L || f == MOE_FMT_Q2K_L || f == MOE_FMT_Q8_0_L || f == MOE_FMT_Q4K_L ||
-         f == MOE_FMT_MXFP4_L;
+         f == MOE_FMT_MXFP4_L || f == MOE_FMT_VQ12_L || f == MOE_FMT_VQ13_L;
 }
+static_assert(MOE_FMT_VQ12_L == FMT_VQ12 && MOE_FMT_VQ13_L == FMT_VQ13 && MOE_FMT_MXFP4_L == FMT_MX4,
+              "format ids of the header and of the kernels agree");
 
 #define NEED_PTR(p, what)                                                                       \
   do {                                                                                          \
@@ -266,11 +268,26 @@ static int check_layer(const char* fn, const moe_layer* L, bool need_router, int
   NEED_PTR(L->w_up, "w_up");
   NEED_PTR(L->w_down, "w_down");
   bool iq2 = L->fmt_gate_up == MOE_FMT_IQ2XXS_L || L->fmt_down == MOE_FMT_IQ2XXS_L;
+  if (is_vq(L->fmt_gate_up) || is_vq(L->fmt_down)) {
+    if (is_vq(L->fmt_gate_up) != is_vq(L->fmt_down))
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "%s: the VQ formats cover a layer's routed gate/up and down together (one codebook per layer); "
+                  "gate/up format %d with down format %d", fn, L->fmt_gate_up, L->fmt_down);
+    NEED_PTR(L->vq_codebook, "vq_codebook");
+    if (L->vq_codes != 4096 && L->vq_codes != 8192)
+      return fail(MOE_ERR_INVALID_ARG, "%s: vq_codes %d is neither 4096 nor 8192", fn, L->vq_codes);
+    const int need = max(is_vq(L->fmt_gate_up) ? vq_codes(L->fmt_gate_up) : 0,
+                         is_vq(L->fmt_down) ? vq_codes(L->fmt_down) : 0);
+    if (L->vq_codes < need)
+      return fail(MOE_ERR_INVALID_ARG, "%s: a 13-bit VQ matrix needs 8192 codewords, the codebook has %d", fn,
+                  L->vq_codes);
+  }
   if (L->has_shared) {
     if (!fmt_known(L->fmt_shared)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown shared format %d", fn, L->fmt_shared);
-    if (L->fmt_shared == MOE_FMT_Q4K_L || L->fmt_shared == MOE_FMT_MXFP4_L)
+    if (L->fmt_shared == MOE_FMT_Q4K_L || L->fmt_shared == MOE_FMT_MXFP4_L || is_vq(L->fmt_shared))
       return fail(MOE_ERR_UNSUPPORTED,
-                  "%s: Q4K_L and MXFP4_L are routed-expert formats (shared expert: IQ2XXS_L, Q2K_L or Q8_0_L)", fn);
+                  "%s: Q4K_L, MXFP4_L and the VQ formats are routed-expert formats (shared expert: IQ2XXS_L, "
+                  "Q2K_L or Q8_0_L)", fn);
     NEED_PTR(L->s_gate, "s_gate");
     NEED_PTR(L->s_up, "s_up");
     NEED_PTR(L->s_down, "s_down");
@@ -419,9 +436,9 @@ extern "C" int moe_matrix_bytes(int32_t fmt, int32_t n_experts, int32_t rows, in
   const char* fn = "moe_matrix_bytes";
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "%s: bytes is null", fn);
   if (!fmt_known(fmt)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
-  if (n_experts < 1 || rows < 1 || K < 1 || K % block_weights(fmt) != 0)
+  if (n_experts < 1 || rows < 1 || K < 1 || K % k_multiple(fmt) != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: bad shape (%d experts, %d rows, K %d)", fn, n_experts, rows, K);
-  *bytes = (size_t)n_experts * rows * (K / block_weights(fmt)) * block_bytes(fmt);
+  *bytes = (size_t)matrix_bytes(fmt, n_experts, rows, K);
   return ok();
 }
 
@@ -461,16 +478,15 @@ extern "C" int moe_repack(int32_t fmt, int32_t n_experts, int32_t rows, int32_t 
                           int32_t direction, void* stream) {
   const char* fn = "moe_repack";
   if (!fmt_known(fmt)) return fail(MOE_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
-  if (n_experts < 1 || rows < 1 || K < 1 || K % block_weights(fmt) != 0)
+  if (n_experts < 1 || rows < 1 || K < 1 || K % k_multiple(fmt) != 0)
     return fail(MOE_ERR_INVALID_ARG, "%s: bad shape (%d experts, %d rows, K %d)", fn, n_experts, rows, K);
   if (direction != MOE_REPACK_TO_DEVICE && direction != MOE_REPACK_TO_CANONICAL)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown direction %d", fn, direction);
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "%s: null buffer", fn);
   if (src == dst) return fail(MOE_ERR_INVALID_ARG, "%s: src and dst must be distinct buffers", fn);
-  const int64_t nb = (int64_t)n_experts * rows * (K / block_weights(fmt));
   hipStream_t s = (hipStream_t)stream;
   const int pid = prof_begin("repack", s);
-  hipError_t e = launch_repack(fmt, nb, src, dst, direction == MOE_REPACK_TO_DEVICE, s);
+  hipError_t e = launch_repack(fmt, (int64_t)n_experts * rows, K, src, dst, direction == MOE_REPACK_TO_DEVICE, s);
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -501,11 +517,11 @@ extern "C" int moe_prepare_weights(const moe_layer* canonical, moe_layer* device
     const Job& j = jobs[i];
     if (!j.dst) return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s is null", fn, j.name);
     if (!aligned16(j.dst)) return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s is not 16-byte aligned", fn, j.name);
-    const size_t bytes = (size_t)j.E * j.rows * (j.K / block_weights(j.fmt)) * block_bytes(j.fmt);
+    const size_t bytes = (size_t)matrix_bytes(j.fmt, j.E, j.rows, j.K);
     const uintptr_t d0 = (uintptr_t)j.dst, d1 = d0 + bytes;
     for (int k = 0; k < n_jobs; k++) {  // no destination may overlap a source or another destination
       const Job& o = jobs[k];
-      const size_t ob = (size_t)o.E * o.rows * (o.K / block_weights(o.fmt)) * block_bytes(o.fmt);
+      const size_t ob = (size_t)matrix_bytes(o.fmt, o.E, o.rows, o.K);
       const uintptr_t s0 = (uintptr_t)o.src, s1 = s0 + ob;
       if (d0 < s1 && s0 < d1)
         return fail(MOE_ERR_INVALID_ARG, "%s: device_out->%s overlaps the canonical %s", fn, j.name, o.name);
@@ -519,9 +535,8 @@ extern "C" int moe_prepare_weights(const moe_layer* canonical, moe_layer* device
   hipStream_t s = (hipStream_t)stream;
   for (int i = 0; i < n_jobs; i++) {
     const Job& j = jobs[i];
-    const int64_t nb = (int64_t)j.E * j.rows * (j.K / block_weights(j.fmt));
     const int pid = prof_begin("repack", s);
-    hipError_t e = launch_repack(j.fmt, nb, j.src, const_cast<void*>(j.dst), 1, s);
+    hipError_t e = launch_repack(j.fmt, (int64_t)j.E * j.rows, j.K, j.src, const_cast<void*>(j.dst), 1, s);
     prof_end(pid, s);
     if (e != hipSuccess) return hip_fail(e, fn);
   }
@@ -608,6 +623,7 @@ static DecodeLaunch decode_launch(const moe_layer* L, const void* x, int x_dtype
   D.s_up = L->s_up;
   D.s_down = L->s_down;
   D.grid = L->iq2_grid;
+  D.vq_cb = L->vq_codebook;
   D.w_router = L->w_router;
   D.x = x;
   D.x_dtype = x_dtype;
@@ -634,6 +650,7 @@ static PrefillLaunch prefill_launch(const moe_layer* L, const void* x, int x_dty
   P.s_up = L->s_up;
   P.s_down = L->s_down;
   P.grid = L->iq2_grid;
+  P.vq_cb = L->vq_codebook;
   P.x = x;
   P.x_dtype = x_dtype;
   P.down_gain = L->down_gain;

@@ -26,7 +26,7 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecodeWsLayout {
-  size_t xq, xs, xq_s, xs_s, hsh, hq, hs, total;
+  size_t xq, xs, xq_s, xs_s, hsh, hq, hs, hf, total;
 };
 
 DecodeWsLayout ws_layout(int T, int k, int d, int f) {
@@ -46,6 +46,8 @@ DecodeWsLayout ws_layout(int T, int k, int d, int f) {
   off = align256(off + (size_t)T * k * (f / 16) * G16_BYTES);
   L.hs = off;
   off = align256(off + (size_t)T * k * (f / 16) * 4);
+  L.hf = off;
+  off = align256(off + (size_t)T * k * f * 4);
   L.total = off;
   return L;
 }
@@ -55,8 +57,6 @@ hipError_t cu_count(int* n) {
   int per_cu = 0;
   return launch_shape(nullptr, 0, 0, 0, &per_cu, n);
 }
-
-int64_t row_bytes(int fmt, int K) { return (int64_t)(K / block_weights(fmt)) * block_bytes(fmt); }
 
 }  // namespace
 
@@ -77,6 +77,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     a.s_gate = a.s_up = a.s_down = a.gate;
   }
   a.grid = L.grid;
+  a.vq_cb = L.vq_cb;
   a.w_router = L.w_router;
   a.E = L.E;
   a.d = L.d;
@@ -105,6 +106,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.hsh = reinterpret_cast<float*>(q + W.hsh);
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);
+  a.hf = reinterpret_cast<float*>(q + W.hf);
   a.y = L.y;
   int ncu = 256;
   if (hipError_t e = cu_count(&ncu); e != hipSuccess) return e;

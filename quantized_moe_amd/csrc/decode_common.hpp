@@ -679,7 +679,7 @@ struct RowScales {
 template <int FMT, int K, int NM, int NR>
 struct ScaleStage {
   using RS = RowScales<FMT, K>;
-  static constexpr int CPR = RS::BYTES / 16;  // chunks per row
+  static constexpr int CPR = RS::BYTES >= 16 ? RS::BYTES / 16 : 1;  // chunks per row (only staged rows use it)
   static constexpr int CH = NM * NR * CPR;
   static constexpr int NV = (CH + 63) / 64;
   uint4 v[NV];
@@ -911,6 +911,7 @@ struct DecodeArgs {
   QMat gate, up, down;        // routed experts
   QMat s_gate, s_up, s_down;  // shared expert
   const uint8_t* grid;
+  const uint8_t* vq_cb;       // E4M3 codewords [n][8] (VQ routed formats)
   const float* w_router;
   int E, d, f, k, T;
   int has_shared;
@@ -933,6 +934,7 @@ struct DecodeArgs {
   float* hsh;        // [T][f] shared SwiGLU output, fp32
   uint8_t* hq;       // [T*k][f/16] quantized routed SwiGLU outputs
   float* hs;         // [T*k][f/16]
+  float* hf;         // [T*k][f] routed SwiGLU outputs in fp32 (VQ routed formats)
   float* y;          // [T][d]
 };
 

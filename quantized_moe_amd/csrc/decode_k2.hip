@@ -13,6 +13,10 @@
 // while the routes are not yet known.  Then every wave requests its rows'
 // scale bytes and first weights and the rows run software-pipelined (x comes
 // quantized from the first launch).
+//
+// VQ routed formats: waves 1..7 also copy the codebook into LDS during the
+// prologue; the rows take x in fp32 straight from the caller's tensor and
+// write h in fp32 (no quantization: the down rows read it as it is).
 #include "decode_rows.hpp"
 #include "topk.hpp"
 
@@ -25,7 +29,7 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   __shared__ __attribute__((aligned(16))) float hbuf[16 * GCNT];
   __shared__ int s_sel[TOPK_MAX_K];
   __shared__ float s_zs[TOPK_MAX_K];
-  using G = Geo<FMT, D>;
+  extern __shared__ __align__(16) uint8_t k2_cb[];  // VQ: the codebook (dynamic LDS)
   constexpr int RPW = 2 * GCNT;  // h rows per wave
   // One step of codes in flight ahead of the compute: the rows are bound by
   // the decode arithmetic once streaming, and a deeper start (every wave of
@@ -65,6 +69,7 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
       s_sel[lane] = a.idx[(int64_t)t * a.k + lane];
     }
   } else {
+    if constexpr (is_vq(FMT)) vq_stage_codebook(a.vq_cb, k2_cb, vq_codes(FMT), threadIdx.x - 64, THREADS - 64);
     if constexpr (FMT == FMT_IQ2 || FS == FMT_IQ2) iq2_build(a.grid, threadIdx.x - 64, &itab);  // 384 items
     if constexpr (FS != FMT_IQ2) {
       if (a.shared_k2) shared_rows();
@@ -76,11 +81,19 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
   }
 
   // ---- this wave's rows, software-pipelined ----
-  gateup_rows<FMT, D, RPW, PD>(a.gate, a.up, a.E, a.f, a.k, R0 + wave * RPW, t, s_sel, -1,
-                               a.xq + (int64_t)t * (D / 64) * CHUNK_BYTES, a.xs + (int64_t)t * (D / 64), &itab,
-                               s_scl + wave * SCL_BYTES, hbuf + wave * RPW);
-  __syncthreads();
-  if (wave == 0) quant_g32(hbuf, GCNT, 0, down_layout, a.hq + (int64_t)g0 * G16_BYTES, a.hs + g0);
+  if constexpr (is_vq(FMT)) {
+    VqAct<D> act;
+    act.load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
+             (threadIdx.x & 63) % VqGeo<D>::LPR);
+    vq_gateup_rows<FMT, D, RPW, 2>(a.gate, a.up, a.E, a.f, a.k, R0 + wave * RPW, t, s_sel, act, k2_cb,
+                                   a.hf + R0 + wave * RPW);
+  } else {
+    gateup_rows<FMT, D, RPW, PD>(a.gate, a.up, a.E, a.f, a.k, R0 + wave * RPW, t, s_sel, -1,
+                                 a.xq + (int64_t)t * (D / 64) * CHUNK_BYTES, a.xs + (int64_t)t * (D / 64), &itab,
+                                 s_scl + wave * SCL_BYTES, hbuf + wave * RPW);
+    __syncthreads();
+    if (wave == 0) quant_g32(hbuf, GCNT, 0, down_layout, a.hq + (int64_t)g0 * G16_BYTES, a.hs + g0);
+  }
   // The token's first block publishes its routes and mixing weights (needed
   // only by the next launch, so off the prologue's critical path).
   if (wave == 1 && a.fused_topk && R0 % (a.k * a.f) == 0) {
@@ -97,7 +110,14 @@ __global__ __launch_bounds__(THREADS) void k2_kernel(DecodeArgs a, int down_layo
 
 template <int FMT, int FS, int D, int GCNT>
 static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, hipStream_t s) {
-  QMOE_LAUNCH((k2_kernel<FMT, FS, D, GCNT>), dim3(blocks), dim3(THREADS), 0, s, a, down_layout);
+  constexpr int dyn = is_vq(FMT) ? vq_codes(FMT) * 8 : 0;  // the codebook in LDS
+  if constexpr (dyn > 0) {  // (raises the kernel's dynamic-LDS limit on first use)
+    int per_cu = 0, n_cus = 0;
+    if (hipError_t e = launch_shape((const void*)k2_kernel<FMT, FS, D, GCNT>, THREADS, dyn, dyn, &per_cu, &n_cus);
+        e != hipSuccess)
+      return e;
+  }
+  QMOE_LAUNCH((k2_kernel<FMT, FS, D, GCNT>), dim3(blocks), dim3(THREADS), dyn, s, a, down_layout);
   return hipGetLastError();
 }
 
@@ -126,6 +146,8 @@ hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks,
     case FMT_Q2K: return run_k2_s<FMT_Q2K, D>(a, fs, gcnt, blocks, down_layout, s); \
     case FMT_Q4K: return run_k2_s<FMT_Q4K, D>(a, fs, gcnt, blocks, down_layout, s); \
     case FMT_MX4: return run_k2_s<FMT_MX4, D>(a, fs, gcnt, blocks, down_layout, s); \
+    case FMT_VQ12: return run_k2_s<FMT_VQ12, D>(a, fs, gcnt, blocks, down_layout, s); \
+    case FMT_VQ13: return run_k2_s<FMT_VQ13, D>(a, fs, gcnt, blocks, down_layout, s); \
     default: return run_k2_s<FMT_Q8, D>(a, fs, gcnt, blocks, down_layout, s);       \
   }
   switch (a.d) {

@@ -8,7 +8,8 @@
 // each, or two tasks of 8 rows) and the shared expert (in two or four
 // tasks); a wave runs one task at a time with that task's h slice in
 // registers (the shared expert's fp32 h is quantized by the task itself).
-// Row results meet in LDS.
+// Row results meet in LDS.  VQ routed down rows read the fp32 h of the
+// previous launch and the codebook, which the block first copies into LDS.
 #include "decode_rows.hpp"
 
 namespace qmoe {
@@ -64,13 +65,13 @@ __global__ __launch_bounds__(64 * k3_waves(FR, FS, F)) void k3_kernel(DecodeArgs
   constexpr int SCL_S = RowScales<FS, F>::STAGE ? SH_ROWS * RowScales<FS, F>::BYTES : 16;
   constexpr int SCL_BYTES = SCL_R > SCL_S ? SCL_R : SCL_S;
   __shared__ __attribute__((aligned(16))) uint8_t s_scl[K3_WAVES * SCL_BYTES];
+  extern __shared__ __align__(16) uint8_t k3_cb[];  // VQ: the codebook (dynamic LDS)
   const int wave = threadIdx.x >> 6;
   const int t = blockIdx.y;
   const int row0 = blockIdx.x * DN_ROWS;
-  if constexpr (FR == FMT_IQ2 || FS == FMT_IQ2) {
-    iq2_build(a.grid, threadIdx.x, &itab);
-    __syncthreads();
-  }
+  if constexpr (is_vq(FR)) vq_stage_codebook(a.vq_cb, k3_cb, vq_codes(FR), threadIdx.x, 64 * K3_WAVES);
+  if constexpr (FR == FMT_IQ2 || FS == FMT_IQ2) iq2_build(a.grid, threadIdx.x, &itab);
+  if constexpr (is_vq(FR) || FR == FMT_IQ2 || FS == FMT_IQ2) __syncthreads();
   constexpr int NG = F / 16;  // groups of 16 per h vector
   constexpr int RT_ROWS = DN_ROWS / RT_PARTS;
   const int n_rt = a.k * RT_PARTS;
@@ -82,8 +83,13 @@ __global__ __launch_bounds__(64 * k3_waves(FR, FS, F)) void k3_kernel(DecodeArgs
       const int e = a.idx[r];
       // the expert's output gains scale its row results (ye holds g * y_e)
       const float* gain = a.down_gain && (unsigned)e < (unsigned)a.E ? a.down_gain + (int64_t)e * a.d : nullptr;
-      down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hq + r * NG * G16_BYTES, a.hs + r * NG,
-                                nullptr, gain, &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
+      if constexpr (is_vq(FR)) {
+        vq_down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hf + r * F, gain, k3_cb,
+                                     ye + q * DN_ROWS + part * RT_ROWS);
+      } else {
+        down_rows<FR, F, RT_ROWS>(a.down, e, a.E, row0 + part * RT_ROWS, a.hq + r * NG * G16_BYTES, a.hs + r * NG,
+                                  nullptr, gain, &itab, s_scl + wave * SCL_BYTES, ye + q * DN_ROWS + part * RT_ROWS);
+      }
     } else {
       const int part = task - n_rt;
       down_rows<FS, F, SH_ROWS>(a.s_down, 0, 1, row0 + part * SH_ROWS, nullptr, nullptr, a.hsh + (int64_t)t * F,
@@ -102,7 +108,15 @@ __global__ __launch_bounds__(64 * k3_waves(FR, FS, F)) void k3_kernel(DecodeArgs
 
 template <int FR, int FS, int F>
 static hipError_t run_k3(const DecodeArgs& a, hipStream_t s) {
-  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(64 * k3_waves(FR, FS, F)), 0, s, a);
+  constexpr int dyn = is_vq(FR) ? vq_codes(FR) * 8 : 0;  // the codebook in LDS
+  constexpr int threads = 64 * k3_waves(FR, FS, F);
+  if constexpr (dyn > 0) {  // (raises the kernel's dynamic-LDS limit on first use)
+    int per_cu = 0, n_cus = 0;
+    if (hipError_t e = launch_shape((const void*)k3_kernel<FR, FS, F>, threads, dyn, dyn, &per_cu, &n_cus);
+        e != hipSuccess)
+      return e;
+  }
+  QMOE_LAUNCH((k3_kernel<FR, FS, F>), dim3(a.d / DN_ROWS, a.T), dim3(threads), dyn, s, a);
   return hipGetLastError();
 }
 
@@ -119,6 +133,8 @@ static hipError_t run_k3_f(const DecodeArgs& a, int fr, int fs, hipStream_t s) {
     case FMT_Q2K: K3_FS(FMT_Q2K)
     case FMT_Q4K: K3_FS(FMT_Q4K)
     case FMT_MX4: K3_FS(FMT_MX4)
+    case FMT_VQ12: K3_FS(FMT_VQ12)
+    case FMT_VQ13: K3_FS(FMT_VQ13)
     default: K3_FS(FMT_Q8)
   }
 #undef K3_FS

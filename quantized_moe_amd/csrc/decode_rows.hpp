@@ -5,6 +5,7 @@
 
 #include "decode_common.hpp"
 #include "topk.hpp"
+#include "vq.hpp"
 
 namespace qmoe {
 namespace dec {
@@ -284,6 +285,175 @@ struct DownRows {
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// VQ rows (MOE_FMT_VQ12_L / VQ13_L)
+// ---------------------------------------------------------------------------
+// The activations stay fp32 (x as given, h as the gate/up rows wrote it) and
+// each codeword is converted to fp32 from the LDS codebook: 8 fused
+// multiply-adds per index, no fixed point.  A row of K inputs is K / 64
+// pieces; lane (sub, c) with sub = lane / LPR, c = lane % LPR takes pieces
+// c + LPR * k (k < CPL) of row sub of each step.
+template <int K>
+struct VqGeo {
+  static constexpr int PR = K / 64;
+  static constexpr int LPR = PR < 64 ? PR : 64;
+  static constexpr int CPL = PR / LPR;
+  static constexpr int RPS = 64 / LPR;
+};
+
+// A lane's activation slice: CPL pieces of 64 fp32 values.
+template <int K>
+struct VqAct {
+  using G = VqGeo<K>;
+  float v[G::CPL][64];
+  // from an fp32 (x_dtype X_F32) or bf16 vector of K values
+  __device__ __forceinline__ void load(const void* src, int x_dtype, int c) {
+#pragma unroll
+    for (int k = 0; k < G::CPL; k++) {
+      const int i0 = 64 * (c + G::LPR * k);
+      if (x_dtype == X_BF16) {
+        const uint16_t* p = static_cast<const uint16_t*>(src) + i0;
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const uint4 b = ld16(p + 8 * u);
+          const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            v[k][8 * u + 2 * i] = __uint_as_float(bw[i] << 16);
+            v[k][8 * u + 2 * i + 1] = __uint_as_float(bw[i] & 0xffff0000u);
+          }
+        }
+      } else {
+        const float* p = static_cast<const float*>(src) + i0;
+#pragma unroll
+        for (int u = 0; u < 16; u++) {
+          const float4 f = *reinterpret_cast<const float4*>(p + 4 * u);
+          v[k][4 * u] = f.x;
+          v[k][4 * u + 1] = f.y;
+          v[k][4 * u + 2] = f.z;
+          v[k][4 * u + 3] = f.w;
+        }
+      }
+    }
+  }
+};
+
+// sum over the piece's 64 inputs of codeword value * activation, in a fixed
+// order (two chains: even and odd indices, added at the end)
+template <bool B13>
+__device__ __forceinline__ float vq_dot(const VqPiece& p, const float* x, const uint8_t* cb) {
+  float acc[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int q = 0; q < 8; q++) {
+    float w[8];
+    vq_to_f32(vq_codeword(cb, vq_index<B13>(p, q)), w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[q & 1] = __builtin_fmaf(w[i], x[8 * q + i], acc[q & 1]);
+  }
+  return acc[0] + acc[1];
+}
+
+__device__ __forceinline__ float vq_gain(const QMat& m, int64_t row) {
+  return half_bits_to_float(reinterpret_cast<const uint16_t*>(m.p_scale)[row]);
+}
+
+// One wave's RPW consecutive h rows starting at global row Rw (route-major,
+// as gateup_rows) of token t against the fp32 slice act of x:
+// h = silu(g_G (C x)) * (g_U (C x)) per row, to out[0 .. RPW) (0 for an
+// out-of-range expert id).  PD steps of codes are kept in flight.
+template <int FMT, int D, int RPW, int PD>
+__device__ __forceinline__ void vq_gateup_rows(const QMat& gm, const QMat& um, int E, int f, int k, int Rw, int t,
+                                               const int* s_sel, const VqAct<D>& act, const uint8_t* cb,
+                                               float* out) {
+  using G = VqGeo<D>;
+  constexpr bool B13 = FMT == FMT_VQ13;
+  constexpr int NS = (RPW + G::RPS - 1) / G::RPS;
+  const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
+  const int r0 = Rw / f;
+  const int n0 = Rw - r0 * f;
+  const int jb = f - n0;
+  const int r1 = min(r0 + 1, t * k + k - 1);
+  const int e0 = s_sel[r0 - t * k], e1 = s_sel[r1 - t * k];
+  const bool ok0 = (unsigned)e0 < (unsigned)E, ok1 = (unsigned)e1 < (unsigned)E;
+  VqPiece pg[NS][G::CPL], pu[NS][G::CPL];
+  float gg[NS], gu[NS];
+  bool ok[NS];
+  int lr[NS];
+  auto issue = [&](int s) {
+    const int jj = s * G::RPS + sub;
+    const bool valid = jj < RPW;
+    const int j = valid ? jj : 0;
+    lr[s] = j;
+    const bool second = j >= jb;
+    ok[s] = valid && (second ? ok1 : ok0);
+    const int e = second ? (ok1 ? e1 : 0) : (ok0 ? e0 : 0);
+    const int64_t row = (int64_t)e * f + (second ? n0 + j - f : n0 + j);
+    gg[s] = vq_gain(gm, row);
+    gu[s] = vq_gain(um, row);
+#pragma unroll
+    for (int kk = 0; kk < G::CPL; kk++) {
+      pg[s][kk] = vq_load_piece<B13>(gm.p_a, gm.p_b, row, D, c + G::LPR * kk);
+      pu[s][kk] = vq_load_piece<B13>(um.p_a, um.p_b, row, D, c + G::LPR * kk);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < PD && s < NS; s++) issue(s);
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    if (s + PD < NS) issue(s + PD);
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < G::CPL; kk++) {
+      g += vq_dot<B13>(pg[s][kk], act.v[kk], cb);
+      u += vq_dot<B13>(pu[s][kk], act.v[kk], cb);
+    }
+    g = group_sum<G::LPR>(g);
+    u = group_sum<G::LPR>(u);
+    if (c == G::LPR - 1 && s * G::RPS + sub < RPW) out[lr[s]] = ok[s] ? silu(g * gg[s]) * (u * gu[s]) : 0.0f;
+  }
+}
+
+// ROWS rows r0 .. r0 + ROWS - 1 of expert e's VQ down matrix against the
+// fp32 h vector hf (K values): out[j] = gain_row * (C h) (times the
+// expert's per-channel output gain when given; 0 for an out-of-range e).
+template <int FMT, int K, int ROWS>
+__device__ __forceinline__ void vq_down_rows(const QMat& m, int e, int E, int r0, const float* hf,
+                                             const float* gain, const uint8_t* cb, float* out) {
+  using G = VqGeo<K>;
+  constexpr bool B13 = FMT == FMT_VQ13;
+  constexpr int NS = (ROWS + G::RPS - 1) / G::RPS;
+  constexpr int PD = G::CPL > 1 ? 2 : 4;  // steps of codes in flight
+  const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
+  if ((unsigned)e >= (unsigned)E) {
+    if (lane < ROWS) out[lane] = 0.0f;
+    return;
+  }
+  VqPiece p[NS][G::CPL];
+  float gr[NS], gc[NS];
+  auto issue = [&](int s) {
+    const int j = min(s * G::RPS + sub, ROWS - 1);
+    const int64_t row = (int64_t)e * m.rows + r0 + j;
+    gr[s] = vq_gain(m, row);
+    gc[s] = gain ? gain[r0 + j] : 1.0f;
+#pragma unroll
+    for (int kk = 0; kk < G::CPL; kk++) p[s][kk] = vq_load_piece<B13>(m.p_a, m.p_b, row, K, c + G::LPR * kk);
+  };
+  VqAct<K> act;
+  act.load(hf, X_F32, c);  // requested before the codes
+#pragma unroll
+  for (int s = 0; s < PD && s < NS; s++) issue(s);
+#pragma unroll
+  for (int s = 0; s < NS; s++) {
+    if (s + PD < NS) issue(s + PD);
+    float v = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < G::CPL; kk++) v += vq_dot<B13>(p[s][kk], act.v[kk], cb);
+    v = group_sum<G::LPR>(v);
+    const int j = s * G::RPS + sub;
+    if (c == G::LPR - 1 && j < ROWS) out[j] = (v * gr[s]) * gc[s];
+  }
+}
 
 }  // namespace dec
 }  // namespace qmoe

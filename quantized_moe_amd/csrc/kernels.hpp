@@ -60,6 +60,7 @@ struct DecodeLaunch {
   int fmt_gate_up, fmt_down, fmt_shared, has_shared;
   const void *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down;
   const uint8_t* grid;
+  const uint8_t* vq_cb;    // E4M3 codewords [n][8] (VQ routed formats)
   const float* w_router;   // used when fused_topk
   const void* x;
   int x_dtype;
@@ -85,6 +86,7 @@ struct PrefillLaunch {
   int fmt_gate_up, fmt_down, fmt_shared, has_shared;
   const void *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down;
   const uint8_t* grid;
+  const uint8_t* vq_cb;  // E4M3 codewords [n][8] (VQ routed formats)
   const void* x;
   int x_dtype;
   const int32_t *counts, *offsets, *tile_start, *perm, *pos;
@@ -111,7 +113,7 @@ inline bool prefill_fits(int T, int k, int d, int f) {
   return (int64_t)T * d * 2 < (int64_t(1) << 31) && (int64_t)T * k * f * 2 < (int64_t(1) << 31);
 }
 
-// repack.hip
-hipError_t launch_repack(int fmt, int64_t n_blocks, const void* src, void* dst, int to_device, hipStream_t s);
+// repack.hip: n_rows rows of K inputs
+hipError_t launch_repack(int fmt, int64_t n_rows, int K, const void* src, void* dst, int to_device, hipStream_t s);
 
 }  // namespace qmoe

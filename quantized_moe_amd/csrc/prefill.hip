@@ -43,6 +43,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_iq2.hpp"
+#include "vq.hpp"
 
 namespace qmoe {
 
@@ -126,6 +127,7 @@ __global__ __launch_bounds__(256) void x16_kernel(const void* __restrict__ x, in
 struct GemmArgs {
   QMat B0, B1;                 // B0 = gate (or down), B1 = up (gate/up only)
   const uint8_t* grid;         // IQ2 grid [256][8]
+  const uint8_t* vq_cb;        // VQ codebook: E4M3 codewords [n][8]
   const uint16_t* a16;         // fp16 A rows: x16 [T][K] (gate/up) or H [rows][K] (down)
   int a16_bytes;               // size of a16 (below 2^31)
   const float* rowxs;          // gate/up: scale of x16 for each row of the row space
@@ -277,6 +279,36 @@ struct BRegs<FMT_MX4, KS> {
       e = m.p_scale[blk0 + lb];
     else
       e = *reinterpret_cast<const uint16_t*>(m.p_scale + blk0 + lb);
+  }
+};
+
+// VQ rows: the 8 indices of inputs 64*g4 .. +63 of the superblock (12 stream
+// bytes, one 12-byte load) and, for 13 bits, their plane byte.  Only whole
+// superblocks per wave (KS = 1): half a lane's slice would start mid-dword.
+template <int KS>
+struct BRegs<FMT_VQ12, KS> {
+  static_assert(KS == 1, "VQ rows are read in whole superblocks");
+  VqPiece p;
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int) {
+    const int rs = 3 * m.K / 16;  // stream bytes per row
+    const uint3 v = *reinterpret_cast<const uint3*>(m.p_a + row0 * rs + sb * 48 + (uint32_t)(lrow * rs + 12 * g4));
+    p.w0 = v.x;
+    p.w1 = v.y;
+    p.w2 = v.z;
+    p.pl = 0u;
+  }
+};
+template <int KS>
+struct BRegs<FMT_VQ13, KS> {
+  static_assert(KS == 1, "VQ rows are read in whole superblocks");
+  VqPiece p;
+  __device__ __forceinline__ void load(const QMat& m, int64_t row0, int lrow, int sb, int g4, int) {
+    const int rs = 3 * m.K / 16, bs = m.K / 64;  // stream and plane bytes per row
+    const uint3 v = *reinterpret_cast<const uint3*>(m.p_a + row0 * rs + sb * 48 + (uint32_t)(lrow * rs + 12 * g4));
+    p.w0 = v.x;
+    p.w1 = v.y;
+    p.w2 = v.z;
+    p.pl = m.p_b[row0 * bs + sb * 4 + (uint32_t)(lrow * bs + g4)];
   }
 };
 
@@ -486,12 +518,13 @@ struct GemmLds {
   static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
   static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
   static constexpr int kTqs = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
+  static constexpr int kCb = is_vq(FMT) ? vq_codes(FMT) * 8 : 0;      // VQ codebook (E4M3)
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
   static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
   static constexpr int kTok = 3 * BM * 8;                             // token (gate/up) and scale of each row, 3 items
   static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
   static constexpr int kMax = GATEUP ? 2 * BM * 4 : 0;                // gate/up: [item parity][BM] row maxima of |h|
-  static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oA = oTqs + kTqs, oS = oA + kA, oTok = oS + kS,
+  static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oCb = oTqs + kTqs, oA = oCb + kCb, oS = oA + kA, oTok = oS + kS,
                        oRed = oTok + kTok, oMax = oRed + kRed, oTiles = oMax + kMax;
   // then tile_start, counts, offsets of the routed experts: [3][E + 1]
   static constexpr int bytes_for(int E) { return oTiles + 3 * (E + 1) * 4; }
@@ -532,6 +565,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   if constexpr (FMT == FMT_IQ2)
     build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid, GEMM_THREADS);
   if constexpr (FMT == FMT_Q2K) build_q2k_table(reinterpret_cast<uint2*>(lds + L::oTqs));
+  if constexpr (is_vq(FMT)) vq_stage_codebook(a.vq_cb, lds + L::oCb, vq_codes(FMT), tid, GEMM_THREADS);
   if constexpr (GATEUP) {
     if (tid < 2 * BM) sMax[tid] = 0u;
   }
@@ -723,6 +757,18 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int m = 0; m < NSUB; m++) acc0[m] = acc1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // VQ: the fp16 row gains of this lane's output column (gate and up, or
+  // down) for the current item, requested as the item becomes current (a
+  // whole item before its epilogue reads them)
+  float vg0 = 1.0f, vg1 = 1.0f;
+  auto load_gains = [&](const Item& it) {
+    if constexpr (is_vq(FMT)) {
+      const int64_t row = (int64_t)it.e * a.N + it.nt * BN + lrow;  // (an item past the end: e = nt = 0)
+      vg0 = half_bits_to_float(reinterpret_cast<const uint16_t*>(a.B0.p_scale)[row]);
+      if constexpr (GATEUP) vg1 = half_bits_to_float(reinterpret_cast<const uint16_t*>(a.B1.p_scale)[row]);
+    }
+  };
+
   // One superblock half-step with NM (a compile-time 1 or 2) active
   // sub-tiles: straight-line code, so the scheduler can overlap the table
   // reads, the fragment arithmetic and the MFMAs of consecutive k32 steps.
@@ -734,7 +780,26 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     auto aread = [&](int m, int i) {
       return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
     };
-    if constexpr (FMT == FMT_MX4) {
+    if constexpr (is_vq(FMT)) {
+      // B fragment of step q = the codeword of the lane's index q, converted
+      // to fp16 exactly; no per-superblock scale (the row gain is applied in
+      // the item epilogue)
+      const uint8_t* cb = lds + L::oCb;
+      constexpr bool B13 = FMT == FMT_VQ13;
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const uint4 f0 = vq_to_f16(vq_codeword(cb, vq_index<B13>(B0.p, q)));
+        uint4 f1;
+        if constexpr (GATEUP) f1 = vq_to_f16(vq_codeword(cb, vq_index<B13>(B1.p, q)));
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          const uint4 av = aread(m, q);
+          acc0[m] = mfma32(av, f0, acc0[m]);
+          if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
+        }
+        if (q % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bound the live fragments
+      }
+    } else if constexpr (FMT == FMT_MX4) {
       float f00, f01, f10 = 0.f, f11 = 0.f;
       const float ps0 = mx4_prescale<KS>(B0.e, f00, f01);
       float ps1 = 0.0f;
@@ -945,7 +1010,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
               const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
               const float v1 = KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r];
               const float xs = sXs[(j % 3) * BM + i];
-              hv = silu(v0 * xs) * (v1 * xs);
+              hv = is_vq(FMT) ? silu(v0 * xs * vg0) * (v1 * xs * vg1) : silu(v0 * xs) * (v1 * xs);
             }
             hbuf[i * HROW + cl] = hv;
             const float mx = row16_max(fabsf(hv));
@@ -993,7 +1058,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
             const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
             const int i = m * 16 + 4 * g4 + r;
             const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
-            if (i < it.rows) static_cast<float*>(a.out)[(int64_t)it.p0 * a.N + (i * a.N + n)] = v0 * sXs[(j % 3) * BM + i];
+            const float v = is_vq(FMT) ? v0 * sXs[(j % 3) * BM + i] * vg0 : v0 * sXs[(j % 3) * BM + i];
+            if (i < it.rows) static_cast<float*>(a.out)[(int64_t)it.p0 * a.N + (i * a.N + n)] = v;
           }
         }
       }
@@ -1007,6 +1073,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   // before the weight loads issued in the step before it is needed: waiting
   // for it never waits for weights that are not yet due.
   Item cur = item(0), nxt = item(1);
+  load_gains(cur);
   tok_issue(cur);
   tok_commit(0);
   tok_issue(nxt);
@@ -1057,6 +1124,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         __syncthreads();
         epilogue(j, cur, s & 1);
         cur = nxt;
+        load_gains(cur);
         nxt = item(j + 2);
         tok_commit(j + 2);  // slot (j + 2) % 3 was last read for item j - 1
         tok_issue(item(j + 3));
@@ -1177,7 +1245,10 @@ static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
 template <int FMT, bool GATEUP>
 static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int nsb = a.K / 256;
-  if constexpr (FMT == FMT_MX4) {  // whole superblocks per wave: 32 bytes of codes per lane and matrix
+  if constexpr (is_vq(FMT)) {  // whole superblocks per wave: 12 (13) bytes of indices per lane and matrix
+    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+    return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+  } else if constexpr (FMT == FMT_MX4) {  // whole superblocks per wave: 32 bytes of codes per lane and matrix
     if constexpr (GATEUP) {
       return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
     } else {
@@ -1226,6 +1297,8 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
     case FMT_Q2K: { constexpr int F = FMT_Q2K; __VA_ARGS__; } break;   \
     case FMT_Q4K: { constexpr int F = FMT_Q4K; __VA_ARGS__; } break;   \
     case FMT_MX4: { constexpr int F = FMT_MX4; __VA_ARGS__; } break;   \
+    case FMT_VQ12: { constexpr int F = FMT_VQ12; __VA_ARGS__; } break; \
+    case FMT_VQ13: { constexpr int F = FMT_VQ13; __VA_ARGS__; } break; \
     default: { constexpr int F = FMT_Q8; __VA_ARGS__; } break;         \
   }
 
@@ -1244,6 +1317,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.B0 = make_qmat(P.w_gate, P.fmt_gate_up, P.E, P.f, P.d);
     a.B1 = make_qmat(P.w_up, P.fmt_gate_up, P.E, P.f, P.d);
     a.grid = P.grid;
+    a.vq_cb = P.vq_cb;
     a.a16 = P.x16;
     a.a16_bytes = P.T * P.d * 2;
     a.rowxs = P.route_xs;
@@ -1267,6 +1341,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.B0 = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
     a.B1 = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
     a.grid = P.grid;
+    a.vq_cb = P.vq_cb;
     a.a16 = P.x16;
     a.a16_bytes = P.T * P.d * 2;
     a.rowxs = P.xs;
@@ -1296,6 +1371,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     GemmArgs a{};
     a.B0 = make_qmat(P.w_down, P.fmt_down, P.E, P.d, P.f);
     a.grid = P.grid;
+    a.vq_cb = P.vq_cb;
     a.a16 = static_cast<const uint16_t*>(P.H);
     a.a16_bytes = n * P.f * 2;
     a.K = P.f;
@@ -1317,6 +1393,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     GemmArgs b{};
     b.B0 = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
     b.grid = P.grid;
+    b.vq_cb = P.vq_cb;
     b.a16 = static_cast<const uint16_t*>(P.Hs);
     b.a16_bytes = P.T * P.f * 2;
     b.K = P.f;

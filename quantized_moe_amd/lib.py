@@ -16,10 +16,11 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 
-MOE_ABI_VERSION = 2
+MOE_ABI_VERSION = 3
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FMT_NONE, MOE_FMT_IQ2XXS_L, MOE_FMT_Q2K_L, MOE_FMT_Q8_0_L, MOE_FMT_Q4K_L = 0, 1, 2, 3, 4
+MOE_FMT_MXFP4_L, MOE_FMT_VQ12_L, MOE_FMT_VQ13_L = 5, 6, 7
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_DEVICE = 0, 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_LAYER = 0, 1, 2, 3
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
@@ -61,6 +62,8 @@ class MoeLayer(ctypes.Structure):
         ("s_down", ctypes.c_void_p),
         ("router_bias", ctypes.c_void_p),
         ("down_gain", ctypes.c_void_p),
+        ("vq_codebook", ctypes.c_void_p),
+        ("vq_codes", ctypes.c_int32),
     ]
 
 
@@ -238,7 +241,7 @@ class DeviceLayer:
 
     def __init__(self, E, d, f, k, fmt_gate_up, fmt_down, w_gate, w_up, w_down, grid, w_router,
                  fmt_shared=MOE_FMT_NONE, s_gate=None, s_up=None, s_down=None, device="cuda",
-                 router_bias=None, down_gain=None):
+                 router_bias=None, down_gain=None, vq_codebook=None):
         self.E, self.d, self.f, self.k = E, d, f, k
         self.device = torch.device(device)
         has_shared = s_gate is not None
@@ -260,6 +263,11 @@ class DeviceLayer:
             self.tensors["router_bias"] = torch.from_numpy(np.ascontiguousarray(router_bias, np.float32)).to(self.device)
         if down_gain is not None:
             self.tensors["down_gain"] = torch.from_numpy(np.ascontiguousarray(down_gain, np.float32)).to(self.device)
+        n_codes = 0
+        if vq_codebook is not None:
+            cb = np.ascontiguousarray(vq_codebook, np.uint8).reshape(-1, 8)
+            n_codes = cb.shape[0]
+            self.tensors["vq_codebook"] = _to_device_bytes(cb, self.device)
         t = self.tensors
         src = MoeLayer(
             abi_version=MOE_ABI_VERSION, n_experts=E, d_model=d, d_ff=f, top_k=k, fmt_gate_up=fmt_gate_up,
@@ -268,7 +276,8 @@ class DeviceLayer:
             w_router=_ptr(t["w_router"]), has_shared=1 if has_shared else 0,
             fmt_shared=fmt_shared if has_shared else 0, s_gate=_ptr(canon.get("s_gate")),
             s_up=_ptr(canon.get("s_up")), s_down=_ptr(canon.get("s_down")),
-            router_bias=_ptr(t.get("router_bias")), down_gain=_ptr(t.get("down_gain")))
+            router_bias=_ptr(t.get("router_bias")), down_gain=_ptr(t.get("down_gain")),
+            vq_codebook=_ptr(t.get("vq_codebook")), vq_codes=n_codes)
         self.desc = MoeLayer(w_gate=_ptr(t["w_gate"]), w_up=_ptr(t["w_up"]), w_down=_ptr(t["w_down"]),
                              s_gate=_ptr(t.get("s_gate")), s_up=_ptr(t.get("s_up")), s_down=_ptr(t.get("s_down")))
         prepare_weights(src, self.desc)
@@ -281,7 +290,7 @@ class DeviceLayer:
         return cls(s.E, s.d, s.f, s.k, s.fmt_gate_up, s.fmt_down, L.w_gate, L.w_up, L.w_down, L.grid, L.w_router,
                    fmt_shared=s.fmt_shared if s.has_shared else MOE_FMT_NONE, s_gate=L.s_gate, s_up=L.s_up,
                    s_down=L.s_down, device=device, router_bias=getattr(L, "router_bias", None),
-                   down_gain=getattr(L, "down_gain", None))
+                   down_gain=getattr(L, "down_gain", None), vq_codebook=getattr(L, "vq_codebook", None))
 
     def workspace(self, T: int, op: int = MOE_OP_LAYER) -> torch.Tensor:
         n = workspace_bytes(self.desc, T, op)

@@ -40,7 +40,8 @@ def test_abi_and_status_strings():
 
 
 @pytest.mark.parametrize("fmt,E,rows,K", [(1, 384, 2048, 4096), (2, 384, 4096, 2048), (3, 1, 2048, 4096),
-                                          (2, 8, 512, 256), (4, 384, 2048, 4096), (5, 384, 4096, 2048)])
+                                          (2, 8, 512, 256), (4, 384, 2048, 4096), (5, 384, 4096, 2048),
+                                          (6, 384, 2048, 4096), (7, 384, 4096, 2048), (6, 3, 5, 64), (7, 2, 3, 128)])
 def test_matrix_bytes_matches_format_sizes(fmt, E, rows, K):
     assert lib.matrix_bytes(fmt, E, rows, K) == synth.matrix_bytes(fmt, E, rows, K)
 
@@ -52,6 +53,10 @@ def test_matrix_bytes_of_the_decode_layer():
     assert lib.matrix_bytes(3, 1, 2048, 4096) == 8912896
     assert lib.matrix_bytes(4, 1, 2048, 4096) == 4718592   # Q4K: 144 B per 256 weights
     assert lib.matrix_bytes(5, 1, 2048, 4096) == 4456448   # MXFP4: 17 B per 32 weights
+    assert lib.matrix_bytes(6, 1, 2048, 4096) == 1576960   # VQ12: 2 + 768 B per row of 4096
+    assert lib.matrix_bytes(7, 1, 2048, 4096) == 1708032   # VQ13: 2 + 768 + 64 B per row of 4096
+    with pytest.raises(lib.MoeError):
+        lib.matrix_bytes(6, 1, 16, 32)                     # VQ rows: K a multiple of 64
 
 
 def _layer(**over):
@@ -74,6 +79,7 @@ def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
 
 @pytest.mark.parametrize("over,code", [
     (dict(abi_version=1), lib.MOE_ERR_UNSUPPORTED),      # the layout before router_bias / down_gain
+    (dict(abi_version=2), lib.MOE_ERR_UNSUPPORTED),      # the layout before vq_codebook / vq_codes
     (dict(abi_version=99), lib.MOE_ERR_UNSUPPORTED),
     (dict(layout=lib.MOE_LAYOUT_CANONICAL), lib.MOE_ERR_UNSUPPORTED),
     (dict(layout=7), lib.MOE_ERR_UNSUPPORTED),
@@ -81,7 +87,14 @@ def _forward(layer, T=1, x=4096, y=4864, ws=5120, ws_bytes=0, path=0, dtype=0):
     (dict(fmt_down=0), lib.MOE_ERR_UNSUPPORTED),
     (dict(fmt_shared=4), lib.MOE_ERR_UNSUPPORTED),        # Q4K_L: routed experts only
     (dict(fmt_shared=5), lib.MOE_ERR_UNSUPPORTED),        # MXFP4_L: routed experts only
-    (dict(fmt_shared=6), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_shared=6), lib.MOE_ERR_UNSUPPORTED),        # VQ: routed experts only
+    (dict(fmt_shared=7), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_gate_up=8), lib.MOE_ERR_UNSUPPORTED),
+    (dict(fmt_gate_up=6, vq_codebook=0x8000, vq_codes=4096), lib.MOE_ERR_UNSUPPORTED),  # VQ gate/up, Q2K down
+    (dict(fmt_gate_up=6, fmt_down=6, vq_codes=4096), lib.MOE_ERR_INVALID_ARG),           # no codebook
+    (dict(fmt_gate_up=6, fmt_down=6, vq_codebook=0x8008, vq_codes=4096), lib.MOE_ERR_INVALID_ARG),  # misaligned
+    (dict(fmt_gate_up=6, fmt_down=6, vq_codebook=0x8000, vq_codes=1000), lib.MOE_ERR_INVALID_ARG),
+    (dict(fmt_gate_up=7, fmt_down=6, vq_codebook=0x8000, vq_codes=4096), lib.MOE_ERR_INVALID_ARG),  # 13 bits: 8192
     (dict(n_experts=0), lib.MOE_ERR_INVALID_ARG),
     (dict(n_experts=1025), lib.MOE_ERR_INVALID_ARG),
     (dict(d_model=4000), lib.MOE_ERR_INVALID_ARG),
@@ -107,6 +120,14 @@ def test_grid_not_needed_without_iq2_and_shared_optional():
     layer = _layer(fmt_gate_up=2, iq2_grid=0, has_shared=0, s_gate=0, s_up=0, s_down=0)
     # gets past layer validation; fails on the (deliberately) empty workspace
     assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE
+
+
+def test_vq_layers_pass_validation():
+    for gu, dn, n in [(6, 6, 4096), (6, 6, 8192), (7, 6, 8192), (6, 7, 8192), (7, 7, 8192)]:
+        layer = _layer(fmt_gate_up=gu, fmt_down=dn, vq_codebook=0x8000, vq_codes=n, iq2_grid=0)
+        assert _ffn_decode(layer) == lib.MOE_ERR_WORKSPACE, (gu, dn, n)  # past validation
+    # the codebook is not read by block formats
+    assert _ffn_decode(_layer(vq_codebook=0x8008, vq_codes=5)) == lib.MOE_ERR_WORKSPACE
 
 
 def test_bias_and_gains_are_optional():

@@ -121,6 +121,17 @@ FORMAT_CASES = [
     (8, 2, 256, 8192, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 2, synth.F32),   # four pieces per lane (f)
     (8, 1, 8192, 256, synth.FMT_MX4, synth.FMT_MX4, None, 2, synth.F32),           # four pieces per lane (d)
     (9, 2, 256, 256, synth.FMT_MX4, synth.FMT_MX4, synth.FMT_Q8, 40, synth.F32),   # rows of 8 pieces: 8 rows per wave step
+    # VQ routed experts (12- and 13-bit codeword indices, per-layer E4M3 codebook)
+    (16, 4, 256, 512, synth.FMT_VQ12, synth.FMT_VQ12, synth.FMT_Q8, 1, synth.F32),  # rows of 4 pieces
+    (16, 4, 256, 512, synth.FMT_VQ12, synth.FMT_VQ12, synth.FMT_Q8, 3, synth.F32),
+    (16, 4, 256, 512, synth.FMT_VQ13, synth.FMT_VQ13, synth.FMT_Q8, 37, synth.BF16),
+    (12, 3, 512, 1024, synth.FMT_VQ13, synth.FMT_VQ12, synth.FMT_Q2K, 1, synth.F32),
+    (12, 3, 1024, 512, synth.FMT_VQ12, synth.FMT_VQ13, synth.FMT_IQ2, 6, synth.BF16),
+    (10, 3, 2048, 1024, synth.FMT_VQ13, synth.FMT_VQ13, synth.FMT_Q8, 70, synth.BF16),
+    (8, 2, 256, 8192, synth.FMT_VQ12, synth.FMT_VQ12, synth.FMT_Q8, 2, synth.F32),  # two pieces per lane (f)
+    (8, 1, 8192, 256, synth.FMT_VQ13, synth.FMT_VQ13, None, 2, synth.F32),          # two pieces per lane (d)
+    (9, 2, 256, 256, synth.FMT_VQ12, synth.FMT_VQ12, synth.FMT_Q8, 40, synth.F32),
+    (1000, 5, 256, 256, synth.FMT_VQ13, synth.FMT_VQ13, synth.FMT_Q8, 7, synth.F32),  # many experts
 ]
 
 
@@ -189,11 +200,13 @@ def test_route_topk_with_bias():
 
 
 @pytest.mark.parametrize("T,dt,fmt", [(1, synth.F32, synth.FMT_IQ2), (3, synth.F32, synth.FMT_IQ2),
+                                      (2, synth.F32, synth.FMT_VQ12), (45, synth.BF16, synth.FMT_VQ13),
                                       (37, synth.BF16, synth.FMT_IQ2), (1, synth.F32, synth.FMT_Q4K),
                                       (8, synth.F32, synth.FMT_Q4K), (45, synth.BF16, synth.FMT_Q4K),
                                       (2, synth.F32, synth.FMT_MX4), (45, synth.BF16, synth.FMT_MX4)])
 def test_layer_with_bias_and_gains(T, dt, fmt):
-    fdn = {synth.FMT_IQ2: synth.FMT_Q2K, synth.FMT_Q4K: synth.FMT_Q4K, synth.FMT_MX4: synth.FMT_MX4}[fmt]
+    fdn = {synth.FMT_IQ2: synth.FMT_Q2K, synth.FMT_Q4K: synth.FMT_Q4K, synth.FMT_MX4: synth.FMT_MX4,
+           synth.FMT_VQ12: synth.FMT_VQ12, synth.FMT_VQ13: synth.FMT_VQ12}[fmt]
     spec = synth.scaled_spec(E=24, k=4, d=512, f=512, fmt_gate_up=fmt, fmt_down=fdn)
     L = _bias_gain_layer(spec, 32)
     dl = lib.DeviceLayer.from_synth(L, DEV)
@@ -367,6 +380,69 @@ def test_mxfp4_layer_full_size_decode_and_prefill():
         torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", [synth.FMT_VQ12, synth.FMT_VQ13])
+def test_vq_layer_full_size_decode_and_prefill(fmt):
+    """The decode workload's shape with VQ routed gate/up/down (the
+    8-dimensional vector quantization with a per-layer codebook): one-token
+    decode on three tokens, and a 1024-token bf16 chunk with routes
+    bit-exact and 64 tokens compared one by one."""
+    spec = synth.scaled_spec(E=384, k=6, d=4096, f=2048, fmt_gate_up=fmt, fmt_down=fmt)
+    L = synth.random_layer(spec, seed=8, workload="vq")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    try:
+        for i in range(3):
+            x = synth.activations(8, ("vq", "x", i), 1, 4096, synth.F32)
+            y, idx, wt = run_layer(dl, x, synth.F32, lib.MOE_PATH_AUTO)
+            y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, synth.F32)
+            assert np.array_equal(idx, idx_ref)
+            assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
+        T = 1024
+        x = synth.activations(8, ("vq", "prefill"), T, 4096, synth.BF16)
+        y, idx, wt = run_layer(dl, x, synth.BF16, lib.MOE_PATH_AUTO)
+        _, idx_ref, wt_ref = oracle.route(x, oracle.BF16, L.w_router, 6)
+        assert np.array_equal(idx, idx_ref)
+        tok = np.unique(np.concatenate([np.arange(0, T, 16), [1, T - 1]]))
+        y_ref = oracle.ffn(L, x, oracle.BF16, idx_ref, wt_ref, tokens=tok, grouped=True)
+        err = per_token_rel_l2(y[tok], y_ref)
+        assert err.max() <= REL_L2, err.max()
+    finally:
+        del dl
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_VQ12, synth.FMT_VQ13])
+def test_vq_every_code_and_gains_far_from_unit(fmt):
+    """A codebook holding every finite E4M3 code (zeros, subnormals, up to
+    448) with indices drawn so that those codewords are common, and row gains
+    spread over 2^-12 .. 2^4 with both signs: every token within the bar on
+    both paths."""
+    spec = synth.scaled_spec(E=12, k=3, d=1024, f=512, fmt_gate_up=fmt, fmt_down=fmt)
+    L = synth.random_layer(spec, seed=46, workload="vqcodes")
+    rng = np.random.default_rng(46 + fmt)
+    cb = synth.make_codebook(46, synth.VQ_CODES[fmt], every_code=True)
+    bits = 12 if fmt == synth.FMT_VQ12 else 13
+
+    def mat(rows, K):
+        idx = rng.integers(0, 1 << bits, size=(rows, K // 8))
+        special = rng.random(idx.shape) < 0.25  # a quarter of the indices name the every-code codewords 0..31
+        idx[special] = rng.integers(0, 32, size=int(special.sum()))
+        gain = (rng.choice([-1.0, 1.0], rows) * np.exp2(rng.uniform(-12, 4, rows)) * 1e-3).astype(np.float16)
+        return synth.pack_vq(gain, idx, bits).reshape(-1)
+    E, d, f = spec.E, spec.d, spec.f
+    L = synth.Layer(**{**L.__dict__, "vq_codebook": cb,
+                       "w_gate": np.concatenate([mat(f, d) for _ in range(E)]),
+                       "w_up": np.concatenate([mat(f, d) for _ in range(E)]),
+                       "w_down": np.concatenate([mat(d, f) for _ in range(E)])})
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    for T, dt, path in ((40, synth.BF16, lib.MOE_PATH_PREFILL), (3, synth.F32, lib.MOE_PATH_DECODE)):
+        x = synth.activations(46, ("vqcodes", T), T, spec.d, dt)
+        y, idx, wt = run_layer(dl, x, dt, path)
+        y_ref, idx_ref, _ = oracle.layer_forward(L, x, dt)
+        assert np.array_equal(idx, idx_ref)
+        err = per_token_rel_l2(y, y_ref)
+        assert err.max() <= REL_L2, (path, err.max())
+
+
 @pytest.mark.parametrize("shift", [-20, 20])
 def test_mxfp4_block_scales_far_from_unit(shift):
     """MXFP4 experts whose E8M0 exponents sit 20 binades below or above the
@@ -455,6 +531,31 @@ def test_repack_round_trip(decode_layer):
         assert np.array_equal(back.cpu().numpy(), canon), name
 
 
+@pytest.mark.parametrize("fmt", [synth.FMT_VQ12, synth.FMT_VQ13, synth.FMT_MX4])
+def test_repack_vq_rows_and_mx4(fmt):
+    """Canonical -> device -> canonical is the identity for VQ rows (gain,
+    index stream and bit plane planes) and MXFP4 blocks at every width, and
+    the device layout puts the planes where the kernels read them."""
+    rng = np.random.default_rng(fmt)
+    for K in (64, 256, 2048, 8192):
+        E, rows = 3, 5
+        n = synth.matrix_bytes(fmt, E, rows, K)
+        canon = rng.integers(0, 256, n, dtype=np.uint8)
+        src = torch.from_numpy(canon).to(DEV)
+        dev_buf = torch.empty_like(src)
+        back = torch.empty_like(src)
+        lib.repack(fmt, E, rows, K, src, dev_buf, lib.MOE_REPACK_TO_DEVICE)
+        lib.repack(fmt, E, rows, K, dev_buf, back, lib.MOE_REPACK_TO_CANONICAL)
+        torch.cuda.synchronize()
+        assert np.array_equal(back.cpu().numpy(), canon), (fmt, K)
+        if fmt != synth.FMT_MX4:
+            R, rb = E * rows, synth.row_bytes(fmt, K)
+            c = canon.reshape(R, rb)
+            dv = dev_buf.cpu().numpy()
+            planes = [c[:, :2], c[:, 2:2 + 3 * K // 16]] + ([c[:, 2 + 3 * K // 16:]] if fmt == synth.FMT_VQ13 else [])
+            assert np.array_equal(dv, np.concatenate([p.reshape(-1) for p in planes])), (fmt, K)
+
+
 @pytest.mark.parametrize("fmt", [synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_Q4K])
 def test_repack_round_trip_all_widths(fmt):
     """Canonical -> device -> canonical is the identity for every row width,
@@ -531,6 +632,7 @@ SCALE_SPECS = [
     synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_Q8, fmt_down=synth.FMT_IQ2,
                       fmt_shared=synth.FMT_Q2K),
     synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_MX4, fmt_down=synth.FMT_MX4),
+    synth.scaled_spec(E=24, k=4, d=1024, f=1024, fmt_gate_up=synth.FMT_VQ13, fmt_down=synth.FMT_VQ12),
 ]
 
 
