@@ -89,6 +89,60 @@ KERNEL_SYMBOLS = {
     "prefill_gateup": "gemm_kernel<1, true",
     "prefill_down": "gemm_kernel<2, false",
 }
+# the shared expert's GEMMs (Q8), for the instruction-counter tables only
+PMC_EXTRA_SYMBOLS = {"prefill_shared_gateup": "gemm_kernel<3, true", "prefill_shared_down": "gemm_kernel<3, false"}
+
+
+def pmc_table(dirs) -> int:
+    """Per-launch means of every SQ/GRBM counter in rocprofv3 --pmc runs of
+    bench.py --pmc-mode, per library kernel, and the ratios derived from
+    them.  Kernel cycles C = GRBM_GUI_ACTIVE / 8 (the counter is summed over
+    the 8 XCDs); 256 CUs, 1024 SIMDs."""
+    import csv
+    import glob
+
+    vals = {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    vals.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    syms = {**KERNEL_SYMBOLS, **PMC_EXTRA_SYMBOLS}
+    rows = {}
+    for (kname, counter), vs in vals.items():
+        for lib_name, sym in syms.items():
+            if sym in kname:
+                rows.setdefault(lib_name, {}).setdefault(counter, []).extend(vs)
+    def m(r, c):
+        v = r.get(c)
+        return float(np.mean(v)) if v else None
+    for lib_name in syms:
+        r = rows.get(lib_name)
+        if not r:
+            continue
+        print(f"{lib_name}:")
+        for c in sorted(r):
+            print(f"  {c:32s} {m(r, c):16.0f}")
+        C = m(r, "GRBM_GUI_ACTIVE")
+        C = C / 8.0 if C else None
+        def ratio(num, den, scale=1.0):
+            a, b = m(r, num), (m(r, den) if isinstance(den, str) else den)
+            return None if a is None or not b else a * scale / b
+        derived = {
+            "kernel cycles C (GRBM_GUI_ACTIVE / 8)": C,
+            "VALU instructions per wave": ratio("SQ_INSTS_VALU", "SQ_WAVES"),
+            "LDS instructions per wave": ratio("SQ_INSTS_LDS", "SQ_WAVES"),
+            "VALU busy per SIMD (4 ACTIVE_INST_VALU / 1024 C)": ratio("SQ_ACTIVE_INST_VALU", 1024 * C, 4) if C else None,
+            "MFMA busy per SIMD (MFMA_BUSY_CYCLES / 1024 C)": ratio("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * C) if C else None,
+            "LDS busy per CU (LDS_IDX_ACTIVE / 256 C)": ratio("SQ_LDS_IDX_ACTIVE", 256 * C) if C else None,
+            "LDS bank-conflict share (BANK_CONFLICT / IDX_ACTIVE)": ratio("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+            "wave time waiting on anything (WAIT_ANY / WAVE_CYCLES)": ratio("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+            "wave time waiting to issue (WAIT_INST_ANY / WAVE_CYCLES)": ratio("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+        }
+        for k, v in derived.items():
+            if v is not None:
+                print(f"  = {k:58s} {v:12.3f}" if v < 100 else f"  = {k:58s} {v:12.0f}")
+    return 0
 
 
 def pmc_summarize(fetch_dir: str, write_dir: str) -> int:
@@ -243,10 +297,14 @@ def main() -> int:
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn the two counter runs into profiles/traffic_counters.json (no GPU)")
+    ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                    help="print per-kernel instruction/LDS/MFMA counters of --pmc-mode runs (no GPU)")
     args = ap.parse_args()
 
     if args.pmc_summarize:
         return pmc_summarize(*args.pmc_summarize)
+    if args.pmc_table:
+        return pmc_table(args.pmc_table)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel sharding is "
@@ -410,6 +468,8 @@ def main() -> int:
         prof = profile(step, args.profile_steps)
         kern = {}
         for name, nbytes in decode_kernels.items():
+            if name not in prof:  # (a library build without that launch)
+                continue
             avg_us = prof[name]["avg_us"]
             kern[name] = {"avg_us": avg_us, "launches": prof[name]["launches"], "algorithmic_bytes": nbytes,
                           "achieved_GBs": round(nbytes / (avg_us * 1e-6) / 1e9, 1)}

@@ -1,5 +1,4 @@
-// fp16 MFMA helpers and the IQ2 codebook tables shared by the prefill grouped
-// GEMMs and the decode gate/up GEMV.
+// fp16 MFMA helpers and the IQ2 codebook tables of the prefill grouped GEMMs.
 //
 // "YoungAi -- DeepSeek V4.1 Flash on one DGX Spark", section 4.4 feeds 16-bit
 // matrix units with codewords that convert without rounding.  Here every IQ2
@@ -33,33 +32,33 @@ __device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c) {
 __device__ __forceinline__ uint32_t to_h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 __device__ __forceinline__ float from_h(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
 
-// IQ2 tables in LDS.  tm[row][s] = the 8 grid magnitudes of row times (2s+1)
-// as fp16, 16 bytes, row stride 256 bytes: the byte address row << 8 | s << 4
-// is one v_perm of the payload word and s << 4.  sgn[b7][c] = XOR masks of the
-// 7 stored signs plus the parity sign, stored TAB_COPIES times (copy c at bank
-// quad c); lane l reads copy l % 16, so the 16 lanes of a row never meet in a
-// bank whatever patterns they look up.
-constexpr int IQ2_TM_BYTES = 256 * 16 * 16;
+// IQ2 tables in LDS.  tm[row][c] = the 8 grid magnitudes of row as fp16, 16
+// bytes, stored TAB_COPIES times (copy c at bank quad c, row stride 256
+// bytes): the byte address row << 8 | c << 4 is one v_perm of the payload
+// word and c << 4.  sgn[b7][c] = XOR masks of the 7 stored signs plus the
+// parity sign, stored the same way.  Lane l reads copy l % 16 of both, so
+// the 16 lanes of a row never meet in a bank whatever rows and patterns
+// they look up (a table indexed by the sub-block scale as well put every
+// lane with the same scale on the same banks).  The scale (2s+1) is one
+// packed fp16 multiply per word: (2s+1) * g <= 217 is exact.
+constexpr int IQ2_TM_BYTES = 256 * TAB_COPIES * 16;
 constexpr int IQ2_SGN_BYTES = 128 * TAB_COPIES * 16;
 
 // Both tables, built by threads t0 .. t0 + nt - 1 of the block: a thread
-// that owns a grid row reads it once and writes its 16 scaled entries; the
-// sign table needs no loads and is spread over all of them.
+// that owns a grid row reads it once and writes its 16 copies; the sign
+// table needs no loads and is spread over all of them.
 __device__ inline void build_iq2_tables(const uint8_t* grid, uint4* tm, uint4* sgn, int t0, int nt) {
   for (int row = t0; row < 256; row += nt) {
     const uint2 g = *reinterpret_cast<const uint2*>(grid + 8 * row);
-#pragma unroll 4
-    for (int sidx = 0; sidx < 16; sidx++) {
-      const int sc = 2 * sidx + 1;
-      uint32_t w[4];
+    uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const uint32_t word = i < 2 ? g.x : g.y;
-        const uint32_t v0 = (word >> (16 * (i & 1))) & 255u, v1 = (word >> (16 * (i & 1) + 8)) & 255u;
-        w[i] = to_h((float)(sc * v0)) | (to_h((float)(sc * v1)) << 16);
-      }
-      tm[row * 16 + sidx] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < 4; i++) {
+      const uint32_t word = i < 2 ? g.x : g.y;
+      const uint32_t v0 = (word >> (16 * (i & 1))) & 255u, v1 = (word >> (16 * (i & 1) + 8)) & 255u;
+      w[i] = to_h((float)v0) | (to_h((float)v1) << 16);
     }
+#pragma unroll 4
+    for (int c = 0; c < TAB_COPIES; c++) tm[row * TAB_COPIES + c] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   for (int e = t0; e < 128 * TAB_COPIES; e += nt) {
     const uint32_t b = e / TAB_COPIES;
@@ -71,21 +70,29 @@ __device__ inline void build_iq2_tables(const uint8_t* grid, uint4* tm, uint4* s
   }
 }
 
-// IQ2 sub-block scale s (the top nibble of its B word) as s << 4
-__device__ __forceinline__ uint32_t iq2_scale16(uint32_t bword) { return (bword >> 24) & 0xf0u; }
+// IQ2 sub-block scale (2s+1) (s the top nibble of its B word) as a packed
+// pair of fp16
+__device__ __forceinline__ uint32_t iq2_scale_h2(uint32_t bword) {
+  const uint32_t h = to_h((float)(2u * (bword >> 28) + 1u));
+  return h | (h << 16);
+}
 
 // The 8 exact integers of group i (0..3) of a sub-block with payload words
-// (A, B): S16 = iq2_scale16(B), CB = (lane % 16) << 4.
-__device__ __forceinline__ uint4 iq2_frag_words(uint32_t A, uint32_t B, int i, uint32_t S16, uint32_t CB,
+// (A, B): SC = iq2_scale_h2(B), CB = (lane % 16) << 4.
+__device__ __forceinline__ uint4 iq2_frag_words(uint32_t A, uint32_t B, int i, uint32_t SC, uint32_t CB,
                                                 const uint8_t* tm, const uint8_t* sgn) {
-  // row << 8 | s << 4: byte 0 from S16, byte 1 = byte i of A
-  const uint32_t maddr = __builtin_amdgcn_perm(A, S16, 0x0c0c0000u | ((4u + i) << 8));
+  // row << 8 | copy << 4: byte 0 from CB, byte 1 = byte i of A
+  const uint32_t maddr = __builtin_amdgcn_perm(A, CB, 0x0c0c0000u | ((4u + i) << 8));
   // (7 sign bits) << 8 | copy << 4
   const uint32_t sh = i == 0 ? (B << 8) : i == 1 ? (B << 1) : i == 2 ? (B >> 6) : (B >> 13);
   const uint32_t saddr = (sh & 0x7f00u) | CB;
   const uint4 m = *reinterpret_cast<const uint4*>(tm + maddr);
   const uint4 s = *reinterpret_cast<const uint4*>(sgn + saddr);
-  return make_uint4(m.x ^ s.x, m.y ^ s.y, m.z ^ s.z, m.w ^ s.w);
+  const f16x2_t sc = __builtin_bit_cast(f16x2_t, SC);
+  auto word = [&](uint32_t mw, uint32_t sw) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, mw ^ sw) * sc);
+  };
+  return make_uint4(word(m.x, s.x), word(m.y, s.y), word(m.z, s.z), word(m.w, s.w));
 }
 
 }  // namespace qmoe

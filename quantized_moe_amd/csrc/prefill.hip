@@ -149,20 +149,6 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------------------
-// LDS tables (built once per persistent block)
-// ---------------------------------------------------------------------------
-// Q2K: tqs[sc][byte] = 4 x fp16 sc * q_i for the four 2-bit quants of byte.
-__device__ void build_q2k_table(uint2* tqs) {
-  for (int e = threadIdx.x; e < 16 * 256; e += blockDim.x) {
-    const int sc = e >> 8, b = e & 255;
-    uint32_t v[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = to_h((float)(sc * ((b >> (2 * i)) & 3)));
-    tqs[e] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-  }
-}
-
-// ---------------------------------------------------------------------------
 // B operand: one lane's weight row, a superblock (KS = 1) or half a
 // superblock (KS = 2) at a time.
 //
@@ -363,26 +349,51 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 }
 
 // Fragment of local step i (q = 4h + i): 8 exact integers, group i of the
-// lane's sub-block.  S16 = iq2_scale16 of the sub-block, CB = (lane % 16) << 4.
+// lane's sub-block.  SC = iq2_scale_h2 of the sub-block, CB = (lane % 16) << 4.
 template <int KS>
-__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2, KS>& b, int hh, int i, uint32_t S16, uint32_t CB,
+__device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2, KS>& b, int hh, int i, uint32_t SC, uint32_t CB,
                                           const uint8_t* tm, const uint8_t* sgn) {
-  return iq2_frag_words(b.w[2 * hh], b.w[2 * hh + 1], i, S16, CB, tm, sgn);
+  return iq2_frag_words(b.w[2 * hh], b.w[2 * hh + 1], i, SC, CB, tm, sgn);
 }
 
-// Q2K fragment of local step i: quant bytes 2i, 2i+1 of the lane's 8, whose
-// sub-block scale is sc (SC = sc << 16); lookup byte address of quant byte x
-// is (sc << 8 | x) << 3 = perm(word, SC) >> 5 with x placed in byte 1.
+// Q2K fragment constants of a sub-block with scale sc: quants placed under
+// the fp16 exponent byte 0x64 read 1024 + 4^p q for field p of their byte, and
+// one packed fused multiply-add with (mul, add) per pair of fields leaves the
+// exact integers sc * q (<= 45): fields 0, 1 take (sc, sc / 4) and
+// (-1024 sc, -256 sc); fields 2, 3 take (sc / 16, sc / 64) and (-64 sc, -16 sc).
+struct Q2kConst {
+  f16x2_t mul01, add01, mul23, add23;
+};
+__device__ __forceinline__ Q2kConst q2k_const(uint32_t sc) {
+  const _Float16 h = (_Float16)(float)sc;
+  const f16x2_t hh = {h, h};
+  Q2kConst k;
+  k.mul01 = hh * f16x2_t{(_Float16)1.0f, (_Float16)0.25f};
+  k.add01 = hh * f16x2_t{(_Float16)-1024.0f, (_Float16)-256.0f};
+  k.mul23 = hh * f16x2_t{(_Float16)0.0625f, (_Float16)0.015625f};
+  k.add23 = hh * f16x2_t{(_Float16)-64.0f, (_Float16)-16.0f};
+  return k;
+}
+
+// Q2K fragment of local step i: quant bytes 2i, 2i+1 of the lane's 8 (four
+// 2-bit quants each, weight 4j + p in field p of byte j) as the 8 exact
+// integers sc * q, computed in registers: a table lookup per byte would put
+// lanes with equal (sc, byte) bits on the same LDS banks.
 template <int KS>
-__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K, KS>& b, int hh, int i, uint32_t SC,
-                                          const uint8_t* tqs) {
+__device__ __forceinline__ uint4 q2k_frag(const BRegs<FMT_Q2K, KS>& b, int hh, int i, const Q2kConst& k) {
   const uint32_t w = (i >> 1) ? b.q[2 * hh + 1] : b.q[2 * hh];
-  const int x0 = 2 * (i & 1);  // quant bytes x0, x0 + 1 of word w
-  const uint32_t a0 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((4u + x0) << 8)) >> 5;
-  const uint32_t a1 = __builtin_amdgcn_perm(w, SC, 0x0c020000u | ((5u + x0) << 8)) >> 5;
-  const uint2 lo = *reinterpret_cast<const uint2*>(tqs + a0);
-  const uint2 hi = *reinterpret_cast<const uint2*>(tqs + a1);
-  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  const uint32_t x0 = 2u * (uint32_t)(i & 1);  // quant bytes x0, x0 + 1 of word w
+  auto words = [&](uint32_t x, uint32_t& w01, uint32_t& w23) {
+    const uint32_t t = __builtin_amdgcn_perm(w, 0x64646464u, 0x00040004u + 0x00010001u * x);  // byte x in bytes 0, 2
+    w01 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t & 0xff0cff03u),
+                                                                 k.mul01, k.add01));
+    w23 = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, t & 0xffc0ff30u),
+                                                                 k.mul23, k.add23));
+  };
+  uint32_t a, bb, c, d;
+  words(x0, a, bb);
+  words(x0 + 1, c, d);
+  return make_uint4(a, bb, c, d);
 }
 
 // Q2K min-term B fragment (K = the 16 sub-blocks): 16 m_j for j = 4*g4 .. +3,
@@ -517,14 +528,13 @@ template <int FMT, bool GATEUP, int KS>
 struct GemmLds {
   static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
   static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
-  static constexpr int kTqs = FMT == FMT_Q2K ? 16 * 256 * 8 : 0;
   static constexpr int kCb = is_vq(FMT) ? vq_codes(FMT) * 8 : 0;      // VQ codebook (E4M3)
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
   static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
   static constexpr int kTok = 3 * BM * 8;                             // token (gate/up) and scale of each row, 3 items
   static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
   static constexpr int kMax = GATEUP ? 2 * BM * 4 : 0;                // gate/up: [item parity][BM] row maxima of |h|
-  static constexpr int oSgn = kMag, oTqs = oSgn + kSgn, oCb = oTqs + kTqs, oA = oCb + kCb, oS = oA + kA, oTok = oS + kS,
+  static constexpr int oSgn = kMag, oCb = oSgn + kSgn, oA = oCb + kCb, oS = oA + kA, oTok = oS + kS,
                        oRed = oTok + kTok, oMax = oRed + kRed, oTiles = oMax + kMax;
   // then tile_start, counts, offsets of the routed experts: [3][E + 1]
   static constexpr int bytes_for(int E) { return oTiles + 3 * (E + 1) * 4; }
@@ -546,7 +556,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const uint8_t* tm = lds;
   const uint8_t* sgn = lds + L::oSgn;
-  const uint8_t* tqs = lds + L::oTqs;
   uint8_t* sA = lds + L::oA;
   uint16_t* sS = reinterpret_cast<uint16_t*>(lds + L::oS);
   int* sTok = reinterpret_cast<int*>(lds + L::oTok);              // [3][BM]
@@ -564,7 +573,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 
   if constexpr (FMT == FMT_IQ2)
     build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid, GEMM_THREADS);
-  if constexpr (FMT == FMT_Q2K) build_q2k_table(reinterpret_cast<uint2*>(lds + L::oTqs));
   if constexpr (is_vq(FMT)) vq_stage_codebook(a.vq_cb, lds + L::oCb, vq_codes(FMT), tid, GEMM_THREADS);
   if constexpr (GATEUP) {
     if (tid < 2 * BM) sMax[tid] = 0u;
@@ -866,9 +874,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       for (int hh = 0; hh < 3 - KS; hh++) {  // halves of the lane's slice (one for KS = 2)
         uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
         f16x2_t mul0 = {}, add0 = {}, mul1 = {}, add1 = {};
+        Q2kConst kq0 = {}, kq1 = {};
         if constexpr (FMT == FMT_IQ2) {
-          S0 = iq2_scale16(B0.w[2 * hh + 1]);
-          if constexpr (GATEUP) S1 = iq2_scale16(B1.w[2 * hh + 1]);
+          S0 = iq2_scale_h2(B0.w[2 * hh + 1]);
+          if constexpr (GATEUP) S1 = iq2_scale_h2(B1.w[2 * hh + 1]);
         } else if constexpr (FMT == FMT_Q4K) {
           const int sbl = KS == 2 ? h : hh;  // the lane's sub-block 2*g4 + sbl
           auto consts = [&](uint32_t sc, f16x2_t& mul, f16x2_t& add) {
@@ -893,10 +902,13 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
             f0 = q4k_frag(word_of(B0.q[KS == 2 ? 0 : hh], i), mul0, add0);
             if constexpr (GATEUP) f1 = q4k_frag(word_of(B1.q[KS == 2 ? 0 : hh], i), mul1, add1);
           } else {
-            // low nibble of scale byte i/2, as sc << 16
-            const int sh = 16 - 8 * (i >> 1);
-            f0 = q2k_frag(B0, hh, i, (sc0 << sh) & 0xf0000u, tqs);
-            if constexpr (GATEUP) f1 = q2k_frag(B1, hh, i, (sc1 << sh) & 0xf0000u, tqs);
+            // low nibble of scale byte i/2
+            if (i % 2 == 0) {
+              kq0 = q2k_const((sc0 >> (8 * (i >> 1))) & 15u);
+              if constexpr (GATEUP) kq1 = q2k_const((sc1 >> (8 * (i >> 1))) & 15u);
+            }
+            f0 = q2k_frag(B0, hh, i, kq0);
+            if constexpr (GATEUP) f1 = q2k_frag(B1, hh, i, kq1);
           }
 #pragma unroll
           for (int m = 0; m < NM; m++) {
@@ -1273,7 +1285,10 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
           return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
         }
       } else {
-        if constexpr (!(GATEUP && FMT == FMT_Q2K)) {
+        // (gate/up: two superblocks in flight spill once the IQ2 fragments
+        // carry their scale multiply; measured 1.62 ms against 1.90 ms with
+        // two at 8 x 4096 Zipf tokens)
+        if constexpr (!GATEUP) {
           if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
         }
         return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
