@@ -20,7 +20,7 @@ OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "bucket.hip", "repack.hip", "decode.hip", "decode_k1.hip", "decode_k2.hip",
-           "decode_k3.hip", "prefill.hip"]
+           "decode_k3.hip", "decode_unique.hip", "prefill.hip"]
 PROBE_SOURCES = ["probe.hip"]
 # packed-fp32 VALU forms are disabled: only ordinary fp32 instructions
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -7,6 +7,10 @@
 //      streams while the blocks wait for the router logits and the top-k;
 //   3. routed and shared down projections and the fixed-order combine.
 //
+// With several tokens (block formats) a small planning launch between 1 and
+// 2 takes the top-k and lists the distinct experts, and 2 and 3 run over
+// those experts (decode_unique.hip).
+//
 // The kernels are in decode_k1/k2/k3.hip; their common pieces (activation
 // fixed point, IQ2 nibble table, weight pieces, dot products) in
 // decode_common.hpp.
@@ -17,6 +21,8 @@ namespace dec {
 hipError_t launch_k1(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_layout, hipStream_t s);
 hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks, int down_layout, hipStream_t s);
 hipError_t launch_k3(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
+hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_k3u(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
 }  // namespace dec
 
 using namespace dec;
@@ -26,7 +32,7 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecodeWsLayout {
-  size_t xq, xs, xq_s, xs_s, hsh, hq, hs, hf, total;
+  size_t xq, xs, xq_s, xs_s, hsh, hq, hs, hf, plan, total;
 };
 
 DecodeWsLayout ws_layout(int T, int k, int d, int f) {
@@ -48,8 +54,29 @@ DecodeWsLayout ws_layout(int T, int k, int d, int f) {
   off = align256(off + (size_t)T * k * (f / 16) * 4);
   L.hf = off;
   off = align256(off + (size_t)T * k * f * 4);
+  L.plan = off;  // distinct experts (at most T k) and the routes grouped by them
+  off = align256(off + (size_t)(2 + 3 * T * k) * 4);
   L.total = off;
   return L;
+}
+
+// Groups of 16 routed h rows per gate/up block: GCNT minimises (rounds of
+// blocks) x (work per block), blocks never straddling a token.
+int gcnt_of(int k, int f, int T, int ncu) {
+  const int groups_per_token = k * f / 16;
+  const int NG = T * groups_per_token;
+  int best = 1;
+  int64_t best_cost = -1;
+  for (int g = 3; g >= 1; g--) {
+    if (groups_per_token % g) continue;
+    const int64_t blocks = NG / g;
+    const int64_t cost = ((blocks + ncu - 1) / ncu) * g;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = g;
+    }
+  }
+  return best;
 }
 
 // CUs of the current device (cached per device by launch_shape)
@@ -107,6 +134,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);
   a.hf = reinterpret_cast<float*>(q + W.hf);
+  a.plan = reinterpret_cast<int*>(q + W.plan);
+  a.umax = L.E < L.T * L.k ? L.E : L.T * L.k;
   a.y = L.y;
   int ncu = 256;
   if (hipError_t e = cu_count(&ncu); e != hipSuccess) return e;
@@ -136,7 +165,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
       pl.spb = 1;
       pl.n_sb = 0;
     }
-    pl.n_xb = pl.n_rb == 0 ? 1 : 0;  // x for the routed gate/up is quantized by a block of its own
+    // x for the routed gate/up: by the router blocks' last waves, or without a
+    // router by blocks of its own, one octet of chunks per wave
+    const int n_oct = (L.T * (L.d / 64) + 7) / 8;
+    pl.n_xb = pl.n_rb == 0 ? (n_oct + WAVES - 1) / WAVES : 0;
   }
   {
     const int pid = prof_begin("decode_router", s);
@@ -145,22 +177,37 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
 
-  // launch 2: groups of 16 routed h rows, GCNT per block, blocks never
-  // straddling a token; GCNT minimises (rounds of blocks) x (work per block)
-  {
-    const int groups_per_token = L.k * L.f / 16;
-    const int NG = L.T * groups_per_token;
-    int best = 1;
-    int64_t best_cost = -1;
-    for (int g = 3; g >= 1; g--) {
-      if (groups_per_token % g) continue;
-      const int64_t blocks = NG / g;
-      const int64_t cost = ((blocks + ncu - 1) / ncu) * g;
-      if (best_cost < 0 || cost < best_cost) {
-        best_cost = cost;
-        best = g;
-      }
+  // Several tokens (block formats): the top-k and the distinct experts in a
+  // small launch of their own, then gate/up and down over the distinct
+  // experts, each expert's codes loaded once for all its routes.
+  if (L.T >= 2 && !is_vq(L.fmt_gate_up)) {
+    {
+      const int pid = prof_begin("decode_plan", s);
+      hipError_t e = launch_plan(a, s);
+      prof_end(pid, s);
+      if (e != hipSuccess) return e;
     }
+    {  // per token, the routes from the plan
+      DecodeArgs b = a;
+      b.fused_topk = 0;
+      const int pid = prof_begin("decode_gateup", s);
+      hipError_t e = launch_k2(b, L.fmt_gate_up, fs, gcnt_of(L.k, L.f, L.T, ncu), L.T * L.k * L.f / 16 /
+                               gcnt_of(L.k, L.f, L.T, ncu), nib_layout(L.fmt_down), s);
+      prof_end(pid, s);
+      if (e != hipSuccess) return e;
+    }
+    // (rows of more than 2048 inputs: the one-token kernel, per token)
+    const int pid = prof_begin("decode_down_combine", s);
+    hipError_t e = L.f <= 2048 ? launch_k3u(a, L.fmt_down, fs, s) : launch_k3(a, L.fmt_down, fs, s);
+    prof_end(pid, s);
+    return e;
+  }
+
+  // launch 2: groups of 16 routed h rows, GCNT per block, blocks never
+  // straddling a token
+  {
+    const int best = gcnt_of(L.k, L.f, L.T, ncu);
+    const int NG = L.T * L.k * L.f / 16;
     const int pid = prof_begin("decode_gateup", s);
     hipError_t e = launch_k2(a, L.fmt_gate_up, fs, best, NG / best, nib_layout(L.fmt_down), s);
     prof_end(pid, s);

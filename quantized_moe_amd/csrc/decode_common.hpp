@@ -935,8 +935,22 @@ struct DecodeArgs {
   uint8_t* hq;       // [T*k][f/16] quantized routed SwiGLU outputs
   float* hs;         // [T*k][f/16]
   float* hf;         // [T*k][f] routed SwiGLU outputs in fp32 (VQ routed formats)
+  int* plan;         // several tokens: distinct experts and their routes (decode_unique.hip)
+  int umax;          // the plan's capacity in distinct experts, min(E, T k)
   float* y;          // [T][d]
 };
+
+// Up to 2048 inputs per row and a Q8 shared expert: 16 waves, a routed
+// expert's 16 rows as two tasks of 8 and the shared expert's as four tasks
+// of 4 (16 tasks for k = 6, four per SIMD); longer rows, or a 2-bit shared
+// expert (whose h slice is quantized from 64 fp32 values per piece), need
+// more registers per wave: 8 waves, one task per routed expert and two for
+// the shared expert.
+// (Q4K routed rows, with twice the code registers per piece, and VQ rows,
+// whose h slice is 64 fp32 values per piece, take 8 waves.)
+constexpr int k3_waves(int FR, int FS, int F) {
+  return F <= 2048 && FS == FMT_Q8 && FR != FMT_Q4K && !is_vq(FR) ? 16 : 8;
+}
 
 // Work split of the first kernel: blocks [0, n_rb) hold epb (< 8) router
 // experts each (one per wave; the last wave quantizes x for the routed
@@ -945,7 +959,7 @@ struct DecodeArgs {
 // same number of bytes.
 struct K1Plan {
   int n_rb, epb, n_sb, spb, n_steps;
-  int n_xb;  // 1 when only a block quantizing x runs (no router, no shared expert)
+  int n_xb;  // blocks that only quantize x (one octet of chunks per wave), when no router runs
 };
 
 }  // namespace dec

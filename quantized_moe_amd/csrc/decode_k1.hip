@@ -6,7 +6,9 @@
 // Blocks [0, n_rb) are router blocks: one expert per wave.  Blocks
 // [n_rb, n_rb + n_sb) are shared-expert blocks: each takes spb consecutive
 // wave steps of the shared gate/up; its waves issue their weight loads
-// first, then quantize x into LDS together (once per token), then compute.
+// first, then quantize every token's x into LDS together (dynamic LDS,
+// T x d/64 chunks and scales), then run every token against the weights in
+// registers, with no barrier between tokens.
 // epb and spb are chosen by the host so that all blocks stream about the same
 // number of bytes.
 #include "decode_rows.hpp"
@@ -27,11 +29,13 @@ __device__ __forceinline__ void load_x_act(typename RoutedAct<FMT, D>::type& act
   }
 }
 
+// Dynamic LDS of the shared blocks for T tokens.
+__host__ __device__ constexpr int k1_x_lds_bytes(int T, int D) { return T * (D / 64) * (CHUNK_BYTES + 4); }
+
 template <int FMT_S, int D>
 __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, int gu_layout) {
   __shared__ Iq2Tab itab;
-  __shared__ __attribute__((aligned(16))) uint8_t s_xq[(D / 64) * CHUNK_BYTES];
-  __shared__ float s_xs[D / 64];
+  extern __shared__ __align__(16) uint8_t k1_dyn[];  // shared blocks: x chunks [T][D/64], then scales [T][D/64]
   constexpr int SCL_BYTES =
       RowScales<FMT_S, D>::STAGE ? 4 * Geo<FMT_S, D>::RPS * RowScales<FMT_S, D>::BYTES : 16;
   __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * SCL_BYTES];
@@ -39,12 +43,21 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nch_all = a.T * (D / 64);       // x chunks of all tokens, for the routed gate/up
   const int n_oct = (nch_all + 7) / 8;      // ... in octets, one per wave call
-  if (b < pl.n_rb || b >= pl.n_rb + pl.n_sb) {  // a router block, or the lone x block
-    if (wave < pl.epb && b < pl.n_rb) {
-      const int e = b * pl.epb + wave;
-      if (e < a.E) router_item<D>(a, e);
-    } else if (wave == WAVES - 1) {
-      const int first = b < pl.n_rb ? b : 0, stride = pl.n_rb > 0 ? pl.n_rb : 1;
+  if (b < pl.n_rb || b >= pl.n_rb + pl.n_sb) {  // a router block, or an x block
+    int first = -1, stride = 1;
+    if (b < pl.n_rb) {
+      if (wave < pl.epb) {
+        const int e = b * pl.epb + wave;
+        if (e < a.E) router_item<D>(a, e);
+      } else if (wave == WAVES - 1) {  // the last wave quantizes x
+        first = b;
+        stride = pl.n_rb;
+      }
+    } else {  // x blocks: every wave an octet
+      first = (b - pl.n_rb - pl.n_sb) * WAVES + wave;
+      stride = pl.n_xb * WAVES;
+    }
+    if (first >= 0) {
       for (int o = first; o < n_oct; o += stride) {
         quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
         if (a.shared_k2) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
@@ -53,28 +66,18 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
     return;
   }
   // shared-expert block: waves take steps s_lo + wave, s_lo + wave + 8 (two
-  // per round).  Loads complete in order, so the x loads go out first, then
-  // the scale bytes, then the weights; x is quantized into LDS (one octet of
-  // chunks per wave) once it is back.
+  // per round).  The scale bytes and weights of the first round are
+  // requested, then every token's x is quantized into LDS ((token, octet)
+  // items over the waves); one barrier; then every token runs against the
+  // round's weights.
   using G = Geo<FMT_S, D>;
   constexpr int NOCT = (D / 64 + 7) / 8;    // octets of chunks of one token
-  constexpr int OPW = (NOCT + WAVES - 1) / WAVES;
+  uint8_t* s_xq = k1_dyn;                                                          // [T][D/64][128]
+  float* s_xs = reinterpret_cast<float*>(k1_dyn + (size_t)a.T * (D / 64) * CHUNK_BYTES);  // [T][D/64]
   const int sub = lane / G::LPR, c = lane % G::LPR;
   const int s_lo = (b - pl.n_rb) * pl.spb;
   const int s_hi = min(pl.n_steps, s_lo + pl.spb);
   const EPlanes Gp = expert_planes<FMT_S>(a.s_gate, 0), Up = expert_planes<FMT_S>(a.s_up, 0);
-  XOctet xo[OPW];
-  auto x_load = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < OPW; i++)
-      xo[i].load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
-                 D / 64, 8 * (wave + WAVES * i), nib_layout(FMT_S));
-  };
-  auto x_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < OPW; i++) xo[i].store(D / 64, s_xq, s_xs, nib_layout(FMT_S));
-  };
-  x_load(0);
   if constexpr (FMT_S == FMT_IQ2) iq2_build(a.grid, threadIdx.x, &itab);  // published by the barrier below
   using SS = ScaleStage<FMT_S, D, 2, 2 * G::RPS>;  // gate/up x (2 steps x RPS rows)
   constexpr bool STAGE = SS::RS::STAGE;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
   };
   auto compute = [&](int t) {
     typename RoutedAct<FMT_S, D>::type act;  // chunk-quantized x, as for the routed rows
-    load_x_act<FMT_S, D>(act, s_xq, s_xs);
+    load_x_act<FMT_S, D>(act, s_xq + (size_t)t * (D / 64) * CHUNK_BYTES, s_xs + (size_t)t * (D / 64));
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       if constexpr (STAGE) {
@@ -127,40 +130,37 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
       if (c == G::LPR - 1 && st[i] < s_hi) a.hsh[(int64_t)t * a.f + st[i] * G::RPS + sub] = silu(g) * u;
     }
   };
-  // first round, first token: straight-line, so x is waited for alone
-  {
-    SS ss;
-    if constexpr (STAGE) ss = stage(s_lo);
-    issue(0, s_lo);
-    issue(1, s_lo);
-    if constexpr (STAGE) ss.store(my_scales);
-    x_store();
-    __syncthreads();
-    compute(0);
-  }
-  // further tokens and rounds (more than one token, or a block with more
-  // than 16 steps)
   for (int base = s_lo; base < s_hi; base += 2 * WAVES) {
-    if (base != s_lo) {
-      SS ss;
-      if constexpr (STAGE) ss = stage(base);
-      issue(0, base);
-      issue(1, base);
-      if constexpr (STAGE) ss.store(my_scales);
-    }
-    for (int t = (base == s_lo ? 1 : 0); t < a.T; t++) {
-      __syncthreads();  // the previous token's chunks are no longer read
-      x_load(t);
-      x_store();
+    SS ss;
+    if constexpr (STAGE) ss = stage(base);
+    issue(0, base);
+    issue(1, base);
+    if constexpr (STAGE) ss.store(my_scales);
+    if (base == s_lo) {
+      for (int item = wave; item < a.T * NOCT; item += WAVES) {
+        const int t = item / NOCT, o = item % NOCT;
+        XOctet xo;
+        xo.load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
+                D / 64, 8 * o, nib_layout(FMT_S));
+        xo.store(D / 64, s_xq + (size_t)t * (D / 64) * CHUNK_BYTES, s_xs + (size_t)t * (D / 64), nib_layout(FMT_S));
+      }
       __syncthreads();
-      compute(t);
     }
+    for (int t = 0; t < a.T; t++) compute(t);
   }
 }
 
 template <int FMT_S, int D>
 static hipError_t run_k1(const DecodeArgs& a, const K1Plan& pl, int gu_layout, hipStream_t s) {
-  QMOE_LAUNCH((k1_kernel<FMT_S, D>), dim3(pl.n_rb + pl.n_sb + pl.n_xb), dim3(THREADS), 0, s, a, pl, gu_layout);
+  const int dyn = pl.n_sb > 0 ? k1_x_lds_bytes(a.T, D) : 0;
+  if (dyn > 0) {  // (raises the kernel's dynamic-LDS limit on first use)
+    int per_cu = 0, n_cus = 0;
+    if (hipError_t e = launch_shape((const void*)k1_kernel<FMT_S, D>, THREADS, dyn,
+                                    k1_x_lds_bytes(DECODE_MAX_T, D), &per_cu, &n_cus);
+        e != hipSuccess)
+      return e;
+  }
+  QMOE_LAUNCH((k1_kernel<FMT_S, D>), dim3(pl.n_rb + pl.n_sb + pl.n_xb), dim3(THREADS), dyn, s, a, pl, gu_layout);
   return hipGetLastError();
 }
 

@@ -44,18 +44,6 @@ __device__ __forceinline__ void down_rows(const QMat& m, int e, int E, int r0, c
   dr.run(tab, my_scales, out);
 }
 
-// Up to 2048 inputs per row and a Q8 shared expert: 16 waves, a routed
-// expert's 16 rows as two tasks of 8 and the shared expert's as four tasks
-// of 4 (16 tasks for k = 6, four per SIMD); longer rows, or a 2-bit shared
-// expert (whose h slice is quantized from 64 fp32 values per piece), need
-// more registers per wave: 8 waves, one task per routed expert and two for
-// the shared expert.
-// (Q4K routed rows, with twice the code registers per piece, and VQ rows,
-// whose h slice is 64 fp32 values per piece, take 8 waves.)
-constexpr int k3_waves(int FR, int FS, int F) {
-  return F <= 2048 && FS == FMT_Q8 && FR != FMT_Q4K && !is_vq(FR) ? 16 : 8;
-}
-
 template <int FR, int FS, int F>
 __global__ __launch_bounds__(64 * k3_waves(FR, FS, F)) void k3_kernel(DecodeArgs a) {
   constexpr int K3_WAVES = k3_waves(FR, FS, F);

@@ -260,7 +260,10 @@ struct DownRows {
     for (int s = 0; s < PD; s++) issue_step(s);
     if constexpr (STAGE) ss.store(my_scales);
   }
-  __device__ __forceinline__ void run(const Iq2Tab* tab, const uint8_t* my_scales, float* out) {
+  // issue_more = false: every step's codes are already in registers (a
+  // later h vector against the same rows, after a first run)
+  __device__ __forceinline__ void run(const Iq2Tab* tab, const uint8_t* my_scales, float* out,
+                                      bool issue_more = true) {
     const int lane = threadIdx.x & 63, sub = lane / G::LPR, c = lane % G::LPR;
     if (!valid) {
       if (lane < ROWS) out[lane] = 0.0f;
@@ -269,7 +272,7 @@ struct DownRows {
     if constexpr (FMT != FMT_Q8 && FMT != FMT_MX4) act.sums();  // Q2K's min term, IQ2's 2u - 7 offset
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      if (s + PD < NS) issue_step(s + PD);
+      if (issue_more && s + PD < NS) issue_step(s + PD);
       const int j = s * G::RPS + sub;
       if constexpr (STAGE) {
 #pragma unroll

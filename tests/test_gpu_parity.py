@@ -255,9 +255,10 @@ def test_route_topk_ties_and_zero():
     assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
 
 
-@pytest.mark.parametrize("T,dt", [(1, synth.F32), (7, synth.BF16), (1024, synth.BF16), (300, synth.F32)])
+@pytest.mark.parametrize("T,dt", [(1, synth.F32), (7, synth.BF16), (8, synth.F32), (12, synth.BF16),
+                                  (1024, synth.BF16), (300, synth.F32)])
 def test_route_topk_full_router(T, dt):
-    """384 experts x d=4096 router, both router kernels (T <= 16 and tiled)."""
+    """384 experts x d=4096 router, both router kernels (T <= 8 and tiled)."""
     W = synth.router_weights(0, ("decode", 0, "router"), 384, 4096)
     x = synth.activations(0, ("route", T), T, 4096, dt)
     idx = torch.empty(T, 6, dtype=torch.int32, device=DEV)
@@ -270,7 +271,26 @@ def test_route_topk_full_router(T, dt):
     assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
 
 
-@pytest.mark.parametrize("T,k,E", [(1, 6, 384), (3, 2, 8), (1024, 6, 384), (4096, 6, 384), (50, 16, 17)])
+@pytest.mark.parametrize("T,k,E,dt", [(5, 16, 1000, synth.F32), (300, 6, 520, synth.BF16), (3, 6, 1024, synth.BF16)])
+def test_route_topk_more_than_512_experts(T, k, E, dt):
+    """E > 512 takes the two-register-per-lane top-k; router rows are
+    duplicated in pairs so that equal logits must resolve to the lower
+    index."""
+    W = synth.router_weights(0, ("route-large", E), E, 1024)
+    W[1::2] = W[0::2][: E // 2]
+    x = synth.activations(0, ("route-large", T, E), T, 1024, dt)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    ws = torch.empty(T * E * 4 + 4096, dtype=torch.uint8, device=DEV)
+    lib.route_topk(torch.from_numpy(W).to(DEV), to_dev_x(x, dt), k, idx, wt, ws)
+    torch.cuda.synchronize()
+    _, idx_ref, wt_ref = oracle.route(x, dt, W, k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(wt.cpu().numpy() - wt_ref)) <= WT_TOL
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 6, 384), (3, 2, 8), (1024, 6, 384), (4096, 6, 384), (50, 16, 17),
+                                   (64, 16, 1000), (300, 6, 520), (2, 16, 1024)])
 def test_bucket_bit_exact(T, k, E):
     rng = np.random.default_rng(T + k + E)
     if T == 4096:
@@ -490,6 +510,27 @@ def test_decode_batch_invariance(decode_layer):
     for t in range(4):
         y1 = run_ffn(dl, x[t:t + 1], synth.F32, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
         assert np.array_equal(y1[0], y4[t])
+
+
+@pytest.mark.parametrize("bias_gain", [False, True])
+def test_decode_several_tokens_equal_single_token_calls(bias_gain):
+    """Several tokens with fused routing (top-k in the planning launch, each
+    chosen expert read once for all its routes) give bitwise the rows,
+    routes and weights of one-token calls, also with a router bias and down
+    gains; and every token matches the oracle."""
+    spec = synth.scaled_spec(E=40, k=6, d=1024, f=1024)
+    L = _bias_gain_layer(spec, 61, gains=bias_gain) if bias_gain else synth.random_layer(spec, seed=61, workload="multi")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    T = 7
+    x = synth.activations(61, ("multi", "x"), T, spec.d, synth.F32)
+    x[3] = x[1]  # two equal tokens: the same experts twice
+    y, idx, wt = run_layer(dl, x, synth.F32, lib.MOE_PATH_DECODE)
+    for t in range(T):
+        y1, idx1, wt1 = run_layer(dl, x[t:t + 1], synth.F32, lib.MOE_PATH_DECODE)
+        assert np.array_equal(y1[0], y[t]) and np.array_equal(idx1[0], idx[t]) and np.array_equal(wt1[0], wt[t]), t
+    y_ref, idx_ref, _ = oracle.layer_forward(L, x, synth.F32)
+    assert np.array_equal(idx, idx_ref)
+    assert per_token_rel_l2(y, y_ref).max() <= REL_L2
 
 
 def test_determinism_and_graph_replay(decode_layer):
