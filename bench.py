@@ -577,7 +577,7 @@ def main() -> int:
 
     if "crossover" in want:
         rows = {}
-        for T in (1, 2, 4, 8, 16, 32, 64, 128):
+        for T in (1, 2, 4, 8, 16, 24, 32, 64, 128):
             idx_h, wt_h = synth.session_routes(0, sessions=max(1, T // 4) if T >= 4 else T, steps=min(4, T) if T >= 4
                                                else 1, tag=f"sweep{T}")
             x_h = synth.activations(0, ("bench", "sweep", T), T, d, synth.F32)

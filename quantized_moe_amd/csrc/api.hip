@@ -354,12 +354,12 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   w.xs = (float*)c.take((size_t)T * 4);
   w.route_xs = (float*)c.take(n * 4);
   w.H = c.take(n * f * 2);
-  w.Hexp = (int8_t*)c.take(n * (f / 128));
+  w.Hexp = (int8_t*)c.take(n * (f / PREFILL_HCHUNK));
   w.Hsc = (float*)c.take(n * 4);
   w.Ye = (float*)c.take(n * d * 4);
   if (has_shared) {
     w.Hs = c.take((size_t)T * f * 2);
-    w.Hsexp = (int8_t*)c.take((size_t)T * (f / 128));
+    w.Hsexp = (int8_t*)c.take((size_t)T * (f / PREFILL_HCHUNK));
     w.Hssc = (float*)c.take((size_t)T * 4);
     w.Ysh = (float*)c.take((size_t)T * d * 4);
   } else {
@@ -398,9 +398,9 @@ size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
   Carve c;
   LayerWs lw;
   carve_layer_routes(c, lw, E, T, k);
-  if (path == MOE_PATH_DECODE) {
+  if (path == MOE_PATH_DECODE) {  // (calls above the decode limit run in chunks of at most that many tokens)
     DecodeWs w;
-    carve_decode(c, w, T, k, d, f);
+    carve_decode(c, w, T < DECODE_MAX_T ? T : DECODE_MAX_T, k, d, f);
   } else {
     PrefillWs w;
     carve_prefill(c, w, E, T, k, d, f, sh, false);
@@ -787,7 +787,7 @@ static int layer_forward(const char* fn, const moe_layer* L, const void* x, int3
   if (path != MOE_PATH_AUTO && path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown path %d", fn, path);
   const int p = resolve_path(path, T);
-  if (p == MOE_PATH_DECODE && T > DECODE_MAX_T)
+  if (path == MOE_PATH_DECODE && T > DECODE_MAX_T)
     return fail(MOE_ERR_INVALID_ARG, "%s: T %d above the decode limit %d", fn, T, DECODE_MAX_T);
   if (p == MOE_PATH_PREFILL && (rc = check_prefill_size(fn, T, L->top_k, L->d_model, L->d_ff))) return rc;
   if (T == 0) return ok();
@@ -813,20 +813,30 @@ static int layer_forward(const char* fn, const moe_layer* L, const void* x, int3
   carve_layer_routes(c, lw, E, T, k);
   hipStream_t s = (hipStream_t)stream;
   if (p == MOE_PATH_DECODE) {
+    // MOE_PATH_AUTO may pick the decode path above its per-call limit: then
+    // consecutive chunks of at most DECODE_MAX_T tokens, each a whole decode
+    // call on its slices of x, y, the routes and the workspace's quantized
+    // activations (reused by every chunk, in stream order)
+    const int d = L->d_model;
+    const int Tc = T < DECODE_MAX_T ? T : DECODE_MAX_T;
     DecodeWs w;
-    carve_decode(c, w, T, k, L->d_model, L->d_ff);
-    DecodeLaunch D = decode_launch(L, x, x_dtype, T);
-    D.z = lw.z;
-    D.zkey = lw.zkey;
-    D.idx = lw.idx;
-    D.wt = lw.wt;
-    D.idx_out = idx_out;
-    D.wt_out = wt_out;
-    D.quant = w.quant;
-    D.y = y;
-    D.fused_topk = 1;
-    hipError_t e = launch_decode(D, s);
-    if (e != hipSuccess) return hip_fail(e, fn);
+    carve_decode(c, w, Tc, k, d, L->d_ff);
+    const size_t x_el = x_dtype == MOE_BF16 ? 2 : 4;
+    for (int t0 = 0; t0 < T; t0 += Tc) {
+      const int n = T - t0 < Tc ? T - t0 : Tc;
+      DecodeLaunch D = decode_launch(L, static_cast<const uint8_t*>(x) + (size_t)t0 * d * x_el, x_dtype, n);
+      D.z = lw.z + (size_t)t0 * E;
+      D.zkey = lw.zkey + (size_t)t0 * E;
+      D.idx = lw.idx + (size_t)t0 * k;
+      D.wt = lw.wt + (size_t)t0 * k;
+      D.idx_out = idx_out ? idx_out + (size_t)t0 * k : nullptr;
+      D.wt_out = wt_out ? wt_out + (size_t)t0 * k : nullptr;
+      D.quant = w.quant;
+      D.y = y + (size_t)t0 * d;
+      D.fused_topk = 1;
+      hipError_t e = launch_decode(D, s);
+      if (e != hipSuccess) return hip_fail(e, fn);
+    }
     return ok();
   }
   int pid = prof_begin(T <= ROUTER_ROWS_MAX_T ? "router_rows" : "router_tiled", s);

@@ -80,7 +80,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s);
 size_t decode_quant_bytes(int T, int k, int d, int f);
 
 // prefill.hip: grouped GEMMs + combine (bucketing already done).
-constexpr int PREFILL_BM = 32;  // M tile of the grouped GEMMs (rows of one expert's bucket)
+constexpr int PREFILL_BM = 32;         // M tile of the routed grouped GEMMs (rows of one expert's bucket)
+constexpr int PREFILL_SHARED_BM = 64;  // M tile of the shared expert's GEMMs
+constexpr int PREFILL_HCHUNK = 64;  // outputs per power-of-two exponent of the gate/up GEMMs' fp16 H rows
 struct PrefillLaunch {
   int E, d, f, k, T;
   int fmt_gate_up, fmt_down, fmt_shared, has_shared;

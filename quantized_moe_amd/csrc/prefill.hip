@@ -14,22 +14,24 @@
 //   * the activations x are converted once to fp16 with a per-token power of
 //     two (exact) that puts max|x_t| in [2^13, 2^14), undone in the gate/up
 //     epilogue; the SwiGLU output h is stored as fp16 times a power of two
-//     per (row, 128 outputs) that puts max|h| over the work item's N tile
-//     (256 or 128 outputs) in [2^14, 2^15) (one rounding, 2^-11 relative,
+//     per (row, 64 outputs) that puts max|h| over the work item's N tile
+//     (a multiple of 64 outputs) in [2^14, 2^15) (one rounding, 2^-11 relative,
 //     whatever the scale of x and of the weights); a short pass then brings
 //     every row to its largest exponent (exact but for fp16 subnormals,
 //     below 2^-24 of the row's maximum), and the down GEMM applies the row's
 //     power of two to its fp32 outputs.
 //
 // One persistent kernel per GEMM (routed gate/up, routed down, shared gate/up,
-// shared down), 16 waves per block.  A work item is (M tile of 32 rows of one
-// expert's bucket, N tile of output rows); every wave owns 16 output rows and
-// both 16-row M sub-tiles, so each decoded B fragment feeds up to two MFMAs
-// per matrix.  Each wave takes whole superblocks (KS = 1, N tile 256): a
-// lane's weights of a superblock are one 16-byte load for the 2-bit formats.
-// Only the Q8 gate/up (two matrices of 4x the bytes, which would spill) has
-// the two waves of a pair split every superblock's inputs (KS = 2, N tile
-// 128), their partial sums meeting in LDS once per item.
+// shared down).  A work item is (M tile of BM rows of one expert's bucket, or
+// of the shared expert's rows, N tile of output rows); every wave owns 16
+// output rows and all 16-row M sub-tiles, so each decoded B fragment feeds up
+// to BM / 16 MFMAs per matrix.  The routed GEMMs run 32-row tiles in 16-wave
+// blocks (128 VGPRs per wave), the shared GEMMs 64-row tiles in 8-wave blocks
+// (256 VGPRs).  Each wave takes whole superblocks (KS = 1, N tile 16 per
+// wave): a lane's weights of a superblock are one 16-byte load for the 2-bit
+// formats.  Only two-matrix gate/up GEMMs that would spill (Q8 and Q4K in
+// 16-wave blocks) have the two waves of a pair split every superblock's
+// inputs (KS = 2), their partial sums meeting in LDS once per item.
 // The K loop runs over 256-input superblocks and is software-pipelined across
 // work items: every wave keeps its weight loads PD superblocks ahead in
 // registers, the A rows of the next superblock are loaded while the current
@@ -47,16 +49,29 @@
 
 namespace qmoe {
 
-constexpr int GEMM_PAIRS = 8;              // KS = 2: wave pairs, 16 output rows each
-constexpr int GEMM_WAVES = 2 * GEMM_PAIRS;  // (the two waves of a pair take the two halves of K)
-constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-// output rows per work item: 16 per wave, the waves of a pair sharing them (KS = 2) or not (KS = 1)
-__host__ __device__ constexpr int gemm_bn(int ks) { return 16 * GEMM_WAVES / ks; }
-constexpr int BM = PREFILL_BM;            // M rows per work item
-constexpr int NSUB = BM / 16;             // 16-row MFMA sub-tiles
-constexpr int A_PIECES = BM * 32;         // 16-byte pieces of one A superblock chunk
-constexpr int A_ROW = 33 * 16;            // LDS bytes per A row (32 pieces + one of padding)
-constexpr int A_BUF = BM * A_ROW;         // LDS bytes per A buffer
+constexpr int A_ROW = 33 * 16;  // LDS bytes per A row (32 pieces + one of padding)
+
+// Work-item shape: BM rows of A (one expert's bucket, or the shared
+// expert's rows) by 16 output rows per wave of a W-wave block, the two waves
+// of a pair sharing their output rows (KS = 2) or not (KS = 1).  The routed
+// GEMMs run (32, 16): four waves per SIMD at 128 VGPRs hide the weight
+// stream's latency, and their buckets hold few rows.  The shared GEMMs run
+// (64, 8): every item has 64 rows, each decoded weight fragment feeds up to
+// four MFMAs, and 256 VGPRs per wave hold them (measured at 1024 and 8 x
+// 4096 tokens: (64, 8) was faster for the shared expert and slower for the
+// routed experts, (64, 16) spilled).
+template <int BM_, int W_>
+struct GemmTile {
+  static constexpr int BM = BM_, W = W_;
+  static constexpr int THREADS = 64 * W, PAIRS = W / 2;
+  static constexpr int NSUB = BM / 16;       // 16-row MFMA sub-tiles
+  static constexpr int A_PIECES = BM * 32;   // 16-byte pieces of one A superblock chunk
+  static constexpr int A_BUF = BM * A_ROW;   // LDS bytes per A buffer
+  static constexpr int SGN = BM == 64 ? 8 : 16;  // IQ2 sign-table copies (the LDS of 64-row tiles)
+  static constexpr int bn(int ks) { return 16 * W / ks; }  // output rows per work item
+};
+using RoutedTile = GemmTile<PREFILL_BM, 16>;
+using SharedTile = GemmTile<PREFILL_SHARED_BM, 8>;
 
 // ---------------------------------------------------------------------------
 // x -> fp16 with a per-token power-of-two scale
@@ -137,14 +152,13 @@ struct GemmArgs {
   int routed;                  // 1: buckets of a routed expert, 0: shared (identity)
   int n_rows;                  // shared: number of rows (T)
   int E, k;
-  const int32_t* counts;       // routed: [E]
   const int32_t* offsets;      // routed: [E+1]
   const int32_t* tile_start;   // routed: [E+1]
   const int32_t* perm;         // routed: [T*k]
   // output
   void* out;                   // gate/up: fp16 H [rows][N]; down: fp32 [rows][N]
-  // power-of-two exponents of H: H[row][c] = fp16(h * 2^-hexp[row][c / 128])
-  int8_t* hexp_out;            // gate/up: written, [rows][N / 128]
+  // power-of-two exponents of H: H[row][c] = fp16(h * 2^-hexp[row][c / PREFILL_HCHUNK])
+  int8_t* hexp_out;            // gate/up: written, [rows][N / PREFILL_HCHUNK]
   const float* row_scale;      // down: 2^e of each A row (H row = fp16(h 2^-e)), [rows]
 };
 
@@ -349,11 +363,12 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 }
 
 // Fragment of local step i (q = 4h + i): 8 exact integers, group i of the
-// lane's sub-block.  SC = iq2_scale_h2 of the sub-block, CB = (lane % 16) << 4.
-template <int KS>
+// lane's sub-block.  SC = iq2_scale_h2 of the sub-block, CB = (lane % 16) << 4,
+// CS = (lane % SGN) << 4.
+template <int SGN, int KS>
 __device__ __forceinline__ uint4 iq2_frag(const BRegs<FMT_IQ2, KS>& b, int hh, int i, uint32_t SC, uint32_t CB,
-                                          const uint8_t* tm, const uint8_t* sgn) {
-  return iq2_frag_words(b.w[2 * hh], b.w[2 * hh + 1], i, SC, CB, tm, sgn);
+                                          uint32_t CS, const uint8_t* tm, const uint8_t* sgn) {
+  return iq2_frag_words<SGN>(b.w[2 * hh], b.w[2 * hh + 1], i, SC, CB, CS, tm, sgn);
 }
 
 // Q2K fragment constants of a sub-block with scale sc: quants placed under
@@ -524,10 +539,11 @@ __device__ __forceinline__ float row16_max(float v) {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int FMT, bool GATEUP, int KS>
+template <int FMT, bool GATEUP, int KS, class G>
 struct GemmLds {
+  static constexpr int BM = G::BM, NSUB = G::NSUB, A_BUF = G::A_BUF, GEMM_PAIRS = G::PAIRS;
   static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
-  static constexpr int kSgn = FMT == FMT_IQ2 ? IQ2_SGN_BYTES : 0;
+  static constexpr int kSgn = FMT == FMT_IQ2 ? iq2_sgn_bytes<G::SGN>() : 0;
   static constexpr int kCb = is_vq(FMT) ? vq_codes(FMT) * 8 : 0;      // VQ codebook (E4M3)
   static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
   static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
@@ -536,8 +552,8 @@ struct GemmLds {
   static constexpr int kMax = GATEUP ? 2 * BM * 4 : 0;                // gate/up: [item parity][BM] row maxima of |h|
   static constexpr int oSgn = kMag, oCb = oSgn + kSgn, oA = oCb + kCb, oS = oA + kA, oTok = oS + kS,
                        oRed = oTok + kTok, oMax = oRed + kRed, oTiles = oMax + kMax;
-  // then tile_start, counts, offsets of the routed experts: [3][E + 1]
-  static constexpr int bytes_for(int E) { return oTiles + 3 * (E + 1) * 4; }
+  // then tile_start and offsets of the routed experts: [2][E + 1]
+  static constexpr int bytes_for(int E) { return oTiles + 2 * (E + 1) * 4; }
 };
 
 // A work item's rows.
@@ -549,10 +565,12 @@ struct Item {
   int nm;      // active 16-row sub-tiles
 };
 
-template <int FMT, bool GATEUP, int PD, int KS>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
-  using L = GemmLds<FMT, GATEUP, KS>;
-  constexpr int BN = gemm_bn(KS);  // output rows per work item
+template <int FMT, bool GATEUP, int PD, int KS, class G>
+__global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
+  using L = GemmLds<FMT, GATEUP, KS, G>;
+  constexpr int BM = G::BM, NSUB = G::NSUB, A_PIECES = G::A_PIECES, A_BUF = G::A_BUF;
+  constexpr int GEMM_THREADS = G::THREADS, GEMM_PAIRS = G::PAIRS;
+  constexpr int BN = G::bn(KS);  // output rows per work item
   extern __shared__ __align__(16) uint8_t lds[];
   const uint8_t* tm = lds;
   const uint8_t* sgn = lds + L::oSgn;
@@ -563,8 +581,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   float* sRed = reinterpret_cast<float*>(lds + L::oRed);
   uint32_t* sMax = reinterpret_cast<uint32_t*>(lds + L::oMax);  // gate/up: [j % 2][BM], fp32 bits of max|h|
   int* sTiles = reinterpret_cast<int*>(lds + L::oTiles);
-  int* sCounts = sTiles + (a.E + 1);
-  int* sOffsets = sCounts + (a.E + 1);
+  int* sOffsets = sTiles + (a.E + 1);  // (an expert's row count: the difference of two offsets)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = KS == 2 ? wave % GEMM_PAIRS : wave;  // output rows 16 wv .. of the N tile
@@ -572,7 +589,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   const int g4 = lane >> 4, c16 = lane & 15;
 
   if constexpr (FMT == FMT_IQ2)
-    build_iq2_tables(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid, GEMM_THREADS);
+    build_iq2_tables<G::SGN>(a.grid, reinterpret_cast<uint4*>(lds), reinterpret_cast<uint4*>(lds + L::oSgn), tid,
+                             GEMM_THREADS);
   if constexpr (is_vq(FMT)) vq_stage_codebook(a.vq_cb, lds + L::oCb, vq_codes(FMT), tid, GEMM_THREADS);
   if constexpr (GATEUP) {
     if (tid < 2 * BM) sMax[tid] = 0u;
@@ -581,7 +599,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     for (int i = tid; i <= a.E; i += GEMM_THREADS) {
       sTiles[i] = a.tile_start[i];
       sOffsets[i] = a.offsets[i];
-      sCounts[i] = i < a.E ? a.counts[i] : 0;
     }
   }
   __syncthreads();
@@ -635,7 +652,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       while (e + 1 < a.E && sTiles[e + 1] <= tt) e++;  // skip experts with no tiles
       const int m0 = (tt - sTiles[e]) * BM;
       it.e = e;
-      it.rows = min(BM, sCounts[e] - m0);
+      it.rows = min(BM, sOffsets[e + 1] - sOffsets[e] - m0);
       it.p0 = sOffsets[e] + m0;
     } else {
       const int m0 = tt * BM;
@@ -676,39 +693,47 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
   };
 
   // ---- A rows: issue (into registers) and store (into LDS) ----
-  // Thread tid holds piece tid: row tid / 32, piece tid % 32, stored at byte
-  // row * A_ROW + 16 * piece.  The row stride of 33 pieces puts the 16 rows an
-  // MFMA operand read touches in 16 different bank quads, and the piece of
-  // k32 step q is an immediate offset.  A loads are raw buffer loads: a piece
-  // outside the item's active rows is given an offset past the end of a16 and
-  // reads as zero, so every step issues the same loads.
-  static_assert(A_PIECES == GEMM_THREADS, "one A piece per thread");
+  // Thread tid holds pieces tid + GEMM_THREADS * i (i < PPT): row
+  // tid / 32 + (GEMM_THREADS / 32) i, piece tid % 32, stored at byte row * A_ROW + 16 * piece.
+  // The row stride of 33 pieces puts the 16 rows an MFMA operand read
+  // touches in 16 different bank quads, and the piece of k32 step q is an
+  // immediate offset.  A loads are raw buffer loads: a piece outside the
+  // item's active rows is given an offset past the end of a16 and reads as
+  // zero, so every step issues the same loads.
+  constexpr int PPT = A_PIECES / GEMM_THREADS;  // A pieces per thread
+  constexpr int RPP = GEMM_THREADS / 32;        // A rows per pass of the block
+  static_assert(A_PIECES == PPT * GEMM_THREADS, "whole pieces per thread");
   // DA superblocks of A in flight in registers (set s % 2 holds superblock s)
   constexpr int DA = PD % 2 == 0 ? 2 : 1;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.a16), (short)0, a.a16_bytes, 0x00020000);
   const int a_row = tid >> 5, a_piece = tid & 31;
-  uint4 av0, av1;              // sets 0 and 1
-  int ap0 = -1, ap1 = -1;      // their LDS byte offset, -1 if inactive
-  auto issue_piece = [&](int j, const Item& it, int sb, uint4& v, int& pos) {
-    const bool active = a_row < 16 * it.nm;
+  uint4 av0[PPT], av1[PPT];  // sets 0 and 1
+  int ap0[PPT], ap1[PPT];    // their LDS byte offsets, -1 if inactive
+#pragma unroll
+  for (int i = 0; i < PPT; i++) ap0[i] = ap1[i] = -1;
+  auto issue_piece = [&](int j, const Item& it, int sb, int row, uint4& v, int& pos) {
+    const bool active = row < 16 * it.nm;
     int src;
     if constexpr (GATEUP) {
-      src = sTok[(j % 3) * BM + a_row];
+      src = sTok[(j % 3) * BM + row];
     } else {
-      src = it.p0 + (a_row < it.rows ? a_row : 0);
+      src = it.p0 + (row < it.rows ? row : 0);
     }
     const int off = active ? (src * a.K + sb * 256 + 8 * a_piece) * 2 : 0x7ffffff0;
     const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0);
     v = make_uint4(w[0], w[1], w[2], w[3]);
-    pos = active ? a_row * A_ROW + 16 * a_piece : -1;
+    pos = active ? row * A_ROW + 16 * a_piece : -1;
   };
   // (a branch on set, not a reference chosen by it: the sets stay in registers)
   auto issueA = [&](int set, int j, const Item& it, int sb) {
-    if (set) issue_piece(j, it, sb, av1, ap1);
-    else issue_piece(j, it, sb, av0, ap0);
+#pragma unroll
+    for (int i = 0; i < PPT; i++) {
+      if (set) issue_piece(j, it, sb, a_row + RPP * i, av1[i], ap1[i]);
+      else issue_piece(j, it, sb, a_row + RPP * i, av0[i], ap0[i]);
+    }
   };
-  auto store_piece = [&](int buf, const uint4& v, int pos) {
+  auto store_piece = [&](int buf, const uint4& v, int pos, int row) {
     uint8_t* dst = sA + buf * A_BUF;
     if (pos >= 0) *reinterpret_cast<uint4*>(dst + pos) = v;
     if constexpr (FMT == FMT_Q2K || FMT == FMT_Q4K) {
@@ -729,14 +754,17 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         const float t = (sum + o) * 0.0625f;
         const uint32_t hs = to_h(t);
         uint16_t* ss = sS + buf * (2 * BM * 16);
-        ss[a_row * 16 + (a_piece >> 1)] = (uint16_t)hs;
-        ss[BM * 16 + a_row * 16 + (a_piece >> 1)] = (uint16_t)to_h(t - from_h(hs));
+        ss[row * 16 + (a_piece >> 1)] = (uint16_t)hs;
+        ss[BM * 16 + row * 16 + (a_piece >> 1)] = (uint16_t)to_h(t - from_h(hs));
       }
     }
   };
   auto storeA = [&](int set, int buf) {
-    if (set) store_piece(buf, av1, ap1);
-    else store_piece(buf, av0, ap0);
+#pragma unroll
+    for (int i = 0; i < PPT; i++) {
+      if (set) store_piece(buf, av1[i], ap1[i], a_row + RPP * i);
+      else store_piece(buf, av0[i], ap0[i], a_row + RPP * i);
+    }
   };
 
   // ---- B rows: PD superblocks in flight ----
@@ -869,7 +897,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       f32x4_t s0[NM], s1[NM];
 #pragma unroll
       for (int m = 0; m < NM; m++) s0[m] = s1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint32_t CB = (uint32_t)c16 << 4;
+      const uint32_t CB = (uint32_t)c16 << 4, CS = (uint32_t)(lane & (G::SGN - 1)) << 4;
 #pragma unroll
       for (int hh = 0; hh < 3 - KS; hh++) {  // halves of the lane's slice (one for KS = 2)
         uint32_t S0 = 0, S1 = 0, sc0 = 0, sc1 = 0;
@@ -896,8 +924,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         for (int i = 0; i < 4; i++) {
           uint4 f0, f1;
           if constexpr (FMT == FMT_IQ2) {
-            f0 = iq2_frag(B0, hh, i, S0, CB, tm, sgn);
-            if constexpr (GATEUP) f1 = iq2_frag(B1, hh, i, S1, CB, tm, sgn);
+            f0 = iq2_frag<G::SGN>(B0, hh, i, S0, CB, CS, tm, sgn);
+            if constexpr (GATEUP) f1 = iq2_frag<G::SGN>(B1, hh, i, S1, CB, CS, tm, sgn);
           } else if constexpr (FMT == FMT_Q4K) {
             f0 = q4k_frag(word_of(B0.q[KS == 2 ? 0 : hh], i), mul0, add0);
             if constexpr (GATEUP) f1 = q4k_frag(word_of(B1.q[KS == 2 ? 0 : hh], i), mul1, add1);
@@ -1035,7 +1063,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       if (h == 0) {
         // wave-uniform bases (scalar registers), 32-bit lane offsets
         _Float16* hout = static_cast<_Float16*>(a.out) + (int64_t)it.p0 * a.N + it.nt * BN;
-        int8_t* eout = a.hexp_out + (int64_t)it.p0 * (a.N / 128) + it.nt * (BN / 128) + wv;
+        constexpr int HC = PREFILL_HCHUNK;
+        static_assert(BN % HC == 0, "whole exponent chunks per N tile");
+        int8_t* eout = a.hexp_out + (int64_t)it.p0 * (a.N / HC) + it.nt * (BN / HC) + wv;
 #pragma unroll
         for (int m = 0; m < NSUB; m++) {
           if (m < it.nm) {
@@ -1054,7 +1084,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
                 }
                 const float hv = hbuf[i * HROW + cl];
                 hout[i * a.N + cl] = (_Float16)(hv * __builtin_amdgcn_ldexpf(1.0f, -e));
-                if (wv < BN / 128 && c16 == 0) eout[i * (a.N / 128)] = (int8_t)e;  // one lane per row and chunk
+                if (wv < BN / HC && c16 == 0) eout[i * (a.N / HC)] = (int8_t)e;  // one lane per row and chunk
               }
             }
           }
@@ -1120,7 +1150,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
       {
         const uint32_t sw0 = u == 0 ? g0n.word(0) : g0c.word(u);
         const uint32_t sw1 = u == 0 ? g1n.word(0) : g1c.word(u);
-        if (cur.nm == 2) compute(std::integral_constant<int, 2>{}, u, s & 1, sw0, sw1);
+        static_assert(NSUB == 2 || NSUB == 4, "sub-tile dispatch");
+        if (NSUB == 4 && cur.nm == 4) compute(std::integral_constant<int, NSUB == 4 ? 4 : 2>{}, u, s & 1, sw0, sw1);
+        else if (NSUB == 4 && cur.nm == 3) compute(std::integral_constant<int, NSUB == 4 ? 3 : 2>{}, u, s & 1, sw0, sw1);
+        else if (cur.nm == 2) compute(std::integral_constant<int, 2>{}, u, s & 1, sw0, sw1);
         else compute(std::integral_constant<int, 1>{}, u, s & 1, sw0, sw1);
         if (u == 0) {  // the group's scales are back (its first codes were waited for)
           g0c = g0n;
@@ -1153,7 +1186,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // row normalisation of H between the two GEMMs
 // ---------------------------------------------------------------------------
-// The gate/up epilogue stores each 128-output chunk c of a row as
+// The gate/up epilogue stores each PREFILL_HCHUNK-output chunk c of a row as
 // fp16(h 2^-e_c).  One wave per row: e = max_c e_c; every chunk with e_c < e
 // is multiplied by 2^(e_c - e) in place (exact but for fp16 subnormals,
 // which lie below 2^-24 of the row's largest |h|), so the row is fp16(h 2^-e)
@@ -1163,21 +1196,24 @@ __global__ __launch_bounds__(256) void hnorm_kernel(uint16_t* __restrict__ H0, c
                                                     float* __restrict__ sc0, int n0, uint16_t* __restrict__ H1,
                                                     const int8_t* __restrict__ e1, float* __restrict__ sc1, int n1,
                                                     int f) {
+  constexpr int HC = PREFILL_HCHUNK;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n0 + n1) return;  // uniform per wave
   const bool first = row < n0;
   const int r = first ? row : row - n0;
   uint16_t* h = (first ? H0 : H1) + (int64_t)r * f;
-  const int nch = f / 128;  // chunks per row (<= 64)
+  const int nch = f / HC;  // chunks per row (<= 128: lane l holds chunks l and l + 64)
   const int8_t* er = (first ? e0 : e1) + (int64_t)r * nch;
-  const int ec = lane < nch ? er[lane] : -128;
-  int e = ec;
+  const int ea = lane < nch ? er[lane] : -128, eb = lane + 64 < nch ? er[lane + 64] : -128;
+  int e = max(ea, eb);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) e = max(e, __shfl_xor(e, o, 64));
-  // 16-byte pieces: piece q of the row covers values 8q .. 8q + 7 (chunk q / 16)
+  // 16-byte pieces: piece q of the row covers values 8q .. 8q + 7 (chunk q / (HC / 8))
   for (int q = lane; q < f / 8; q += 64) {
-    const int d = __shfl(ec, q / 16, 64) - e;
+    const int c = q / (HC / 8);
+    const int ca = __shfl(ea, c & 63, 64), cb = __shfl(eb, c & 63, 64);
+    const int d = (c < 64 ? ca : cb) - e;
     if (d != 0) {
       const _Float16 fac = (_Float16)__builtin_amdgcn_ldexpf(1.0f, d);
       const f16x2_t ff = {fac, fac};
@@ -1233,39 +1269,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int FMT, bool GATEUP, int PD, int KS>
+template <int FMT, bool GATEUP, int PD, int KS, class G>
 static hipError_t run_gemm_pd(const GemmArgs& a, int m_tiles, hipStream_t s) {
-  const int max_items = m_tiles * (a.N / gemm_bn(KS));
+  const int max_items = m_tiles * (a.N / G::bn(KS));
   const char* name = GATEUP ? (a.routed ? "prefill_gateup" : "prefill_shared_gateup")
                             : (a.routed ? "prefill_down" : "prefill_shared_down");
-  using L = GemmLds<FMT, GATEUP, KS>;
-  auto kern = gemm_kernel<FMT, GATEUP, PD, KS>;
+  using L = GemmLds<FMT, GATEUP, KS, G>;
+  static_assert(L::bytes_for(MAX_EXPERTS) <= 160 * 1024, "LDS of one block");
+  auto kern = gemm_kernel<FMT, GATEUP, PD, KS, G>;
   const int bytes = L::bytes_for(a.routed ? a.E : 0);
   int per_cu = 1, n_cus = 256;  // resident blocks per CU at that LDS size, CUs of the device
-  hipError_t e = launch_shape((const void*)kern, GEMM_THREADS, bytes, L::bytes_for(MAX_EXPERTS), &per_cu, &n_cus);
+  hipError_t e = launch_shape((const void*)kern, G::THREADS, bytes, L::bytes_for(MAX_EXPERTS), &per_cu, &n_cus);
   if (e != hipSuccess) return e;
   int grid = per_cu * n_cus;
   grid = (grid / 8) * 8;
   if (max_items < grid) grid = ((max_items + 7) / 8) * 8;
   if (grid < 8) grid = 8;
   const int pid = prof_begin(name, s);
-  QMOE_LAUNCH(kern, dim3(grid), dim3(GEMM_THREADS), bytes, s, a);
+  QMOE_LAUNCH(kern, dim3(grid), dim3(G::THREADS), bytes, s, a);
   prof_end(pid, s);
   return hipGetLastError();
 }
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, class G>
 static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
   const int nsb = a.K / 256;
   if constexpr (is_vq(FMT)) {  // whole superblocks per wave: 12 (13) bytes of indices per lane and matrix
-    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-    return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+    if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
+    return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
   } else if constexpr (FMT == FMT_MX4) {  // whole superblocks per wave: 32 bytes of codes per lane and matrix
     if constexpr (GATEUP) {
-      return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+      return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
     } else {
-      if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-      return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+      if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
+      return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
     }
   } else {
     // 2-bit formats: a wave takes whole superblocks (KS = 1, 16-byte weight
@@ -1273,38 +1310,49 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
     // (16 waves per CU).
     if constexpr (FMT != FMT_Q8) {
       if constexpr (!GATEUP && FMT != FMT_Q4K) {
-        if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1>(a, m_tiles, s);
+        if (nsb % 4 == 0) return run_gemm_pd<FMT, GATEUP, 4, 1, G>(a, m_tiles, s);
       }
       // (two Q2K or Q4K matrices hold more registers per superblock than two
       // IQ2 ones; one Q4K superblock holds twice the quant registers)
       if constexpr (FMT == FMT_Q4K) {
         if constexpr (GATEUP) {  // the two waves of a pair split each superblock (as Q8 gate/up; deeper spills)
-          return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+          return run_gemm_pd<FMT, GATEUP, 1, 2, G>(a, m_tiles, s);
         } else {
-          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-          return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
+          return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
         }
       } else {
         // (gate/up: two superblocks in flight spill once the IQ2 fragments
         // carry their scale multiply; measured 1.62 ms against 1.90 ms with
         // two at 8 x 4096 Zipf tokens)
         if constexpr (!GATEUP) {
-          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
+          if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
         }
-        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+        return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
       }
     } else {
       // Q8: whole superblocks for the one-matrix down GEMM; the two-matrix
       // gate/up keeps the pair split (whole superblocks of two matrices spill)
       if constexpr (!GATEUP) {
-        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1>(a, m_tiles, s);
-        return run_gemm_pd<FMT, GATEUP, 1, 1>(a, m_tiles, s);
+        if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
+        return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
       }
-      // (two superblocks in flight spill: measured 220 us against 152 us with one)
-      return run_gemm_pd<FMT, GATEUP, 1, 2>(a, m_tiles, s);
+      // (two superblocks in flight spill: measured 220 us against 152 us with
+      // one).  With 8-wave blocks (256 VGPRs per wave) whole superblocks of
+      // both matrices fit: 404 against 510 us at 8 x 4096 tokens.
+      if constexpr (G::W == 8) return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
+      return run_gemm_pd<FMT, GATEUP, 1, 2, G>(a, m_tiles, s);
     }
   }
 }
+
+// (the shared expert takes IQ2XXS_L, Q2K_L or Q8_0_L only)
+#define PF_SHARED_FMT_SWITCH(fmt, F, ...)                              \
+  switch (fmt) {                                                       \
+    case FMT_IQ2: { constexpr int F = FMT_IQ2; __VA_ARGS__; } break;   \
+    case FMT_Q2K: { constexpr int F = FMT_Q2K; __VA_ARGS__; } break;   \
+    default: { constexpr int F = FMT_Q8; __VA_ARGS__; } break;         \
+  }
 
 #define PF_FMT_SWITCH(fmt, F, ...)                                     \
   switch (fmt) {                                                       \
@@ -1341,14 +1389,13 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.routed = 1;
     a.E = P.E;
     a.k = P.k;
-    a.counts = P.counts;
     a.offsets = P.offsets;
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.H;
     a.hexp_out = P.Hexp;
-    const int m_tiles = n / BM + P.E;
-    PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true>(a, m_tiles, s)))
+    const int m_tiles = n / RoutedTile::BM + P.E;
+    PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true, RoutedTile>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   if (P.has_shared) {
@@ -1368,8 +1415,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.k = 1;
     a.out = P.Hs;
     a.hexp_out = P.Hsexp;
-    const int m_tiles = (P.T + BM - 1) / BM;
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true>(a, m_tiles, s)))
+    const int m_tiles = (P.T + SharedTile::BM - 1) / SharedTile::BM;
+    PF_SHARED_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, true, SharedTile>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   // every row of H and Hs to one exponent (the down GEMMs scale their outputs by it)
@@ -1394,14 +1441,13 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     a.routed = 1;
     a.E = P.E;
     a.k = P.k;
-    a.counts = P.counts;
     a.offsets = P.offsets;
     a.tile_start = P.tile_start;
     a.perm = P.perm;
     a.out = P.Ye;
     a.row_scale = P.Hsc;
-    const int m_tiles = n / BM + P.E;
-    PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false>(a, m_tiles, s)))
+    const int m_tiles = n / RoutedTile::BM + P.E;
+    PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false, RoutedTile>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
   if (P.has_shared) {
@@ -1419,8 +1465,8 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     b.k = 1;
     b.out = P.Ysh;
     b.row_scale = P.Hssc;
-    const int m_tiles2 = (P.T + BM - 1) / BM;
-    PF_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false>(b, m_tiles2, s)))
+    const int m_tiles2 = (P.T + SharedTile::BM - 1) / SharedTile::BM;
+    PF_SHARED_FMT_SWITCH(P.fmt_shared, F, err = (run_gemm<F, false, SharedTile>(b, m_tiles2, s)))
     if (err != hipSuccess) return err;
   }
   const int pid = prof_begin("prefill_combine", s);

@@ -25,7 +25,7 @@ MOE_LAYOUT_CANONICAL, MOE_LAYOUT_DEVICE = 0, 1
 MOE_OP_ROUTE, MOE_OP_DECODE, MOE_OP_PREFILL, MOE_OP_LAYER = 0, 1, 2, 3
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_DECODE_MAX_T = 8
-MOE_AUTO_DECODE_MAX_T = 8
+MOE_AUTO_DECODE_MAX_T = 24
 MOE_REPACK_TO_DEVICE, MOE_REPACK_TO_CANONICAL = 0, 1
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 

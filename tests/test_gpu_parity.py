@@ -153,6 +153,31 @@ def test_layer_formats_and_shapes(case):
         assert rel_l2(y, y_ref) <= REL_L2, (path, rel_l2(y, y_ref))
 
 
+@pytest.mark.parametrize("T,dt,fgu,fdn", [(13, synth.BF16, synth.FMT_IQ2, synth.FMT_Q2K),
+                                          (24, synth.F32, synth.FMT_IQ2, synth.FMT_Q2K),
+                                          (11, synth.F32, synth.FMT_VQ12, synth.FMT_VQ12)])
+def test_auto_path_runs_decode_in_chunks_above_the_call_limit(T, dt, fgu, fdn):
+    """MOE_PATH_AUTO takes the decode path up to MOE_AUTO_DECODE_MAX_T tokens,
+    above the decode path's per-call limit, as consecutive calls of at most
+    MOE_DECODE_MAX_T tokens: bitwise the explicit decode-path calls on those
+    chunks, and within the parity bar of the oracle."""
+    assert lib.MOE_DECODE_MAX_T < T <= lib.MOE_AUTO_DECODE_MAX_T
+    spec = synth.scaled_spec(E=40, k=4, d=512, f=1024, fmt_gate_up=fgu, fmt_down=fdn)
+    L = synth.random_layer(spec, seed=61, workload="auto_chunks")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(61, ("auto_chunks", T), T, spec.d, dt)
+    y, idx, wt = run_layer(dl, x, dt, lib.MOE_PATH_AUTO)
+    y_ref, idx_ref, wt_ref = oracle.layer_forward(L, x, dt)
+    assert np.array_equal(idx, idx_ref)
+    assert np.max(np.abs(wt - wt_ref)) <= WT_TOL
+    assert rel_l2(y, y_ref) <= REL_L2, rel_l2(y, y_ref)
+    step = lib.MOE_DECODE_MAX_T
+    for a in range(0, T, step):
+        yc, ic, wc = run_layer(dl, x[a:a + step], dt, lib.MOE_PATH_DECODE)
+        assert np.array_equal(yc, y[a:a + step]), a
+        assert np.array_equal(ic, idx[a:a + step]) and np.array_equal(wc, wt[a:a + step]), a
+
+
 @pytest.mark.parametrize("fgu", [synth.FMT_Q2K, synth.FMT_Q4K])
 def test_prefill_min_term_with_same_sign_rows(fgu):
     """K-quant gate/up in prefill on rows of one sign and similar magnitude:
