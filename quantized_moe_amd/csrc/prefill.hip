@@ -29,9 +29,9 @@
 // blocks (128 VGPRs per wave), the shared GEMMs 64-row tiles in 8-wave blocks
 // (256 VGPRs).  Each wave takes whole superblocks (KS = 1, N tile 16 per
 // wave): a lane's weights of a superblock are one 16-byte load for the 2-bit
-// formats.  Only two-matrix gate/up GEMMs that would spill (Q8 and Q4K in
-// 16-wave blocks) have the two waves of a pair split every superblock's
-// inputs (KS = 2), their partial sums meeting in LDS once per item.
+// formats.  Only the two-matrix Q8 gate/up in 16-wave blocks, which would
+// spill, has the two waves of a pair split every superblock's inputs
+// (KS = 2), their partial sums meeting in LDS once per item.
 // The K loop runs over 256-input superblocks and is software-pipelined across
 // work items: every wave keeps its weight loads PD superblocks ahead in
 // registers, the A rows of the next superblock are loaded while the current
@@ -792,6 +792,16 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
   f32x4_t acc0[NSUB], acc1[NSUB];
 #pragma unroll
   for (int m = 0; m < NSUB; m++) acc0[m] = acc1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // K-quant gate/up GEMMs (two matrices of Q2K or Q4K) keep no per-superblock
+  // partial sums, whose registers spilled: acc holds the item's sums in units
+  // of the scale D of the last superblock with d != 0 (the lane's output row:
+  // the sums are acc * D).  A superblock with d != 0 first multiplies acc by
+  // D / d and sets D = d, and its exact-integer fragments then accumulate
+  // straight into acc, its min term scaled by dmin / D; one with d = 0
+  // zeroes its fragments' scales and leaves D.  |D / d| <= 2^40 for fp16
+  // scales, so no sum leaves the fp32 range; each ratio is one rounding.
+  // (Every other GEMM keeps D = 1.)
+  float D0 = 1.0f, D1 = 1.0f;
 
   // VQ: the fp16 row gains of this lane's output column (gate and up, or
   // down) for the current item, requested as the item becomes current (a
@@ -892,6 +902,91 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
       for (int m = 0; m < NM; m++) {
         acc0[m] += ps0 * s0[m];
         if constexpr (GATEUP) acc1[m] += ps1 * s1[m];
+      }
+    } else if constexpr ((FMT == FMT_Q2K || FMT == FMT_Q4K) && GATEUP) {
+      // the running scale: acc in units of D (d, and for the min term dmin,
+      // from the superblock's scale word)
+      const uint32_t db0 = sw0 & 0xffffu, db1 = GATEUP ? sw1 & 0xffffu : 0u;
+      const bool z0 = (db0 & 0x7fffu) == 0u, z1 = (db1 & 0x7fffu) == 0u;
+      auto rescale = [&](f32x4_t* acc, float& D, uint32_t db, bool z) {
+        if (!z) {
+          const float dv = from_h(db);
+          const float r = D * __builtin_amdgcn_rcpf(dv);
+          D = dv;
+#pragma unroll
+          for (int m = 0; m < NM; m++) acc[m] *= r;
+        }
+      };
+      rescale(acc0, D0, db0, z0);
+      if constexpr (GATEUP) rescale(acc1, D1, db1, z1);
+#pragma unroll
+      for (int hh = 0; hh < 3 - KS; hh++) {
+        uint32_t sc0 = 0, sc1 = 0;
+        f16x2_t mul0 = {}, add0 = {}, mul1 = {}, add1 = {};
+        Q2kConst kq0 = {}, kq1 = {};
+        if constexpr (FMT == FMT_Q4K) {
+          const int sbl = KS == 2 ? h : hh;
+          auto consts = [&](uint32_t sc, f16x2_t& mul, f16x2_t& add) {
+            const float f = (float)sc;
+            mul = f16x2_t{(_Float16)f, (_Float16)(f * 0.0625f)};
+            add = f16x2_t{(_Float16)(-1024.0f * f), (_Float16)(-64.0f * f)};
+          };
+          consts(z0 ? 0u : q4k_sc(B0, sbl), mul0, add0);
+          if constexpr (GATEUP) consts(z1 ? 0u : q4k_sc(B1, sbl), mul1, add1);
+        } else {
+          const int hs = KS == 2 ? h : hh;
+          sc0 = z0 ? 0u : B0.sc >> (16 * hs);
+          if constexpr (GATEUP) sc1 = z1 ? 0u : B1.sc >> (16 * hs);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          uint4 f0, f1;
+          if constexpr (FMT == FMT_Q4K) {
+            f0 = q4k_frag(word_of(B0.q[KS == 2 ? 0 : hh], i), mul0, add0);
+            if constexpr (GATEUP) f1 = q4k_frag(word_of(B1.q[KS == 2 ? 0 : hh], i), mul1, add1);
+          } else {
+            if (i % 2 == 0) {
+              kq0 = q2k_const((sc0 >> (8 * (i >> 1))) & 15u);
+              if constexpr (GATEUP) kq1 = q2k_const((sc1 >> (8 * (i >> 1))) & 15u);
+            }
+            f0 = q2k_frag(B0, hh, i, kq0);
+            if constexpr (GATEUP) f1 = q2k_frag(B1, hh, i, kq1);
+          }
+#pragma unroll
+          for (int m = 0; m < NM; m++) {
+            const uint4 av = aread(m, 4 * hh + i);
+            acc0[m] = mfma32(av, f0, acc0[m]);
+            if constexpr (GATEUP) acc1[m] = mfma32(av, f1, acc1[m]);
+          }
+          if (i == 1 || i == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (h == 0) {
+        const float dm0 = from_h(sw0 >> 16) * __builtin_amdgcn_rcpf(D0);
+        float dm1 = 0.0f;
+        if constexpr (GATEUP) dm1 = from_h(sw1 >> 16) * __builtin_amdgcn_rcpf(D1);
+        uint2 mf0, mf1;
+        if constexpr (FMT == FMT_Q4K) {
+          mf0 = q4k_min_frag(B0);
+          if constexpr (GATEUP) mf1 = q4k_min_frag(B1);
+        } else {
+          mf0 = q2k_min_frag(B0);
+          if constexpr (GATEUP) mf1 = q2k_min_frag(B1);
+        }
+        const uint16_t* ss = sS + buf * (2 * BM * 16);
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          const uint2 shi = *reinterpret_cast<const uint2*>(ss + (m * 16 + c16) * 16 + 4 * g4);
+          const uint2 slo = *reinterpret_cast<const uint2*>(ss + BM * 16 + (m * 16 + c16) * 16 + 4 * g4);
+          f32x4_t mm = mfma16(shi, mf0, f32x4_t{0.f, 0.f, 0.f, 0.f});
+          mm = mfma16(slo, mf0, mm);
+          acc0[m] -= dm0 * mm;
+          if constexpr (GATEUP) {
+            f32x4_t m1 = mfma16(shi, mf1, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            m1 = mfma16(slo, mf1, m1);
+            acc1[m] -= dm1 * m1;
+          }
+        }
       }
     } else {
       f32x4_t s0[NM], s1[NM];
@@ -1047,8 +1142,8 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
             const int i = m * 16 + 4 * g4 + r;
             float hv = 0.0f;
             if (m < it.nm && i < it.rows) {
-              const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
-              const float v1 = KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r];
+              const float v0 = (KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r]) * D0;
+              const float v1 = (KS == 2 ? acc1[m][r] + red1[o] : acc1[m][r]) * D1;
               const float xs = sXs[(j % 3) * BM + i];
               hv = is_vq(FMT) ? silu(v0 * xs * vg0) * (v1 * xs * vg1) : silu(v0 * xs) * (v1 * xs);
             }
@@ -1099,7 +1194,7 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
           for (int r = 0; r < 4; r++) {
             const int o = ((m * 4 + r) * GEMM_PAIRS + wv) * 64 + lane;
             const int i = m * 16 + 4 * g4 + r;
-            const float v0 = KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r];
+            const float v0 = (KS == 2 ? acc0[m][r] + sRed[o] : acc0[m][r]) * D0;
             const float v = is_vq(FMT) ? v0 * sXs[(j % 3) * BM + i] * vg0 : v0 * sXs[(j % 3) * BM + i];
             if (i < it.rows) static_cast<float*>(a.out)[(int64_t)it.p0 * a.N + (i * a.N + n)] = v;
           }
@@ -1108,6 +1203,7 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < NSUB; m++) acc0[m] = acc1[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    D0 = D1 = 1.0f;
   };
 
   // ---- prologue ----
@@ -1315,8 +1411,8 @@ static hipError_t run_gemm(const GemmArgs& a, int m_tiles, hipStream_t s) {
       // (two Q2K or Q4K matrices hold more registers per superblock than two
       // IQ2 ones; one Q4K superblock holds twice the quant registers)
       if constexpr (FMT == FMT_Q4K) {
-        if constexpr (GATEUP) {  // the two waves of a pair split each superblock (as Q8 gate/up; deeper spills)
-          return run_gemm_pd<FMT, GATEUP, 1, 2, G>(a, m_tiles, s);
+        if constexpr (GATEUP) {  // whole superblocks of both matrices (spill-free with the running scale)
+          return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
         } else {
           if (nsb % 2 == 0) return run_gemm_pd<FMT, GATEUP, 2, 1, G>(a, m_tiles, s);
           return run_gemm_pd<FMT, GATEUP, 1, 1, G>(a, m_tiles, s);
