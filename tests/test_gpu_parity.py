@@ -132,6 +132,10 @@ FORMAT_CASES = [
     (8, 1, 8192, 256, synth.FMT_VQ13, synth.FMT_VQ13, None, 2, synth.F32),          # two pieces per lane (d)
     (9, 2, 256, 256, synth.FMT_VQ12, synth.FMT_VQ12, synth.FMT_Q8, 40, synth.F32),
     (1000, 5, 256, 256, synth.FMT_VQ13, synth.FMT_VQ13, synth.FMT_Q8, 7, synth.F32),  # many experts
+    # the shared expert's 64-row M tiles, several of them with a ragged last one
+    (16, 4, 512, 512, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_IQ2, 100, synth.BF16),
+    (16, 4, 512, 512, synth.FMT_Q4K, synth.FMT_Q4K, synth.FMT_Q2K, 130, synth.F32),
+    (16, 4, 512, 512, synth.FMT_Q2K, synth.FMT_Q2K, synth.FMT_Q8, 193, synth.F32),
 ]
 
 
@@ -176,6 +180,46 @@ def test_auto_path_runs_decode_in_chunks_above_the_call_limit(T, dt, fgu, fdn):
         yc, ic, wc = run_layer(dl, x[a:a + step], dt, lib.MOE_PATH_DECODE)
         assert np.array_equal(yc, y[a:a + step]), a
         assert np.array_equal(ic, idx[a:a + step]) and np.array_equal(wc, wt[a:a + step]), a
+
+
+@pytest.mark.parametrize("fgu", [synth.FMT_Q2K, synth.FMT_Q4K])
+def test_kquant_rows_with_zero_and_far_superblock_scales(fgu):
+    """K-quant matrices whose superblock scales vary along a row: d = 0 with
+    dmin != 0 (only the min term remains), d = dmin = 0, and d moved 2^12 up
+    or down (fp16 subnormal), on both paths.  The prefill gate/up keeps its
+    sums in units of the last nonzero d and rescales at every change."""
+    spec = synth.scaled_spec(E=8, k=2, d=1024, f=512, fmt_gate_up=fgu, fmt_down=fgu)
+    L = synth.random_layer(spec, seed=12, workload="kquant_scales")
+    bb = synth.BLOCK_BYTES[fgu]
+
+    def edit(w, rows, nb):
+        blk = w.reshape(-1, bb)                      # [expert * rows * nb] blocks
+        d = blk[:, 0:2].copy().view("<f2").reshape(-1).astype(np.float32)
+        dm = blk[:, 2:4].copy().view("<f2").reshape(-1).astype(np.float32)
+        b = np.arange(blk.shape[0])
+        row, j = b // nb, b % nb
+        d[(j == 1) & (row % 2 == 0)] = 0.0           # min term alone
+        z = (j == 2) & (row % 3 == 0)
+        d[z] = 0.0                                    # an all-zero superblock
+        dm[z] = 0.0
+        d[(j == 3) & (row % 5 == 0)] *= 4096.0
+        d[(j == 0) & (row % 7 == 0)] /= 4096.0        # fp16 subnormal
+        blk[:, 0:2] = d.astype("<f2").view(np.uint8).reshape(-1, 2)
+        blk[:, 2:4] = dm.astype("<f2").view(np.uint8).reshape(-1, 2)
+
+    edit(L.w_gate, spec.f, spec.d // 256)
+    edit(L.w_up, spec.f, spec.d // 256)
+    edit(L.w_down, spec.d, spec.f // 256)
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    for T, dt in [(3, synth.F32), (40, synth.BF16)]:
+        x = synth.activations(12, ("kquant_scales", T), T, spec.d, dt)
+        y_ref, idx_ref, _ = oracle.layer_forward(L, x, dt)
+        paths = [lib.MOE_PATH_PREFILL] + ([lib.MOE_PATH_DECODE] if T <= lib.MOE_DECODE_MAX_T else [])
+        for path in paths:
+            y, idx, _ = run_layer(dl, x, dt, path)
+            assert np.array_equal(idx, idx_ref), (T, path)
+            err = per_token_rel_l2(y, y_ref)
+            assert err.max() <= REL_L2, (T, path, err.max())
 
 
 @pytest.mark.parametrize("fgu", [synth.FMT_Q2K, synth.FMT_Q4K])
@@ -315,7 +359,8 @@ def test_route_topk_more_than_512_experts(T, k, E, dt):
 
 
 @pytest.mark.parametrize("T,k,E", [(1, 6, 384), (3, 2, 8), (1024, 6, 384), (4096, 6, 384), (50, 16, 17),
-                                   (64, 16, 1000), (300, 6, 520), (2, 16, 1024)])
+                                   (64, 16, 1000), (300, 6, 520), (2, 16, 1024),
+                                   (20000, 8, 64)])  # the most chunks (1024) of 157 routes
 def test_bucket_bit_exact(T, k, E):
     rng = np.random.default_rng(T + k + E)
     if T == 4096:
