@@ -49,7 +49,15 @@
 
 namespace qmoe {
 
-constexpr int A_ROW = 33 * 16;  // LDS bytes per A row (32 pieces + one of padding)
+// A rows in LDS (one superblock of fp16 inputs, 32 pieces of 16 bytes) in
+// one of two layouts.  Swizzled, for the one-matrix down GEMMs: no padding,
+// piece p of row r at slot p ^ (r % 8); an MFMA operand read (16 rows at one
+// piece, four lane groups 8 pieces apart) meets no bank twice (measured 7.2
+// LDS clocks per 1 KB wave read, against 9.0 with a 33-piece row stride and
+// 7.5 for consecutive addresses), for one XOR per read step.  Padded, for
+// the two-matrix gate/up GEMMs, which are bound by vector instructions and
+// were slower with that XOR: 33-piece rows, every read an immediate offset.
+__host__ __device__ constexpr int a_row_bytes(bool swizzled) { return swizzled ? 32 * 16 : 33 * 16; }
 
 // Work-item shape: BM rows of A (one expert's bucket, or the shared
 // expert's rows) by 16 output rows per wave of a W-wave block, the two waves
@@ -66,7 +74,6 @@ struct GemmTile {
   static constexpr int THREADS = 64 * W, PAIRS = W / 2;
   static constexpr int NSUB = BM / 16;       // 16-row MFMA sub-tiles
   static constexpr int A_PIECES = BM * 32;   // 16-byte pieces of one A superblock chunk
-  static constexpr int A_BUF = BM * A_ROW;   // LDS bytes per A buffer
   static constexpr int SGN = BM == 64 ? 8 : 16;  // IQ2 sign-table copies (the LDS of 64-row tiles)
   static constexpr int bn(int ks) { return 16 * W / ks; }  // output rows per work item
 };
@@ -541,11 +548,18 @@ __device__ __forceinline__ float row16_max(float v) {
 // ---------------------------------------------------------------------------
 template <int FMT, bool GATEUP, int KS, class G>
 struct GemmLds {
-  static constexpr int BM = G::BM, NSUB = G::NSUB, A_BUF = G::A_BUF, GEMM_PAIRS = G::PAIRS;
+  static constexpr int BM = G::BM, NSUB = G::NSUB, GEMM_PAIRS = G::PAIRS;
+  static constexpr bool SWZ = !GATEUP;          // A rows swizzled (one-matrix GEMMs) or padded
+  static constexpr int A_ROW = a_row_bytes(SWZ);
+  static constexpr int A_BUF = BM * A_ROW;      // LDS bytes per A buffer
   static constexpr int kMag = FMT == FMT_IQ2 ? IQ2_TM_BYTES : 0;
   static constexpr int kSgn = FMT == FMT_IQ2 ? iq2_sgn_bytes<G::SGN>() : 0;
   static constexpr int kCb = is_vq(FMT) ? vq_codes(FMT) * 8 : 0;      // VQ codebook (E4M3)
-  static constexpr int kA = 2 * A_BUF;                                 // double-buffered A superblock chunk
+  // double-buffered A superblock chunk; the gate/up epilogue's h tile
+  // (BM x (BN + 4) floats) overlays both buffers (KS = 1) or follows them
+  // (KS = 2, whose epilogue holds partial sums in one of them)
+  static constexpr int kHt = GATEUP ? BM * (G::bn(KS) + 4) * 4 : 0;
+  static constexpr int kA = KS == 1 ? (2 * A_BUF > kHt ? 2 * A_BUF : kHt) : 2 * A_BUF + kHt;
   static constexpr int kS = FMT == FMT_Q2K || FMT == FMT_Q4K ? 2 * 2 * BM * 16 * 2 : 0;  // sums of 16 inputs: [buf][hi/lo][BM][16]
   static constexpr int kTok = 3 * BM * 8;                             // token (gate/up) and scale of each row, 3 items
   static constexpr int kRed = KS == 2 ? NSUB * 4 * GEMM_PAIRS * 64 * 4 : 0;  // one matrix's partial sums of the second halves
@@ -568,7 +582,9 @@ struct Item {
 template <int FMT, bool GATEUP, int PD, int KS, class G>
 __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
   using L = GemmLds<FMT, GATEUP, KS, G>;
-  constexpr int BM = G::BM, NSUB = G::NSUB, A_PIECES = G::A_PIECES, A_BUF = G::A_BUF;
+  constexpr int BM = G::BM, NSUB = G::NSUB, A_PIECES = G::A_PIECES;
+  constexpr bool SWZ = L::SWZ;
+  constexpr int A_ROW = L::A_ROW, A_BUF = L::A_BUF;
   constexpr int GEMM_THREADS = G::THREADS, GEMM_PAIRS = G::PAIRS;
   constexpr int BN = G::bn(KS);  // output rows per work item
   extern __shared__ __align__(16) uint8_t lds[];
@@ -694,10 +710,10 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
 
   // ---- A rows: issue (into registers) and store (into LDS) ----
   // Thread tid holds pieces tid + GEMM_THREADS * i (i < PPT): row
-  // tid / 32 + (GEMM_THREADS / 32) i, piece tid % 32, stored at byte row * A_ROW + 16 * piece.
-  // The row stride of 33 pieces puts the 16 rows an MFMA operand read
-  // touches in 16 different bank quads, and the piece of k32 step q is an
-  // immediate offset.  A loads are raw buffer loads: a piece outside the
+  // tid / 32 + (GEMM_THREADS / 32) i, piece tid % 32, stored at byte
+  // row * A_ROW + 16 * (piece ^ row % 8) (swizzled) or + 16 * piece.
+  // The swizzle or the padding spreads the 16 rows an MFMA operand read
+  // touches over the banks.  A loads are raw buffer loads: a piece outside the
   // item's active rows is given an offset past the end of a16 and reads as
   // zero, so every step issues the same loads.
   constexpr int PPT = A_PIECES / GEMM_THREADS;  // A pieces per thread
@@ -723,7 +739,7 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
     const int off = active ? (src * a.K + sb * 256 + 8 * a_piece) * 2 : 0x7ffffff0;
     const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, off, 0, 0);
     v = make_uint4(w[0], w[1], w[2], w[3]);
-    pos = active ? row * A_ROW + 16 * a_piece : -1;
+    pos = active ? row * A_ROW + 16 * (SWZ ? a_piece ^ (row & 7) : a_piece) : -1;
   };
   // (a branch on set, not a reference chosen by it: the sets stay in registers)
   auto issueA = [&](int set, int j, const Item& it, int sb) {
@@ -822,9 +838,13 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
     constexpr int NM = decltype(nm_c)::value;
     const BRegs<FMT, KS>& B0 = b0[slot];
     const BRegs<FMT, KS>& B1 = b1[slot];
-    const uint8_t* A = sA + buf * A_BUF + c16 * A_ROW + g4 * 128 + h * 64;
+    // piece 8 g4 + j (j = 4 h + i) of row 16 m + c16: slot 8 g4 + j, or
+    // 8 g4 + (j ^ c16 % 8) swizzled
+    const int abase = SWZ ? (buf * A_BUF + c16 * A_ROW + g4 * 128) | (((c16 & 7) ^ (4 * h)) << 4)
+                          : buf * A_BUF + c16 * A_ROW + g4 * 128 + h * 64;
     auto aread = [&](int m, int i) {
-      return *reinterpret_cast<const uint4*>(A + m * 16 * A_ROW + 16 * i);
+      const int off = SWZ ? abase ^ (i << 4) : abase + 16 * i;
+      return *reinterpret_cast<const uint4*>(sA + off + m * 16 * A_ROW);
     };
     if constexpr (is_vq(FMT)) {
       // B fragment of step q = the codeword of the lane's index q, converted
@@ -1130,8 +1150,8 @@ __global__ __launch_bounds__(G::THREADS) void gemm_kernel(GemmArgs a) {
       // h is stored as fp16(h 2^-e).  (h goes through LDS rather than
       // registers so that nothing is held across the barrier.)
       constexpr int HROW = BN + 4;  // floats per row of the h tile (padded: the 4 row groups meet other banks)
-      static_assert(BM * HROW * 4 <= (KS == 1 ? 2 : 1) * A_BUF, "the h tile fits the free A buffers");
-      float* hbuf = reinterpret_cast<float*>(sA + (KS == 1 ? 0 : (freebuf ^ 1) * A_BUF));
+      static_assert(BM * HROW * 4 == L::kHt, "the h tile's LDS");
+      float* hbuf = reinterpret_cast<float*>(sA + (KS == 1 ? 0 : 2 * A_BUF));
       uint32_t* rmax = sMax + (j & 1) * BM;
       if (h == 0) {
 #pragma unroll
