@@ -43,11 +43,12 @@ def _check(dl, x, path):
 
 
 def test_noalloc_full_size_decode_two_calls():
-    """The 384-expert, top-6, d=4096, f=2048 layer: T = 8 then T = 1."""
+    """The 384-expert, top-6, d=4096, f=2048 layer: T = 24 (the automatic
+    path's decode in three chunks of 8), then T = 8, then T = 1."""
     L = synth.random_layer(synth.DECODE_SPEC, seed=0, workload="decode")
     dl = lib.DeviceLayer.from_synth(L, DEV)
     try:
-        for T in (8, 1):
+        for T in (24, 8, 1):
             x = _x(synth.activations(7, ("noalloc", "decode", T), T, 4096, synth.F32), synth.F32)
             _check(dl, x, lib.MOE_PATH_AUTO)
     finally:
