@@ -325,6 +325,7 @@ struct DecodeWs {
 };
 struct PrefillWs {
   int32_t *counts, *offsets, *tile_start, *perm, *pos;
+  int32_t* bucket_hist;  // the bucketing's chunk histograms
   uint16_t* x16;
   float *xs, *route_xs;
   void *H, *Hs;
@@ -350,6 +351,7 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   }
   w.tile_start = (int32_t*)c.take((size_t)(E + 1) * 4);
   w.pos = (int32_t*)c.take(n * 4);
+  w.bucket_hist = (int32_t*)c.take(bucket_scratch_ints((int)n, E) * 4);
   w.x16 = (uint16_t*)c.take((size_t)T * d * 2);
   w.xs = (float*)c.take((size_t)T * 4);
   w.route_xs = (float*)c.take(n * 4);
@@ -598,9 +600,7 @@ extern "C" int moe_bucket(const int32_t* idx, int32_t T, int32_t k, int32_t E, i
   NEED_PTR(perm, "perm");
   NEED_PTR(pos, "pos");
   hipStream_t s = (hipStream_t)stream;
-  const int pid = prof_begin("bucket", s);
-  hipError_t e = launch_bucket(idx, T, k, E, counts, offsets, perm, pos, nullptr, 1, s);
-  prof_end(pid, s);
+  hipError_t e = launch_bucket(idx, T, k, E, counts, offsets, perm, pos, nullptr, 1, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
@@ -689,9 +689,7 @@ static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_
   P.Ysh = w.Ysh;
   P.y = y;
   const int tile_m = PREFILL_BM;
-  int pid = prof_begin("bucket", s);
-  hipError_t e = launch_bucket(idx, T, k, E, w.counts, w.offsets, w.perm, w.pos, w.tile_start, tile_m, s);
-  prof_end(pid, s);
+  hipError_t e = launch_bucket(idx, T, k, E, w.counts, w.offsets, w.perm, w.pos, w.tile_start, tile_m, w.bucket_hist, s);
   if (e != hipSuccess) return hip_fail(e, fn);
   e = launch_prefill_gemms(P, s);
   if (e != hipSuccess) return hip_fail(e, fn);

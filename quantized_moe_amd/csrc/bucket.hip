@@ -4,23 +4,23 @@
 // V4.1 Flash on one DGX Spark", section 4.4: the verify batch reads each
 // chosen expert's bits once for all of its rows).
 //
-// Four small launches, each reading the routes once (O(T k + C E) work for
-// C chunks of consecutive routes):
+// Small launches, each reading the routes once (O(T k + C E) work for C
+// chunks of consecutive routes):
 //   1. per chunk, the histogram of its keys (LDS integer counts: the order
-//      of the increments cannot change them), stored in `pos`, which is
-//      free until the last launch (C E <= T k by the choice of C; a single
-//      chunk writes `counts` directly);
+//      of the increments cannot change them), stored in a scratch array of
+//      C E counts: the caller's (the prefill workspace), or else `pos`,
+//      which is free until the last launch (then C E <= T k by the choice
+//      of C; a single chunk writes `counts` directly);
 //   2. one block: counts[e] (sum over chunks), each chunk's count of key e
 //      turned into the number of earlier routes with key e, offsets and the
 //      M-tile starts;
-//   3. one wave per chunk walks its routes in order, 64 at a time: lanes
-//      with equal keys are grouped by ballots, each lane's rank in its group
-//      is the number of lower lanes in it, and one lane per group claims the
-//      group's places from the chunk's running count of that key in LDS
-//      (distinct keys per claim, batches in route order: stable);
-//   4. pos = the inverse of perm (and n for an out-of-range key, which has
-//      no place).
-// No global atomics, no host round trip.
+//   3. one block per chunk: a route's place is its key's offset, plus the
+//      routes with that key in earlier chunks, plus those earlier in the
+//      chunk (counted from the chunk's keys in LDS): stable, no atomics;
+//      with a scratch array it also writes pos;
+//   4. (histograms in pos) pos = the inverse of perm.
+// An out-of-range key has no place (pos = n marks it).  No global atomics,
+// no host round trip.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,6 +41,7 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(const int32_t* __restr
   for (int i = lane; i < E; i += 64) hist[i] = 0;
   __syncthreads();
   const int r0 = c * ch, r1 = min(n, r0 + ch);
+#pragma unroll 8
   for (int r = r0 + lane; r < r1; r += 64) {
     const int key = idx[r];
     if ((unsigned)key < (unsigned)E) atomicAdd(&hist[key], 1);
@@ -100,40 +101,39 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int n, int E, int C, 
   }
 }
 
-// One wave per chunk.
-__global__ __launch_bounds__(64) void bucket_place_kernel(const int32_t* __restrict__ idx, int n, int E, int ch, int C,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ hist, int32_t* __restrict__ perm) {
-  __shared__ int next[MAX_EXPERTS];  // next place of key e in this chunk
-  const int c = blockIdx.x, lane = threadIdx.x;
-  for (int i = lane; i < E; i += 64) next[i] = offsets[i] + (C == 1 ? 0 : hist[(int64_t)c * E + i]);
+// One block per chunk (ch <= PLACE_MAX_CH routes); pos_out (nullable)
+// receives pos directly.  A route's place is the chunk's base for its key
+// plus its rank: the number of earlier routes of the chunk with that key,
+// counted from the chunk's keys in LDS (every lane of a wave reads the same
+// word at a step: no bank conflicts).
+constexpr int PLACE_MAX_CH = 2048;
+__global__ __launch_bounds__(256) void bucket_place_kernel(const int32_t* __restrict__ idx, int n, int E, int ch, int C,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ hist, int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ pos_out) {
+  __shared__ __align__(16) int skey[PLACE_MAX_CH + 4];
+  __shared__ int base[MAX_EXPERTS];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const int r0 = c * ch, len = min(n, r0 + ch) - r0;
+  for (int i = tid; i < E; i += 256) base[i] = offsets[i] + (C == 1 ? 0 : hist[(int64_t)c * E + i]);
+  for (int i = tid; i < len; i += 256) skey[i] = idx[r0 + i];
+  if (tid < 4) skey[len + tid] = -1;  // (a whole last quad)
   __syncthreads();
-  const unsigned long long below = (1ull << lane) - 1ull;
-  const int r0 = c * ch, r1 = min(n, r0 + ch);
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const int key = r < r1 ? idx[r] : -1;
-    const bool ok = (unsigned)key < (unsigned)E;
-    // group the lanes by key: one ballot per distinct key of the batch
-    unsigned long long todo = __ballot(ok);
-    int rank = 0, leader = 0, gsize = 0;
-    while (todo) {
-      const int l = __builtin_ctzll(todo);
-      const int kl = __builtin_amdgcn_readlane(key, l);
-      const unsigned long long m = __ballot(ok && key == kl);
-      if (ok && key == kl) {
-        rank = __popcll(m & below);
-        leader = l;
-        gsize = __popcll(m);
-      }
-      todo &= ~m;
+  for (int t = tid; t < len; t += 256) {
+    const int key = skey[t];
+    if ((unsigned)key >= (unsigned)E) {
+      if (pos_out) pos_out[r0 + t] = n;
+      continue;
     }
-    // each group's lowest lane claims its places (distinct keys: no two
-    // lanes of the wave touch one counter)
-    int first = 0;
-    if (ok && rank == 0) first = atomicAdd(&next[key], gsize);
-    first = __shfl(first, leader, 64);
-    if (ok) perm[first + rank] = r;
+    int rank = 0;
+    for (int i = 0; i < (t & ~3); i += 4) {  // whole quads before t, then the rest
+      const int4 q = *reinterpret_cast<const int4*>(skey + i);
+      rank += (q.x == key) + (q.y == key) + (q.z == key) + (q.w == key);
+    }
+    for (int i = t & ~3; i < t; i++) rank += skey[i] == key;
+    const int p = base[key] + rank;
+    perm[p] = r0 + t;
+    if (pos_out) pos_out[r0 + t] = p;
   }
 }
 
@@ -153,21 +153,36 @@ __global__ __launch_bounds__(256) void bucket_inverse_kernel(const int32_t* __re
 }  // namespace
 
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
-                         int32_t* pos, int32_t* tile_start, int tile_m, hipStream_t s) {
+                         int32_t* pos, int32_t* tile_start, int tile_m, int32_t* scratch, hipStream_t s) {
   const int n = T * k;
   const int C = bucket_chunks(n, E);
-  const int ch = (n + C - 1) / C;
-  int32_t* hist = C == 1 ? counts : pos;  // C E <= n when C > 1
+  const int ch = (n + C - 1) / C;  // <= 1.5 E + 1 for 2 <= C < 1024, < 2 E for C = 1, n / 1024 at the cap
+  if (ch > PLACE_MAX_CH) return hipErrorInvalidValue;
+  int32_t* hist = C == 1 ? counts : scratch ? scratch : pos;  // pos: C E <= n when C > 1
+  int pid = prof_begin("bucket_count", s);
   QMOE_LAUNCH(bucket_count_kernel, dim3(C), dim3(64), 0, s, idx, n, E, ch, hist);
+  prof_end(pid, s);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  pid = prof_begin("bucket_scan", s);
   QMOE_LAUNCH(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, n, E, C, counts, hist, offsets, tile_start,
               tile_m > 0 ? tile_m : 1);
+  prof_end(pid, s);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  QMOE_LAUNCH(bucket_place_kernel, dim3(C), dim3(64), 0, s, idx, n, E, ch, C, offsets, hist, perm);
+  const bool direct = C == 1 || scratch != nullptr;  // pos is not the histogram store: written by the placement
+  pid = prof_begin("bucket_place", s);
+  QMOE_LAUNCH(bucket_place_kernel, dim3(C), dim3(256), 0, s, idx, n, E, ch, C, offsets, hist, perm,
+              direct ? pos : nullptr);
+  prof_end(pid, s);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (direct) return hipSuccess;
   const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  pid = prof_begin("bucket_inverse", s);
   QMOE_LAUNCH(bucket_inverse_kernel, dim3(blocks), dim3(256), 0, s, idx, n, E, counts, offsets, perm, pos);
+  prof_end(pid, s);
   return hipGetLastError();
 }
+
+// Scratch counts that launch_bucket can take for n routes and E keys.
+size_t bucket_scratch_ints(int n, int E) { return (size_t)bucket_chunks(n, E) * (size_t)E; }
 
 }  // namespace qmoe

@@ -50,8 +50,12 @@ hipError_t launch_topk(const float* z, int T, int E, int k, const float* bias, i
 
 // bucket.hip.  tile_start (nullable): [E+1] exclusive prefix of
 // ceil(counts[e] / tile_m) -- the M-tile schedule of the grouped GEMMs.
+// scratch (nullable): bucket_scratch_ints(T k, E) counts, which saves a
+// launch (without it the chunk histograms are kept in pos).  Each launch is
+// timed under its own profiler name (bucket_count, _scan, _place, _inverse).
 hipError_t launch_bucket(const int32_t* idx, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
-                         int32_t* pos, int32_t* tile_start, int tile_m, hipStream_t s);
+                         int32_t* pos, int32_t* tile_start, int tile_m, int32_t* scratch, hipStream_t s);
+size_t bucket_scratch_ints(int n, int E);
 
 // decode.hip (+ decode_k1/k2/k3.hip): the three decode launches of one layer
 // (or of given routes).
