@@ -384,6 +384,15 @@ int moe_expert_ffn_decode(const moe_layer* L, const void* x, int32_t x_dtype,
  * units with exact products), then a fixed-order combine.
  *   bucket_out (nullable) receives counts | offsets | perm, int32
  *   [E + (E + 1) + T*k], exactly as moe_bucket defines them.
+ * A Q8 shared expert runs as dense fp16 GEMMs (hipBLASLt) on fp16 copies of
+ * its weights that each call writes into the workspace (its size counts
+ * them: 2 * 3 * d * f bytes more), as the RTX 5080 page's table of launcher
+ * variables lists an optional Q8-to-F16 weight conversion.  The first call
+ * of a token count (rounded up to a multiple of 64) on a device makes that
+ * size's GEMM plans, which may allocate; under stream capture a call whose
+ * plans do not exist yet runs the shared expert on the grouped kernels
+ * instead (the same function, other rounding), so capture after one eager
+ * call of the same size to record the dense path.
  */
 int moe_expert_ffn_prefill(const moe_layer* L, const void* x, int32_t x_dtype,
                            int32_t T, const int32_t* idx, const float* wt,
@@ -403,14 +412,16 @@ int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype,
  * moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  The same computation with the
- * same kernels as moe_layer_forward (bitwise the same outputs); the
- * workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library
- * holds in each device's memory from its load until the process ends.
- * Nothing is allocated by the call (the first call on a device looks up
- * that device's array).  That covers every decode call (T <= 8 at any
- * supported shape) and short prefill chunks; a call that would need more
- * (moe_workspace_bytes(L, T, MOE_OP_LAYER) on its path) returns
- * MOE_ERR_WORKSPACE and enqueues nothing.  Every call on one device shares
+ * same kernels as moe_layer_forward (bitwise the same outputs), except that
+ * a Q8 shared expert on the prefill path runs on the grouped kernels rather
+ * than as dense GEMMs (other rounding, the same accuracy); the workspace is
+ * a fixed array of MOE_NOALLOC_SCRATCH_BYTES that the library holds in each
+ * device's memory from its load until the process ends.  Nothing is
+ * allocated by the call (the first call on a device looks up that device's
+ * array).  That covers every decode call (T <= 8 at any supported shape)
+ * and short prefill chunks; a call that would need more (the workspace of
+ * moe_layer_forward on its path, less the dense shared expert's buffers)
+ * returns MOE_ERR_WORKSPACE and enqueues nothing.  Every call on one device shares
  * that device's array, and the array keeps the last call's contents (no
  * call needs it cleared): calls that overlap in time on one device (several
  * streams or host threads) race, and must be ordered by the caller.

@@ -20,12 +20,14 @@ OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "route.hip", "bucket.hip", "repack.hip", "decode.hip", "decode_k1.hip", "decode_k2.hip",
-           "decode_k3.hip", "decode_unique.hip", "prefill.hip"]
+           "decode_k3.hip", "decode_unique.hip", "prefill.hip", "dense.hip"]
 PROBE_SOURCES = ["probe.hip"]
 # packed-fp32 VALU forms are disabled: only ordinary fp32 instructions
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 PER_FILE = {"route.hip": ["-ffp-contract=off"]}
+# hipBLASLt runs the dense shared-expert GEMMs of long prefill chunks (dense.hip)
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 
 
 def _compile(src: str) -> str:
@@ -41,9 +43,9 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _link(objs, out):
+def _link(objs, out, libs=()):
     tmp = out + ".tmp"
-    cmd = ["hipcc", "-shared", "-o", tmp, f"--offload-arch={ARCH}"] + objs
+    cmd = ["hipcc", "-shared", "-o", tmp, f"--offload-arch={ARCH}"] + objs + list(libs)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
@@ -54,7 +56,7 @@ def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(10, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[:len(SOURCES)], OUT, LIBS)
     _link(objs[len(SOURCES):], PROBE_OUT)
     if verbose:
         print(f"built {OUT} and {PROBE_OUT}")

@@ -88,9 +88,21 @@ void prof_take_events(hipEvent_t* start, hipEvent_t* stop) {
   t_pend_a = t_pend_b = nullptr;
 }
 
+static thread_local hipEvent_t t_lib_b = nullptr;
+
+void prof_library_call(hipStream_t s) {
+  if (t_pend_a == nullptr) return;
+  (void)hipEventRecord(t_pend_a, s);
+  t_lib_b = t_pend_b;
+  t_pend_a = t_pend_b = nullptr;
+}
+
 void prof_end(int id, hipStream_t s) {
   if (id < 0) return;
-  if (t_pend_a != nullptr) {  // no launch consumed the pair: record it empty
+  if (t_lib_b != nullptr) {  // a library call's region: its end in stream order
+    (void)hipEventRecord(t_lib_b, s);
+    t_lib_b = nullptr;
+  } else if (t_pend_a != nullptr) {  // no launch consumed the pair: record it empty
     (void)hipEventRecord(t_pend_a, s);
     (void)hipEventRecord(t_pend_b, s);
     t_pend_a = t_pend_b = nullptr;
@@ -332,6 +344,8 @@ struct PrefillWs {
   int8_t *Hexp, *Hsexp;
   float *Hsc, *Hssc;
   float *Ye, *Ysh;
+  uint16_t *Wgu, *Wdn;  // the dense shared expert's fp16 weights (null without)
+  float *colsc, *Dgu;
 };
 struct LayerWs {
   float* z;
@@ -342,7 +356,8 @@ struct LayerWs {
 
 void carve_route(Carve& c, RouteWs& w, int E, int T) { w.z = (float*)c.take((size_t)T * E * 4); }
 void carve_decode(Carve& c, DecodeWs& w, int T, int k, int d, int f) { w.quant = c.take(decode_quant_bytes(T, k, d, f)); }
-void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, int has_shared, bool bucket_out) {
+void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, int has_shared, bool dense,
+                   bool bucket_out) {
   const size_t n = (size_t)T * k;
   if (!bucket_out) {
     w.counts = (int32_t*)c.take((size_t)E * 4);
@@ -352,7 +367,8 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   w.tile_start = (int32_t*)c.take((size_t)(E + 1) * 4);
   w.pos = (int32_t*)c.take(n * 4);
   w.bucket_hist = (int32_t*)c.take(bucket_scratch_ints((int)n, E) * 4);
-  w.x16 = (uint16_t*)c.take((size_t)T * d * 2);
+  const size_t Tg = dense && has_shared ? dense_rows(T) : T;  // rows of the dense shared GEMMs' operands
+  w.x16 = (uint16_t*)c.take(Tg * d * 2);
   w.xs = (float*)c.take((size_t)T * 4);
   w.route_xs = (float*)c.take(n * 4);
   w.H = c.take(n * f * 2);
@@ -360,15 +376,23 @@ void carve_prefill(Carve& c, PrefillWs& w, int E, int T, int k, int d, int f, in
   w.Hsc = (float*)c.take(n * 4);
   w.Ye = (float*)c.take(n * d * 4);
   if (has_shared) {
-    w.Hs = c.take((size_t)T * f * 2);
+    w.Hs = c.take(Tg * f * 2);
     w.Hsexp = (int8_t*)c.take((size_t)T * (f / PREFILL_HCHUNK));
     w.Hssc = (float*)c.take((size_t)T * 4);
-    w.Ysh = (float*)c.take((size_t)T * d * 4);
+    w.Ysh = (float*)c.take(Tg * d * 4);
   } else {
     w.Hs = nullptr;
     w.Hsexp = nullptr;
     w.Hssc = nullptr;
     w.Ysh = nullptr;
+  }
+  w.Wgu = w.Wdn = nullptr;
+  w.colsc = w.Dgu = nullptr;
+  if (has_shared && dense) {
+    w.Wgu = (uint16_t*)c.take((size_t)2 * f * d * 2);
+    w.Wdn = (uint16_t*)c.take((size_t)d * f * 2);
+    w.colsc = (float*)c.take((size_t)(2 * f + d) * 4);
+    w.Dgu = (float*)c.take(Tg * 2 * f * 4);
   }
 }
 void carve_layer_routes(Carve& c, LayerWs& w, int E, int T, int k) {
@@ -390,13 +414,13 @@ size_t ws_decode(int T, int k, int d, int f) {
   carve_decode(c, w, T, k, d, f);
   return c.off;
 }
-size_t ws_prefill(int E, int T, int k, int d, int f, int sh) {
+size_t ws_prefill(int E, int T, int k, int d, int f, int sh, bool dense) {
   Carve c;
   PrefillWs w;
-  carve_prefill(c, w, E, T, k, d, f, sh, false);
+  carve_prefill(c, w, E, T, k, d, f, sh, dense, false);
   return c.off;
 }
-size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
+size_t ws_layer(int E, int T, int k, int d, int f, int sh, bool dense, int path) {
   Carve c;
   LayerWs lw;
   carve_layer_routes(c, lw, E, T, k);
@@ -405,11 +429,18 @@ size_t ws_layer(int E, int T, int k, int d, int f, int sh, int path) {
     carve_decode(c, w, T < DECODE_MAX_T ? T : DECODE_MAX_T, k, d, f);
   } else {
     PrefillWs w;
-    carve_prefill(c, w, E, T, k, d, f, sh, false);
+    carve_prefill(c, w, E, T, k, d, f, sh, dense, false);
   }
   return c.off;
 }
 }  // namespace
+
+// The shared expert of a prefill call as dense fp16 GEMMs (dense.hip): a Q8
+// shared expert and a caller's workspace (the fp16 weights do not fit the
+// fixed no-alloc array, and the library GEMM's first use allocates).
+static bool dense_shared(const moe_layer* L, bool noalloc) {
+  return !noalloc && L->has_shared && L->fmt_shared == FMT_Q8;
+}
 
 static int resolve_path(int path, int T) {
   if (path == MOE_PATH_AUTO) return T <= AUTO_DECODE_MAX_T ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
@@ -461,11 +492,11 @@ extern "C" int moe_workspace_bytes(const moe_layer* L, int32_t T, int32_t op, si
   const int E = L->n_experts, d = L->d_model, f = L->d_ff, k = L->top_k, sh = L->has_shared ? 1 : 0;
   switch (op) {
     case MOE_OP_DECODE: *bytes = ws_decode(T, k, d, f); break;
-    case MOE_OP_PREFILL: *bytes = ws_prefill(E, T, k, d, f, sh); break;
+    case MOE_OP_PREFILL: *bytes = ws_prefill(E, T, k, d, f, sh, dense_shared(L, false)); break;
     case MOE_OP_LAYER: {
-      size_t b = ws_layer(E, T, k, d, f, sh, MOE_PATH_PREFILL);
+      size_t b = ws_layer(E, T, k, d, f, sh, dense_shared(L, false), MOE_PATH_PREFILL);
       if (T <= AUTO_DECODE_MAX_T) {
-        const size_t b2 = ws_layer(E, T, k, d, f, sh, MOE_PATH_DECODE);
+        const size_t b2 = ws_layer(E, T, k, d, f, sh, false, MOE_PATH_DECODE);
         if (b2 > b) b = b2;
       }
       *bytes = b;
@@ -659,10 +690,10 @@ static PrefillLaunch prefill_launch(const moe_layer* L, const void* x, int x_dty
 
 // bucketing + grouped GEMMs + combine for routes already in device memory
 static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_dtype, int T, const int32_t* idx,
-                       const float* wt, float* y, int32_t* bucket_out, Carve& c, hipStream_t s) {
+                       const float* wt, float* y, int32_t* bucket_out, bool dense, Carve& c, hipStream_t s) {
   const int E = L->n_experts, k = L->top_k;
   PrefillWs w;
-  carve_prefill(c, w, E, T, k, L->d_model, L->d_ff, L->has_shared, bucket_out != nullptr);
+  carve_prefill(c, w, E, T, k, L->d_model, L->d_ff, L->has_shared, dense, bucket_out != nullptr);
   if (bucket_out) {
     w.counts = bucket_out;
     w.offsets = bucket_out + E;
@@ -687,6 +718,10 @@ static int run_prefill(const char* fn, const moe_layer* L, const void* x, int x_
   P.Hssc = w.Hssc;
   P.Ye = w.Ye;
   P.Ysh = w.Ysh;
+  P.Wgu = w.Wgu;
+  P.Wdn = w.Wdn;
+  P.colsc = w.colsc;
+  P.Dgu = w.Dgu;
   P.y = y;
   const int tile_m = PREFILL_BM;
   hipError_t e = launch_bucket(idx, T, k, E, w.counts, w.offsets, w.perm, w.pos, w.tile_start, tile_m, w.bucket_hist, s);
@@ -741,11 +776,12 @@ extern "C" int moe_expert_ffn_prefill(const moe_layer* L, const void* x, int32_t
   NEED_PTR(y, "y");
   NEED_PTR(ws, "workspace");
   if (bucket_out && ((uintptr_t)bucket_out & 3u)) return fail(MOE_ERR_INVALID_ARG, "%s: bucket_out misaligned", fn);
-  const size_t need = ws_prefill(L->n_experts, T, L->top_k, L->d_model, L->d_ff, L->has_shared);
+  const bool dense = dense_shared(L, false);
+  const size_t need = ws_prefill(L->n_experts, T, L->top_k, L->d_model, L->d_ff, L->has_shared, dense);
   if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   Carve c;
   c.base = (uint8_t*)ws;
-  return run_prefill(fn, L, x, x_dtype, T, idx, wt, y, bucket_out, c, (hipStream_t)stream);
+  return run_prefill(fn, L, x, x_dtype, T, idx, wt, y, bucket_out, dense, c, (hipStream_t)stream);
 }
 
 // The device array behind moe_layer_forward_noalloc: a fixed workspace in
@@ -795,7 +831,8 @@ static int layer_forward(const char* fn, const moe_layer* L, const void* x, int3
   if (idx_out && !aligned16(idx_out)) return fail(MOE_ERR_INVALID_ARG, "%s: idx_out is not 16-byte aligned", fn);
   if (wt_out && !aligned16(wt_out)) return fail(MOE_ERR_INVALID_ARG, "%s: wt_out is not 16-byte aligned", fn);
   const int E = L->n_experts, k = L->top_k;
-  const size_t need = ws_layer(E, T, k, L->d_model, L->d_ff, L->has_shared, p);
+  const bool dense = p == MOE_PATH_PREFILL && dense_shared(L, noalloc);
+  const size_t need = ws_layer(E, T, k, L->d_model, L->d_ff, L->has_shared, dense, p);
   if (noalloc) {
     if (need > MOE_NOALLOC_SCRATCH_BYTES)
       return fail(MOE_ERR_WORKSPACE,
@@ -845,7 +882,7 @@ static int layer_forward(const char* fn, const moe_layer* L, const void* x, int3
   e = launch_topk(lw.z, T, E, k, L->router_bias, lw.idx, lw.wt, idx_out, wt_out, s);
   prof_end(pid, s);
   if (e != hipSuccess) return hip_fail(e, fn);
-  return run_prefill(fn, L, x, x_dtype, T, lw.idx, lw.wt, y, nullptr, c, s);
+  return run_prefill(fn, L, x, x_dtype, T, lw.idx, lw.wt, y, nullptr, dense, c, s);
 }
 
 extern "C" int moe_layer_forward(const moe_layer* L, const void* x, int32_t x_dtype, int32_t T, float* y,

@@ -1,0 +1,250 @@
+// The shared expert on the prefill path as plain dense GEMMs: every token of
+// a chunk goes through it, so its Q8 weights are converted to fp16 once per
+// call (one pass over the three matrices) and multiplied by a library GEMM
+// (hipBLASLt, fp16 operands, fp32 accumulation and output) instead of being
+// decoded again for every M tile.  The pages
+// run prefill experts on 16-bit matrix units ("YoungAi -- DeepSeek V4.1
+// Flash on one DGX Spark", section 4.4, prefill), and list a Q8-to-F16
+// weight conversion among the optional CUDA settings ("Running DeepSeek V4
+// Flash on an RTX 5080 with 16GB VRAM Under Linux/WSL2 via DS4", table of
+// launcher variables).
+//
+//   1. dequant: row n of a Q8 matrix -> fp16(d q 2^k_n), one rounding, with
+//      2^k_n a power of two per row that puts the row's largest |d| * 128 in
+//      [2^14, 2^15): no product overflows, and every nonzero one is a
+//      normal fp16 when its block scale is at least 2^-21 of the row's
+//      largest; colsc[n] = 2^-k_n;
+//   2. G|U = x16 W_gu^T (T x 2f, fp32) by hipBLASLt, on dense_rows(T) rows;
+//   3. swiglu: h = silu(g xs_t colsc) * (u xs_t colsc), stored as the grouped
+//      GEMMs' gate/up epilogue stores it (fp16 times a power of two per row
+//      and 64 outputs, with its exponent), so the row normalisation and the
+//      down GEMM that follow are unchanged;
+//   4. Ysh' = Hs W_d^T (T x d, fp32) by hipBLASLt; the combine multiplies it
+//      by the row's and the column's powers of two.
+#include <hipblaslt/hipblaslt.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qmoe {
+
+namespace {
+
+// One wave per row of a Q8 matrix with K inputs (K / 32 blocks): lane l
+// takes blocks l, l + 64, ...
+__global__ __launch_bounds__(256) void dequant_q8_kernel(QMat m, int rows, uint16_t* __restrict__ out,
+                                                         float* __restrict__ colsc) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= rows) return;  // uniform per wave
+  const int nb = m.nb;
+  const uint16_t* ds = reinterpret_cast<const uint16_t*>(m.p_scale) + (int64_t)n * nb;
+  float dmax = 0.0f;
+  for (int b = lane; b < nb; b += 64) dmax = fmaxf(dmax, fabsf(half_bits_to_float(ds[b])));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o, 64));
+  int k = 0;
+  const float mx = dmax * 128.0f;
+  if (mx > 0.0f && mx <= 3.4e38f) {
+    int ex;
+    frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+    k = min(max(15 - ex, -100), 100);
+  }
+  if (lane == 0) colsc[n] = __builtin_amdgcn_ldexpf(1.0f, -k);
+  for (int b = lane; b < nb; b += 64) {
+    const float d = __builtin_amdgcn_ldexpf(half_bits_to_float(ds[b]), k);
+    const int8_t* q = reinterpret_cast<const int8_t*>(m.p_a) + ((int64_t)n * nb + b) * 32;
+    uint16_t* o = out + (int64_t)n * m.K + 32 * b;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const uint4 w = *reinterpret_cast<const uint4*>(q + 16 * u);
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float v0 = d * (float)(int8_t)(wv[i] & 255u), v1 = d * (float)(int8_t)((wv[i] >> 8) & 255u);
+        const float v2 = d * (float)(int8_t)((wv[i] >> 16) & 255u), v3 = d * (float)(int8_t)(wv[i] >> 24);
+        h[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+        h[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
+      }
+      *reinterpret_cast<uint4*>(o + 16 * u) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(o + 16 * u + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+    }
+  }
+}
+
+// One wave per (token, 256 outputs): lane l takes outputs 4l .. 4l + 3 of
+// the wave's run, and each group of 16 lanes one 64-output exponent chunk.
+// D = [T][2f] (gate columns, then up).
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ D, const float* __restrict__ xs,
+                                                     const float* __restrict__ colsc, int T, int f,
+                                                     uint16_t* __restrict__ H, int8_t* __restrict__ Hexp) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int runs = f / 256;
+  if (w >= T * runs) return;  // uniform per wave
+  const int t = w / runs;
+  const int n = 256 * (w - t * runs) + 4 * lane;
+  const float x = xs[t];
+  const float4 g = *reinterpret_cast<const float4*>(D + (int64_t)t * 2 * f + n);
+  const float4 u = *reinterpret_cast<const float4*>(D + (int64_t)t * 2 * f + f + n);
+  const float4 cg = *reinterpret_cast<const float4*>(colsc + n);
+  const float4 cu = *reinterpret_cast<const float4*>(colsc + f + n);
+  float hv[4] = {silu(g.x * x * cg.x) * (u.x * x * cu.x), silu(g.y * x * cg.y) * (u.y * x * cu.y),
+                 silu(g.z * x * cg.z) * (u.z * x * cu.z), silu(g.w * x * cg.w) * (u.w * x * cu.w)};
+  float mx = fmaxf(fmaxf(fabsf(hv[0]), fabsf(hv[1])), fmaxf(fabsf(hv[2]), fabsf(hv[3])));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));  // over the 16 lanes of the chunk
+  int e = 0;
+  if (mx > 0.0f && mx <= 3.4e38f) {
+    int ex;
+    frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+    e = min(max(ex - 15, -100), 100);
+  }
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, -e);
+  uint32_t h01 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(hv[0] * sc)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(hv[1] * sc)) << 16);
+  uint32_t h23 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(hv[2] * sc)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(hv[3] * sc)) << 16);
+  *reinterpret_cast<uint2*>(H + (int64_t)t * f + n) = make_uint2(h01, h23);
+  if ((lane & 15) == 0) Hexp[(int64_t)t * (f / 64) + n / 64] = (int8_t)e;
+}
+
+// hipBLASLt: one handle per device, one plan (descriptors and the
+// heuristic's first algorithm) per device and shape, made on first use under
+// a lock and kept until the process ends.  Only algorithms that need no
+// workspace are taken: nothing is cleared between calls, the same bits come
+// back every call, and a captured graph holds nothing but kernel launches.
+struct GemmPlan {
+  int dev, T, N, K;
+  hipblasLtMatmulDesc_t md;
+  hipblasLtMatrixLayout_t la, lb, ld;
+  hipblasLtMatmulAlgo_t algo;
+};
+std::mutex g_blt_mu;
+std::vector<std::pair<int, hipblasLtHandle_t>> g_handles;
+std::vector<GemmPlan> g_plans;
+
+hipError_t blt_err(hipblasStatus_t st) { return st == HIPBLAS_STATUS_SUCCESS ? hipSuccess : hipErrorUnknown; }
+
+const GemmPlan* find_plan(int dev, int T, int N, int K) {  // (under the lock)
+  for (const auto& p : g_plans)
+    if (p.dev == dev && p.T == T && p.N == N && p.K == K) return &p;
+  return nullptr;
+}
+
+hipError_t get_plan(int T, int N, int K, hipblasLtHandle_t* h_out, GemmPlan* p_out) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_blt_mu);
+  hipblasLtHandle_t h = nullptr;
+  for (auto& x : g_handles)
+    if (x.first == dev) h = x.second;
+  if (!h) {
+    if (hipblasStatus_t st = hipblasLtCreate(&h); st != HIPBLAS_STATUS_SUCCESS) return blt_err(st);
+    g_handles.emplace_back(dev, h);
+  }
+  *h_out = h;
+  if (const GemmPlan* q = find_plan(dev, T, N, K)) {
+    *p_out = *q;
+    return hipSuccess;
+  }
+  // D^T (N x T, column-major) = op(W) * A^T with W given as K x N
+  // (transposed) and A^T as K x T: column-major views of the row-major
+  // [N][K], [T][K] and [T][N] arrays
+  GemmPlan p{};
+  p.dev = dev;
+  p.T = T;
+  p.N = N;
+  p.K = K;
+  hipblasStatus_t st;
+  if ((st = hipblasLtMatmulDescCreate(&p.md, HIPBLAS_COMPUTE_32F, HIP_R_32F)) != HIPBLAS_STATUS_SUCCESS)
+    return blt_err(st);
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  if ((st = hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta))) ||
+      (st = hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb))) ||
+      (st = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16F, K, N, K)) ||
+      (st = hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16F, K, T, K)) ||
+      (st = hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_32F, N, T, N)))
+    return blt_err(st);
+  hipblasLtMatmulPreference_t pref;
+  if ((st = hipblasLtMatmulPreferenceCreate(&pref)) != HIPBLAS_STATUS_SUCCESS) return blt_err(st);
+  const uint64_t no_ws = 0;
+  hipblasLtMatmulHeuristicResult_t res[8];
+  int nres = 0;
+  st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws, sizeof(no_ws));
+  if (st == HIPBLAS_STATUS_SUCCESS)
+    st = hipblasLtMatmulAlgoGetHeuristic(h, p.md, p.la, p.lb, p.ld, p.ld, pref, 8, res, &nres);
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (st != HIPBLAS_STATUS_SUCCESS) return blt_err(st);
+  int best = -1;
+  for (int i = 0; i < nres && best < 0; i++)
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize == 0) best = i;
+  if (best < 0) return hipErrorNotSupported;
+  p.algo = res[best].algo;
+  g_plans.push_back(p);
+  *p_out = p;
+  return hipSuccess;
+}
+
+// D [T][N] fp32 (row-major) = A [T][K] fp16 times W [N][K]^T fp16
+hipError_t gemm_tn(int T, int N, int K, const uint16_t* A, const uint16_t* W, float* D, hipStream_t s) {
+  hipblasLtHandle_t h;
+  GemmPlan p;
+  if (hipError_t e = get_plan(T, N, K, &h, &p); e != hipSuccess) return e;
+  const float alpha = 1.0f, beta = 0.0f;
+  return blt_err(hipblasLtMatmul(h, p.md, &alpha, W, p.la, A, p.lb, &beta, D, p.ld, D, p.ld, &p.algo, nullptr, 0, s));
+}
+
+hipError_t dequant(const QMat& m, int rows, uint16_t* out, float* colsc, hipStream_t s) {
+  QMOE_LAUNCH(dequant_q8_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, m, rows, out, colsc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool shared_dense_ready(int T, int d, int f, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return false;
+  if (cs == hipStreamCaptureStatusNone) return true;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lk(g_blt_mu);
+  return find_plan(dev, dense_rows(T), 2 * f, d) && find_plan(dev, dense_rows(T), d, f);
+}
+
+hipError_t launch_shared_dense_gateup(const SharedDense& S, hipStream_t s) {
+  int pid = prof_begin("prefill_shared_dequant", s);
+  hipError_t e = dequant(S.gate, S.f, S.w_gu, S.colsc, s);
+  if (e == hipSuccess) e = dequant(S.up, S.f, S.w_gu + (size_t)S.f * S.d, S.colsc + S.f, s);
+  if (e == hipSuccess) e = dequant(S.down, S.d, S.w_dn, S.colsc + 2 * S.f, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return e;
+  pid = prof_begin("prefill_shared_gateup", s);
+  prof_library_call(s);
+  e = gemm_tn(dense_rows(S.T), 2 * S.f, S.d, S.x16, S.w_gu, S.dgu, s);
+  prof_end(pid, s);
+  if (e != hipSuccess) return e;
+  pid = prof_begin("prefill_shared_swiglu", s);
+  const int waves = S.T * (S.f / 256);
+  QMOE_LAUNCH(swiglu_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, (const float*)S.dgu, S.xs, (const float*)S.colsc,
+              S.T, S.f, S.hs, S.hsexp);
+  prof_end(pid, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_dense_down(const SharedDense& S, hipStream_t s) {
+  const int pid = prof_begin("prefill_shared_down", s);
+  prof_library_call(s);
+  const hipError_t e = gemm_tn(dense_rows(S.T), S.d, S.f, S.hs, S.w_dn, S.ysh, s);
+  prof_end(pid, s);
+  return e;
+}
+
+}  // namespace qmoe

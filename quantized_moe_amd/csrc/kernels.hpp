@@ -26,6 +26,10 @@ constexpr int AUTO_DECODE_MAX_T = MOE_AUTO_DECODE_MAX_T;  // MOE_PATH_AUTO's swi
 int prof_begin(const char* name, hipStream_t s);
 void prof_end(int id, hipStream_t s);
 void prof_take_events(hipEvent_t* start, hipEvent_t* stop);  // the pending pair, or nulls
+// A region around a library call instead of one QMOE_LAUNCH: the start event
+// is recorded on the stream now, the stop by prof_end (stream order, so the
+// time includes the gaps between the library's launches).
+void prof_library_call(hipStream_t s);
 
 #define QMOE_LAUNCH(kern, grid, block, shmem, stream, ...)                                   \
   do {                                                                                         \
@@ -104,15 +108,44 @@ struct PrefillLaunch {
   float* route_xs;  // [T*k]: the same at each route, in bucket order
   void* H;      // fp16 [T*k][f]: h * 2^-Hexp of its 128-column chunk
   void* Hs;     // fp16 [T][f]
-  int8_t* Hexp;   // [T*k][f/128]
-  int8_t* Hsexp;  // [T][f/128]
+  int8_t* Hexp;   // [T*k][f/PREFILL_HCHUNK]
+  int8_t* Hsexp;  // [T][f/PREFILL_HCHUNK]
   float* Hsc;     // [T*k]: 2^e of each H row once its chunks share one exponent
   float* Hssc;    // [T]
   float* Ye;    // [T*k][d]
   float* Ysh;   // [T][d]
   float* y;     // [T][d]
+  // a Q8 shared expert as dense fp16 GEMMs (dense.hip): the buffers, all
+  // null when the workspace has none (then the grouped kernels run it)
+  uint16_t *Wgu, *Wdn;  // fp16 [2f][d] (gate rows, then up), [d][f]
+  float* colsc;         // [2f + d]: each dequantized row's power of two
+  float* Dgu;           // fp32 [T][2f]
 };
 hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s);
+
+// dense.hip: the shared expert of a prefill chunk as dense GEMMs on fp16
+// copies of its Q8 weights (made by each call).  The GEMMs run on
+// dense_rows(T) rows (a multiple of 64, so that one GEMM plan serves 64 chunk
+// sizes); x16, Hs and Ysh are carved with that many rows, and the rows past
+// T hold whatever the buffers held (their results are never read).
+inline int dense_rows(int T) { return (T + 63) & ~63; }
+struct SharedDense {
+  int T, d, f;
+  QMat gate, up, down;
+  const uint16_t* x16;  // [T][d], x16 * xs = x
+  const float* xs;      // [T]
+  uint16_t *w_gu, *w_dn;
+  float* colsc;  // [2f + d]
+  float* dgu;    // [T][2f]
+  uint16_t* hs;  // [T][f]: fp16 h times a power of two per 64 outputs ...
+  int8_t* hsexp;  // [T][f/64]: ... and its exponent
+  float* ysh;     // [T][d]: before the row and column powers of two
+};
+// false under stream capture before the chunk size's GEMM plans exist
+// (making them may allocate): then the grouped kernels run the shared expert
+bool shared_dense_ready(int T, int d, int f, hipStream_t s);
+hipError_t launch_shared_dense_gateup(const SharedDense& S, hipStream_t s);
+hipError_t launch_shared_dense_down(const SharedDense& S, hipStream_t s);
 // The grouped GEMMs address their A operands (x16, H, Hs) with 32-bit byte
 // offsets: false when T, k, d, f would pass 2^31.
 inline bool prefill_fits(int T, int k, int d, int f) {

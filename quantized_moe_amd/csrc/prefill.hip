@@ -1346,9 +1346,11 @@ __global__ __launch_bounds__(256) void hnorm_kernel(uint16_t* __restrict__ H0, c
 
 // ---------------------------------------------------------------------------
 // combine: y[t] = sum_j wt[t][j] * (g_e * Ye[pos[t*k+j]]) + ysh[t]   (fixed j order; g_e the route's
-// per-channel down gains, one when none are given)
+// per-channel down gains, one when none are given; ysh[t][c] times ysh_row[t] ysh_col[c] when those
+// are given: the dense shared expert's powers of two)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ye, const float* __restrict__ ysh,
+                                                      const float* __restrict__ ysh_row, const float* __restrict__ ysh_col,
                                                       const int32_t* __restrict__ pos, const float* __restrict__ wt,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ gain,
                                                       int E, int k, int d, int n_routes, float* __restrict__ y) {
@@ -1372,7 +1374,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       acc.w = __builtin_fmaf(w, v.w, acc.w);
     }
     if (ysh) {
-      const float4 s = *reinterpret_cast<const float4*>(ysh + (int64_t)t * d + 4 * c);
+      float4 s = *reinterpret_cast<const float4*>(ysh + (int64_t)t * d + 4 * c);
+      if (ysh_col) {
+        const float r = ysh_row[t];
+        const float4 cs = *reinterpret_cast<const float4*>(ysh_col + 4 * c);
+        s = make_float4(s.x * r * cs.x, s.y * r * cs.y, s.z * r * cs.z, s.w * r * cs.w);
+      }
       acc.x += s.x;
       acc.y += s.y;
       acc.z += s.z;
@@ -1514,7 +1521,28 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     PF_FMT_SWITCH(P.fmt_gate_up, F, err = (run_gemm<F, true, RoutedTile>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
-  if (P.has_shared) {
+  // the shared expert as dense fp16 GEMMs when the workspace has their
+  // buffers (a Q8 shared expert and a caller's workspace)
+  const bool dense = P.has_shared && P.Wgu && shared_dense_ready(P.T, P.d, P.f, s);
+  SharedDense S{};
+  if (dense) {
+    S.T = P.T;
+    S.d = P.d;
+    S.f = P.f;
+    S.gate = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
+    S.up = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
+    S.down = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
+    S.x16 = P.x16;
+    S.xs = P.xs;
+    S.w_gu = P.Wgu;
+    S.w_dn = P.Wdn;
+    S.colsc = P.colsc;
+    S.dgu = P.Dgu;
+    S.hs = static_cast<uint16_t*>(P.Hs);
+    S.hsexp = P.Hsexp;
+    S.ysh = P.Ysh;
+    if ((err = launch_shared_dense_gateup(S, s)) != hipSuccess) return err;
+  } else if (P.has_shared) {
     GemmArgs a{};
     a.B0 = make_qmat(P.s_gate, P.fmt_shared, 1, P.f, P.d);
     a.B1 = make_qmat(P.s_up, P.fmt_shared, 1, P.f, P.d);
@@ -1566,7 +1594,9 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
     PF_FMT_SWITCH(P.fmt_down, F, err = (run_gemm<F, false, RoutedTile>(a, m_tiles, s)))
     if (err != hipSuccess) return err;
   }
-  if (P.has_shared) {
+  if (dense) {
+    if ((err = launch_shared_dense_down(S, s)) != hipSuccess) return err;
+  } else if (P.has_shared) {
     GemmArgs b{};
     b.B0 = make_qmat(P.s_down, P.fmt_shared, 1, P.d, P.f);
     b.grid = P.grid;
@@ -1587,6 +1617,7 @@ hipError_t launch_prefill_gemms(const PrefillLaunch& P, hipStream_t s) {
   }
   const int pid = prof_begin("prefill_combine", s);
   QMOE_LAUNCH(combine_kernel, dim3(P.T), dim3(256), 0, s, (const float*)P.Ye, (const float*)(P.has_shared ? P.Ysh : nullptr),
+              (const float*)(dense ? P.Hssc : nullptr), (const float*)(dense ? P.colsc + 2 * P.f : nullptr),
               (const int32_t*)P.pos, (const float*)P.wt, P.idx, P.down_gain, P.E, P.k, P.d, P.T * P.k, P.y);
   prof_end(pid, s);
   return hipGetLastError();

@@ -222,6 +222,94 @@ def test_kquant_rows_with_zero_and_far_superblock_scales(fgu):
             assert err.max() <= REL_L2, (T, path, err.max())
 
 
+def _spread_q8_scales(w, nb):
+    """Q8 block scales of a [rows][nb] matrix moved apart along rows: 2^2 up
+    (the row's largest, which sets the row's power of two in the fp16 copy),
+    2^12 down (fp16 subnormal) and zero, on different blocks and rows.  (A
+    block far above the rest would leave a few products dominating each
+    output, whose cancellation in some tokens asks more than the fp16
+    operands give, on either path.)"""
+    blk = w.reshape(-1, synth.BLOCK_BYTES[synth.FMT_Q8])
+    d = blk[:, 0:2].copy().view("<f2").reshape(-1).astype(np.float32)
+    b = np.arange(blk.shape[0])
+    row, j = b // nb, b % nb
+    d[(j == 1) & (row % 3 == 0)] *= 4.0
+    d[(j == 2) & (row % 5 == 0)] /= 4096.0
+    d[(j == 0) & (row % 7 == 0)] = 0.0
+    blk[:, 0:2] = d.astype("<f2").view(np.uint8).reshape(-1, 2)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 200])
+def test_dense_shared_expert_beside_the_grouped_kernels(T):
+    """A Q8 shared expert on the prefill path runs as dense fp16 GEMMs on
+    per-call fp16 copies of its weights (one power of two per row), over the
+    token count rounded up to a multiple of 64; the no-alloc call has no room
+    for those copies and runs the grouped kernels on the same input.  Both
+    within the parity bar of the oracle, on shared rows whose block scales
+    lie up to 2^14 apart or are zero."""
+    spec = synth.scaled_spec(E=16, k=4, d=512, f=512, fmt_gate_up=synth.FMT_IQ2, fmt_down=synth.FMT_Q2K,
+                             has_shared=True, fmt_shared=synth.FMT_Q8)
+    L = synth.random_layer(spec, seed=13, workload="dense_shared")
+    _spread_q8_scales(L.s_gate, spec.d // 32)
+    _spread_q8_scales(L.s_up, spec.d // 32)
+    _spread_q8_scales(L.s_down, spec.f // 32)
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    x = synth.activations(13, ("dense_shared", T), T, spec.d, synth.BF16)
+    y_ref, idx_ref, _ = oracle.layer_forward(L, x, synth.BF16)
+    y, idx, _ = run_layer(dl, x, synth.BF16, lib.MOE_PATH_PREFILL)
+    assert np.array_equal(idx, idx_ref)
+    assert per_token_rel_l2(y, y_ref).max() <= REL_L2
+    y2 = torch.empty(T, spec.d, dtype=torch.float32, device=DEV)
+    lib.layer_forward_noalloc(dl.desc, to_dev_x(x, synth.BF16), y2, path=lib.MOE_PATH_PREFILL)
+    torch.cuda.synchronize()
+    y2 = y2.cpu().numpy()
+    assert per_token_rel_l2(y2, y_ref).max() <= REL_L2
+
+
+def test_dense_shared_expert_under_graph_capture():
+    """A capture that meets a chunk size whose dense GEMM plans do not exist
+    yet (making them may allocate) records the grouped kernels instead: its
+    replays equal the no-alloc call's bits.  Once an eager call has made the
+    plans, a new capture records the dense path and replays the eager bits.
+    (No other test runs a Q8 shared expert at d = 1024, f = 256.)"""
+    spec = synth.scaled_spec(E=16, k=4, d=1024, f=256, fmt_gate_up=synth.FMT_Q2K, fmt_down=synth.FMT_IQ2,
+                             has_shared=True, fmt_shared=synth.FMT_Q8)
+    L = synth.random_layer(spec, seed=14, workload="dense_capture")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    T = 77
+    x = to_dev_x(synth.activations(14, ("dense_capture", T), T, spec.d, synth.F32), synth.F32)
+    ws = dl.workspace(T)
+    y = torch.empty(T, spec.d, dtype=torch.float32, device=DEV)
+
+    def capture():
+        stream = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        y.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            lib.layer_forward(dl.desc, x, y, ws, path=lib.MOE_PATH_PREFILL)
+        return g
+
+    def replays(g, want):
+        for _ in range(3):
+            y.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, want)
+
+    y_grouped = torch.empty_like(y)
+    lib.layer_forward_noalloc(dl.desc, x, y_grouped, path=lib.MOE_PATH_PREFILL)
+    torch.cuda.synchronize()
+    replays(capture(), y_grouped)
+    lib.layer_forward(dl.desc, x, y, ws, path=lib.MOE_PATH_PREFILL)  # eager: makes the plans
+    torch.cuda.synchronize()
+    y_dense = y.clone()
+    replays(capture(), y_dense)
+    y_ref, _, _ = oracle.layer_forward(L, x.cpu().numpy(), synth.F32)
+    assert per_token_rel_l2(y_dense.cpu().numpy(), y_ref).max() <= REL_L2
+
+
 @pytest.mark.parametrize("fgu", [synth.FMT_Q2K, synth.FMT_Q4K])
 def test_prefill_min_term_with_same_sign_rows(fgu):
     """K-quant gate/up in prefill on rows of one sign and similar magnitude:

@@ -59,7 +59,7 @@ def test_library_host_code_under_asan_ubsan(tmp_path):
     exe = str(tmp_path / "api_driver")
     _run(["hipcc", "-std=c++17", "-I", os.path.join(ROOT, "include")] + HOST_FLAGS +
          ["-x", "c++", os.path.join(SAN, "api_driver.cpp"), str(stub), "-x", "none"] +
-         [o for _, o in objs] + ["-o", exe])
+         [o for _, o in objs] + ["-L/opt/rocm/lib", "-lhipblaslt", "-o", exe])
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")  # (the HIP runtime keeps allocations to exit)
     r = _run([exe], env=env)
     assert r.stdout.strip().endswith("OK")

@@ -1,7 +1,9 @@
 """moe_layer_forward_noalloc (the library's fixed per-device scratch array in
 place of a workspace) against moe_layer_forward on the same inputs: the same
-kernels, so bitwise the same outputs.  Two calls in a row, the second with a
-smaller input (the array keeps the first call's contents)."""
+kernels, so bitwise the same outputs, except for a Q8 shared expert on the
+prefill path (dense GEMMs with a workspace, the grouped kernels without
+one), where the outputs agree to the parity bar.  Two calls in a row, the
+second with a smaller input (the array keeps the first call's contents)."""
 import numpy as np
 import pytest
 import torch
@@ -34,12 +36,19 @@ def _both(dl, x, path):
     return out
 
 
-def _check(dl, x, path):
+REL_L2 = 1e-3
+
+
+def _check(dl, x, path, bitwise=True):
     (y0, i0, w0), (y1, i1, w1) = _both(dl, x, path)
     assert np.all(np.isfinite(y0))
     assert np.array_equal(i1, i0)
     assert np.array_equal(w1, w0)
-    assert np.array_equal(y1, y0)
+    if bitwise:
+        assert np.array_equal(y1, y0)
+    else:
+        a, b = y1.astype(np.float64), y0.astype(np.float64)
+        assert (np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)).max() <= REL_L2
 
 
 def test_noalloc_full_size_decode_two_calls():
@@ -56,10 +65,12 @@ def test_noalloc_full_size_decode_two_calls():
         torch.cuda.empty_cache()
 
 
-def test_noalloc_small_layer_both_paths_two_calls():
+@pytest.mark.parametrize("fmt_shared", [synth.FMT_Q2K, synth.FMT_Q8])
+def test_noalloc_small_layer_both_paths_two_calls(fmt_shared):
     """A small layer on the decode path (T = 6, then 2) and on the prefill
-    path (T = 40, then 9) with bf16 x, a router bias and down gains."""
-    spec = synth.scaled_spec(E=32, k=4, d=1024, f=512)
+    path (T = 40, then 9) with bf16 x, a router bias and down gains; with a
+    Q8 shared expert the prefill outputs agree to the parity bar."""
+    spec = synth.scaled_spec(E=32, k=4, d=1024, f=512, fmt_shared=fmt_shared)
     L = synth.random_layer(spec, seed=8, workload="noalloc")
     rng = np.random.default_rng(8)
     L = synth.Layer(**{**L.__dict__, "router_bias": rng.normal(0, 0.05, spec.E).astype(np.float32),
@@ -68,7 +79,7 @@ def test_noalloc_small_layer_both_paths_two_calls():
     for path, Ts in ((lib.MOE_PATH_DECODE, (6, 2)), (lib.MOE_PATH_PREFILL, (40, 9))):
         for T in Ts:
             x = _x(synth.activations(8, ("noalloc", path, T), T, spec.d, synth.BF16), synth.BF16)
-            _check(dl, x, path)
+            _check(dl, x, path, bitwise=path == lib.MOE_PATH_DECODE or fmt_shared != synth.FMT_Q8)
 
 
 def test_noalloc_rejects_calls_above_its_scratch():
