@@ -89,8 +89,11 @@ KERNEL_SYMBOLS = {
     "prefill_gateup": "gemm_kernel<1, true",
     "prefill_down": "gemm_kernel<2, false",
 }
-# the shared expert's GEMMs (Q8), for the instruction-counter tables only
-PMC_EXTRA_SYMBOLS = {"prefill_shared_gateup": "gemm_kernel<3, true", "prefill_shared_down": "gemm_kernel<3, false"}
+# the shared expert's kernels (Q8: fp16 weight copies, the two library GEMMs
+# -- hipBLASLt's kernel names start with Cijk_ -- and the SwiGLU), for the
+# instruction-counter tables only
+PMC_EXTRA_SYMBOLS = {"prefill_shared_dequant": "dequant_q8_kernel", "prefill_shared_gemms (hipBLASLt)": "Cijk_",
+                     "prefill_shared_swiglu": "swiglu_kernel"}
 
 
 def pmc_table(dirs) -> int:

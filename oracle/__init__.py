@@ -148,6 +148,8 @@ def bucket(idx, E):
     idx = _c(idx, np.int32)
     T, k = idx.shape
     n = T * k
+    if n and (idx.min() < 0 or idx.max() >= E):
+        raise ValueError("bucket: every key must lie in [0, E)")
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     perm = np.empty(n, np.int32)

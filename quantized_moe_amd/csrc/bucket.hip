@@ -50,23 +50,62 @@ __global__ __launch_bounds__(64) void bucket_count_kernel(const int32_t* __restr
   for (int i = lane; i < E; i += 64) hist_out[(int64_t)c * E + i] = hist[i];
 }
 
-// One block of 1024 threads: thread e owns expert e (E <= 1024).
+// One block of 1024 threads (E <= 1024).  Each chunk's count of key e
+// becomes the number of routes with key e in the chunks before it, either
+// by thread e walking the C chunks (eight loads in flight: about C / 8
+// dependent load rounds), or, when that is the longer (few keys, many
+// routes), by wave w taking keys w, w + 16, ... with its lanes on 64 chunks
+// at a time (four loads in flight per lane, ceil(E / 16) ceil(C / 256)
+// rounds) and a wave prefix sum.
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(int n, int E, int C, int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ hist, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ tile_start, int tile_m) {
   __shared__ int wsum[2][16];
+  __shared__ int s_cnt[MAX_EXPERTS];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int cnt = 0;
-  if (e < E) {
-    if (C == 1) {
-      cnt = counts[e];
-    } else {
+  if (C == 1 || ((E + 15) / 16) * ((C + 255) / 256) * 8 >= C) {  // (uniform)
+    if (e < E) {
+      if (C == 1) {
+        cnt = counts[e];
+      } else {
 #pragma unroll 8
-      for (int c = 0; c < C; c++) {  // chunk c's count -> routes of key e in chunks before c
-        const int h = hist[(int64_t)c * E + e];
-        hist[(int64_t)c * E + e] = cnt;
-        cnt += h;
+        for (int c = 0; c < C; c++) {
+          const int h = hist[(int64_t)c * E + e];
+          hist[(int64_t)c * E + e] = cnt;
+          cnt += h;
+        }
+        counts[e] = cnt;
       }
+    }
+  } else {
+    for (int key = wave; key < E; key += 16) {  // (uniform per wave)
+      int carry = 0;
+      for (int c0 = 0; c0 < C; c0 += 256) {
+        int h[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int c = c0 + 64 * j + lane;
+          h[j] = c < C ? hist[(int64_t)c * E + key] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          int v = h[j];  // inclusive prefix over the wave's 64 chunks
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(v, o, 64);
+            if (lane >= o) v += y;
+          }
+          const int c = c0 + 64 * j + lane;
+          if (c < C) hist[(int64_t)c * E + key] = carry + v - h[j];
+          carry += __shfl(v, 63, 64);
+        }
+      }
+      if (lane == 0) s_cnt[key] = carry;
+    }
+    __syncthreads();
+    if (e < E) {
+      cnt = s_cnt[e];
       counts[e] = cnt;
     }
   }

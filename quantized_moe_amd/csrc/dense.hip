@@ -34,19 +34,25 @@ namespace qmoe {
 
 namespace {
 
-// One wave per row of a Q8 matrix with K inputs (K / 32 blocks): lane l
-// takes blocks l, l + 64, ...
-__global__ __launch_bounds__(256) void dequant_q8_kernel(QMat m, int rows, uint16_t* __restrict__ out,
+// One launch for the three matrices: row r < f of gate, f + r of up and
+// 2f + r of down (the order of w_gu, w_dn and colsc), one wave per row.
+// Lane l takes the row's 16-byte code pieces l, l + 64, ... (half a block
+// each), so a wave reads 1 KB of codes and writes 2 KB of fp16 contiguously.
+__global__ __launch_bounds__(256) void dequant_q8_kernel(QMat gate, QMat up, QMat down, int f, int d,
+                                                         uint16_t* __restrict__ w_gu, uint16_t* __restrict__ w_dn,
                                                          float* __restrict__ colsc) {
   const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= rows) return;  // uniform per wave
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= 2 * f + d) return;  // uniform per wave
+  const QMat& m = r < f ? gate : (r < 2 * f ? up : down);
+  const int n = r < f ? r : (r < 2 * f ? r - f : r - 2 * f);
+  uint16_t* o = r < 2 * f ? w_gu + (int64_t)r * d : w_dn + (int64_t)(r - 2 * f) * f;
   const int nb = m.nb;
   const uint16_t* ds = reinterpret_cast<const uint16_t*>(m.p_scale) + (int64_t)n * nb;
   float dmax = 0.0f;
   for (int b = lane; b < nb; b += 64) dmax = fmaxf(dmax, fabsf(half_bits_to_float(ds[b])));
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, o, 64));
+  for (int s = 32; s >= 1; s >>= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, s, 64));
   int k = 0;
   const float mx = dmax * 128.0f;
   if (mx > 0.0f && mx <= 3.4e38f) {
@@ -54,28 +60,24 @@ __global__ __launch_bounds__(256) void dequant_q8_kernel(QMat m, int rows, uint1
     frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
     k = min(max(15 - ex, -100), 100);
   }
-  if (lane == 0) colsc[n] = __builtin_amdgcn_ldexpf(1.0f, -k);
-  for (int b = lane; b < nb; b += 64) {
-    const float d = __builtin_amdgcn_ldexpf(half_bits_to_float(ds[b]), k);
-    const int8_t* q = reinterpret_cast<const int8_t*>(m.p_a) + ((int64_t)n * nb + b) * 32;
-    uint16_t* o = out + (int64_t)n * m.K + 32 * b;
+  if (lane == 0) colsc[r] = __builtin_amdgcn_ldexpf(1.0f, -k);
+  const uint8_t* q = m.p_a + (int64_t)n * nb * 32;
+  for (int p = lane; p < 2 * nb; p += 64) {
+    const float sc = __builtin_amdgcn_ldexpf(half_bits_to_float(ds[p >> 1]), k);
+    const uint4 w = *reinterpret_cast<const uint4*>(q + 16 * p);
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[8];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const uint4 w = *reinterpret_cast<const uint4*>(q + 16 * u);
-      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-      uint32_t h[8];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float v0 = d * (float)(int8_t)(wv[i] & 255u), v1 = d * (float)(int8_t)((wv[i] >> 8) & 255u);
-        const float v2 = d * (float)(int8_t)((wv[i] >> 16) & 255u), v3 = d * (float)(int8_t)(wv[i] >> 24);
-        h[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
-        h[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
-      }
-      *reinterpret_cast<uint4*>(o + 16 * u) = make_uint4(h[0], h[1], h[2], h[3]);
-      *reinterpret_cast<uint4*>(o + 16 * u + 8) = make_uint4(h[4], h[5], h[6], h[7]);
+    for (int i = 0; i < 4; i++) {
+      const float v0 = sc * (float)(int8_t)(wv[i] & 255u), v1 = sc * (float)(int8_t)((wv[i] >> 8) & 255u);
+      const float v2 = sc * (float)(int8_t)((wv[i] >> 16) & 255u), v3 = sc * (float)(int8_t)(wv[i] >> 24);
+      h[2 * i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1) << 16);
+      h[2 * i + 1] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v2) |
+                     ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v3) << 16);
     }
+    *reinterpret_cast<uint4*>(o + 16 * p) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(o + 16 * p + 8) = make_uint4(h[4], h[5], h[6], h[7]);
   }
 }
 
@@ -202,11 +204,6 @@ hipError_t gemm_tn(int T, int N, int K, const uint16_t* A, const uint16_t* W, fl
   return blt_err(hipblasLtMatmul(h, p.md, &alpha, W, p.la, A, p.lb, &beta, D, p.ld, D, p.ld, &p.algo, nullptr, 0, s));
 }
 
-hipError_t dequant(const QMat& m, int rows, uint16_t* out, float* colsc, hipStream_t s) {
-  QMOE_LAUNCH(dequant_q8_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, m, rows, out, colsc);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 bool shared_dense_ready(int T, int d, int f, hipStream_t s) {
@@ -221,10 +218,10 @@ bool shared_dense_ready(int T, int d, int f, hipStream_t s) {
 
 hipError_t launch_shared_dense_gateup(const SharedDense& S, hipStream_t s) {
   int pid = prof_begin("prefill_shared_dequant", s);
-  hipError_t e = dequant(S.gate, S.f, S.w_gu, S.colsc, s);
-  if (e == hipSuccess) e = dequant(S.up, S.f, S.w_gu + (size_t)S.f * S.d, S.colsc + S.f, s);
-  if (e == hipSuccess) e = dequant(S.down, S.d, S.w_dn, S.colsc + 2 * S.f, s);
+  QMOE_LAUNCH(dequant_q8_kernel, dim3((2 * S.f + S.d + 3) / 4), dim3(256), 0, s, S.gate, S.up, S.down, S.f, S.d,
+              S.w_gu, S.w_dn, S.colsc);
   prof_end(pid, s);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   pid = prof_begin("prefill_shared_gateup", s);
   prof_library_call(s);

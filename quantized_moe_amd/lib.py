@@ -173,6 +173,9 @@ def route_topk(w_router, x, k, idx, wt, ws, stream=None, bias=None) -> None:
 
 def bucket(idx, E, counts, offsets, perm, pos, stream=None) -> None:
     T, k = idx.shape
+    for t, n, name in ((counts, E, "counts"), (offsets, E + 1, "offsets"), (perm, T * k, "perm"), (pos, T * k, "pos")):
+        if t.numel() < n:
+            raise ValueError(f"bucket: {name} holds {t.numel()} entries, needs {n}")
     _check(lib().moe_bucket(_ptr(idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(pos),
                             _stream(stream)))
 

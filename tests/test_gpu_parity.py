@@ -448,13 +448,15 @@ def test_route_topk_more_than_512_experts(T, k, E, dt):
 
 @pytest.mark.parametrize("T,k,E", [(1, 6, 384), (3, 2, 8), (1024, 6, 384), (4096, 6, 384), (50, 16, 17),
                                    (64, 16, 1000), (300, 6, 520), (2, 16, 1024),
-                                   (20000, 8, 64)])  # the most chunks (1024) of 157 routes
+                                   (20000, 8, 64),  # the most chunks (1024) of 157 routes
+                                   (4096, 2, 8), (3000, 4, 64), (256, 2, 8)])  # chunks scanned a wave at a time
 def test_bucket_bit_exact(T, k, E):
     rng = np.random.default_rng(T + k + E)
-    if T == 4096:
+    if (T, k, E) == (4096, 6, 384):  # the long-prefill routes
         idx, _ = synth.zipf_routes(0, T)
     else:
         idx = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    assert idx.shape == (T, k) and 0 <= idx.min() and idx.max() < E
     it = torch.from_numpy(idx).to(DEV)
     outs = [torch.empty(n, dtype=torch.int32, device=DEV) for n in (E, E + 1, T * k, T * k)]
     lib.bucket(it, E, *outs)

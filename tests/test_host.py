@@ -33,3 +33,18 @@ def test_traffic_is_reported_only_for_the_sources_it_was_measured_on(tmp_path, m
 def test_kernel_source_hash_is_stable():
     assert bench.kernel_source_hash() == bench.kernel_source_hash()
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_bucket_binding_refuses_short_buffers():
+    """The binding checks each output buffer against T*k and E before the
+    library sees it (a short perm or pos would take writes past its end)."""
+    import pytest
+    import torch
+    from quantized_moe_amd import lib
+    idx = torch.zeros((4, 2), dtype=torch.int32)
+    good = dict(counts=torch.empty(8, dtype=torch.int32), offsets=torch.empty(9, dtype=torch.int32),
+                perm=torch.empty(8, dtype=torch.int32), pos=torch.empty(8, dtype=torch.int32))
+    for name, n in (("counts", 7), ("offsets", 8), ("perm", 7), ("pos", 4)):
+        bad = dict(good, **{name: torch.empty(n, dtype=torch.int32)})
+        with pytest.raises(ValueError, match=name):
+            lib.bucket(idx, 8, bad["counts"], bad["offsets"], bad["perm"], bad["pos"])

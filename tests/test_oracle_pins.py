@@ -572,6 +572,13 @@ def test_bucket_matches_stable_argsort():
         assert np.array_equal(pos[perm], np.arange(T * k))
 
 
+def test_bucket_refuses_keys_out_of_range():
+    for bad in (8, -1):
+        idx = np.array([[0, 3], [bad, 1]], np.int32)
+        with pytest.raises(ValueError):
+            oracle.bucket(idx, 8)
+
+
 def test_bucket_mean_load_matches_closed_form():
     # T*k/E routed rows per expert on average: 8,192 tokens x 6 / 384 = 128,
     # the ~128 rows per expert the YoungAi page (section 4.2) quotes.
