@@ -120,11 +120,14 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ D
 
 // hipBLASLt: one handle per device, one plan (descriptors and the
 // heuristic's first algorithm) per device and shape, made on first use under
-// a lock and kept until the process ends.  Only algorithms that need no
-// workspace are taken: nothing is cleared between calls, the same bits come
-// back every call, and a captured graph holds nothing but kernel launches.
+// a lock and kept until the process ends; a shape the library has no
+// algorithm for is remembered as such (ok = false) and not asked again.
+// Only algorithms that need no workspace are taken: nothing is cleared
+// between calls, the same bits come back every call, and a captured graph
+// holds nothing but kernel launches.
 struct GemmPlan {
   int dev, T, N, K;
+  bool ok;
   hipblasLtMatmulDesc_t md;
   hipblasLtMatrixLayout_t la, lb, ld;
   hipblasLtMatmulAlgo_t algo;
@@ -141,6 +144,50 @@ const GemmPlan* find_plan(int dev, int T, int N, int K) {  // (under the lock)
   return nullptr;
 }
 
+// The descriptors and algorithm of D^T (N x T, column-major) = op(W) A^T,
+// with W given as K x N (transposed) and A^T as K x T: column-major views of
+// the row-major [N][K], [T][K] and [T][N] arrays.  p.ok = false when any
+// step fails (whatever was created is destroyed).
+void make_plan(hipblasLtHandle_t h, GemmPlan& p) {
+  p.ok = false;
+  p.md = nullptr;
+  p.la = p.lb = p.ld = nullptr;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  bool good = hipblasLtMatmulDescCreate(&p.md, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16F, p.K, p.N, p.K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16F, p.K, p.T, p.K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_32F, p.N, p.T, p.N) == HIPBLAS_STATUS_SUCCESS;
+  if (good) {
+    hipblasLtMatmulPreference_t pref = nullptr;
+    const uint64_t no_ws = 0;
+    hipblasLtMatmulHeuristicResult_t res[8];
+    int nres = 0;
+    good = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws,
+                                                 sizeof(no_ws)) == HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulAlgoGetHeuristic(h, p.md, p.la, p.lb, p.ld, p.ld, pref, 8, res, &nres) ==
+               HIPBLAS_STATUS_SUCCESS;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    for (int i = 0; good && i < nres && !p.ok; i++)
+      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize == 0) {
+        p.algo = res[i].algo;
+        p.ok = true;
+      }
+  }
+  if (!p.ok) {
+    if (p.ld) hipblasLtMatrixLayoutDestroy(p.ld);
+    if (p.lb) hipblasLtMatrixLayoutDestroy(p.lb);
+    if (p.la) hipblasLtMatrixLayoutDestroy(p.la);
+    if (p.md) hipblasLtMatmulDescDestroy(p.md);
+    p.md = nullptr;
+    p.la = p.lb = p.ld = nullptr;
+  }
+}
+
 hipError_t get_plan(int T, int N, int K, hipblasLtHandle_t* h_out, GemmPlan* p_out) {
   int dev = 0;
   if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
@@ -153,45 +200,19 @@ hipError_t get_plan(int T, int N, int K, hipblasLtHandle_t* h_out, GemmPlan* p_o
     g_handles.emplace_back(dev, h);
   }
   *h_out = h;
-  if (const GemmPlan* q = find_plan(dev, T, N, K)) {
-    *p_out = *q;
-    return hipSuccess;
+  const GemmPlan* q = find_plan(dev, T, N, K);
+  if (!q) {
+    GemmPlan p{};
+    p.dev = dev;
+    p.T = T;
+    p.N = N;
+    p.K = K;
+    make_plan(h, p);
+    g_plans.push_back(p);
+    q = &g_plans.back();
   }
-  // D^T (N x T, column-major) = op(W) * A^T with W given as K x N
-  // (transposed) and A^T as K x T: column-major views of the row-major
-  // [N][K], [T][K] and [T][N] arrays
-  GemmPlan p{};
-  p.dev = dev;
-  p.T = T;
-  p.N = N;
-  p.K = K;
-  hipblasStatus_t st;
-  if ((st = hipblasLtMatmulDescCreate(&p.md, HIPBLAS_COMPUTE_32F, HIP_R_32F)) != HIPBLAS_STATUS_SUCCESS)
-    return blt_err(st);
-  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-  if ((st = hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta))) ||
-      (st = hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb))) ||
-      (st = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16F, K, N, K)) ||
-      (st = hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16F, K, T, K)) ||
-      (st = hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_32F, N, T, N)))
-    return blt_err(st);
-  hipblasLtMatmulPreference_t pref;
-  if ((st = hipblasLtMatmulPreferenceCreate(&pref)) != HIPBLAS_STATUS_SUCCESS) return blt_err(st);
-  const uint64_t no_ws = 0;
-  hipblasLtMatmulHeuristicResult_t res[8];
-  int nres = 0;
-  st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &no_ws, sizeof(no_ws));
-  if (st == HIPBLAS_STATUS_SUCCESS)
-    st = hipblasLtMatmulAlgoGetHeuristic(h, p.md, p.la, p.lb, p.ld, p.ld, pref, 8, res, &nres);
-  hipblasLtMatmulPreferenceDestroy(pref);
-  if (st != HIPBLAS_STATUS_SUCCESS) return blt_err(st);
-  int best = -1;
-  for (int i = 0; i < nres && best < 0; i++)
-    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize == 0) best = i;
-  if (best < 0) return hipErrorNotSupported;
-  p.algo = res[best].algo;
-  g_plans.push_back(p);
-  *p_out = p;
+  if (!q->ok) return hipErrorNotSupported;
+  *p_out = *q;
   return hipSuccess;
 }
 
@@ -209,11 +230,17 @@ hipError_t gemm_tn(int T, int N, int K, const uint16_t* A, const uint16_t* W, fl
 bool shared_dense_ready(int T, int d, int f, hipStream_t s) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess) return false;
-  if (cs == hipStreamCaptureStatusNone) return true;
+  if (cs == hipStreamCaptureStatusNone) {  // make both plans now; none (no handle, no algorithm): grouped kernels
+    hipblasLtHandle_t h;
+    GemmPlan p;
+    return get_plan(dense_rows(T), 2 * f, d, &h, &p) == hipSuccess && get_plan(dense_rows(T), d, f, &h, &p) == hipSuccess;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> lk(g_blt_mu);
-  return find_plan(dev, dense_rows(T), 2 * f, d) && find_plan(dev, dense_rows(T), d, f);
+  const GemmPlan* gu = find_plan(dev, dense_rows(T), 2 * f, d);
+  const GemmPlan* dn = find_plan(dev, dense_rows(T), d, f);
+  return gu && gu->ok && dn && dn->ok;
 }
 
 hipError_t launch_shared_dense_gateup(const SharedDense& S, hipStream_t s) {

@@ -141,8 +141,10 @@ struct SharedDense {
   int8_t* hsexp;  // [T][f/64]: ... and its exponent
   float* ysh;     // [T][d]: before the row and column powers of two
 };
-// false under stream capture before the chunk size's GEMM plans exist
-// (making them may allocate): then the grouped kernels run the shared expert
+// Whether the dense path can run this chunk: outside stream capture it makes
+// the chunk size's two GEMM plans (false if the library offers no algorithm
+// or no handle); under capture it only looks them up (making them may
+// allocate).  false: the grouped kernels run the shared expert.
 bool shared_dense_ready(int T, int d, int f, hipStream_t s);
 hipError_t launch_shared_dense_gateup(const SharedDense& S, hipStream_t s);
 hipError_t launch_shared_dense_down(const SharedDense& S, hipStream_t s);
