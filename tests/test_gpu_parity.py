@@ -90,6 +90,7 @@ FORMAT_CASES = [
     (10, 2, 1024, 256, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_IQ2, 8, synth.F32),
     (10, 2, 1024, 256, synth.FMT_Q2K, synth.FMT_Q8, synth.FMT_IQ2, 65, synth.BF16),
     (8, 1, 8192, 256, synth.FMT_IQ2, synth.FMT_Q2K, None, 2, synth.F32),      # two chunks per lane (d)
+    (8, 2, 8192, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 70, synth.BF16),  # dense shared GEMMs, K = 8192
     (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 2, synth.F32),  # two chunks per lane (f)
     (8, 2, 256, 8192, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 20, synth.BF16),
     (16, 16, 256, 256, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8, 4, synth.F32),  # k = E
