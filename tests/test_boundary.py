@@ -221,6 +221,22 @@ def test_workspace_sizes_cover_their_buffers():
     assert lib.workspace_bytes(layer, 1, lib.MOE_OP_LAYER) >= lib.workspace_bytes(layer, 1, lib.MOE_OP_DECODE)
 
 
+def test_prefill_workspace_counts_the_dense_shared_expert():
+    """A Q8 shared expert on the prefill path runs as dense GEMMs on fp16
+    copies of its three matrices (2 * 3 * d * f bytes), fp32 gate/up outputs
+    and operands on the token count rounded up to 64 rows; other shared
+    formats need none of that."""
+    d, f = 4096, 2048
+    for T in (1, 100, 1024):
+        Tg = (T + 63) // 64 * 64
+        q8 = lib.workspace_bytes(_layer(), T, lib.MOE_OP_PREFILL)
+        q2k = lib.workspace_bytes(_layer(fmt_shared=2), T, lib.MOE_OP_PREFILL)
+        extra = 6 * d * f + Tg * 2 * f * 4 + (2 * f + d) * 4 + (Tg - T) * (d * 2 + f * 2 + d * 4)
+        assert extra <= q8 - q2k <= extra + 16 * 256, (T, q8 - q2k, extra)
+        assert lib.workspace_bytes(_layer(fmt_shared=2), T, lib.MOE_OP_PREFILL) == \
+            lib.workspace_bytes(_layer(fmt_shared=1), T, lib.MOE_OP_PREFILL)
+
+
 def test_route_and_bucket_validation():
     L = lib.lib()
     assert L.moe_route_topk(256, None, 384, 4096, 512, 0, 1, 0, 768, 1024, 1280, 1 << 20, None) == lib.MOE_ERR_INVALID_ARG
