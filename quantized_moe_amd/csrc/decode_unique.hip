@@ -144,8 +144,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) {
 // The last launch over the distinct experts (d_ff <= 2048); FS is the shared
 // expert's format.  8 waves: a routed task is 16 rows of one expert, a shared
 // task 8 rows.  Where its rows' codes take at most 64 registers a task keeps
-// them while it runs its routes; otherwise it requests them again per route
-// (L2-resident after the first).
+// them while it runs its routes, and requests all of them at once (one load
+// round per task: a wave runs several tasks one after the other); otherwise
+// it requests them again per route (L2-resident after the first), a few
+// steps ahead.
 constexpr int K3U_WAVES = 8;
 template <int FMT, int K, int ROWS>
 constexpr bool keep_codes() {
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * K3U_WAVES) void k3u_kernel(DecodeArgs a) {
       const float* gain = a.down_gain ? a.down_gain + (int64_t)e * a.d : nullptr;
       constexpr int NS = DownRows<FR, F, RT_ROWS, 1>::NS;
       constexpr int CPL = Geo<FR, F>::CPL;
-      constexpr int PDMAX = FR == FMT_Q4K || FR == FMT_MX4 ? (CPL > 1 ? 1 : 2) : 3;
+      constexpr int PDMAX = keep_codes<FR, F, RT_ROWS>() ? NS : (FR == FMT_Q4K || FR == FMT_MX4 ? (CPL > 1 ? 1 : 2) : 3);
       using DR = DownRows<FR, F, RT_ROWS, (NS < PDMAX ? NS : PDMAX)>;
       uint8_t* my_scales = s_scl + wave * SCL_BYTES;
       if constexpr (keep_codes<FR, F, RT_ROWS>()) {
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * K3U_WAVES) void k3u_kernel(DecodeArgs a) {
     } else {
       const int part = task - n_rt;
       constexpr int NS = DownRows<FS, F, SH_ROWS, 1>::NS;
-      constexpr int PDMAX = 3;
+      constexpr int PDMAX = keep_codes<FS, F, SH_ROWS>() ? NS : 3;
       using DR = DownRows<FS, F, SH_ROWS, (NS < PDMAX ? NS : PDMAX)>;
       uint8_t* my_scales = s_scl + wave * SCL_BYTES;
       if constexpr (keep_codes<FS, F, SH_ROWS>()) {
