@@ -166,8 +166,11 @@
  * Conventions for every entry point:
  *   - Every pointer is a DEVICE pointer unless its comment says [host].
  *     moe_layer descriptors are [host] structs read only during the call.
- *   - The caller owns every buffer.  The library never allocates, frees or
- *     keeps device memory, and retains no pointer after a call returns.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     for a call's data and retains no pointer after a call returns; what it
+ *     keeps until the process ends is the fixed scratch array of
+ *     moe_layer_forward_noalloc and the GEMM library's handle and plans of
+ *     the dense shared expert (moe_expert_ffn_prefill), made on first use.
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
  *     MOE_OK means "validated and enqueued on stream", not "finished".  A
  *     kernel fault surfaces at the caller's next synchronisation.
@@ -176,7 +179,10 @@
  *     message (thread-local, valid until the next call on that thread).
  *   - T = 0 is a valid no-op for every entry point that takes T.
  *   - Identical inputs give bitwise identical outputs (no floating-point
- *     atomics anywhere; every reduction has a fixed order).
+ *     atomics anywhere; every reduction has a fixed order).  One exception:
+ *     a prefill call with a Q8 shared expert recorded under stream capture
+ *     before its chunk size's GEMM plans exist runs that expert on the
+ *     grouped kernels (other rounding, the same accuracy).
  *   - Size limits: 1 <= n_experts <= 1024; 1 <= top_k <= min(n_experts, 16);
  *     d_model and d_ff are powers of two in [256, 8192]; 0 <= T <= 65536.
  *     Pointers must be 16-byte aligned (torch allocations are 256-byte).
