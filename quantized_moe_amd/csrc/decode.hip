@@ -1,15 +1,18 @@
 // Decode path launcher: three launches per layer (or per set of given routes).
 //
 //   1. router logits (when routing is fused), x quantized for the gate/up
-//      rows, and (more than one token) the shared expert's gate/up + SwiGLU;
+//      rows, and (more than one token, VQ formats) the shared expert's
+//      gate/up + SwiGLU;
 //   2. exact top-k, routed gate/up + SwiGLU, routed h quantized in groups of
 //      16, and (one token) the shared expert's gate/up + SwiGLU, which
 //      streams while the blocks wait for the router logits and the top-k;
 //   3. routed and shared down projections and the fixed-order combine.
 //
-// With several tokens (block formats) a small planning launch between 1 and
-// 2 takes the top-k and lists the distinct experts, and 2 and 3 run over
-// those experts (decode_unique.hip).
+// With several tokens (block formats) a planning launch between 1 and 2
+// takes the top-k and lists the distinct experts in one block while its
+// other blocks run the tokens' shared gate/up (and, with the caller's
+// routes, quantize x, so that launch 1 is not needed), and 2 and 3 run over
+// those experts (decode_unique.hip, decode_plan.hpp).
 //
 // The kernels are in decode_k1/k2/k3.hip; their common pieces (activation
 // fixed point, IQ2 nibble table, weight pieces, dot products) in
@@ -22,6 +25,7 @@ hipError_t launch_k1(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_la
 hipError_t launch_k2(const DecodeArgs& a, int fmt, int fs, int gcnt, int blocks, int down_layout, hipStream_t s);
 hipError_t launch_k3(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_plan_shared(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_layout, hipStream_t s);
 hipError_t launch_k3u(const DecodeArgs& a, int fmt_down, int fmt_shared, hipStream_t s);
 }  // namespace dec
 
@@ -140,15 +144,20 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   int ncu = 256;
   if (hipError_t e = cu_count(&ncu); e != hipSuccess) return e;
 
+  // Several tokens (block formats) take the planning launch, which also runs
+  // their shared gate/up (plan_shared_kernel); otherwise the first launch
+  // does (more than one token) or the second (one token).
+  const bool plan_path = L.T >= 2 && !is_vq(L.fmt_gate_up);
+  const int pw_s = fs == FMT_Q8 ? 16 : 64;
+  const int rps_s = L.d / pw_s >= 64 ? 1 : 64 / (L.d / pw_s);
+  const int64_t sb = 2 * rps_s * row_bytes(fs, L.d);  // bytes of one shared gate/up step
   // launch 1: router blocks of epb experts, shared blocks of spb steps, all
   // streaming about the same bytes
   K1Plan pl{};
   {
     const int n_router = L.fused_topk ? L.E : 0;
-    const int pw_s = fs == FMT_Q8 ? 16 : 64;
-    const int rps_s = L.d / pw_s >= 64 ? 1 : 64 / (L.d / pw_s);
-    pl.n_steps = L.has_shared && !a.shared_k2 ? L.f / rps_s : 0;
-    const int64_t rb = (int64_t)L.d * 4, sb = 2 * rps_s * row_bytes(fs, L.d);
+    pl.n_steps = L.has_shared && !a.shared_k2 && !plan_path ? L.f / rps_s : 0;
+    const int64_t rb = (int64_t)L.d * 4;
     const int64_t total = n_router * rb + (int64_t)pl.n_steps * sb;
     int64_t nb = total / (32 << 10);
     nb = nb < 1 ? 1 : (nb > ncu ? ncu : nb);
@@ -170,7 +179,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
     const int n_oct = (L.T * (L.d / 64) + 7) / 8;
     pl.n_xb = pl.n_rb == 0 ? (n_oct + WAVES - 1) / WAVES : 0;
   }
-  {
+  // (several tokens with the caller's routes: the planning launch also
+  // quantizes x, and there is no first launch)
+  const bool merged = plan_path && !L.fused_topk;
+  if (!merged) {
     const int pid = prof_begin("decode_router", s);
     hipError_t e = launch_k1(a, pl, fs, nib_layout(L.fmt_gate_up), s);
     prof_end(pid, s);
@@ -180,10 +192,27 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   // Several tokens (block formats): the top-k and the distinct experts in a
   // small launch of their own, then gate/up and down over the distinct
   // experts, each expert's codes loaded once for all its routes.
-  if (L.T >= 2 && !is_vq(L.fmt_gate_up)) {
+  if (plan_path) {
     {
+      hipError_t e;
       const int pid = prof_begin("decode_plan", s);
-      hipError_t e = launch_plan(a, s);
+      if (L.has_shared || merged) {
+        // block 0 the plan; then the shared gate/up blocks, about 32 KB of
+        // weights each; then (merged) the x blocks
+        K1Plan ps{};
+        ps.n_rb = 1;
+        if (L.has_shared) {
+          ps.n_steps = L.f / rps_s;
+          int64_t nb = (int64_t)ps.n_steps * sb / (32 << 10);
+          nb = nb < 1 ? 1 : (nb > ncu ? ncu : nb);
+          ps.spb = (int)((ps.n_steps + nb - 1) / nb);
+          ps.n_sb = (ps.n_steps + ps.spb - 1) / ps.spb;
+        }
+        ps.n_xb = merged ? pl.n_xb : 0;
+        e = launch_plan_shared(a, ps, fs, nib_layout(L.fmt_gate_up), s);
+      } else {
+        e = launch_plan(a, s);
+      }
       prof_end(pid, s);
       if (e != hipSuccess) return e;
     }

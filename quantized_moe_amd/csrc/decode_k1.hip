@@ -1,7 +1,9 @@
 // First decode launch: router logits, x quantized for the gate/up rows, and
-// (for more than one token) the shared expert's gate/up + SwiGLU: everything
-// that depends on x alone.  A single token's shared gate/up runs in the
-// second launch instead, in the time its blocks wait for the routes.
+// (more than one token, VQ formats) the shared expert's gate/up + SwiGLU:
+// everything that depends on x alone.  A single token's shared gate/up runs
+// in the second launch instead, in the time its blocks wait for the routes;
+// several tokens of the block formats run it in the planning launch
+// (plan_shared_kernel below), beside the plan's single block.
 //
 // Blocks [0, n_rb) are router blocks: one expert per wave.  Blocks
 // [n_rb, n_rb + n_sb) are shared-expert blocks: each takes spb consecutive
@@ -11,7 +13,7 @@
 // registers, with no barrier between tokens.
 // epb and spb are chosen by the host so that all blocks stream about the same
 // number of bytes.
-#include "decode_rows.hpp"
+#include "decode_plan.hpp"
 
 namespace qmoe {
 namespace dec {
@@ -32,44 +34,24 @@ __device__ __forceinline__ void load_x_act(typename RoutedAct<FMT, D>::type& act
 // Dynamic LDS of the shared blocks for T tokens.
 __host__ __device__ constexpr int k1_x_lds_bytes(int T, int D) { return T * (D / 64) * (CHUNK_BYTES + 4); }
 
+// Static LDS of a shared gate/up block: the IQ2 nibble table and the
+// waves' staged scale bytes.
 template <int FMT_S, int D>
-__global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, int gu_layout) {
-  __shared__ Iq2Tab itab;
-  extern __shared__ __align__(16) uint8_t k1_dyn[];  // shared blocks: x chunks [T][D/64], then scales [T][D/64]
-  constexpr int SCL_BYTES =
-      RowScales<FMT_S, D>::STAGE ? 4 * Geo<FMT_S, D>::RPS * RowScales<FMT_S, D>::BYTES : 16;
-  __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * SCL_BYTES];
-  const int b = blockIdx.x;
+constexpr int k1_scl_bytes() {
+  return RowScales<FMT_S, D>::STAGE ? 4 * Geo<FMT_S, D>::RPS * RowScales<FMT_S, D>::BYTES : 16;
+}
+
+// Shared gate/up block b of a launch whose plan pl lists pl.n_rb other
+// blocks first (router or plan blocks): waves take steps s_lo + wave,
+// s_lo + wave + 8 (two per round).  The scale bytes and weights of the first
+// round are requested, then every token's x is quantized into LDS ((token,
+// octet) items over the waves); one barrier; then every token runs against
+// the round's weights.
+template <int FMT_S, int D>
+__device__ __forceinline__ void k1_shared_block(const DecodeArgs& a, const K1Plan& pl, int b, Iq2Tab& itab,
+                                                uint8_t* s_scl, uint8_t* k1_dyn) {
+  constexpr int SCL_BYTES = k1_scl_bytes<FMT_S, D>();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nch_all = a.T * (D / 64);       // x chunks of all tokens, for the routed gate/up
-  const int n_oct = (nch_all + 7) / 8;      // ... in octets, one per wave call
-  if (b < pl.n_rb || b >= pl.n_rb + pl.n_sb) {  // a router block, or an x block
-    int first = -1, stride = 1;
-    if (b < pl.n_rb) {
-      if (wave < pl.epb) {
-        const int e = b * pl.epb + wave;
-        if (e < a.E) router_item<D>(a, e);
-      } else if (wave == WAVES - 1) {  // the last wave quantizes x
-        first = b;
-        stride = pl.n_rb;
-      }
-    } else {  // x blocks: every wave an octet
-      first = (b - pl.n_rb - pl.n_sb) * WAVES + wave;
-      stride = pl.n_xb * WAVES;
-    }
-    if (first >= 0) {
-      for (int o = first; o < n_oct; o += stride) {
-        quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
-        if (a.shared_k2) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
-      }
-    }
-    return;
-  }
-  // shared-expert block: waves take steps s_lo + wave, s_lo + wave + 8 (two
-  // per round).  The scale bytes and weights of the first round are
-  // requested, then every token's x is quantized into LDS ((token, octet)
-  // items over the waves); one barrier; then every token runs against the
-  // round's weights.
   using G = Geo<FMT_S, D>;
   constexpr int NOCT = (D / 64 + 7) / 8;    // octets of chunks of one token
   uint8_t* s_xq = k1_dyn;                                                          // [T][D/64][128]
@@ -151,6 +133,64 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
 }
 
 template <int FMT_S, int D>
+__global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, int gu_layout) {
+  __shared__ Iq2Tab itab;
+  extern __shared__ __align__(16) uint8_t k1_dyn[];  // shared blocks: x chunks [T][D/64], then scales [T][D/64]
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * k1_scl_bytes<FMT_S, D>()];
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int nch_all = a.T * (D / 64);       // x chunks of all tokens, for the routed gate/up
+  const int n_oct = (nch_all + 7) / 8;      // ... in octets, one per wave call
+  if (b < pl.n_rb || b >= pl.n_rb + pl.n_sb) {  // a router block, or an x block
+    int first = -1, stride = 1;
+    if (b < pl.n_rb) {
+      if (wave < pl.epb) {
+        const int e = b * pl.epb + wave;
+        if (e < a.E) router_item<D>(a, e);
+      } else if (wave == WAVES - 1) {  // the last wave quantizes x
+        first = b;
+        stride = pl.n_rb;
+      }
+    } else {  // x blocks: every wave an octet
+      first = (b - pl.n_rb - pl.n_sb) * WAVES + wave;
+      stride = pl.n_xb * WAVES;
+    }
+    if (first >= 0) {
+      for (int o = first; o < n_oct; o += stride) {
+        quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
+        if (a.shared_k2) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
+      }
+    }
+    return;
+  }
+  k1_shared_block<FMT_S, D>(a, pl, b, itab, s_scl, k1_dyn);
+}
+
+// Several tokens: block 0 takes the plan (decode_plan.hpp) while blocks
+// 1 .. n_sb run the tokens' shared gate/up, whose weights do not depend on
+// the routes, and (routes given by the caller, so no router launch before
+// this one) the last n_xb blocks quantize x for the routed gate/up, one
+// octet of chunks per wave.  The plan alone would leave every other CU idle.
+template <int FMT_S, int D>
+__global__ __launch_bounds__(THREADS) void plan_shared_kernel(DecodeArgs a, K1Plan pl, int gu_layout) {
+  __shared__ Iq2Tab itab;
+  extern __shared__ __align__(16) uint8_t k1_dyn[];  // shared blocks: x chunks [T][D/64], then scales [T][D/64]
+  __shared__ __attribute__((aligned(16))) uint8_t s_scl[WAVES * k1_scl_bytes<FMT_S, D>()];
+  const int b = blockIdx.x;
+  if (b == 0) {
+    plan_block(a);
+    return;
+  }
+  if (b >= pl.n_rb + pl.n_sb) {
+    const int nch_all = a.T * (D / 64), n_oct = (nch_all + 7) / 8;
+    for (int o = (b - pl.n_rb - pl.n_sb) * WAVES + (threadIdx.x >> 6); o < n_oct; o += pl.n_xb * WAVES)
+      quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
+    return;
+  }
+  k1_shared_block<FMT_S, D>(a, pl, b, itab, s_scl, k1_dyn);
+}
+
+template <int FMT_S, int D>
 static hipError_t run_k1(const DecodeArgs& a, const K1Plan& pl, int gu_layout, hipStream_t s) {
   const int dyn = pl.n_sb > 0 ? k1_x_lds_bytes(a.T, D) : 0;
   if (dyn > 0) {  // (raises the kernel's dynamic-LDS limit on first use)
@@ -162,6 +202,41 @@ static hipError_t run_k1(const DecodeArgs& a, const K1Plan& pl, int gu_layout, h
   }
   QMOE_LAUNCH((k1_kernel<FMT_S, D>), dim3(pl.n_rb + pl.n_sb + pl.n_xb), dim3(THREADS), dyn, s, a, pl, gu_layout);
   return hipGetLastError();
+}
+
+template <int FMT_S, int D>
+static hipError_t run_plan_shared(const DecodeArgs& a, const K1Plan& pl, int gu_layout, hipStream_t s) {
+  const int dyn = pl.n_sb > 0 ? k1_x_lds_bytes(a.T, D) : 0;
+  if (dyn > 0) {  // (raises the kernel's dynamic-LDS limit on first use)
+    int per_cu = 0, n_cus = 0;
+    if (hipError_t e = launch_shape((const void*)plan_shared_kernel<FMT_S, D>, THREADS, dyn,
+                                    k1_x_lds_bytes(DECODE_MAX_T, D), &per_cu, &n_cus);
+        e != hipSuccess)
+      return e;
+  }
+  QMOE_LAUNCH((plan_shared_kernel<FMT_S, D>), dim3(pl.n_rb + pl.n_sb + pl.n_xb), dim3(THREADS), dyn, s, a, pl,
+              gu_layout);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t run_plan_shared_f(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gl, hipStream_t s) {
+  switch (fmt_s) {
+    case FMT_IQ2: return run_plan_shared<FMT_IQ2, D>(a, pl, gl, s);
+    case FMT_Q2K: return run_plan_shared<FMT_Q2K, D>(a, pl, gl, s);
+    default: return run_plan_shared<FMT_Q8, D>(a, pl, gl, s);
+  }
+}
+
+hipError_t launch_plan_shared(const DecodeArgs& a, const K1Plan& pl, int fmt_s, int gu_layout, hipStream_t s) {
+  switch (a.d) {
+    case 256: return run_plan_shared_f<256>(a, pl, fmt_s, gu_layout, s);
+    case 512: return run_plan_shared_f<512>(a, pl, fmt_s, gu_layout, s);
+    case 1024: return run_plan_shared_f<1024>(a, pl, fmt_s, gu_layout, s);
+    case 2048: return run_plan_shared_f<2048>(a, pl, fmt_s, gu_layout, s);
+    case 4096: return run_plan_shared_f<4096>(a, pl, fmt_s, gu_layout, s);
+    default: return run_plan_shared_f<8192>(a, pl, fmt_s, gu_layout, s);
+  }
 }
 
 template <int D>

@@ -7,12 +7,14 @@
 // expert x rows) that reads each chosen expert's bits once; section 2.2
 // counts 6 / 10 / 13.3 / 17.4 / 21.7 distinct experts for 1 .. 5 consecutive
 // tokens, so a small batch reads far fewer expert bytes than its tokens
-// times six.  Here, after the first launch (router logits, x quantized, the
-// shared expert's gate/up for every token):
+// times six.  Here, after the first launch (router logits, x quantized;
+// none with the caller's routes):
 //
-//   plan   one block: the exact top-k of every token (as the one-token path
-//          does it), then the list of distinct experts in increasing id and,
-//          for each, its routes r = t k + j in increasing r;
+//   plan   one block (decode_plan.hpp): the exact top-k of every token (as
+//          the one-token path does it), then the list of distinct experts in
+//          increasing id and, for each, its routes r = t k + j in increasing
+//          r; the same launch's other blocks run every token's shared gate/up
+//          and, with the caller's routes, quantize x (decode_k1.hip);
 //   gate/up  the one-token kernel, per token, reading the plan's routes (a
 //          version over (distinct expert, rows) that loaded each block's
 //          codes once for all its routes was slower: 80 against 54 us for 8
@@ -26,120 +28,12 @@
 // Every row result is computed by the same instructions on the same inputs
 // as in the one-token path, so the output does not depend on the batch
 // (bitwise).
-#include "decode_rows.hpp"
-#include "topk.hpp"
+#include "decode_plan.hpp"
 
 namespace qmoe {
 namespace dec {
 
-constexpr int PLAN_THREADS = 1024;
-constexpr int MAX_ROUTES = DECODE_MAX_T * TOPK_MAX_K;
-
-// plan layout in the workspace (int32): [0] = U, [1, 1 + umax) distinct
-// experts, [1 + umax, 2 + 2 umax) their first route slot (U + 1 entries),
-// [2 + 2 umax, 2 + 2 umax + T k) the routes grouped by expert
-struct PlanView {
-  int* n;
-  int* uexp;
-  int* uoff;
-  int* uroute;
-};
-__device__ __forceinline__ PlanView plan_view(const DecodeArgs& a) {
-  PlanView p;
-  p.n = a.plan;
-  p.uexp = a.plan + 1;
-  p.uoff = a.plan + 1 + a.umax;
-  p.uroute = a.plan + 2 + 2 * a.umax;
-  return p;
-}
-
-__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) {
-  __shared__ int s_sel[MAX_ROUTES];
-  __shared__ float s_zs[MAX_ROUTES];
-  __shared__ int s_rank[MAX_EXPERTS];  // 1 for a chosen expert, then its rank among the chosen
-  __shared__ int s_wsum[PLAN_THREADS / 64];
-  __shared__ int s_cnt[MAX_ROUTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = a.T * a.k;
-  // ---- routes: the top-k of each token, one wave per token ----
-  for (int t = wave; t < a.T; t += PLAN_THREADS / 64) {
-    if (a.fused_topk) {
-      if (a.router_bias)
-        wave_topk(a.zkey + (int64_t)t * a.E, a.E, a.k, s_sel + t * a.k, s_zs + t * a.k, nullptr,
-                  a.z + (int64_t)t * a.E);
-      else
-        wave_topk(a.z + (int64_t)t * a.E, a.E, a.k, s_sel + t * a.k, s_zs + t * a.k, nullptr);
-    } else if (lane < a.k) {
-      s_sel[t * a.k + lane] = a.idx[(int64_t)t * a.k + lane];
-    }
-  }
-  for (int e = tid; e < a.E; e += PLAN_THREADS) s_rank[e] = 0;
-  for (int i = tid; i < MAX_ROUTES; i += PLAN_THREADS) s_cnt[i] = 0;
-  __syncthreads();
-  if (a.fused_topk) {  // publish the routes and mixing weights
-    for (int t = wave; t < a.T; t += PLAN_THREADS / 64) {
-      const float w = topk_weight_lane(s_zs + t * a.k, a.k);
-      if (lane < a.k) {
-        const int64_t o = (int64_t)t * a.k + lane;
-        a.idx[o] = s_sel[o];
-        a.wt[o] = w;
-        if (a.idx_out) a.idx_out[o] = s_sel[o];
-        if (a.wt_out) a.wt_out[o] = w;
-      }
-    }
-  }
-  // ---- distinct experts (an out-of-range id, a caller error, has none) ----
-  if (tid < R) {
-    const int e = s_sel[tid];
-    if ((unsigned)e < (unsigned)a.E) s_rank[e] = 1;
-  }
-  __syncthreads();
-  // exclusive scan of the flags over the E <= 1024 experts: one per thread
-  const int f = tid < a.E ? s_rank[tid] : 0;
-  int incl = f;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int v = __shfl_up(incl, s, 64);
-    if (lane >= s) incl += v;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; w++) before += s_wsum[w];
-  int total = 0;
-  for (int w = 0; w < PLAN_THREADS / 64; w++) total += s_wsum[w];
-  const PlanView P = plan_view(a);
-  __syncthreads();  // every flag read before the ranks overwrite them
-  if (tid < a.E && f) {
-    const int rank = before + incl - 1;
-    s_rank[tid] = rank;
-    P.uexp[rank] = tid;
-  }
-  if (tid == 0) P.n[0] = total;
-  __syncthreads();
-  // routes per distinct expert, then the routes grouped, in increasing r
-  int pos = 0, u = -1;
-  if (tid < R) {
-    const int e = s_sel[tid];
-    if ((unsigned)e < (unsigned)a.E) {
-      u = s_rank[e];
-      for (int r = 0; r < tid; r++) pos += s_sel[r] == e;
-      atomicAdd(&s_cnt[u], 1);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int off = 0;
-    for (int v = 0; v < total; v++) {
-      P.uoff[v] = off;
-      off += s_cnt[v];
-    }
-    P.uoff[total] = off;
-    for (int v = 0; v < total; v++) s_cnt[v] = P.uoff[v];  // (re-read below as first slots)
-  }
-  __syncthreads();
-  if (u >= 0) P.uroute[s_cnt[u] + pos] = tid;
-}
+__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(DecodeArgs a) { plan_block(a); }
 
 // The last launch over the distinct experts (d_ff <= 2048); FS is the shared
 // expert's format.  8 waves: a routed task is 16 rows of one expert, a shared
