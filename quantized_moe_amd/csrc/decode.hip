@@ -134,6 +134,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
   a.xq_s = q + W.xq_s;
   a.xs_s = reinterpret_cast<float*>(q + W.xs_s);
   a.shared_k2 = L.has_shared && L.T == 1;
+  // several tokens with routing in the first launch: that launch quantizes x
+  // for the shared gate/up too, which the planning launch's blocks copy
+  a.xs_global = L.has_shared && L.T >= 2 && !is_vq(L.fmt_gate_up) && L.fused_topk;
   a.hsh = reinterpret_cast<float*>(q + W.hsh);
   a.hq = q + W.hq;
   a.hs = reinterpret_cast<float*>(q + W.hs);

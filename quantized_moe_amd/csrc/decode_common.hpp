@@ -928,6 +928,8 @@ struct DecodeArgs {
   uint8_t* xq_s;     // [T][d/64] x in the shared gate/up format's layout (when shared_k2)
   float* xs_s;       // [T][d/64]
   int shared_k2;     // the shared gate/up runs in the second launch (one token), not the first
+  int xs_global;     // (several tokens) the first launch also quantizes x into xq_s / xs_s, which the
+                     // shared gate/up blocks then copy instead of quantizing x themselves
   const float* router_bias;  // nullable [E]: selection on sigmoid32(z) + bias
   float* zkey;               // [T][E] the selection keys (fused routing with a bias), from the first launch
   const float* down_gain;    // nullable [E][d]: per-channel gains of the routed outputs

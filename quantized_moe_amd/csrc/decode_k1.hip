@@ -119,12 +119,19 @@ __device__ __forceinline__ void k1_shared_block(const DecodeArgs& a, const K1Pla
     issue(1, base);
     if constexpr (STAGE) ss.store(my_scales);
     if (base == s_lo) {
-      for (int item = wave; item < a.T * NOCT; item += WAVES) {
-        const int t = item / NOCT, o = item % NOCT;
-        XOctet xo;
-        xo.load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
-                D / 64, 8 * o, nib_layout(FMT_S));
-        xo.store(D / 64, s_xq + (size_t)t * (D / 64) * CHUNK_BYTES, s_xs + (size_t)t * (D / 64), nib_layout(FMT_S));
+      if (a.xs_global) {  // quantized by the first launch (the same chunks, the same layout): copied
+        const int n16 = a.T * (D / 64) * (CHUNK_BYTES / 16);
+        for (int i = threadIdx.x; i < n16; i += THREADS)
+          reinterpret_cast<uint4*>(s_xq)[i] = reinterpret_cast<const uint4*>(a.xq_s)[i];
+        for (int i = threadIdx.x; i < a.T * (D / 64); i += THREADS) s_xs[i] = a.xs_s[i];
+      } else {
+        for (int item = wave; item < a.T * NOCT; item += WAVES) {
+          const int t = item / NOCT, o = item % NOCT;
+          XOctet xo;
+          xo.load(static_cast<const uint8_t*>(a.x) + (int64_t)t * D * (a.x_dtype == X_BF16 ? 2 : 4), a.x_dtype,
+                  D / 64, 8 * o, nib_layout(FMT_S));
+          xo.store(D / 64, s_xq + (size_t)t * (D / 64) * CHUNK_BYTES, s_xs + (size_t)t * (D / 64), nib_layout(FMT_S));
+        }
       }
       __syncthreads();
     }
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(THREADS) void k1_kernel(DecodeArgs a, K1Plan pl, in
     if (first >= 0) {
       for (int o = first; o < n_oct; o += stride) {
         quant_x8(a.x, a.x_dtype, nch_all, 8 * o, gu_layout, a.xq, a.xs);
-        if (a.shared_k2) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
+        if (a.shared_k2 || a.xs_global) quant_x8(a.x, a.x_dtype, nch_all, 8 * o, nib_layout(FMT_S), a.xq_s, a.xs_s);
       }
     }
     return;
