@@ -69,7 +69,8 @@ __device__ __forceinline__ void k1_shared_block(const DecodeArgs& a, const K1Pla
   auto issue = [&](int i, int base) {
     const int s = base + wave + WAVES * i;
     st[i] = s;
-    const uint32_t n = (uint32_t)((s < s_hi ? s : s_lo) * G::RPS + sub);
+    if (s >= s_hi) return;  // (uniform per wave) no step: compute skips it too
+    const uint32_t n = (uint32_t)(s * G::RPS + sub);
 #pragma unroll
     for (int k = 0; k < G::CPL; k++) {
       wg[i][k].template load<G::NB>(Gp, n, c + G::LPR * k);
@@ -94,6 +95,7 @@ __device__ __forceinline__ void k1_shared_block(const DecodeArgs& a, const K1Pla
     load_x_act<FMT_S, D>(act, s_xq + (size_t)t * (D / 64) * CHUNK_BYTES, s_xs + (size_t)t * (D / 64));
 #pragma unroll
     for (int i = 0; i < 2; i++) {
+      if (st[i] >= s_hi) continue;  // (uniform per wave) a step past the block's share: nothing to compute
       if constexpr (STAGE) {
 #pragma unroll
         for (int k = 0; k < G::CPL; k++) {
