@@ -662,6 +662,30 @@ def test_small_batch_both_paths(decode_layer):
     assert rel_l2(y_dec, y_ref) <= REL_L2
 
 
+@pytest.mark.parametrize("fsh", [None, synth.FMT_IQ2, synth.FMT_Q2K, synth.FMT_Q8])
+def test_decode_caller_routes_several_tokens(fsh):
+    """The decode path with the caller's routes and several tokens runs no
+    first launch: the planning launch's blocks take the plan, the shared
+    gate/up (when there is a shared expert) and the x quantization.  Every
+    row equals the one-token call's bit for bit, and the oracle's to the bar;
+    with and without a shared expert, in each shared format."""
+    spec = synth.scaled_spec(E=24, k=4, d=1024, f=512, has_shared=fsh is not None, fmt_shared=fsh or synth.FMT_Q8)
+    L = synth.random_layer(spec, seed=71, workload="caller_routes")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    T = 7
+    rng = np.random.default_rng(71)
+    idx = np.stack([rng.choice(spec.E, spec.k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[4] = idx[2]  # a repeated route set: the same experts twice
+    wt = rng.dirichlet(np.ones(spec.k), T).astype(np.float32)
+    x = synth.activations(71, ("caller_routes", "x"), T, spec.d, synth.BF16)
+    y = run_ffn(dl, x, synth.BF16, idx, wt, lib.MOE_PATH_DECODE)
+    for t in range(T):
+        y1 = run_ffn(dl, x[t:t + 1], synth.BF16, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
+        assert np.array_equal(y1[0], y[t]), t
+    y_ref = oracle.ffn(L, x, oracle.BF16, idx, wt)
+    assert per_token_rel_l2(y, y_ref).max() <= REL_L2
+
+
 def test_decode_batch_invariance(decode_layer):
     """Decode rows of a batch equal separate single-row calls, bit for bit."""
     L, dl = decode_layer
