@@ -65,10 +65,14 @@ DecodeWsLayout ws_layout(int T, int k, int d, int f) {
 }
 
 // Groups of 16 routed h rows per gate/up block: GCNT minimises (rounds of
-// blocks) x (work per block), blocks never straddling a token.
-int gcnt_of(int k, int f, int T, int ncu) {
+// blocks) x (work per block), blocks never straddling a token.  Several
+// tokens of the block formats (wide6) take blocks of 6 groups once those make
+// at least two rounds of the GPU: fewer, longer blocks (measured 6 % faster
+// at 8 tokens, 4 % at 4; at 2 tokens, one round, slower).
+int gcnt_of(int k, int f, int T, int ncu, bool wide6 = false) {
   const int groups_per_token = k * f / 16;
   const int NG = T * groups_per_token;
+  if (wide6 && groups_per_token % 6 == 0 && NG / 6 >= 2 * ncu) return 6;
   int best = 1;
   int64_t best_cost = -1;
   for (int g = 3; g >= 1; g--) {
@@ -223,8 +227,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t s) {
       DecodeArgs b = a;
       b.fused_topk = 0;
       const int pid = prof_begin("decode_gateup", s);
-      hipError_t e = launch_k2(b, L.fmt_gate_up, fs, gcnt_of(L.k, L.f, L.T, ncu), L.T * L.k * L.f / 16 /
-                               gcnt_of(L.k, L.f, L.T, ncu), nib_layout(L.fmt_down), s);
+      const int g = gcnt_of(L.k, L.f, L.T, ncu, true);
+      hipError_t e = launch_k2(b, L.fmt_gate_up, fs, g, L.T * L.k * L.f / 16 / g, nib_layout(L.fmt_down), s);
       prof_end(pid, s);
       if (e != hipSuccess) return e;
     }

@@ -123,6 +123,9 @@ static hipError_t run_k2(const DecodeArgs& a, int blocks, int down_layout, hipSt
 
 template <int FMT, int FS, int D>
 static hipError_t run_k2_g(const DecodeArgs& a, int gcnt, int blocks, int dl, hipStream_t s) {
+  if constexpr (!is_vq(FMT)) {  // (several tokens of the block formats only)
+    if (gcnt == 6) return run_k2<FMT, FS, D, 6>(a, blocks, dl, s);
+  }
   switch (gcnt) {
     case 3: return run_k2<FMT, FS, D, 3>(a, blocks, dl, s);
     case 2: return run_k2<FMT, FS, D, 2>(a, blocks, dl, s);

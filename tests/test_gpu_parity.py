@@ -687,14 +687,16 @@ def test_decode_caller_routes_several_tokens(fsh):
 
 
 def test_decode_batch_invariance(decode_layer):
-    """Decode rows of a batch equal separate single-row calls, bit for bit."""
+    """Decode rows of a batch equal separate single-row calls, bit for bit:
+    4 and 8 tokens (gate/up blocks of 6 groups of 16 rows), 2 tokens (3)."""
     L, dl = decode_layer
-    idx, wt = synth.session_routes(1, sessions=4, steps=1, tag="inv")
-    x = synth.activations(1, ("inv", "x"), 4, 4096, synth.F32)
-    y4 = run_ffn(dl, x, synth.F32, idx, wt, lib.MOE_PATH_DECODE)
-    for t in range(4):
-        y1 = run_ffn(dl, x[t:t + 1], synth.F32, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
-        assert np.array_equal(y1[0], y4[t])
+    for T, steps in ((4, 1), (8, 2), (2, 1)):
+        idx, wt = synth.session_routes(1, sessions=T // steps, steps=steps, tag=f"inv{T}")
+        x = synth.activations(1, ("inv", "x", T), T, 4096, synth.F32)
+        yT = run_ffn(dl, x, synth.F32, idx, wt, lib.MOE_PATH_DECODE)
+        for t in range(T):
+            y1 = run_ffn(dl, x[t:t + 1], synth.F32, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
+            assert np.array_equal(y1[0], yT[t]), (T, t)
 
 
 @pytest.mark.parametrize("bias_gain", [False, True])
