@@ -68,14 +68,21 @@ __global__ __launch_bounds__(64 * K3U_WAVES) void k3u_kernel(DecodeArgs a) {
   const int R = a.T * a.k;
   const PlanView P = plan_view(a);
   const int U = P.n[0];
+  __shared__ int s_next;  // the first task no wave has taken yet
+  if (threadIdx.x == 0) s_next = K3_WAVES;
   for (int i = threadIdx.x; i < R * DN_ROWS; i += 64 * K3_WAVES) ye[i] = 0.0f;  // routes with no expert
   if constexpr (FR == FMT_IQ2 || FS == FMT_IQ2) iq2_build(a.grid, threadIdx.x, &itab);
   __syncthreads();
-  const int n_rt = U * RT_PARTS;
-  const int n_tasks = n_rt + (a.has_shared ? SH_PARTS : 0);
-  for (int task = wave; task < n_tasks; task += K3_WAVES) {
-    if (task < n_rt) {
-      const int u = task / RT_PARTS, part = task % RT_PARTS;
+  // The shared tasks (each runs every token) come first, then one task per
+  // distinct expert; a wave that finishes a task takes the next one not yet
+  // taken (the longest tasks start first, and the waves' chains come out
+  // even whatever the experts' route counts).  Each task writes its own ye
+  // entries, so the order changes no result.
+  const int n_sh = a.has_shared ? SH_PARTS : 0;
+  const int n_tasks = n_sh + U * RT_PARTS;
+  for (int task = wave; task < n_tasks;) {
+    if (task >= n_sh) {
+      const int u = (task - n_sh) / RT_PARTS, part = (task - n_sh) % RT_PARTS;
       const int e = P.uexp[u], r0 = P.uoff[u], nr = P.uoff[u + 1] - r0;
       const float* gain = a.down_gain ? a.down_gain + (int64_t)e * a.d : nullptr;
       constexpr int NS = DownRows<FR, F, RT_ROWS, 1>::NS;
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(64 * K3U_WAVES) void k3u_kernel(DecodeArgs a) {
         }
       }
     } else {
-      const int part = task - n_rt;
+      const int part = task;
       constexpr int NS = DownRows<FS, F, SH_ROWS, 1>::NS;
       constexpr int PDMAX = keep_codes<FS, F, SH_ROWS>() ? NS : 3;
       using DR = DownRows<FS, F, SH_ROWS, (NS < PDMAX ? NS : PDMAX)>;
@@ -124,6 +131,9 @@ __global__ __launch_bounds__(64 * K3U_WAVES) void k3u_kernel(DecodeArgs a) {
         }
       }
     }
+    int next = 0;
+    if ((threadIdx.x & 63) == 0) next = atomicAdd(&s_next, 1);  // LDS
+    task = __builtin_amdgcn_readfirstlane(next);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < a.T * DN_ROWS; i += 64 * K3_WAVES) {
