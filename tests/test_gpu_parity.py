@@ -686,6 +686,36 @@ def test_decode_caller_routes_several_tokens(fsh):
     assert per_token_rel_l2(y, y_ref).max() <= REL_L2
 
 
+@pytest.mark.parametrize("pattern", ["same", "distinct"])
+@pytest.mark.parametrize("shared", [False, True])
+def test_decode_several_tokens_route_extremes(pattern, shared):
+    """The several-token down launch runs the shared tasks first and lets
+    each wave take the next task not yet taken.  At the extremes of the
+    distinct-expert count the rows still equal one-token calls bit for bit:
+    every token on the same two experts (each route order rotated; fewer
+    tasks than waves, every expert with 8 routes) and every route on an
+    expert of its own (48 distinct experts)."""
+    k = 2 if pattern == "same" else 6
+    spec = synth.scaled_spec(E=64, k=k, d=1024, f=512, has_shared=shared)
+    L = synth.random_layer(spec, seed=73, workload="route_extremes")
+    dl = lib.DeviceLayer.from_synth(L, DEV)
+    T = 8
+    rng = np.random.default_rng(73)
+    if pattern == "same":
+        base = rng.choice(spec.E, k, replace=False)
+        idx = np.stack([np.roll(base, t) for t in range(T)]).astype(np.int32)
+    else:
+        idx = rng.permutation(spec.E)[:T * k].reshape(T, k).astype(np.int32)
+    wt = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    x = synth.activations(73, ("route_extremes", "x", pattern), T, spec.d, synth.BF16)
+    y = run_ffn(dl, x, synth.BF16, idx, wt, lib.MOE_PATH_DECODE)
+    for t in range(T):
+        y1 = run_ffn(dl, x[t:t + 1], synth.BF16, idx[t:t + 1], wt[t:t + 1], lib.MOE_PATH_DECODE)
+        assert np.array_equal(y1[0], y[t]), t
+    y_ref = oracle.ffn(L, x, oracle.BF16, idx, wt)
+    assert per_token_rel_l2(y, y_ref).max() <= REL_L2
+
+
 def test_decode_batch_invariance(decode_layer):
     """Decode rows of a batch equal separate single-row calls, bit for bit:
     4 and 8 tokens (gate/up blocks of 6 groups of 16 rows), 2 tokens (3)."""
