@@ -244,9 +244,10 @@ extern "C" {
 /* Where MOE_PATH_AUTO switches to prefill: the largest T at which the decode
  * path (in consecutive calls of at most MOE_DECODE_MAX_T tokens) measured
  * faster than one prefill call on the 384-expert, top-6, d=4096, f=2048
- * layer (bench.py, crossover with the caller's routes: 24 tokens 322
- * against 385 us, 32 tokens 427 against 404 us).  Under MOE_PATH_AUTO, moe_layer_forward runs such T in
- * chunks of MOE_DECODE_MAX_T tokens; the workspace covers one chunk. */
+ * layer (bench.py, crossover with the caller's routes: 24 tokens 318
+ * against 389 us, 32 tokens 424 against 414 us).  Under MOE_PATH_AUTO,
+ * moe_layer_forward runs such T in chunks of MOE_DECODE_MAX_T tokens; the
+ * workspace covers one chunk. */
 #define MOE_AUTO_DECODE_MAX_T 24
 
 /* moe_repack directions. */
